@@ -1,0 +1,17 @@
+"""MI355X (gfx950) gradient-aggregation hot path for P simulated
+data-parallel workers held in one GPU's HBM: Tensor Fusion pack/unpack,
+ring all-reduce (sum | avg), and THC uniform stochastic quantization with
+homomorphic integer aggregation.
+
+The computation lives in libga.so (HIP, built from csrc/ by build.py); the
+functions below are its C ABI (include/ga.h) under the same names, with
+torch tensors supplying device memory and the current stream. ``synth``
+holds the seeded workload generators.
+"""
+from ._native import (  # noqa: F401
+    AVG, BF16, EXPORTS, F32, LIB_PATH, MAX_WORKERS, RING_FUSED, RING_STEPWISE, SUM,
+    CopyDesc, FusionTables, GAError, RingStats, build_copy_table, ga_fuse_desc_check,
+    ga_fuse_pack, ga_fuse_plan, ga_fuse_unpack, ga_ring_allreduce_sim, load, n_partitions,
+    packed_bytes, thc_dequant, thc_int_aggregate, thc_minmax, thc_nmse, thc_nmse_ws_bytes,
+    thc_usq_quantize, upload_table,
+)

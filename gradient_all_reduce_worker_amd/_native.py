@@ -1,0 +1,290 @@
+"""ctypes binding of libga.so: the C ABI declared in include/ga.h, with the
+same names. Argument marshalling only (torch tensors -> device pointers and
+the current stream); every step of the path runs in the HIP library.
+
+Functions raise GAError on a non-zero status, carrying ga_last_error().
+If libga.so is missing or cannot be loaded, load() raises: there is no
+fallback implementation.
+"""
+import ctypes as C
+import os
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+F32, BF16 = 0, 1
+SUM, AVG = 0, 1
+RING_FUSED, RING_STEPWISE = 0, 1
+MAX_WORKERS = 64
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libga.so")
+
+EXPORTS = (
+    "ga_fuse_plan", "ga_fuse_desc_check", "ga_fuse_pack", "ga_fuse_unpack",
+    "ga_ring_allreduce_sim", "thc_minmax", "thc_usq_quantize", "thc_int_aggregate",
+    "thc_dequant", "thc_nmse", "thc_nmse_ws_bytes", "ga_last_error",
+)
+
+
+class GAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[{status}] {msg}")
+        self.status = status
+
+
+class CopyDesc(C.Structure):
+    _fields_ = [("src", C.c_void_p), ("dst", C.c_void_p), ("n", C.c_int64), ("start", C.c_int64)]
+
+
+class RingStats(C.Structure):
+    _fields_ = [("steps", C.c_int64), ("bytes_sent_per_worker", C.c_int64),
+                ("hbm_bytes", C.c_int64), ("launches", C.c_int64)]
+
+
+DESC_DTYPE = np.dtype([("src", np.uint64), ("dst", np.uint64), ("n", np.int64), ("start", np.int64)])
+
+_lib = None
+
+
+def load() -> C.CDLL:
+    """Load libga.so (built by __graft_entry__.build()); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    L = C.CDLL(LIB_PATH)
+    vp, i64, i32, u64 = C.c_void_p, C.c_int64, C.c_int32, C.c_uint64
+    P64 = C.POINTER(C.c_int64)
+    P32 = C.POINTER(C.c_int32)
+    L.ga_fuse_plan.argtypes = [P64, P32, i32, i64, P32, P64, P64, P32, P32]
+    L.ga_fuse_desc_check.argtypes = [vp, i64, i32, P64]
+    L.ga_fuse_pack.argtypes = [vp, i64, i64, i32, vp]
+    L.ga_fuse_unpack.argtypes = [vp, i64, i64, i32, vp]
+    L.ga_ring_allreduce_sim.argtypes = [C.POINTER(vp), i32, i64, i32, i32, i64, i32,
+                                        C.POINTER(RingStats), vp]
+    L.thc_minmax.argtypes = [C.POINTER(vp), i32, i64, i32, i64, vp, vp]
+    L.thc_usq_quantize.argtypes = [C.POINTER(vp), i32, i32, i64, i32, i64, vp, i32, u64,
+                                   C.POINTER(vp), vp]
+    L.thc_int_aggregate.argtypes = [C.POINTER(vp), i32, i64, i32, vp, vp]
+    L.thc_dequant.argtypes = [vp, i64, i32, i32, i64, vp, vp, i32, vp]
+    L.thc_nmse.argtypes = [vp, vp, i64, i32, vp, vp, C.c_size_t, vp]
+    L.thc_nmse_ws_bytes.argtypes = [i64]
+    L.thc_nmse_ws_bytes.restype = C.c_size_t
+    L.ga_last_error.argtypes = []
+    L.ga_last_error.restype = C.c_char_p
+    for name in EXPORTS:
+        if name not in ("thc_nmse_ws_bytes", "ga_last_error"):
+            getattr(L, name).restype = C.c_int
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise GAError(status, load().ga_last_error().decode())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"gradient buffers are float32 or bfloat16, not {t.dtype}")
+
+
+def _dev(t: torch.Tensor, what: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t.data_ptr()
+
+
+def _ptr_array(tensors: Sequence[torch.Tensor], what: str):
+    return (C.c_void_p * len(tensors))(*[_dev(t, what) for t in tensors])
+
+
+# ------------------------------------------------------------------ fusion
+def ga_fuse_plan(n_elems: Sequence[int], dtypes: Optional[Sequence[int]], cap_bytes: int):
+    """Host-only plan. Returns (buf_of, off_of, fill, buf_dtype) lists."""
+    L = load()
+    T = len(n_elems)
+    n = (C.c_int64 * max(T, 1))(*[int(v) for v in n_elems])
+    dts = None if dtypes is None else (C.c_int32 * max(T, 1))(*[int(v) for v in dtypes])
+    buf_of = (C.c_int32 * max(T, 1))()
+    off_of = (C.c_int64 * max(T, 1))()
+    fill = (C.c_int64 * max(T, 1))()
+    bdt = (C.c_int32 * max(T, 1))()
+    nb = C.c_int32()
+    _check(L.ga_fuse_plan(n, dts, T, int(cap_bytes), buf_of, off_of, fill, bdt, C.byref(nb)))
+    k = nb.value
+    return list(buf_of)[:T], list(off_of)[:T], list(fill)[:k], list(bdt)[:k]
+
+
+def ga_fuse_desc_check(h_desc: np.ndarray, dt: int) -> int:
+    """Validate a host descriptor table (DESC_DTYPE array); return its total."""
+    L = load()
+    h_desc = np.ascontiguousarray(h_desc, dtype=DESC_DTYPE)
+    total = C.c_int64()
+    _check(L.ga_fuse_desc_check(h_desc.ctypes.data if h_desc.size else None, h_desc.size, dt,
+                                C.byref(total)))
+    return total.value
+
+
+def ga_fuse_pack(d_desc: torch.Tensor, n_desc: int, total: int, dt: int, stream=None) -> None:
+    _check(load().ga_fuse_pack(_dev(d_desc, "d_desc"), n_desc, total, dt, _stream(stream)))
+
+
+def ga_fuse_unpack(d_desc: torch.Tensor, n_desc: int, total: int, dt: int, stream=None) -> None:
+    _check(load().ga_fuse_unpack(_dev(d_desc, "d_desc"), n_desc, total, dt, _stream(stream)))
+
+
+def build_copy_table(srcs: Sequence[int], dsts: Sequence[int], ns: Sequence[int]) -> np.ndarray:
+    """Host descriptor table from parallel lists of addresses and counts."""
+    t = np.zeros(len(ns), dtype=DESC_DTYPE)
+    t["src"] = np.asarray(srcs, dtype=np.uint64)
+    t["dst"] = np.asarray(dsts, dtype=np.uint64)
+    t["n"] = np.asarray(ns, dtype=np.int64)
+    if len(ns):
+        t["start"][1:] = np.cumsum(t["n"])[:-1]
+    return t
+
+
+def upload_table(h_desc: np.ndarray, device) -> torch.Tensor:
+    """Device copy of a descriptor table, as a uint8 tensor."""
+    raw = torch.from_numpy(h_desc.view(np.uint8).copy())
+    return raw.to(device)
+
+
+class FusionTables:
+    """Pack and unpack descriptor tables for P workers' tensors and fusion
+    buffers, built once on the host from a plan and uploaded once."""
+
+    def __init__(self, worker_tensors: List[List[torch.Tensor]], fusion_bufs: List[List[torch.Tensor]],
+                 buf_of: Sequence[int], off_of: Sequence[int]):
+        dt = _dt(worker_tensors[0][0])
+        self.dt = dt
+        es = 4 if dt == F32 else 2
+        srcs, dsts, ns = [], [], []
+        for w, tensors in enumerate(worker_tensors):
+            for t, x in enumerate(tensors):
+                if _dt(x) != dt:
+                    raise TypeError("one data type per fusion table")
+                srcs.append(_dev(x, "tensor"))
+                dsts.append(_dev(fusion_bufs[w][buf_of[t]], "fusion buffer") + int(off_of[t]) * es)
+                ns.append(x.numel())
+        self.h_pack = build_copy_table(srcs, dsts, ns)
+        self.h_unpack = build_copy_table(dsts, srcs, ns)
+        self.total = ga_fuse_desc_check(self.h_pack, dt)
+        ga_fuse_desc_check(self.h_unpack, dt)
+        device = worker_tensors[0][0].device
+        self.d_pack = upload_table(self.h_pack, device)
+        self.d_unpack = upload_table(self.h_unpack, device)
+        self.n_desc = len(ns)
+
+    def pack(self, stream=None) -> None:
+        ga_fuse_pack(self.d_pack, self.n_desc, self.total, self.dt, stream)
+
+    def unpack(self, stream=None) -> None:
+        ga_fuse_unpack(self.d_unpack, self.n_desc, self.total, self.dt, stream)
+
+
+# ------------------------------------------------------------------ ring
+def ga_ring_allreduce_sim(bufs: Sequence[torch.Tensor], op: int = AVG, part_elems: int = 0,
+                          mode: int = RING_FUSED, stream=None) -> dict:
+    L = load()
+    P = len(bufs)
+    if P == 0:
+        raise ValueError("no buffers")
+    N = bufs[0].numel()
+    dt = _dt(bufs[0])
+    for b in bufs:
+        if b.numel() != N or _dt(b) != dt:
+            raise ValueError("all worker buffers need the same size and dtype")
+    st = RingStats()
+    _check(L.ga_ring_allreduce_sim(_ptr_array(bufs, "buffer"), P, N, dt, op, part_elems, mode,
+                                   C.byref(st), _stream(stream)))
+    return {"steps": st.steps, "bytes_sent_per_worker": st.bytes_sent_per_worker,
+            "hbm_bytes": st.hbm_bytes, "launches": st.launches}
+
+
+# ------------------------------------------------------------------ THC
+def n_partitions(N: int, part_elems: int) -> int:
+    if N == 0:
+        return 0
+    plen = part_elems if part_elems > 0 else N
+    return (N + plen - 1) // plen
+
+
+def thc_minmax(bufs: Sequence[torch.Tensor], part_elems: int = 0, out: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    N = bufs[0].numel()
+    if out is None:
+        out = torch.empty((max(n_partitions(N, part_elems), 1), 2), dtype=torch.float32,
+                          device=bufs[0].device)
+    _check(load().thc_minmax(_ptr_array(bufs, "buffer"), len(bufs), N, _dt(bufs[0]), part_elems,
+                             _dev(out, "mM"), _stream(stream)))
+    return out
+
+
+def packed_bytes(N: int, b: int) -> int:
+    return (N * b + 7) // 8
+
+
+def thc_usq_quantize(bufs: Sequence[torch.Tensor], mM: torch.Tensor, b: int, seed: int,
+                     part_elems: int = 0, worker0: int = 0,
+                     packed: Optional[Sequence[torch.Tensor]] = None, stream=None):
+    N = bufs[0].numel()
+    if packed is None:
+        packed = [torch.empty(packed_bytes(N, b), dtype=torch.uint8, device=bufs[0].device)
+                  for _ in bufs]
+    _check(load().thc_usq_quantize(_ptr_array(bufs, "buffer"), len(bufs), worker0, N, _dt(bufs[0]),
+                                   part_elems, _dev(mM, "mM"), b, seed,
+                                   _ptr_array(packed, "packed"), _stream(stream)))
+    return packed
+
+
+def thc_int_aggregate(packed: Sequence[torch.Tensor], N: int, b: int,
+                      out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty(max(N, 1), dtype=torch.int32, device=packed[0].device)
+    _check(load().thc_int_aggregate(_ptr_array(packed, "packed"), len(packed), N, b,
+                                    _dev(out, "sum"), _stream(stream)))
+    return out
+
+
+def thc_dequant(S: torch.Tensor, N: int, P: int, b: int, mM: torch.Tensor, part_elems: int = 0,
+                out_dtype=torch.float32, out: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty(max(N, 1), dtype=out_dtype, device=S.device)
+    _check(load().thc_dequant(_dev(S, "sum"), N, P, b, part_elems, _dev(mM, "mM"), _dev(out, "out"),
+                              _dt(out), _stream(stream)))
+    return out
+
+
+def thc_nmse_ws_bytes(N: int) -> int:
+    return int(load().thc_nmse_ws_bytes(N))
+
+
+def thc_nmse(x: torch.Tensor, xhat: torch.Tensor, out: Optional[torch.Tensor] = None,
+             ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    N = x.numel()
+    if out is None:
+        out = torch.empty(3, dtype=torch.float64, device=x.device)
+    if ws is None:
+        ws = torch.empty(thc_nmse_ws_bytes(N), dtype=torch.uint8, device=x.device)
+    _check(load().thc_nmse(_dev(x, "x"), _dev(xhat, "xhat"), N, _dt(x), _dev(out, "out"),
+                           _dev(ws, "ws"), ws.numel(), _stream(stream)))
+    return out

@@ -1,0 +1,61 @@
+"""Build libga.so (HIP, gfx950) in-tree from csrc/*.hip.
+
+Floating-point flags matter for the results, not only for speed:
+  -ffp-contract=off          no fused multiply-add: every binary32 add,
+                             multiply and divide rounds on its own, in the
+                             order written
+  -fno-gpu-flush-denormals-to-zero, -fhip-fp32-correctly-rounded-divide-sqrt
+                             IEEE subnormals and a correctly rounded divide
+  -mno-packed-fp32-ops (via -Xclang -target-feature)
+                             no packed fp32 instructions
+"""
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(os.path.dirname(HERE), "_build")
+LIB = os.path.join(HERE, "libga.so")
+SOURCES = ["common.hip", "fusion.hip", "ring.hip", "thc.hip"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "-ffp-contract=off", "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+    # the host pass does not know the GPU feature flag; anything else is shown
+    noise = "unknown target feature"
+    for line in r.stderr.splitlines():
+        if line.strip() and noise not in line and "packed-fp32-ops" not in line and verbose:
+            print(line)
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,67 @@
+// common.hpp -- internals shared by the libga.so translation units: error
+// reporting across the C ABI, the worker pointer table passed by value in
+// kernel arguments, bf16 widening/rounding, and small launch helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "../../include/ga.h"
+
+namespace ga {
+
+constexpr int kThreads = 256;  // every kernel runs 256-thread workgroups (4 wave64)
+
+// ------------------------------------------------------------------ errors
+ga_status fail(ga_status code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ga_status check_launch(const char* what);
+
+// ------------------------------------------------------------------ pointers
+// Up to GA_MAX_WORKERS device pointers, passed by value (512 bytes of kernel
+// arguments). Indexing with a wave-uniform index compiles to a scalar load.
+struct PtrTable {
+    void* p[GA_MAX_WORKERS];
+};
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+inline size_t elem_size(ga_dtype dt) { return dt == GA_BF16 ? 2 : 4; }
+
+inline bool valid_dtype(int dt) { return dt == GA_F32 || dt == GA_BF16; }
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline int64_t n_partitions(int64_t N, int64_t part) {
+    if (N <= 0) return 0;
+    int64_t plen = part > 0 ? part : N;
+    return ceil_div(N, plen);
+}
+
+// Common argument checks for an array of P worker pointers.
+ga_status check_workers(const void* const* bufs, int32_t P, size_t align, const char* what);
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// binary32 -> bf16 with round-to-nearest-even: add 0x7FFF plus the lowest
+// kept bit, then drop the low 16 bits (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// 64-bit element index of the first element handled by this thread when
+// every thread of the grid handles `per_thread` consecutive elements.
+__device__ __forceinline__ int64_t thread_base(int per_thread) {
+    return ((int64_t)blockIdx.x * kThreads + threadIdx.x) * per_thread;
+}
+
+}  // namespace ga

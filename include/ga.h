@@ -1,0 +1,245 @@
+/*
+ * ga.h -- C ABI of libga.so, the MI355X (gfx950) gradient-aggregation hot
+ * path: P simulated data-parallel workers whose gradient buffers all sit in
+ * one GPU's HBM.
+ *
+ *   ga_fuse_plan / ga_fuse_pack / ga_fuse_unpack   Tensor Fusion
+ *   ga_ring_allreduce_sim                          ring all-reduce (sum | avg)
+ *   thc_minmax / thc_usq_quantize / thc_int_aggregate / thc_dequant / thc_nmse
+ *                                                  THC uniform quantization
+ *
+ * Pages cited:
+ *   [HVD]  "Horovod: Fast and Easy Distributed Deep Learning in TensorFlow"
+ *          (paper summary page), section 3.4 (ring-allreduce; Tensor Fusion).
+ *   [RING] systemcraft lesson "Collective Communication: Ring All-Reduce",
+ *          sections 4, 5 and 7 (schedule, volume, simulator).
+ *   [THC]  "THC: Accelerating Distributed Deep Learning Using Tensor
+ *          Homomorphic Compression", sections 2-4 (NMSE, uniform THC,
+ *          Algorithm 1, aggregation by the server) and 8 (aggregate width).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Ownership: the caller allocates and owns every buffer. The library keeps
+ *   no state between calls and allocates no device memory.
+ * Pointers: "device" pointers are HBM addresses (hipMalloc, or a torch
+ *   tensor's data_ptr()); "host" pointers are ordinary process memory.
+ *   Arrays of worker pointers (bufs, packed) are host arrays of device
+ *   pointers, P <= GA_MAX_WORKERS entries, read during the call only.
+ * Alignment: every device pointer must be aligned to its element size.
+ *   Buffers whose bases are 16-byte aligned take the 128-bit vector path;
+ *   others are handled by a slower per-element path with identical results.
+ * Execution: every call that takes `stream` (a hipStream_t; NULL is the
+ *   null stream) only enqueues work on it and returns. There is no implicit
+ *   device synchronisation; calls on one stream run in order.
+ * Errors: a negative status. On GA_EINVAL and GA_ENOTSUP nothing has been
+ *   enqueued. GA_EHIP reports a failed launch (hipGetLastError after the
+ *   launch). ga_last_error() returns a thread-local message for the last
+ *   failure on the calling thread. No C++ exception crosses the ABI.
+ * Empty input: N == 0 (or n_desc == 0) is a successful no-op.
+ * Values: floating-point inputs must be finite.
+ */
+#ifndef GA_H
+#define GA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int ga_status;
+#define GA_OK 0
+#define GA_EINVAL (-1)   /* bad argument; nothing enqueued */
+#define GA_ENOTSUP (-2)  /* valid but unsupported combination; nothing enqueued */
+#define GA_EHIP (-3)     /* the HIP runtime reported an error */
+
+#define GA_MAX_WORKERS 64
+
+typedef enum { GA_F32 = 0, GA_BF16 = 1 } ga_dtype;
+typedef enum { GA_SUM = 0, GA_AVG = 1 } ga_op;
+typedef enum { GA_RING_FUSED = 0, GA_RING_STEPWISE = 1 } ga_ring_mode;
+
+/* ------------------------------------------------------------------ */
+/* Tensor Fusion  ([HVD] 3.4, Tensor Fusion steps 1-6)                  */
+/* ------------------------------------------------------------------ */
+
+/*
+ * ga_fuse_plan -- host only, synchronous.
+ * Walks T tensors in the caller's (ready) order and assigns each to a
+ * fusion buffer of cap_bytes bytes: a tensor joins the open buffer while it
+ * fits in the remaining space and has the buffer's data type (step 1); the
+ * buffer is closed at the first tensor that does not, and that tensor opens
+ * the next one; an exact fit counts as a fit; a tensor larger than cap_bytes
+ * is reduced alone in a buffer of its own. Tensors are placed densely,
+ * without padding (step 3: "concatenated into a contiguous memory region").
+ *   n_elems[T]   element count of each tensor (>= 0)
+ *   dtype_of[T]  ga_dtype of each tensor, or NULL for all GA_F32
+ *   cap_bytes    fusion buffer capacity in bytes (> 0; [HVD] default 64 MB)
+ * Outputs (host arrays the caller sizes): buf_of[T] buffer id of each
+ * tensor; off_of[T] element offset inside that buffer; fill[T] (at most T
+ * buffers) element count of each buffer; buf_dtype[T] (nullable) the data
+ * type of each buffer; *n_buf the number of buffers.
+ */
+ga_status ga_fuse_plan(const int64_t* n_elems, const int32_t* dtype_of, int32_t T,
+                       int64_t cap_bytes, int32_t* buf_of, int64_t* off_of, int64_t* fill,
+                       int32_t* buf_dtype, int32_t* n_buf);
+
+/*
+ * One contiguous copy of n elements from src to dst. `start` is the
+ * exclusive prefix sum of n over the descriptor table (start[0] = 0,
+ * start[k+1] = start[k] + n[k]); the kernel uses it to find the copy that
+ * each workgroup's slice of the concatenated index space belongs to.
+ */
+typedef struct {
+    const void* src;   /* device */
+    void* dst;         /* device */
+    int64_t n;         /* elements */
+    int64_t start;     /* elements before this copy in the table */
+} ga_copy_desc;
+
+/*
+ * ga_fuse_desc_check -- host only. Validates a host copy of a descriptor
+ * table (non-null pointers aligned to the element size, n >= 0, consistent
+ * start values) and returns the total element count in *total_elems.
+ */
+ga_status ga_fuse_desc_check(const ga_copy_desc* h_desc, int64_t n_desc, ga_dtype dt,
+                             int64_t* total_elems);
+
+/*
+ * ga_fuse_pack / ga_fuse_unpack -- one launch performs every copy of the
+ * table: pack (step 3) copies each worker's tensors into its fusion buffers,
+ * unpack (step 5) copies the reduced buffers back into the tensors. The two
+ * differ only in which side of each descriptor is the fusion buffer.
+ *   d_desc       device copy of the table (caller uploads it once and may
+ *                reuse it across calls); must equal a table that
+ *                ga_fuse_desc_check accepts
+ *   n_desc       number of descriptors
+ *   total_elems  sum of n over the table
+ *   dt           element type (GA_F32: 4 bytes, GA_BF16: 2 bytes)
+ * Sources and destinations of different descriptors must not overlap.
+ * Each copy only touches [src, src + n) and [dst, dst + n).
+ */
+ga_status ga_fuse_pack(const ga_copy_desc* d_desc, int64_t n_desc, int64_t total_elems,
+                       ga_dtype dt, void* stream);
+ga_status ga_fuse_unpack(const ga_copy_desc* d_desc, int64_t n_desc, int64_t total_elems,
+                         ga_dtype dt, void* stream);
+
+/* ------------------------------------------------------------------ */
+/* Ring all-reduce over P simulated workers  ([HVD] 3.4; [RING] 4, 5, 7) */
+/* ------------------------------------------------------------------ */
+
+typedef struct {
+    int64_t steps;                 /* 2 (P - 1) communication steps per ring */
+    int64_t bytes_sent_per_worker; /* sum over partitions of 2 (P-1) C elem_bytes */
+    int64_t hbm_bytes;             /* algorithmic HBM bytes of the chosen mode */
+    int64_t launches;              /* kernel launches enqueued */
+} ga_ring_stats;
+
+/*
+ * ga_ring_allreduce_sim -- in place: every one of the P buffers ends holding
+ * the element-wise sum (op = GA_SUM) or average (GA_AVG) of all P, exactly
+ * as the ring schedule computes it.
+ *
+ * Each partition [p0, p0 + n) (part_elems elements; 0 means the whole
+ * buffer) is cut into P chunks of C = ceil(n / P) elements (trailing chunks
+ * shorter or empty). Scatter-reduce runs P - 1 steps: at step s worker i
+ * sends chunk (i - s) mod P to worker i + 1, which adds it into its own copy;
+ * after it worker j holds the finished sum of chunk (j + 1) mod P. All-gather
+ * runs P - 1 steps in which the finished chunk overwrites the other copies.
+ * So the sum of chunk c is folded in the order c, c+1, ..., c+P-1 (mod P),
+ * in binary32 with round-to-nearest-even and no fused multiply-add; bf16
+ * inputs are widened exactly and the partial sums stay binary32 on every
+ * hop, with one round-to-nearest-even to bf16 at the end. GA_AVG divides
+ * the finished sum by P once (binary32 division).
+ *   bufs        host array of P device pointers, each N elements of dt
+ *   P           1..GA_MAX_WORKERS
+ *   mode        GA_RING_FUSED: one pass that reads every buffer once and
+ *               writes every buffer once (2 P N elem_bytes of HBM traffic),
+ *               folding each element in the schedule's order.
+ *               GA_RING_STEPWISE: one launch per communication step,
+ *               2 (P - 1) launches moving the chunks as the schedule does
+ *               (5 (P - 1) N elem_bytes); GA_F32 only (bf16 partials need
+ *               binary32 storage on the wire) -> GA_ENOTSUP for GA_BF16.
+ *   st          optional (nullable) host struct receiving the accounting.
+ * Both modes give bit-identical results.
+ */
+ga_status ga_ring_allreduce_sim(void* const* bufs, int32_t P, int64_t N, ga_dtype dt, ga_op op,
+                                int64_t part_elems, ga_ring_mode mode, ga_ring_stats* st,
+                                void* stream);
+
+/* ------------------------------------------------------------------ */
+/* THC uniform stochastic quantization  ([THC] 2-4, Algorithm 1)        */
+/* ------------------------------------------------------------------ */
+
+/*
+ * thc_minmax -- Algorithm 1's preliminary round: per partition p of
+ * part_elems elements (0: one partition), m = the smallest and M = the
+ * largest element over all P workers' elements of that partition, written
+ * as d_mM[2p] = m, d_mM[2p + 1] = M (binary32; a negative zero is returned
+ * as +0). d_mM is a device array of 2 * ceil(N / part_elems) floats.
+ */
+ga_status thc_minmax(const void* const* bufs, int32_t P, int64_t N, ga_dtype dt,
+                     int64_t part_elems, float* d_mM, void* stream);
+
+/*
+ * thc_usq_quantize -- every worker quantizes its vector on the shared grid
+ * q_k = m + k (M - m) / (2^b - 1), k = 0 .. 2^b - 1, of its partition, by
+ * stochastic rounding to one of the two neighbouring grid points (unbiased,
+ * [THC] section 3), and emits the b-bit indices packed least significant
+ * bits first: element e occupies bits [(e b) mod 8, +b) of byte e b / 8.
+ * Arithmetic (binary32, L = 2^b - 1): range = M - m; s = L / range;
+ * u = (a - m) s; z0 = min(floor(u), L - 1); f = u - z0; up = (2 r + 1) <
+ * f 2^17 with r the element's 16-bit uniform; z = z0 + up; range == 0 gives
+ * z = 0. The uniform of element e of worker w is half (e mod 2) of word
+ * (e mod 8) / 2 of Philox4x32-10 (Salmon et al., SC'11) on counter
+ * (g mod 2^32, g >> 32, w, 0), g = e / 8, key (seed mod 2^32, seed >> 32).
+ *   bufs[P]     device vectors of N elements (dt); worker id of bufs[i] is
+ *               worker0 + i
+ *   d_mM        device grid ends from thc_minmax (same part_elems)
+ *   b           1, 2, 4 or 8
+ *   packed[P]   host array of device pointers, ceil(N b / 8) bytes each;
+ *               bits past element N - 1 in the last byte are written 0
+ */
+ga_status thc_usq_quantize(const void* const* bufs, int32_t P, int32_t worker0, int64_t N,
+                           ga_dtype dt, int64_t part_elems, const float* d_mM, int32_t b,
+                           uint64_t seed, uint8_t* const* packed, void* stream);
+
+/*
+ * thc_int_aggregate -- the server side of Algorithm 1: d_sum[e] = sum over
+ * the P workers of their b-bit index of element e, in int32 (exact; at most
+ * P (2^b - 1) <= 16320). packed as written by thc_usq_quantize; d_sum is a
+ * device array of N int32.
+ */
+ga_status thc_int_aggregate(const uint8_t* const* packed, int32_t P, int64_t N, int32_t b,
+                            int32_t* d_sum, void* stream);
+
+/*
+ * thc_dequant -- Algorithm 1's last step: divide the index sum by the
+ * number of workers P and map it back onto the grid:
+ * delta = range / L; out[e] = m + ((float)S[e] / (float)P) delta (binary32,
+ * no fused multiply-add); range == 0 gives m. out_dt GA_BF16 rounds the
+ * final value to nearest-even. d_sum: N int32; out: N elements of out_dt.
+ */
+ga_status thc_dequant(const int32_t* d_sum, int64_t N, int32_t P, int32_t b, int64_t part_elems,
+                      const float* d_mM, void* out, ga_dtype out_dt, void* stream);
+
+/*
+ * thc_nmse -- [THC] section 2, Figure 2(b): NMSE(x, xhat) =
+ * ||x - xhat||^2 / ||x||^2 with binary64 accumulation. Writes
+ * d_out[0] = numerator, d_out[1] = denominator, d_out[2] = their ratio
+ * (0 if both are 0, +inf if only the denominator is). d_ws is a device
+ * workspace of at least thc_nmse_ws_bytes(N) bytes.
+ */
+ga_status thc_nmse(const void* x, const void* xhat, int64_t N, ga_dtype dt, double* d_out,
+                   void* d_ws, size_t ws_bytes, void* stream);
+size_t thc_nmse_ws_bytes(int64_t N);
+
+/* Thread-local message describing the last failure on this thread. */
+const char* ga_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GA_H */

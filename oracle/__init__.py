@@ -50,7 +50,7 @@ def lib():
         L.orc_philox4x32_10.restype = None
         L.orc_uniform16.argtypes = [C.c_uint64, i32, i64]
         L.orc_uniform16.restype = C.c_uint32
-        L.orc_usq_quantize.argtypes = [vp, i64, i32, i32, i64, vp, i32, C.c_uint64, vp]
+        L.orc_usq_quantize.argtypes = [vp, i64, i32, i32, i64, vp, i32, C.c_uint64, i64, vp]
         L.orc_unpack_indices.argtypes = [vp, i64, i32, vp]
         L.orc_int_aggregate.argtypes = [C.POINTER(vp), i32, i64, i32, vp]
         L.orc_dequant.argtypes = [vp, i64, i32, i32, i64, vp, vp, i32]
@@ -144,14 +144,15 @@ def uniform16(seed: int, worker: int, e: int) -> int:
     return int(lib().orc_uniform16(seed, worker, e))
 
 
-def usq_quantize(x: np.ndarray, worker: int, part: int, mM: np.ndarray, b: int, seed: int
-                 ) -> np.ndarray:
+def usq_quantize(x: np.ndarray, worker: int, part: int, mM: np.ndarray, b: int, seed: int,
+                 e_offset: int = 0) -> np.ndarray:
+    """e_offset: index of x[0] in the worker's whole vector (keys the generator)."""
     N = x.size
     out = np.zeros((N * b + 7) // 8, dtype=np.uint8)
     mM = np.ascontiguousarray(mM, dtype=np.float32)
     x = np.ascontiguousarray(x)
     _check(lib().orc_usq_quantize(x.ctypes.data, N, _dt(x), worker, part, mM.ctypes.data, b,
-                                  seed, out.ctypes.data), "usq_quantize")
+                                  seed, e_offset, out.ctypes.data), "usq_quantize")
     return out
 
 

@@ -378,10 +378,13 @@ uint32_t orc_uniform16(uint64_t seed, int worker, int64_t e)
  *   z = z0 + up.
  * Packing: element e occupies bits [(e b) mod 8, (e b) mod 8 + b) of byte
  * floor(e b / 8), least significant bits first; unused bits are zero.
- * worker is the worker id keying the generator (counter word 2).
+ * worker is the worker id keying the generator (counter word 2); e_offset is
+ * the index of x[0] in the worker's whole vector (0 for a whole vector; the
+ * start of a partition when one partition is quantized on its own), so the
+ * generator is keyed by global element indices either way.
  */
 int orc_usq_quantize(const void *x, int64_t N, int dt, int worker, int64_t part, const float *mM,
-                     int b, uint64_t seed, uint8_t *packed)
+                     int b, uint64_t seed, int64_t e_offset, uint8_t *packed)
 {
     if (!(b == 1 || b == 2 || b == 4 || b == 8) || N < 0)
         return -1;
@@ -404,7 +407,7 @@ int orc_usq_quantize(const void *x, int64_t N, int dt, int worker, int64_t part,
                 if (z0 > (float)(L - 1))
                     z0 = (float)(L - 1);
                 float f = u - z0;
-                uint32_t r = uniform16(seed, worker, e);
+                uint32_t r = uniform16(seed, worker, e_offset + e);
                 int up = (float)(2u * r + 1u) < f * 131072.0f;
                 z = (uint32_t)z0 + (uint32_t)up;
             }

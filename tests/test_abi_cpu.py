@@ -1,0 +1,135 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, the host-only fusion plan matches the oracle's, and
+argument errors come back as status codes before anything is enqueued."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from gradient_all_reduce_worker_amd import _native as nat
+from gradient_all_reduce_worker_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ga.h")
+EINVAL, ENOTSUP = -1, -2
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:ga|thc)_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported():
+    L = nat.load()
+    names = _declared()
+    assert len(names) == 12
+    assert set(names) == set(nat.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+    syms = subprocess.run(["nm", "-D", "--defined-only", nat.LIB_PATH], capture_output=True,
+                          text=True, check=True).stdout
+    exported = {line.split()[-1] for line in syms.splitlines() if " T " in line}
+    assert set(names) <= exported
+
+
+@pytest.mark.parametrize("name", ["fusion", "resnet101", "vgg16"])
+def test_fuse_plan_matches_oracle_on_workloads(name):
+    w = synth.workload(name)
+    got = nat.ga_fuse_plan(w.sizes, None, 64 << 20)
+    want = oracle.fuse_plan(w.sizes, [0] * len(w.sizes), 64 << 20)
+    assert tuple(got) == tuple(want)
+
+
+def test_fuse_plan_matches_oracle_random():
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        T = int(rng.integers(0, 50))
+        sizes = [int(v) for v in rng.integers(0, 3000, size=T)]
+        dts = [int(v) for v in rng.integers(0, 2, size=T)]
+        cap = int(rng.integers(1, 20000))
+        assert tuple(nat.ga_fuse_plan(sizes, dts, cap)) == tuple(oracle.fuse_plan(sizes, dts, cap))
+
+
+def test_fuse_plan_errors():
+    with pytest.raises(nat.GAError) as e:
+        nat.ga_fuse_plan([1, 2], None, 0)
+    assert e.value.status == EINVAL
+    with pytest.raises(nat.GAError):
+        nat.ga_fuse_plan([1, -2], None, 100)
+    with pytest.raises(nat.GAError):
+        nat.ga_fuse_plan([1, 2], [0, 7], 100)
+
+
+def test_desc_check():
+    t = nat.build_copy_table([0x1000, 0x2000], [0x3000, 0x4000], [10, 20])
+    assert nat.ga_fuse_desc_check(t, nat.F32) == 30
+    bad = t.copy()
+    bad["start"][1] = 11
+    with pytest.raises(nat.GAError):
+        nat.ga_fuse_desc_check(bad, nat.F32)
+    bad = t.copy()
+    bad["src"][0] = 0x1002            # not 4-byte aligned for fp32
+    with pytest.raises(nat.GAError):
+        nat.ga_fuse_desc_check(bad, nat.F32)
+    assert nat.ga_fuse_desc_check(bad, nat.BF16) == 30
+    assert nat.ga_fuse_desc_check(t[:0], nat.F32) == 0
+
+
+def _ptrs(vals):
+    return (C.c_void_p * len(vals))(*vals)
+
+
+def test_argument_errors_return_before_enqueue():
+    """These calls fail validation, so the (null) stream is never touched."""
+    L = nat.load()
+    good = _ptrs([0x10000 * (i + 1) for i in range(4)])
+    st = nat.RingStats()
+    ring = L.ga_ring_allreduce_sim
+    assert ring(good, 0, 16, 0, 1, 0, 0, C.byref(st), None) == EINVAL          # P = 0
+    assert ring(good, 65, 16, 0, 1, 0, 0, C.byref(st), None) == EINVAL         # P > 64
+    assert ring(good, 4, -1, 0, 1, 0, 0, C.byref(st), None) == EINVAL          # N < 0
+    assert ring(good, 4, 16, 5, 1, 0, 0, C.byref(st), None) == EINVAL          # dtype
+    assert ring(good, 4, 16, 0, 9, 0, 0, C.byref(st), None) == EINVAL          # op
+    assert ring(good, 4, 16, 0, 1, 0, 7, C.byref(st), None) == EINVAL          # mode
+    assert ring(_ptrs([0x10000, 0, 0x30000, 0x40000]), 4, 16, 0, 1, 0, 0, None, None) == EINVAL
+    assert ring(_ptrs([0x10002, 0x20000, 0x30000, 0x40000]), 4, 16, 0, 1, 0, 0, None, None) == EINVAL
+    assert ring(_ptrs([0x10000, 0x10020, 0x30000, 0x40000]), 4, 16, 0, 1, 0, 0, None, None) == EINVAL
+    assert ring(good, 4, 16, 1, 1, 0, 1, None, None) == ENOTSUP                # stepwise bf16
+    assert b"stepwise" in L.ga_last_error()
+    # empty input is a successful no-op that still reports the accounting
+    assert ring(good, 4, 0, 0, 1, 0, 0, C.byref(st), None) == 0
+    assert st.steps == 0 and st.launches == 0
+
+    mM = 0x50000
+    assert L.thc_minmax(good, 4, 16, 0, -1, mM, None) == EINVAL
+    assert L.thc_minmax(good, 4, 16, 0, 0, None, None) == EINVAL
+    q = L.thc_usq_quantize
+    assert q(good, 4, 0, 16, 0, 0, mM, 3, 1, good, None) == EINVAL             # b = 3
+    assert q(good, 4, -1, 16, 0, 0, mM, 4, 1, good, None) == EINVAL            # worker0
+    assert q(good, 4, 0, 16, 0, 0, None, 4, 1, good, None) == EINVAL           # grid
+    assert L.thc_int_aggregate(good, 4, 16, 16, 0x60000, None) == EINVAL       # b = 16
+    assert L.thc_int_aggregate(good, 4, 16, 4, 0x60002, None) == EINVAL        # misaligned sum
+    assert L.thc_dequant(0x60000, 16, 0, 4, 0, mM, 0x70000, 0, None) == EINVAL  # P = 0
+    assert L.thc_dequant(0x60000, 16, 4, 4, 0, mM, 0x70001, 1, None) == EINVAL  # misaligned out
+    ws = nat.thc_nmse_ws_bytes(16)
+    assert L.thc_nmse(0x60000, 0x70000, 16, 0, 0x80000, 0x90000, ws - 8, None) == EINVAL
+    assert L.ga_fuse_pack(0x1000, 3, 30, 4, None) == EINVAL                    # dtype
+    assert L.ga_fuse_pack(0x1000, -1, 30, 0, None) == EINVAL
+    assert L.ga_fuse_pack(None, 0, 0, 0, None) == 0                            # empty table
+
+
+def test_ring_stats_accounting_without_gpu():
+    """The stats reported for an empty-of-work call follow the ring volume
+    formula; here checked through the oracle's accounting on the same
+    geometry (P N elements split in ceil chunks)."""
+    for P, N, part in [(4, 8, 0), (3, 10, 0), (8, 1 << 12, 1000)]:
+        steps, nbytes = oracle.ring_stats(P, N, part, 4)
+        assert steps == 2 * (P - 1)
+        plen = part or N
+        want = sum(2 * (P - 1) * -(-min(plen, N - p0) // P) * 4 for p0 in range(0, N, plen))
+        assert nbytes == want

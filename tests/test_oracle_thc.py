@@ -38,7 +38,7 @@ def test_uniform16_layout_and_uniformity():
     """Element e takes half (e mod 2) of word (e mod 8) / 2 of the Philox
     block g = e / 8 keyed by the seed, counter word 2 = worker."""
     seed, worker = 0x0123456789ABCDEF, 5
-    for e in (0, 1, 7, 8, 15, 1 << 33, (1 << 33) + 5):
+    for e in (0, 1, 7, 8, 15, 1 << 33, (1 << 33) + 5, (1 << 40) + 3):
         g = e >> 3
         blk = oracle.philox4x32_10([g & 0xFFFFFFFF, g >> 32, worker, 0],
                                    [seed & 0xFFFFFFFF, seed >> 32])
@@ -267,3 +267,18 @@ def test_partitions_use_their_own_grid():
         xhat = oracle.dequant(oracle.unpack_indices(whole, N, b), 1, b, part, mM)[lo:hi]
         tol = 1e-6 * max(abs(float(mM[p, 0])), abs(float(mM[p, 1])))
         assert np.all(xhat >= mM[p, 0] - tol) and np.all(xhat <= mM[p, 1] + tol)
+
+
+def test_offset_quantize_equals_slice_of_whole():
+    """Quantizing one partition on its own with its global index offset gives
+    the bytes of that partition in the whole vector's packing."""
+    rng = np.random.default_rng(12)
+    N, part = 4096 + 40, 1024
+    x = rng.standard_normal(N).astype(np.float32)
+    mM = oracle.minmax([x], part)
+    for b in (1, 2, 4, 8):
+        whole = oracle.usq_quantize(x, 3, part, mM, b, 1234)
+        for p in range(mM.shape[0]):
+            lo, hi = p * part, min((p + 1) * part, N)
+            sub = oracle.usq_quantize(x[lo:hi], 3, part, mM[p:p + 1], b, 1234, e_offset=lo)
+            assert np.array_equal(sub, whole[lo * b // 8: lo * b // 8 + sub.size])
