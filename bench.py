@@ -1,0 +1,209 @@
+"""Throughput of the whole gradient-aggregation hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload shard]
+
+One step is one pass of every stage over one batch of synthetic gradients
+already resident in HBM (see gradient_all_reduce_worker_amd.pipeline):
+for the default workload, 8 simulated workers x 2^31 bf16 gradients each
+(Laplace(0, 1e-3)): THC min/max, USQ quantize (b = 2), ring all-reduce
+average with fp32 accumulation over 2^20-element partitions, integer
+aggregate, dequantize, NMSE. `value` is aggregated gradient bytes
+(P N elem_bytes) per second of step time.
+
+Prints ONE JSON line. `roofline` describes the dominant kernel (the fused
+ring) from HIP events around its launches inside the timed steps;
+`cpu_baseline` times the oracle (plain C, one thread) on a bounded sample of
+the same workload's partitions on this host; `traffic` comes from the
+committed rocprofv3 PMC summary when it was taken on the current ring
+source, else null.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "aggregated gradient GB/s (P·N·bytes/s) vs HBM peak; THC quantize Gelem/s + NMSE"
+HBM_PEAK_GBS = 8000.0
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "ring_fused_shard_pmc.json")
+RING_SRC = os.path.join(ROOT, "gradient_all_reduce_worker_amd", "csrc", "ring.hip")
+
+DESCRIPTIONS = {
+    "small": "4 workers x 1,048,576 fp32 N(0,0.01^2); ring avg + THC USQ b=4",
+    "fusion": "8 workers x 200 fp32 tensors (log-uniform 1K..256K); 64 MiB fusion, ring avg",
+    "resnet101": "16 workers x ResNet-101 gradients (314 tensors, 44,549,160 fp32); fusion + ring avg",
+    "vgg16": "32 workers x VGG-16 gradients (138,357,544 fp32); THC USQ b=4,8 + ring avg + NMSE",
+    "shard": ("8 workers x 2,147,483,648 bf16 Laplace(0,1e-3); ring avg with fp32 accumulation "
+              "in 2^20-element partitions + THC USQ b=2 (uint8-packed), int32 sum, dequant, NMSE"),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def ring_source_hash() -> str:
+    with open(RING_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per ring launch from the committed PMC summary, if it was
+    measured on this workload and on the current ring source."""
+    try:
+        with open(PMC_SUMMARY) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("workload") != workload or d.get("ring_src_sha256_16") != ring_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(pipe, samples, budget_s: float):
+    """The oracle on whole partitions of the same workload: every stage of
+    the step, on the host, single-threaded. Returns aggregated GB/s."""
+    import numpy as np
+
+    import oracle
+
+    w = pipe.w
+    P = pipe.P
+    done_elems, t_total, used = 0, 0.0, 0
+    for p in sorted(samples):
+        xs = [a.copy() for a in samples[p]]
+        n = xs[0].size
+        lo = p * (w.part_elems or pipe.N)
+        t0 = time.perf_counter()
+        mM = oracle.minmax(xs, n)
+        packed = {b: [oracle.usq_quantize(xs[i], i, n, mM, b, w.quant_seed, e_offset=lo)
+                      for i in range(P)] for b in w.thc_bits}
+        oracle.ring_fold(xs, op=oracle.AVG, part=w.ring_part_elems and n)
+        for b in w.thc_bits:
+            S = oracle.int_aggregate(packed[b], n, b)
+            xh = oracle.dequant(S, P, b, n, mM, w.dtype)
+            oracle.nmse(xs[0], xh)
+        t_total += time.perf_counter() - t0
+        done_elems += n
+        used += 1
+        if t_total >= budget_s:
+            break
+    gbs = P * done_elems * w.elem_bytes / t_total / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{used} of {pipe.n_partitions()} partitions ({done_elems} elements x {P} "
+                      f"workers), all stages, {t_total:.1f} s on one host thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="shard", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one 1 GiB torch copy first (PMC calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py: this build measures one GPU only (P simulated workers in one HBM); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gradient_all_reduce_worker_amd as ga
+    from gradient_all_reduce_worker_amd.pipeline import Pipeline, StageTimer
+
+    ga.load()                       # fails loudly without the HIP library
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    pipe = Pipeline(args.workload)
+    t0 = time.perf_counter()
+    pipe.setup()
+    log(f"setup {args.workload}: {time.perf_counter() - t0:.1f} s")
+
+    samples = None
+    if not args.no_cpu and not pipe.w.fused:
+        n_part = pipe.n_partitions()
+        want = min(n_part, 160)
+        which = sorted({int(i * n_part / want) for i in range(want)})
+        samples = pipe.sample_inputs(which)
+
+    if args.copy_probe:
+        # a plain device copy of known size (1 GiB read, 1 GiB written), for
+        # scaling the PMC byte counters of the kernels against it
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # the first pass sees the pristine gradients: its NMSE is the one reported
+    # (later passes run the same kernels over the averaged buffers)
+    pipe.step()
+    torch.cuda.synchronize()
+    nmse = {b: pipe.nmse[b].cpu().numpy().tolist() for b in pipe.nmse}
+    for _ in range(max(args.warmup - 1, 0)):
+        pipe.step()
+    torch.cuda.synchronize()
+
+    timer = StageTimer()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        pipe.step(timer)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stage_ms = timer.mean_ms()
+    calls = timer.count()
+    log(f"timed {args.steps} steps: {elapsed:.3f} s")
+
+    P, N, s = pipe.P, pipe.N, pipe.w.elem_bytes
+    ms_step = elapsed / args.steps * 1e3
+    value = P * N * s / (elapsed / args.steps) / 1e9
+    nbytes = pipe.stage_bytes()
+    stages = {}
+    for k, ms in stage_ms.items():
+        gbs = nbytes[k] / (ms * 1e-3) / 1e9
+        stages[k] = {"ms": round(ms, 4), "calls_per_step": calls[k] // args.steps,
+                     "alg_bytes": nbytes[k], "GB/s": round(gbs, 1),
+                     "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    quant = {k: round(P * N / (v * 1e-3) / 1e9, 2) for k, v in stage_ms.items()
+             if k.startswith("thc_usq_quantize")}
+
+    ring_ms = stage_ms["ring_allreduce"]
+    achieved = nbytes["ring_allreduce"] / (ring_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic_from_profile(args.workload),
+                "kernel": "ring_fused_vec_kernel", "alg_bytes_per_launch": nbytes["ring_allreduce"]}
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {DESCRIPTIONS[args.workload]}", "P": P, "N": N,
+                   "elem": "bf16" if pipe.w.dtype == ga.BF16 else "fp32",
+                   "partition_elems": pipe.w.part_elems, "thc_bits": list(pipe.w.thc_bits),
+                   "parallelism": "1 GPU, P simulated workers"},
+        "roofline": roofline,
+        "thc_quantize_gelem_s": quant,
+        "nmse": {f"b{b}": v[2] for b, v in nmse.items()},
+        "stages": stages,
+    }
+    if samples is not None:
+        out["cpu_baseline"] = cpu_baseline(pipe, samples, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -309,7 +309,13 @@ extern "C" ga_status ga_ring_allreduce_sim(void* const* bufs, int32_t P, int64_t
     if (mode != GA_RING_FUSED && mode != GA_RING_STEPWISE)
         return fail(GA_EINVAL, "%s: unknown mode %d", what, (int)mode);
     if (N < 0 || part_elems < 0) return fail(GA_EINVAL, "%s: negative size", what);
+    if (P < 1 || P > GA_MAX_WORKERS)
+        return fail(GA_EINVAL, "%s: P = %d outside [1, %d]", what, P, GA_MAX_WORKERS);
     const size_t es = elem_size(dt);
+    if (N == 0) {                       // empty buffers (possibly null): nothing to do
+        if (st) *st = ga_ring_stats{0, 0, 0, 0};
+        return GA_OK;
+    }
     ga_status rc = check_workers(bufs, P, es, what);
     if (rc) return rc;
     if (!disjoint(bufs, P, N * (int64_t)es))

@@ -499,9 +499,10 @@ extern "C" ga_status thc_minmax(const void* const* bufs, int32_t P, int64_t N, g
     const char* what = "thc_minmax";
     if (!valid_dtype(dt)) return fail(GA_EINVAL, "%s: unknown dtype %d", what, (int)dt);
     if (N < 0 || part_elems < 0) return fail(GA_EINVAL, "%s: negative size", what);
+    if (P < 1 || P > GA_MAX_WORKERS) return fail(GA_EINVAL, "%s: P = %d outside [1, %d]", what, P, GA_MAX_WORKERS);
+    if (N == 0) return GA_OK;
     ga_status rc = check_workers(bufs, P, elem_size(dt), what);
     if (rc) return rc;
-    if (N == 0) return GA_OK;
     if (!d_mM || !aligned(d_mM, 8)) return fail(GA_EINVAL, "%s: bad output pointer", what);
     const int64_t plen = part_elems > 0 ? part_elems : N;
     const int64_t n_part = n_partitions(N, part_elems);
@@ -534,10 +535,11 @@ extern "C" ga_status thc_usq_quantize(const void* const* bufs, int32_t P, int32_
     if (!valid_dtype(dt)) return fail(GA_EINVAL, "%s: unknown dtype %d", what, (int)dt);
     if (!valid_bits(b)) return fail(GA_EINVAL, "%s: b = %d is not 1, 2, 4 or 8", what, b);
     if (N < 0 || part_elems < 0 || worker0 < 0) return fail(GA_EINVAL, "%s: negative argument", what);
+    if (P < 1 || P > GA_MAX_WORKERS) return fail(GA_EINVAL, "%s: P = %d outside [1, %d]", what, P, GA_MAX_WORKERS);
+    if (N == 0) return GA_OK;
     ga_status rc = check_workers(bufs, P, elem_size(dt), what);
     if (rc) return rc;
     if ((rc = check_workers(reinterpret_cast<const void* const*>(packed), P, 1, what))) return rc;
-    if (N == 0) return GA_OK;
     if (!d_mM || !aligned(d_mM, 4)) return fail(GA_EINVAL, "%s: bad grid pointer", what);
     const int64_t plen = part_elems > 0 ? part_elems : N;
     int vec_ok = 1;
@@ -579,9 +581,10 @@ extern "C" ga_status thc_int_aggregate(const uint8_t* const* packed, int32_t P, 
     const char* what = "thc_int_aggregate";
     if (!valid_bits(b)) return fail(GA_EINVAL, "%s: b = %d is not 1, 2, 4 or 8", what, b);
     if (N < 0) return fail(GA_EINVAL, "%s: negative size", what);
+    if (P < 1 || P > GA_MAX_WORKERS) return fail(GA_EINVAL, "%s: P = %d outside [1, %d]", what, P, GA_MAX_WORKERS);
+    if (N == 0) return GA_OK;
     ga_status rc = check_workers(reinterpret_cast<const void* const*>(packed), P, 1, what);
     if (rc) return rc;
-    if (N == 0) return GA_OK;
     if (!d_sum || !aligned(d_sum, 4)) return fail(GA_EINVAL, "%s: bad output pointer", what);
     const int64_t nbytes = (N * b + 7) / 8;
     int vec_ok = aligned(d_sum, 16);

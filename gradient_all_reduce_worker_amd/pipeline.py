@@ -1,0 +1,176 @@
+"""One pass of the whole gradient-aggregation path over a workload, on one GPU.
+
+A step runs, in this order, on the current stream:
+  fused workloads (Tensor Fusion, Horovod page section 3.4):
+      pack every worker's tensors into its fusion buffers (one launch),
+      ring-average each fusion buffer across the P workers,
+      unpack the averages back into the tensors (one launch);
+      a tensor larger than the fusion buffer is reduced alone, in place;
+  flat workloads (one gradient vector per worker):
+      THC min/max per partition, USQ quantize for every bit width (both read
+      the workers' gradients before the ring overwrites them),
+      ring-average the gradients in place (the exact average),
+      then per bit width: integer aggregate, dequantize, NMSE of the THC
+      estimate against the exact average.
+
+Only the binding is called; all arithmetic runs in libga.so. Per-call HIP
+events (torch.cuda.Event on the stream the kernels are launched on) time
+every stage when a timer is passed.
+"""
+from collections import defaultdict
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+from . import _native as ga
+from . import synth
+
+
+class StageTimer:
+    """Events around every library call of a step, per stage name."""
+
+    def __init__(self):
+        self.pairs: Dict[str, list] = defaultdict(list)
+
+    def wrap(self, name: str, fn, *a, **k):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        out = fn(*a, **k)
+        e.record()
+        self.pairs[name].append((s, e))
+        return out
+
+    def mean_ms(self) -> Dict[str, float]:
+        torch.cuda.synchronize()
+        return {k: float(np.mean([s.elapsed_time(e) for s, e in v])) for k, v in self.pairs.items()}
+
+    def count(self) -> Dict[str, int]:
+        return {k: len(v) for k, v in self.pairs.items()}
+
+
+def _call(timer: Optional[StageTimer], name: str, fn, *a, **k):
+    if timer is None:
+        return fn(*a, **k)
+    return timer.wrap(name, fn, *a, **k)
+
+
+class Pipeline:
+    def __init__(self, name: str, device="cuda", cap_bytes: int = 64 << 20):
+        self.w = synth.workload(name)
+        self.device = torch.device(device)
+        self.cap = cap_bytes
+        self.tdt = torch.float32 if self.w.dtype == ga.F32 else torch.bfloat16
+        self.P = self.w.P
+        self.N = self.w.N
+        self.nmse: Dict[int, torch.Tensor] = {}
+
+    # ------------------------------------------------------------ setup
+    def setup(self) -> None:
+        w, dev = self.w, self.device
+        if w.fused:
+            self.tensors = [synth.worker_tensors(w, i, dev) for i in range(self.P)]
+            self.buf_of, self.off_of, self.fill, _ = ga.ga_fuse_plan(w.sizes, None, self.cap)
+            es = w.elem_bytes
+            # a buffer holding one tensor larger than the capacity: reduce that
+            # tensor in place instead of copying it
+            self.alone = {k for k, f in enumerate(self.fill) if f * es > self.cap}
+            self.bufs = [[None if k in self.alone else torch.empty(f, dtype=self.tdt, device=dev)
+                          for k, f in enumerate(self.fill)] for _ in range(self.P)]
+            for k in self.alone:
+                t = self.buf_of.index(k)
+                for i in range(self.P):
+                    self.bufs[i][k] = self.tensors[i][t]
+            keep = [t for t in range(len(w.sizes)) if self.buf_of[t] not in self.alone]
+            self.tables = ga.FusionTables([[self.tensors[i][t] for t in keep] for i in range(self.P)],
+                                          self.bufs, [self.buf_of[t] for t in keep],
+                                          [self.off_of[t] for t in keep]) if keep else None
+        else:
+            self.flat = [torch.empty(self.N, dtype=self.tdt, device=dev) for _ in range(self.P)]
+            for i in range(self.P):
+                synth.worker_flat(w, i, self.flat[i])
+            n_part = ga.n_partitions(self.N, w.part_elems)
+            self.mM = torch.empty((n_part, 2), dtype=torch.float32, device=dev)
+            self.packed = {b: [torch.empty(ga.packed_bytes(self.N, b), dtype=torch.uint8, device=dev)
+                               for _ in range(self.P)] for b in w.thc_bits}
+            self.S = {b: torch.empty(self.N, dtype=torch.int32, device=dev) for b in w.thc_bits}
+            self.xhat = {b: torch.empty(self.N, dtype=self.tdt, device=dev) for b in w.thc_bits}
+            self.nmse = {b: torch.empty(3, dtype=torch.float64, device=dev) for b in w.thc_bits}
+            self.ws = torch.empty(ga.thc_nmse_ws_bytes(self.N), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    # ------------------------------------------------------------ step
+    def step(self, timer: Optional[StageTimer] = None) -> None:
+        w = self.w
+        if w.fused:
+            if self.tables is not None:
+                _call(timer, "fuse_pack", self.tables.pack)
+            for k in range(len(self.fill)):
+                _call(timer, "ring_allreduce", ga.ga_ring_allreduce_sim,
+                      [self.bufs[i][k] for i in range(self.P)], ga.AVG, w.ring_part_elems)
+            if self.tables is not None:
+                _call(timer, "fuse_unpack", self.tables.unpack)
+            return
+        part = w.part_elems
+        _call(timer, "thc_minmax", ga.thc_minmax, self.flat, part, self.mM)
+        for b in w.thc_bits:
+            _call(timer, f"thc_usq_quantize_b{b}", ga.thc_usq_quantize, self.flat, self.mM, b,
+                  w.quant_seed, part, 0, self.packed[b])
+        _call(timer, "ring_allreduce", ga.ga_ring_allreduce_sim, self.flat, ga.AVG,
+              w.ring_part_elems)
+        for b in w.thc_bits:
+            _call(timer, f"thc_int_aggregate_b{b}", ga.thc_int_aggregate, self.packed[b], self.N, b,
+                  self.S[b])
+            _call(timer, f"thc_dequant_b{b}", ga.thc_dequant, self.S[b], self.N, self.P, b, self.mM,
+                  part, self.tdt, self.xhat[b])
+            _call(timer, f"thc_nmse_b{b}", ga.thc_nmse, self.flat[0], self.xhat[b], self.nmse[b],
+                  self.ws)
+
+    # ------------------------------------------------------------ accounting
+    def stage_bytes(self) -> Dict[str, float]:
+        """Algorithmic HBM bytes of one call of each stage (per launch)."""
+        w, P, N, s = self.w, self.P, self.N, self.w.elem_bytes
+        out = {}
+        if w.fused:
+            moved = sum(int(n) for t, n in enumerate(w.sizes) if self.buf_of[t] not in self.alone)
+            out["fuse_pack"] = out["fuse_unpack"] = 2.0 * P * moved * s
+            out["ring_allreduce"] = 2.0 * P * N * s / len(self.fill)   # mean over the buffers
+            return out
+        out["thc_minmax"] = 1.0 * P * N * s
+        out["ring_allreduce"] = 2.0 * P * N * s
+        for b in w.thc_bits:
+            out[f"thc_usq_quantize_b{b}"] = P * N * (s + b / 8.0)
+            out[f"thc_int_aggregate_b{b}"] = P * N * b / 8.0 + 4.0 * N
+            out[f"thc_dequant_b{b}"] = 4.0 * N + N * s
+            out[f"thc_nmse_b{b}"] = 2.0 * N * s
+        return out
+
+    # ------------------------------------------------------------ sampling
+    def partition_ranges(self, which: List[int]):
+        plen = self.w.part_elems or self.N
+        return [(p, p * plen, min((p + 1) * plen, self.N)) for p in which]
+
+    def n_partitions(self) -> int:
+        return ga.n_partitions(self.N, self.w.part_elems)
+
+    def sample_inputs(self, which: List[int]) -> Dict[int, List[np.ndarray]]:
+        """Host copies of every worker's elements of the chosen partitions."""
+        out = {}
+        for p, lo, hi in self.partition_ranges(which):
+            out[p] = [synth.to_numpy_bits(self.flat[i][lo:hi]) for i in range(self.P)]
+        return out
+
+    def sample_outputs(self, which: List[int]) -> Dict[int, dict]:
+        out = {}
+        for p, lo, hi in self.partition_ranges(which):
+            d = {"ring": [synth.to_numpy_bits(self.flat[i][lo:hi]) for i in range(self.P)],
+                 "mM": self.mM[p].cpu().numpy().copy(), "packed": {}, "xhat": {}, "S": {}}
+            for b in self.w.thc_bits:
+                bl, bh = lo * b // 8, (hi * b + 7) // 8
+                d["packed"][b] = [self.packed[b][i][bl:bh].cpu().numpy().copy()
+                                  for i in range(self.P)]
+                d["xhat"][b] = synth.to_numpy_bits(self.xhat[b][lo:hi])
+                d["S"][b] = self.S[b][lo:hi].cpu().numpy().copy()
+            out[p] = d
+        return out
