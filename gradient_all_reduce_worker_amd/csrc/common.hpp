@@ -58,6 +58,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
+// Streaming 16-byte accesses: the nontemporal hint keeps single-use
+// gradient data from displacing other lines in the caches (measured ~8%
+// faster than plain accesses for the multi-stream ring on MI355X).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+    const u32x4_t r = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+    return make_uint4(r.x, r.y, r.z, r.w);
+}
+__device__ __forceinline__ void store_stream(void* p, uint4 v) {
+    const u32x4_t r = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(r, static_cast<u32x4_t*>(p));
+}
+
 // 64-bit element index of the first element handled by this thread when
 // every thread of the grid handles `per_thread` consecutive elements.
 __device__ __forceinline__ int64_t thread_base(int per_thread) {

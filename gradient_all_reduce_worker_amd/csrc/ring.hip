@@ -28,8 +28,8 @@
 namespace ga {
 namespace {
 
-constexpr int kVecPerThread = 2;   // 16-byte vectors per thread per workgroup
-constexpr int kLoadBatch = 8;      // worker loads issued before their adds
+constexpr int kVecPerThread = 1;   // 16-byte vectors per thread per workgroup
+constexpr int kLoadBatch = 16;     // worker loads issued before their adds
 
 struct Div {                        // average: x / P, or x * (1/P) when exact
     int avg;
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void ring_fused_vec_kernel(PtrTable bufs,
         const uint4* src = static_cast<const uint4*>(bufs.p[r]);
 #pragma unroll
         for (int j = 0; j < kVecPerThread; j++) {
-            uint4 raw = ok[j] ? src[v[j]] : make_uint4(0, 0, 0, 0);
+            uint4 raw = ok[j] ? load_stream(src + v[j]) : make_uint4(0, 0, 0, 0);
             E::widen(raw, acc[j]);
         }
     }
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void ring_fused_vec_kernel(PtrTable bufs,
                 const uint4* src = static_cast<const uint4*>(bufs.p[w]);
 #pragma unroll
                 for (int j = 0; j < kVecPerThread; j++)
-                    raw[kk][j] = ok[j] ? src[v[j]] : make_uint4(0, 0, 0, 0);
+                    raw[kk][j] = ok[j] ? load_stream(src + v[j]) : make_uint4(0, 0, 0, 0);
             }
         }
 #pragma unroll
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void ring_fused_vec_kernel(PtrTable bufs,
         uint4* dst = static_cast<uint4*>(bufs.p[w]);
 #pragma unroll
         for (int j = 0; j < kVecPerThread; j++)
-            if (ok[j]) dst[v[j]] = out[j];
+            if (ok[j]) store_stream(dst + v[j], out[j]);
     }
 }
 

@@ -29,14 +29,15 @@ template <ga_dtype DT> struct Vec16;
 template <> struct Vec16<GA_F32> {
     static constexpr int kElems = 4;
     __device__ static __forceinline__ void load(const void* p, int64_t v, float* f) {
-        const float4 x = static_cast<const float4*>(p)[v];
-        f[0] = x.x; f[1] = x.y; f[2] = x.z; f[3] = x.w;
+        const uint4 x = load_stream(static_cast<const uint4*>(p) + v);
+        f[0] = __uint_as_float(x.x); f[1] = __uint_as_float(x.y);
+        f[2] = __uint_as_float(x.z); f[3] = __uint_as_float(x.w);
     }
 };
 template <> struct Vec16<GA_BF16> {
     static constexpr int kElems = 8;
     __device__ static __forceinline__ void load(const void* p, int64_t v, float* f) {
-        const uint4 r = static_cast<const uint4*>(p)[v];
+        const uint4 r = load_stream(static_cast<const uint4*>(p) + v);
         f[0] = bf16_lo(r.x); f[1] = bf16_hi(r.x); f[2] = bf16_lo(r.y); f[3] = bf16_hi(r.y);
         f[4] = bf16_lo(r.z); f[5] = bf16_hi(r.z); f[6] = bf16_lo(r.w); f[7] = bf16_hi(r.w);
     }
@@ -162,13 +163,13 @@ __global__ __launch_bounds__(kThreads) void minmax_kernel(PtrTable bufs, int P, 
 }
 
 // ------------------------------------------------------------------ quantize
-constexpr int kQElems = 16;   // elements per thread: two Philox calls of 8 uniforms
-
-template <int B> struct Packed;               // 16 b-bit indices
-template <> struct Packed<8> { using T = uint4; };
-template <> struct Packed<4> { using T = uint2; };
-template <> struct Packed<2> { using T = uint32_t; };
-template <> struct Packed<1> { using T = uint16_t; };
+// One Philox call serves a group of 8 consecutive elements (g = e / 8). A
+// thread takes kQGroups groups spaced one workgroup width apart, so every
+// 16-byte load and every store instruction covers a contiguous span across
+// the wave. When the partition length is a multiple of a workgroup's span
+// of elements, all its groups share one grid, loaded once (scalar loads).
+constexpr int kQGroups = 4;
+constexpr int64_t kQSpan = (int64_t)kThreads * kQGroups * 8;   // elements per workgroup
 
 struct Grid {                // one partition's grid
     float m;
@@ -191,235 +192,308 @@ __device__ __forceinline__ uint32_t usq_index(float a, Grid g, int L, uint32_t r
     return (uint32_t)z0 + (up ? 1u : 0u);
 }
 
+__device__ __forceinline__ uint32_t uniform16(const Philox4& r, int i) {
+    return (r.v[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+}
+
+template <ga_dtype DT>
+__device__ __forceinline__ void load_group(const void* x, int64_t g, float* a) {
+    if (DT == GA_BF16) {
+        const uint4 r = load_stream(static_cast<const uint4*>(x) + g);
+        a[0] = bf16_lo(r.x); a[1] = bf16_hi(r.x); a[2] = bf16_lo(r.y); a[3] = bf16_hi(r.y);
+        a[4] = bf16_lo(r.z); a[5] = bf16_hi(r.z); a[6] = bf16_lo(r.w); a[7] = bf16_hi(r.w);
+    } else {
+        const uint4 r0 = load_stream(static_cast<const uint4*>(x) + 2 * g);
+        const uint4 r1 = load_stream(static_cast<const uint4*>(x) + 2 * g + 1);
+        a[0] = __uint_as_float(r0.x); a[1] = __uint_as_float(r0.y);
+        a[2] = __uint_as_float(r0.z); a[3] = __uint_as_float(r0.w);
+        a[4] = __uint_as_float(r1.x); a[5] = __uint_as_float(r1.y);
+        a[6] = __uint_as_float(r1.z); a[7] = __uint_as_float(r1.w);
+    }
+}
+
+// The 8 b-bit indices of a group, least significant bits first (8 b bits).
+template <int B>
+__device__ __forceinline__ uint64_t pack_group(const uint32_t* z) {
+    uint64_t acc = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc |= (uint64_t)z[i] << (i * B);
+    return acc;
+}
+
+template <int B>
+__device__ __forceinline__ void store_group(uint8_t* out, int64_t g, uint64_t bits) {
+    if (B == 8) *reinterpret_cast<uint2*>(out + 8 * g) = make_uint2((uint32_t)bits, (uint32_t)(bits >> 32));
+    else if (B == 4) reinterpret_cast<uint32_t*>(out)[g] = (uint32_t)bits;
+    else if (B == 2) reinterpret_cast<uint16_t*>(out)[g] = (uint16_t)bits;
+    else out[g] = (uint8_t)bits;
+}
+
+// Fast kernel: every group of the workgroup is whole, the buffers are
+// 16-byte aligned and the workgroup lies in one partition (the host only
+// launches it over such workgroups). No bounds checks, grid loaded once.
+template <ga_dtype DT, int B>
+__global__ __launch_bounds__(kThreads) void usq_quantize_fast_kernel(PtrTable bufs, PtrTable packed,
+                                                                     int worker0, int64_t plen,
+                                                                     const float* __restrict__ mM,
+                                                                     uint32_t k0, uint32_t k1) {
+    constexpr int L = (1 << B) - 1;
+    const int slot = blockIdx.y;
+    const void* x = bufs.p[slot];
+    uint8_t* out = static_cast<uint8_t*>(packed.p[slot]);
+    const uint32_t wid = (uint32_t)(worker0 + slot);
+    const int64_t e_blk = (int64_t)blockIdx.x * kQSpan;
+    const Grid gb = grid_of(mM, e_blk / plen, L);
+    float a[kQGroups][8];
+#pragma unroll
+    for (int j = 0; j < kQGroups; j++)
+        load_group<DT>(x, e_blk / 8 + (int64_t)j * kThreads + threadIdx.x, a[j]);
+#pragma unroll
+    for (int j = 0; j < kQGroups; j++) {
+        const int64_t g = e_blk / 8 + (int64_t)j * kThreads + threadIdx.x;
+        const Philox4 r = philox4x32_10((uint32_t)g, (uint32_t)((uint64_t)g >> 32), wid, 0u, k0, k1);
+        uint32_t z[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) z[i] = usq_index(a[j][i], gb, L, uniform16(r, i));
+        store_group<B>(out, g, pack_group<B>(z));
+    }
+}
+
+// Generic kernel for the workgroups the fast one does not take (from
+// workgroup blk0 on): partial groups, misaligned buffers, partitions that
+// are not a multiple of a workgroup's span.
 template <ga_dtype DT, int B>
 __global__ __launch_bounds__(kThreads) void usq_quantize_kernel(PtrTable bufs, PtrTable packed,
                                                                 int worker0, int64_t N, int64_t plen,
                                                                 const float* __restrict__ mM,
                                                                 uint32_t k0, uint32_t k1,
-                                                                int vec_ok) {
+                                                                int vec_ok, int64_t blk0) {
     constexpr int L = (1 << B) - 1;
     const int slot = blockIdx.y;
-    const int64_t e0 = thread_base(kQElems);
-    if (e0 >= N) return;
     const void* x = bufs.p[slot];
     uint8_t* out = static_cast<uint8_t*>(packed.p[slot]);
-    const bool full = e0 + kQElems <= N;
-
-    float a[kQElems];
-    if (full && vec_ok) {
-        using V = Vec16<DT>;
-#pragma unroll
-        for (int i = 0; i < kQElems / V::kElems; i++) V::load(x, e0 / V::kElems + i, a + i * V::kElems);
-    } else {
-#pragma unroll
-        for (int i = 0; i < kQElems; i++) a[i] = (e0 + i < N) ? load_as_f32(x, e0 + i, DT) : 0.0f;
-    }
-
-    // counter (g mod 2^32, g >> 32, worker, 0) for g = e / 8
-    const uint64_t g = (uint64_t)e0 >> 3;
     const uint32_t wid = (uint32_t)(worker0 + slot);
-    const Philox4 r0 = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), wid, 0u, k0, k1);
-    const Philox4 r1 = philox4x32_10((uint32_t)(g + 1), (uint32_t)((g + 1) >> 32), wid, 0u, k0, k1);
-
-    uint32_t z[kQElems];
-    if (plen % kQElems == 0) {
-        const Grid gr = grid_of(mM, e0 / plen, L);
+    const int64_t e_blk = (blk0 + blockIdx.x) * kQSpan;
+    const int64_t n_full = N / 8;                      // groups of 8 elements
+#pragma unroll 1
+    for (int j = 0; j < kQGroups; j++) {
+        const int64_t g = e_blk / 8 + (int64_t)j * kThreads + threadIdx.x;
+        const int64_t e = g * 8;
+        if (e >= N) break;
+        const Philox4 r = philox4x32_10((uint32_t)g, (uint32_t)((uint64_t)g >> 32), wid, 0u, k0, k1);
+        uint32_t z[8];
+        if (g < n_full) {
+            float a[8];
+            if (vec_ok) {
+                load_group<DT>(x, g, a);
+            } else {
 #pragma unroll
-        for (int i = 0; i < kQElems; i++) {
-            const Philox4& r = i < 8 ? r0 : r1;
-            const int j = i & 7;
-            const uint32_t r16 = (r.v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-            z[i] = usq_index(a[i], gr, L, r16);
+                for (int i = 0; i < 8; i++) a[i] = load_as_f32(x, e + i, DT);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                z[i] = usq_index(a[i], grid_of(mM, (e + i) / plen, L), L, uniform16(r, i));
+            const uint64_t bits = pack_group<B>(z);
+            if (vec_ok) {
+                store_group<B>(out, g, bits);
+            } else {
+#pragma unroll
+                for (int i = 0; i < B; i++) out[g * B + i] = (uint8_t)(bits >> (8 * i));
+            }
+        } else {
+            // the last, partial group: elements past N - 1 get index 0
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                z[i] = e + i < N ? usq_index(load_as_f32(x, e + i, DT),
+                                             grid_of(mM, (e + i) / plen, L), L, uniform16(r, i))
+                                 : 0u;
+            const uint64_t bits = pack_group<B>(z);
+            const int64_t nbytes = (N * B + 7) / 8;
+#pragma unroll
+            for (int i = 0; i < B; i++)
+                if (g * B + i < nbytes) out[g * B + i] = (uint8_t)(bits >> (8 * i));
         }
-    } else {
-#pragma unroll
-        for (int i = 0; i < kQElems; i++) {
-            const Grid gr = grid_of(mM, min(e0 + i, N - 1) / plen, L);
-            const Philox4& r = i < 8 ? r0 : r1;
-            const int j = i & 7;
-            const uint32_t r16 = (r.v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-            z[i] = usq_index(a[i], gr, L, r16);
-        }
-    }
-    if (!full) {
-#pragma unroll
-        for (int i = 0; i < kQElems; i++)
-            if (e0 + i >= N) z[i] = 0;
-    }
-
-    // pack least significant bits first: 16 B bits = 2 B bytes
-    uint32_t words[B / 2 > 0 ? B / 2 : 1];
-    if (B == 1) {
-        uint32_t acc = 0;
-#pragma unroll
-        for (int i = 0; i < 16; i++) acc |= z[i] << i;
-        words[0] = acc;
-    } else {
-        constexpr int per_word = 32 / B;
-#pragma unroll
-        for (int q = 0; q < (B / 2 > 0 ? B / 2 : 1); q++) {
-            uint32_t acc = 0;
-#pragma unroll
-            for (int i = 0; i < per_word; i++) acc |= z[q * per_word + i] << (i * B);
-            words[q] = acc;
-        }
-    }
-    const int64_t byte0 = e0 / 8 * B;          // e0 is a multiple of 16
-    if (full && vec_ok) {
-        typename Packed<B>::T v;
-        __builtin_memcpy(&v, words, sizeof v);
-        *reinterpret_cast<typename Packed<B>::T*>(out + byte0) = v;
-    } else {
-        const int64_t nbytes = (N * B + 7) / 8;
-        const uint8_t* bytes = reinterpret_cast<const uint8_t*>(words);
-        for (int i = 0; i < 2 * B; i++)
-            if (byte0 + i < nbytes) out[byte0 + i] = bytes[i];
     }
 }
 
 // ------------------------------------------------------------------ aggregate
-// Each thread sums WB bytes of every worker. Indices are summed as pairs in
-// 16-bit lanes of 32-bit registers (at most 64 * 255 = 16320 per lane, no
-// carry between lanes): lane pair g of a word collects elements g and
-// g + 16 / B of that word.
+// A unit is 4 consecutive elements: 4 b bits of every worker in, one
+// 16-byte int4 out. A thread takes kAUnits units spaced one workgroup width
+// apart, so both the narrow per-worker loads and the 16-byte stores are
+// contiguous across the wave. b = 8 sums two elements per 32-bit register in
+// 16-bit lanes (at most 64 * 255 = 16320 per lane); smaller widths extract
+// each index with one bit-field extract.
+constexpr int kAUnits = 4;
+
+template <int B>
+__device__ __forceinline__ uint32_t unit_bits(const uint8_t* src, int64_t u) {
+    if (B == 8) return reinterpret_cast<const uint32_t*>(src)[u];
+    if (B == 4) return reinterpret_cast<const uint16_t*>(src)[u];
+    if (B == 2) return src[u];
+    return (uint32_t)(src[u >> 1] >> (4 * (u & 1))) & 0xFu;
+}
+
+template <int B>
+__device__ __forceinline__ uint32_t unit_bits_bounded(const uint8_t* src, int64_t u, int64_t nbytes) {
+    // bit offset of the unit: 4 u B; bytes past nbytes read as zero
+    const int64_t bit0 = 4 * u * B;
+    uint64_t v = 0;
+    for (int k = 0; k < (4 * B + 7) / 8 + 1; k++) {   // at most 5 bytes
+        const int64_t byte = bit0 / 8 + k;
+        if (byte < nbytes) v |= (uint64_t)src[byte] << (8 * k);
+    }
+    return (uint32_t)((v >> (bit0 & 7)) & ((1ull << (4 * B)) - 1));
+}
+
 template <int B>
 __global__ __launch_bounds__(kThreads) void int_aggregate_kernel(PtrTable packed, int P, int64_t N,
                                                                  int64_t nbytes,
                                                                  int32_t* __restrict__ sum,
                                                                  int vec_ok) {
-    constexpr int WB = B >= 4 ? 16 : (B == 2 ? 8 : 4);   // bytes per worker per thread
-    constexpr int NW = WB / 4;                           // words per worker
-    constexpr int EPW = 32 / B;                          // elements per word
-    constexpr int G = 16 / B;                            // lane pairs per word
     constexpr uint32_t LM = (1u << B) - 1u;
-    constexpr uint32_t MASK = LM | (LM << 16);
-    const int64_t byte0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * WB;
-    if (byte0 >= nbytes) return;
-    const int64_t e0 = byte0 * 8 / B;
-    const bool full = vec_ok && byte0 + WB <= nbytes;
-
-    uint32_t acc[NW][G];
+    const int64_t n_units = (N + 3) / 4;
+    const int64_t u_blk = (int64_t)blockIdx.x * kThreads * kAUnits;
+    uint32_t acc[kAUnits][4];
 #pragma unroll
-    for (int q = 0; q < NW; q++)
+    for (int j = 0; j < kAUnits; j++)
 #pragma unroll
-        for (int g = 0; g < G; g++) acc[q][g] = 0;
+        for (int i = 0; i < 4; i++) acc[j][i] = 0;
 
+    int64_t u[kAUnits];
+    bool full[kAUnits];
+#pragma unroll
+    for (int j = 0; j < kAUnits; j++) {
+        u[j] = u_blk + (int64_t)j * kThreads + threadIdx.x;
+        // every byte the unit's bits touch lies below nbytes
+        full[j] = vec_ok && (4 * (u[j] + 1) * B + 7) / 8 <= nbytes;
+    }
     constexpr int kBatch = 8;
     for (int i0 = 0; i0 < P; i0 += kBatch) {
-        uint32_t w[kBatch][NW];
+        uint32_t w[kBatch][kAUnits];
 #pragma unroll
         for (int k = 0; k < kBatch; k++) {
             if (i0 + k < P) {
-                const uint8_t* src = static_cast<const uint8_t*>(packed.p[i0 + k]) + byte0;
-                if (full) {
-                    if constexpr (NW == 4) {
-                        const uint4 t = *reinterpret_cast<const uint4*>(src);
-                        w[k][0] = t.x; w[k][1] = t.y; w[k][2] = t.z; w[k][3] = t.w;
-                    } else if constexpr (NW == 2) {
-                        const uint2 t = *reinterpret_cast<const uint2*>(src);
-                        w[k][0] = t.x; w[k][1] = t.y;
+                const uint8_t* src = static_cast<const uint8_t*>(packed.p[i0 + k]);
+#pragma unroll
+                for (int j = 0; j < kAUnits; j++)
+                    w[k][j] = u[j] < n_units ? (full[j] ? unit_bits<B>(src, u[j])
+                                                        : unit_bits_bounded<B>(src, u[j], nbytes))
+                                             : 0u;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; k++) {
+            if (i0 + k < P) {
+#pragma unroll
+                for (int j = 0; j < kAUnits; j++) {
+                    if (B == 8) {
+                        acc[j][0] += w[k][j] & 0x00FF00FFu;          // elements 0 and 2
+                        acc[j][1] += (w[k][j] >> 8) & 0x00FF00FFu;   // elements 1 and 3
                     } else {
-                        w[k][0] = *reinterpret_cast<const uint32_t*>(src);
-                    }
-                } else {
 #pragma unroll
-                    for (int q = 0; q < NW; q++) {
-                        uint32_t v = 0;
-#pragma unroll
-                        for (int c = 0; c < 4; c++)
-                            if (byte0 + q * 4 + c < nbytes) v |= (uint32_t)src[q * 4 + c] << (8 * c);
-                        w[k][q] = v;
+                        for (int i = 0; i < 4; i++) acc[j][i] += (w[k][j] >> (i * B)) & LM;
                     }
                 }
             }
         }
-#pragma unroll
-        for (int k = 0; k < kBatch; k++) {
-            if (i0 + k < P) {
-#pragma unroll
-                for (int q = 0; q < NW; q++)
-#pragma unroll
-                    for (int g = 0; g < G; g++) acc[q][g] += (w[k][q] >> (g * B)) & MASK;
-            }
-        }
     }
-
-    // element e0 + q * EPW + t: t < G in the low lane of acc[q][t], else the
-    // high lane of acc[q][t - G]
-    int32_t outv[NW * EPW];
 #pragma unroll
-    for (int q = 0; q < NW; q++)
+    for (int j = 0; j < kAUnits; j++) {
+        if (u[j] >= n_units) continue;
+        int32_t o[4];
+        if (B == 8) {
+            o[0] = (int32_t)(acc[j][0] & 0xFFFFu); o[2] = (int32_t)(acc[j][0] >> 16);
+            o[1] = (int32_t)(acc[j][1] & 0xFFFFu); o[3] = (int32_t)(acc[j][1] >> 16);
+        } else {
 #pragma unroll
-        for (int t = 0; t < EPW; t++)
-            outv[q * EPW + t] = (int32_t)(t < G ? (acc[q][t] & 0xFFFFu) : (acc[q][t - G] >> 16));
-
-    if (full && e0 + NW * EPW <= N) {
-        int4* dst = reinterpret_cast<int4*>(sum + e0);
+            for (int i = 0; i < 4; i++) o[i] = (int32_t)acc[j][i];
+        }
+        const int64_t e = 4 * u[j];
+        if (vec_ok && e + 4 <= N) {
+            store_stream(sum + e, make_uint4((uint32_t)o[0], (uint32_t)o[1], (uint32_t)o[2], (uint32_t)o[3]));
+        } else {
 #pragma unroll
-        for (int i = 0; i < NW * EPW / 4; i++)
-            dst[i] = make_int4(outv[4 * i], outv[4 * i + 1], outv[4 * i + 2], outv[4 * i + 3]);
-    } else {
-#pragma unroll
-        for (int i = 0; i < NW * EPW; i++)
-            if (e0 + i < N) sum[e0 + i] = outv[i];
+            for (int i = 0; i < 4; i++)
+                if (e + i < N) sum[e + i] = o[i];
+        }
     }
 }
 
 // ------------------------------------------------------------------ dequant
-constexpr int kDElems = 8;
+// A unit is 4 consecutive sums (one 16-byte load); a thread takes kDUnits
+// units spaced one workgroup width apart.
+constexpr int kDUnits = 4;
+constexpr int64_t kDSpan = (int64_t)kThreads * kDUnits * 4;     // elements per workgroup
 
 template <ga_dtype OUT>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const int32_t* __restrict__ S, int64_t N,
                                                            int64_t plen, const float* __restrict__ mM,
                                                            int L, int pow2, float pf, float recip,
                                                            void* out, int vec_ok) {
-    const int64_t e0 = thread_base(kDElems);
-    if (e0 >= N) return;
-    const bool full = vec_ok && e0 + kDElems <= N;
-    int32_t s[kDElems];
-    if (full) {
-        const int4 a = reinterpret_cast<const int4*>(S + e0)[0];
-        const int4 b = reinterpret_cast<const int4*>(S + e0)[1];
-        s[0] = a.x; s[1] = a.y; s[2] = a.z; s[3] = a.w;
-        s[4] = b.x; s[5] = b.y; s[6] = b.z; s[7] = b.w;
-    } else {
-#pragma unroll
-        for (int i = 0; i < kDElems; i++) s[i] = e0 + i < N ? S[e0 + i] : 0;
+    const int64_t e_blk = (int64_t)blockIdx.x * kDSpan;
+    const bool uniform = plen % kDSpan == 0;
+    float m0 = 0.0f, range0 = 0.0f, delta0 = 0.0f;
+    if (uniform) {
+        const int64_t p = e_blk / plen;
+        m0 = mM[2 * p];
+        range0 = mM[2 * p + 1] - m0;
+        delta0 = range0 / (float)L;
     }
-    float v[kDElems];
+    int32_t s[kDUnits][4];
 #pragma unroll
-    for (int i = 0; i < kDElems; i++) {
-        const int64_t p = (plen % kDElems == 0 ? e0 : min(e0 + i, N - 1)) / plen;
-        const float m = mM[2 * p], M = mM[2 * p + 1];
-        const float range = M - m;
-        const float delta = range / (float)L;
-        const float avg_index = pow2 ? (float)s[i] * recip : (float)s[i] / pf;
-        v[i] = range != 0.0f ? m + avg_index * delta : m;
-    }
-    if (OUT == GA_F32) {
-        float* o = static_cast<float*>(out);
-        if (full) {
-            reinterpret_cast<float4*>(o + e0)[0] = make_float4(v[0], v[1], v[2], v[3]);
-            reinterpret_cast<float4*>(o + e0)[1] = make_float4(v[4], v[5], v[6], v[7]);
+    for (int j = 0; j < kDUnits; j++) {
+        const int64_t e = e_blk + 4 * ((int64_t)j * kThreads + threadIdx.x);
+        if (vec_ok && e + 4 <= N) {
+            const uint4 r = load_stream(S + e);
+            s[j][0] = (int32_t)r.x; s[j][1] = (int32_t)r.y; s[j][2] = (int32_t)r.z; s[j][3] = (int32_t)r.w;
         } else {
-            for (int i = 0; i < kDElems; i++)
-                if (e0 + i < N) o[e0 + i] = v[i];
+#pragma unroll
+            for (int i = 0; i < 4; i++) s[j][i] = e + i < N ? S[e + i] : 0;
         }
-    } else {
-        uint16_t* o = static_cast<uint16_t*>(out);
-        if (full) {
-            reinterpret_cast<uint4*>(o + e0)[0] =
-                make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                           pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    }
+#pragma unroll
+    for (int j = 0; j < kDUnits; j++) {
+        const int64_t e = e_blk + 4 * ((int64_t)j * kThreads + threadIdx.x);
+        if (e >= N) break;
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            float m = m0, range = range0, delta = delta0;
+            if (!uniform) {
+                const int64_t p = min(e + i, N - 1) / plen;
+                m = mM[2 * p];
+                range = mM[2 * p + 1] - m;
+                delta = range / (float)L;
+            }
+            const float avg_index = pow2 ? (float)s[j][i] * recip : (float)s[j][i] / pf;
+            v[i] = range != 0.0f ? m + avg_index * delta : m;
+        }
+        const bool whole = vec_ok && e + 4 <= N;
+        if (OUT == GA_F32) {
+            float* o = static_cast<float*>(out);
+            if (whole) {
+                store_stream(o + e, make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                               __float_as_uint(v[2]), __float_as_uint(v[3])));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    if (e + i < N) o[e + i] = v[i];
+            }
         } else {
-            for (int i = 0; i < kDElems; i++)
-                if (e0 + i < N) o[e0 + i] = (uint16_t)f32_to_bf16_rne(v[i]);
+            uint16_t* o = static_cast<uint16_t*>(out);
+            if (whole) {
+                *reinterpret_cast<uint2*>(o + e) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    if (e + i < N) o[e + i] = (uint16_t)f32_to_bf16_rne(v[i]);
+            }
         }
     }
 }
 
 // ------------------------------------------------------------------ NMSE
-constexpr int kNmseBlocks = 1024;
+constexpr int kNmseBlocks = 2048;
 
 __device__ __forceinline__ double block_sum(double v, double* sh) {
 #pragma unroll
@@ -549,14 +623,21 @@ extern "C" ga_status thc_usq_quantize(const void* const* bufs, int32_t P, int32_
         tp.p[i] = packed[i];
         vec_ok &= aligned(bufs[i], 16) && aligned(packed[i], 16);
     }
-    const int64_t blocks = ceil_div(N, (int64_t)kThreads * kQElems);
+    const int64_t blocks = ceil_div(N, kQSpan);
     if (blocks > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: N too large", what);
-    const dim3 grid((unsigned)blocks, (unsigned)P);
+    // workgroups wholly inside N and inside one partition take the fast kernel
+    const int64_t fast = (vec_ok && plen % kQSpan == 0) ? N / kQSpan : 0;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
-#define GA_Q(DT, B)                                                                                  \
-    hipLaunchKernelGGL((usq_quantize_kernel<DT, B>), grid, dim3(kThreads), 0, hs, tx, tp, worker0, N, \
-                       plen, d_mM, k0, k1, vec_ok)
+#define GA_Q(DT, B)                                                                                   \
+    do {                                                                                              \
+        if (fast > 0)                                                                                 \
+            hipLaunchKernelGGL((usq_quantize_fast_kernel<DT, B>), dim3((unsigned)fast, (unsigned)P),   \
+                               dim3(kThreads), 0, hs, tx, tp, worker0, plen, d_mM, k0, k1);          \
+        if (blocks > fast)                                                                            \
+            hipLaunchKernelGGL((usq_quantize_kernel<DT, B>), dim3((unsigned)(blocks - fast), (unsigned)P), \
+                               dim3(kThreads), 0, hs, tx, tp, worker0, N, plen, d_mM, k0, k1, vec_ok, fast); \
+    } while (0)
     if (dt == GA_F32) {
         switch (b) {
             case 1: GA_Q(GA_F32, 1); break;
@@ -591,10 +672,9 @@ extern "C" ga_status thc_int_aggregate(const uint8_t* const* packed, int32_t P, 
     PtrTable t{};
     for (int i = 0; i < P; i++) {
         t.p[i] = const_cast<uint8_t*>(packed[i]);
-        vec_ok &= aligned(packed[i], 16);
+        vec_ok &= aligned(packed[i], 4);
     }
-    const int WB = b >= 4 ? 16 : (b == 2 ? 8 : 4);
-    const int64_t blocks = ceil_div(nbytes, (int64_t)kThreads * WB);
+    const int64_t blocks = ceil_div(ceil_div(N, 4), (int64_t)kThreads * kAUnits);
     if (blocks > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: N too large", what);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)blocks);
@@ -621,7 +701,7 @@ extern "C" ga_status thc_dequant(const int32_t* d_sum, int64_t N, int32_t P, int
         return fail(GA_EINVAL, "%s: null or misaligned pointer", what);
     const int64_t plen = part_elems > 0 ? part_elems : N;
     const int vec_ok = aligned(d_sum, 16) && aligned(out, 16);
-    const int64_t blocks = ceil_div(N, (int64_t)kThreads * kDElems);
+    const int64_t blocks = ceil_div(N, kDSpan);
     if (blocks > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: N too large", what);
     const int L = (1 << b) - 1;
     const int pow2 = (P & (P - 1)) == 0;

@@ -56,6 +56,25 @@ def _call(timer: Optional[StageTimer], name: str, fn, *a, **k):
     return timer.wrap(name, fn, *a, **k)
 
 
+# Worker buffers whose byte size is a multiple of 64 KiB would start at the
+# same offset modulo the HBM channel-interleave period, so the P concurrent
+# streams of the ring (same element of every worker) fall on the same
+# channels. Such buffers are carved from one allocation with a 12 KiB skew
+# between workers (measured on MI355X: 8 x 4 GiB ring 70.6% -> 74.6% of
+# peak); other sizes keep one allocation per worker, which measured best.
+SKEW_BYTES = 12 << 10
+
+
+def worker_buffers(P: int, N: int, dtype, device) -> List[torch.Tensor]:
+    es = torch.empty((), dtype=dtype).element_size()
+    nbytes = N * es
+    if P > 1 and nbytes % (64 << 10) == 0:
+        stride = (nbytes + SKEW_BYTES) // es
+        slab = torch.empty(stride * P, dtype=dtype, device=device)
+        return [slab[i * stride: i * stride + N] for i in range(P)]
+    return [torch.empty(N, dtype=dtype, device=device) for _ in range(P)]
+
+
 class Pipeline:
     def __init__(self, name: str, device="cuda", cap_bytes: int = 64 << 20):
         self.w = synth.workload(name)
@@ -87,7 +106,7 @@ class Pipeline:
                                           self.bufs, [self.buf_of[t] for t in keep],
                                           [self.off_of[t] for t in keep]) if keep else None
         else:
-            self.flat = [torch.empty(self.N, dtype=self.tdt, device=dev) for _ in range(self.P)]
+            self.flat = worker_buffers(self.P, self.N, self.tdt, dev)
             for i in range(self.P):
                 synth.worker_flat(w, i, self.flat[i])
             n_part = ga.n_partitions(self.N, w.part_elems)
