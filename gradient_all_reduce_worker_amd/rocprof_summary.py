@@ -11,6 +11,11 @@
       run (DIR1) and a WRITE_SIZE run (DIR2). Each counter is scaled by what
       it reads for the probe kernel (a plain copy that reads B bytes and
       writes B bytes), so the result is in bytes whatever the counter's unit.
+
+  python -m gradient_all_reduce_worker_amd.rocprof_summary pmc-table \
+      --fetch DIR1 --write DIR2 --probe REGEX --probe-bytes B --cmd "..." \
+      NAME=REGEX=ALG_BYTES ...
+      The same scaling for several kernels, as a markdown table.
 """
 import argparse
 import csv
@@ -110,6 +115,32 @@ def cmd_pmc(a):
     print()
 
 
+def cmd_pmc_table(a):
+    """Markdown table: per kernel, scaled fetch/write bytes per launch against
+    the algorithmic bytes given as NAME=REGEX=BYTES triples."""
+    fetch = _per_kernel(a.fetch, "FETCH_SIZE")
+    write = _per_kernel(a.write, "WRITE_SIZE")
+    pre = re.compile(a.probe)
+    pf = max(x for k, v in fetch.items() if pre.search(k) for x in v)
+    pw = max(x for k, v in write.items() if pre.search(k) for x in v)
+    print(f"# HBM traffic per launch from rocprofv3 PMC counters: {a.title}\n")
+    print("FETCH_SIZE and WRITE_SIZE were collected in two separate runs and scaled by what")
+    print(f"each reads for a plain copy of {a.probe_bytes:.0f} bytes each way (`{a.probe}`:")
+    print(f"FETCH_SIZE {pf:.2f}, WRITE_SIZE {pw:.2f}).\n")
+    print(f"Commands (run from the repository root on one MI355X):\n\n    {a.cmd}\n")
+    print("| kernel | launches | read GB | written GB | algorithmic GB | traffic / algorithmic |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for spec in a.kernels:
+        name, rx, alg = spec.split("=")
+        r = re.compile(rx)
+        kf = [x for k, v in fetch.items() if r.search(k) for x in v]
+        kw = [x for k, v in write.items() if r.search(k) for x in v]
+        fb = statistics.mean(kf) * a.probe_bytes / pf
+        wb = statistics.mean(kw) * a.probe_bytes / pw
+        print(f"| `{name}` | {len(kf)} | {fb / 1e9:.3f} | {wb / 1e9:.3f} | {float(alg) / 1e9:.3f} | "
+              f"{(fb + wb) / float(alg):.4f} |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -127,8 +158,16 @@ def main():
     p.add_argument("--workload", required=True)
     p.add_argument("--src", required=True)
     p.add_argument("--cmd", required=True)
+    t = sub.add_parser("pmc-table")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--probe", required=True)
+    t.add_argument("--probe-bytes", type=float, required=True)
+    t.add_argument("--title", default="")
+    t.add_argument("--cmd", required=True)
+    t.add_argument("kernels", nargs="+", help="NAME=REGEX=ALG_BYTES")
     a = ap.parse_args()
-    cmd_stats(a) if a.mode == "stats" else cmd_pmc(a)
+    {"stats": cmd_stats, "pmc": cmd_pmc, "pmc-table": cmd_pmc_table}[a.mode](a)
 
 
 if __name__ == "__main__":
