@@ -28,8 +28,7 @@
 namespace ga {
 namespace {
 
-constexpr int kVecPerThread = 1;   // 16-byte vectors per thread per workgroup
-constexpr int kLoadBatch = 16;     // worker loads issued before their adds
+constexpr int kVecPerThread = 1;   // 16-byte vectors per thread (stepwise kernels)
 
 struct Div {                        // average: x / P, or x * (1/P) when exact
     int avg;
@@ -84,6 +83,13 @@ struct Where {
 };
 
 __device__ __forceinline__ Where locate(int64_t e, int64_t N, int64_t plen, int P) {
+    if (N < 0xFFFFFF00ll) {            // 32-bit index arithmetic is exact here
+        const uint32_t ue = (uint32_t)e, un = (uint32_t)N, ul = (uint32_t)plen;
+        const uint32_t p = ue / ul, p0 = p * ul;
+        const uint32_t n = un - p0 < ul ? un - p0 : ul;
+        const uint32_t C = (n + (uint32_t)P - 1u) / (uint32_t)P;
+        return {(int64_t)p, (int)((ue - p0) / C)};
+    }
     int64_t p = e / plen;
     int64_t p0 = p * plen;
     int64_t n = N - p0 < plen ? N - p0 : plen;
@@ -108,60 +114,97 @@ __device__ __forceinline__ void fold_one(const PtrTable& bufs, int P, int64_t N,
     for (int i = 0; i < P; i++) E::store1(bufs.p[i], e, acc);
 }
 
+// One 16-byte vector v whose elements all start their fold at worker r
+// (lane-varying r: pointers are read per lane).
 template <ga_dtype DT>
+__device__ __forceinline__ void fold_vec(const PtrTable& bufs, int P, int64_t v, int r, Div div) {
+    using E = Elem<DT>;
+    constexpr int V = E::kVec;
+    float acc[V];
+    E::widen(load_stream(static_cast<const uint4*>(bufs.p[r]) + v), acc);
+    int w = r;
+    for (int k = 1; k < P; k++) {
+        w = (w + 1 == P) ? 0 : w + 1;
+        float t[V];
+        E::widen(load_stream(static_cast<const uint4*>(bufs.p[w]) + v), t);
+#pragma unroll
+        for (int i = 0; i < V; i++) acc[i] = acc[i] + t[i];
+    }
+    if (div.avg) {
+#pragma unroll
+        for (int i = 0; i < V; i++) acc[i] = div.apply(acc[i]);
+    }
+    const uint4 o = E::narrow(acc);
+    for (int i = 0; i < P; i++) store_stream(static_cast<uint4*>(bufs.p[i]) + v, o);
+}
+
+// VPT 16-byte vectors per thread and BATCH worker loads in flight: one vector
+// and 16 loads for P <= 8, two vectors and 8 loads for larger P (measured).
+template <ga_dtype DT, int VPT, int BATCH>
 __global__ __launch_bounds__(kThreads) void ring_fused_vec_kernel(PtrTable bufs, int P, int64_t N,
                                                                   int64_t plen, int64_t n_vec,
                                                                   Div div) {
     using E = Elem<DT>;
     constexpr int V = E::kVec;
-    const int64_t vb0 = (int64_t)blockIdx.x * (kThreads * kVecPerThread);
-    const int64_t vb1 = min(vb0 + (int64_t)(kThreads * kVecPerThread), n_vec);
+    const int64_t vb0 = (int64_t)blockIdx.x * (kThreads * VPT);
+    const int64_t vb1 = min(vb0 + (int64_t)(kThreads * VPT), n_vec);
     const Where first = locate(vb0 * V, N, plen, P);
     const Where last = locate(vb1 * V - 1, N, plen, P);
 
     if (first.part != last.part || first.chunk != last.chunk) {
-        // straddles a chunk or partition boundary: one element at a time
-        for (int64_t e = vb0 * V + threadIdx.x; e < vb1 * V; e += kThreads)
-            fold_one<DT>(bufs, P, N, plen, e, div);
+        // straddles a chunk or partition boundary: every thread folds its own
+        // vectors with their own rotation; only a vector that itself crosses
+        // a boundary goes element by element
+        for (int j = 0; j < VPT; j++) {
+            const int64_t v = vb0 + threadIdx.x + (int64_t)j * kThreads;
+            if (v >= vb1) continue;
+            const Where a = locate(v * V, N, plen, P);
+            const Where b = locate(v * V + V - 1, N, plen, P);
+            if (a.part == b.part && a.chunk == b.chunk) {
+                fold_vec<DT>(bufs, P, v, a.chunk, div);
+            } else {
+                for (int i = 0; i < V; i++) fold_one<DT>(bufs, P, N, plen, v * V + i, div);
+            }
+        }
         return;
     }
 
     const int r = first.chunk;  // every element of this workgroup starts its fold at worker r
-    int64_t v[kVecPerThread];
-    bool ok[kVecPerThread];
+    int64_t v[VPT];
+    bool ok[VPT];
 #pragma unroll
-    for (int j = 0; j < kVecPerThread; j++) {
+    for (int j = 0; j < VPT; j++) {
         v[j] = vb0 + threadIdx.x + (int64_t)j * kThreads;
         ok[j] = v[j] < vb1;
     }
 
-    float acc[kVecPerThread][V];
+    float acc[VPT][V];
     {
         const uint4* src = static_cast<const uint4*>(bufs.p[r]);
 #pragma unroll
-        for (int j = 0; j < kVecPerThread; j++) {
+        for (int j = 0; j < VPT; j++) {
             uint4 raw = ok[j] ? load_stream(src + v[j]) : make_uint4(0, 0, 0, 0);
             E::widen(raw, acc[j]);
         }
     }
-    for (int k = 1; k < P; k += kLoadBatch) {
-        uint4 raw[kLoadBatch][kVecPerThread];
+    for (int k = 1; k < P; k += BATCH) {
+        uint4 raw[BATCH][VPT];
 #pragma unroll
-        for (int kk = 0; kk < kLoadBatch; kk++) {
+        for (int kk = 0; kk < BATCH; kk++) {
             if (k + kk < P) {
                 int w = r + k + kk;
                 if (w >= P) w -= P;
                 const uint4* src = static_cast<const uint4*>(bufs.p[w]);
 #pragma unroll
-                for (int j = 0; j < kVecPerThread; j++)
+                for (int j = 0; j < VPT; j++)
                     raw[kk][j] = ok[j] ? load_stream(src + v[j]) : make_uint4(0, 0, 0, 0);
             }
         }
 #pragma unroll
-        for (int kk = 0; kk < kLoadBatch; kk++) {
+        for (int kk = 0; kk < BATCH; kk++) {
             if (k + kk < P) {
 #pragma unroll
-                for (int j = 0; j < kVecPerThread; j++) {
+                for (int j = 0; j < VPT; j++) {
                     float t[V];
                     E::widen(raw[kk][j], t);
 #pragma unroll
@@ -170,9 +213,9 @@ __global__ __launch_bounds__(kThreads) void ring_fused_vec_kernel(PtrTable bufs,
             }
         }
     }
-    uint4 out[kVecPerThread];
+    uint4 out[VPT];
 #pragma unroll
-    for (int j = 0; j < kVecPerThread; j++) {
+    for (int j = 0; j < VPT; j++) {
         if (div.avg) {
 #pragma unroll
             for (int i = 0; i < V; i++) acc[j][i] = div.apply(acc[j][i]);
@@ -182,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void ring_fused_vec_kernel(PtrTable bufs,
     for (int w = 0; w < P; w++) {
         uint4* dst = static_cast<uint4*>(bufs.p[w]);
 #pragma unroll
-        for (int j = 0; j < kVecPerThread; j++)
+        for (int j = 0; j < VPT; j++)
             if (ok[j]) store_stream(dst + v[j], out[j]);
     }
 }
@@ -355,11 +398,19 @@ extern "C" ga_status ga_ring_allreduce_sim(void* const* bufs, int32_t P, int64_t
             if (vec_ok && n_vec > 0) {
                 PtrTable t{};
                 for (int i = 0; i < P; i++) t.p[i] = bufs[i];
-                if (dt == GA_F32)
-                    hipLaunchKernelGGL(ring_fused_vec_kernel<GA_F32>, dim3((unsigned)vblocks),
+                const bool wide = P > 8;
+                const unsigned blocks = (unsigned)ceil_div(n_vec, (int64_t)kThreads * (wide ? 2 : 1));
+                if (dt == GA_F32 && wide)
+                    hipLaunchKernelGGL((ring_fused_vec_kernel<GA_F32, 2, 8>), dim3(blocks),
+                                       dim3(kThreads), 0, hs, t, P, N, plen, n_vec, div);
+                else if (dt == GA_F32)
+                    hipLaunchKernelGGL((ring_fused_vec_kernel<GA_F32, 1, 16>), dim3(blocks),
+                                       dim3(kThreads), 0, hs, t, P, N, plen, n_vec, div);
+                else if (wide)
+                    hipLaunchKernelGGL((ring_fused_vec_kernel<GA_BF16, 2, 8>), dim3(blocks),
                                        dim3(kThreads), 0, hs, t, P, N, plen, n_vec, div);
                 else
-                    hipLaunchKernelGGL(ring_fused_vec_kernel<GA_BF16>, dim3((unsigned)vblocks),
+                    hipLaunchKernelGGL((ring_fused_vec_kernel<GA_BF16, 1, 16>), dim3(blocks),
                                        dim3(kThreads), 0, hs, t, P, N, plen, n_vec, div);
                 launches++;
                 if ((rc = check_launch(what))) return rc;
