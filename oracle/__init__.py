@@ -55,6 +55,9 @@ def lib():
         L.orc_int_aggregate.argtypes = [C.POINTER(vp), i32, i64, i32, vp]
         L.orc_dequant.argtypes = [vp, i64, i32, i32, i64, vp, vp, i32]
         L.orc_nmse.argtypes = [vp, vp, i64, i32, vp]
+        L.orc_nuhc_quantize.argtypes = [vp, i64, i32, i32, i64, vp, i32, i32, vp, C.c_uint64, i64, vp]
+        L.orc_nuhc_aggregate.argtypes = [C.POINTER(vp), i32, i64, i32, i32, vp, vp]
+        L.orc_nuhc_dequant.argtypes = [vp, i64, i32, i32, i64, vp, vp, i32]
         L.orc_f32_to_bf16.argtypes = [vp, i64, vp]
         L.orc_f32_to_bf16.restype = None
         L.orc_bf16_to_f32.argtypes = [vp, i64, vp]
@@ -190,3 +193,40 @@ def nmse(x: np.ndarray, xhat: np.ndarray):
     _check(lib().orc_nmse(x.ctypes.data, xhat.ctypes.data, x.size, _dt(x), out.ctypes.data),
            "nmse")
     return float(out[0]), float(out[1]), float(out[2])
+
+
+# ---------------------------------------------------------------- non-uniform THC
+def _table(T):
+    return np.ascontiguousarray(T, dtype=np.int32)
+
+
+def nuhc_quantize(x: np.ndarray, worker: int, part: int, mM: np.ndarray, b: int, g: int, T,
+                  seed: int, e_offset: int = 0) -> np.ndarray:
+    N = x.size
+    out = np.zeros((N * b + 7) // 8, dtype=np.uint8)
+    mM = np.ascontiguousarray(mM, dtype=np.float32)
+    x = np.ascontiguousarray(x)
+    T = _table(T)
+    _check(lib().orc_nuhc_quantize(x.ctypes.data, N, _dt(x), worker, part, mM.ctypes.data, b, g,
+                                   T.ctypes.data, seed, e_offset, out.ctypes.data), "nuhc_quantize")
+    return out
+
+
+def nuhc_aggregate(packed_list, N: int, b: int, g: int, T) -> np.ndarray:
+    Y = np.zeros(N, dtype=np.int32)
+    packed_list = [np.ascontiguousarray(p, dtype=np.uint8) for p in packed_list]
+    T = _table(T)
+    _check(lib().orc_nuhc_aggregate(_ptrs(packed_list), len(packed_list), N, b, g, T.ctypes.data,
+                                    Y.ctypes.data), "nuhc_aggregate")
+    return Y
+
+
+def nuhc_dequant(Y: np.ndarray, P: int, g: int, part: int, mM: np.ndarray, out_dt: int = F32
+                 ) -> np.ndarray:
+    N = Y.size
+    Y = np.ascontiguousarray(Y, dtype=np.int32)
+    mM = np.ascontiguousarray(mM, dtype=np.float32)
+    out = np.zeros(N, dtype=np.float32 if out_dt == F32 else np.uint16)
+    _check(lib().orc_nuhc_dequant(Y.ctypes.data, N, P, g, part, mM.ctypes.data, out.ctypes.data,
+                                  out_dt), "nuhc_dequant")
+    return out

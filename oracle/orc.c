@@ -459,12 +459,9 @@ int orc_int_aggregate(const uint8_t *const *packed, int P, int64_t N, int b, int
  * all binary32; range == 0 gives xhat = m. out_dt = bf16 rounds the final
  * value to nearest-even.
  */
-int orc_dequant(const int32_t *S, int64_t N, int P, int b, int64_t part, const float *mM, void *out,
-                int out_dt)
+static int dequant_levels(const int32_t *S, int64_t N, int P, int L, int64_t part, const float *mM,
+                          void *out, int out_dt)
 {
-    if (!(b == 1 || b == 2 || b == 4 || b == 8) || P < 1)
-        return -1;
-    const int L = (1 << b) - 1;
     int64_t plen = part_len(N, part);
     int64_t p = 0;
     for (int64_t p0 = 0; p0 < N; p0 += plen, p++) {
@@ -482,6 +479,115 @@ int orc_dequant(const int32_t *S, int64_t N, int P, int b, int64_t part, const f
         }
     }
     return 0;
+}
+
+int orc_dequant(const int32_t *S, int64_t N, int P, int b, int64_t part, const float *mM, void *out,
+                int out_dt)
+{
+    if (!(b == 1 || b == 2 || b == 4 || b == 8) || P < 1)
+        return -1;
+    return dequant_levels(S, N, P, (1 << b) - 1, part, mM, out, out_dt);
+}
+
+/* ------------------------------------------------------------------ */
+/* Non-uniform THC (lookup table)                                      */
+/* ------------------------------------------------------------------ */
+
+/*
+ * [THC] section 4, Algorithm 2. A table T maps the 2^b indices a worker may
+ * send into the larger integer range <g+1> = {0, ..., g}, with
+ * 0 = T[0] < T[1] < ... < T[2^b - 1] = g (granularity g >= 2^b - 1). Index z
+ * stands for the value m + T[z] (M - m) / g. Reading: the page's prose
+ * writes (M - m)/(g + 1) but its own worked example (T2 = {0, 1, 3, 4},
+ * g = 4 on [-1, 1], T2[1] -> -1/2) divides by g; this build divides by g.
+ *
+ * A worker rounds each coordinate stochastically to one of the two
+ * neighbouring table values (unbiased), binary32 throughout:
+ *   range = M - m (0: every index 0);  s = g / range;  u = (a - m) s;
+ *   k = min(floor(u), g - 1);  z0 = the largest z with T[z] <= k
+ *   (at most 2^b - 2, since T[2^b - 1] = g > k);  lo = T[z0], hi = T[z0 + 1];
+ *   f = (u - lo) / (hi - lo);  up = (2 r + 1) < f 2^17;  z = z0 + up,
+ * with the same 16-bit uniforms and packing as the uniform quantizer. With
+ * g = 2^b - 1 and T the identity this is exactly orc_usq_quantize.
+ */
+static int table_ok(int b, int g, const int32_t *T)
+{
+    int n = 1 << b;
+    if (!(b == 1 || b == 2 || b == 4 || b == 8) || g < n - 1 || T[0] != 0 || T[n - 1] != g)
+        return 0;
+    for (int z = 1; z < n; z++)
+        if (T[z] <= T[z - 1])
+            return 0;
+    return 1;
+}
+
+int orc_nuhc_quantize(const void *x, int64_t N, int dt, int worker, int64_t part, const float *mM,
+                      int b, int g, const int32_t *T, uint64_t seed, int64_t e_offset,
+                      uint8_t *packed)
+{
+    if (!table_ok(b, g, T) || N < 0)
+        return -1;
+    const int n = 1 << b;
+    int64_t nbytes = (N * b + 7) / 8;
+    memset(packed, 0, (size_t)nbytes);
+    int64_t plen = part_len(N, part);
+    int64_t p = 0;
+    for (int64_t p0 = 0; p0 < N; p0 += plen, p++) {
+        int64_t len = (N - p0 < plen) ? N - p0 : plen;
+        float m = mM[2 * p], M = mM[2 * p + 1];
+        float range = M - m;
+        float s = (range == 0.0f) ? 0.0f : (float)g / range;
+        for (int64_t e = p0; e < p0 + len; e++) {
+            uint32_t z = 0;
+            if (range != 0.0f) {
+                float a = load_elem(x, dt, e);
+                float u = (a - m) * s;
+                float k = floorf(u);
+                if (k > (float)(g - 1))
+                    k = (float)(g - 1);
+                int z0 = 0;
+                for (int t = 1; t < n; t++)
+                    if ((float)T[t] <= k)
+                        z0 = t;
+                float lo = (float)T[z0], hi = (float)T[z0 + 1];
+                float f = (u - lo) / (hi - lo);
+                uint32_t r = uniform16(seed, worker, e_offset + e);
+                int up = (float)(2u * r + 1u) < f * 131072.0f;
+                z = (uint32_t)z0 + (uint32_t)up;
+            }
+            int64_t bit = e * b;
+            packed[bit >> 3] |= (uint8_t)(z << (bit & 7));
+        }
+    }
+    return 0;
+}
+
+/* [THC] section 4, Algorithm 2 (server): look every index up in T and add:
+ * Y[e] = sum_i T[z_i[e]] (int32, at most P g). */
+int orc_nuhc_aggregate(const uint8_t *const *packed, int P, int64_t N, int b, int g,
+                       const int32_t *T, int32_t *Y)
+{
+    if (!table_ok(b, g, T) || P < 1)
+        return -1;
+    const int L = (1 << b) - 1;
+    for (int64_t e = 0; e < N; e++) {
+        int64_t bit = e * b;
+        int32_t acc = 0;
+        for (int i = 0; i < P; i++)
+            acc += T[(packed[i][bit >> 3] >> (bit & 7)) & L];
+        Y[e] = acc;
+    }
+    return 0;
+}
+
+/* [THC] section 4, Algorithm 2 (worker, last two steps): divide Y by n and
+ * map back: xhat = m + ((float)Y / P) (range / g), binary32. */
+int orc_nuhc_dequant(const int32_t *Y, int64_t N, int P, int g, int64_t part, const float *mM,
+                     void *out, int out_dt)
+{
+    if (g < 1 || P < 1)
+        return -1;
+    return dequant_levels(Y, N, P, g, part, mM, out, out_dt);
 }
 
 /*
