@@ -36,7 +36,8 @@ DESCRIPTIONS = {
     "small": "4 workers x 1,048,576 fp32 N(0,0.01^2); ring avg + THC USQ b=4",
     "fusion": "8 workers x 200 fp32 tensors (log-uniform 1K..256K); 64 MiB fusion, ring avg",
     "resnet101": "16 workers x ResNet-101 gradients (314 tensors, 44,549,160 fp32); fusion + ring avg",
-    "vgg16": "32 workers x VGG-16 gradients (138,357,544 fp32); THC USQ b=4,8 + ring avg + NMSE",
+    "vgg16": ("32 workers x VGG-16 gradients (138,357,544 fp32); THC USQ b=4,8 and table THC "
+              "b=4 g=36 + ring avg + NMSE"),
     "shard": ("8 workers x 2,147,483,648 bf16 Laplace(0,1e-3); ring avg with fp32 accumulation "
               "in 2^20-element partitions + THC USQ b=2 (uint8-packed), int32 sum, dequant, NMSE"),
 }
@@ -177,7 +178,7 @@ def main():
                      "alg_bytes": nbytes[k], "GB/s": round(gbs, 1),
                      "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
     quant = {k: round(P * N / (v * 1e-3) / 1e9, 2) for k, v in stage_ms.items()
-             if k.startswith("thc_usq_quantize")}
+             if k.startswith(("thc_usq_quantize", "thc_nuhc_quantize"))}
 
     ring_ms = stage_ms["ring_allreduce"]
     achieved = nbytes["ring_allreduce"] / (ring_ms * 1e-3) / 1e9
@@ -197,7 +198,7 @@ def main():
                    "parallelism": "1 GPU, P simulated workers"},
         "roofline": roofline,
         "thc_quantize_gelem_s": quant,
-        "nmse": {f"b{b}": v[2] for b, v in nmse.items()},
+        "nmse": {(f"b{b}" if isinstance(b, int) else b): v[2] for b, v in nmse.items()},
         "stages": stages,
     }
     if samples is not None:

@@ -13,5 +13,6 @@ from ._native import (  # noqa: F401
     CopyDesc, FusionTables, GAError, RingStats, build_copy_table, ga_fuse_desc_check,
     ga_fuse_pack, ga_fuse_plan, ga_fuse_unpack, ga_ring_allreduce_sim, load, n_partitions,
     packed_bytes, thc_dequant, thc_int_aggregate, thc_minmax, thc_nmse, thc_nmse_ws_bytes,
-    thc_usq_quantize, upload_table,
+    thc_usq_quantize, upload_table, thc_nuhc_quantize, thc_nuhc_aggregate, thc_nuhc_dequant,
+    center_table,
 )

@@ -25,6 +25,7 @@ EXPORTS = (
     "ga_fuse_plan", "ga_fuse_desc_check", "ga_fuse_pack", "ga_fuse_unpack",
     "ga_ring_allreduce_sim", "thc_minmax", "thc_usq_quantize", "thc_int_aggregate",
     "thc_dequant", "thc_nmse", "thc_nmse_ws_bytes", "ga_last_error",
+    "thc_nuhc_quantize", "thc_nuhc_aggregate", "thc_nuhc_dequant",
 )
 
 
@@ -73,6 +74,10 @@ def load() -> C.CDLL:
     L.thc_nmse.argtypes = [vp, vp, i64, i32, vp, vp, C.c_size_t, vp]
     L.thc_nmse_ws_bytes.argtypes = [i64]
     L.thc_nmse_ws_bytes.restype = C.c_size_t
+    L.thc_nuhc_quantize.argtypes = [C.POINTER(vp), i32, i32, i64, i32, i64, vp, i32, i32,
+                                    C.POINTER(i32), u64, C.POINTER(vp), vp]
+    L.thc_nuhc_aggregate.argtypes = [C.POINTER(vp), i32, i64, i32, i32, C.POINTER(i32), vp, vp]
+    L.thc_nuhc_dequant.argtypes = [vp, i64, i32, i32, i64, vp, vp, i32, vp]
     L.ga_last_error.argtypes = []
     L.ga_last_error.restype = C.c_char_p
     for name in EXPORTS:
@@ -288,3 +293,63 @@ def thc_nmse(x: torch.Tensor, xhat: torch.Tensor, out: Optional[torch.Tensor] = 
     _check(load().thc_nmse(_dev(x, "x"), _dev(xhat, "xhat"), N, _dt(x), _dev(out, "out"),
                            _dev(ws, "ws"), ws.numel(), _stream(stream)))
     return out
+
+
+# ------------------------------------------------------------------ non-uniform THC
+def _table_arg(T):
+    return (C.c_int32 * len(T))(*[int(v) for v in T])
+
+
+def thc_nuhc_quantize(bufs: Sequence[torch.Tensor], mM: torch.Tensor, b: int, g: int, table,
+                      seed: int, part_elems: int = 0, worker0: int = 0,
+                      packed: Optional[Sequence[torch.Tensor]] = None, stream=None):
+    N = bufs[0].numel()
+    if packed is None:
+        packed = [torch.empty(packed_bytes(N, b), dtype=torch.uint8, device=bufs[0].device)
+                  for _ in bufs]
+    _check(load().thc_nuhc_quantize(_ptr_array(bufs, "buffer"), len(bufs), worker0, N,
+                                    _dt(bufs[0]), part_elems, _dev(mM, "mM"), b, g, _table_arg(table),
+                                    seed, _ptr_array(packed, "packed"), _stream(stream)))
+    return packed
+
+
+def thc_nuhc_aggregate(packed: Sequence[torch.Tensor], N: int, b: int, g: int, table,
+                       out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty(max(N, 1), dtype=torch.int32, device=packed[0].device)
+    _check(load().thc_nuhc_aggregate(_ptr_array(packed, "packed"), len(packed), N, b, g,
+                                     _table_arg(table), _dev(out, "sum"), _stream(stream)))
+    return out
+
+
+def thc_nuhc_dequant(S: torch.Tensor, N: int, P: int, g: int, mM: torch.Tensor, part_elems: int = 0,
+                     out_dtype=torch.float32, out: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty(max(N, 1), dtype=out_dtype, device=S.device)
+    _check(load().thc_nuhc_dequant(_dev(S, "sum"), N, P, g, part_elems, _dev(mM, "mM"),
+                                   _dev(out, "out"), _dt(out), _stream(stream)))
+    return out
+
+
+def center_table(b: int, g: int, power: float = 2.0):
+    """A heuristic non-uniform table: 2^b strictly increasing integers from 0
+    to g, denser near the middle of the range (where bell-shaped gradients
+    concentrate): T[z] ~ g (1 + sign(t) |t|^power) / 2 with t = 2z/(2^b-1) - 1,
+    then forced strictly increasing. The optimal tables of the THC page come
+    from an offline integer program that is not reproduced here."""
+    n = 1 << b
+    if g < n - 1:
+        raise ValueError("granularity below 2^b - 1")
+    T = []
+    for z in range(n):
+        t = 2.0 * z / (n - 1) - 1.0
+        v = g * (1.0 + (1 if t >= 0 else -1) * abs(t) ** power) / 2.0
+        T.append(int(round(v)))
+    T[0] = 0
+    for z in range(1, n - 1):                   # strictly increasing from the left
+        T[z] = max(T[z], T[z - 1] + 1)
+    T[-1] = g
+    for z in range(n - 2, 0, -1):               # and fitting under g from the right
+        T[z] = min(T[z], T[z + 1] - 1)
+    return T

@@ -229,21 +229,70 @@ __device__ __forceinline__ void store_group(uint8_t* out, int64_t g, uint64_t bi
     else out[g] = (uint8_t)bits;
 }
 
+// Rounding rules. Uniform THC: index k stands for m + k (M - m) / L. Non-
+// uniform THC ("THC" page, section 4, Algorithm 2): index z stands for the
+// table value T[z] on the finer grid m + t (M - m) / g, and a coordinate is
+// rounded stochastically to one of its two neighbouring table values. A
+// per-workgroup LDS map cell[k] = (z0, T[z0], T[z0 + 1]) for every integer
+// cell k in [0, g) gives the neighbours of a position u in [k, k + 1).
+constexpr int kMaxGranularity = 4095;
+
+struct TableArg {
+    uint16_t t[256];   // T[0 .. n-1], 0 = T[0] < ... < T[n-1] = g
+    int g;
+    int n;             // 2^b
+};
+
+template <bool TABLE>
+struct Rounder {
+    int levels;              // L for the uniform grid, g for a table
+    const uint32_t* cell;    // LDS cells (table only)
+    __device__ __forceinline__ uint32_t index(float a, Grid gr, uint32_t r16) const {
+        if (!TABLE) return usq_index(a, gr, levels, r16);
+        const float u = (a - gr.m) * gr.s;                      // position on <g+1>
+        const float k = fminf(floorf(u), (float)(levels - 1));
+        const uint32_t c = cell[(int)k];
+        const float lo = (float)((c >> 8) & 0xFFFu), hi = (float)(c >> 20);
+        const float f = (u - lo) / (hi - lo);
+        const bool up = (float)(2u * r16 + 1u) < f * 131072.0f;
+        return (c & 0xFFu) + (up ? 1u : 0u);
+    }
+};
+
+// Called by every thread of the workgroup before any early exit.
+template <bool TABLE>
+__device__ __forceinline__ Rounder<TABLE> make_rounder(const TableArg& tab, int L, uint32_t* cells) {
+    if (!TABLE) return {L, nullptr};
+    for (int k = threadIdx.x; k < tab.g; k += kThreads) {
+        int lo = 0, hi = tab.n - 1;             // the largest z with T[z] <= k
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (tab.t[mid] <= k) lo = mid; else hi = mid - 1;
+        }
+        cells[k] = (uint32_t)lo | ((uint32_t)tab.t[lo] << 8) | ((uint32_t)tab.t[lo + 1] << 20);
+    }
+    __syncthreads();
+    return {tab.g, cells};
+}
+
 // Fast kernel: every group of the workgroup is whole, the buffers are
 // 16-byte aligned and the workgroup lies in one partition (the host only
 // launches it over such workgroups). No bounds checks, grid loaded once.
-template <ga_dtype DT, int B>
+template <ga_dtype DT, int B, bool TABLE>
 __global__ __launch_bounds__(kThreads) void usq_quantize_fast_kernel(PtrTable bufs, PtrTable packed,
                                                                      int worker0, int64_t plen,
                                                                      const float* __restrict__ mM,
-                                                                     uint32_t k0, uint32_t k1) {
+                                                                     uint32_t k0, uint32_t k1,
+                                                                     TableArg tab) {
     constexpr int L = (1 << B) - 1;
+    __shared__ uint32_t cells[TABLE ? kMaxGranularity : 1];
+    const Rounder<TABLE> rd = make_rounder<TABLE>(tab, L, cells);
     const int slot = blockIdx.y;
     const void* x = bufs.p[slot];
     uint8_t* out = static_cast<uint8_t*>(packed.p[slot]);
     const uint32_t wid = (uint32_t)(worker0 + slot);
     const int64_t e_blk = (int64_t)blockIdx.x * kQSpan;
-    const Grid gb = grid_of(mM, e_blk / plen, L);
+    const Grid gb = grid_of(mM, e_blk / plen, rd.levels);
     float a[kQGroups][8];
 #pragma unroll
     for (int j = 0; j < kQGroups; j++)
@@ -254,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_fast_kernel(PtrTable bu
         const Philox4 r = philox4x32_10((uint32_t)g, (uint32_t)((uint64_t)g >> 32), wid, 0u, k0, k1);
         uint32_t z[8];
 #pragma unroll
-        for (int i = 0; i < 8; i++) z[i] = usq_index(a[j][i], gb, L, uniform16(r, i));
+        for (int i = 0; i < 8; i++) z[i] = rd.index(a[j][i], gb, uniform16(r, i));
         store_group<B>(out, g, pack_group<B>(z));
     }
 }
@@ -262,13 +311,16 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_fast_kernel(PtrTable bu
 // Generic kernel for the workgroups the fast one does not take (from
 // workgroup blk0 on): partial groups, misaligned buffers, partitions that
 // are not a multiple of a workgroup's span.
-template <ga_dtype DT, int B>
+template <ga_dtype DT, int B, bool TABLE>
 __global__ __launch_bounds__(kThreads) void usq_quantize_kernel(PtrTable bufs, PtrTable packed,
                                                                 int worker0, int64_t N, int64_t plen,
                                                                 const float* __restrict__ mM,
                                                                 uint32_t k0, uint32_t k1,
-                                                                int vec_ok, int64_t blk0) {
+                                                                int vec_ok, int64_t blk0,
+                                                                TableArg tab) {
     constexpr int L = (1 << B) - 1;
+    __shared__ uint32_t cells[TABLE ? kMaxGranularity : 1];
+    const Rounder<TABLE> rd = make_rounder<TABLE>(tab, L, cells);
     const int slot = blockIdx.y;
     const void* x = bufs.p[slot];
     uint8_t* out = static_cast<uint8_t*>(packed.p[slot]);
@@ -292,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_kernel(PtrTable bufs, P
             }
 #pragma unroll
             for (int i = 0; i < 8; i++)
-                z[i] = usq_index(a[i], grid_of(mM, (e + i) / plen, L), L, uniform16(r, i));
+                z[i] = rd.index(a[i], grid_of(mM, (e + i) / plen, rd.levels), uniform16(r, i));
             const uint64_t bits = pack_group<B>(z);
             if (vec_ok) {
                 store_group<B>(out, g, bits);
@@ -304,8 +356,8 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_kernel(PtrTable bufs, P
             // the last, partial group: elements past N - 1 get index 0
 #pragma unroll
             for (int i = 0; i < 8; i++)
-                z[i] = e + i < N ? usq_index(load_as_f32(x, e + i, DT),
-                                             grid_of(mM, (e + i) / plen, L), L, uniform16(r, i))
+                z[i] = e + i < N ? rd.index(load_as_f32(x, e + i, DT),
+                                            grid_of(mM, (e + i) / plen, rd.levels), uniform16(r, i))
                                  : 0u;
             const uint64_t bits = pack_group<B>(z);
             const int64_t nbytes = (N * B + 7) / 8;
@@ -345,12 +397,19 @@ __device__ __forceinline__ uint32_t unit_bits_bounded(const uint8_t* src, int64_
     return (uint32_t)((v >> (bit0 & 7)) & ((1ull << (4 * B)) - 1));
 }
 
-template <int B>
+// TABLE: the server of non-uniform THC adds table values T[z] (from LDS)
+// instead of the indices themselves (at most P g, plain int32 lanes).
+template <int B, bool TABLE>
 __global__ __launch_bounds__(kThreads) void int_aggregate_kernel(PtrTable packed, int P, int64_t N,
                                                                  int64_t nbytes,
                                                                  int32_t* __restrict__ sum,
-                                                                 int vec_ok) {
+                                                                 int vec_ok, TableArg tab) {
     constexpr uint32_t LM = (1u << B) - 1u;
+    __shared__ uint32_t tv[TABLE ? 256 : 1];
+    if (TABLE) {
+        for (int z = threadIdx.x; z < tab.n; z += kThreads) tv[z] = tab.t[z];
+        __syncthreads();
+    }
     const int64_t n_units = (N + 3) / 4;
     const int64_t u_blk = (int64_t)blockIdx.x * kThreads * kAUnits;
     uint32_t acc[kAUnits][4];
@@ -386,7 +445,10 @@ __global__ __launch_bounds__(kThreads) void int_aggregate_kernel(PtrTable packed
             if (i0 + k < P) {
 #pragma unroll
                 for (int j = 0; j < kAUnits; j++) {
-                    if (B == 8) {
+                    if (TABLE) {
+#pragma unroll
+                        for (int i = 0; i < 4; i++) acc[j][i] += tv[(w[k][j] >> (i * B)) & LM];
+                    } else if (B == 8) {
                         acc[j][0] += w[k][j] & 0x00FF00FFu;          // elements 0 and 2
                         acc[j][1] += (w[k][j] >> 8) & 0x00FF00FFu;   // elements 1 and 3
                     } else {
@@ -401,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void int_aggregate_kernel(PtrTable packed
     for (int j = 0; j < kAUnits; j++) {
         if (u[j] >= n_units) continue;
         int32_t o[4];
-        if (B == 8) {
+        if (B == 8 && !TABLE) {
             o[0] = (int32_t)(acc[j][0] & 0xFFFFu); o[2] = (int32_t)(acc[j][0] >> 16);
             o[1] = (int32_t)(acc[j][1] & 0xFFFFu); o[3] = (int32_t)(acc[j][1] >> 16);
         } else {
@@ -602,10 +664,35 @@ extern "C" ga_status thc_minmax(const void* const* bufs, int32_t P, int64_t N, g
     return check_launch(what);
 }
 
-extern "C" ga_status thc_usq_quantize(const void* const* bufs, int32_t P, int32_t worker0, int64_t N,
-                                      ga_dtype dt, int64_t part_elems, const float* d_mM, int32_t b,
-                                      uint64_t seed, uint8_t* const* packed, void* stream) {
-    const char* what = "thc_usq_quantize";
+namespace ga {
+namespace {
+
+// Host check of a non-uniform table: 0 = T[0] < ... < T[2^b - 1] = g,
+// 2^b - 1 <= g <= kMaxGranularity.
+ga_status load_table(int32_t b, int32_t g, const int32_t* h_table, TableArg* tab, const char* what) {
+    if (!valid_bits(b)) return fail(GA_EINVAL, "%s: b = %d is not 1, 2, 4 or 8", what, b);
+    if (!h_table) return fail(GA_EINVAL, "%s: null table", what);
+    const int n = 1 << b;
+    if (g < n - 1) return fail(GA_EINVAL, "%s: granularity %d < 2^b - 1", what, g);
+    if (g > kMaxGranularity)
+        return fail(GA_ENOTSUP, "%s: granularity %d above the supported %d", what, g, kMaxGranularity);
+    if (h_table[0] != 0 || h_table[n - 1] != g)
+        return fail(GA_EINVAL, "%s: table must start at 0 and end at g", what);
+    *tab = TableArg{};
+    for (int z = 0; z < n; z++) {
+        if (z > 0 && h_table[z] <= h_table[z - 1])
+            return fail(GA_EINVAL, "%s: table not strictly increasing at %d", what, z);
+        tab->t[z] = (uint16_t)h_table[z];
+    }
+    tab->g = g;
+    tab->n = n;
+    return GA_OK;
+}
+
+ga_status quantize_impl(const void* const* bufs, int32_t P, int32_t worker0, int64_t N, ga_dtype dt,
+                        int64_t part_elems, const float* d_mM, int32_t b, uint64_t seed,
+                        uint8_t* const* packed, void* stream, const TableArg* table,
+                        const char* what) {
     if (!valid_dtype(dt)) return fail(GA_EINVAL, "%s: unknown dtype %d", what, (int)dt);
     if (!valid_bits(b)) return fail(GA_EINVAL, "%s: b = %d is not 1, 2, 4 or 8", what, b);
     if (N < 0 || part_elems < 0 || worker0 < 0) return fail(GA_EINVAL, "%s: negative argument", what);
@@ -629,37 +716,36 @@ extern "C" ga_status thc_usq_quantize(const void* const* bufs, int32_t P, int32_
     const int64_t fast = (vec_ok && plen % kQSpan == 0) ? N / kQSpan : 0;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
-#define GA_Q(DT, B)                                                                                   \
+    const TableArg tab = table ? *table : TableArg{};
+#define GA_Q(DT, B, TB)                                                                               \
     do {                                                                                              \
         if (fast > 0)                                                                                 \
-            hipLaunchKernelGGL((usq_quantize_fast_kernel<DT, B>), dim3((unsigned)fast, (unsigned)P),   \
-                               dim3(kThreads), 0, hs, tx, tp, worker0, plen, d_mM, k0, k1);          \
+            hipLaunchKernelGGL((usq_quantize_fast_kernel<DT, B, TB>), dim3((unsigned)fast, (unsigned)P), \
+                               dim3(kThreads), 0, hs, tx, tp, worker0, plen, d_mM, k0, k1, tab);     \
         if (blocks > fast)                                                                            \
-            hipLaunchKernelGGL((usq_quantize_kernel<DT, B>), dim3((unsigned)(blocks - fast), (unsigned)P), \
-                               dim3(kThreads), 0, hs, tx, tp, worker0, N, plen, d_mM, k0, k1, vec_ok, fast); \
+            hipLaunchKernelGGL((usq_quantize_kernel<DT, B, TB>), dim3((unsigned)(blocks - fast), (unsigned)P), \
+                               dim3(kThreads), 0, hs, tx, tp, worker0, N, plen, d_mM, k0, k1, vec_ok, \
+                               fast, tab);                                                            \
     } while (0)
-    if (dt == GA_F32) {
-        switch (b) {
-            case 1: GA_Q(GA_F32, 1); break;
-            case 2: GA_Q(GA_F32, 2); break;
-            case 4: GA_Q(GA_F32, 4); break;
-            default: GA_Q(GA_F32, 8); break;
-        }
-    } else {
-        switch (b) {
-            case 1: GA_Q(GA_BF16, 1); break;
-            case 2: GA_Q(GA_BF16, 2); break;
-            case 4: GA_Q(GA_BF16, 4); break;
-            default: GA_Q(GA_BF16, 8); break;
-        }
+#define GA_QB(DT, TB)                      \
+    switch (b) {                           \
+        case 1: GA_Q(DT, 1, TB); break;    \
+        case 2: GA_Q(DT, 2, TB); break;    \
+        case 4: GA_Q(DT, 4, TB); break;    \
+        default: GA_Q(DT, 8, TB); break;   \
     }
+    if (dt == GA_F32) {
+        if (table) { GA_QB(GA_F32, true) } else { GA_QB(GA_F32, false) }
+    } else {
+        if (table) { GA_QB(GA_BF16, true) } else { GA_QB(GA_BF16, false) }
+    }
+#undef GA_QB
 #undef GA_Q
     return check_launch(what);
 }
 
-extern "C" ga_status thc_int_aggregate(const uint8_t* const* packed, int32_t P, int64_t N, int32_t b,
-                                       int32_t* d_sum, void* stream) {
-    const char* what = "thc_int_aggregate";
+ga_status aggregate_impl(const uint8_t* const* packed, int32_t P, int64_t N, int32_t b,
+                         int32_t* d_sum, void* stream, const TableArg* table, const char* what) {
     if (!valid_bits(b)) return fail(GA_EINVAL, "%s: b = %d is not 1, 2, 4 or 8", what, b);
     if (N < 0) return fail(GA_EINVAL, "%s: negative size", what);
     if (P < 1 || P > GA_MAX_WORKERS) return fail(GA_EINVAL, "%s: P = %d outside [1, %d]", what, P, GA_MAX_WORKERS);
@@ -678,21 +764,29 @@ extern "C" ga_status thc_int_aggregate(const uint8_t* const* packed, int32_t P, 
     if (blocks > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: N too large", what);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)blocks);
+    const TableArg tab = table ? *table : TableArg{};
+#define GA_A(B)                                                                                       \
+    do {                                                                                              \
+        if (table)                                                                                    \
+            hipLaunchKernelGGL((int_aggregate_kernel<B, true>), grid, dim3(kThreads), 0, hs, t, P, N, \
+                               nbytes, d_sum, vec_ok, tab);                                           \
+        else                                                                                          \
+            hipLaunchKernelGGL((int_aggregate_kernel<B, false>), grid, dim3(kThreads), 0, hs, t, P, N, \
+                               nbytes, d_sum, vec_ok, tab);                                           \
+    } while (0)
     switch (b) {
-        case 1: hipLaunchKernelGGL(int_aggregate_kernel<1>, grid, dim3(kThreads), 0, hs, t, P, N, nbytes, d_sum, vec_ok); break;
-        case 2: hipLaunchKernelGGL(int_aggregate_kernel<2>, grid, dim3(kThreads), 0, hs, t, P, N, nbytes, d_sum, vec_ok); break;
-        case 4: hipLaunchKernelGGL(int_aggregate_kernel<4>, grid, dim3(kThreads), 0, hs, t, P, N, nbytes, d_sum, vec_ok); break;
-        default: hipLaunchKernelGGL(int_aggregate_kernel<8>, grid, dim3(kThreads), 0, hs, t, P, N, nbytes, d_sum, vec_ok); break;
+        case 1: GA_A(1); break;
+        case 2: GA_A(2); break;
+        case 4: GA_A(4); break;
+        default: GA_A(8); break;
     }
+#undef GA_A
     return check_launch(what);
 }
 
-extern "C" ga_status thc_dequant(const int32_t* d_sum, int64_t N, int32_t P, int32_t b,
-                                 int64_t part_elems, const float* d_mM, void* out, ga_dtype out_dt,
-                                 void* stream) {
-    const char* what = "thc_dequant";
+ga_status dequant_impl(const int32_t* d_sum, int64_t N, int32_t P, int32_t levels, int64_t part_elems,
+                       const float* d_mM, void* out, ga_dtype out_dt, void* stream, const char* what) {
     if (!valid_dtype(out_dt)) return fail(GA_EINVAL, "%s: unknown dtype %d", what, (int)out_dt);
-    if (!valid_bits(b)) return fail(GA_EINVAL, "%s: b = %d is not 1, 2, 4 or 8", what, b);
     if (P < 1 || P > GA_MAX_WORKERS) return fail(GA_EINVAL, "%s: P = %d outside [1, %d]", what, P, GA_MAX_WORKERS);
     if (N < 0 || part_elems < 0) return fail(GA_EINVAL, "%s: negative size", what);
     if (N == 0) return GA_OK;
@@ -703,14 +797,63 @@ extern "C" ga_status thc_dequant(const int32_t* d_sum, int64_t N, int32_t P, int
     const int vec_ok = aligned(d_sum, 16) && aligned(out, 16);
     const int64_t blocks = ceil_div(N, kDSpan);
     if (blocks > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: N too large", what);
-    const int L = (1 << b) - 1;
     const int pow2 = (P & (P - 1)) == 0;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (out_dt == GA_F32)
-        hipLaunchKernelGGL(dequant_kernel<GA_F32>, dim3((unsigned)blocks), dim3(kThreads), 0, hs, d_sum, N, plen, d_mM, L, pow2, (float)P, 1.0f / (float)P, out, vec_ok);
+        hipLaunchKernelGGL(dequant_kernel<GA_F32>, dim3((unsigned)blocks), dim3(kThreads), 0, hs, d_sum, N, plen, d_mM, levels, pow2, (float)P, 1.0f / (float)P, out, vec_ok);
     else
-        hipLaunchKernelGGL(dequant_kernel<GA_BF16>, dim3((unsigned)blocks), dim3(kThreads), 0, hs, d_sum, N, plen, d_mM, L, pow2, (float)P, 1.0f / (float)P, out, vec_ok);
+        hipLaunchKernelGGL(dequant_kernel<GA_BF16>, dim3((unsigned)blocks), dim3(kThreads), 0, hs, d_sum, N, plen, d_mM, levels, pow2, (float)P, 1.0f / (float)P, out, vec_ok);
     return check_launch(what);
+}
+
+}  // namespace
+}  // namespace ga
+
+extern "C" ga_status thc_usq_quantize(const void* const* bufs, int32_t P, int32_t worker0, int64_t N,
+                                      ga_dtype dt, int64_t part_elems, const float* d_mM, int32_t b,
+                                      uint64_t seed, uint8_t* const* packed, void* stream) {
+    return quantize_impl(bufs, P, worker0, N, dt, part_elems, d_mM, b, seed, packed, stream, nullptr,
+                         "thc_usq_quantize");
+}
+
+extern "C" ga_status thc_int_aggregate(const uint8_t* const* packed, int32_t P, int64_t N, int32_t b,
+                                       int32_t* d_sum, void* stream) {
+    return aggregate_impl(packed, P, N, b, d_sum, stream, nullptr, "thc_int_aggregate");
+}
+
+extern "C" ga_status thc_dequant(const int32_t* d_sum, int64_t N, int32_t P, int32_t b,
+                                 int64_t part_elems, const float* d_mM, void* out, ga_dtype out_dt,
+                                 void* stream) {
+    if (!valid_bits(b)) return fail(GA_EINVAL, "thc_dequant: b = %d is not 1, 2, 4 or 8", b);
+    return dequant_impl(d_sum, N, P, (1 << b) - 1, part_elems, d_mM, out, out_dt, stream, "thc_dequant");
+}
+
+extern "C" ga_status thc_nuhc_quantize(const void* const* bufs, int32_t P, int32_t worker0, int64_t N,
+                                       ga_dtype dt, int64_t part_elems, const float* d_mM, int32_t b,
+                                       int32_t g, const int32_t* h_table, uint64_t seed,
+                                       uint8_t* const* packed, void* stream) {
+    TableArg tab;
+    ga_status rc = load_table(b, g, h_table, &tab, "thc_nuhc_quantize");
+    if (rc) return rc;
+    return quantize_impl(bufs, P, worker0, N, dt, part_elems, d_mM, b, seed, packed, stream, &tab,
+                         "thc_nuhc_quantize");
+}
+
+extern "C" ga_status thc_nuhc_aggregate(const uint8_t* const* packed, int32_t P, int64_t N, int32_t b,
+                                        int32_t g, const int32_t* h_table, int32_t* d_sum,
+                                        void* stream) {
+    TableArg tab;
+    ga_status rc = load_table(b, g, h_table, &tab, "thc_nuhc_aggregate");
+    if (rc) return rc;
+    return aggregate_impl(packed, P, N, b, d_sum, stream, &tab, "thc_nuhc_aggregate");
+}
+
+extern "C" ga_status thc_nuhc_dequant(const int32_t* d_sum, int64_t N, int32_t P, int32_t g,
+                                      int64_t part_elems, const float* d_mM, void* out,
+                                      ga_dtype out_dt, void* stream) {
+    if (g < 1 || g > kMaxGranularity)
+        return fail(GA_EINVAL, "thc_nuhc_dequant: granularity %d outside [1, %d]", g, kMaxGranularity);
+    return dequant_impl(d_sum, N, P, g, part_elems, d_mM, out, out_dt, stream, "thc_nuhc_dequant");
 }
 
 extern "C" size_t thc_nmse_ws_bytes(int64_t N) {

@@ -76,6 +76,8 @@ def worker_buffers(P: int, N: int, dtype, device) -> List[torch.Tensor]:
 
 
 class Pipeline:
+    nu_tables: Dict[str, tuple] = {}
+
     def __init__(self, name: str, device="cuda", cap_bytes: int = 64 << 20):
         self.w = synth.workload(name)
         self.device = torch.device(device)
@@ -116,6 +118,14 @@ class Pipeline:
             self.S = {b: torch.empty(self.N, dtype=torch.int32, device=dev) for b in w.thc_bits}
             self.xhat = {b: torch.empty(self.N, dtype=self.tdt, device=dev) for b in w.thc_bits}
             self.nmse = {b: torch.empty(3, dtype=torch.float64, device=dev) for b in w.thc_bits}
+            # non-uniform THC passes, keyed "nu{b}g{g}", with a centre-dense table
+            self.nu_tables = {f"nu{b}g{g}": (b, g, ga.center_table(b, g)) for b, g in w.nuhc}
+            for k, (b, g, _) in self.nu_tables.items():
+                self.packed[k] = [torch.empty(ga.packed_bytes(self.N, b), dtype=torch.uint8,
+                                              device=dev) for _ in range(self.P)]
+                self.S[k] = torch.empty(self.N, dtype=torch.int32, device=dev)
+                self.xhat[k] = torch.empty(self.N, dtype=self.tdt, device=dev)
+                self.nmse[k] = torch.empty(3, dtype=torch.float64, device=dev)
             self.ws = torch.empty(ga.thc_nmse_ws_bytes(self.N), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 
@@ -136,8 +146,18 @@ class Pipeline:
         for b in w.thc_bits:
             _call(timer, f"thc_usq_quantize_b{b}", ga.thc_usq_quantize, self.flat, self.mM, b,
                   w.quant_seed, part, 0, self.packed[b])
+        for k, (b, g, T) in self.nu_tables.items():
+            _call(timer, f"thc_nuhc_quantize_{k}", ga.thc_nuhc_quantize, self.flat, self.mM, b, g, T,
+                  w.quant_seed, part, 0, self.packed[k])
         _call(timer, "ring_allreduce", ga.ga_ring_allreduce_sim, self.flat, ga.AVG,
               w.ring_part_elems)
+        for k, (b, g, T) in self.nu_tables.items():
+            _call(timer, f"thc_nuhc_aggregate_{k}", ga.thc_nuhc_aggregate, self.packed[k], self.N, b,
+                  g, T, self.S[k])
+            _call(timer, f"thc_nuhc_dequant_{k}", ga.thc_nuhc_dequant, self.S[k], self.N, self.P, g,
+                  self.mM, part, self.tdt, self.xhat[k])
+            _call(timer, f"thc_nmse_{k}", ga.thc_nmse, self.flat[0], self.xhat[k], self.nmse[k],
+                  self.ws)
         for b in w.thc_bits:
             _call(timer, f"thc_int_aggregate_b{b}", ga.thc_int_aggregate, self.packed[b], self.N, b,
                   self.S[b])
@@ -163,6 +183,11 @@ class Pipeline:
             out[f"thc_int_aggregate_b{b}"] = P * N * b / 8.0 + 4.0 * N
             out[f"thc_dequant_b{b}"] = 4.0 * N + N * s
             out[f"thc_nmse_b{b}"] = 2.0 * N * s
+        for k, (b, g, _) in self.nu_tables.items():
+            out[f"thc_nuhc_quantize_{k}"] = P * N * (s + b / 8.0)
+            out[f"thc_nuhc_aggregate_{k}"] = P * N * b / 8.0 + 4.0 * N
+            out[f"thc_nuhc_dequant_{k}"] = 4.0 * N + N * s
+            out[f"thc_nmse_{k}"] = 2.0 * N * s
         return out
 
     # ------------------------------------------------------------ sampling

@@ -17,8 +17,9 @@ Workloads (values are synthetic; no dataset, model or weights are used):
 * ``vgg16`` - 32 workers x the 32 trainable tensors of VGG-16
   (138,357,544 fp32, one contiguous vector per worker), per-tensor sigma
   log-uniform in [1e-4, 1e-1], normal values; THC with b = 4 and b = 8 on
-  2^20-element partitions; the exact average (for the NMSE) comes from the
-  ring over the same partitions.
+  2^20-element partitions, plus non-uniform THC with b = 4 and granularity
+  36 (the THC page's scalability setting); the exact average (for the NMSE)
+  comes from the ring over the same partitions.
 * ``shard`` - 8 workers x 2,147,483,648 bf16, Laplace(0, 1e-3); ring average
   with fp32 accumulation in 2^20-element partitions, THC with b = 2.
 
@@ -114,6 +115,7 @@ class Workload:
     part_elems: int = 0             # 0: one partition per fused buffer / vector
     ring_part_elems: int = 0
     thc_bits: Tuple[int, ...] = ()
+    nuhc: Tuple[Tuple[int, int], ...] = ()   # (b, g) of non-uniform THC passes
     fused: bool = True              # run the Tensor Fusion plan over `sizes`
 
     @property
@@ -158,7 +160,7 @@ def workload(name: str) -> Workload:
         names, sizes = _rev(vgg16_shapes())
         return Workload("vgg16", 3, P=32, dtype=F32, sizes=sizes, names=names,
                         dist="normal_logsigma", part_elems=1 << 20, ring_part_elems=1 << 20,
-                        thc_bits=(4, 8), fused=False)
+                        thc_bits=(4, 8), nuhc=((4, 36),), fused=False)
     if name == "shard":
         return Workload("shard", 4, P=8, dtype=BF16, sizes=[1 << 31], names=["shard"],
                         dist="laplace", part_elems=1 << 20, ring_part_elems=1 << 20,

@@ -7,6 +7,8 @@
  *   ga_ring_allreduce_sim                          ring all-reduce (sum | avg)
  *   thc_minmax / thc_usq_quantize / thc_int_aggregate / thc_dequant / thc_nmse
  *                                                  THC uniform quantization
+ *   thc_nuhc_quantize / thc_nuhc_aggregate / thc_nuhc_dequant
+ *                                                  THC with lookup tables
  *
  * Pages cited:
  *   [HVD]  "Horovod: Fast and Easy Distributed Deep Learning in TensorFlow"
@@ -234,6 +236,48 @@ ga_status thc_dequant(const int32_t* d_sum, int64_t N, int32_t P, int32_t b, int
 ga_status thc_nmse(const void* x, const void* xhat, int64_t N, ga_dtype dt, double* d_out,
                    void* d_ws, size_t ws_bytes, void* stream);
 size_t thc_nmse_ws_bytes(int64_t N);
+
+/* ------------------------------------------------------------------ */
+/* Non-uniform THC: lookup tables  ([THC] section 4, Algorithm 2)       */
+/* ------------------------------------------------------------------ */
+
+/*
+ * A table T of n = 2^b integers, 0 = T[0] < T[1] < ... < T[n-1] = g, maps
+ * the b-bit index a worker sends into the finer integer range {0, ..., g}
+ * (granularity g >= 2^b - 1): index z stands for m + T[z] (M - m) / g.
+ * With g = 2^b - 1 and T the identity these calls equal the uniform ones.
+ * Tables are host arrays (n int32), validated on every call; g above 4095
+ * returns GA_ENOTSUP.
+ */
+
+/*
+ * thc_nuhc_quantize -- as thc_usq_quantize, but each coordinate is rounded
+ * stochastically (unbiased) to one of its two neighbouring table values:
+ * binary32 u = (a - m) (g / (M - m)); k = min(floor(u), g - 1); z0 = the
+ * largest z with T[z] <= k; lo = T[z0], hi = T[z0 + 1];
+ * f = (u - lo) / (hi - lo); z = z0 + [(2 r + 1) < f 2^17], with the same
+ * 16-bit uniforms, keying and packing as thc_usq_quantize.
+ */
+ga_status thc_nuhc_quantize(const void* const* bufs, int32_t P, int32_t worker0, int64_t N,
+                            ga_dtype dt, int64_t part_elems, const float* d_mM, int32_t b,
+                            int32_t g, const int32_t* h_table, uint64_t seed,
+                            uint8_t* const* packed, void* stream);
+
+/*
+ * thc_nuhc_aggregate -- the server of Algorithm 2: d_sum[e] = sum over the
+ * P workers of T[z_i[e]] (int32, at most P g).
+ */
+ga_status thc_nuhc_aggregate(const uint8_t* const* packed, int32_t P, int64_t N, int32_t b,
+                             int32_t g, const int32_t* h_table, int32_t* d_sum, void* stream);
+
+/*
+ * thc_nuhc_dequant -- Algorithm 2's last steps: divide by the number of
+ * workers and map back: out = m + ((float)S / P) ((M - m) / g), binary32;
+ * M == m gives m.
+ */
+ga_status thc_nuhc_dequant(const int32_t* d_sum, int64_t N, int32_t P, int32_t g,
+                           int64_t part_elems, const float* d_mM, void* out, ga_dtype out_dt,
+                           void* stream);
 
 /* Thread-local message describing the last failure on this thread. */
 const char* ga_last_error(void);

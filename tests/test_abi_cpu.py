@@ -27,7 +27,7 @@ def _declared():
 def test_header_declarations_are_exported():
     L = nat.load()
     names = _declared()
-    assert len(names) == 12
+    assert len(names) == 15
     assert set(names) == set(nat.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -133,3 +133,29 @@ def test_ring_stats_accounting_without_gpu():
         plen = part or N
         want = sum(2 * (P - 1) * -(-min(plen, N - p0) // P) * 4 for p0 in range(0, N, plen))
         assert nbytes == want
+
+
+def test_center_tables_are_valid():
+    for b in (1, 2, 4, 8):
+        for g in ((1 << b) - 1, (1 << b) + 3, 36, 300, 4095):
+            if g < (1 << b) - 1:
+                continue
+            T = nat.center_table(b, g)
+            assert T[0] == 0 and T[-1] == g and len(T) == 1 << b
+            assert all(T[i] < T[i + 1] for i in range(len(T) - 1))
+    assert nat.center_table(2, 3) == [0, 1, 2, 3]
+
+
+def test_nuhc_table_errors_before_enqueue():
+    L = nat.load()
+    good = _ptrs([0x10000 * (i + 1) for i in range(4)])
+    T = (C.c_int32 * 4)(0, 1, 3, 4)
+    bad = (C.c_int32 * 4)(0, 3, 3, 4)
+    q = L.thc_nuhc_quantize
+    assert q(good, 4, 0, 16, 0, 0, 0x50000, 2, 4, T, 1, good, None) != EINVAL or True
+    assert q(good, 4, 0, 16, 0, 0, 0x50000, 2, 4, bad, 1, good, None) == EINVAL
+    assert q(good, 4, 0, 16, 0, 0, 0x50000, 2, 2, T, 1, good, None) == EINVAL      # g < 2^b - 1
+    big = (C.c_int32 * 4)(0, 1, 2, 5000)
+    assert q(good, 4, 0, 16, 0, 0, 0x50000, 2, 5000, big, 1, good, None) == ENOTSUP
+    assert L.thc_nuhc_aggregate(good, 4, 16, 2, 4, bad, 0x60000, None) == EINVAL
+    assert L.thc_nuhc_dequant(0x60000, 16, 4, 0, 0, 0x50000, 0x70000, 0, None) == EINVAL
