@@ -58,6 +58,14 @@ def lib():
         L.orc_nuhc_quantize.argtypes = [vp, i64, i32, i32, i64, vp, i32, i32, vp, C.c_uint64, i64, vp]
         L.orc_nuhc_aggregate.argtypes = [C.POINTER(vp), i32, i64, i32, i32, vp, vp]
         L.orc_nuhc_dequant.argtypes = [vp, i64, i32, i32, i64, vp, vp, i32]
+        L.orc_rht_forward.argtypes = [vp, i32, i64, i64, C.c_uint64, vp]
+        L.orc_rht_inverse.argtypes = [vp, i64, i64, C.c_uint64, vp, i32]
+        L.orc_rht_sumsq.argtypes = [vp, i32, i64, i64, vp]
+        L.orc_rht_range.argtypes = [vp, i32, i64, i64, C.c_double, vp]
+        L.orc_clamp.argtypes = [vp, i64, i64, vp]
+        L.orc_clamp.restype = None
+        L.orc_rademacher.argtypes = [C.c_uint64, i64, i64, vp]
+        L.orc_rademacher.restype = None
         L.orc_f32_to_bf16.argtypes = [vp, i64, vp]
         L.orc_f32_to_bf16.restype = None
         L.orc_bf16_to_f32.argtypes = [vp, i64, vp]
@@ -230,3 +238,49 @@ def nuhc_dequant(Y: np.ndarray, P: int, g: int, part: int, mM: np.ndarray, out_d
     _check(lib().orc_nuhc_dequant(Y.ctypes.data, N, P, g, part, mM.ctypes.data, out.ctypes.data,
                                   out_dt), "nuhc_dequant")
     return out
+
+
+# ---------------------------------------------------------------- RHT pre/post-processing
+def rht_forward(x: np.ndarray, d: int, seed: int) -> np.ndarray:
+    """Zero-pads to a multiple of d; returns ceil(N/d) d binary32 values."""
+    x = np.ascontiguousarray(x)
+    y = np.zeros(-(-x.size // d) * d, dtype=np.float32)
+    _check(lib().orc_rht_forward(x.ctypes.data, _dt(x), x.size, d, seed, y.ctypes.data), "rht_forward")
+    return y
+
+
+def rht_inverse(y: np.ndarray, d: int, seed: int, out_dt: int = F32) -> np.ndarray:
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.zeros(y.size, dtype=np.float32 if out_dt == F32 else np.uint16)
+    _check(lib().orc_rht_inverse(y.ctypes.data, y.size, d, seed, out.ctypes.data, out_dt),
+           "rht_inverse")
+    return out
+
+
+def rademacher(seed: int, e0: int, n: int) -> np.ndarray:
+    out = np.zeros(n, dtype=np.float32)
+    lib().orc_rademacher(seed, e0, n, out.ctypes.data)
+    return out
+
+
+def rht_sumsq(x: np.ndarray, d: int) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    out = np.zeros(-(-x.size // d), dtype=np.float64)
+    _check(lib().orc_rht_sumsq(x.ctypes.data, _dt(x), x.size, d, out.ctypes.data), "rht_sumsq")
+    return out
+
+
+def rht_range(sumsq: np.ndarray, d: int, t_p: float) -> np.ndarray:
+    """sumsq: [P, nblk] float64 -> mM [nblk, 2] float32."""
+    sumsq = np.ascontiguousarray(sumsq, dtype=np.float64)
+    P, nblk = sumsq.shape
+    mM = np.zeros((nblk, 2), dtype=np.float32)
+    _check(lib().orc_rht_range(sumsq.ctypes.data, P, nblk, d, t_p, mM.ctypes.data), "rht_range")
+    return mM
+
+
+def clamp(y: np.ndarray, d: int, mM: np.ndarray) -> np.ndarray:
+    y = np.ascontiguousarray(y, dtype=np.float32).copy()
+    mM = np.ascontiguousarray(mM, dtype=np.float32)
+    lib().orc_clamp(y.ctypes.data, y.size, d, mM.ctypes.data)
+    return y

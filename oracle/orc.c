@@ -590,6 +590,151 @@ int orc_nuhc_dequant(const int32_t *Y, int64_t N, int P, int g, int64_t part, co
     return dequant_levels(Y, N, P, g, part, mM, out, out_dt);
 }
 
+/* ------------------------------------------------------------------ */
+/* Randomized Hadamard Transform pre/post-processing                   */
+/* ------------------------------------------------------------------ */
+
+/*
+ * [THC] section 5: RHT(x) = (1/sqrt(d)) H D x and RHT^-1(y) = (1/sqrt(d)) D H y
+ * with H the d x d Hadamard matrix and D a diagonal of independent +-1
+ * (Rademacher) signs, applied here to every block of d = 2^k consecutive
+ * coordinates (the block is the quantizer's partition).
+ *
+ * Readings: D is shared by all workers (the transform must be the same
+ * linear map for the sum of transformed vectors to invert), drawn from
+ * Philox4x32-10 with key (seed mod 2^32, seed >> 32) and counter
+ * (q mod 2^32, q >> 32, 0x52485400, 0), q = e / 128: coordinate e takes bit
+ * (e mod 32) of output word (e / 32) mod 4, and a set bit means -1. H x is
+ * the textbook in-place transform: for s = 0, 1, ..., k-1, every pair
+ * (i, i + 2^s) with bit s of i clear becomes (x_i + x_j, x_i - x_j); all in
+ * binary32, the scaling by fl32(1/sqrt(d)) after the last stage. The
+ * quantizer's integer decisions depend on these values, so the transform
+ * runs in the kernels' precision (binary32); its accuracy against the exact
+ * transform is pinned separately.
+ */
+static float rademacher(uint64_t seed, int64_t e)
+{
+    uint64_t q = (uint64_t)e >> 7;
+    uint32_t ctr[4] = {(uint32_t)q, (uint32_t)(q >> 32), 0x52485400u, 0u};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    orc_philox4x32_10(ctr, key, out);
+    uint32_t bit = (out[(e >> 5) & 3] >> (e & 31)) & 1u;
+    return bit ? -1.0f : 1.0f;
+}
+
+void orc_rademacher(uint64_t seed, int64_t e0, int64_t n, float *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = rademacher(seed, e0 + i);
+}
+
+static void fwht_block(float *v, int64_t d)
+{
+    for (int64_t h = 1; h < d; h <<= 1)
+        for (int64_t i = 0; i < d; i++)
+            if ((i & h) == 0) {
+                float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+}
+
+static int pow2_ok(int64_t d)
+{
+    return d >= 2 && (d & (d - 1)) == 0;
+}
+
+/* y[e] for e in [0, ceil(N/d) d): a vector whose length is not a multiple
+ * of d is zero-padded to one; x fp32 or bf16, y fp32. */
+int orc_rht_forward(const void *x, int dt, int64_t N, int64_t d, uint64_t seed, float *y)
+{
+    if (!pow2_ok(d) || N < 0)
+        return -1;
+    const float c = (float)(1.0 / sqrt((double)d));
+    const int64_t Np = (N + d - 1) / d * d;
+    for (int64_t b0 = 0; b0 < Np; b0 += d) {
+        for (int64_t i = 0; i < d; i++)
+            y[b0 + i] = rademacher(seed, b0 + i) * (b0 + i < N ? load_elem(x, dt, b0 + i) : 0.0f);
+        fwht_block(y + b0, d);
+        for (int64_t i = 0; i < d; i++)
+            y[b0 + i] = y[b0 + i] * c;
+    }
+    return 0;
+}
+
+/* out[e] = (1/sqrt(d)) D H y, binary32, rounded to bf16 if asked. */
+int orc_rht_inverse(const float *y, int64_t N, int64_t d, uint64_t seed, void *out, int out_dt)
+{
+    if (!pow2_ok(d) || N % d)
+        return -1;
+    const float c = (float)(1.0 / sqrt((double)d));
+    float *v = (float *)malloc((size_t)d * sizeof(float));
+    if (!v)
+        return -2;
+    for (int64_t b0 = 0; b0 < N; b0 += d) {
+        memcpy(v, y + b0, (size_t)d * sizeof(float));
+        fwht_block(v, d);
+        for (int64_t i = 0; i < d; i++)
+            store_elem(out, out_dt, b0 + i, rademacher(seed, b0 + i) * (v[i] * c));
+    }
+    free(v);
+    return 0;
+}
+
+/*
+ * [THC] section 5, norm-based range: every worker computes the norm of each
+ * of its blocks; the range of block p is M = (t_p / sqrt(d)) * l_p, m = -M,
+ * with l_p the largest norm among the workers. Reading: the page writes
+ * "l = max ||x_i||^2"; only the norm itself (not its square) has the units
+ * of M, so l is the norm. Sums of squares in binary64 (the squares of
+ * binary32 values are exact there), in index order; M rounded once to
+ * binary32 from binary64 t_p sqrt(max sum) / sqrt(d).
+ */
+int orc_rht_sumsq(const void *x, int dt, int64_t N, int64_t d, double *sumsq)
+{
+    if (!pow2_ok(d) || N < 0)
+        return -1;
+    for (int64_t b0 = 0, p = 0; b0 < N; b0 += d, p++) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < d && b0 + i < N; i++) {
+            double v = (double)load_elem(x, dt, b0 + i);
+            acc += v * v;
+        }
+        sumsq[p] = acc;
+    }
+    return 0;
+}
+
+int orc_rht_range(const double *sumsq, int P, int64_t nblk, int64_t d, double t_p, float *mM)
+{
+    if (P < 1 || !pow2_ok(d))
+        return -1;
+    for (int64_t p = 0; p < nblk; p++) {
+        double mx = 0.0;
+        for (int i = 0; i < P; i++)
+            if (sumsq[(int64_t)i * nblk + p] > mx)
+                mx = sumsq[(int64_t)i * nblk + p];
+        float M = (float)(t_p * sqrt(mx) / sqrt((double)d));
+        mM[2 * p] = -M;
+        mM[2 * p + 1] = M;
+    }
+    return 0;
+}
+
+/* [THC] section 5, truncation: coordinates beyond the range are rounded to
+ * its ends. */
+void orc_clamp(float *y, int64_t N, int64_t d, const float *mM)
+{
+    for (int64_t e = 0; e < N; e++) {
+        int64_t p = e / d;
+        if (y[e] < mM[2 * p])
+            y[e] = mM[2 * p];
+        if (y[e] > mM[2 * p + 1])
+            y[e] = mM[2 * p + 1];
+    }
+}
+
 /*
  * [THC] section 2, Figure 2(b): NMSE(x, xhat) = ||x - xhat||^2 / ||x||^2,
  * accumulated in binary64 in index order. out = {num, den, num/den}; a zero
