@@ -58,8 +58,8 @@ def lib():
         L.orc_nuhc_quantize.argtypes = [vp, i64, i32, i32, i64, vp, i32, i32, vp, C.c_uint64, i64, vp]
         L.orc_nuhc_aggregate.argtypes = [C.POINTER(vp), i32, i64, i32, i32, vp, vp]
         L.orc_nuhc_dequant.argtypes = [vp, i64, i32, i32, i64, vp, vp, i32]
-        L.orc_rht_forward.argtypes = [vp, i32, i64, i64, C.c_uint64, vp]
-        L.orc_rht_inverse.argtypes = [vp, i64, i64, C.c_uint64, vp, i32]
+        L.orc_rht_forward.argtypes = [vp, i32, i64, i64, C.c_uint64, i64, vp]
+        L.orc_rht_inverse.argtypes = [vp, i64, i64, C.c_uint64, i64, vp, i32]
         L.orc_rht_sumsq.argtypes = [vp, i32, i64, i64, vp]
         L.orc_rht_range.argtypes = [vp, i32, i64, i64, C.c_double, vp]
         L.orc_clamp.argtypes = [vp, i64, i64, vp]
@@ -241,18 +241,20 @@ def nuhc_dequant(Y: np.ndarray, P: int, g: int, part: int, mM: np.ndarray, out_d
 
 
 # ---------------------------------------------------------------- RHT pre/post-processing
-def rht_forward(x: np.ndarray, d: int, seed: int) -> np.ndarray:
-    """Zero-pads to a multiple of d; returns ceil(N/d) d binary32 values."""
+def rht_forward(x: np.ndarray, d: int, seed: int, e0: int = 0) -> np.ndarray:
+    """Zero-pads to a multiple of d; returns ceil(N/d) d binary32 values.
+    e0: index of x[0] in the whole vector (a multiple of d; selects the signs)."""
     x = np.ascontiguousarray(x)
     y = np.zeros(-(-x.size // d) * d, dtype=np.float32)
-    _check(lib().orc_rht_forward(x.ctypes.data, _dt(x), x.size, d, seed, y.ctypes.data), "rht_forward")
+    _check(lib().orc_rht_forward(x.ctypes.data, _dt(x), x.size, d, seed, e0, y.ctypes.data),
+           "rht_forward")
     return y
 
 
-def rht_inverse(y: np.ndarray, d: int, seed: int, out_dt: int = F32) -> np.ndarray:
+def rht_inverse(y: np.ndarray, d: int, seed: int, out_dt: int = F32, e0: int = 0) -> np.ndarray:
     y = np.ascontiguousarray(y, dtype=np.float32)
     out = np.zeros(y.size, dtype=np.float32 if out_dt == F32 else np.uint16)
-    _check(lib().orc_rht_inverse(y.ctypes.data, y.size, d, seed, out.ctypes.data, out_dt),
+    _check(lib().orc_rht_inverse(y.ctypes.data, y.size, d, seed, e0, out.ctypes.data, out_dt),
            "rht_inverse")
     return out
 

@@ -646,16 +646,19 @@ static int pow2_ok(int64_t d)
 }
 
 /* y[e] for e in [0, ceil(N/d) d): a vector whose length is not a multiple
- * of d is zero-padded to one; x fp32 or bf16, y fp32. */
-int orc_rht_forward(const void *x, int dt, int64_t N, int64_t d, uint64_t seed, float *y)
+ * of d is zero-padded to one; x fp32 or bf16, y fp32. e0 is the index of
+ * x[0] in the whole vector (a multiple of d), which selects the signs, so a
+ * run of blocks can be transformed on its own. */
+int orc_rht_forward(const void *x, int dt, int64_t N, int64_t d, uint64_t seed, int64_t e0,
+                    float *y)
 {
-    if (!pow2_ok(d) || N < 0)
+    if (!pow2_ok(d) || N < 0 || e0 < 0 || e0 % d)
         return -1;
     const float c = (float)(1.0 / sqrt((double)d));
     const int64_t Np = (N + d - 1) / d * d;
     for (int64_t b0 = 0; b0 < Np; b0 += d) {
         for (int64_t i = 0; i < d; i++)
-            y[b0 + i] = rademacher(seed, b0 + i) * (b0 + i < N ? load_elem(x, dt, b0 + i) : 0.0f);
+            y[b0 + i] = rademacher(seed, e0 + b0 + i) * (b0 + i < N ? load_elem(x, dt, b0 + i) : 0.0f);
         fwht_block(y + b0, d);
         for (int64_t i = 0; i < d; i++)
             y[b0 + i] = y[b0 + i] * c;
@@ -663,10 +666,12 @@ int orc_rht_forward(const void *x, int dt, int64_t N, int64_t d, uint64_t seed, 
     return 0;
 }
 
-/* out[e] = (1/sqrt(d)) D H y, binary32, rounded to bf16 if asked. */
-int orc_rht_inverse(const float *y, int64_t N, int64_t d, uint64_t seed, void *out, int out_dt)
+/* out[e] = (1/sqrt(d)) D H y, binary32, rounded to bf16 if asked; e0 as
+ * for the forward transform. */
+int orc_rht_inverse(const float *y, int64_t N, int64_t d, uint64_t seed, int64_t e0, void *out,
+                    int out_dt)
 {
-    if (!pow2_ok(d) || N % d)
+    if (!pow2_ok(d) || N % d || e0 < 0 || e0 % d)
         return -1;
     const float c = (float)(1.0 / sqrt((double)d));
     float *v = (float *)malloc((size_t)d * sizeof(float));
@@ -676,7 +681,7 @@ int orc_rht_inverse(const float *y, int64_t N, int64_t d, uint64_t seed, void *o
         memcpy(v, y + b0, (size_t)d * sizeof(float));
         fwht_block(v, d);
         for (int64_t i = 0; i < d; i++)
-            store_elem(out, out_dt, b0 + i, rademacher(seed, b0 + i) * (v[i] * c));
+            store_elem(out, out_dt, b0 + i, rademacher(seed, e0 + b0 + i) * (v[i] * c));
     }
     free(v);
     return 0;

@@ -129,3 +129,17 @@ def test_ragged_length_is_zero_padded():
     pad = np.concatenate([x, np.zeros(d - 17, dtype=np.float32)])
     assert np.array_equal(oracle.rht_forward(x, d, 3), oracle.rht_forward(pad, d, 3))
     assert np.array_equal(oracle.rht_sumsq(x, d), oracle.rht_sumsq(pad, d))
+
+
+def test_block_offset_selects_the_same_signs():
+    """Transforming blocks q.. on their own (e0 = q d) gives the whole
+    vector's blocks q.. (the signs follow global indices)."""
+    d, seed = 64, 21
+    x = np.random.default_rng(2).standard_normal(5 * d).astype(np.float32)
+    y = oracle.rht_forward(x, d, seed)
+    assert np.array_equal(oracle.rht_forward(x[2 * d:], d, seed, e0=2 * d), y[2 * d:])
+    assert np.array_equal(oracle.rht_inverse(y[3 * d:], d, seed, e0=3 * d),
+                          oracle.rht_inverse(y, d, seed)[3 * d:])
+    assert not np.array_equal(oracle.rht_forward(x[2 * d:], d, seed), y[2 * d:])
+    with pytest.raises(Exception):
+        oracle.rht_forward(x, d, seed, e0=5)
