@@ -36,8 +36,8 @@ DESCRIPTIONS = {
     "small": "4 workers x 1,048,576 fp32 N(0,0.01^2); ring avg + THC USQ b=4",
     "fusion": "8 workers x 200 fp32 tensors (log-uniform 1K..256K); 64 MiB fusion, ring avg",
     "resnet101": "16 workers x ResNet-101 gradients (314 tensors, 44,549,160 fp32); fusion + ring avg",
-    "vgg16": ("32 workers x VGG-16 gradients (138,357,544 fp32); THC USQ b=4,8 and table THC "
-              "b=4 g=36 + ring avg + NMSE"),
+    "vgg16": ("32 workers x VGG-16 gradients (138,357,544 fp32); THC USQ b=4,8, table THC "
+              "b=4 g=36, and RHT (d=2^20, p=1/32) + table THC b=4 g=36 + inverse; ring avg; NMSE"),
     "shard": ("8 workers x 2,147,483,648 bf16 Laplace(0,1e-3); ring avg with fp32 accumulation "
               "in 2^20-element partitions + THC USQ b=2 (uint8-packed), int32 sum, dequant, NMSE"),
 }
@@ -71,9 +71,11 @@ def cpu_baseline(pipe, samples, budget_s: float):
     import numpy as np
 
     import oracle
+    from gradient_all_reduce_worker_amd.pipeline import t_p
 
     w = pipe.w
     P = pipe.P
+    tp = t_p(w.rht_p)
     done_elems, t_total, used = 0, 0.0, 0
     for p in sorted(samples):
         xs = [a.copy() for a in samples[p]]
@@ -83,11 +85,27 @@ def cpu_baseline(pipe, samples, budget_s: float):
         mM = oracle.minmax(xs, n)
         packed = {b: [oracle.usq_quantize(xs[i], i, n, mM, b, w.quant_seed, e_offset=lo)
                       for i in range(P)] for b in w.thc_bits}
+        for k, (b, g, T) in pipe.nu_tables.items():
+            packed[k] = [oracle.nuhc_quantize(xs[i], i, n, mM, b, g, T, w.quant_seed, e_offset=lo)
+                         for i in range(P)]
+        rht = {}
+        for k, (b, g, d, T) in pipe.rht.items():       # blocks of d are the partitions
+            rm = oracle.rht_range(np.stack([oracle.rht_sumsq(x, d) for x in xs]), d, tp)
+            ys = [oracle.clamp(oracle.rht_forward(x, d, w.rht_seed, e0=lo), d, rm) for x in xs]
+            rht[k] = (rm, [oracle.nuhc_quantize(ys[i], i, d, rm, b, g, T, w.quant_seed,
+                                                e_offset=lo) for i in range(P)])
         oracle.ring_fold(xs, op=oracle.AVG, part=w.ring_part_elems and n)
         for b in w.thc_bits:
             S = oracle.int_aggregate(packed[b], n, b)
             xh = oracle.dequant(S, P, b, n, mM, w.dtype)
             oracle.nmse(xs[0], xh)
+        for k, (b, g, T) in pipe.nu_tables.items():
+            Y = oracle.nuhc_aggregate(packed[k], n, b, g, T)
+            oracle.nmse(xs[0], oracle.nuhc_dequant(Y, P, g, n, mM, w.dtype))
+        for k, (b, g, d, T) in pipe.rht.items():
+            rm, pk = rht[k]
+            avg = oracle.nuhc_dequant(oracle.nuhc_aggregate(pk, d, b, g, T), P, g, d, rm)
+            oracle.nmse(xs[0], oracle.rht_inverse(avg, d, w.rht_seed, w.dtype, e0=lo)[:n])
         t_total += time.perf_counter() - t0
         done_elems += n
         used += 1

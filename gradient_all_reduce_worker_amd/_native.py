@@ -26,6 +26,7 @@ EXPORTS = (
     "ga_ring_allreduce_sim", "thc_minmax", "thc_usq_quantize", "thc_int_aggregate",
     "thc_dequant", "thc_nmse", "thc_nmse_ws_bytes", "ga_last_error",
     "thc_nuhc_quantize", "thc_nuhc_aggregate", "thc_nuhc_dequant",
+    "thc_rht_sumsq", "thc_rht_range", "thc_rht_forward", "thc_rht_inverse",
 )
 
 
@@ -78,6 +79,10 @@ def load() -> C.CDLL:
                                     C.POINTER(i32), u64, C.POINTER(vp), vp]
     L.thc_nuhc_aggregate.argtypes = [C.POINTER(vp), i32, i64, i32, i32, C.POINTER(i32), vp, vp]
     L.thc_nuhc_dequant.argtypes = [vp, i64, i32, i32, i64, vp, vp, i32, vp]
+    L.thc_rht_sumsq.argtypes = [C.POINTER(vp), i32, i64, i32, i64, vp, vp]
+    L.thc_rht_range.argtypes = [vp, i32, i64, i64, C.c_double, vp, vp]
+    L.thc_rht_forward.argtypes = [C.POINTER(vp), i32, i64, i32, i64, u64, vp, C.POINTER(vp), vp]
+    L.thc_rht_inverse.argtypes = [vp, i64, i64, u64, vp, i32, vp]
     L.ga_last_error.argtypes = []
     L.ga_last_error.restype = C.c_char_p
     for name in EXPORTS:
@@ -329,6 +334,61 @@ def thc_nuhc_dequant(S: torch.Tensor, N: int, P: int, g: int, mM: torch.Tensor, 
         out = torch.empty(max(N, 1), dtype=out_dtype, device=S.device)
     _check(load().thc_nuhc_dequant(_dev(S, "sum"), N, P, g, part_elems, _dev(mM, "mM"),
                                    _dev(out, "out"), _dt(out), _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------------ randomized Hadamard transform
+def rht_padded(N: int, d: int) -> int:
+    """Length of a transformed vector: N rounded up to whole blocks of d."""
+    return (N + d - 1) // d * d
+
+
+def thc_rht_sumsq(bufs: Sequence[torch.Tensor], d: int, out: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    N = bufs[0].numel()
+    nblk = (N + d - 1) // d
+    if out is None:
+        out = torch.empty((len(bufs), max(nblk, 1)), dtype=torch.float64, device=bufs[0].device)
+    _check(load().thc_rht_sumsq(_ptr_array(bufs, "buffer"), len(bufs), N, _dt(bufs[0]), d,
+                                _dev(out, "sumsq"), _stream(stream)))
+    return out
+
+
+def thc_rht_range(sumsq: torch.Tensor, d: int, t_p: float, out: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """sumsq: (P, nblk) float64 on the device."""
+    P, nblk = sumsq.shape
+    if out is None:
+        out = torch.empty((max(nblk, 1), 2), dtype=torch.float32, device=sumsq.device)
+    _check(load().thc_rht_range(_dev(sumsq, "sumsq"), P, nblk, d, float(t_p), _dev(out, "mM"),
+                                _stream(stream)))
+    return out
+
+
+def thc_rht_forward(bufs: Sequence[torch.Tensor], d: int, seed: int,
+                    mM: Optional[torch.Tensor] = None,
+                    y: Optional[Sequence[torch.Tensor]] = None, stream=None):
+    N = bufs[0].numel()
+    if y is None:
+        y = [torch.empty(max(rht_padded(N, d), 1), dtype=torch.float32, device=bufs[0].device)
+             for _ in bufs]
+    if any(t.dtype != torch.float32 or t.numel() < rht_padded(N, d) for t in y):
+        raise ValueError("y buffers must be float32 with rht_padded(N, d) elements")
+    _check(load().thc_rht_forward(_ptr_array(bufs, "buffer"), len(bufs), N, _dt(bufs[0]), d, seed,
+                                  _dev(mM, "mM") if mM is not None else None,
+                                  _ptr_array(y, "y"), _stream(stream)))
+    return y
+
+
+def thc_rht_inverse(y: torch.Tensor, N: int, d: int, seed: int, out_dtype=torch.float32,
+                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y (rht_padded(N, d) float32) is overwritten when d > 4096."""
+    if out is None:
+        out = torch.empty(max(N, 1), dtype=out_dtype, device=y.device)
+    if y.dtype != torch.float32 or y.numel() < rht_padded(N, d) or out.numel() < N:
+        raise ValueError("y must hold rht_padded(N, d) float32 and out N elements")
+    _check(load().thc_rht_inverse(_dev(y, "y"), N, d, seed, _dev(out, "out"), _dt(out),
+                                  _stream(stream)))
     return out
 
 

@@ -9,14 +9,19 @@ A step runs, in this order, on the current stream:
   flat workloads (one gradient vector per worker):
       THC min/max per partition, USQ quantize for every bit width (both read
       the workers' gradients before the ring overwrites them),
+      for every THC pass behind the randomized Hadamard transform (THC page
+      section 5): per-block norms, the norm-based range, the transform with
+      truncation, the table quantizer on the transformed coordinates,
       ring-average the gradients in place (the exact average),
       then per bit width: integer aggregate, dequantize, NMSE of the THC
-      estimate against the exact average.
+      estimate against the exact average (for RHT passes: table-sum
+      aggregate, dequantize, inverse transform, NMSE).
 
 Only the binding is called; all arithmetic runs in libga.so. Per-call HIP
 events (torch.cuda.Event on the stream the kernels are launched on) time
 every stage when a timer is passed.
 """
+import statistics
 from collections import defaultdict
 from typing import Dict, List, Optional
 
@@ -75,8 +80,14 @@ def worker_buffers(P: int, N: int, dtype, device) -> List[torch.Tensor]:
     return [torch.empty(N, dtype=dtype, device=device) for _ in range(P)]
 
 
+def t_p(p: float) -> float:
+    """Truncation threshold Phi^-1(1 - p/2) of a standard normal."""
+    return statistics.NormalDist().inv_cdf(1.0 - p / 2.0)
+
+
 class Pipeline:
     nu_tables: Dict[str, tuple] = {}
+    rht: Dict[str, tuple] = {}
 
     def __init__(self, name: str, device="cuda", cap_bytes: int = 64 << 20):
         self.w = synth.workload(name)
@@ -126,6 +137,22 @@ class Pipeline:
                 self.S[k] = torch.empty(self.N, dtype=torch.int32, device=dev)
                 self.xhat[k] = torch.empty(self.N, dtype=self.tdt, device=dev)
                 self.nmse[k] = torch.empty(3, dtype=torch.float64, device=dev)
+            # RHT passes, keyed "rht{b}g{g}d{log2 d}"; the quantizer's partitions
+            # are the transform's blocks
+            self.rht = {f"rht{b}g{g}d{k}": (b, g, 1 << k, ga.center_table(b, g))
+                        for b, g, k in w.rht}
+            self.rht_y, self.rht_sumsq, self.rht_mM, self.rht_avg = {}, {}, {}, {}
+            for key, (b, g, d, _) in self.rht.items():
+                Np = ga.rht_padded(self.N, d)
+                self.rht_y[key] = worker_buffers(self.P, Np, torch.float32, dev)
+                self.rht_sumsq[key] = torch.empty((self.P, Np // d), dtype=torch.float64, device=dev)
+                self.rht_mM[key] = torch.empty((Np // d, 2), dtype=torch.float32, device=dev)
+                self.packed[key] = [torch.empty(ga.packed_bytes(Np, b), dtype=torch.uint8,
+                                                device=dev) for _ in range(self.P)]
+                self.S[key] = torch.empty(Np, dtype=torch.int32, device=dev)
+                self.rht_avg[key] = torch.empty(Np, dtype=torch.float32, device=dev)
+                self.xhat[key] = torch.empty(self.N, dtype=self.tdt, device=dev)
+                self.nmse[key] = torch.empty(3, dtype=torch.float64, device=dev)
             self.ws = torch.empty(ga.thc_nmse_ws_bytes(self.N), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 
@@ -149,8 +176,27 @@ class Pipeline:
         for k, (b, g, T) in self.nu_tables.items():
             _call(timer, f"thc_nuhc_quantize_{k}", ga.thc_nuhc_quantize, self.flat, self.mM, b, g, T,
                   w.quant_seed, part, 0, self.packed[k])
+        tp = t_p(w.rht_p)
+        for key, (b, g, d, T) in self.rht.items():
+            _call(timer, f"thc_rht_sumsq_{key}", ga.thc_rht_sumsq, self.flat, d, self.rht_sumsq[key])
+            _call(timer, f"thc_rht_range_{key}", ga.thc_rht_range, self.rht_sumsq[key], d, tp,
+                  self.rht_mM[key])
+            _call(timer, f"thc_rht_forward_{key}", ga.thc_rht_forward, self.flat, d, w.rht_seed,
+                  self.rht_mM[key], self.rht_y[key])
+            _call(timer, f"thc_nuhc_quantize_{key}", ga.thc_nuhc_quantize, self.rht_y[key],
+                  self.rht_mM[key], b, g, T, w.quant_seed, d, 0, self.packed[key])
         _call(timer, "ring_allreduce", ga.ga_ring_allreduce_sim, self.flat, ga.AVG,
               w.ring_part_elems)
+        for key, (b, g, d, T) in self.rht.items():
+            Np = self.rht_avg[key].numel()
+            _call(timer, f"thc_nuhc_aggregate_{key}", ga.thc_nuhc_aggregate, self.packed[key], Np, b,
+                  g, T, self.S[key])
+            _call(timer, f"thc_nuhc_dequant_{key}", ga.thc_nuhc_dequant, self.S[key], Np, self.P, g,
+                  self.rht_mM[key], d, torch.float32, self.rht_avg[key])
+            _call(timer, f"thc_rht_inverse_{key}", ga.thc_rht_inverse, self.rht_avg[key], self.N, d,
+                  w.rht_seed, self.tdt, self.xhat[key])
+            _call(timer, f"thc_nmse_{key}", ga.thc_nmse, self.flat[0], self.xhat[key], self.nmse[key],
+                  self.ws)
         for k, (b, g, T) in self.nu_tables.items():
             _call(timer, f"thc_nuhc_aggregate_{k}", ga.thc_nuhc_aggregate, self.packed[k], self.N, b,
                   g, T, self.S[k])
@@ -188,6 +234,17 @@ class Pipeline:
             out[f"thc_nuhc_aggregate_{k}"] = P * N * b / 8.0 + 4.0 * N
             out[f"thc_nuhc_dequant_{k}"] = 4.0 * N + N * s
             out[f"thc_nmse_{k}"] = 2.0 * N * s
+        for k, (b, g, d, _) in self.rht.items():
+            Np = ga.rht_padded(N, d)
+            nblk = Np // d
+            out[f"thc_rht_sumsq_{k}"] = P * N * s + 8.0 * P * nblk
+            out[f"thc_rht_range_{k}"] = 8.0 * P * nblk + 8.0 * nblk
+            out[f"thc_rht_forward_{k}"] = P * N * s + 4.0 * P * Np
+            out[f"thc_nuhc_quantize_{k}"] = P * Np * (4 + b / 8.0)
+            out[f"thc_nuhc_aggregate_{k}"] = P * Np * b / 8.0 + 4.0 * Np
+            out[f"thc_nuhc_dequant_{k}"] = 8.0 * Np
+            out[f"thc_rht_inverse_{k}"] = 4.0 * Np + N * s
+            out[f"thc_nmse_{k}"] = 2.0 * N * s
         return out
 
     # ------------------------------------------------------------ sampling
@@ -216,5 +273,26 @@ class Pipeline:
                                   for i in range(self.P)]
                 d["xhat"][b] = synth.to_numpy_bits(self.xhat[b][lo:hi])
                 d["S"][b] = self.S[b][lo:hi].cpu().numpy().copy()
+            for k, (b, g, _) in self.nu_tables.items():
+                bl, bh = lo * b // 8, (hi * b + 7) // 8
+                d["packed"][k] = [self.packed[k][i][bl:bh].cpu().numpy().copy()
+                                  for i in range(self.P)]
+                d["xhat"][k] = synth.to_numpy_bits(self.xhat[k][lo:hi])
+                d["S"][k] = self.S[k][lo:hi].cpu().numpy().copy()
             out[p] = d
+        return out
+
+    def sample_rht_outputs(self, key: str, which: List[int]) -> Dict[int, dict]:
+        """Block p of an RHT pass: its range, every worker's packed indices
+        (whole block, padding included), the table sums and the estimate."""
+        b, g, d, _ = self.rht[key]
+        out = {}
+        for p in which:
+            lo, hi = p * d, min((p + 1) * d, self.N)
+            bl, bh = lo * b // 8, (lo + d) * b // 8
+            out[p] = {"mM": self.rht_mM[key][p].cpu().numpy().copy(),
+                      "packed": [self.packed[key][i][bl:bh].cpu().numpy().copy()
+                                 for i in range(self.P)],
+                      "S": self.S[key][lo:lo + d].cpu().numpy().copy(),
+                      "xhat": synth.to_numpy_bits(self.xhat[key][lo:hi])}
         return out

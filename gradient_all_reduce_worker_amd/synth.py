@@ -116,6 +116,10 @@ class Workload:
     ring_part_elems: int = 0
     thc_bits: Tuple[int, ...] = ()
     nuhc: Tuple[Tuple[int, int], ...] = ()   # (b, g) of non-uniform THC passes
+    # (b, g, log2 d) of THC passes behind the randomized Hadamard transform;
+    # a fraction rht_p of the transformed coordinates is expected to be cut
+    rht: Tuple[Tuple[int, int, int], ...] = ()
+    rht_p: float = 1.0 / 32
     fused: bool = True              # run the Tensor Fusion plan over `sizes`
 
     @property
@@ -129,6 +133,10 @@ class Workload:
     @property
     def quant_seed(self) -> int:
         return 2000 + self.index
+
+    @property
+    def rht_seed(self) -> int:
+        return 3000 + self.index
 
     @property
     def elem_bytes(self) -> int:
@@ -160,7 +168,7 @@ def workload(name: str) -> Workload:
         names, sizes = _rev(vgg16_shapes())
         return Workload("vgg16", 3, P=32, dtype=F32, sizes=sizes, names=names,
                         dist="normal_logsigma", part_elems=1 << 20, ring_part_elems=1 << 20,
-                        thc_bits=(4, 8), nuhc=((4, 36),), fused=False)
+                        thc_bits=(4, 8), nuhc=((4, 36),), rht=((4, 36, 20),), fused=False)
     if name == "shard":
         return Workload("shard", 4, P=8, dtype=BF16, sizes=[1 << 31], names=["shard"],
                         dist="laplace", part_elems=1 << 20, ring_part_elems=1 << 20,

@@ -9,6 +9,10 @@
  *                                                  THC uniform quantization
  *   thc_nuhc_quantize / thc_nuhc_aggregate / thc_nuhc_dequant
  *                                                  THC with lookup tables
+ *   thc_rht_sumsq / thc_rht_range / thc_rht_forward / thc_rht_inverse
+ *                                                  randomized Hadamard
+ *                                                  transform, norm-based
+ *                                                  range, truncation
  *
  * Pages cited:
  *   [HVD]  "Horovod: Fast and Easy Distributed Deep Learning in TensorFlow"
@@ -17,7 +21,9 @@
  *          sections 4, 5 and 7 (schedule, volume, simulator).
  *   [THC]  "THC: Accelerating Distributed Deep Learning Using Tensor
  *          Homomorphic Compression", sections 2-4 (NMSE, uniform THC,
- *          Algorithm 1, aggregation by the server) and 8 (aggregate width).
+ *          Algorithm 1, aggregation by the server), 4 (Algorithm 2), 5
+ *          (randomized Hadamard transform, truncation, norm-based range)
+ *          and 8 (aggregate width).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -278,6 +284,69 @@ ga_status thc_nuhc_aggregate(const uint8_t* const* packed, int32_t P, int64_t N,
 ga_status thc_nuhc_dequant(const int32_t* d_sum, int64_t N, int32_t P, int32_t g,
                            int64_t part_elems, const float* d_mM, void* out, ga_dtype out_dt,
                            void* stream);
+
+/* ------------------------------------------------------------------ */
+/* Randomized Hadamard transform  ([THC] section 5)                    */
+/* ------------------------------------------------------------------ */
+
+/*
+ * A vector of N coordinates is cut into blocks of d = 2^k coordinates
+ * (2 <= d <= 2^22); a last, partial block is zero-padded, so a transformed
+ * vector holds Np = ceil(N / d) d binary32 values. Block p covers
+ * coordinates [p d, (p + 1) d).
+ *
+ * Forward:  y = (1/sqrt(d)) H D x,  inverse:  x = (1/sqrt(d)) D H y, with H
+ * the d x d Walsh-Hadamard matrix (H H = d I) and D a diagonal of random
+ * signs shared by every worker (seeded; the same seed must reach both
+ * directions). H is applied as the radix-2 butterfly: stage s = 0 .. k-1
+ * maps every pair (i, i + 2^s), bit s of i clear, to (a + b, a - b) in
+ * binary32; the result is then multiplied by c = fl32(1/sqrt(d)). Results
+ * are bit-exact against that loop (the pairing inside a stage does not
+ * change any rounding).
+ * Signs: Philox4x32-10 keyed by seed (low word first), counter
+ * (q mod 2^32, q >> 32, 0x52485400, 0) with q = e / 128; coordinate e is
+ * negated when bit e mod 32 of output word (e / 32) mod 4 is set.
+ */
+
+/*
+ * thc_rht_sumsq -- per-block squared norms of the P worker vectors:
+ * d_sumsq[i nblk + p] = sum over the coordinates of block p of x_i[e]^2,
+ * binary64 (each square is exact there; the order of the additions is a
+ * tree, so results may differ from a sequential sum in the last bits).
+ * nblk = ceil(N / d); d_sumsq is a device array of P nblk doubles.
+ */
+ga_status thc_rht_sumsq(const void* const* bufs, int32_t P, int64_t N, ga_dtype dt, int64_t d,
+                        double* d_sumsq, void* stream);
+
+/*
+ * thc_rht_range -- the norm-based range of every block, shared by all
+ * workers: l_p = sqrt(max over i of d_sumsq[i nblk + p]) (the largest
+ * worker norm; the page's "squared norm" is read as the norm, the only
+ * reading with the units of a coordinate), M = fl32(t_p l_p / sqrt(d))
+ * computed in binary64, m = -M. d_mM receives nblk (m, M) pairs. t_p > 0,
+ * normally the standard normal quantile Phi^-1(1 - p/2) of the fraction p
+ * of coordinates allowed to fall outside the range.
+ */
+ga_status thc_rht_range(const double* d_sumsq, int32_t P, int64_t nblk, int64_t d, double t_p,
+                        float* d_mM, void* stream);
+
+/*
+ * thc_rht_forward -- y_i = RHT(x_i) for P workers (x fp32 or bf16, N
+ * coordinates; y_i device buffers of Np binary32, written in full). With
+ * d_mM non-NULL each y coordinate of block p is then truncated to
+ * [m_p, M_p] (d_mM as from thc_rht_range): the truncation step of THC's
+ * RHT variant. y must not overlap x.
+ */
+ga_status thc_rht_forward(const void* const* bufs, int32_t P, int64_t N, ga_dtype dt, int64_t d,
+                          uint64_t seed, const float* d_mM, float* const* y, void* stream);
+
+/*
+ * thc_rht_inverse -- out = RHT^-1(y) for one vector: y holds Np binary32
+ * (device; used as scratch and overwritten when d > 4096), out receives the
+ * first N coordinates as fp32 or bf16 (round to nearest even).
+ */
+ga_status thc_rht_inverse(float* y, int64_t N, int64_t d, uint64_t seed, void* out,
+                          ga_dtype out_dt, void* stream);
 
 /* Thread-local message describing the last failure on this thread. */
 const char* ga_last_error(void);

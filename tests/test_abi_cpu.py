@@ -27,7 +27,7 @@ def _declared():
 def test_header_declarations_are_exported():
     L = nat.load()
     names = _declared()
-    assert len(names) == 15
+    assert len(names) == 19
     assert set(names) == set(nat.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -152,10 +152,37 @@ def test_nuhc_table_errors_before_enqueue():
     T = (C.c_int32 * 4)(0, 1, 3, 4)
     bad = (C.c_int32 * 4)(0, 3, 3, 4)
     q = L.thc_nuhc_quantize
-    assert q(good, 4, 0, 16, 0, 0, 0x50000, 2, 4, T, 1, good, None) != EINVAL or True
     assert q(good, 4, 0, 16, 0, 0, 0x50000, 2, 4, bad, 1, good, None) == EINVAL
     assert q(good, 4, 0, 16, 0, 0, 0x50000, 2, 2, T, 1, good, None) == EINVAL      # g < 2^b - 1
     big = (C.c_int32 * 4)(0, 1, 2, 5000)
     assert q(good, 4, 0, 16, 0, 0, 0x50000, 2, 5000, big, 1, good, None) == ENOTSUP
     assert L.thc_nuhc_aggregate(good, 4, 16, 2, 4, bad, 0x60000, None) == EINVAL
     assert L.thc_nuhc_dequant(0x60000, 16, 4, 0, 0, 0x50000, 0x70000, 0, None) == EINVAL
+
+
+def test_rht_argument_errors_before_enqueue():
+    L = nat.load()
+    good = _ptrs([0x10000 * (i + 1) for i in range(4)])
+    ys = _ptrs([0x100000 * (i + 1) for i in range(4)])
+    fwd = L.thc_rht_forward
+    for d in (0, 1, 3, 6, 1 << 23, -4):                                        # not 2^k in [2, 2^22]
+        assert fwd(good, 4, 16, 0, d, 1, None, ys, None) == EINVAL
+        assert L.thc_rht_sumsq(good, 4, 16, 0, d, 0x60000, None) == EINVAL
+        assert L.thc_rht_range(0x60000, 4, 2, d, 2.0, 0x70000, None) == EINVAL
+        assert L.thc_rht_inverse(0x60000, 16, d, 1, 0x70000, 0, None) == EINVAL
+    assert fwd(good, 0, 16, 0, 8, 1, None, ys, None) == EINVAL                  # P = 0
+    assert fwd(good, 4, -1, 0, 8, 1, None, ys, None) == EINVAL                  # N < 0
+    assert fwd(good, 4, 16, 2, 8, 1, None, ys, None) == EINVAL                  # dtype
+    assert fwd(good, 4, 16, 0, 8, 1, 0x50004, ys, None) == EINVAL               # misaligned mM
+    assert fwd(good, 4, 16, 0, 8, 1, None, _ptrs([0x100000, 0, 0x300000, 0x400000]), None) == EINVAL
+    assert fwd(good, 4, 0, 0, 8, 1, None, ys, None) == 0                        # empty
+    assert L.thc_rht_sumsq(good, 4, 16, 0, 8, 0x60004, None) == EINVAL          # misaligned sums
+    for t_p in (0.0, -1.0, float("nan"), float("inf")):
+        assert L.thc_rht_range(0x60000, 4, 2, 8, t_p, 0x70000, None) == EINVAL
+    assert L.thc_rht_range(0x60000, 65, 2, 8, 2.0, 0x70000, None) == EINVAL      # P > 64
+    assert L.thc_rht_range(0x60000, 4, 0, 8, 2.0, 0x70000, None) == 0           # no blocks
+    assert L.thc_rht_inverse(0x60002, 16, 8, 1, 0x70000, 0, None) == EINVAL     # misaligned y
+    assert L.thc_rht_inverse(0x60000, 16, 8, 1, 0x70001, 1, None) == EINVAL     # misaligned bf16 out
+    assert L.thc_rht_inverse(0x60000, 0, 8, 1, 0x70000, 0, None) == 0
+    assert L.thc_rht_inverse(0x60002, 16, 8, 1, 0x70000, 0, None) == EINVAL
+    assert b"thc_rht_inverse" in L.ga_last_error()

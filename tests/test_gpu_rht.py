@@ -1,0 +1,163 @@
+"""GPU parity for THC's randomized Hadamard transform step (THC page,
+section 5): per-block norms, the norm-based range, the forward transform
+with truncation and the inverse, against the oracle -- bit for bit except
+the binary64 sums of squares, whose addition order differs (tree against
+sequential) and which are held to a relative 1e-12."""
+import statistics
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gradient_all_reduce_worker_amd import _native as ga
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+SEED = 0x0DDB_A11C_0FFE_E123
+
+
+def _inputs(P, N, dt, seed, scale=0.01):
+    rng = np.random.default_rng(seed)
+    t = torch.from_numpy((rng.standard_normal((P, N)) * scale).astype(np.float32))
+    if dt == ga.BF16:
+        t = t.to(torch.bfloat16)
+    return [t[i].clone().to(DEV) for i in range(P)]
+
+
+def _host(t):
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.numpy().copy()
+
+
+def _bits(a):
+    return np.ascontiguousarray(a).view(np.uint32)
+
+
+# one tile per block (d <= 4096, several blocks per tile), two passes (d > 4096),
+# ragged tails, a single partial block, the largest d
+SHAPES = [(2, 2, 7), (3, 8, 1001), (2, 128, 300), (4, 256, 5000), (2, 4096, 3 * 4096 + 5),
+          (3, 8192, 2 * 8192 - 3), (2, 1 << 14, (1 << 14) + 77), (2, 1 << 16, 70000),
+          (2, 1 << 20, (1 << 21) + 12345), (1, 1 << 22, (1 << 22) + 5), (2, 1 << 12, 100)]
+
+
+@pytest.mark.parametrize("dt", [ga.F32, ga.BF16])
+@pytest.mark.parametrize("P,d,N", SHAPES)
+def test_forward_inverse_bit_exact(P, d, N, dt):
+    bufs = _inputs(P, N, dt, seed=N + d)
+    y = ga.thc_rht_forward(bufs, d, SEED)
+    Np = ga.rht_padded(N, d)
+    for i in range(P):
+        want = oracle.rht_forward(_host(bufs[i]), d, SEED)
+        assert want.size == Np
+        assert np.array_equal(_bits(y[i].cpu().numpy()[:Np]), _bits(want)), i
+    # inverse of an oracle-made vector, written as fp32 and as bf16
+    yo = oracle.rht_forward(_host(bufs[0]), d, SEED)
+    for out_dt, tdt in ((ga.F32, torch.float32), (ga.BF16, torch.bfloat16)):
+        yd = torch.from_numpy(yo.copy()).to(DEV)
+        out = ga.thc_rht_inverse(yd, N, d, SEED, out_dtype=tdt)
+        want = oracle.rht_inverse(yo, d, SEED, out_dt)[:N]
+        assert np.array_equal(_host(out)[:N], want), out_dt
+
+
+@pytest.mark.parametrize("P,d,N", [(3, 8, 1001), (4, 4096, 3 * 4096 + 5), (2, 1 << 16, 70000),
+                                   (2, 1 << 20, (1 << 21) + 12345)])
+def test_truncation_and_range(P, d, N):
+    bufs = _inputs(P, N, ga.F32, seed=7 * N)
+    xs = [_host(b) for b in bufs]
+    t_p = statistics.NormalDist().inv_cdf(1 - 1 / 64)
+    S = ga.thc_rht_sumsq(bufs, d)
+    Sw = np.stack([oracle.rht_sumsq(x, d) for x in xs])
+    np.testing.assert_allclose(S.cpu().numpy(), Sw, rtol=1e-12, atol=0)
+    # the range from the oracle's sums: bit for bit
+    mM = ga.thc_rht_range(torch.from_numpy(Sw).to(DEV), d, t_p)
+    mMw = oracle.rht_range(Sw, d, t_p)
+    assert np.array_equal(_bits(mM.cpu().numpy()), _bits(mMw))
+    y = ga.thc_rht_forward(bufs, d, SEED, mM=mM)
+    clipped = 0
+    for i in range(P):
+        yo = oracle.rht_forward(xs[i], d, SEED)
+        yc = oracle.clamp(yo, d, mMw)
+        clipped += int(np.count_nonzero(yc != yo))
+        assert np.array_equal(_bits(y[i].cpu().numpy()), _bits(yc)), i
+    assert clipped > 0                 # the truncation did act on these inputs
+
+
+def test_sumsq_and_range_edge_cases():
+    d = 1 << 10
+    # a zero vector gives a zero range; a single non-zero coordinate its magnitude
+    z = [torch.zeros(3 * d, device=DEV), torch.zeros(3 * d, device=DEV)]
+    z[1][d + 5] = -3.0
+    S = ga.thc_rht_sumsq(z, d)
+    assert S.cpu().numpy().tolist() == [[0.0, 0.0, 0.0], [0.0, 9.0, 0.0]]
+    mM = ga.thc_rht_range(S, d, 2.0).cpu().numpy()
+    assert mM[0].tolist() == [0.0, 0.0] and mM[2].tolist() == [0.0, 0.0]
+    assert mM[1, 1] == np.float32(2.0 * 3.0 / 32.0) and mM[1, 0] == -mM[1, 1]
+    # bf16 input, N not a multiple of d
+    bufs = _inputs(2, 2 * d + 3, ga.BF16, seed=4)
+    S = ga.thc_rht_sumsq(bufs, d).cpu().numpy()
+    Sw = np.stack([oracle.rht_sumsq(_host(b), d) for b in bufs])
+    np.testing.assert_allclose(S, Sw, rtol=1e-12, atol=0)
+
+
+def test_empty_is_noop():
+    e = [torch.empty(0, device=DEV)]
+    ga.thc_rht_forward(e, 16, SEED, y=[torch.zeros(1, device=DEV)])
+    ga.thc_rht_sumsq(e, 16)
+    ga.thc_rht_inverse(torch.zeros(16, device=DEV), 0, 16, SEED, out=torch.zeros(1, device=DEV))
+    torch.cuda.synchronize()
+
+
+def test_inverse_undoes_forward():
+    """(1/d) H H = I: the round trip returns x within binary32 rounding."""
+    d, N = 1 << 16, 3 * (1 << 16) - 11
+    x = _inputs(1, N, ga.F32, seed=12)
+    y = ga.thc_rht_forward(x, d, SEED)[0]
+    back = ga.thc_rht_inverse(y, N, d, SEED)
+    err = (back - x[0]).abs().max().item()
+    assert err <= 64 * np.finfo(np.float32).eps * x[0].abs().max().item()
+
+
+@pytest.mark.parametrize("b", [2, 4, 8])
+@pytest.mark.parametrize("P,d,N", [(4, 1 << 12, 50001), (3, 1 << 16, 3 * (1 << 16) + 999)])
+def test_full_rht_chain_matches_oracle(P, d, N, b):
+    """Norms -> range -> forward + truncation -> uniform THC on the
+    transformed coordinates (one partition per block) -> integer sum ->
+    average -> inverse, against the same chain in the oracle."""
+    bufs = _inputs(P, N, ga.F32, seed=N + b)
+    xs = [_host(t) for t in bufs]
+    t_p = statistics.NormalDist().inv_cdf(1 - 1 / 64)
+    qseed = 0xA5A5_0000_1234 + b
+    Np = ga.rht_padded(N, d)
+
+    S = ga.thc_rht_sumsq(bufs, d)
+    mM = ga.thc_rht_range(S, d, t_p)
+    y = ga.thc_rht_forward(bufs, d, SEED, mM=mM)
+    packed = ga.thc_usq_quantize(y, mM, b, qseed, part_elems=d)
+    Y = ga.thc_int_aggregate(packed, Np, b)
+    avg = ga.thc_dequant(Y, Np, P, b, mM, part_elems=d)
+    out = ga.thc_rht_inverse(avg, N, d, SEED)
+
+    Sw = np.stack([oracle.rht_sumsq(x, d) for x in xs])
+    mMw = oracle.rht_range(Sw, d, t_p)
+    # the two sums differ in their last bits at most; the range rounds them
+    # to binary32, where these seeded inputs agree
+    assert np.array_equal(_bits(mM.cpu().numpy()), _bits(mMw))
+    want_packed = []
+    for i in range(P):
+        yc = oracle.clamp(oracle.rht_forward(xs[i], d, SEED), d, mMw)
+        wp = oracle.usq_quantize(yc, i, d, mMw, b, qseed)
+        assert np.array_equal(packed[i].cpu().numpy(), wp), i
+        want_packed.append(wp)
+    Yw = oracle.int_aggregate(want_packed, Np, b)
+    assert np.array_equal(Y.cpu().numpy()[:Np], Yw)
+    avgw = oracle.dequant(Yw, P, b, d, mMw)
+    outw = oracle.rht_inverse(avgw, d, SEED)[:N]
+    assert np.array_equal(_bits(out.cpu().numpy()[:N]), _bits(outw))
+    # and the estimate is close to the true average (unbiased quantizer;
+    # error shrinks with b)
+    mean = np.mean(np.stack(xs), axis=0, dtype=np.float64)
+    nm = oracle.nmse(mean.astype(np.float32), outw)[2]
+    assert nm < {2: 0.6, 4: 0.05, 8: 0.02}[b]

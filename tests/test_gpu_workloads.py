@@ -17,7 +17,7 @@ import torch
 import oracle
 from gradient_all_reduce_worker_amd import _native as ga
 from gradient_all_reduce_worker_amd import synth
-from gradient_all_reduce_worker_amd.pipeline import Pipeline
+from gradient_all_reduce_worker_amd.pipeline import Pipeline, t_p
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +33,7 @@ def _free_memory():
     torch.cuda.empty_cache()
 
 
-def _check_partition(w, P, lo, xs, got):
+def _check_partition(w, P, lo, xs, got, nu_tables=None):
     """Oracle on one partition [lo, lo + n) of a flat workload."""
     n = xs[0].size
     xs = [x.copy() for x in xs]
@@ -45,6 +45,11 @@ def _check_partition(w, P, lo, xs, got):
                      for i in range(P)]
         for i in range(P):
             assert np.array_equal(got["packed"][b][i], packed[b][i]), (b, i)
+    for k, (b, g, T) in (nu_tables or {}).items():
+        packed[k] = [oracle.nuhc_quantize(xs[i], i, n, mM, b, g, T, w.quant_seed, e_offset=lo)
+                     for i in range(P)]
+        for i in range(P):
+            assert np.array_equal(got["packed"][k][i], packed[k][i]), (k, i)
     oracle.ring_fold(xs, op=oracle.AVG, part=n)
     for i in range(P):
         assert np.array_equal(_u(got["ring"][i]), _u(xs[i])), i
@@ -53,10 +58,36 @@ def _check_partition(w, P, lo, xs, got):
         assert np.array_equal(got["S"][b], S)
         xh = oracle.dequant(S, P, b, n, mM, w.dtype)
         assert np.array_equal(_u(got["xhat"][b]), _u(xh))
+    for k, (b, g, T) in (nu_tables or {}).items():
+        Y = oracle.nuhc_aggregate(packed[k], n, b, g, T)
+        assert np.array_equal(got["S"][k], Y), k
+        xh = oracle.nuhc_dequant(Y, P, g, n, mM, w.dtype)
+        assert np.array_equal(_u(got["xhat"][k]), _u(xh)), k
+
+
+def _check_rht_block(pipe, key, p, xs, got):
+    """Oracle on block p of an RHT pass: norms, range, transform with
+    truncation, table quantizer, table sums, dequant, inverse."""
+    b, g, d, T = pipe.rht[key]
+    w, P, lo = pipe.w, pipe.P, p * d
+    S2 = np.stack([oracle.rht_sumsq(x, d) for x in xs])
+    mM = oracle.rht_range(S2, d, t_p(w.rht_p))
+    # binary64 sums in another order, rounded to the same binary32 range
+    assert np.array_equal(got["mM"].view(np.uint32), mM[0].view(np.uint32)), key
+    packed = []
+    for i in range(P):
+        y = oracle.clamp(oracle.rht_forward(xs[i], d, w.rht_seed, e0=lo), d, mM)
+        packed.append(oracle.nuhc_quantize(y, i, d, mM, b, g, T, w.quant_seed, e_offset=lo))
+        assert np.array_equal(got["packed"][i], packed[i]), (key, i)
+    Y = oracle.nuhc_aggregate(packed, d, b, g, T)
+    assert np.array_equal(got["S"], Y), key
+    avg = oracle.nuhc_dequant(Y, P, g, d, mM)
+    xh = oracle.rht_inverse(avg, d, w.rht_seed, w.dtype, e0=lo)[:xs[0].size]
+    assert np.array_equal(_u(got["xhat"]), _u(xh)), key
 
 
 def _nmse_property(pipe, slab=1 << 26):
-    for b in pipe.w.thc_bits:
+    for b in pipe.xhat:
         num = den = 0.0
         for lo in range(0, pipe.N, slab):
             x = pipe.flat[0][lo:lo + slab].double()
@@ -81,7 +112,12 @@ def test_flat_workload_sampled(name):
     after = pipe.sample_outputs(which)
     plen = pipe.w.part_elems
     for p in which:
-        _check_partition(pipe.w, pipe.P, p * plen, before[p], after[p])
+        _check_partition(pipe.w, pipe.P, p * plen, before[p], after[p], pipe.nu_tables)
+    for key, (_, _, d, _) in pipe.rht.items():
+        assert d == plen                    # RHT blocks are the sampled partitions
+        got = pipe.sample_rht_outputs(key, which)
+        for p in which:
+            _check_rht_block(pipe, key, p, before[p], got[p])
     # all workers end with identical averages (sampled: every worker's first
     # and last partition were compared above; here, whole buffers on device)
     for i in range(1, pipe.P):
