@@ -6,16 +6,23 @@
 //
 // The transform is the textbook radix-2 one: stage s = 0 .. k-1 turns every
 // pair (i, i + 2^s), bit s of i clear, into (a + b, a - b) in binary32, and
-// the result is scaled by fl32(1/sqrt(d)) at the end. Two passes keep every
-// stage in LDS:
-//  * tile pass: a workgroup loads 4096 consecutive coordinates (16 KiB;
-//    several whole blocks when d < 4096) and runs stages 0 .. log2(T) - 1,
-//    T = min(d, 4096);
-//  * cross pass (d > T only): a workgroup loads a G x W sub-matrix of one
-//    block (G = d / T rows spaced T apart, W = 4096 / G consecutive
-//    columns) and runs the remaining stages along the rows.
-// Each stage pairs the same elements in the same order as the plain loop,
-// so the output is bit-for-bit that loop's.
+// the result is scaled by fl32(1/sqrt(d)) at the end. Stages on different
+// bits do not commute in floating point, so they run strictly in that order.
+//
+// Layout of the work (512-thread workgroups, an 8192-coordinate tile of
+// 32 KiB in LDS, padded by one word per 16 against bank conflicts; three
+// workgroups fit a CU, so one loads while another computes):
+//  * tile pass: a workgroup loads 8192 consecutive coordinates (several
+//    whole blocks when d < 8192) and runs stages 0 .. log2(T) - 1 with
+//    T = min(d, 8192);
+//  * cross pass (d > 8192 only): a workgroup loads a G x W sub-matrix of
+//    one block (G = d / 8192 rows spaced 8192 apart, W = 8192 / G >= 16
+//    consecutive columns) and runs the remaining stages along the rows.
+// Inside a pass, stages go four at a time through registers: every thread
+// takes the 16 coordinates that differ only in four consecutive index bits,
+// runs the stages on those bits, and writes them back (one LDS round trip
+// per four stages). Each butterfly adds and subtracts the same two values
+// as the plain loop, so the output is bit-for-bit that loop's.
 //
 // The Rademacher signs come from Philox4x32-10: key (seed), counter
 // (q mod 2^32, q >> 32, 0x52485400, 0) with q = e / 128; coordinate e takes
@@ -29,9 +36,17 @@
 namespace ga {
 namespace {
 
-constexpr int kTile = 4096;                 // coordinates per LDS tile
-constexpr int kMaxRows = 1024;              // cross-pass rows: d <= kTile * kMaxRows = 2^22
+constexpr int kTileBits = 13;
+constexpr int kTile = 1 << kTileBits;       // coordinates per LDS tile
+constexpr int kTT = 512;                    // threads per transform workgroup
+constexpr int kPer = kTile / kTT;           // coordinates per thread (16)
+constexpr int kLds = kTile + kTile / 16;    // padded tile, in words
+constexpr int kMaxBits = 22;                // d <= 2^22: G <= 512, W >= 16
+constexpr int kSignWords = 4 * 512;         // Philox blocks a workgroup may need, x 4
+static_assert(kPer == 16, "one set of 16 coordinates per thread and group");
 constexpr uint32_t kSignDomain = 0x52485400u;
+
+__device__ __forceinline__ int pad(int i) { return i + (i >> 4); }
 
 __device__ __forceinline__ float load_coord(const void* x, int64_t e, int64_t N, ga_dtype dt) {
     if (e >= N) return 0.0f;                 // zero padding to a whole block
@@ -39,25 +54,63 @@ __device__ __forceinline__ float load_coord(const void* x, int64_t e, int64_t N,
     return static_cast<const float*>(x)[e];
 }
 
-// Butterflies on pairs (i, i + h), bit h of i clear, for h = h0, 2 h0, ...
-// while h < h1, over the n coordinates in LDS; a barrier after each stage.
-__device__ __forceinline__ void lds_stages(float* s, int n, int h0, int h1) {
-    for (int h = h0; h < h1; h <<= 1) {
-        for (int q = threadIdx.x; q < n / 2; q += kThreads) {
-            const int i = ((q & ~(h - 1)) << 1) | (q & (h - 1));
-            const float a = s[i], b = s[i + h];
-            s[i] = a + b;
-            s[i + h] = a - b;
+// Stages on index bits lo .. hi-1 of the tile in LDS (WB <= lo < hi <= WB + 4,
+// WB <= kTileBits - 4): thread o takes the 16 coordinates whose index bits
+// WB .. WB+3 vary and whose other bits spell o. With WB fixed at compile
+// time the 16 LDS addresses are one register plus immediate offsets.
+template <int WB>
+__device__ __forceinline__ void group16(float* s, int lo, int hi) {
+    const int o = threadIdx.x;
+    const int base = ((o >> WB) << (WB + 4)) | (o & ((1 << WB) - 1));
+    float* p = s + pad(base);
+    // pad(base + (r << WB)) - pad(base): bits WB.. of base are clear
+    constexpr int step = WB >= 4 ? (1 << WB) + (1 << (WB - 4)) : 1;
+    float v[16];
+#pragma unroll
+    for (int r = 0; r < 16; r++) v[r] = p[r * step];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        if (WB + q >= lo && WB + q < hi) {
+            const int h = 1 << q;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                if (!(r & h)) {
+                    const float a = v[r], b = v[r | h];
+                    v[r] = a + b;
+                    v[r | h] = a - b;
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; r++) p[r * step] = v[r];
+}
+
+// Stages on index bits lo .. hi-1, four at a time, a barrier after each group.
+__device__ __forceinline__ void stages(float* s, int lo, int hi) {
+    for (int b0 = lo; b0 < hi; b0 += 4) {
+        const int wb = b0 < kTileBits - 4 ? b0 : kTileBits - 4;
+        const int h = b0 + 4 < hi ? b0 + 4 : hi;
+        switch (wb) {
+            case 0: group16<0>(s, b0, h); break;
+            case 1: group16<1>(s, b0, h); break;
+            case 2: group16<2>(s, b0, h); break;
+            case 3: group16<3>(s, b0, h); break;
+            case 4: group16<4>(s, b0, h); break;
+            case 5: group16<5>(s, b0, h); break;
+            case 6: group16<6>(s, b0, h); break;
+            case 7: group16<7>(s, b0, h); break;
+            case 8: group16<8>(s, b0, h); break;
+            default: group16<kTileBits - 4>(s, b0, h); break;
         }
         __syncthreads();
     }
 }
 
-// Philox blocks q0 .. q0 + nq - 1 of the sign stream into LDS (nq <= 4 kThreads
-// words handled: each thread computes at most one block).
+// Philox blocks q0 .. q0 + nq - 1 of the sign stream into LDS.
 __device__ __forceinline__ void sign_blocks(uint32_t* words, int64_t q0, int nq, uint32_t k0,
                                             uint32_t k1) {
-    for (int t = threadIdx.x; t < nq; t += kThreads) {
+    for (int t = threadIdx.x; t < nq; t += kTT) {
         const uint64_t q = (uint64_t)(q0 + t);
         const Philox4 r = philox4x32_10((uint32_t)q, (uint32_t)(q >> 32), kSignDomain, 0u, k0, k1);
         words[4 * t + 0] = r.v[0];
@@ -67,9 +120,10 @@ __device__ __forceinline__ void sign_blocks(uint32_t* words, int64_t q0, int nq,
     }
 }
 
-__device__ __forceinline__ float sign_of(const uint32_t* words, int64_t q0, int64_t e) {
-    const uint32_t w = words[4 * ((e >> 7) - q0) + ((e >> 5) & 3)];
-    return ((w >> (e & 31)) & 1u) ? -1.0f : 1.0f;
+// Sign bit of a coordinate from its Philox block (index blk in words) and
+// any integer congruent to its index modulo 128.
+__device__ __forceinline__ bool negated(const uint32_t* words, int blk, int e) {
+    return (words[4 * blk + ((e >> 5) & 3)] >> (e & 31)) & 1u;
 }
 
 __device__ __forceinline__ float clamp_to(float v, const float* mM, int64_t p) {
@@ -77,67 +131,106 @@ __device__ __forceinline__ float clamp_to(float v, const float* mM, int64_t p) {
     return v < m ? m : (v > M ? M : v);
 }
 
-// ---------------------------------------------------------------- forward
+
+// ---------------------------------------------------------------- tile pass
+
+// Coordinate e0 + i of a worker's input: x (fp32 or bf16) for the forward
+// transform, the fp32 transformed vector for the inverse.
+template <bool FWD, ga_dtype DT>
+__device__ __forceinline__ float load_tile(const void* x, int64_t e0, int i) {
+    if (FWD && DT == GA_BF16)
+        return __uint_as_float((uint32_t)(static_cast<const uint16_t*>(x) + e0)[i] << 16);
+    return (static_cast<const float*>(x) + e0)[i];
+}
 
 // Tile pass over n = min(kTile, Np - e0) consecutive coordinates (a whole
 // number of blocks when d < kTile, one tile of a block otherwise): stages
-// h = 1 .. T/2 with T = min(d, kTile). FINAL (d <= kTile): scale, clamp when
-// mM is given, store; else store the partial transform for the cross pass.
-template <ga_dtype DT, bool FINAL>
-__global__ __launch_bounds__(kThreads) void rht_fwd_tile_kernel(PtrTable x, PtrTable y, int64_t N,
-                                                                int64_t Np, int T, int64_t d,
-                                                                uint32_t k0, uint32_t k1, float c,
-                                                                const float* __restrict__ mM) {
-    __shared__ float s[kTile];
+// 0 .. kbits-1, kbits = log2(min(d, kTile)).
+// FWD: apply the signs on load; else (inverse) on the final store.
+// FINAL (d <= kTile): scale, then clamp (forward, mM given) or sign
+// (inverse) and store; else store the partial transform for the cross pass.
+template <bool FWD, bool FINAL, ga_dtype DT>
+__global__ __launch_bounds__(kTT) void rht_tile_kernel(PtrTable x, PtrTable y, int64_t N, int64_t Np,
+                                                       int kbits, uint32_t k0, uint32_t k1, float c,
+                                                       const float* __restrict__ mM) {
+    __shared__ float s[kLds];
     __shared__ uint32_t words[4 * (kTile / 128)];
     const int w = blockIdx.y;
-    const int64_t e0 = (int64_t)blockIdx.x * kTile;
-    const int n = (int)min((int64_t)kTile, Np - e0);
-    const int64_t q0 = e0 >> 7;
-    sign_blocks(words, q0, (n + 127) / 128, k0, k1);
-    __syncthreads();
-    const void* xw = x.p[w];
-    for (int i = threadIdx.x; i < n; i += kThreads)
-        s[i] = sign_of(words, q0, e0 + i) * load_coord(xw, e0 + i, N, DT);
-    __syncthreads();
-    lds_stages(s, n, 1, T);
-    float* yw = static_cast<float*>(y.p[w]);
-    for (int i = threadIdx.x; i < n; i += kThreads) {
-        float v = s[i];
-        if (FINAL) {
-            v = v * c;
-            if (mM) v = clamp_to(v, mM, (e0 + i) / d);
+    const int64_t e0 = (int64_t)blockIdx.x * kTile;  // a multiple of 128
+    const int n = (int)min((int64_t)kTile, Np - e0);  // coordinates of this tile
+    const int nx = (int)max((int64_t)0, min((int64_t)kTile, N - e0));   // ... that exist in x
+    if (FWD || FINAL) sign_blocks(words, e0 >> 7, (n + 127) >> 7, k0, k1);
+    // all loads first, unconditionally on a full tile, so they are in flight together
+    float v[kPer];
+    const int lim = FWD ? nx : n;
+    if (lim == kTile) {
+#pragma unroll
+        for (int k = 0; k < kPer; k++) v[k] = load_tile<FWD, DT>(x.p[w], e0, threadIdx.x + k * kTT);
+    } else {
+#pragma unroll
+        for (int k = 0; k < kPer; k++) {
+            const int i = threadIdx.x + k * kTT;
+            v[k] = i < lim ? load_tile<FWD, DT>(x.p[w], e0, i) : 0.0f;
         }
-        yw[e0 + i] = v;
+    }
+    __syncthreads();                                  // the sign words
+#pragma unroll
+    for (int k = 0; k < kPer; k++) {
+        const int i = threadIdx.x + k * kTT;
+        s[pad(i)] = FWD && negated(words, i >> 7, i) ? -v[k] : v[k];
+    }
+    __syncthreads();
+    stages(s, 0, kbits);
+#pragma unroll
+    for (int k = 0; k < kPer; k++) {
+        const int i = threadIdx.x + k * kTT;
+        float r = s[pad(i)];
+        if (!FINAL) {
+            if (i < n) (static_cast<float*>(y.p[w]) + e0)[i] = r;
+        } else if (FWD) {
+            if (i < n) {
+                r = r * c;
+                if (mM) r = clamp_to(r, mM, (e0 + i) >> kbits);
+                (static_cast<float*>(y.p[w]) + e0)[i] = r;
+            }
+        } else if (i < nx) {
+            r = r * c;
+            if (negated(words, i >> 7, i)) r = -r;
+            if (DT == GA_F32) (static_cast<float*>(y.p[w]) + e0)[i] = r;
+            else (static_cast<uint16_t*>(y.p[w]) + e0)[i] = (uint16_t)f32_to_bf16_rne(r);
+        }
     }
 }
 
-// Cross pass: rows j = 0 .. G-1 of block b at stride T, columns c0 .. c0+W-1.
-// FWD: scale and clamp; else (inverse): scale, apply the signs, write out.
+// ---------------------------------------------------------------- cross pass
+
+// Rows j = 0 .. G-1 of block b at stride kTile, columns c0 .. c0+W-1
+// (W = 2^wbits >= 16): stages on the row bits, i.e. LDS index bits
+// wbits .. kTileBits-1. FWD: scale and clamp; else scale, sign, write out.
 template <bool FWD, ga_dtype OUT>
-__global__ __launch_bounds__(kThreads) void rht_cross_kernel(PtrTable y, PtrTable out, int64_t N,
-                                                             int T, int64_t d, int G, int W,
-                                                             uint32_t k0, uint32_t k1, float c,
-                                                             const float* __restrict__ mM) {
-    __shared__ float s[kTile];
-    // inverse only: the Philox blocks of every (row, 128-column group)
-    __shared__ uint32_t words[FWD ? 1 : 4 * kMaxRows];
+__global__ __launch_bounds__(kTT) void rht_cross_kernel(PtrTable y, PtrTable out, int64_t N, int dbits,
+                                                        int wbits, uint32_t k0, uint32_t k1, float c,
+                                                        const float* __restrict__ mM) {
+    __shared__ float s[kLds];
+    __shared__ uint32_t words[FWD ? 1 : kSignWords];
     const int w = blockIdx.y;
-    const int64_t cols_per_block = T / W;
-    const int64_t b = blockIdx.x / cols_per_block;
-    const int64_t c0 = (blockIdx.x % cols_per_block) * W;
-    const int64_t base = b * d + c0;           // a multiple of min(W, 128)
-    float* yw = static_cast<float*>(y.p[w]);
-    const int n = G * W;
-    const int R = W >= 128 ? W / 128 : 1;      // sign blocks per row
-    for (int i = threadIdx.x; i < n; i += kThreads) {
-        const int j = i / W, col = i % W;
-        s[i] = yw[base + (int64_t)j * T + col];
+    const int W = 1 << wbits;
+    const int gbits = dbits - kTileBits;             // G = 2^gbits rows
+    const int G = 1 << gbits;
+    const int64_t b = blockIdx.x >> gbits;
+    const int64_t base = (b << dbits) + (int64_t)(blockIdx.x & (G - 1)) * W;   // a multiple of 16
+    float* yb = static_cast<float*>(y.p[w]) + base;
+#pragma unroll
+    for (int k = 0; k < kPer; k++) {
+        const int i = threadIdx.x + k * kTT;
+        s[pad(i)] = yb[(i >> wbits) * kTile + (i & (W - 1))];
     }
+    // inverse: the Philox blocks of every (row, 128-column group); R per row
+    const int R = W >= 128 ? W >> 7 : 1;
     if (!FWD) {
-        for (int t = threadIdx.x; t < G * R; t += kThreads) {
+        for (int t = threadIdx.x; t < G * R; t += kTT) {
             const int j = t / R, gi = t % R;
-            const uint64_t q = (uint64_t)(((base + (int64_t)j * T) >> 7) + gi);
+            const uint64_t q = (uint64_t)(((base + (int64_t)j * kTile) >> 7) + gi);
             const Philox4 r = philox4x32_10((uint32_t)q, (uint32_t)(q >> 32), kSignDomain, 0u, k0, k1);
             words[4 * t + 0] = r.v[0];
             words[4 * t + 1] = r.v[1];
@@ -146,61 +239,52 @@ __global__ __launch_bounds__(kThreads) void rht_cross_kernel(PtrTable y, PtrTabl
         }
     }
     __syncthreads();
-    lds_stages(s, n, W, n);
-    for (int i = threadIdx.x; i < n; i += kThreads) {
-        const int j = i / W, col = i % W;
-        const int64_t e = base + (int64_t)j * T + col;
-        const float v = s[i] * c;
+    stages(s, wbits, kTileBits);
+    const int nb = (int)min(N - base, (int64_t)1 << 30);   // inverse: offsets below nb exist
+    const int eb = (int)(base & 127);
+#pragma unroll
+    for (int k = 0; k < kPer; k++) {
+        const int i = threadIdx.x + k * kTT;
+        const int j = i >> wbits, col = i & (W - 1);
+        const int off = j * kTile + col;
+        float v = s[pad(i)] * c;
         if (FWD) {
-            yw[e] = mM ? clamp_to(v, mM, b) : v;
-        } else if (e < N) {
-            const uint32_t wd = words[4 * (j * R + (col >> 7)) + ((e >> 5) & 3)];
-            const float r = ((wd >> (e & 31)) & 1u) ? -v : v;
-            if (OUT == GA_F32) static_cast<float*>(out.p[w])[e] = r;
-            else static_cast<uint16_t*>(out.p[w])[e] = (uint16_t)f32_to_bf16_rne(r);
-        }
-    }
-}
-
-// ---------------------------------------------------------------- inverse
-
-template <bool FINAL, ga_dtype OUT>
-__global__ __launch_bounds__(kThreads) void rht_inv_tile_kernel(float* y, void* out, int64_t N,
-                                                                int64_t Np, int T, uint32_t k0,
-                                                                uint32_t k1, float c) {
-    __shared__ float s[kTile];
-    __shared__ uint32_t words[FINAL ? 4 * (kTile / 128) : 1];
-    const int64_t e0 = (int64_t)blockIdx.x * kTile;
-    const int n = (int)min((int64_t)kTile, Np - e0);
-    const int64_t q0 = e0 >> 7;
-    if (FINAL) sign_blocks(words, q0, (n + 127) / 128, k0, k1);
-    for (int i = threadIdx.x; i < n; i += kThreads) s[i] = y[e0 + i];
-    __syncthreads();
-    lds_stages(s, n, 1, T);
-    for (int i = threadIdx.x; i < n; i += kThreads) {
-        const int64_t e = e0 + i;
-        if (!FINAL) {
-            y[e] = s[i];
-        } else if (e < N) {
-            const float r = sign_of(words, q0, e) * (s[i] * c);
-            if (OUT == GA_F32) static_cast<float*>(out)[e] = r;
-            else static_cast<uint16_t*>(out)[e] = (uint16_t)f32_to_bf16_rne(r);
+            yb[off] = mM ? clamp_to(v, mM, b) : v;
+        } else if (off < nb) {
+            if (negated(words, j * R + (col >> 7), eb + col)) v = -v;
+            if (OUT == GA_F32) (static_cast<float*>(out.p[w]) + base)[off] = v;
+            else (static_cast<uint16_t*>(out.p[w]) + base)[off] = (uint16_t)f32_to_bf16_rne(v);
         }
     }
 }
 
 // ---------------------------------------------------------------- norms and range
 
+// One workgroup per (block, worker): 16 coalesced loads in flight per thread,
+// squares summed in binary64 (exact products), then a tree over the threads.
 template <ga_dtype DT>
-__global__ __launch_bounds__(kThreads) void rht_sumsq_kernel(PtrTable x, int64_t N, int64_t d,
+__global__ __launch_bounds__(kThreads) void rht_sumsq_kernel(PtrTable x, int64_t N, int dbits,
                                                              int64_t nblk, double* sumsq) {
     const int w = blockIdx.y;
     const int64_t b = blockIdx.x;
-    const int64_t lo = b * d, hi = min(lo + d, N);
+    const int64_t lo = b << dbits, hi = min(lo + ((int64_t)1 << dbits), N);
+    const void* xw = x.p[w];
     double acc = 0.0;
-    for (int64_t e = lo + threadIdx.x; e < hi; e += kThreads) {
-        const double v = (double)load_coord(x.p[w], e, N, DT);
-        acc += v * v;
+    for (int64_t c0 = lo; c0 < hi; c0 += 16 * kThreads) {
+        float v[16];
+        const int64_t e0 = c0 + threadIdx.x;
+        if (c0 + 16 * kThreads <= hi) {               // a full chunk: loads in flight together
+#pragma unroll
+            for (int k = 0; k < 16; k++) v[k] = load_coord(xw, e0 + k * kThreads, hi, DT);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 16; k++) {
+                const int64_t e = e0 + k * kThreads;
+                v[k] = e < hi ? load_coord(xw, e, hi, DT) : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 16; k++) acc += (double)v[k] * (double)v[k];
     }
     __shared__ double sh[kThreads / 64];
 #pragma unroll
@@ -225,20 +309,13 @@ __global__ __launch_bounds__(kThreads) void rht_range_kernel(const double* sumsq
     mM[2 * p + 1] = M;
 }
 
-bool pow2_block(int64_t d) { return d >= 2 && d <= (int64_t)kTile * kMaxRows && (d & (d - 1)) == 0; }
-
-// Tile size and cross-pass shape for a block length d.
-struct Shape {
-    int T, G, W;
-};
-Shape shape_of(int64_t d) {
-    Shape s;
-    s.T = (int)(d < kTile ? d : kTile);
-    s.G = (int)(d / s.T);
-    s.W = s.G > 1 ? kTile / s.G : 0;
-    if (s.G > 1 && s.W > s.T) s.W = s.T;
-    return s;
+int log2_block(int64_t d) {
+    if (d < 2 || d > (1ll << kMaxBits) || (d & (d - 1))) return -1;
+    int k = 0;
+    while ((1ll << k) < d) k++;
+    return k;
 }
+bool pow2_block(int64_t d) { return log2_block(d) > 0; }
 
 float inv_sqrt_d(int64_t d) { return (float)(1.0 / std::sqrt((double)d)); }
 
@@ -251,7 +328,8 @@ extern "C" ga_status thc_rht_sumsq(const void* const* bufs, int32_t P, int64_t N
                                    int64_t d, double* d_sumsq, void* stream) {
     const char* what = "thc_rht_sumsq";
     if (!valid_dtype(dt)) return fail(GA_EINVAL, "%s: unknown dtype %d", what, (int)dt);
-    if (!pow2_block(d)) return fail(GA_EINVAL, "%s: d = %lld is not a power of two in [2, 2^22]", what, (long long)d);
+    const int dbits = log2_block(d);
+    if (dbits < 0) return fail(GA_EINVAL, "%s: d = %lld is not a power of two in [2, 2^22]", what, (long long)d);
     if (N < 0) return fail(GA_EINVAL, "%s: negative size", what);
     if (P < 1 || P > GA_MAX_WORKERS) return fail(GA_EINVAL, "%s: P = %d outside [1, %d]", what, P, GA_MAX_WORKERS);
     if (N == 0) return GA_OK;
@@ -264,9 +342,9 @@ extern "C" ga_status thc_rht_sumsq(const void* const* bufs, int32_t P, int64_t N
     for (int i = 0; i < P; i++) t.p[i] = const_cast<void*>(bufs[i]);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (dt == GA_F32)
-        hipLaunchKernelGGL(rht_sumsq_kernel<GA_F32>, dim3((unsigned)nblk, (unsigned)P), dim3(kThreads), 0, hs, t, N, d, nblk, d_sumsq);
+        hipLaunchKernelGGL(rht_sumsq_kernel<GA_F32>, dim3((unsigned)nblk, (unsigned)P), dim3(kThreads), 0, hs, t, N, dbits, nblk, d_sumsq);
     else
-        hipLaunchKernelGGL(rht_sumsq_kernel<GA_BF16>, dim3((unsigned)nblk, (unsigned)P), dim3(kThreads), 0, hs, t, N, d, nblk, d_sumsq);
+        hipLaunchKernelGGL(rht_sumsq_kernel<GA_BF16>, dim3((unsigned)nblk, (unsigned)P), dim3(kThreads), 0, hs, t, N, dbits, nblk, d_sumsq);
     return check_launch(what);
 }
 
@@ -289,7 +367,8 @@ extern "C" ga_status thc_rht_forward(const void* const* bufs, int32_t P, int64_t
                                      void* stream) {
     const char* what = "thc_rht_forward";
     if (!valid_dtype(dt)) return fail(GA_EINVAL, "%s: unknown dtype %d", what, (int)dt);
-    if (!pow2_block(d)) return fail(GA_EINVAL, "%s: d = %lld is not a power of two in [2, 2^22]", what, (long long)d);
+    const int dbits = log2_block(d);
+    if (dbits < 0) return fail(GA_EINVAL, "%s: d = %lld is not a power of two in [2, 2^22]", what, (long long)d);
     if (N < 0) return fail(GA_EINVAL, "%s: negative size", what);
     if (P < 1 || P > GA_MAX_WORKERS) return fail(GA_EINVAL, "%s: P = %d outside [1, %d]", what, P, GA_MAX_WORKERS);
     if (N == 0) return GA_OK;
@@ -298,7 +377,6 @@ extern "C" ga_status thc_rht_forward(const void* const* bufs, int32_t P, int64_t
     if ((rc = check_workers(reinterpret_cast<const void* const*>(y), P, 4, what))) return rc;
     if (d_mM && !aligned(d_mM, 8)) return fail(GA_EINVAL, "%s: misaligned range", what);
     const int64_t Np = ceil_div(N, d) * d;
-    const Shape sh = shape_of(d);
     const int64_t tiles = ceil_div(Np, kTile);
     if (tiles > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: too many tiles", what);
     PtrTable tx{}, ty{};
@@ -310,20 +388,22 @@ extern "C" ga_status thc_rht_forward(const void* const* bufs, int32_t P, int64_t
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
     const float c = inv_sqrt_d(d);
     const dim3 g1((unsigned)tiles, (unsigned)P);
-    if (sh.G == 1) {
+    const bool one = dbits <= kTileBits;
+    const int kbits = one ? dbits : kTileBits;
+    if (one) {
         if (dt == GA_F32)
-            hipLaunchKernelGGL((rht_fwd_tile_kernel<GA_F32, true>), g1, dim3(kThreads), 0, hs, tx, ty, N, Np, sh.T, d, k0, k1, c, d_mM);
+            hipLaunchKernelGGL((rht_tile_kernel<true, true, GA_F32>), g1, dim3(kTT), 0, hs, tx, ty, N, Np, kbits, k0, k1, c, d_mM);
         else
-            hipLaunchKernelGGL((rht_fwd_tile_kernel<GA_BF16, true>), g1, dim3(kThreads), 0, hs, tx, ty, N, Np, sh.T, d, k0, k1, c, d_mM);
+            hipLaunchKernelGGL((rht_tile_kernel<true, true, GA_BF16>), g1, dim3(kTT), 0, hs, tx, ty, N, Np, kbits, k0, k1, c, d_mM);
         return check_launch(what);
     }
     if (dt == GA_F32)
-        hipLaunchKernelGGL((rht_fwd_tile_kernel<GA_F32, false>), g1, dim3(kThreads), 0, hs, tx, ty, N, Np, sh.T, d, k0, k1, c, d_mM);
+        hipLaunchKernelGGL((rht_tile_kernel<true, false, GA_F32>), g1, dim3(kTT), 0, hs, tx, ty, N, Np, kbits, k0, k1, c, d_mM);
     else
-        hipLaunchKernelGGL((rht_fwd_tile_kernel<GA_BF16, false>), g1, dim3(kThreads), 0, hs, tx, ty, N, Np, sh.T, d, k0, k1, c, d_mM);
+        hipLaunchKernelGGL((rht_tile_kernel<true, false, GA_BF16>), g1, dim3(kTT), 0, hs, tx, ty, N, Np, kbits, k0, k1, c, d_mM);
     if ((rc = check_launch(what))) return rc;
-    const dim3 g2((unsigned)((Np / d) * (sh.T / sh.W)), (unsigned)P);
-    hipLaunchKernelGGL((rht_cross_kernel<true, GA_F32>), g2, dim3(kThreads), 0, hs, ty, ty, Np, sh.T, d, sh.G, sh.W, k0, k1, c, d_mM);
+    const int wbits = 2 * kTileBits - dbits;         // W = kTile / G
+    hipLaunchKernelGGL((rht_cross_kernel<true, GA_F32>), g1, dim3(kTT), 0, hs, ty, ty, Np, dbits, wbits, k0, k1, c, d_mM);
     return check_launch(what);
 }
 
@@ -331,35 +411,37 @@ extern "C" ga_status thc_rht_inverse(float* y, int64_t N, int64_t d, uint64_t se
                                      ga_dtype out_dt, void* stream) {
     const char* what = "thc_rht_inverse";
     if (!valid_dtype(out_dt)) return fail(GA_EINVAL, "%s: unknown dtype %d", what, (int)out_dt);
-    if (!pow2_block(d)) return fail(GA_EINVAL, "%s: d = %lld is not a power of two in [2, 2^22]", what, (long long)d);
+    const int dbits = log2_block(d);
+    if (dbits < 0) return fail(GA_EINVAL, "%s: d = %lld is not a power of two in [2, 2^22]", what, (long long)d);
     if (N < 0) return fail(GA_EINVAL, "%s: negative size", what);
     if (N == 0) return GA_OK;
     if (!y || !out || !aligned(y, 4) || !aligned(out, elem_size(out_dt)))
         return fail(GA_EINVAL, "%s: null or misaligned pointer", what);
     const int64_t Np = ceil_div(N, d) * d;
-    const Shape sh = shape_of(d);
     const int64_t tiles = ceil_div(Np, kTile);
     if (tiles > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: too many tiles", what);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
     const float c = inv_sqrt_d(d);
-    ga_status rc;
-    if (sh.G == 1) {
-        if (out_dt == GA_F32)
-            hipLaunchKernelGGL((rht_inv_tile_kernel<true, GA_F32>), dim3((unsigned)tiles), dim3(kThreads), 0, hs, y, out, N, Np, sh.T, k0, k1, c);
-        else
-            hipLaunchKernelGGL((rht_inv_tile_kernel<true, GA_BF16>), dim3((unsigned)tiles), dim3(kThreads), 0, hs, y, out, N, Np, sh.T, k0, k1, c);
-        return check_launch(what);
-    }
-    hipLaunchKernelGGL((rht_inv_tile_kernel<false, GA_F32>), dim3((unsigned)tiles), dim3(kThreads), 0, hs, y, out, N, Np, sh.T, k0, k1, c);
-    if ((rc = check_launch(what))) return rc;
     PtrTable ty{}, to{};
     ty.p[0] = y;
     to.p[0] = out;
-    const dim3 g2((unsigned)((Np / d) * (sh.T / sh.W)), 1u);
+    const dim3 g1((unsigned)tiles, 1u);
+    const float* none = nullptr;
+    if (dbits <= kTileBits) {
+        if (out_dt == GA_F32)
+            hipLaunchKernelGGL((rht_tile_kernel<false, true, GA_F32>), g1, dim3(kTT), 0, hs, ty, to, N, Np, dbits, k0, k1, c, none);
+        else
+            hipLaunchKernelGGL((rht_tile_kernel<false, true, GA_BF16>), g1, dim3(kTT), 0, hs, ty, to, N, Np, dbits, k0, k1, c, none);
+        return check_launch(what);
+    }
+    hipLaunchKernelGGL((rht_tile_kernel<false, false, GA_F32>), g1, dim3(kTT), 0, hs, ty, ty, N, Np, (int)kTileBits, k0, k1, c, none);
+    ga_status rc = check_launch(what);
+    if (rc) return rc;
+    const int wbits = 2 * kTileBits - dbits;
     if (out_dt == GA_F32)
-        hipLaunchKernelGGL((rht_cross_kernel<false, GA_F32>), g2, dim3(kThreads), 0, hs, ty, to, N, sh.T, d, sh.G, sh.W, k0, k1, c, (const float*)nullptr);
+        hipLaunchKernelGGL((rht_cross_kernel<false, GA_F32>), g1, dim3(kTT), 0, hs, ty, to, N, dbits, wbits, k0, k1, c, none);
     else
-        hipLaunchKernelGGL((rht_cross_kernel<false, GA_BF16>), g2, dim3(kThreads), 0, hs, ty, to, N, sh.T, d, sh.G, sh.W, k0, k1, c, (const float*)nullptr);
+        hipLaunchKernelGGL((rht_cross_kernel<false, GA_BF16>), g1, dim3(kTT), 0, hs, ty, to, N, dbits, wbits, k0, k1, c, none);
     return check_launch(what);
 }
