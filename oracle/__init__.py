@@ -43,6 +43,8 @@ def lib():
         vp, i64, i32 = C.c_void_p, C.c_int64, C.c_int
         L.orc_ring_fold.argtypes = [C.POINTER(vp), i32, i64, i32, i32, i64]
         L.orc_ring_stepwise.argtypes = [C.POINTER(vp), i32, i64, i32, i32, i64, i32]
+        L.orc_dual_ring_fold.argtypes = [C.POINTER(vp), i32, i64, i32, i32, i64]
+        L.orc_dual_ring_stepwise.argtypes = [C.POINTER(vp), i32, i64, i32, i32, i64]
         L.orc_ring_stats.argtypes = [i32, i64, i64, i32, C.POINTER(i64), C.POINTER(i64)]
         L.orc_ring_stats.restype = None
         L.orc_minmax.argtypes = [C.POINTER(vp), i32, i64, i32, i64, vp]
@@ -126,6 +128,19 @@ def ring_stepwise(bufs, op: int = AVG, part: int = 0, rs_only: bool = False) -> 
     P, N = len(bufs), bufs[0].size
     _check(lib().orc_ring_stepwise(_ptrs(bufs), P, N, _dt(bufs[0]), op, part, int(rs_only)),
            "ring_stepwise")
+
+
+def dual_ring_fold(bufs, op: int = AVG, part: int = 0) -> None:
+    """In place: the bidirectional ring's result (2P sub-chunks, see orc.c)."""
+    P, N = len(bufs), bufs[0].size
+    _check(lib().orc_dual_ring_fold(_ptrs(bufs), P, N, _dt(bufs[0]), op, part), "dual_ring_fold")
+
+
+def dual_ring_stepwise(bufs, op: int = AVG, part: int = 0) -> None:
+    """In place: the literal two-direction schedule with send copies."""
+    P, N = len(bufs), bufs[0].size
+    _check(lib().orc_dual_ring_stepwise(_ptrs(bufs), P, N, _dt(bufs[0]), op, part),
+           "dual_ring_stepwise")
 
 
 def ring_stats(P: int, N: int, part: int, elem_bytes: int):

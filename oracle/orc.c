@@ -230,6 +230,123 @@ int orc_ring_stepwise(void *const *bufs, int P, int64_t N, int dt, int op, int64
 }
 
 /*
+ * Bidirectional ring ([RING] section 11, Exercise 1 and its worked solution):
+ * a partition is cut into 2P sub-chunks; sub-chunks 0 .. P-1 travel a
+ * clockwise ring (worker i sends to i + 1) and sub-chunks P .. 2P-1 a
+ * counter-clockwise ring (worker i sends to i - 1), both at once. Every
+ * ring runs the schedule of section 7 in its own direction: at
+ * scatter-reduce step s worker i passes its partial of ring sub-chunk
+ * (i - dir s) mod P on, and the neighbour adds its own copy; so a clockwise
+ * sub-chunk c is folded x_c, x_{c+1}, ..., x_{c-1} and a counter-clockwise
+ * one x_c, x_{c-1}, ..., x_{c+1}.
+ *
+ * Readings: sub-chunk size C2 = ceil(n / (2P)) with short or empty trailing
+ * sub-chunks (the page assumes 2P divides n); average, bf16 and partitions
+ * as for the single ring.
+ */
+int orc_dual_ring_fold(void *const *bufs, int P, int64_t N, int dt, int op, int64_t part)
+{
+    if (P < 1 || N < 0)
+        return -1;
+    int64_t plen = part_len(N, part);
+    for (int64_t p0 = 0; p0 < N; p0 += plen) {
+        int64_t n = (N - p0 < plen) ? N - p0 : plen;
+        int64_t C2 = (n + 2 * P - 1) / (2 * P);
+        for (int64_t e = p0; e < p0 + n; e++) {
+            int k = (int)((e - p0) / C2);
+            int dir = k < P ? 1 : -1;
+            int c = k < P ? k : k - P;
+            float acc = load_elem(bufs[c], dt, e);
+            for (int j = 1; j < P; j++)
+                acc = acc + load_elem(bufs[mod_p(c + dir * j, P)], dt, e);
+            if (op == ORC_AVG)
+                acc = acc / (float)P;
+            for (int w = 0; w < P; w++)
+                store_elem(bufs[w], dt, e, acc);
+        }
+    }
+    return 0;
+}
+
+/* One communication step of one ring direction on the working copies:
+ * every worker i first copies out ring sub-chunk (i - dir * shift) mod P
+ * (index base + that, length len(...)), then worker i + dir adds (reduce)
+ * or writes (gather) what it received into the same sub-chunk. */
+static void dual_step(float **work, float **send, int P, int dir, int base, int64_t C2, int64_t n,
+                      int shift, int reduce)
+{
+    for (int i = 0; i < P; i++) {
+        int64_t k = base + mod_p(i - (int64_t)dir * shift, P);
+        int64_t lo = k * C2 < n ? k * C2 : n, hi = (k + 1) * C2 < n ? (k + 1) * C2 : n;
+        memcpy(send[i], work[i] + lo, (size_t)(hi - lo) * sizeof(float));
+    }
+    for (int i = 0; i < P; i++) {
+        int j = mod_p(i + dir, P);                       /* the receiver */
+        int64_t k = base + mod_p(i - (int64_t)dir * shift, P);
+        int64_t lo = k * C2 < n ? k * C2 : n, hi = (k + 1) * C2 < n ? (k + 1) * C2 : n;
+        for (int64_t t = lo; t < hi; t++)
+            work[j][t] = reduce ? work[j][t] + send[i][t - lo] : send[i][t - lo];
+    }
+}
+
+/*
+ * orc_dual_ring_stepwise: the literal schedule of the bidirectional ring,
+ * P - 1 scatter-reduce steps then P - 1 all-gather steps, both directions
+ * in every step, on binary32 working copies with explicit send copies.
+ * Scatter-reduce step s moves sub-chunk (i - dir s) of worker i; all-gather
+ * step s moves (i - dir (s - 1)), the finished one. avg divides at the end.
+ */
+int orc_dual_ring_stepwise(void *const *bufs, int P, int64_t N, int dt, int op, int64_t part)
+{
+    if (P < 1 || N < 0)
+        return -1;
+    int64_t plen = part_len(N, part);
+    float **work = (float **)calloc((size_t)P, sizeof(float *));
+    float **send = (float **)calloc((size_t)P, sizeof(float *));
+    if (!work || !send)
+        return -2;
+    int rc = 0;
+    for (int64_t p0 = 0; p0 < N && rc == 0; p0 += plen) {
+        int64_t n = (N - p0 < plen) ? N - p0 : plen;
+        int64_t C2 = (n + 2 * P - 1) / (2 * P);
+        for (int i = 0; i < P; i++) {
+            work[i] = (float *)malloc((size_t)n * sizeof(float));
+            send[i] = (float *)malloc((size_t)(C2 > 0 ? C2 : 1) * sizeof(float));
+            if (!work[i] || !send[i])
+                rc = -2;
+        }
+        if (rc == 0) {
+            for (int i = 0; i < P; i++)
+                for (int64_t t = 0; t < n; t++)
+                    work[i][t] = load_elem(bufs[i], dt, p0 + t);
+            for (int s = 0; s < P - 1; s++) {
+                dual_step(work, send, P, +1, 0, C2, n, s, 1);
+                dual_step(work, send, P, -1, P, C2, n, s, 1);
+            }
+            for (int s = 0; s < P - 1; s++) {
+                dual_step(work, send, P, +1, 0, C2, n, s - 1, 0);
+                dual_step(work, send, P, -1, P, C2, n, s - 1, 0);
+            }
+            if (op == ORC_AVG)
+                for (int i = 0; i < P; i++)
+                    for (int64_t t = 0; t < n; t++)
+                        work[i][t] = work[i][t] / (float)P;
+            for (int i = 0; i < P; i++)
+                for (int64_t t = 0; t < n; t++)
+                    store_elem(bufs[i], dt, p0 + t, work[i][t]);
+        }
+        for (int i = 0; i < P; i++) {
+            free(work[i]);
+            free(send[i]);
+            work[i] = send[i] = NULL;
+        }
+    }
+    free(work);
+    free(send);
+    return rc;
+}
+
+/*
  * Communication accounting as the [RING] section 7 simulator keeps it: each
  * of the 2(P-1) steps sends one chunk of C elements per worker, so a worker
  * sends 2(P-1) * C * elem_bytes per partition ([HVD] 3.4: 2 (N-1)/N * K).
