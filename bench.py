@@ -125,6 +125,10 @@ def main():
     ap.add_argument("--workload", default="shard", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-fusion", action="store_true",
+                    help="fused workloads: pack -> ring -> unpack instead of the zero-copy ring")
+    ap.add_argument("--ring-mode", default="fused", choices=["fused", "dual"],
+                    help="single ring or the bidirectional dual ring fold order")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one 1 GiB torch copy first (PMC calibration)")
     args = ap.parse_args()
@@ -144,7 +148,8 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
 
-    pipe = Pipeline(args.workload)
+    pipe = Pipeline(args.workload, zero_copy=not args.copy_fusion,
+                    ring_mode=ga.RING_DUAL if args.ring_mode == "dual" else ga.RING_FUSED)
     t0 = time.perf_counter()
     pipe.setup()
     log(f"setup {args.workload}: {time.perf_counter() - t0:.1f} s")
@@ -198,12 +203,14 @@ def main():
     quant = {k: round(P * N / (v * 1e-3) / 1e9, 2) for k, v in stage_ms.items()
              if k.startswith(("thc_usq_quantize", "thc_nuhc_quantize"))}
 
-    ring_ms = stage_ms["ring_allreduce"]
-    achieved = nbytes["ring_allreduce"] / (ring_ms * 1e-3) / 1e9
+    ring_key = "ring_allreduce" if "ring_allreduce" in stage_ms else "fusion_ring"
+    ring_ms = stage_ms[ring_key]
+    achieved = nbytes[ring_key] / (ring_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic_from_profile(args.workload),
-                "kernel": "ring_fused_vec_kernel", "alg_bytes_per_launch": nbytes["ring_allreduce"]}
+                "traffic": traffic_from_profile(args.workload) if ring_key == "ring_allreduce" else None,
+                "kernel": "ring_fused_vec_kernel" if ring_key == "ring_allreduce" else "fusion_ring_kernel",
+                "alg_bytes_per_launch": nbytes[ring_key]}
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
@@ -213,6 +220,9 @@ def main():
         "config": {"workload": f"{args.workload}: {DESCRIPTIONS[args.workload]}", "P": P, "N": N,
                    "elem": "bf16" if pipe.w.dtype == ga.BF16 else "fp32",
                    "partition_elems": pipe.w.part_elems, "thc_bits": list(pipe.w.thc_bits),
+                   "ring": args.ring_mode,
+                   "fusion": (None if not pipe.w.fused else
+                              "pack-ring-unpack" if args.copy_fusion else "zero-copy"),
                    "parallelism": "1 GPU, P simulated workers"},
         "roofline": roofline,
         "thc_quantize_gelem_s": quant,

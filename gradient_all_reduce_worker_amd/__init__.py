@@ -1,7 +1,8 @@
 """MI355X (gfx950) gradient-aggregation hot path for P simulated
-data-parallel workers held in one GPU's HBM: Tensor Fusion pack/unpack,
-ring all-reduce (sum | avg), and THC uniform stochastic quantization with
-homomorphic integer aggregation.
+data-parallel workers held in one GPU's HBM: Tensor Fusion (pack/unpack or
+zero-copy), ring all-reduce (sum | avg; single or bidirectional), and THC
+stochastic quantization (uniform and table-based) with homomorphic integer
+aggregation, behind an optional randomized Hadamard transform.
 
 The computation lives in libga.so (HIP, built from csrc/ by build.py); the
 functions below are its C ABI (include/ga.h) under the same names, with
@@ -14,5 +15,6 @@ from ._native import (  # noqa: F401
     ga_fuse_pack, ga_fuse_plan, ga_fuse_unpack, ga_ring_allreduce_sim, load, n_partitions,
     packed_bytes, thc_dequant, thc_int_aggregate, thc_minmax, thc_nmse, thc_nmse_ws_bytes,
     thc_usq_quantize, upload_table, thc_nuhc_quantize, thc_nuhc_aggregate, thc_nuhc_dequant,
-    center_table,
+    center_table, RING_DUAL, FTENSOR_DTYPE, FusionRing, ga_fusion_ring_plan, rht_padded,
+    thc_rht_sumsq, thc_rht_range, thc_rht_forward, thc_rht_inverse,
 )

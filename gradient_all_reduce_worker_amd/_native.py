@@ -15,7 +15,7 @@ import torch
 
 F32, BF16 = 0, 1
 SUM, AVG = 0, 1
-RING_FUSED, RING_STEPWISE = 0, 1
+RING_FUSED, RING_STEPWISE, RING_DUAL = 0, 1, 2
 MAX_WORKERS = 64
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -27,6 +27,7 @@ EXPORTS = (
     "thc_dequant", "thc_nmse", "thc_nmse_ws_bytes", "ga_last_error",
     "thc_nuhc_quantize", "thc_nuhc_aggregate", "thc_nuhc_dequant",
     "thc_rht_sumsq", "thc_rht_range", "thc_rht_forward", "thc_rht_inverse",
+    "ga_fusion_ring_plan", "ga_fusion_ring_allreduce",
 )
 
 
@@ -46,6 +47,9 @@ class RingStats(C.Structure):
 
 
 DESC_DTYPE = np.dtype([("src", np.uint64), ("dst", np.uint64), ("n", np.int64), ("start", np.int64)])
+# ga_fusion_tensor
+FTENSOR_DTYPE = np.dtype([("start", np.int64), ("n", np.int64), ("vstart", np.int64),
+                          ("vec", np.int32), ("reserved", np.int32)])
 
 _lib = None
 
@@ -83,6 +87,9 @@ def load() -> C.CDLL:
     L.thc_rht_range.argtypes = [vp, i32, i64, i64, C.c_double, vp, vp]
     L.thc_rht_forward.argtypes = [C.POINTER(vp), i32, i64, i32, i64, u64, vp, C.POINTER(vp), vp]
     L.thc_rht_inverse.argtypes = [vp, i64, i64, u64, vp, i32, vp]
+    L.ga_fusion_ring_plan.argtypes = [vp, vp, i64, i32, i32, i64, C.POINTER(i64)]
+    L.ga_fusion_ring_allreduce.argtypes = [vp, vp, i64, i64, i32, i64, i32, i32, i32, i64,
+                                           C.POINTER(RingStats), vp]
     L.ga_last_error.argtypes = []
     L.ga_last_error.restype = C.c_char_p
     for name in EXPORTS:
@@ -227,6 +234,70 @@ def ga_ring_allreduce_sim(bufs: Sequence[torch.Tensor], op: int = AVG, part_elem
                                    C.byref(st), _stream(stream)))
     return {"steps": st.steps, "bytes_sent_per_worker": st.bytes_sent_per_worker,
             "hbm_bytes": st.hbm_bytes, "launches": st.launches}
+
+
+# ------------------------------------------------------------------ zero-copy fusion ring
+def ga_fusion_ring_plan(h_tensors: np.ndarray, h_ptrs: np.ndarray, P: int, dt: int, fill: int) -> int:
+    """Host-only: checks the table of one fusion buffer (FTENSOR_DTYPE rows
+    in buffer order; h_ptrs uint64 [n_tensors, P]), fills vstart and vec in
+    place, returns the number of work vectors."""
+    if h_tensors.dtype != FTENSOR_DTYPE or not h_tensors.flags.c_contiguous:
+        raise TypeError("h_tensors must be a contiguous FTENSOR_DTYPE array")
+    h_ptrs = np.ascontiguousarray(h_ptrs, dtype=np.uint64)
+    if h_ptrs.size != h_tensors.size * P:
+        raise ValueError("h_ptrs must hold n_tensors x P pointers")
+    n = C.c_int64(0)
+    _check(load().ga_fusion_ring_plan(h_tensors.ctypes.data if h_tensors.size else None,
+                                      h_ptrs.ctypes.data if h_ptrs.size else None,
+                                      h_tensors.size, P, dt, fill, C.byref(n)))
+    return int(n.value)
+
+
+class FusionRing:
+    """Tensor Fusion without the fusion buffers: for every buffer of a plan,
+    the table of its tensors and the P workers' pointers to them, checked
+    and uploaded once; allreduce() then folds each buffer in place in the
+    workers' tensors (one launch per buffer)."""
+
+    def __init__(self, worker_tensors: List[List[torch.Tensor]], buf_of: Sequence[int],
+                 off_of: Sequence[int], fill: Sequence[int]):
+        self.P = len(worker_tensors)
+        self.dt = _dt(worker_tensors[0][0])
+        self.fill = [int(f) for f in fill]
+        device = worker_tensors[0][0].device
+        self.bufs = []
+        for k, f in enumerate(self.fill):
+            ts = sorted((int(off_of[t]), t) for t in range(len(buf_of)) if buf_of[t] == k)
+            h = np.zeros(len(ts), dtype=FTENSOR_DTYPE)
+            ptrs = np.zeros((len(ts), self.P), dtype=np.uint64)
+            for r, (off, t) in enumerate(ts):
+                h[r]["start"] = off
+                h[r]["n"] = worker_tensors[0][t].numel()
+                for i in range(self.P):
+                    x = worker_tensors[i][t]
+                    if _dt(x) != self.dt or x.numel() != h[r]["n"]:
+                        raise TypeError("workers' tensors must agree in size and data type")
+                    ptrs[r, i] = _dev(x, "tensor")
+            n_work = ga_fusion_ring_plan(h, ptrs, self.P, self.dt, f)
+            d_t = torch.from_numpy(h.view(np.uint8).copy()).to(device)
+            d_p = torch.from_numpy(ptrs.view(np.uint8).reshape(-1).copy()).to(device)
+            self.bufs.append((d_t, d_p, len(ts), n_work, f))
+
+    def allreduce_buffer(self, k: int, op: int = AVG, mode: int = RING_FUSED, part_elems: int = 0,
+                         stream=None) -> dict:
+        d_t, d_p, nt, n_work, f = self.bufs[k]
+        st = RingStats()
+        _check(load().ga_fusion_ring_allreduce(d_t.data_ptr() if nt else None,
+                                               d_p.data_ptr() if nt else None, nt, n_work, self.P,
+                                               f, self.dt, op, mode, part_elems, C.byref(st),
+                                               _stream(stream)))
+        return {"steps": st.steps, "bytes_sent_per_worker": st.bytes_sent_per_worker,
+                "hbm_bytes": st.hbm_bytes, "launches": st.launches}
+
+    def allreduce(self, op: int = AVG, mode: int = RING_FUSED, part_elems: int = 0,
+                  stream=None) -> None:
+        for k in range(len(self.bufs)):
+            self.allreduce_buffer(k, op, mode, part_elems, stream)
 
 
 # ------------------------------------------------------------------ THC

@@ -62,14 +62,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // gradient data from displacing other lines in the caches (measured ~8%
 // faster than plain accesses for the multi-stream ring on MI355X).
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+// Device memory (global address space): pointers read from a table in
+// memory are otherwise generic and would be accessed with flat instructions,
+// whose completion counter also gates scalar loads.
+typedef __attribute__((address_space(1))) u32x4_t g_u32x4_t;
 
 __device__ __forceinline__ uint4 load_stream(const void* p) {
-    const u32x4_t r = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+    const u32x4_t r = __builtin_nontemporal_load((const g_u32x4_t*)p);
     return make_uint4(r.x, r.y, r.z, r.w);
 }
 __device__ __forceinline__ void store_stream(void* p, uint4 v) {
     const u32x4_t r = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(r, static_cast<u32x4_t*>(p));
+    __builtin_nontemporal_store(r, (g_u32x4_t*)p);
 }
 
 // 64-bit element index of the first element handled by this thread when

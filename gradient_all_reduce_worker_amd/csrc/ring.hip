@@ -19,10 +19,21 @@
 //    GPU's share of a real multi-GPU ring, run for all P workers at once.
 // Both give bit-identical results.
 //
+// Bidirectional ring (lesson section 11, Exercise 1): each partition is cut
+// into 2P sub-chunks of C2 = ceil(n / 2P); sub-chunks 0..P-1 run the
+// schedule clockwise (fold c, c+1, ..., c-1), sub-chunks P..2P-1
+// counter-clockwise (sub-chunk P + c folds c, c-1, ..., c+1). One GPU
+// executes it fused, with the same traffic as the single ring; the two
+// directions matter for links, not for HBM.
+//
 // Rotation is uniform inside a chunk, so a workgroup whose elements all lie
 // in one chunk of one partition selects its worker pointers with scalar
 // loads; the few workgroups straddling a chunk or partition boundary, the
 // ragged tail and unaligned buffers take a per-element path.
+#include <algorithm>
+#include <utility>
+#include <vector>
+
 #include "common.hpp"
 
 namespace ga {
@@ -82,51 +93,86 @@ struct Where {
     int chunk;
 };
 
-__device__ __forceinline__ Where locate(int64_t e, int64_t N, int64_t plen, int P) {
+// nch chunks per partition: P for the single ring, 2P for the dual ring.
+__device__ __forceinline__ Where locate(int64_t e, int64_t N, int64_t plen, int nch) {
     if (N < 0xFFFFFF00ll) {            // 32-bit index arithmetic is exact here
         const uint32_t ue = (uint32_t)e, un = (uint32_t)N, ul = (uint32_t)plen;
         const uint32_t p = ue / ul, p0 = p * ul;
         const uint32_t n = un - p0 < ul ? un - p0 : ul;
-        const uint32_t C = (n + (uint32_t)P - 1u) / (uint32_t)P;
+        const uint32_t C = (n + (uint32_t)nch - 1u) / (uint32_t)nch;
         return {(int64_t)p, (int)((ue - p0) / C)};
     }
     int64_t p = e / plen;
     int64_t p0 = p * plen;
     int64_t n = N - p0 < plen ? N - p0 : plen;
-    int64_t C = (n + P - 1) / P;
+    int64_t C = (n + nch - 1) / nch;
     return {p, (int)((e - p0) / C)};
+}
+
+// Fold start and direction of a chunk: worker r, then r + dir, r + 2 dir, ...
+struct Rot {
+    int r;
+    int dir;
+};
+
+template <bool DUAL>
+__device__ __forceinline__ Rot rot_of(int chunk, int P) {
+    if (DUAL && chunk >= P) return {chunk - P, -1};
+    return {chunk, 1};
+}
+
+__device__ __forceinline__ int next_worker(int w, int dir, int P) {
+    if (dir > 0) return w + 1 == P ? 0 : w + 1;
+    return w == 0 ? P - 1 : w - 1;
 }
 
 // ---------------------------------------------------------------- fused fold
 
-template <ga_dtype DT>
-__device__ __forceinline__ void fold_one(const PtrTable& bufs, int P, int64_t N, int64_t plen,
-                                         int64_t e, Div div) {
+// Where the workers' base pointers come from: the kernel-argument table of a
+// flat all-reduce, or a row of a device table (one fusion-buffer tensor).
+struct ArgPtrs {
+    const PtrTable& t;
+    __device__ __forceinline__ void* operator[](int w) const { return t.p[w]; }
+};
+struct RowPtrs {
+    void* const* p;
+    __device__ __forceinline__ void* operator[](int w) const { return p[w]; }
+};
+
+// Element idx of every worker, folded from worker rt.r in direction rt.dir.
+template <ga_dtype DT, typename PS>
+__device__ __forceinline__ void fold_elem(const PS& bufs, int P, int64_t idx, Rot rt, Div div) {
     using E = Elem<DT>;
-    const int c = locate(e, N, plen, P).chunk;
-    float acc = E::load1(bufs.p[c], e);
-    int w = c;
+    float acc = E::load1(bufs[rt.r], idx);
+    int w = rt.r;
     for (int k = 1; k < P; k++) {
-        w = (w + 1 == P) ? 0 : w + 1;
-        acc = acc + E::load1(bufs.p[w], e);
+        w = next_worker(w, rt.dir, P);
+        acc = acc + E::load1(bufs[w], idx);
     }
     if (div.avg) acc = div.apply(acc);
-    for (int i = 0; i < P; i++) E::store1(bufs.p[i], e, acc);
+    for (int i = 0; i < P; i++) E::store1(bufs[i], idx, acc);
+}
+
+template <ga_dtype DT, bool DUAL>
+__device__ __forceinline__ void fold_one(const PtrTable& bufs, int P, int64_t N, int64_t plen,
+                                         int64_t e, Div div) {
+    fold_elem<DT>(ArgPtrs{bufs}, P, e, rot_of<DUAL>(locate(e, N, plen, DUAL ? 2 * P : P).chunk, P),
+                  div);
 }
 
 // One 16-byte vector v whose elements all start their fold at worker r
 // (lane-varying r: pointers are read per lane).
-template <ga_dtype DT>
-__device__ __forceinline__ void fold_vec(const PtrTable& bufs, int P, int64_t v, int r, Div div) {
+template <ga_dtype DT, typename PS>
+__device__ __forceinline__ void fold_vec(const PS& bufs, int P, int64_t v, Rot rt, Div div) {
     using E = Elem<DT>;
     constexpr int V = E::kVec;
     float acc[V];
-    E::widen(load_stream(static_cast<const uint4*>(bufs.p[r]) + v), acc);
-    int w = r;
+    E::widen(load_stream(static_cast<const uint4*>(bufs[rt.r]) + v), acc);
+    int w = rt.r;
     for (int k = 1; k < P; k++) {
-        w = (w + 1 == P) ? 0 : w + 1;
+        w = next_worker(w, rt.dir, P);
         float t[V];
-        E::widen(load_stream(static_cast<const uint4*>(bufs.p[w]) + v), t);
+        E::widen(load_stream(static_cast<const uint4*>(bufs[w]) + v), t);
 #pragma unroll
         for (int i = 0; i < V; i++) acc[i] = acc[i] + t[i];
     }
@@ -135,52 +181,21 @@ __device__ __forceinline__ void fold_vec(const PtrTable& bufs, int P, int64_t v,
         for (int i = 0; i < V; i++) acc[i] = div.apply(acc[i]);
     }
     const uint4 o = E::narrow(acc);
-    for (int i = 0; i < P; i++) store_stream(static_cast<uint4*>(bufs.p[i]) + v, o);
+    for (int i = 0; i < P; i++) store_stream(static_cast<uint4*>(bufs[i]) + v, o);
 }
 
-// VPT 16-byte vectors per thread and BATCH worker loads in flight: one vector
-// and 16 loads for P <= 8, two vectors and 8 loads for larger P (measured).
-template <ga_dtype DT, int VPT, int BATCH>
-__global__ __launch_bounds__(kThreads) void ring_fused_vec_kernel(PtrTable bufs, int P, int64_t N,
-                                                                  int64_t plen, int64_t n_vec,
-                                                                  Div div) {
+// The P workers' 16-byte vectors v[j] (where ok[j]), every element folded
+// from worker rt.r in direction rt.dir: BATCH worker loads in flight per
+// vector, then the average, stored to all P workers.
+template <ga_dtype DT, int VPT, int BATCH, typename PS>
+__device__ __forceinline__ void fold_uniform(const PS& bufs, int P, const int64_t* v,
+                                             const bool* ok, Rot rt, Div div) {
     using E = Elem<DT>;
     constexpr int V = E::kVec;
-    const int64_t vb0 = (int64_t)blockIdx.x * (kThreads * VPT);
-    const int64_t vb1 = min(vb0 + (int64_t)(kThreads * VPT), n_vec);
-    const Where first = locate(vb0 * V, N, plen, P);
-    const Where last = locate(vb1 * V - 1, N, plen, P);
-
-    if (first.part != last.part || first.chunk != last.chunk) {
-        // straddles a chunk or partition boundary: every thread folds its own
-        // vectors with their own rotation; only a vector that itself crosses
-        // a boundary goes element by element
-        for (int j = 0; j < VPT; j++) {
-            const int64_t v = vb0 + threadIdx.x + (int64_t)j * kThreads;
-            if (v >= vb1) continue;
-            const Where a = locate(v * V, N, plen, P);
-            const Where b = locate(v * V + V - 1, N, plen, P);
-            if (a.part == b.part && a.chunk == b.chunk) {
-                fold_vec<DT>(bufs, P, v, a.chunk, div);
-            } else {
-                for (int i = 0; i < V; i++) fold_one<DT>(bufs, P, N, plen, v * V + i, div);
-            }
-        }
-        return;
-    }
-
-    const int r = first.chunk;  // every element of this workgroup starts its fold at worker r
-    int64_t v[VPT];
-    bool ok[VPT];
-#pragma unroll
-    for (int j = 0; j < VPT; j++) {
-        v[j] = vb0 + threadIdx.x + (int64_t)j * kThreads;
-        ok[j] = v[j] < vb1;
-    }
-
+    const int r = rt.r;
     float acc[VPT][V];
     {
-        const uint4* src = static_cast<const uint4*>(bufs.p[r]);
+        const uint4* src = static_cast<const uint4*>(bufs[r]);
 #pragma unroll
         for (int j = 0; j < VPT; j++) {
             uint4 raw = ok[j] ? load_stream(src + v[j]) : make_uint4(0, 0, 0, 0);
@@ -192,9 +207,10 @@ __global__ __launch_bounds__(kThreads) void ring_fused_vec_kernel(PtrTable bufs,
 #pragma unroll
         for (int kk = 0; kk < BATCH; kk++) {
             if (k + kk < P) {
-                int w = r + k + kk;
+                int w = rt.dir < 0 ? r - (k + kk) : r + k + kk;
                 if (w >= P) w -= P;
-                const uint4* src = static_cast<const uint4*>(bufs.p[w]);
+                if (w < 0) w += P;
+                const uint4* src = static_cast<const uint4*>(bufs[w]);
 #pragma unroll
                 for (int j = 0; j < VPT; j++)
                     raw[kk][j] = ok[j] ? load_stream(src + v[j]) : make_uint4(0, 0, 0, 0);
@@ -223,20 +239,130 @@ __global__ __launch_bounds__(kThreads) void ring_fused_vec_kernel(PtrTable bufs,
         out[j] = E::narrow(acc[j]);
     }
     for (int w = 0; w < P; w++) {
-        uint4* dst = static_cast<uint4*>(bufs.p[w]);
+        uint4* dst = static_cast<uint4*>(bufs[w]);
 #pragma unroll
         for (int j = 0; j < VPT; j++)
             if (ok[j]) store_stream(dst + v[j], out[j]);
     }
 }
 
-template <ga_dtype DT>
+// VPT 16-byte vectors per thread and BATCH worker loads in flight: one vector
+// and 16 loads for P <= 8, two vectors and 8 loads for larger P (measured).
+template <ga_dtype DT, int VPT, int BATCH, bool DUAL>
+__global__ __launch_bounds__(kThreads) void ring_fused_vec_kernel(PtrTable bufs, int P, int64_t N,
+                                                                  int64_t plen, int64_t n_vec,
+                                                                  Div div) {
+    using E = Elem<DT>;
+    constexpr int V = E::kVec;
+    const int nch = DUAL ? 2 * P : P;
+    const int64_t vb0 = (int64_t)blockIdx.x * (kThreads * VPT);
+    const int64_t vb1 = min(vb0 + (int64_t)(kThreads * VPT), n_vec);
+    const Where first = locate(vb0 * V, N, plen, nch);
+    const Where last = locate(vb1 * V - 1, N, plen, nch);
+
+    if (first.part != last.part || first.chunk != last.chunk) {
+        // straddles a chunk or partition boundary: every thread folds its own
+        // vectors with their own rotation; only a vector that itself crosses
+        // a boundary goes element by element
+        for (int j = 0; j < VPT; j++) {
+            const int64_t v = vb0 + threadIdx.x + (int64_t)j * kThreads;
+            if (v >= vb1) continue;
+            const Where a = locate(v * V, N, plen, nch);
+            const Where b = locate(v * V + V - 1, N, plen, nch);
+            if (a.part == b.part && a.chunk == b.chunk) {
+                fold_vec<DT>(ArgPtrs{bufs}, P, v, rot_of<DUAL>(a.chunk, P), div);
+            } else {
+                for (int i = 0; i < V; i++) fold_one<DT, DUAL>(bufs, P, N, plen, v * V + i, div);
+            }
+        }
+        return;
+    }
+
+    // every element of this workgroup starts its fold at worker r, direction dir
+    int64_t v[VPT];
+    bool ok[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; j++) {
+        v[j] = vb0 + threadIdx.x + (int64_t)j * kThreads;
+        ok[j] = v[j] < vb1;
+    }
+    fold_uniform<DT, VPT, BATCH>(ArgPtrs{bufs}, P, v, ok, rot_of<DUAL>(first.chunk, P), div);
+}
+
+template <ga_dtype DT, bool DUAL>
 __global__ __launch_bounds__(kThreads) void ring_fused_elem_kernel(PtrTable bufs, int P, int64_t N,
                                                                    int64_t plen, int64_t e_begin,
                                                                    int64_t e_end, Div div) {
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     for (int64_t e = e_begin + (int64_t)blockIdx.x * kThreads + threadIdx.x; e < e_end; e += stride)
-        fold_one<DT>(bufs, P, N, plen, e, div);
+        fold_one<DT, DUAL>(bufs, P, N, plen, e, div);
+}
+
+// ---------------------------------------------------------------- zero-copy fusion ring
+
+// Largest t with T[t].vstart <= u: the tensor holding work vector u.
+__device__ __forceinline__ int64_t tensor_of(const ga_fusion_tensor* T, int64_t nt, int64_t u) {
+    int64_t lo = 0, hi = nt - 1;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) >> 1;
+        if (T[mid].vstart <= u) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Tensor Fusion without the copies: the fold of a fusion buffer is taken at
+// each tensor's own memory. Work vector u is 16 bytes of one tensor (its
+// last one possibly short); its elements sit at buffer offsets start + j,
+// which decide the partition, chunk and so the fold order, exactly as in the
+// packed buffer. A workgroup whose vectors are whole, lie in one tensor with
+// 16-byte aligned copies, and share one chunk folds with one rotation and
+// the tensor's pointers read once; any other takes them vector by vector.
+template <ga_dtype DT, bool DUAL>
+__global__ __launch_bounds__(kThreads) void fusion_ring_kernel(const ga_fusion_tensor* __restrict__ T,
+                                                               void* const* __restrict__ ptrs,
+                                                               int64_t nt, int64_t n_work, int P,
+                                                               int64_t fill, int64_t plen, Div div) {
+    using E = Elem<DT>;
+    constexpr int V = E::kVec;
+    const int nch = DUAL ? 2 * P : P;
+    const int64_t u0 = (int64_t)blockIdx.x * kThreads;
+    const int64_t u1 = min(u0 + (int64_t)kThreads, n_work);
+    const int64_t t0 = tensor_of(T, nt, u0);
+    if (tensor_of(T, nt, u1 - 1) == t0 && T[t0].vec) {
+        const ga_fusion_tensor d = T[t0];
+        const int64_t j0 = u0 - d.vstart, j1 = u1 - d.vstart;     // vectors of the tensor
+        if (j1 * V <= d.n) {
+            const Where first = locate(d.start + j0 * V, fill, plen, nch);
+            const Where last = locate(d.start + j1 * V - 1, fill, plen, nch);
+            if (first.part == last.part && first.chunk == last.chunk) {
+                const RowPtrs row{ptrs + t0 * P};
+                int64_t v[1] = {j0 + threadIdx.x};
+                bool ok[1] = {v[0] < j1};
+                const Rot rt = rot_of<DUAL>(first.chunk, P);
+                if (P <= 8) fold_uniform<DT, 1, 16>(row, P, v, ok, rt, div);
+                else fold_uniform<DT, 1, 8>(row, P, v, ok, rt, div);
+                return;
+            }
+        }
+    }
+    const int64_t u = u0 + threadIdx.x;
+    if (u >= u1) return;
+    const int64_t t = tensor_of(T, nt, u);
+    const ga_fusion_tensor d = T[t];
+    const RowPtrs row{ptrs + t * P};
+    const int64_t j = u - d.vstart;
+    const int64_t e0 = j * V, e1 = min(e0 + V, d.n);                // tensor elements
+    if (d.vec && e1 - e0 == V) {
+        const Where a = locate(d.start + e0, fill, plen, nch);
+        const Where b = locate(d.start + e1 - 1, fill, plen, nch);
+        if (a.part == b.part && a.chunk == b.chunk) {
+            fold_vec<DT>(row, P, j, rot_of<DUAL>(a.chunk, P), div);
+            return;
+        }
+    }
+    for (int64_t e = e0; e < e1; e++)
+        fold_elem<DT>(row, P, e, rot_of<DUAL>(locate(d.start + e, fill, plen, nch).chunk, P), div);
 }
 
 // ---------------------------------------------------------------- stepwise
@@ -338,6 +464,52 @@ bool disjoint(void* const* bufs, int P, int64_t bytes) {
     return true;
 }
 
+// The fused fold over the whole buffer: the vector kernel over 16-byte
+// vectors when every buffer is 16-byte aligned, the element kernel for the
+// rest. Returns the number of launches, or a negative status.
+template <bool DUAL>
+int64_t launch_fused(void* const* bufs, int P, int64_t N, ga_dtype dt, int64_t plen, Div div,
+                     hipStream_t hs, const char* what) {
+    const int64_t n_vec = N / (dt == GA_F32 ? 4 : 8);
+    const int64_t vec_elems = n_vec * (dt == GA_F32 ? 4 : 8);
+    bool vec_ok = true;
+    for (int i = 0; i < P; i++) vec_ok = vec_ok && aligned(bufs[i], 16);
+    PtrTable t{};
+    for (int i = 0; i < P; i++) t.p[i] = bufs[i];
+    int64_t launches = 0;
+    ga_status rc;
+    if (vec_ok && n_vec > 0) {
+        const bool wide = P > 8;
+        const unsigned blocks = (unsigned)ceil_div(n_vec, (int64_t)kThreads * (wide ? 2 : 1));
+        if (dt == GA_F32 && wide)
+            hipLaunchKernelGGL((ring_fused_vec_kernel<GA_F32, 2, 8, DUAL>), dim3(blocks),
+                               dim3(kThreads), 0, hs, t, P, N, plen, n_vec, div);
+        else if (dt == GA_F32)
+            hipLaunchKernelGGL((ring_fused_vec_kernel<GA_F32, 1, 16, DUAL>), dim3(blocks),
+                               dim3(kThreads), 0, hs, t, P, N, plen, n_vec, div);
+        else if (wide)
+            hipLaunchKernelGGL((ring_fused_vec_kernel<GA_BF16, 2, 8, DUAL>), dim3(blocks),
+                               dim3(kThreads), 0, hs, t, P, N, plen, n_vec, div);
+        else
+            hipLaunchKernelGGL((ring_fused_vec_kernel<GA_BF16, 1, 16, DUAL>), dim3(blocks),
+                               dim3(kThreads), 0, hs, t, P, N, plen, n_vec, div);
+        launches++;
+        if ((rc = check_launch(what))) return rc;
+    }
+    const int64_t e0 = (vec_ok && n_vec > 0) ? vec_elems : 0;
+    if (e0 < N) {
+        if (dt == GA_F32)
+            hipLaunchKernelGGL((ring_fused_elem_kernel<GA_F32, DUAL>), dim3(elem_grid(N - e0)),
+                               dim3(kThreads), 0, hs, t, P, N, plen, e0, N, div);
+        else
+            hipLaunchKernelGGL((ring_fused_elem_kernel<GA_BF16, DUAL>), dim3(elem_grid(N - e0)),
+                               dim3(kThreads), 0, hs, t, P, N, plen, e0, N, div);
+        launches++;
+        if ((rc = check_launch(what))) return rc;
+    }
+    return launches;
+}
+
 }  // namespace
 }  // namespace ga
 
@@ -349,7 +521,7 @@ extern "C" ga_status ga_ring_allreduce_sim(void* const* bufs, int32_t P, int64_t
     const char* what = "ga_ring_allreduce_sim";
     if (!valid_dtype(dt)) return fail(GA_EINVAL, "%s: unknown dtype %d", what, (int)dt);
     if (op != GA_SUM && op != GA_AVG) return fail(GA_EINVAL, "%s: unknown op %d", what, (int)op);
-    if (mode != GA_RING_FUSED && mode != GA_RING_STEPWISE)
+    if (mode != GA_RING_FUSED && mode != GA_RING_STEPWISE && mode != GA_RING_DUAL)
         return fail(GA_EINVAL, "%s: unknown mode %d", what, (int)mode);
     if (N < 0 || part_elems < 0) return fail(GA_EINVAL, "%s: negative size", what);
     if (P < 1 || P > GA_MAX_WORKERS)
@@ -375,14 +547,18 @@ extern "C" ga_status ga_ring_allreduce_sim(void* const* bufs, int32_t P, int64_t
 
     ga_ring_stats s{};
     {
+        // every step sends one chunk per ring; the dual ring sends one
+        // sub-chunk of ceil(n / 2P) in each direction
         int64_t bytes = 0;
         for (int64_t p0 = 0; p0 < N; p0 += plen) {
             int64_t n = N - p0 < plen ? N - p0 : plen;
-            bytes += 2 * (int64_t)(P - 1) * ceil_div(n, P) * (int64_t)es;
+            bytes += mode == GA_RING_DUAL
+                         ? 2 * 2 * (int64_t)(P - 1) * ceil_div(n, 2 * (int64_t)P) * (int64_t)es
+                         : 2 * (int64_t)(P - 1) * ceil_div(n, P) * (int64_t)es;
         }
         s.steps = N > 0 ? 2 * (int64_t)(P - 1) : 0;
         s.bytes_sent_per_worker = bytes;
-        if (mode == GA_RING_FUSED)
+        if (mode != GA_RING_STEPWISE)
             s.hbm_bytes = (P > 1) ? 2 * (int64_t)P * N * (int64_t)es : 0;
         else
             s.hbm_bytes = 5 * (int64_t)(P - 1) * N * (int64_t)es;
@@ -394,40 +570,12 @@ extern "C" ga_status ga_ring_allreduce_sim(void* const* bufs, int32_t P, int64_t
 
     if (N > 0 && P > 1) {
         const int64_t vblocks = ceil_div(n_vec, kThreads * kVecPerThread);
-        if (mode == GA_RING_FUSED) {
-            if (vec_ok && n_vec > 0) {
-                PtrTable t{};
-                for (int i = 0; i < P; i++) t.p[i] = bufs[i];
-                const bool wide = P > 8;
-                const unsigned blocks = (unsigned)ceil_div(n_vec, (int64_t)kThreads * (wide ? 2 : 1));
-                if (dt == GA_F32 && wide)
-                    hipLaunchKernelGGL((ring_fused_vec_kernel<GA_F32, 2, 8>), dim3(blocks),
-                                       dim3(kThreads), 0, hs, t, P, N, plen, n_vec, div);
-                else if (dt == GA_F32)
-                    hipLaunchKernelGGL((ring_fused_vec_kernel<GA_F32, 1, 16>), dim3(blocks),
-                                       dim3(kThreads), 0, hs, t, P, N, plen, n_vec, div);
-                else if (wide)
-                    hipLaunchKernelGGL((ring_fused_vec_kernel<GA_BF16, 2, 8>), dim3(blocks),
-                                       dim3(kThreads), 0, hs, t, P, N, plen, n_vec, div);
-                else
-                    hipLaunchKernelGGL((ring_fused_vec_kernel<GA_BF16, 1, 16>), dim3(blocks),
-                                       dim3(kThreads), 0, hs, t, P, N, plen, n_vec, div);
-                launches++;
-                if ((rc = check_launch(what))) return rc;
-            }
-            const int64_t e0 = (vec_ok && n_vec > 0) ? vec_elems : 0;
-            if (e0 < N) {
-                PtrTable t{};
-                for (int i = 0; i < P; i++) t.p[i] = bufs[i];
-                if (dt == GA_F32)
-                    hipLaunchKernelGGL(ring_fused_elem_kernel<GA_F32>, dim3(elem_grid(N - e0)),
-                                       dim3(kThreads), 0, hs, t, P, N, plen, e0, N, div);
-                else
-                    hipLaunchKernelGGL(ring_fused_elem_kernel<GA_BF16>, dim3(elem_grid(N - e0)),
-                                       dim3(kThreads), 0, hs, t, P, N, plen, e0, N, div);
-                launches++;
-                if ((rc = check_launch(what))) return rc;
-            }
+        if (mode == GA_RING_FUSED || mode == GA_RING_DUAL) {
+            const int64_t n = mode == GA_RING_DUAL
+                                  ? launch_fused<true>(bufs, P, N, dt, plen, div, hs, what)
+                                  : launch_fused<false>(bufs, P, N, dt, plen, div, hs, what);
+            if (n < 0) return (ga_status)n;
+            launches += n;
         } else {
             PtrTable t{};
             for (int i = 0; i < P; i++) t.p[i] = bufs[i];
@@ -452,6 +600,110 @@ extern "C" ga_status ga_ring_allreduce_sim(void* const* bufs, int32_t P, int64_t
         }
     }
     s.launches = launches;
+    if (st) *st = s;
+    return GA_OK;
+}
+
+// ---------------------------------------------------------------- zero-copy fusion ring (host)
+
+extern "C" ga_status ga_fusion_ring_plan(ga_fusion_tensor* h_tensors, void* const* h_ptrs,
+                                         int64_t n_tensors, int32_t P, ga_dtype dt, int64_t fill,
+                                         int64_t* n_work) {
+    const char* what = "ga_fusion_ring_plan";
+    if (!valid_dtype(dt)) return fail(GA_EINVAL, "%s: unknown dtype %d", what, (int)dt);
+    if (P < 1 || P > GA_MAX_WORKERS)
+        return fail(GA_EINVAL, "%s: P = %d outside [1, %d]", what, P, GA_MAX_WORKERS);
+    if (n_tensors < 0 || fill < 0 || !n_work) return fail(GA_EINVAL, "%s: bad sizes", what);
+    if (n_tensors > 0 && (!h_tensors || !h_ptrs)) return fail(GA_EINVAL, "%s: null table", what);
+    const int64_t es = (int64_t)elem_size(dt);
+    const int64_t V = 16 / es;
+    int64_t off = 0, nv = 0;
+    std::vector<std::pair<uintptr_t, uintptr_t>> spans;
+    spans.reserve((size_t)(n_tensors * P));
+    for (int64_t t = 0; t < n_tensors; t++) {
+        ga_fusion_tensor& d = h_tensors[t];
+        if (d.n < 0 || d.start != off)
+            return fail(GA_EINVAL, "%s: tensor %lld is not dense in buffer order (start %lld, "
+                        "expected %lld)", what, (long long)t, (long long)d.start, (long long)off);
+        int vec = 1;
+        for (int i = 0; i < P; i++) {
+            const void* q = h_ptrs[t * P + i];
+            if (d.n > 0 && (!q || !aligned(q, (uintptr_t)es)))
+                return fail(GA_EINVAL, "%s: tensor %lld, worker %d: null or misaligned pointer",
+                            what, (long long)t, i);
+            vec = vec && aligned(q, 16);
+            if (d.n > 0) spans.push_back({(uintptr_t)q, (uintptr_t)q + (uintptr_t)(d.n * es)});
+        }
+        d.vstart = nv;
+        d.vec = vec;
+        d.reserved = 0;
+        off += d.n;
+        nv += ceil_div(d.n, V);
+    }
+    if (off != fill)
+        return fail(GA_EINVAL, "%s: tensors cover %lld elements, fill is %lld", what,
+                    (long long)off, (long long)fill);
+    std::sort(spans.begin(), spans.end());
+    for (size_t k = 1; k < spans.size(); k++)
+        if (spans[k].first < spans[k - 1].second)
+            return fail(GA_EINVAL, "%s: two tensor copies overlap", what);
+    *n_work = nv;
+    return GA_OK;
+}
+
+extern "C" ga_status ga_fusion_ring_allreduce(const ga_fusion_tensor* d_tensors, void* const* d_ptrs,
+                                              int64_t n_tensors, int64_t n_work, int32_t P,
+                                              int64_t fill, ga_dtype dt, ga_op op, ga_ring_mode mode,
+                                              int64_t part_elems, ga_ring_stats* st, void* stream) {
+    const char* what = "ga_fusion_ring_allreduce";
+    if (!valid_dtype(dt)) return fail(GA_EINVAL, "%s: unknown dtype %d", what, (int)dt);
+    if (op != GA_SUM && op != GA_AVG) return fail(GA_EINVAL, "%s: unknown op %d", what, (int)op);
+    if (mode == GA_RING_STEPWISE)
+        return fail(GA_ENOTSUP, "%s: the zero-copy ring runs the fused fold only", what);
+    if (mode != GA_RING_FUSED && mode != GA_RING_DUAL)
+        return fail(GA_EINVAL, "%s: unknown mode %d", what, (int)mode);
+    if (P < 1 || P > GA_MAX_WORKERS)
+        return fail(GA_EINVAL, "%s: P = %d outside [1, %d]", what, P, GA_MAX_WORKERS);
+    if (n_tensors < 0 || n_work < 0 || fill < 0 || part_elems < 0)
+        return fail(GA_EINVAL, "%s: negative size", what);
+    if (n_work > 0 && (n_tensors == 0 || fill == 0))
+        return fail(GA_EINVAL, "%s: work without tensors", what);
+    const int64_t es = (int64_t)elem_size(dt);
+    ga_ring_stats s{};
+    if (fill > 0) {
+        const int64_t plen = part_elems > 0 ? part_elems : fill;
+        const int nch = mode == GA_RING_DUAL ? 2 * P : P;
+        int64_t bytes = 0;
+        for (int64_t p0 = 0; p0 < fill; p0 += plen) {
+            const int64_t n = fill - p0 < plen ? fill - p0 : plen;
+            bytes += 2 * (int64_t)(P - 1) * (nch / P) * ceil_div(n, nch) * es;
+        }
+        s.steps = 2 * (int64_t)(P - 1);
+        s.bytes_sent_per_worker = bytes;
+        s.hbm_bytes = P > 1 ? 2 * (int64_t)P * fill * es : 0;
+    }
+    if (n_work == 0 || P == 1) {
+        if (st) *st = s;
+        return GA_OK;
+    }
+    if (!d_tensors || !d_ptrs || !aligned(d_tensors, 8) || !aligned(d_ptrs, 8))
+        return fail(GA_EINVAL, "%s: null or misaligned table", what);
+    if (ceil_div(n_work, kThreads) > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: too much work", what);
+    const int64_t plen = part_elems > 0 ? part_elems : fill;
+    Div div{op == GA_AVG, (P & (P - 1)) == 0, (float)P, 1.0f / (float)P};
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)ceil_div(n_work, kThreads));
+    if (dt == GA_F32 && mode == GA_RING_DUAL)
+        hipLaunchKernelGGL((fusion_ring_kernel<GA_F32, true>), grid, dim3(kThreads), 0, hs, d_tensors, d_ptrs, n_tensors, n_work, P, fill, plen, div);
+    else if (dt == GA_F32)
+        hipLaunchKernelGGL((fusion_ring_kernel<GA_F32, false>), grid, dim3(kThreads), 0, hs, d_tensors, d_ptrs, n_tensors, n_work, P, fill, plen, div);
+    else if (mode == GA_RING_DUAL)
+        hipLaunchKernelGGL((fusion_ring_kernel<GA_BF16, true>), grid, dim3(kThreads), 0, hs, d_tensors, d_ptrs, n_tensors, n_work, P, fill, plen, div);
+    else
+        hipLaunchKernelGGL((fusion_ring_kernel<GA_BF16, false>), grid, dim3(kThreads), 0, hs, d_tensors, d_ptrs, n_tensors, n_work, P, fill, plen, div);
+    ga_status rc = check_launch(what);
+    if (rc) return rc;
+    s.launches = 1;
     if (st) *st = s;
     return GA_OK;
 }

@@ -2,10 +2,12 @@
 
 A step runs, in this order, on the current stream:
   fused workloads (Tensor Fusion, Horovod page section 3.4):
-      pack every worker's tensors into its fusion buffers (one launch),
-      ring-average each fusion buffer across the P workers,
-      unpack the averages back into the tensors (one launch);
-      a tensor larger than the fusion buffer is reduced alone, in place;
+      zero_copy (default): ring-average each fusion buffer in place in the
+      workers' tensors, one launch per buffer, no copies;
+      else: pack every worker's tensors into its fusion buffers (one
+      launch), ring-average each fusion buffer across the P workers, unpack
+      the averages back into the tensors (one launch); a tensor larger than
+      the fusion buffer is reduced alone, in place;
   flat workloads (one gradient vector per worker):
       THC min/max per partition, USQ quantize for every bit width (both read
       the workers' gradients before the ring overwrites them),
@@ -89,8 +91,11 @@ class Pipeline:
     nu_tables: Dict[str, tuple] = {}
     rht: Dict[str, tuple] = {}
 
-    def __init__(self, name: str, device="cuda", cap_bytes: int = 64 << 20):
+    def __init__(self, name: str, device="cuda", cap_bytes: int = 64 << 20, zero_copy: bool = True,
+                 ring_mode: int = ga.RING_FUSED):
         self.w = synth.workload(name)
+        self.zero_copy = zero_copy
+        self.ring_mode = ring_mode
         self.device = torch.device(device)
         self.cap = cap_bytes
         self.tdt = torch.float32 if self.w.dtype == ga.F32 else torch.bfloat16
@@ -104,6 +109,10 @@ class Pipeline:
         if w.fused:
             self.tensors = [synth.worker_tensors(w, i, dev) for i in range(self.P)]
             self.buf_of, self.off_of, self.fill, _ = ga.ga_fuse_plan(w.sizes, None, self.cap)
+            if self.zero_copy:
+                self.fring = ga.FusionRing(self.tensors, self.buf_of, self.off_of, self.fill)
+                torch.cuda.synchronize()
+                return
             es = w.elem_bytes
             # a buffer holding one tensor larger than the capacity: reduce that
             # tensor in place instead of copying it
@@ -159,12 +168,18 @@ class Pipeline:
     # ------------------------------------------------------------ step
     def step(self, timer: Optional[StageTimer] = None) -> None:
         w = self.w
+        if w.fused and self.zero_copy:
+            for k in range(len(self.fill)):
+                _call(timer, "fusion_ring", self.fring.allreduce_buffer, k, ga.AVG, self.ring_mode,
+                      w.ring_part_elems)
+            return
         if w.fused:
             if self.tables is not None:
                 _call(timer, "fuse_pack", self.tables.pack)
             for k in range(len(self.fill)):
                 _call(timer, "ring_allreduce", ga.ga_ring_allreduce_sim,
-                      [self.bufs[i][k] for i in range(self.P)], ga.AVG, w.ring_part_elems)
+                      [self.bufs[i][k] for i in range(self.P)], ga.AVG, w.ring_part_elems,
+                      self.ring_mode)
             if self.tables is not None:
                 _call(timer, "fuse_unpack", self.tables.unpack)
             return
@@ -186,7 +201,7 @@ class Pipeline:
             _call(timer, f"thc_nuhc_quantize_{key}", ga.thc_nuhc_quantize, self.rht_y[key],
                   self.rht_mM[key], b, g, T, w.quant_seed, d, 0, self.packed[key])
         _call(timer, "ring_allreduce", ga.ga_ring_allreduce_sim, self.flat, ga.AVG,
-              w.ring_part_elems)
+              w.ring_part_elems, self.ring_mode)
         for key, (b, g, d, T) in self.rht.items():
             Np = self.rht_avg[key].numel()
             _call(timer, f"thc_nuhc_aggregate_{key}", ga.thc_nuhc_aggregate, self.packed[key], Np, b,
@@ -217,6 +232,9 @@ class Pipeline:
         """Algorithmic HBM bytes of one call of each stage (per launch)."""
         w, P, N, s = self.w, self.P, self.N, self.w.elem_bytes
         out = {}
+        if w.fused and self.zero_copy:
+            out["fusion_ring"] = 2.0 * P * N * s / len(self.fill)    # mean over the buffers
+            return out
         if w.fused:
             moved = sum(int(n) for t, n in enumerate(w.sizes) if self.buf_of[t] not in self.alone)
             out["fuse_pack"] = out["fuse_unpack"] = 2.0 * P * moved * s

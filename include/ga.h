@@ -4,7 +4,9 @@
  * one GPU's HBM.
  *
  *   ga_fuse_plan / ga_fuse_pack / ga_fuse_unpack   Tensor Fusion
- *   ga_ring_allreduce_sim                          ring all-reduce (sum | avg)
+ *   ga_ring_allreduce_sim                          ring all-reduce (sum | avg;
+ *                                                  single or bidirectional)
+ *   ga_fusion_ring_plan / ga_fusion_ring_allreduce zero-copy fusion ring
  *   thc_minmax / thc_usq_quantize / thc_int_aggregate / thc_dequant / thc_nmse
  *                                                  THC uniform quantization
  *   thc_nuhc_quantize / thc_nuhc_aggregate / thc_nuhc_dequant
@@ -66,7 +68,7 @@ typedef int ga_status;
 
 typedef enum { GA_F32 = 0, GA_BF16 = 1 } ga_dtype;
 typedef enum { GA_SUM = 0, GA_AVG = 1 } ga_op;
-typedef enum { GA_RING_FUSED = 0, GA_RING_STEPWISE = 1 } ga_ring_mode;
+typedef enum { GA_RING_FUSED = 0, GA_RING_STEPWISE = 1, GA_RING_DUAL = 2 } ga_ring_mode;
 
 /* ------------------------------------------------------------------ */
 /* Tensor Fusion  ([HVD] 3.4, Tensor Fusion steps 1-6)                  */
@@ -134,12 +136,13 @@ ga_status ga_fuse_unpack(const ga_copy_desc* d_desc, int64_t n_desc, int64_t tot
                          ga_dtype dt, void* stream);
 
 /* ------------------------------------------------------------------ */
-/* Ring all-reduce over P simulated workers  ([HVD] 3.4; [RING] 4, 5, 7) */
+/* Ring all-reduce over P simulated workers  ([HVD] 3.4; [RING] 4, 5, 7, 11) */
 /* ------------------------------------------------------------------ */
 
 typedef struct {
     int64_t steps;                 /* 2 (P - 1) communication steps per ring */
-    int64_t bytes_sent_per_worker; /* sum over partitions of 2 (P-1) C elem_bytes */
+    int64_t bytes_sent_per_worker; /* sum over partitions of 2 (P-1) C elem_bytes;
+                                      dual ring: 2 (P-1) 2 C2 elem_bytes */
     int64_t hbm_bytes;             /* algorithmic HBM bytes of the chosen mode */
     int64_t launches;              /* kernel launches enqueued */
 } ga_ring_stats;
@@ -169,12 +172,69 @@ typedef struct {
  *               2 (P - 1) launches moving the chunks as the schedule does
  *               (5 (P - 1) N elem_bytes); GA_F32 only (bf16 partials need
  *               binary32 storage on the wire) -> GA_ENOTSUP for GA_BF16.
+ *               GA_RING_DUAL: the bidirectional ring of [RING] section 11
+ *               (Exercise 1), executed like GA_RING_FUSED: each partition
+ *               is cut into 2P sub-chunks of C2 = ceil(n / 2P); sub-chunk c
+ *               < P goes round clockwise (folded c, c+1, ..., c-1), sub-chunk
+ *               P + c counter-clockwise (folded c, c-1, ..., c+1). Same
+ *               rounding rules and traffic as GA_RING_FUSED; a different
+ *               fold order, so results differ from it in the last bits.
  *   st          optional (nullable) host struct receiving the accounting.
- * Both modes give bit-identical results.
+ * GA_RING_FUSED and GA_RING_STEPWISE give bit-identical results.
  */
 ga_status ga_ring_allreduce_sim(void* const* bufs, int32_t P, int64_t N, ga_dtype dt, ga_op op,
                                 int64_t part_elems, ga_ring_mode mode, ga_ring_stats* st,
                                 void* stream);
+
+/* ------------------------------------------------------------------ */
+/* Zero-copy Tensor Fusion ring  ([HVD] 3.4: Tensor Fusion + ring)      */
+/* ------------------------------------------------------------------ */
+
+/*
+ * One tensor of a fusion buffer: elements [start, start + n) of the buffer
+ * the fusion plan assigned it to (ga_fuse_plan's offsets). vstart and vec
+ * are filled in by ga_fusion_ring_plan.
+ */
+typedef struct {
+    int64_t start;    /* offset in the fusion buffer, elements */
+    int64_t n;        /* elements */
+    int64_t vstart;   /* first work vector (16 bytes of the tensor) */
+    int32_t vec;      /* 1: all P copies are 16-byte aligned */
+    int32_t reserved; /* 0 */
+} ga_fusion_tensor;
+
+/*
+ * ga_fusion_ring_plan -- host-only check and completion of the table of one
+ * fusion buffer before ga_fusion_ring_allreduce: the n_tensors entries must
+ * be in buffer order and dense (start[0] = 0, start[t + 1] = start[t] +
+ * n[t], the last ending at fill); h_ptrs is a host array of n_tensors x P
+ * worker pointers (tensor-major: h_ptrs[t P + i] is worker i's copy of
+ * tensor t), each non-null and aligned to the element size, and no two of
+ * the P n_tensors regions may overlap. Fills vstart and vec; *n_work
+ * receives the number of work vectors. Enqueues nothing.
+ */
+ga_status ga_fusion_ring_plan(ga_fusion_tensor* h_tensors, void* const* h_ptrs, int64_t n_tensors,
+                              int32_t P, ga_dtype dt, int64_t fill, int64_t* n_work);
+
+/*
+ * ga_fusion_ring_allreduce -- in place in every worker's tensors: exactly
+ * what ga_fuse_pack, ga_ring_allreduce_sim over the fusion buffer (mode
+ * GA_RING_FUSED or GA_RING_DUAL, same op and part_elems) and ga_fuse_unpack
+ * leave in them, bit for bit, without the fusion buffers: each element is
+ * folded at its tensor's address in the order its buffer offset gives.
+ * HBM traffic 2 P fill elem_bytes instead of 6 P fill elem_bytes.
+ *   d_tensors, d_ptrs  device copies of the planned table and pointers
+ *   n_work             from ga_fusion_ring_plan
+ *   mode               GA_RING_FUSED or GA_RING_DUAL; GA_RING_STEPWISE ->
+ *                      GA_ENOTSUP
+ *   st                 optional accounting, as for ga_ring_allreduce_sim
+ * The device tables are trusted (ga_fusion_ring_plan checked their host
+ * originals); a table that does not match n_work or fill is undefined.
+ */
+ga_status ga_fusion_ring_allreduce(const ga_fusion_tensor* d_tensors, void* const* d_ptrs,
+                                   int64_t n_tensors, int64_t n_work, int32_t P, int64_t fill,
+                                   ga_dtype dt, ga_op op, ga_ring_mode mode, int64_t part_elems,
+                                   ga_ring_stats* st, void* stream);
 
 /* ------------------------------------------------------------------ */
 /* THC uniform stochastic quantization  ([THC] 2-4, Algorithm 1)        */

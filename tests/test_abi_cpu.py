@@ -27,7 +27,7 @@ def _declared():
 def test_header_declarations_are_exported():
     L = nat.load()
     names = _declared()
-    assert len(names) == 19
+    assert len(names) == 21
     assert set(names) == set(nat.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -186,3 +186,78 @@ def test_rht_argument_errors_before_enqueue():
     assert L.thc_rht_inverse(0x60000, 0, 8, 1, 0x70000, 0, None) == 0
     assert L.thc_rht_inverse(0x60002, 16, 8, 1, 0x70000, 0, None) == EINVAL
     assert b"thc_rht_inverse" in L.ga_last_error()
+
+
+def _ftable(sizes):
+    h = np.zeros(len(sizes), dtype=nat.FTENSOR_DTYPE)
+    off = 0
+    for r, n in enumerate(sizes):
+        h[r]["start"], h[r]["n"] = off, n
+        off += n
+    return h, off
+
+
+def test_fusion_ring_plan_fills_vectors_and_alignment():
+    sizes = [5, 8, 0, 13, 4]
+    h, fill = _ftable(sizes)
+    P = 3
+    ptrs = np.zeros((len(sizes), P), dtype=np.uint64)
+    base = 0x100000
+    for t, n in enumerate(sizes):
+        for i in range(P):
+            ptrs[t, i] = base
+            base += (n * 4 + 255) // 256 * 256 + 256
+    ptrs[3, 1] += 4                    # one misaligned (by 16) copy of tensor 3
+    n_work = nat.ga_fusion_ring_plan(h, ptrs, P, nat.F32, fill)
+    want_v = np.cumsum([0] + [-(-n // 4) for n in sizes])
+    assert n_work == want_v[-1]
+    assert h["vstart"].tolist() == want_v[:-1].tolist()
+    assert h["vec"].tolist() == [1, 1, 1, 0, 1]
+    h2, _ = _ftable(sizes)
+    assert nat.ga_fusion_ring_plan(h2, ptrs, P, nat.BF16, fill) == sum(-(-n // 8) for n in sizes)
+
+
+def test_fusion_ring_plan_errors():
+    sizes = [10, 20]
+    P = 2
+    ptrs = np.array([[0x10000, 0x20000], [0x30000, 0x40000]], dtype=np.uint64)
+    h, fill = _ftable(sizes)
+    with pytest.raises(nat.GAError):                              # fill mismatch
+        nat.ga_fusion_ring_plan(h, ptrs, P, nat.F32, fill + 1)
+    h, fill = _ftable(sizes)
+    h[1]["start"] += 1                                            # not dense
+    with pytest.raises(nat.GAError):
+        nat.ga_fusion_ring_plan(h, ptrs, P, nat.F32, fill)
+    h, fill = _ftable(sizes)
+    bad = ptrs.copy()
+    bad[1, 1] = 0x30010                                           # overlaps worker 0's copy
+    with pytest.raises(nat.GAError):
+        nat.ga_fusion_ring_plan(h, bad, P, nat.F32, fill)
+    bad = ptrs.copy()
+    bad[0, 0] = 0x10002                                           # misaligned for fp32
+    with pytest.raises(nat.GAError):
+        nat.ga_fusion_ring_plan(h, bad, P, nat.F32, fill)
+    assert nat.ga_fusion_ring_plan(h, bad, P, nat.BF16, fill) > 0
+    bad = ptrs.copy()
+    bad[1, 0] = 0
+    with pytest.raises(nat.GAError):
+        nat.ga_fusion_ring_plan(h, bad, P, nat.F32, fill)
+    h0 = np.zeros(0, dtype=nat.FTENSOR_DTYPE)
+    assert nat.ga_fusion_ring_plan(h0, np.zeros((0, P), dtype=np.uint64), P, nat.F32, 0) == 0
+
+
+def test_fusion_ring_allreduce_errors_before_enqueue():
+    L = nat.load()
+    st = nat.RingStats()
+    f = L.ga_fusion_ring_allreduce
+    assert f(0x1000, 0x2000, 2, 8, 2, 30, 0, 1, 1, 0, C.byref(st), None) == ENOTSUP   # stepwise
+    assert f(0x1000, 0x2000, 2, 8, 2, 30, 0, 1, 5, 0, None, None) == EINVAL            # mode
+    assert f(0x1000, 0x2000, 2, 8, 0, 30, 0, 1, 0, 0, None, None) == EINVAL            # P = 0
+    assert f(0x1000, 0x2000, 2, 8, 2, 30, 3, 1, 0, 0, None, None) == EINVAL            # dtype
+    assert f(0x1000, 0x2000, 2, 8, 2, 30, 0, 4, 0, 0, None, None) == EINVAL            # op
+    assert f(None, 0x2000, 2, 8, 2, 30, 0, 1, 0, 0, None, None) == EINVAL              # table
+    assert f(0x1000, 0x2000, 0, 8, 2, 0, 0, 1, 0, 0, None, None) == EINVAL             # work, no tensors
+    # nothing to do: still the accounting of the ring over fill elements
+    assert f(None, None, 0, 0, 4, 0, 0, 1, 0, 0, C.byref(st), None) == 0
+    assert f(0x1000, 0x2000, 2, 8, 1, 30, 0, 1, 2, 0, C.byref(st), None) == 0          # P = 1
+    assert st.steps == 0 and st.launches == 0

@@ -1,0 +1,201 @@
+"""GPU parity for the bidirectional ring and the zero-copy fusion ring.
+
+Dual ring (systemcraft ring all-reduce lesson, section 11, Exercise 1):
+ga_ring_allreduce_sim in GA_RING_DUAL mode against the oracle's
+bidirectional fold, bit for bit.
+
+Zero-copy fusion ring (Horovod page, section 3.4, Tensor Fusion + ring):
+folding every fusion buffer at its tensors' own addresses must leave
+exactly what pack -> ring -> unpack leaves, bit for bit; checked against
+the oracle's plan, pack, fold and unpack, and against the GPU copy path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gradient_all_reduce_worker_amd import _native as ga
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _bits(t):
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.numpy().view(np.uint32).copy()
+
+
+def _host(t):
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.numpy().copy()
+
+
+def _u(a):
+    return a.view(np.uint32) if a.dtype == np.float32 else a
+
+
+def _vec(P, N, dt, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((P, N)) * np.exp(rng.uniform(-8, 8, size=(P, N)))
+    t = torch.from_numpy(x.astype(np.float32))
+    if dt == ga.BF16:
+        t = t.to(torch.bfloat16)
+    return [t[i].clone().to(DEV) for i in range(P)]
+
+
+DUAL_SHAPES = [(1, 1000, 0), (2, 4103, 0), (3, 6, 0), (3, 70001, 1000), (4, 1 << 16, 0),
+               (5, 33, 0), (7, 9999, 4096), (8, 1 << 20, 1 << 16), (13, 20000, 0),
+               (16, 100003, 8192), (33, 50000, 777), (64, 70000, 1 << 12), (8, 7, 0), (6, 0, 0)]
+
+
+@pytest.mark.parametrize("dt", [ga.F32, ga.BF16])
+@pytest.mark.parametrize("op", [ga.SUM, ga.AVG])
+@pytest.mark.parametrize("P,N,part", DUAL_SHAPES)
+def test_dual_ring(P, N, part, dt, op):
+    bufs = _vec(P, N, dt, seed=P * 104729 + N)
+    ref = [_host(b) for b in bufs]
+    st = ga.ga_ring_allreduce_sim(bufs, op=op, part_elems=part, mode=ga.RING_DUAL)
+    oracle.dual_ring_fold(ref, op=op, part=part)
+    for i in range(P):
+        assert np.array_equal(_bits(bufs[i]), _u(ref[i])), i
+    if N and P > 1:
+        es = 4 if dt == ga.F32 else 2
+        plen = part or N
+        want = sum(2 * (P - 1) * 2 * -(-min(plen, N - p0) // (2 * P)) * es
+                   for p0 in range(0, N, plen))
+        assert st["bytes_sent_per_worker"] == want and st["hbm_bytes"] == 2 * P * N * es
+
+
+def test_dual_ring_misaligned():
+    P, N = 5, 3001
+    big = _vec(P, N + 1, ga.F32, seed=5)
+    views = [b[1:] for b in big]
+    ref = [_host(v) for v in views]
+    ga.ga_ring_allreduce_sim(views, op=ga.AVG, part_elems=1000, mode=ga.RING_DUAL)
+    oracle.dual_ring_fold(ref, op=ga.AVG, part=1000)
+    for i in range(P):
+        assert np.array_equal(_bits(views[i]), _u(ref[i]))
+
+
+# ------------------------------------------------------------------ zero-copy fusion ring
+
+def _sizes(T, seed, lo=1, hi=300_000, extra=()):
+    rng = np.random.default_rng(seed)
+    s = [int(round(np.exp(v))) for v in rng.uniform(np.log(lo), np.log(hi), size=T)]
+    return list(extra) + s
+
+
+def _tensors(P, sizes, dt, seed, misalign=0):
+    """P workers' tensor lists; misalign > 0 carves every tensor from a slab
+    at an odd element offset, so copies are not 16-byte aligned."""
+    tdt = torch.float32 if dt == ga.F32 else torch.bfloat16
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(P):
+        ts = []
+        for n in sizes:
+            x = torch.from_numpy((rng.standard_normal(n) * np.exp(rng.uniform(-6, 6, size=n)))
+                                 .astype(np.float32)).to(tdt)
+            if misalign:
+                slab = torch.empty(n + misalign, dtype=tdt, device=DEV)
+                v = slab[misalign:]
+                v.copy_(x)
+                ts.append(v)
+            else:
+                ts.append(x.to(DEV))
+        out.append(ts)
+    return out
+
+
+def _oracle_fused(host, sizes, dt, cap, op, part, dual):
+    buf_of, off_of, fill, _ = oracle.fuse_plan(sizes, [dt] * len(sizes), cap)
+    npdt = np.float32 if dt == ga.F32 else np.uint16
+    P = len(host)
+    fused = [oracle.fuse_pack(host[i], buf_of, off_of, fill, npdt) for i in range(P)]
+    for k in range(len(fill)):
+        fold = oracle.dual_ring_fold if dual else oracle.ring_fold
+        fold([fused[i][k] for i in range(P)], op=op, part=part)
+    return [oracle.fuse_unpack(fused[i], buf_of, off_of, sizes) for i in range(P)]
+
+
+@pytest.mark.parametrize("mode", [ga.RING_FUSED, ga.RING_DUAL])
+@pytest.mark.parametrize("dt", [ga.F32, ga.BF16])
+@pytest.mark.parametrize("P,T,cap,part,op,misalign", [
+    (2, 40, 1 << 20, 0, ga.AVG, 0),
+    (3, 60, 1 << 19, 0, ga.SUM, 0),
+    (8, 80, 1 << 22, 4099, ga.AVG, 0),
+    (16, 50, 1 << 21, 0, ga.AVG, 0),
+    (5, 30, 1 << 20, 0, ga.AVG, 1),
+    (33, 20, 1 << 20, 1000, ga.AVG, 0),
+])
+def test_zero_copy_matches_pack_ring_unpack(P, T, cap, part, op, misalign, dt, mode):
+    sizes = _sizes(T, seed=P * 13 + T, extra=(0, 1, 3, 4, 5, 8, 1 << 18))
+    ts = _tensors(P, sizes, dt, seed=P + T + misalign, misalign=misalign)
+    host = [[_host(x) for x in row] for row in ts]
+    want = _oracle_fused(host, sizes, dt, cap, op, part, mode == ga.RING_DUAL)
+    buf_of, off_of, fill, _ = ga.ga_fuse_plan(sizes, [dt] * len(sizes), cap)
+    fr = ga.FusionRing(ts, buf_of, off_of, fill)
+    fr.allreduce(op=op, mode=mode, part_elems=part)
+    torch.cuda.synchronize()
+    for i in range(P):
+        for t in range(len(sizes)):
+            assert np.array_equal(_host(ts[i][t]).view(np.uint8), want[i][t].view(np.uint8)), (i, t)
+
+
+def test_zero_copy_equals_gpu_copy_path():
+    """Same bits as the GPU's own pack -> fused ring -> unpack."""
+    P, dt, cap = 8, ga.F32, 1 << 22
+    sizes = _sizes(120, seed=3, extra=(1 << 21,))         # one tensor above the cap
+    a = _tensors(P, sizes, dt, seed=11)
+    b = [[x.clone() for x in row] for row in a]
+    buf_of, off_of, fill, _ = ga.ga_fuse_plan(sizes, None, cap)
+    ga.FusionRing(a, buf_of, off_of, fill).allreduce(op=ga.AVG)
+    bufs = [[torch.empty(f, dtype=torch.float32, device=DEV) for f in fill] for _ in range(P)]
+    tables = ga.FusionTables(b, bufs, buf_of, off_of)
+    tables.pack()
+    for k in range(len(fill)):
+        ga.ga_ring_allreduce_sim([bufs[i][k] for i in range(P)], op=ga.AVG)
+    tables.unpack()
+    torch.cuda.synchronize()
+    for i in range(P):
+        for t in range(len(sizes)):
+            assert torch.equal(a[i][t].view(torch.int32), b[i][t].view(torch.int32)), (i, t)
+
+
+def test_zero_copy_leaves_neighbours_alone():
+    """Tensors carved from one slab at 16-byte aligned offsets with at least
+    three guard words after each: the guards keep their values (a tensor's
+    short last vector is written element by element)."""
+    P, sizes = 4, [5, 1, 7, 1000, 3, 4]
+    starts, o = [], 4
+    for n in sizes:
+        starts.append(o)
+        o = (o + n + 3 + 3) // 4 * 4
+    total = o + 4
+    slabs, ts = [], []
+    for i in range(P):
+        slab = torch.full((total,), 9.5, device=DEV)
+        row = []
+        for st, n in zip(starts, sizes):
+            v = slab[st:st + n]
+            v.copy_(torch.randn(n, device=DEV))
+            row.append(v)
+        slabs.append(slab)
+        ts.append(row)
+    host = [[_host(x) for x in row] for row in ts]
+    want = _oracle_fused(host, sizes, ga.F32, 1 << 20, ga.AVG, 0, False)
+    buf_of, off_of, fill, _ = ga.ga_fuse_plan(sizes, None, 1 << 20)
+    fr = ga.FusionRing(ts, buf_of, off_of, fill)
+    fr.allreduce(op=ga.AVG)
+    torch.cuda.synchronize()
+    for i in range(P):
+        for t in range(len(sizes)):
+            assert np.array_equal(_host(ts[i][t]).view(np.uint32), want[i][t].view(np.uint32))
+        mask = torch.ones(total, dtype=torch.bool, device=DEV)
+        for st, n in zip(starts, sizes):
+            mask[st:st + n] = False
+        assert torch.all(slabs[i][mask] == 9.5)

@@ -142,9 +142,10 @@ def test_small_workload_full():
     assert abs(pipe.nmse[4].cpu().numpy()[2] - nm[2]) <= 1e-6 * nm[2]
 
 
+@pytest.mark.parametrize("zero_copy", [True, False])
 @pytest.mark.parametrize("name", ["fusion", "resnet101"])
-def test_fused_workload_full(name):
-    pipe = Pipeline(name)
+def test_fused_workload_full(name, zero_copy):
+    pipe = Pipeline(name, zero_copy=zero_copy)
     print(f"workload {name}: P={pipe.P} N={pipe.N}", flush=True)
     pipe.setup()
     w = pipe.w
