@@ -46,6 +46,9 @@ def lib():
         L.orc_dual_ring_fold.argtypes = [C.POINTER(vp), i32, i64, i32, i32, i64]
         L.orc_dual_ring_stepwise.argtypes = [C.POINTER(vp), i32, i64, i32, i32, i64]
         L.orc_ring_stats.argtypes = [i32, i64, i64, i32, C.POINTER(i64), C.POINTER(i64)]
+        L.orc_ef_add.argtypes = [vp, i32, vp, i64, vp]
+        L.orc_ef_add.restype = None
+        L.orc_ef_update.argtypes = [vp, vp, i64, i32, i32, vp, i64, vp, vp]
         L.orc_ring_stats.restype = None
         L.orc_minmax.argtypes = [C.POINTER(vp), i32, i64, i32, i64, vp]
         L.orc_philox4x32_10.argtypes = [vp, vp, vp]
@@ -301,3 +304,31 @@ def clamp(y: np.ndarray, d: int, mM: np.ndarray) -> np.ndarray:
     mM = np.ascontiguousarray(mM, dtype=np.float32)
     lib().orc_clamp(y.ctypes.data, y.size, d, mM.ctypes.data)
     return y
+
+
+# ---------------------------------------------------------------- error feedback
+def ef_add(grad: np.ndarray, e: np.ndarray) -> np.ndarray:
+    """x = grad + e in binary32 (grad fp32, or bf16 as uint16 bits)."""
+    grad = np.ascontiguousarray(grad)
+    e = np.ascontiguousarray(e, dtype=np.float32)
+    assert grad.size == e.size
+    x = np.zeros(grad.size, dtype=np.float32)
+    lib().orc_ef_add(grad.ctypes.data, _dt(grad), e.ctypes.data, grad.size, x.ctypes.data)
+    return x
+
+
+def ef_update(x: np.ndarray, packed: np.ndarray, b: int, part: int, mM: np.ndarray,
+              g: int = 0, T=None) -> np.ndarray:
+    """e' = x - xhat, xhat = the value of the worker's own indices (table T
+    with granularity g, or the uniform grid when T is None)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    mM = np.ascontiguousarray(mM, dtype=np.float32)
+    out = np.zeros(x.size, dtype=np.float32)
+    Tp = None
+    if T is not None:
+        Ta = _table(T)
+        Tp = Ta.ctypes.data
+    _check(lib().orc_ef_update(x.ctypes.data, packed.ctypes.data, x.size, b, g, Tp, part,
+                               mM.ctypes.data, out.ctypes.data), "ef_update")
+    return out

@@ -858,6 +858,47 @@ void orc_clamp(float *y, int64_t N, int64_t d, const float *mM)
 }
 
 /*
+ * [THC] section 5, error feedback: a worker sends x = grad + e, where e is
+ * what its earlier rounds lost to compression, and afterwards keeps the new
+ * loss e' = x - xhat, xhat being the value its own indices stand for.
+ *
+ * Readings: xhat is the worker's own dequantized vector (its indices alone,
+ * mapped back as the server's average is with one worker:
+ * m + (float)v * ((M - m) / levels), or m when M == m, with v = z and
+ * levels = 2^b - 1 for uniform THC, v = T[z] and levels = g for a table),
+ * so e' needs no message from the server; e is binary32, the sum x and the
+ * difference e' are single binary32 operations; a bf16 gradient is widened
+ * exactly first.
+ */
+void orc_ef_add(const void *grad, int dt, const float *e, int64_t N, float *x)
+{
+    for (int64_t i = 0; i < N; i++)
+        x[i] = load_elem(grad, dt, i) + e[i];
+}
+
+int orc_ef_update(const float *x, const uint8_t *packed, int64_t N, int b, int g, const int32_t *T,
+                  int64_t part, const float *mM, float *e_out)
+{
+    if (!(b == 1 || b == 2 || b == 4 || b == 8) || N < 0)
+        return -1;
+    if (T && !table_ok(b, g, T))
+        return -1;
+    const int levels = T ? g : (1 << b) - 1;
+    int64_t plen = part_len(N, part);
+    for (int64_t e = 0; e < N; e++) {
+        int64_t p = e / plen;
+        float m = mM[2 * p], M = mM[2 * p + 1];
+        float range = M - m;
+        int64_t bit = e * b;
+        uint32_t z = (packed[bit >> 3] >> (bit & 7)) & ((1u << b) - 1u);
+        float v = T ? (float)T[z] : (float)z;
+        float xh = range != 0.0f ? m + v * (range / (float)levels) : m;
+        e_out[e] = x[e] - xh;
+    }
+    return 0;
+}
+
+/*
  * [THC] section 2, Figure 2(b): NMSE(x, xhat) = ||x - xhat||^2 / ||x||^2,
  * accumulated in binary64 in index order. out = {num, den, num/den}; a zero
  * denominator gives 0 when num is 0 and +inf otherwise.
