@@ -37,7 +37,8 @@ DESCRIPTIONS = {
     "fusion": "8 workers x 200 fp32 tensors (log-uniform 1K..256K); 64 MiB fusion, ring avg",
     "resnet101": "16 workers x ResNet-101 gradients (314 tensors, 44,549,160 fp32); fusion + ring avg",
     "vgg16": ("32 workers x VGG-16 gradients (138,357,544 fp32); THC USQ b=4,8, table THC "
-              "b=4 g=36, and RHT (d=2^20, p=1/32) + table THC b=4 g=36 + inverse; ring avg; NMSE"),
+              "b=4 g=36, RHT (d=2^20, p=1/32) + table THC b=4 g=36 + inverse, USQ b=4 with error "
+              "feedback, b=4 partial aggregation without 3 stragglers; ring avg; NMSE"),
     "shard": ("8 workers x 2,147,483,648 bf16 Laplace(0,1e-3); ring avg with fp32 accumulation "
               "in 2^20-element partitions + THC USQ b=2 (uint8-packed), int32 sum, dequant, NMSE"),
 }
@@ -88,6 +89,14 @@ def cpu_baseline(pipe, samples, budget_s: float):
         for k, (b, g, T) in pipe.nu_tables.items():
             packed[k] = [oracle.nuhc_quantize(xs[i], i, n, mM, b, g, T, w.quant_seed, e_offset=lo)
                          for i in range(P)]
+        ef = {}
+        for b in w.ef_bits:                             # first step: residuals are zero
+            xe = [oracle.ef_add(x, np.zeros(n, dtype=np.float32)) for x in xs]
+            me = oracle.minmax(xe, n)
+            pk = [oracle.usq_quantize(xe[i], i, n, me, b, w.quant_seed, e_offset=lo)
+                  for i in range(P)]
+            [oracle.ef_update(xe[i], pk[i], b, n, me) for i in range(P)]
+            ef[b] = (me, pk)
         rht = {}
         for k, (b, g, d, T) in pipe.rht.items():       # blocks of d are the partitions
             rm = oracle.rht_range(np.stack([oracle.rht_sumsq(x, d) for x in xs]), d, tp)
@@ -102,6 +111,12 @@ def cpu_baseline(pipe, samples, budget_s: float):
         for k, (b, g, T) in pipe.nu_tables.items():
             Y = oracle.nuhc_aggregate(packed[k], n, b, g, T)
             oracle.nmse(xs[0], oracle.nuhc_dequant(Y, P, g, n, mM, w.dtype))
+        for b, (me, pk) in ef.items():
+            oracle.nmse(xs[0], oracle.dequant(oracle.int_aggregate(pk, n, b), P, b, n, me, w.dtype))
+        if len(pipe.arrived) < P and w.thc_bits:
+            b = w.thc_bits[0]
+            S = oracle.int_aggregate([packed[b][i] for i in pipe.arrived], n, b)
+            oracle.nmse(xs[0], oracle.dequant(S, len(pipe.arrived), b, n, mM, w.dtype))
         for k, (b, g, d, T) in pipe.rht.items():
             rm, pk = rht[k]
             avg = oracle.nuhc_dequant(oracle.nuhc_aggregate(pk, d, b, g, T), P, g, d, rm)

@@ -27,7 +27,7 @@ EXPORTS = (
     "thc_dequant", "thc_nmse", "thc_nmse_ws_bytes", "ga_last_error",
     "thc_nuhc_quantize", "thc_nuhc_aggregate", "thc_nuhc_dequant",
     "thc_rht_sumsq", "thc_rht_range", "thc_rht_forward", "thc_rht_inverse",
-    "ga_fusion_ring_plan", "ga_fusion_ring_allreduce",
+    "ga_fusion_ring_plan", "ga_fusion_ring_allreduce", "thc_ef_minmax", "thc_ef_quantize",
 )
 
 
@@ -90,6 +90,9 @@ def load() -> C.CDLL:
     L.ga_fusion_ring_plan.argtypes = [vp, vp, i64, i32, i32, i64, C.POINTER(i64)]
     L.ga_fusion_ring_allreduce.argtypes = [vp, vp, i64, i64, i32, i64, i32, i32, i32, i64,
                                            C.POINTER(RingStats), vp]
+    L.thc_ef_minmax.argtypes = [C.POINTER(vp), C.POINTER(vp), i32, i64, i32, i64, vp, vp]
+    L.thc_ef_quantize.argtypes = [C.POINTER(vp), C.POINTER(vp), i32, i32, i64, i32, i64, vp, i32,
+                                  i32, C.POINTER(i32), u64, C.POINTER(vp), vp]
     L.ga_last_error.argtypes = []
     L.ga_last_error.restype = C.c_char_p
     for name in EXPORTS:
@@ -406,6 +409,40 @@ def thc_nuhc_dequant(S: torch.Tensor, N: int, P: int, g: int, mM: torch.Tensor, 
     _check(load().thc_nuhc_dequant(_dev(S, "sum"), N, P, g, part_elems, _dev(mM, "mM"),
                                    _dev(out, "out"), _dt(out), _stream(stream)))
     return out
+
+
+# ------------------------------------------------------------------ error feedback
+def _errs(errs: Sequence[torch.Tensor], N: int):
+    if any(e.dtype != torch.float32 or e.numel() != N for e in errs):
+        raise ValueError("error buffers must be float32 with N elements")
+    return _ptr_array(errs, "error buffer")
+
+
+def thc_ef_minmax(bufs: Sequence[torch.Tensor], errs: Sequence[torch.Tensor], part_elems: int = 0,
+                  out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    N = bufs[0].numel()
+    if out is None:
+        out = torch.empty((max(n_partitions(N, part_elems), 1), 2), dtype=torch.float32,
+                          device=bufs[0].device)
+    _check(load().thc_ef_minmax(_ptr_array(bufs, "buffer"), _errs(errs, N), len(bufs), N,
+                                _dt(bufs[0]), part_elems, _dev(out, "mM"), _stream(stream)))
+    return out
+
+
+def thc_ef_quantize(bufs: Sequence[torch.Tensor], errs: Sequence[torch.Tensor], mM: torch.Tensor,
+                    b: int, seed: int, part_elems: int = 0, worker0: int = 0, g: int = 0, table=None,
+                    packed: Optional[Sequence[torch.Tensor]] = None, stream=None):
+    """Quantize grad + e (uniform grid, or table T with granularity g) and
+    overwrite e with the new residual."""
+    N = bufs[0].numel()
+    if packed is None:
+        packed = [torch.empty(packed_bytes(N, b), dtype=torch.uint8, device=bufs[0].device)
+                  for _ in bufs]
+    _check(load().thc_ef_quantize(_ptr_array(bufs, "buffer"), _errs(errs, N), len(bufs), worker0,
+                                  N, _dt(bufs[0]), part_elems, _dev(mM, "mM"), b, g,
+                                  _table_arg(table) if table is not None else None, seed,
+                                  _ptr_array(packed, "packed"), _stream(stream)))
+    return packed
 
 
 # ------------------------------------------------------------------ randomized Hadamard transform

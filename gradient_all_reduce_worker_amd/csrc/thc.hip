@@ -84,10 +84,21 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// Workgroup (p, j) scans slice j of partition p in every worker's buffer.
+// E binary32 error-feedback values of the elements of x vector v (x of
+// type DT; the error buffer shares the element indexing).
 template <ga_dtype DT>
-__global__ __launch_bounds__(kThreads) void minmax_kernel(PtrTable bufs, int P, int64_t N,
-                                                          int64_t plen, int slices,
+__device__ __forceinline__ void load_err_vec(const float* err, int64_t v, float* f) {
+    constexpr int E = Vec16<DT>::kElems;
+#pragma unroll
+    for (int q = 0; q < E / 4; q++) Vec16<GA_F32>::load(err, v * (E / 4) + q, f + 4 * q);
+}
+
+// Workgroup (p, j) scans slice j of partition p in every worker's buffer.
+// EF: the values scanned are x + e (error feedback) in binary32; vec_ok
+// says every x and e buffer is 16-byte aligned, else elements go one by one.
+template <ga_dtype DT, bool EF>
+__global__ __launch_bounds__(kThreads) void minmax_kernel(PtrTable bufs, PtrTable errs, int vec_ok,
+                                                          int P, int64_t N, int64_t plen, int slices,
                                                           int64_t slice_len, uint32_t* keys) {
     using V = Vec16<DT>;
     constexpr int E = V::kElems;
@@ -100,6 +111,14 @@ __global__ __launch_bounds__(kThreads) void minmax_kernel(PtrTable bufs, int P, 
     if (lo >= hi) return;
     float mn = INFINITY, mx = -INFINITY;
     constexpr int es = DT == GA_BF16 ? 2 : 4;
+    if (EF && !vec_ok) {
+        for (int w = 0; w < P; w++)
+            for (int64_t e = lo + threadIdx.x; e < hi; e += kThreads) {
+                const float a = load_as_f32(bufs.p[w], e, DT) + static_cast<const float*>(errs.p[w])[e];
+                mn = fminf(mn, a);
+                mx = fmaxf(mx, a);
+            }
+    } else
     for (int w = 0; w < P; w++) {
         const void* x = bufs.p[w];
         // head: elements before the first 16-byte boundary
@@ -108,18 +127,30 @@ __global__ __launch_bounds__(kThreads) void minmax_kernel(PtrTable bufs, int P, 
         const int64_t vlo = min(mis ? lo + (E - mis) : lo, hi);
         const int64_t nv = (hi - vlo) / E;
         const int64_t vhi = vlo + nv * E;
+        const float* ew = EF ? static_cast<const float*>(errs.p[w]) : nullptr;
         for (int64_t e = lo + threadIdx.x; e < vlo; e += kThreads) {
-            const float a = load_as_f32(x, e, DT);
+            const float a = EF ? load_as_f32(x, e, DT) + ew[e] : load_as_f32(x, e, DT);
             mn = fminf(mn, a);
             mx = fmaxf(mx, a);
         }
         // body: 16-byte vectors from the first aligned element, four in flight
+        // (with EF every buffer is aligned, so vlo is a multiple of E)
         const void* xa = xb + vlo * es;
+        const float* ea = EF ? ew + vlo : nullptr;
         int64_t v = threadIdx.x;
         for (; v + 3 * kThreads < nv; v += 4 * kThreads) {
             float f[4][E];
 #pragma unroll
             for (int u = 0; u < 4; u++) V::load(xa, v + u * kThreads, f[u]);
+            if (EF) {
+                float g[4][E];
+#pragma unroll
+                for (int u = 0; u < 4; u++) load_err_vec<DT>(ea, v + u * kThreads, g[u]);
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+#pragma unroll
+                    for (int i = 0; i < E; i++) f[u][i] = f[u][i] + g[u][i];
+            }
 #pragma unroll
             for (int u = 0; u < 4; u++)
 #pragma unroll
@@ -131,6 +162,12 @@ __global__ __launch_bounds__(kThreads) void minmax_kernel(PtrTable bufs, int P, 
         for (; v < nv; v += kThreads) {
             float f[E];
             V::load(xa, v, f);
+            if (EF) {
+                float g[E];
+                load_err_vec<DT>(ea, v, g);
+#pragma unroll
+                for (int i = 0; i < E; i++) f[i] = f[i] + g[i];
+            }
 #pragma unroll
             for (int i = 0; i < E; i++) {
                 mn = fminf(mn, f[i]);
@@ -139,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void minmax_kernel(PtrTable bufs, int P, 
         }
         // tail
         for (int64_t e = vhi + threadIdx.x; e < hi; e += kThreads) {
-            const float a = load_as_f32(x, e, DT);
+            const float a = EF ? load_as_f32(x, e, DT) + ew[e] : load_as_f32(x, e, DT);
             mn = fminf(mn, a);
             mx = fmaxf(mx, a);
         }
@@ -247,17 +284,56 @@ template <bool TABLE>
 struct Rounder {
     int levels;              // L for the uniform grid, g for a table
     const uint32_t* cell;    // LDS cells (table only)
-    __device__ __forceinline__ uint32_t index(float a, Grid gr, uint32_t r16) const {
-        if (!TABLE) return usq_index(a, gr, levels, r16);
+    // The index of a; *v receives the grid level it stands for (the index
+    // itself, or its table value).
+    __device__ __forceinline__ uint32_t index_v(float a, Grid gr, uint32_t r16, float* v) const {
+        if (!TABLE) {
+            const uint32_t z = usq_index(a, gr, levels, r16);
+            *v = (float)z;
+            return z;
+        }
         const float u = (a - gr.m) * gr.s;                      // position on <g+1>
         const float k = fminf(floorf(u), (float)(levels - 1));
         const uint32_t c = cell[(int)k];
         const float lo = (float)((c >> 8) & 0xFFFu), hi = (float)(c >> 20);
         const float f = (u - lo) / (hi - lo);
         const bool up = (float)(2u * r16 + 1u) < f * 131072.0f;
+        *v = up ? hi : lo;
         return (c & 0xFFu) + (up ? 1u : 0u);
     }
+    __device__ __forceinline__ uint32_t index(float a, Grid gr, uint32_t r16) const {
+        float v;
+        return index_v(a, gr, r16, &v);
+    }
 };
+
+// Error feedback (THC page, section 5): the value a worker's own level v
+// stands for, m + v (M - m) / levels (m when M == m), the same binary32
+// steps as the server's dequantization of a one-worker sum.
+struct EfGrid {
+    float m;
+    float delta;             // (M - m) / levels
+    bool flat;               // M == m
+};
+
+__device__ __forceinline__ EfGrid ef_grid_of(const float* mM, int64_t p, int levels) {
+    const float m = mM[2 * p], M = mM[2 * p + 1];
+    const float range = M - m;
+    return {m, range / (float)levels, range == 0.0f};
+}
+
+__device__ __forceinline__ float ef_value(EfGrid q, float v) {
+    return q.flat ? q.m : q.m + v * q.delta;
+}
+
+__device__ __forceinline__ void store_err_group(float* err, int64_t g, const float* f) {
+    store_stream(reinterpret_cast<uint4*>(err) + 2 * g,
+                 make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                            __float_as_uint(f[3])));
+    store_stream(reinterpret_cast<uint4*>(err) + 2 * g + 1,
+                 make_uint4(__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]),
+                            __float_as_uint(f[7])));
+}
 
 // Called by every thread of the workgroup before any early exit.
 template <bool TABLE>
@@ -278,9 +354,12 @@ __device__ __forceinline__ Rounder<TABLE> make_rounder(const TableArg& tab, int 
 // Fast kernel: every group of the workgroup is whole, the buffers are
 // 16-byte aligned and the workgroup lies in one partition (the host only
 // launches it over such workgroups). No bounds checks, grid loaded once.
-template <ga_dtype DT, int B, bool TABLE>
-__global__ __launch_bounds__(kThreads) void usq_quantize_fast_kernel(PtrTable bufs, PtrTable packed,
-                                                                     int worker0, int64_t plen,
+// EF: the value quantized is x + e, and e is replaced by x + e minus the
+// value of the index sent.
+template <ga_dtype DT, int B, bool TABLE, bool EF>
+__global__ __launch_bounds__(kThreads) void usq_quantize_fast_kernel(PtrTable bufs, PtrTable errs,
+                                                                     PtrTable packed, int worker0,
+                                                                     int64_t plen,
                                                                      const float* __restrict__ mM,
                                                                      uint32_t k0, uint32_t k1,
                                                                      TableArg tab) {
@@ -289,6 +368,7 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_fast_kernel(PtrTable bu
     const Rounder<TABLE> rd = make_rounder<TABLE>(tab, L, cells);
     const int slot = blockIdx.y;
     const void* x = bufs.p[slot];
+    float* err = EF ? static_cast<float*>(errs.p[slot]) : nullptr;
     uint8_t* out = static_cast<uint8_t*>(packed.p[slot]);
     const uint32_t wid = (uint32_t)(worker0 + slot);
     const int64_t e_blk = (int64_t)blockIdx.x * kQSpan;
@@ -297,23 +377,41 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_fast_kernel(PtrTable bu
 #pragma unroll
     for (int j = 0; j < kQGroups; j++)
         load_group<DT>(x, e_blk / 8 + (int64_t)j * kThreads + threadIdx.x, a[j]);
+    if (EF) {
+        float ev[kQGroups][8];
+#pragma unroll
+        for (int j = 0; j < kQGroups; j++)
+            load_group<GA_F32>(err, e_blk / 8 + (int64_t)j * kThreads + threadIdx.x, ev[j]);
+#pragma unroll
+        for (int j = 0; j < kQGroups; j++)
+#pragma unroll
+            for (int i = 0; i < 8; i++) a[j][i] = a[j][i] + ev[j][i];
+    }
+    const EfGrid q = EF ? ef_grid_of(mM, e_blk / plen, rd.levels) : EfGrid{};
 #pragma unroll
     for (int j = 0; j < kQGroups; j++) {
         const int64_t g = e_blk / 8 + (int64_t)j * kThreads + threadIdx.x;
         const Philox4 r = philox4x32_10((uint32_t)g, (uint32_t)((uint64_t)g >> 32), wid, 0u, k0, k1);
         uint32_t z[8];
+        float res[8];
 #pragma unroll
-        for (int i = 0; i < 8; i++) z[i] = rd.index(a[j][i], gb, uniform16(r, i));
+        for (int i = 0; i < 8; i++) {
+            float v;
+            z[i] = rd.index_v(a[j][i], gb, uniform16(r, i), &v);
+            if (EF) res[i] = a[j][i] - ef_value(q, v);
+        }
         store_group<B>(out, g, pack_group<B>(z));
+        if (EF) store_err_group(err, g, res);
     }
 }
 
 // Generic kernel for the workgroups the fast one does not take (from
 // workgroup blk0 on): partial groups, misaligned buffers, partitions that
 // are not a multiple of a workgroup's span.
-template <ga_dtype DT, int B, bool TABLE>
-__global__ __launch_bounds__(kThreads) void usq_quantize_kernel(PtrTable bufs, PtrTable packed,
-                                                                int worker0, int64_t N, int64_t plen,
+template <ga_dtype DT, int B, bool TABLE, bool EF>
+__global__ __launch_bounds__(kThreads) void usq_quantize_kernel(PtrTable bufs, PtrTable errs,
+                                                                PtrTable packed, int worker0,
+                                                                int64_t N, int64_t plen,
                                                                 const float* __restrict__ mM,
                                                                 uint32_t k0, uint32_t k1,
                                                                 int vec_ok, int64_t blk0,
@@ -323,6 +421,7 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_kernel(PtrTable bufs, P
     const Rounder<TABLE> rd = make_rounder<TABLE>(tab, L, cells);
     const int slot = blockIdx.y;
     const void* x = bufs.p[slot];
+    float* err = EF ? static_cast<float*>(errs.p[slot]) : nullptr;
     uint8_t* out = static_cast<uint8_t*>(packed.p[slot]);
     const uint32_t wid = (uint32_t)(worker0 + slot);
     const int64_t e_blk = (blk0 + blockIdx.x) * kQSpan;
@@ -334,36 +433,48 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_kernel(PtrTable bufs, P
         if (e >= N) break;
         const Philox4 r = philox4x32_10((uint32_t)g, (uint32_t)((uint64_t)g >> 32), wid, 0u, k0, k1);
         uint32_t z[8];
-        if (g < n_full) {
-            float a[8];
-            if (vec_ok) {
-                load_group<DT>(x, g, a);
-            } else {
+        const int n_in = g < n_full ? 8 : (int)(N - e);   // elements of this group inside N
+        float a[8], res[8];
+        if (g < n_full && vec_ok) {
+            load_group<DT>(x, g, a);
+            if (EF) {
+                float ev[8];
+                load_group<GA_F32>(err, g, ev);
 #pragma unroll
-                for (int i = 0; i < 8; i++) a[i] = load_as_f32(x, e + i, DT);
-            }
-#pragma unroll
-            for (int i = 0; i < 8; i++)
-                z[i] = rd.index(a[i], grid_of(mM, (e + i) / plen, rd.levels), uniform16(r, i));
-            const uint64_t bits = pack_group<B>(z);
-            if (vec_ok) {
-                store_group<B>(out, g, bits);
-            } else {
-#pragma unroll
-                for (int i = 0; i < B; i++) out[g * B + i] = (uint8_t)(bits >> (8 * i));
+                for (int i = 0; i < 8; i++) a[i] = a[i] + ev[i];
             }
         } else {
-            // the last, partial group: elements past N - 1 get index 0
 #pragma unroll
-            for (int i = 0; i < 8; i++)
-                z[i] = e + i < N ? rd.index(load_as_f32(x, e + i, DT),
-                                            grid_of(mM, (e + i) / plen, rd.levels), uniform16(r, i))
-                                 : 0u;
-            const uint64_t bits = pack_group<B>(z);
+            for (int i = 0; i < 8; i++) {
+                a[i] = i < n_in ? load_as_f32(x, e + i, DT) : 0.0f;
+                if (EF && i < n_in) a[i] = a[i] + err[e + i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            if (i < n_in) {
+                const int64_t p = (e + i) / plen;
+                float v;
+                z[i] = rd.index_v(a[i], grid_of(mM, p, rd.levels), uniform16(r, i), &v);
+                if (EF) res[i] = a[i] - ef_value(ef_grid_of(mM, p, rd.levels), v);
+            } else {
+                z[i] = 0u;                              // past N - 1: index 0
+            }
+        }
+        const uint64_t bits = pack_group<B>(z);
+        if (g < n_full && vec_ok) {
+            store_group<B>(out, g, bits);
+            if (EF) store_err_group(err, g, res);
+        } else {
             const int64_t nbytes = (N * B + 7) / 8;
 #pragma unroll
             for (int i = 0; i < B; i++)
                 if (g * B + i < nbytes) out[g * B + i] = (uint8_t)(bits >> (8 * i));
+            if (EF) {
+#pragma unroll
+                for (int i = 0; i < 8; i++)
+                    if (i < n_in) err[e + i] = res[i];
+            }
         }
     }
 }
@@ -630,15 +741,18 @@ bool valid_bits(int b) { return b == 1 || b == 2 || b == 4 || b == 8; }
 
 using namespace ga;
 
-extern "C" ga_status thc_minmax(const void* const* bufs, int32_t P, int64_t N, ga_dtype dt,
-                                int64_t part_elems, float* d_mM, void* stream) {
-    const char* what = "thc_minmax";
+namespace ga {
+namespace {
+
+ga_status minmax_impl(const void* const* bufs, const float* const* errs, int32_t P, int64_t N,
+                      ga_dtype dt, int64_t part_elems, float* d_mM, void* stream, const char* what) {
     if (!valid_dtype(dt)) return fail(GA_EINVAL, "%s: unknown dtype %d", what, (int)dt);
     if (N < 0 || part_elems < 0) return fail(GA_EINVAL, "%s: negative size", what);
     if (P < 1 || P > GA_MAX_WORKERS) return fail(GA_EINVAL, "%s: P = %d outside [1, %d]", what, P, GA_MAX_WORKERS);
     if (N == 0) return GA_OK;
     ga_status rc = check_workers(bufs, P, elem_size(dt), what);
     if (rc) return rc;
+    if (errs && (rc = check_workers(reinterpret_cast<const void* const*>(errs), P, 4, what))) return rc;
     if (!d_mM || !aligned(d_mM, 8)) return fail(GA_EINVAL, "%s: bad output pointer", what);
     const int64_t plen = part_elems > 0 ? part_elems : N;
     const int64_t n_part = n_partitions(N, part_elems);
@@ -650,18 +764,44 @@ extern "C" ga_status thc_minmax(const void* const* bufs, int32_t P, int64_t N, g
     if (n_part * slices > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: too many partitions", what);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     uint32_t* keys = reinterpret_cast<uint32_t*>(d_mM);
-    PtrTable t{};
-    for (int i = 0; i < P; i++) t.p[i] = const_cast<void*>(bufs[i]);
+    PtrTable t{}, te{};
+    int vec_ok = 1;
+    for (int i = 0; i < P; i++) {
+        t.p[i] = const_cast<void*>(bufs[i]);
+        if (errs) {
+            te.p[i] = const_cast<float*>(errs[i]);
+            vec_ok &= aligned(bufs[i], 16) && aligned(errs[i], 16);
+        }
+    }
     hipLaunchKernelGGL(minmax_init_kernel, dim3(blocks_for(n_part, 1)), dim3(kThreads), 0, hs, keys, n_part);
     if ((rc = check_launch(what))) return rc;
     const dim3 grid((unsigned)(n_part * slices));
-    if (dt == GA_F32)
-        hipLaunchKernelGGL(minmax_kernel<GA_F32>, grid, dim3(kThreads), 0, hs, t, P, N, plen, (int)slices, slice_len, keys);
+    if (dt == GA_F32 && errs)
+        hipLaunchKernelGGL((minmax_kernel<GA_F32, true>), grid, dim3(kThreads), 0, hs, t, te, vec_ok, P, N, plen, (int)slices, slice_len, keys);
+    else if (dt == GA_F32)
+        hipLaunchKernelGGL((minmax_kernel<GA_F32, false>), grid, dim3(kThreads), 0, hs, t, te, vec_ok, P, N, plen, (int)slices, slice_len, keys);
+    else if (errs)
+        hipLaunchKernelGGL((minmax_kernel<GA_BF16, true>), grid, dim3(kThreads), 0, hs, t, te, vec_ok, P, N, plen, (int)slices, slice_len, keys);
     else
-        hipLaunchKernelGGL(minmax_kernel<GA_BF16>, grid, dim3(kThreads), 0, hs, t, P, N, plen, (int)slices, slice_len, keys);
+        hipLaunchKernelGGL((minmax_kernel<GA_BF16, false>), grid, dim3(kThreads), 0, hs, t, te, vec_ok, P, N, plen, (int)slices, slice_len, keys);
     if ((rc = check_launch(what))) return rc;
     hipLaunchKernelGGL(minmax_final_kernel, dim3(blocks_for(n_part, 1)), dim3(kThreads), 0, hs, keys, n_part);
     return check_launch(what);
+}
+
+}  // namespace
+}  // namespace ga
+
+extern "C" ga_status thc_minmax(const void* const* bufs, int32_t P, int64_t N, ga_dtype dt,
+                                int64_t part_elems, float* d_mM, void* stream) {
+    return minmax_impl(bufs, nullptr, P, N, dt, part_elems, d_mM, stream, "thc_minmax");
+}
+
+extern "C" ga_status thc_ef_minmax(const void* const* bufs, const float* const* errs, int32_t P,
+                                   int64_t N, ga_dtype dt, int64_t part_elems, float* d_mM,
+                                   void* stream) {
+    if (!errs) return fail(GA_EINVAL, "thc_ef_minmax: null error buffers");
+    return minmax_impl(bufs, errs, P, N, dt, part_elems, d_mM, stream, "thc_ef_minmax");
 }
 
 namespace ga {
@@ -692,7 +832,7 @@ ga_status load_table(int32_t b, int32_t g, const int32_t* h_table, TableArg* tab
 ga_status quantize_impl(const void* const* bufs, int32_t P, int32_t worker0, int64_t N, ga_dtype dt,
                         int64_t part_elems, const float* d_mM, int32_t b, uint64_t seed,
                         uint8_t* const* packed, void* stream, const TableArg* table,
-                        const char* what) {
+                        const char* what, float* const* errs = nullptr) {
     if (!valid_dtype(dt)) return fail(GA_EINVAL, "%s: unknown dtype %d", what, (int)dt);
     if (!valid_bits(b)) return fail(GA_EINVAL, "%s: b = %d is not 1, 2, 4 or 8", what, b);
     if (N < 0 || part_elems < 0 || worker0 < 0) return fail(GA_EINVAL, "%s: negative argument", what);
@@ -701,14 +841,19 @@ ga_status quantize_impl(const void* const* bufs, int32_t P, int32_t worker0, int
     ga_status rc = check_workers(bufs, P, elem_size(dt), what);
     if (rc) return rc;
     if ((rc = check_workers(reinterpret_cast<const void* const*>(packed), P, 1, what))) return rc;
+    if (errs && (rc = check_workers(reinterpret_cast<const void* const*>(errs), P, 4, what))) return rc;
     if (!d_mM || !aligned(d_mM, 4)) return fail(GA_EINVAL, "%s: bad grid pointer", what);
     const int64_t plen = part_elems > 0 ? part_elems : N;
     int vec_ok = 1;
-    PtrTable tx{}, tp{};
+    PtrTable tx{}, tp{}, te{};
     for (int i = 0; i < P; i++) {
         tx.p[i] = const_cast<void*>(bufs[i]);
         tp.p[i] = packed[i];
         vec_ok &= aligned(bufs[i], 16) && aligned(packed[i], 16);
+        if (errs) {
+            te.p[i] = errs[i];
+            vec_ok &= aligned(errs[i], 16);
+        }
     }
     const int64_t blocks = ceil_div(N, kQSpan);
     if (blocks > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: N too large", what);
@@ -717,15 +862,21 @@ ga_status quantize_impl(const void* const* bufs, int32_t P, int32_t worker0, int
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
     const TableArg tab = table ? *table : TableArg{};
-#define GA_Q(DT, B, TB)                                                                               \
+#define GA_Q2(DT, B, TB, EF)                                                                          \
     do {                                                                                              \
         if (fast > 0)                                                                                 \
-            hipLaunchKernelGGL((usq_quantize_fast_kernel<DT, B, TB>), dim3((unsigned)fast, (unsigned)P), \
-                               dim3(kThreads), 0, hs, tx, tp, worker0, plen, d_mM, k0, k1, tab);     \
+            hipLaunchKernelGGL((usq_quantize_fast_kernel<DT, B, TB, EF>),                             \
+                               dim3((unsigned)fast, (unsigned)P), dim3(kThreads), 0, hs, tx, te, tp,  \
+                               worker0, plen, d_mM, k0, k1, tab);                                     \
         if (blocks > fast)                                                                            \
-            hipLaunchKernelGGL((usq_quantize_kernel<DT, B, TB>), dim3((unsigned)(blocks - fast), (unsigned)P), \
-                               dim3(kThreads), 0, hs, tx, tp, worker0, N, plen, d_mM, k0, k1, vec_ok, \
-                               fast, tab);                                                            \
+            hipLaunchKernelGGL((usq_quantize_kernel<DT, B, TB, EF>),                                  \
+                               dim3((unsigned)(blocks - fast), (unsigned)P), dim3(kThreads), 0, hs,   \
+                               tx, te, tp, worker0, N, plen, d_mM, k0, k1, vec_ok, fast, tab);        \
+    } while (0)
+#define GA_Q(DT, B, TB)                                \
+    do {                                               \
+        if (errs) GA_Q2(DT, B, TB, true);              \
+        else GA_Q2(DT, B, TB, false);                  \
     } while (0)
 #define GA_QB(DT, TB)                      \
     switch (b) {                           \
@@ -741,6 +892,7 @@ ga_status quantize_impl(const void* const* bufs, int32_t P, int32_t worker0, int
     }
 #undef GA_QB
 #undef GA_Q
+#undef GA_Q2
     return check_launch(what);
 }
 
@@ -837,6 +989,23 @@ extern "C" ga_status thc_nuhc_quantize(const void* const* bufs, int32_t P, int32
     if (rc) return rc;
     return quantize_impl(bufs, P, worker0, N, dt, part_elems, d_mM, b, seed, packed, stream, &tab,
                          "thc_nuhc_quantize");
+}
+
+extern "C" ga_status thc_ef_quantize(const void* const* bufs, float* const* errs, int32_t P,
+                                     int32_t worker0, int64_t N, ga_dtype dt, int64_t part_elems,
+                                     const float* d_mM, int32_t b, int32_t g,
+                                     const int32_t* h_table, uint64_t seed, uint8_t* const* packed,
+                                     void* stream) {
+    const char* what = "thc_ef_quantize";
+    if (!errs) return fail(GA_EINVAL, "%s: null error buffers", what);
+    if (!h_table)
+        return quantize_impl(bufs, P, worker0, N, dt, part_elems, d_mM, b, seed, packed, stream,
+                             nullptr, what, errs);
+    TableArg tab;
+    ga_status rc = load_table(b, g, h_table, &tab, what);
+    if (rc) return rc;
+    return quantize_impl(bufs, P, worker0, N, dt, part_elems, d_mM, b, seed, packed, stream, &tab,
+                         what, errs);
 }
 
 extern "C" ga_status thc_nuhc_aggregate(const uint8_t* const* packed, int32_t P, int64_t N, int32_t b,

@@ -14,10 +14,14 @@ A step runs, in this order, on the current stream:
       for every THC pass behind the randomized Hadamard transform (THC page
       section 5): per-block norms, the norm-based range, the transform with
       truncation, the table quantizer on the transformed coordinates,
+      for every error-feedback pass (THC page section 5): min/max and the
+      quantizer on gradient + residual, the residual written back,
       ring-average the gradients in place (the exact average),
       then per bit width: integer aggregate, dequantize, NMSE of the THC
       estimate against the exact average (for RHT passes: table-sum
-      aggregate, dequantize, inverse transform, NMSE).
+      aggregate, dequantize, inverse transform, NMSE); the partial pass
+      (THC page section 8) sums only the workers that arrived and divides
+      by their count.
 
 Only the binding is called; all arithmetic runs in libga.so. Per-call HIP
 events (torch.cuda.Event on the stream the kernels are launched on) time
@@ -162,6 +166,27 @@ class Pipeline:
                 self.rht_avg[key] = torch.empty(Np, dtype=torch.float32, device=dev)
                 self.xhat[key] = torch.empty(self.N, dtype=self.tdt, device=dev)
                 self.nmse[key] = torch.empty(3, dtype=torch.float64, device=dev)
+            # error-feedback passes, keyed "ef{b}", residuals start at zero
+            self.err, self.mM_ef = {}, {}
+            for b in w.ef_bits:
+                k = f"ef{b}"
+                self.err[k] = worker_buffers(self.P, self.N, torch.float32, dev)
+                for e in self.err[k]:
+                    e.zero_()
+                self.mM_ef[k] = torch.empty((n_part, 2), dtype=torch.float32, device=dev)
+                self.packed[k] = [torch.empty(ga.packed_bytes(self.N, b), dtype=torch.uint8,
+                                              device=dev) for _ in range(self.P)]
+                self.S[k] = torch.empty(self.N, dtype=torch.int32, device=dev)
+                self.xhat[k] = torch.empty(self.N, dtype=self.tdt, device=dev)
+                self.nmse[k] = torch.empty(3, dtype=torch.float64, device=dev)
+            # partial aggregation of the first uniform pass without the stragglers
+            self.dropped = synth.straggler_set(w)
+            self.arrived = [i for i in range(self.P) if i not in self.dropped]
+            if self.dropped and w.thc_bits:
+                k = f"part{w.thc_bits[0]}"
+                self.S[k] = torch.empty(self.N, dtype=torch.int32, device=dev)
+                self.xhat[k] = torch.empty(self.N, dtype=self.tdt, device=dev)
+                self.nmse[k] = torch.empty(3, dtype=torch.float64, device=dev)
             self.ws = torch.empty(ga.thc_nmse_ws_bytes(self.N), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 
@@ -200,8 +225,31 @@ class Pipeline:
                   self.rht_mM[key], self.rht_y[key])
             _call(timer, f"thc_nuhc_quantize_{key}", ga.thc_nuhc_quantize, self.rht_y[key],
                   self.rht_mM[key], b, g, T, w.quant_seed, d, 0, self.packed[key])
+        for b in w.ef_bits:
+            k = f"ef{b}"
+            _call(timer, f"thc_ef_minmax_{k}", ga.thc_ef_minmax, self.flat, self.err[k], part,
+                  self.mM_ef[k])
+            _call(timer, f"thc_ef_quantize_{k}", ga.thc_ef_quantize, self.flat, self.err[k],
+                  self.mM_ef[k], b, w.quant_seed, part, 0, 0, None, self.packed[k])
         _call(timer, "ring_allreduce", ga.ga_ring_allreduce_sim, self.flat, ga.AVG,
               w.ring_part_elems, self.ring_mode)
+        for b in w.ef_bits:
+            k = f"ef{b}"
+            _call(timer, f"thc_int_aggregate_{k}", ga.thc_int_aggregate, self.packed[k], self.N, b,
+                  self.S[k])
+            _call(timer, f"thc_dequant_{k}", ga.thc_dequant, self.S[k], self.N, self.P, b,
+                  self.mM_ef[k], part, self.tdt, self.xhat[k])
+            _call(timer, f"thc_nmse_{k}", ga.thc_nmse, self.flat[0], self.xhat[k], self.nmse[k],
+                  self.ws)
+        if self.dropped and w.thc_bits:
+            b = w.thc_bits[0]
+            k = f"part{b}"
+            _call(timer, f"thc_int_aggregate_{k}", ga.thc_int_aggregate,
+                  [self.packed[b][i] for i in self.arrived], self.N, b, self.S[k])
+            _call(timer, f"thc_dequant_{k}", ga.thc_dequant, self.S[k], self.N, len(self.arrived),
+                  b, self.mM, part, self.tdt, self.xhat[k])
+            _call(timer, f"thc_nmse_{k}", ga.thc_nmse, self.flat[0], self.xhat[k], self.nmse[k],
+                  self.ws)
         for key, (b, g, d, T) in self.rht.items():
             Np = self.rht_avg[key].numel()
             _call(timer, f"thc_nuhc_aggregate_{key}", ga.thc_nuhc_aggregate, self.packed[key], Np, b,
@@ -252,6 +300,19 @@ class Pipeline:
             out[f"thc_nuhc_aggregate_{k}"] = P * N * b / 8.0 + 4.0 * N
             out[f"thc_nuhc_dequant_{k}"] = 4.0 * N + N * s
             out[f"thc_nmse_{k}"] = 2.0 * N * s
+        for b in w.ef_bits:
+            k = f"ef{b}"
+            out[f"thc_ef_minmax_{k}"] = P * N * (s + 4.0)
+            out[f"thc_ef_quantize_{k}"] = P * N * (s + 8.0 + b / 8.0)
+            out[f"thc_int_aggregate_{k}"] = P * N * b / 8.0 + 4.0 * N
+            out[f"thc_dequant_{k}"] = 4.0 * N + N * s
+            out[f"thc_nmse_{k}"] = 2.0 * N * s
+        if self.dropped and w.thc_bits:
+            b = w.thc_bits[0]
+            k = f"part{b}"
+            out[f"thc_int_aggregate_{k}"] = len(self.arrived) * N * b / 8.0 + 4.0 * N
+            out[f"thc_dequant_{k}"] = 4.0 * N + N * s
+            out[f"thc_nmse_{k}"] = 2.0 * N * s
         for k, (b, g, d, _) in self.rht.items():
             Np = ga.rht_padded(N, d)
             nblk = Np // d
@@ -295,6 +356,20 @@ class Pipeline:
                 bl, bh = lo * b // 8, (hi * b + 7) // 8
                 d["packed"][k] = [self.packed[k][i][bl:bh].cpu().numpy().copy()
                                   for i in range(self.P)]
+                d["xhat"][k] = synth.to_numpy_bits(self.xhat[k][lo:hi])
+                d["S"][k] = self.S[k][lo:hi].cpu().numpy().copy()
+            d["err"], d["mM_ef"] = {}, {}
+            for b in self.w.ef_bits:
+                k = f"ef{b}"
+                bl, bh = lo * b // 8, (hi * b + 7) // 8
+                d["packed"][k] = [self.packed[k][i][bl:bh].cpu().numpy().copy()
+                                  for i in range(self.P)]
+                d["xhat"][k] = synth.to_numpy_bits(self.xhat[k][lo:hi])
+                d["S"][k] = self.S[k][lo:hi].cpu().numpy().copy()
+                d["err"][k] = [self.err[k][i][lo:hi].cpu().numpy().copy() for i in range(self.P)]
+                d["mM_ef"][k] = self.mM_ef[k][p].cpu().numpy().copy()
+            if self.dropped and self.w.thc_bits:
+                k = f"part{self.w.thc_bits[0]}"
                 d["xhat"][k] = synth.to_numpy_bits(self.xhat[k][lo:hi])
                 d["S"][k] = self.S[k][lo:hi].cpu().numpy().copy()
             out[p] = d

@@ -120,6 +120,8 @@ class Workload:
     # a fraction rht_p of the transformed coordinates is expected to be cut
     rht: Tuple[Tuple[int, int, int], ...] = ()
     rht_p: float = 1.0 / 32
+    ef_bits: Tuple[int, ...] = ()   # uniform THC passes with error feedback
+    stragglers: int = 0             # workers the server does not wait for (partial pass)
     fused: bool = True              # run the Tensor Fusion plan over `sizes`
 
     @property
@@ -168,7 +170,8 @@ def workload(name: str) -> Workload:
         names, sizes = _rev(vgg16_shapes())
         return Workload("vgg16", 3, P=32, dtype=F32, sizes=sizes, names=names,
                         dist="normal_logsigma", part_elems=1 << 20, ring_part_elems=1 << 20,
-                        thc_bits=(4, 8), nuhc=((4, 36),), rht=((4, 36, 20),), fused=False)
+                        thc_bits=(4, 8), nuhc=((4, 36),), rht=((4, 36, 20),), ef_bits=(4,),
+                        stragglers=3, fused=False)
     if name == "shard":
         return Workload("shard", 4, P=8, dtype=BF16, sizes=[1 << 31], names=["shard"],
                         dist="laplace", part_elems=1 << 20, ring_part_elems=1 << 20,
@@ -177,6 +180,15 @@ def workload(name: str) -> Workload:
 
 
 WORKLOADS = ("small", "fusion", "resnet101", "vgg16", "shard")
+
+
+def straggler_set(w: Workload) -> List[int]:
+    """The workers the server does not wait for in the partial pass: a
+    seeded draw of w.stragglers distinct workers."""
+    if w.stragglers <= 0:
+        return []
+    rng = host_rng(w.data_seed, 0x57A6)
+    return sorted(int(i) for i in rng.choice(w.P, size=w.stragglers, replace=False))
 
 
 def tensor_scales(w: Workload) -> np.ndarray:

@@ -11,6 +11,7 @@
  *                                                  THC uniform quantization
  *   thc_nuhc_quantize / thc_nuhc_aggregate / thc_nuhc_dequant
  *                                                  THC with lookup tables
+ *   thc_ef_minmax / thc_ef_quantize                error feedback
  *   thc_rht_sumsq / thc_rht_range / thc_rht_forward / thc_rht_inverse
  *                                                  randomized Hadamard
  *                                                  transform, norm-based
@@ -24,8 +25,8 @@
  *   [THC]  "THC: Accelerating Distributed Deep Learning Using Tensor
  *          Homomorphic Compression", sections 2-4 (NMSE, uniform THC,
  *          Algorithm 1, aggregation by the server), 4 (Algorithm 2), 5
- *          (randomized Hadamard transform, truncation, norm-based range)
- *          and 8 (aggregate width).
+ *          (randomized Hadamard transform, truncation, norm-based range,
+ *          error feedback) and 8 (aggregate width, stragglers).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -344,6 +345,42 @@ ga_status thc_nuhc_aggregate(const uint8_t* const* packed, int32_t P, int64_t N,
 ga_status thc_nuhc_dequant(const int32_t* d_sum, int64_t N, int32_t P, int32_t g,
                            int64_t part_elems, const float* d_mM, void* out, ga_dtype out_dt,
                            void* stream);
+
+/* ------------------------------------------------------------------ */
+/* Error feedback and partial aggregation  ([THC] sections 5 and 8)     */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Error feedback: worker i keeps a binary32 vector e_i of what compression
+ * has lost so far; it sends x_i = fl32(grad_i + e_i) and then keeps
+ * e_i' = fl32(x_i - xhat_i), where xhat_i is the value its own indices
+ * stand for: m + (float)v ((M - m) / levels), or m when M == m, with v = z,
+ * levels = 2^b - 1 (uniform) or v = T[z], levels = g (table). That is the
+ * server's dequantization of a one-worker sum, so e' needs nothing from
+ * the server. errs is a host array of P device pointers to N binary32
+ * values each; the fast path needs them 16-byte aligned like the inputs.
+ *
+ * thc_ef_minmax -- as thc_minmax, over x_i = grad_i + e_i.
+ */
+ga_status thc_ef_minmax(const void* const* bufs, const float* const* errs, int32_t P, int64_t N,
+                        ga_dtype dt, int64_t part_elems, float* d_mM, void* stream);
+
+/*
+ * thc_ef_quantize -- as thc_usq_quantize (h_table NULL; g ignored) or
+ * thc_nuhc_quantize (h_table, g) applied to x_i = grad_i + e_i, with the
+ * same indices, packing and keying; then overwrites e_i with x_i - xhat_i.
+ * One pass: reads grad and e, writes the packed indices and e.
+ *
+ * Partial aggregation (stragglers, [THC] section 8): the server may sum
+ * only the workers that arrived: pass their packed buffers alone to
+ * thc_int_aggregate / thc_nuhc_aggregate and their count as P to
+ * thc_dequant / thc_nuhc_dequant; the result estimates the mean of those
+ * workers.
+ */
+ga_status thc_ef_quantize(const void* const* bufs, float* const* errs, int32_t P, int32_t worker0,
+                          int64_t N, ga_dtype dt, int64_t part_elems, const float* d_mM, int32_t b,
+                          int32_t g, const int32_t* h_table, uint64_t seed, uint8_t* const* packed,
+                          void* stream);
 
 /* ------------------------------------------------------------------ */
 /* Randomized Hadamard transform  ([THC] section 5)                    */

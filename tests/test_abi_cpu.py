@@ -27,7 +27,7 @@ def _declared():
 def test_header_declarations_are_exported():
     L = nat.load()
     names = _declared()
-    assert len(names) == 21
+    assert len(names) == 23
     assert set(names) == set(nat.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -261,3 +261,19 @@ def test_fusion_ring_allreduce_errors_before_enqueue():
     assert f(None, None, 0, 0, 4, 0, 0, 1, 0, 0, C.byref(st), None) == 0
     assert f(0x1000, 0x2000, 2, 8, 1, 30, 0, 1, 2, 0, C.byref(st), None) == 0          # P = 1
     assert st.steps == 0 and st.launches == 0
+
+
+def test_ef_argument_errors_before_enqueue():
+    L = nat.load()
+    good = _ptrs([0x10000 * (i + 1) for i in range(4)])
+    errs = _ptrs([0x100000 * (i + 1) for i in range(4)])
+    assert L.thc_ef_minmax(good, None, 4, 16, 0, 0, 0x50000, None) == EINVAL        # no errors
+    assert L.thc_ef_minmax(good, _ptrs([0x100000, 0x200002, 0x300000, 0x400000]), 4, 16, 0, 0,
+                           0x50000, None) == EINVAL                                # misaligned e
+    assert L.thc_ef_minmax(good, errs, 4, 0, 0, 0, 0x50000, None) == 0              # empty
+    q = L.thc_ef_quantize
+    assert q(good, None, 4, 0, 16, 0, 0, 0x50000, 4, 0, None, 1, good, None) == EINVAL
+    assert q(good, errs, 4, 0, 16, 0, 0, 0x50000, 3, 0, None, 1, good, None) == EINVAL   # b = 3
+    bad = (C.c_int32 * 4)(0, 3, 3, 4)
+    assert q(good, errs, 4, 0, 16, 0, 0, 0x50000, 2, 4, bad, 1, good, None) == EINVAL   # table
+    assert q(good, errs, 4, 0, 0, 0, 0, 0x50000, 4, 0, None, 1, good, None) == 0        # empty

@@ -1,0 +1,102 @@
+"""GPU parity for error feedback and partial aggregation (THC page,
+sections 5 and 8): min/max of grad + e, the quantizer on grad + e with the
+residual written back, several rounds in a row, and the server summing only
+the workers that arrived, all bit for bit against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gradient_all_reduce_worker_amd import _native as ga
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _host(t):
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.numpy().copy()
+
+
+def _grads(P, N, dt, seed, misalign=0):
+    rng = np.random.default_rng(seed)
+    g = torch.from_numpy((rng.standard_normal((P, N + misalign)) * 0.01).astype(np.float32))
+    e = torch.from_numpy((rng.standard_normal((P, N + misalign)) * 0.002).astype(np.float32))
+    if dt == ga.BF16:
+        g = g.to(torch.bfloat16)
+    gs = [g[i].clone().to(DEV)[misalign:] for i in range(P)]
+    es = [e[i].clone().to(DEV)[misalign:] for i in range(P)]
+    return gs, es
+
+
+TABLES = [None, (2, 4, [0, 1, 3, 4]), (4, 36, ga.center_table(4, 36))]
+
+
+@pytest.mark.parametrize("table", TABLES)
+@pytest.mark.parametrize("dt", [ga.F32, ga.BF16])
+@pytest.mark.parametrize("P,N,part,b,mis", [(3, 70001, 1000, 4, 0), (4, 8192 * 6, 8192, 2, 0),
+                                            (2, 17, 0, 8, 0), (8, 1 << 18, 1 << 16, 1, 0),
+                                            (5, 9000, 0, 4, 1)])
+def test_ef_minmax_and_quantize(P, N, part, b, mis, dt, table):
+    if table is not None:
+        b, g, T = table
+    else:
+        g, T = 0, None
+    gs, es = _grads(P, N, dt, seed=N + b + mis, misalign=mis)
+    gh = [_host(x) for x in gs]
+    eh = [_host(x) for x in es]
+    seed = 0xEF00_0000_0000_0001 + b
+    mM = ga.thc_ef_minmax(gs, es, part)
+    xs = [oracle.ef_add(gh[i], eh[i]) for i in range(P)]
+    mMw = oracle.minmax(xs, part)
+    assert np.array_equal(mM.cpu().numpy().view(np.uint32), mMw.view(np.uint32))
+    packed = ga.thc_ef_quantize(gs, es, mM, b, seed, part_elems=part, worker0=1, g=g, table=T)
+    for i in range(P):
+        if T is None:
+            pw = oracle.usq_quantize(xs[i], 1 + i, part, mMw, b, seed)
+        else:
+            pw = oracle.nuhc_quantize(xs[i], 1 + i, part, mMw, b, g, T, seed)
+        assert np.array_equal(packed[i].cpu().numpy(), pw), i
+        ew = oracle.ef_update(xs[i], pw, b, part, mMw, g=g, T=T)
+        assert np.array_equal(_host(es[i]).view(np.uint32), ew.view(np.uint32)), i
+
+
+def test_ef_rounds_track_the_oracle():
+    P, N, part, b, rounds = 4, 3 * 8192 + 77, 8192, 2, 4
+    rng = np.random.default_rng(5)
+    es = [torch.zeros(N, device=DEV) for _ in range(P)]
+    eh = [np.zeros(N, dtype=np.float32) for _ in range(P)]
+    for t in range(rounds):
+        gh = [(rng.standard_normal(N) * 0.01).astype(np.float32) for _ in range(P)]
+        gs = [torch.from_numpy(x).to(DEV) for x in gh]
+        mM = ga.thc_ef_minmax(gs, es, part)
+        packed = ga.thc_ef_quantize(gs, es, mM, b, 77 + t, part_elems=part)
+        xs = [oracle.ef_add(gh[i], eh[i]) for i in range(P)]
+        mMw = oracle.minmax(xs, part)
+        pw = [oracle.usq_quantize(xs[i], i, part, mMw, b, 77 + t) for i in range(P)]
+        eh = [oracle.ef_update(xs[i], pw[i], b, part, mMw) for i in range(P)]
+        S = ga.thc_int_aggregate(packed, N, b)
+        assert np.array_equal(S.cpu().numpy()[:N], oracle.int_aggregate(pw, N, b))
+    for i in range(P):
+        assert np.array_equal(es[i].cpu().numpy().view(np.uint32), eh[i].view(np.uint32))
+
+
+@pytest.mark.parametrize("b", [2, 4, 8])
+def test_partial_aggregation(b):
+    """The server sums only the workers that arrived and divides by their
+    count."""
+    P, N, part = 10, 100003, 4096
+    gs, _ = _grads(P, N, ga.F32, seed=b)
+    mM = ga.thc_minmax(gs, part)
+    packed = ga.thc_usq_quantize(gs, mM, b, 99, part_elems=part)
+    arrived = [0, 1, 3, 4, 6, 8, 9]
+    S = ga.thc_int_aggregate([packed[i] for i in arrived], N, b)
+    est = ga.thc_dequant(S, N, len(arrived), b, mM, part_elems=part)
+    mMw = mM.cpu().numpy()
+    pw = [oracle.usq_quantize(_host(gs[i]), i, part, mMw, b, 99) for i in arrived]
+    Sw = oracle.int_aggregate(pw, N, b)
+    assert np.array_equal(S.cpu().numpy()[:N], Sw)
+    want = oracle.dequant(Sw, len(arrived), b, part, mMw)
+    assert np.array_equal(est.cpu().numpy()[:N].view(np.uint32), want.view(np.uint32))

@@ -33,10 +33,24 @@ def _free_memory():
     torch.cuda.empty_cache()
 
 
-def _check_partition(w, P, lo, xs, got, nu_tables=None):
-    """Oracle on one partition [lo, lo + n) of a flat workload."""
+def _check_partition(w, P, lo, xs, got, nu_tables=None, arrived=None):
+    """Oracle on one partition [lo, lo + n) of a flat workload (first step:
+    error-feedback residuals start at zero)."""
     n = xs[0].size
     xs = [x.copy() for x in xs]
+    for b in w.ef_bits:
+        k = f"ef{b}"
+        xe = [oracle.ef_add(x, np.zeros(n, dtype=np.float32)) for x in xs]
+        mMe = oracle.minmax(xe, n)
+        assert np.array_equal(got["mM_ef"][k].view(np.uint32), mMe[0].view(np.uint32)), k
+        pk = [oracle.usq_quantize(xe[i], i, n, mMe, b, w.quant_seed, e_offset=lo) for i in range(P)]
+        for i in range(P):
+            assert np.array_equal(got["packed"][k][i], pk[i]), (k, i)
+            ew = oracle.ef_update(xe[i], pk[i], b, n, mMe)
+            assert np.array_equal(got["err"][k][i].view(np.uint32), ew.view(np.uint32)), (k, i)
+        S = oracle.int_aggregate(pk, n, b)
+        assert np.array_equal(got["S"][k], S), k
+        assert np.array_equal(_u(got["xhat"][k]), _u(oracle.dequant(S, P, b, n, mMe, w.dtype))), k
     mM = oracle.minmax(xs, n)
     assert np.array_equal(got["mM"].view(np.uint32), mM[0].view(np.uint32))
     packed = {}
@@ -58,6 +72,13 @@ def _check_partition(w, P, lo, xs, got, nu_tables=None):
         assert np.array_equal(got["S"][b], S)
         xh = oracle.dequant(S, P, b, n, mM, w.dtype)
         assert np.array_equal(_u(got["xhat"][b]), _u(xh))
+    if arrived is not None and len(arrived) < P and w.thc_bits:
+        b = w.thc_bits[0]
+        k = f"part{b}"
+        S = oracle.int_aggregate([packed[b][i] for i in arrived], n, b)
+        assert np.array_equal(got["S"][k], S), k
+        xh = oracle.dequant(S, len(arrived), b, n, mM, w.dtype)
+        assert np.array_equal(_u(got["xhat"][k]), _u(xh)), k
     for k, (b, g, T) in (nu_tables or {}).items():
         Y = oracle.nuhc_aggregate(packed[k], n, b, g, T)
         assert np.array_equal(got["S"][k], Y), k
@@ -112,7 +133,8 @@ def test_flat_workload_sampled(name):
     after = pipe.sample_outputs(which)
     plen = pipe.w.part_elems
     for p in which:
-        _check_partition(pipe.w, pipe.P, p * plen, before[p], after[p], pipe.nu_tables)
+        _check_partition(pipe.w, pipe.P, p * plen, before[p], after[p], pipe.nu_tables,
+                         pipe.arrived)
     for key, (_, _, d, _) in pipe.rht.items():
         assert d == plen                    # RHT blocks are the sampled partitions
         got = pipe.sample_rht_outputs(key, which)
