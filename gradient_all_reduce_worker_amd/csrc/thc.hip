@@ -326,13 +326,19 @@ __device__ __forceinline__ float ef_value(EfGrid q, float v) {
     return q.flat ? q.m : q.m + v * q.delta;
 }
 
+// The 8 residuals of group g, read and written through L2 (plain loads and
+// stores): the lines just read are still cached when the two 16-byte
+// halves of each group are written back, so no line is fetched twice.
+__device__ __forceinline__ void load_err_group(const float* err, int64_t g, float* f) {
+    const float4* q = reinterpret_cast<const float4*>(err) + 2 * g;
+    const float4 a = q[0], b = q[1];
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
 __device__ __forceinline__ void store_err_group(float* err, int64_t g, const float* f) {
-    store_stream(reinterpret_cast<uint4*>(err) + 2 * g,
-                 make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
-                            __float_as_uint(f[3])));
-    store_stream(reinterpret_cast<uint4*>(err) + 2 * g + 1,
-                 make_uint4(__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]),
-                            __float_as_uint(f[7])));
+    float4* q = reinterpret_cast<float4*>(err) + 2 * g;
+    q[0] = make_float4(f[0], f[1], f[2], f[3]);
+    q[1] = make_float4(f[4], f[5], f[6], f[7]);
 }
 
 // Called by every thread of the workgroup before any early exit.
@@ -381,7 +387,7 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_fast_kernel(PtrTable bu
         float ev[kQGroups][8];
 #pragma unroll
         for (int j = 0; j < kQGroups; j++)
-            load_group<GA_F32>(err, e_blk / 8 + (int64_t)j * kThreads + threadIdx.x, ev[j]);
+            load_err_group(err, e_blk / 8 + (int64_t)j * kThreads + threadIdx.x, ev[j]);
 #pragma unroll
         for (int j = 0; j < kQGroups; j++)
 #pragma unroll
@@ -439,7 +445,7 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_kernel(PtrTable bufs, P
             load_group<DT>(x, g, a);
             if (EF) {
                 float ev[8];
-                load_group<GA_F32>(err, g, ev);
+                load_err_group(err, g, ev);
 #pragma unroll
                 for (int i = 0; i < 8; i++) a[i] = a[i] + ev[i];
             }
