@@ -246,8 +246,8 @@ __device__ __forceinline__ void fold_uniform(const PS& bufs, int P, const int64_
     }
 }
 
-// VPT 16-byte vectors per thread and BATCH worker loads in flight: one vector
-// and 16 loads for P <= 8, two vectors and 8 loads for larger P (measured).
+// VPT 16-byte vectors per thread and BATCH worker loads in flight per
+// vector (the host picks them with fold_shape).
 template <ga_dtype DT, int VPT, int BATCH, bool DUAL>
 __global__ __launch_bounds__(kThreads) void ring_fused_vec_kernel(PtrTable bufs, int P, int64_t N,
                                                                   int64_t plen, int64_t n_vec,
@@ -315,54 +315,65 @@ __device__ __forceinline__ int64_t tensor_of(const ga_fusion_tensor* T, int64_t 
 // each tensor's own memory. Work vector u is 16 bytes of one tensor (its
 // last one possibly short); its elements sit at buffer offsets start + j,
 // which decide the partition, chunk and so the fold order, exactly as in the
-// packed buffer. A workgroup whose vectors are whole, lie in one tensor with
-// 16-byte aligned copies, and share one chunk folds with one rotation and
-// the tensor's pointers read once; any other takes them vector by vector.
+// packed buffer. A workgroup walks `blocks` consecutive blocks of kThreads
+// vectors; the tensor of its first vector is found by binary search once,
+// later ones by stepping forward. A block whose vectors are
+// whole, lie in one tensor with 16-byte aligned copies, and share one chunk
+// folds with one rotation and the tensor's pointers read once; any other
+// goes vector by vector.
 template <ga_dtype DT, bool DUAL>
 __global__ __launch_bounds__(kThreads) void fusion_ring_kernel(const ga_fusion_tensor* __restrict__ T,
                                                                void* const* __restrict__ ptrs,
                                                                int64_t nt, int64_t n_work, int P,
-                                                               int64_t fill, int64_t plen, Div div) {
+                                                               int64_t fill, int64_t plen, int blocks,
+                                                               Div div) {
     using E = Elem<DT>;
     constexpr int V = E::kVec;
     const int nch = DUAL ? 2 * P : P;
-    const int64_t u0 = (int64_t)blockIdx.x * kThreads;
-    const int64_t u1 = min(u0 + (int64_t)kThreads, n_work);
-    const int64_t t0 = tensor_of(T, nt, u0);
-    if (tensor_of(T, nt, u1 - 1) == t0 && T[t0].vec) {
-        const ga_fusion_tensor d = T[t0];
-        const int64_t j0 = u0 - d.vstart, j1 = u1 - d.vstart;     // vectors of the tensor
-        if (j1 * V <= d.n) {
-            const Where first = locate(d.start + j0 * V, fill, plen, nch);
-            const Where last = locate(d.start + j1 * V - 1, fill, plen, nch);
-            if (first.part == last.part && first.chunk == last.chunk) {
-                const RowPtrs row{ptrs + t0 * P};
-                int64_t v[1] = {j0 + threadIdx.x};
-                bool ok[1] = {v[0] < j1};
-                const Rot rt = rot_of<DUAL>(first.chunk, P);
-                if (P <= 8) fold_uniform<DT, 1, 16>(row, P, v, ok, rt, div);
-                else fold_uniform<DT, 1, 8>(row, P, v, ok, rt, div);
-                return;
+    const int64_t w0 = (int64_t)blockIdx.x * kThreads * blocks;
+    const int64_t w1 = min(w0 + (int64_t)kThreads * blocks, n_work);
+    int64_t t0 = tensor_of(T, nt, w0);
+    for (int64_t u0 = w0; u0 < w1; u0 += kThreads) {
+        const int64_t u1 = min(u0 + (int64_t)kThreads, w1);
+        while (t0 + 1 < nt && T[t0 + 1].vstart <= u0) t0++;        // tensor of u0
+        int64_t tl = t0;                                            // tensor of u1 - 1
+        while (tl + 1 < nt && T[tl + 1].vstart <= u1 - 1) tl++;
+        if (tl == t0 && T[t0].vec) {
+            const ga_fusion_tensor d = T[t0];
+            const int64_t j0 = u0 - d.vstart, j1 = u1 - d.vstart;   // vectors of the tensor
+            if (j1 * V <= d.n) {
+                const Where first = locate(d.start + j0 * V, fill, plen, nch);
+                const Where last = locate(d.start + j1 * V - 1, fill, plen, nch);
+                if (first.part == last.part && first.chunk == last.chunk) {
+                    const RowPtrs row{ptrs + t0 * P};
+                    int64_t v[1] = {j0 + threadIdx.x};
+                    bool ok[1] = {v[0] < j1};
+                    const Rot rt = rot_of<DUAL>(first.chunk, P);
+                    if (P <= 8) fold_uniform<DT, 1, 16>(row, P, v, ok, rt, div);
+                    else fold_uniform<DT, 1, 8>(row, P, v, ok, rt, div);
+                    continue;
+                }
             }
         }
-    }
-    const int64_t u = u0 + threadIdx.x;
-    if (u >= u1) return;
-    const int64_t t = tensor_of(T, nt, u);
-    const ga_fusion_tensor d = T[t];
-    const RowPtrs row{ptrs + t * P};
-    const int64_t j = u - d.vstart;
-    const int64_t e0 = j * V, e1 = min(e0 + V, d.n);                // tensor elements
-    if (d.vec && e1 - e0 == V) {
-        const Where a = locate(d.start + e0, fill, plen, nch);
-        const Where b = locate(d.start + e1 - 1, fill, plen, nch);
-        if (a.part == b.part && a.chunk == b.chunk) {
-            fold_vec<DT>(row, P, j, rot_of<DUAL>(a.chunk, P), div);
-            return;
+        const int64_t u = u0 + threadIdx.x;
+        if (u >= u1) continue;
+        int64_t t = t0;                                             // t0 <= tensor of u <= tl
+        while (t < tl && T[t + 1].vstart <= u) t++;
+        const ga_fusion_tensor d = T[t];
+        const RowPtrs row{ptrs + t * P};
+        const int64_t j = u - d.vstart;
+        const int64_t e0 = j * V, e1 = min(e0 + V, d.n);            // tensor elements
+        if (d.vec && e1 - e0 == V) {
+            const Where a = locate(d.start + e0, fill, plen, nch);
+            const Where b = locate(d.start + e1 - 1, fill, plen, nch);
+            if (a.part == b.part && a.chunk == b.chunk) {
+                fold_vec<DT>(row, P, j, rot_of<DUAL>(a.chunk, P), div);
+                continue;
+            }
         }
+        for (int64_t e = e0; e < e1; e++)
+            fold_elem<DT>(row, P, e, rot_of<DUAL>(locate(d.start + e, fill, plen, nch).chunk, P), div);
     }
-    for (int64_t e = e0; e < e1; e++)
-        fold_elem<DT>(row, P, e, rot_of<DUAL>(locate(d.start + e, fill, plen, nch).chunk, P), div);
 }
 
 // ---------------------------------------------------------------- stepwise
@@ -464,6 +475,36 @@ bool disjoint(void* const* bufs, int P, int64_t bytes) {
     return true;
 }
 
+// Launch shape of the fused fold, measured on MI355X. Folding P streams and
+// writing P back keeps 2P DRAM streams open per workgroup; on large buffers
+// fewer resident workgroups per CU keep fewer rows open and stream faster
+// (8 x 4 GiB bf16: 0.72 -> 0.79 of 8 TB/s at two workgroups per CU; 16
+// workers of 66 MB: 0.68 -> 0.74 at one; 32 workers of 553 MB with four
+// vectors per thread: 0.73 -> 0.77 at four). Residency is capped with
+// unused dynamic LDS (160 KiB per CU). Small buffers keep full occupancy.
+struct FoldShape {
+    int vpt;        // 16-byte vectors per thread
+    int batch;      // worker loads in flight per vector
+    size_t lds;     // dynamic LDS per workgroup (0: no cap)
+};
+
+constexpr size_t kLdsPerCu = 160 * 1024;
+
+size_t cap_workgroups_per_cu(int k) { return kLdsPerCu / (size_t)k - 1024; }
+
+FoldShape fold_shape(int P, int64_t total_bytes) {
+    const bool big = total_bytes >= (int64_t)1 << 30;
+    if (P <= 8) return {1, 16, big ? cap_workgroups_per_cu(2) : 0};
+    if (P <= 16) return {1, 16, big ? cap_workgroups_per_cu(1) : 0};
+    return {4, 4, big ? cap_workgroups_per_cu(4) : 0};
+}
+
+// The zero-copy fusion ring: two resident workgroups per CU on large
+// buffers (ResNet-101 buffers, 16 workers: 0.60 -> 0.64 of 8 TB/s).
+size_t fusion_cap(int64_t total_bytes) {
+    return total_bytes >= (int64_t)1 << 30 ? cap_workgroups_per_cu(2) : 0;
+}
+
 // The fused fold over the whole buffer: the vector kernel over 16-byte
 // vectors when every buffer is 16-byte aligned, the element kernel for the
 // rest. Returns the number of launches, or a negative status.
@@ -479,20 +520,20 @@ int64_t launch_fused(void* const* bufs, int P, int64_t N, ga_dtype dt, int64_t p
     int64_t launches = 0;
     ga_status rc;
     if (vec_ok && n_vec > 0) {
-        const bool wide = P > 8;
-        const unsigned blocks = (unsigned)ceil_div(n_vec, (int64_t)kThreads * (wide ? 2 : 1));
-        if (dt == GA_F32 && wide)
-            hipLaunchKernelGGL((ring_fused_vec_kernel<GA_F32, 2, 8, DUAL>), dim3(blocks),
-                               dim3(kThreads), 0, hs, t, P, N, plen, n_vec, div);
+        const FoldShape sh = fold_shape(P, 2 * (int64_t)P * N * (int64_t)elem_size(dt));
+        const unsigned blocks = (unsigned)ceil_div(n_vec, (int64_t)kThreads * sh.vpt);
+        if (dt == GA_F32 && sh.vpt == 4)
+            hipLaunchKernelGGL((ring_fused_vec_kernel<GA_F32, 4, 4, DUAL>), dim3(blocks),
+                               dim3(kThreads), sh.lds, hs, t, P, N, plen, n_vec, div);
         else if (dt == GA_F32)
             hipLaunchKernelGGL((ring_fused_vec_kernel<GA_F32, 1, 16, DUAL>), dim3(blocks),
-                               dim3(kThreads), 0, hs, t, P, N, plen, n_vec, div);
-        else if (wide)
-            hipLaunchKernelGGL((ring_fused_vec_kernel<GA_BF16, 2, 8, DUAL>), dim3(blocks),
-                               dim3(kThreads), 0, hs, t, P, N, plen, n_vec, div);
+                               dim3(kThreads), sh.lds, hs, t, P, N, plen, n_vec, div);
+        else if (sh.vpt == 4)
+            hipLaunchKernelGGL((ring_fused_vec_kernel<GA_BF16, 4, 4, DUAL>), dim3(blocks),
+                               dim3(kThreads), sh.lds, hs, t, P, N, plen, n_vec, div);
         else
             hipLaunchKernelGGL((ring_fused_vec_kernel<GA_BF16, 1, 16, DUAL>), dim3(blocks),
-                               dim3(kThreads), 0, hs, t, P, N, plen, n_vec, div);
+                               dim3(kThreads), sh.lds, hs, t, P, N, plen, n_vec, div);
         launches++;
         if ((rc = check_launch(what))) return rc;
     }
@@ -688,19 +729,21 @@ extern "C" ga_status ga_fusion_ring_allreduce(const ga_fusion_tensor* d_tensors,
     }
     if (!d_tensors || !d_ptrs || !aligned(d_tensors, 8) || !aligned(d_ptrs, 8))
         return fail(GA_EINVAL, "%s: null or misaligned table", what);
-    if (ceil_div(n_work, kThreads) > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: too much work", what);
+    if (ceil_div(n_work, (int64_t)kThreads) > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: too much work", what);
     const int64_t plen = part_elems > 0 ? part_elems : fill;
     Div div{op == GA_AVG, (P & (P - 1)) == 0, (float)P, 1.0f / (float)P};
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    const dim3 grid((unsigned)ceil_div(n_work, kThreads));
+    const size_t lds = fusion_cap(2 * (int64_t)P * fill * es);
+    const int blocks = 1;   // measured fastest at every residency (ResNet-101 buffers)
+    const dim3 grid((unsigned)ceil_div(n_work, (int64_t)kThreads * blocks));
     if (dt == GA_F32 && mode == GA_RING_DUAL)
-        hipLaunchKernelGGL((fusion_ring_kernel<GA_F32, true>), grid, dim3(kThreads), 0, hs, d_tensors, d_ptrs, n_tensors, n_work, P, fill, plen, div);
+        hipLaunchKernelGGL((fusion_ring_kernel<GA_F32, true>), grid, dim3(kThreads), lds, hs, d_tensors, d_ptrs, n_tensors, n_work, P, fill, plen, blocks, div);
     else if (dt == GA_F32)
-        hipLaunchKernelGGL((fusion_ring_kernel<GA_F32, false>), grid, dim3(kThreads), 0, hs, d_tensors, d_ptrs, n_tensors, n_work, P, fill, plen, div);
+        hipLaunchKernelGGL((fusion_ring_kernel<GA_F32, false>), grid, dim3(kThreads), lds, hs, d_tensors, d_ptrs, n_tensors, n_work, P, fill, plen, blocks, div);
     else if (mode == GA_RING_DUAL)
-        hipLaunchKernelGGL((fusion_ring_kernel<GA_BF16, true>), grid, dim3(kThreads), 0, hs, d_tensors, d_ptrs, n_tensors, n_work, P, fill, plen, div);
+        hipLaunchKernelGGL((fusion_ring_kernel<GA_BF16, true>), grid, dim3(kThreads), lds, hs, d_tensors, d_ptrs, n_tensors, n_work, P, fill, plen, blocks, div);
     else
-        hipLaunchKernelGGL((fusion_ring_kernel<GA_BF16, false>), grid, dim3(kThreads), 0, hs, d_tensors, d_ptrs, n_tensors, n_work, P, fill, plen, div);
+        hipLaunchKernelGGL((fusion_ring_kernel<GA_BF16, false>), grid, dim3(kThreads), lds, hs, d_tensors, d_ptrs, n_tensors, n_work, P, fill, plen, blocks, div);
     ga_status rc = check_launch(what);
     if (rc) return rc;
     s.launches = 1;
