@@ -206,6 +206,7 @@ __global__ __launch_bounds__(kThreads) void minmax_kernel(PtrTable bufs, PtrTabl
 // the wave. When the partition length is a multiple of a workgroup's span
 // of elements, all its groups share one grid, loaded once (scalar loads).
 constexpr int kQGroups = 4;
+constexpr size_t kLdsPerCu = 160 * 1024;      // LDS per CU (residency caps)
 constexpr int64_t kQSpan = (int64_t)kThreads * kQGroups * 8;   // elements per workgroup
 
 struct Grid {                // one partition's grid
@@ -411,16 +412,111 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_fast_kernel(PtrTable bu
     }
 }
 
-// Generic kernel for the workgroups the fast one does not take (from
-// workgroup blk0 on): partial groups, misaligned buffers, partitions that
-// are not a multiple of a workgroup's span.
+// Fast kernel for binary32 inputs. A group of 8 fp32 is 32 bytes; loaded
+// per thread it takes two 16-byte loads that each cover every other half
+// of the lines a wave touches. Here every load and store instruction is
+// contiguous across the wave instead: thread t takes 16-byte vectors t and
+// t + 256 of a 2048-element span (elements 4t..4t+3 and 1024+4t..), i.e.
+// one half of group t/2 and one half of group 128 + t/2. Each lane draws
+// the Philox block of one of those groups and swaps two words with its
+// neighbour (DPP), so a call still serves 8 elements and every element gets
+// the uniform of the same counter and word as in the per-group kernels:
+// identical bits. (MI355X, 32 workers x 138M fp32: b = 4 0.65 -> 0.75 of
+// 8 TB/s, b = 8 0.68 -> 0.75.)
+constexpr int64_t kLSpan = 2048;       // elements per workgroup of the lane kernel
+
+__device__ __forceinline__ uint32_t swap_pair(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // lanes 2k <-> 2k+1
+}
+
+__device__ __forceinline__ void widen_f32(const uint4& r, float* f) {
+    f[0] = __uint_as_float(r.x); f[1] = __uint_as_float(r.y);
+    f[2] = __uint_as_float(r.z); f[3] = __uint_as_float(r.w);
+}
+
+template <int B, bool TABLE, bool EF>
+__global__ __launch_bounds__(kThreads) void usq_quantize_lane_kernel(PtrTable bufs, PtrTable errs,
+                                                                     PtrTable packed, int worker0,
+                                                                     int64_t plen, int64_t n_spans,
+                                                                     int spans,
+                                                                     const float* __restrict__ mM,
+                                                                     uint32_t k0, uint32_t k1,
+                                                                     TableArg tab) {
+    constexpr int L = (1 << B) - 1;
+    __shared__ uint32_t cells[TABLE ? kMaxGranularity : 1];
+    const Rounder<TABLE> rd = make_rounder<TABLE>(tab, L, cells);
+    const int slot = blockIdx.y;
+    const uint4* x = static_cast<const uint4*>(bufs.p[slot]);
+    uint4* err = EF ? static_cast<uint4*>(errs.p[slot]) : nullptr;
+    uint8_t* out = static_cast<uint8_t*>(packed.p[slot]);
+    const uint32_t wid = (uint32_t)(worker0 + slot);
+    const int t = threadIdx.x;
+    const bool odd = t & 1;
+    for (int sp = 0; sp < spans; sp++) {                 // spans of this workgroup
+        const int64_t blk = (int64_t)blockIdx.x * spans + sp;
+        if (blk >= n_spans) break;
+        const int64_t e_blk = blk * kLSpan;
+        const Grid gb = grid_of(mM, e_blk / plen, rd.levels);
+        const int64_t v0 = e_blk / 4 + t;                // vectors v0 and v0 + 256
+        float a[2][4];
+        widen_f32(load_stream(x + v0), a[0]);
+        widen_f32(load_stream(x + v0 + 256), a[1]);
+        if (EF) {
+            float ev[2][4];
+            widen_f32(load_stream(err + v0), ev[0]);
+            widen_f32(load_stream(err + v0 + 256), ev[1]);
+#pragma unroll
+            for (int h = 0; h < 2; h++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) a[h][i] = a[h][i] + ev[h][i];
+        }
+        const EfGrid q = EF ? ef_grid_of(mM, e_blk / plen, rd.levels) : EfGrid{};
+        const int64_t g = e_blk / 8 + (odd ? 128 + (t >> 1) : (t >> 1));
+        const Philox4 r = philox4x32_10((uint32_t)g, (uint32_t)((uint64_t)g >> 32), wid, 0u, k0, k1);
+        const uint32_t ra = swap_pair(odd ? r.v[0] : r.v[2]);
+        const uint32_t rb = swap_pair(odd ? r.v[1] : r.v[3]);
+        // words of the uniforms of this lane's two half-groups
+        const uint32_t u[2][2] = {{odd ? ra : r.v[0], odd ? rb : r.v[1]},
+                                  {odd ? r.v[2] : ra, odd ? r.v[3] : rb}};
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            uint32_t bits = 0;
+            float res[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const uint32_t r16 = (u[h][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                float v;
+                bits |= rd.index_v(a[h][i], gb, r16, &v) << (i * B);
+                if (EF) res[i] = a[h][i] - ef_value(q, v);
+            }
+            const int64_t vv = v0 + h * 256;
+            if (B == 8) {
+                reinterpret_cast<uint32_t*>(out)[vv] = bits;
+            } else if (B == 4) {
+                reinterpret_cast<uint16_t*>(out)[vv] = (uint16_t)bits;
+            } else if (B == 2) {
+                out[vv] = (uint8_t)bits;
+            } else {                                    // two vectors per byte
+                const uint32_t other = swap_pair(bits);
+                if (!odd) out[vv >> 1] = (uint8_t)(bits | (other << 4));
+            }
+            if (EF)
+                store_stream(err + vv, make_uint4(__float_as_uint(res[0]), __float_as_uint(res[1]),
+                                                  __float_as_uint(res[2]), __float_as_uint(res[3])));
+        }
+    }
+}
+
+// Generic kernel for what the fast kernels do not take (from element
+// e_begin, a multiple of 8, on): partial groups, misaligned buffers,
+// partitions that are not a multiple of a fast workgroup's span.
 template <ga_dtype DT, int B, bool TABLE, bool EF>
 __global__ __launch_bounds__(kThreads) void usq_quantize_kernel(PtrTable bufs, PtrTable errs,
                                                                 PtrTable packed, int worker0,
                                                                 int64_t N, int64_t plen,
                                                                 const float* __restrict__ mM,
                                                                 uint32_t k0, uint32_t k1,
-                                                                int vec_ok, int64_t blk0,
+                                                                int vec_ok, int64_t e_begin,
                                                                 TableArg tab) {
     constexpr int L = (1 << B) - 1;
     __shared__ uint32_t cells[TABLE ? kMaxGranularity : 1];
@@ -430,7 +526,7 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_kernel(PtrTable bufs, P
     float* err = EF ? static_cast<float*>(errs.p[slot]) : nullptr;
     uint8_t* out = static_cast<uint8_t*>(packed.p[slot]);
     const uint32_t wid = (uint32_t)(worker0 + slot);
-    const int64_t e_blk = (blk0 + blockIdx.x) * kQSpan;
+    const int64_t e_blk = e_begin + (int64_t)blockIdx.x * kQSpan;
     const int64_t n_full = N / 8;                      // groups of 8 elements
 #pragma unroll 1
     for (int j = 0; j < kQGroups; j++) {
@@ -861,23 +957,36 @@ ga_status quantize_impl(const void* const* bufs, int32_t P, int32_t worker0, int
             vec_ok &= aligned(errs[i], 16);
         }
     }
-    const int64_t blocks = ceil_div(N, kQSpan);
-    if (blocks > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: N too large", what);
-    // workgroups wholly inside N and inside one partition take the fast kernel
-    const int64_t fast = (vec_ok && plen % kQSpan == 0) ? N / kQSpan : 0;
+    if (ceil_div(N, kLSpan) > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: N too large", what);
+    // workgroups wholly inside N and inside one partition take a fast kernel:
+    // binary32 the lane kernel (2048 elements), bf16 the per-group one
+    const int64_t span = dt == GA_F32 ? kLSpan : kQSpan;
+    const int64_t fast = (vec_ok && plen % span == 0) ? N / span : 0;
+    const int64_t e_begin = fast * span;
+    const int64_t blocks = ceil_div(N - e_begin, kQSpan);       // generic workgroups
+    // the lane kernel streams best with at most six workgroups per CU; with
+    // a table each workgroup builds its LDS cell map first, so it takes four
+    // spans to spread that over
+    const size_t lane_lds = kLdsPerCu / 6 - 1024 - (table ? kMaxGranularity * 4 : 4);
+    const int lane_spans = table ? 4 : 1;
+    const int64_t lane_blocks = ceil_div(fast, lane_spans);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
     const TableArg tab = table ? *table : TableArg{};
 #define GA_Q2(DT, B, TB, EF)                                                                          \
     do {                                                                                              \
-        if (fast > 0)                                                                                 \
+        if (fast > 0 && DT == GA_F32)                                                                 \
+            hipLaunchKernelGGL((usq_quantize_lane_kernel<B, TB, EF>),                                 \
+                               dim3((unsigned)lane_blocks, (unsigned)P), dim3(kThreads), lane_lds,    \
+                               hs, tx, te, tp, worker0, plen, fast, lane_spans, d_mM, k0, k1, tab);   \
+        else if (fast > 0)                                                                            \
             hipLaunchKernelGGL((usq_quantize_fast_kernel<DT, B, TB, EF>),                             \
                                dim3((unsigned)fast, (unsigned)P), dim3(kThreads), 0, hs, tx, te, tp,  \
                                worker0, plen, d_mM, k0, k1, tab);                                     \
-        if (blocks > fast)                                                                            \
+        if (blocks > 0)                                                                               \
             hipLaunchKernelGGL((usq_quantize_kernel<DT, B, TB, EF>),                                  \
-                               dim3((unsigned)(blocks - fast), (unsigned)P), dim3(kThreads), 0, hs,   \
-                               tx, te, tp, worker0, N, plen, d_mM, k0, k1, vec_ok, fast, tab);        \
+                               dim3((unsigned)blocks, (unsigned)P), dim3(kThreads), 0, hs,            \
+                               tx, te, tp, worker0, N, plen, d_mM, k0, k1, vec_ok, e_begin, tab);     \
     } while (0)
 #define GA_Q(DT, B, TB)                                \
     do {                                               \
