@@ -16,5 +16,5 @@ from ._native import (  # noqa: F401
     packed_bytes, thc_dequant, thc_int_aggregate, thc_minmax, thc_nmse, thc_nmse_ws_bytes,
     thc_usq_quantize, upload_table, thc_nuhc_quantize, thc_nuhc_aggregate, thc_nuhc_dequant,
     center_table, RING_DUAL, FTENSOR_DTYPE, FusionRing, ga_fusion_ring_plan, rht_padded,
-    thc_rht_sumsq, thc_rht_range, thc_rht_forward, thc_rht_inverse,
+    thc_rht_sumsq, thc_rht_range, thc_rht_forward, thc_rht_inverse, thc_rht_quantize,
 )

@@ -28,6 +28,7 @@ EXPORTS = (
     "thc_nuhc_quantize", "thc_nuhc_aggregate", "thc_nuhc_dequant",
     "thc_rht_sumsq", "thc_rht_range", "thc_rht_forward", "thc_rht_inverse",
     "ga_fusion_ring_plan", "ga_fusion_ring_allreduce", "thc_ef_minmax", "thc_ef_quantize",
+    "thc_rht_quantize",
 )
 
 
@@ -87,6 +88,8 @@ def load() -> C.CDLL:
     L.thc_rht_range.argtypes = [vp, i32, i64, i64, C.c_double, vp, vp]
     L.thc_rht_forward.argtypes = [C.POINTER(vp), i32, i64, i32, i64, u64, vp, C.POINTER(vp), vp]
     L.thc_rht_inverse.argtypes = [vp, i64, i64, u64, vp, i32, vp]
+    L.thc_rht_quantize.argtypes = [C.POINTER(vp), i32, i32, i64, i32, i64, u64, vp, i32, i32,
+                                   C.POINTER(i32), u64, C.POINTER(vp), C.POINTER(vp), vp]
     L.ga_fusion_ring_plan.argtypes = [vp, vp, i64, i32, i32, i64, C.POINTER(i64)]
     L.ga_fusion_ring_allreduce.argtypes = [vp, vp, i64, i64, i32, i64, i32, i32, i32, i64,
                                            C.POINTER(RingStats), vp]
@@ -488,9 +491,36 @@ def thc_rht_forward(bufs: Sequence[torch.Tensor], d: int, seed: int,
     return y
 
 
+def thc_rht_quantize(bufs: Sequence[torch.Tensor], d: int, rht_seed: int, mM: torch.Tensor, b: int,
+                     q_seed: int, worker0: int = 0, g: int = 0, table=None,
+                     y_scratch: Optional[Sequence[torch.Tensor]] = None,
+                     packed: Optional[Sequence[torch.Tensor]] = None, stream=None):
+    """Truncated forward transform, then uniform (table None) or table
+    quantization of the transformed coordinates, one partition per block;
+    returns the packed indices of rht_padded(N, d) coordinates. y_scratch
+    (float32, rht_padded(N, d) each) is needed when d > 8192."""
+    N = bufs[0].numel()
+    Np = rht_padded(N, d)
+    if packed is None:
+        packed = [torch.empty(max(packed_bytes(Np, b), 1), dtype=torch.uint8, device=bufs[0].device)
+                  for _ in bufs]
+    if any(t.numel() < packed_bytes(Np, b) for t in packed):
+        raise ValueError("packed buffers must hold packed_bytes(rht_padded(N, d), b) bytes")
+    if y_scratch is None and d > 8192 and N > 0:
+        y_scratch = [torch.empty(Np, dtype=torch.float32, device=bufs[0].device) for _ in bufs]
+    if y_scratch is not None and any(t.dtype != torch.float32 or t.numel() < Np for t in y_scratch):
+        raise ValueError("y_scratch buffers must be float32 with rht_padded(N, d) elements")
+    _check(load().thc_rht_quantize(_ptr_array(bufs, "buffer"), len(bufs), worker0, N, _dt(bufs[0]),
+                                   d, rht_seed, _dev(mM, "mM"), b, g,
+                                   _table_arg(table) if table is not None else None, q_seed,
+                                   _ptr_array(y_scratch, "y_scratch") if y_scratch is not None else None,
+                                   _ptr_array(packed, "packed"), _stream(stream)))
+    return packed
+
+
 def thc_rht_inverse(y: torch.Tensor, N: int, d: int, seed: int, out_dtype=torch.float32,
                     out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """y (rht_padded(N, d) float32) is overwritten when d > 4096."""
+    """y (rht_padded(N, d) float32) is overwritten when d > 8192."""
     if out is None:
         out = torch.empty(max(N, 1), dtype=out_dtype, device=y.device)
     if y.dtype != torch.float32 or y.numel() < rht_padded(N, d) or out.numel() < N:

@@ -1,0 +1,138 @@
+// quant.hpp -- THC's rounding rules shared by the quantizer kernels (thc.hip)
+// and the transform-and-quantize kernels (rht.hip): the grid of a
+// partition, unbiased stochastic rounding to a uniform grid or to a lookup
+// table's neighbouring values ("THC: Accelerating Distributed Deep Learning
+// Using Tensor Homomorphic Compression", sections 3 and 4), the 16-bit
+// uniforms cut from a Philox4x32-10 block, and LSB-first packing.
+#pragma once
+#include "common.hpp"
+#include "philox.hpp"
+
+namespace ga {
+namespace {
+
+struct Grid {                // one partition's grid
+    float m;
+    float s;                 // L / (M - m), or 0 when M == m
+};
+
+__device__ __forceinline__ Grid grid_of(const float* mM, int64_t p, int L) {
+    const float m = mM[2 * p], M = mM[2 * p + 1];
+    const float range = M - m;
+    return {m, range == 0.0f ? 0.0f : (float)L / range};
+}
+
+// Stochastic rounding of one value to its grid index (binary32 throughout;
+// with s = 0 the index is 0).
+__device__ __forceinline__ uint32_t usq_index(float a, Grid g, int L, uint32_t r16) {
+    const float u = (a - g.m) * g.s;
+    const float z0 = fminf(floorf(u), (float)(L - 1));
+    const float f = u - z0;
+    const bool up = (float)(2u * r16 + 1u) < f * 131072.0f;
+    return (uint32_t)z0 + (up ? 1u : 0u);
+}
+
+__device__ __forceinline__ uint32_t uniform16(const Philox4& r, int i) {
+    return (r.v[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+}
+
+// The 8 b-bit indices of a group, least significant bits first (8 b bits).
+template <int B>
+__device__ __forceinline__ uint64_t pack_group(const uint32_t* z) {
+    uint64_t acc = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc |= (uint64_t)z[i] << (i * B);
+    return acc;
+}
+
+template <int B>
+__device__ __forceinline__ void store_group(uint8_t* out, int64_t g, uint64_t bits) {
+    if (B == 8) *reinterpret_cast<uint2*>(out + 8 * g) = make_uint2((uint32_t)bits, (uint32_t)(bits >> 32));
+    else if (B == 4) reinterpret_cast<uint32_t*>(out)[g] = (uint32_t)bits;
+    else if (B == 2) reinterpret_cast<uint16_t*>(out)[g] = (uint16_t)bits;
+    else out[g] = (uint8_t)bits;
+}
+
+// Rounding rules. Uniform THC: index k stands for m + k (M - m) / L. Non-
+// uniform THC ("THC" page, section 4, Algorithm 2): index z stands for the
+// table value T[z] on the finer grid m + t (M - m) / g, and a coordinate is
+// rounded stochastically to one of its two neighbouring table values. A
+// per-workgroup LDS map cell[k] = (z0, T[z0], T[z0 + 1]) for every integer
+// cell k in [0, g) gives the neighbours of a position u in [k, k + 1).
+constexpr int kMaxGranularity = 4095;
+
+struct TableArg {
+    uint16_t t[256];   // T[0 .. n-1], 0 = T[0] < ... < T[n-1] = g
+    int g;
+    int n;             // 2^b
+};
+
+template <bool TABLE>
+struct Rounder {
+    int levels;              // L for the uniform grid, g for a table
+    const uint32_t* cell;    // LDS cells (table only)
+    // The index of a; *v receives the grid level it stands for (the index
+    // itself, or its table value).
+    __device__ __forceinline__ uint32_t index_v(float a, Grid gr, uint32_t r16, float* v) const {
+        if (!TABLE) {
+            const uint32_t z = usq_index(a, gr, levels, r16);
+            *v = (float)z;
+            return z;
+        }
+        const float u = (a - gr.m) * gr.s;                      // position on <g+1>
+        const float k = fminf(floorf(u), (float)(levels - 1));
+        const uint32_t c = cell[(int)k];
+        const float lo = (float)((c >> 8) & 0xFFFu), hi = (float)(c >> 20);
+        const float f = (u - lo) / (hi - lo);
+        const bool up = (float)(2u * r16 + 1u) < f * 131072.0f;
+        *v = up ? hi : lo;
+        return (c & 0xFFu) + (up ? 1u : 0u);
+    }
+    __device__ __forceinline__ uint32_t index(float a, Grid gr, uint32_t r16) const {
+        float v;
+        return index_v(a, gr, r16, &v);
+    }
+};
+
+// Called by every thread of the workgroup (NT threads) before any early exit.
+template <bool TABLE, int NT = kThreads>
+__device__ __forceinline__ Rounder<TABLE> make_rounder(const TableArg& tab, int L, uint32_t* cells) {
+    if (!TABLE) return {L, nullptr};
+    for (int k = threadIdx.x; k < tab.g; k += NT) {
+        int lo = 0, hi = tab.n - 1;             // the largest z with T[z] <= k
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (tab.t[mid] <= k) lo = mid; else hi = mid - 1;
+        }
+        cells[k] = (uint32_t)lo | ((uint32_t)tab.t[lo] << 8) | ((uint32_t)tab.t[lo + 1] << 20);
+    }
+    __syncthreads();
+    return {tab.g, cells};
+}
+
+inline bool valid_bits(int b) { return b == 1 || b == 2 || b == 4 || b == 8; }
+
+// Host check of a non-uniform table: 0 = T[0] < ... < T[2^b - 1] = g,
+// 2^b - 1 <= g <= kMaxGranularity.
+inline ga_status load_table(int32_t b, int32_t g, const int32_t* h_table, TableArg* tab, const char* what) {
+    if (!valid_bits(b)) return fail(GA_EINVAL, "%s: b = %d is not 1, 2, 4 or 8", what, b);
+    if (!h_table) return fail(GA_EINVAL, "%s: null table", what);
+    const int n = 1 << b;
+    if (g < n - 1) return fail(GA_EINVAL, "%s: granularity %d < 2^b - 1", what, g);
+    if (g > kMaxGranularity)
+        return fail(GA_ENOTSUP, "%s: granularity %d above the supported %d", what, g, kMaxGranularity);
+    if (h_table[0] != 0 || h_table[n - 1] != g)
+        return fail(GA_EINVAL, "%s: table must start at 0 and end at g", what);
+    *tab = TableArg{};
+    for (int z = 0; z < n; z++) {
+        if (z > 0 && h_table[z] <= h_table[z - 1])
+            return fail(GA_EINVAL, "%s: table not strictly increasing at %d", what, z);
+        tab->t[z] = (uint16_t)h_table[z];
+    }
+    tab->g = g;
+    tab->n = n;
+    return GA_OK;
+}
+
+}  // namespace
+}  // namespace ga

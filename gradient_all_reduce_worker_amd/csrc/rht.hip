@@ -32,6 +32,7 @@
 
 #include "common.hpp"
 #include "philox.hpp"
+#include "quant.hpp"
 
 namespace ga {
 namespace {
@@ -258,6 +259,131 @@ __global__ __launch_bounds__(kTT) void rht_cross_kernel(PtrTable y, PtrTable out
     }
 }
 
+// ---------------------------------------------------------------- transform and quantize
+
+// THC's RHT variant quantizes the truncated transform (THC page, section 5,
+// then section 3 or 4 on the result). These kernels take the transform's
+// last pass and, instead of writing the binary32 coordinates, round them
+// at once: the same clamp to [m_p, M_p], the same grid (the block is the
+// quantizer's partition), the same Philox counters (coordinate index in the
+// transformed vector, worker, seed) and packing as thc_rht_forward followed
+// by thc_usq_quantize / thc_nuhc_quantize, so the indices are identical;
+// the transformed vector is never written.
+
+// 8 consecutive coordinates from LDS, scaled, clamped and rounded; grid and
+// range per coordinate (a group can span blocks only when d < 8).
+template <int B, bool TABLE>
+__device__ __forceinline__ uint64_t round_group(const float* s, int i0, int n_in, int64_t e, int dbits,
+                                                float c, const float* mM, const Rounder<TABLE>& rd,
+                                                uint32_t wid, uint32_t q0, uint32_t q1) {
+    const uint64_t g = (uint64_t)e >> 3;
+    const Philox4 r = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), wid, 0u, q0, q1);
+    uint32_t z[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        if (i < n_in) {
+            const int64_t blk = (e + i) >> dbits;
+            const float v = clamp_to(s[pad(i0 + i)] * c, mM, blk);
+            z[i] = rd.index(v, grid_of(mM, blk, rd.levels), uniform16(r, i));
+        } else {
+            z[i] = 0u;                               // past the vector's end: index 0
+        }
+    }
+    return pack_group<B>(z);
+}
+
+// Single pass (d <= kTile): tile of n coordinates from e0, every stage in
+// LDS, then groups of 8 rounded and packed (two groups per thread).
+template <ga_dtype DT, int B, bool TABLE>
+__global__ __launch_bounds__(kTT) void rht_tile_quant_kernel(PtrTable x, PtrTable packed, int worker0,
+                                                             int64_t N, int64_t Np, int kbits,
+                                                             uint32_t k0, uint32_t k1, float c,
+                                                             const float* __restrict__ mM,
+                                                             uint32_t q0, uint32_t q1, TableArg tab) {
+    constexpr int L = (1 << B) - 1;
+    __shared__ float s[kLds];
+    __shared__ uint32_t words[4 * (kTile / 128)];
+    __shared__ uint32_t cells[TABLE ? kMaxGranularity : 1];
+    const Rounder<TABLE> rd = make_rounder<TABLE, kTT>(tab, L, cells);
+    const int w = blockIdx.y;
+    const int64_t e0 = (int64_t)blockIdx.x * kTile;
+    const int n = (int)min((int64_t)kTile, Np - e0);
+    const int nx = (int)max((int64_t)0, min((int64_t)kTile, N - e0));
+    sign_blocks(words, e0 >> 7, (n + 127) >> 7, k0, k1);
+    float v[kPer];
+    if (nx == kTile) {
+#pragma unroll
+        for (int k = 0; k < kPer; k++) v[k] = load_tile<true, DT>(x.p[w], e0, threadIdx.x + k * kTT);
+    } else {
+#pragma unroll
+        for (int k = 0; k < kPer; k++) {
+            const int i = threadIdx.x + k * kTT;
+            v[k] = i < nx ? load_tile<true, DT>(x.p[w], e0, i) : 0.0f;
+        }
+    }
+    __syncthreads();                                  // the sign words
+#pragma unroll
+    for (int k = 0; k < kPer; k++) {
+        const int i = threadIdx.x + k * kTT;
+        s[pad(i)] = negated(words, i >> 7, i) ? -v[k] : v[k];
+    }
+    __syncthreads();
+    stages(s, 0, kbits);
+    uint8_t* out = static_cast<uint8_t*>(packed.p[w]);
+    const int64_t nbytes = (Np * B + 7) / 8;
+    const uint32_t wid = (uint32_t)(worker0 + w);
+#pragma unroll
+    for (int k = 0; k < kPer / 8; k++) {
+        const int i0 = 8 * (threadIdx.x + k * kTT);
+        if (i0 >= n) continue;
+        const int n_in = min(8, n - i0);
+        const int64_t e = e0 + i0;
+        const uint64_t bits = round_group<B, TABLE>(s, i0, n_in, e, kbits, c, mM, rd, wid, q0, q1);
+        if (n_in == 8) {
+            store_group<B>(out, e >> 3, bits);
+        } else {
+#pragma unroll
+            for (int q = 0; q < B; q++)
+                if ((e >> 3) * B + q < nbytes) out[(e >> 3) * B + q] = (uint8_t)(bits >> (8 * q));
+        }
+    }
+}
+
+// Second pass (d > kTile): as rht_cross_kernel, then the G x W sub-matrix
+// rounded in groups of 8 consecutive columns of a row (W >= 16).
+template <int B, bool TABLE>
+__global__ __launch_bounds__(kTT) void rht_cross_quant_kernel(PtrTable y, PtrTable packed, int worker0,
+                                                              int dbits, int wbits, float c,
+                                                              const float* __restrict__ mM,
+                                                              uint32_t q0, uint32_t q1, TableArg tab) {
+    constexpr int L = (1 << B) - 1;
+    __shared__ float s[kLds];
+    __shared__ uint32_t cells[TABLE ? kMaxGranularity : 1];
+    const Rounder<TABLE> rd = make_rounder<TABLE, kTT>(tab, L, cells);
+    const int w = blockIdx.y;
+    const int W = 1 << wbits;
+    const int gbits = dbits - kTileBits;
+    const int G = 1 << gbits;
+    const int64_t b = blockIdx.x >> gbits;
+    const int64_t base = (b << dbits) + (int64_t)(blockIdx.x & (G - 1)) * W;
+    const float* yb = static_cast<const float*>(y.p[w]) + base;
+#pragma unroll
+    for (int k = 0; k < kPer; k++) {
+        const int i = threadIdx.x + k * kTT;
+        s[pad(i)] = yb[(i >> wbits) * kTile + (i & (W - 1))];
+    }
+    __syncthreads();
+    stages(s, wbits, kTileBits);
+    uint8_t* out = static_cast<uint8_t*>(packed.p[w]);
+    const uint32_t wid = (uint32_t)(worker0 + w);
+#pragma unroll
+    for (int k = 0; k < kPer / 8; k++) {
+        const int i0 = 8 * (threadIdx.x + k * kTT);
+        const int64_t e = base + (int64_t)(i0 >> wbits) * kTile + (i0 & (W - 1));
+        store_group<B>(out, e >> 3, round_group<B, TABLE>(s, i0, 8, e, dbits, c, mM, rd, wid, q0, q1));
+    }
+}
+
 // ---------------------------------------------------------------- norms and range
 
 // One workgroup per (block, worker): 16 coalesced loads in flight per thread,
@@ -443,5 +569,88 @@ extern "C" ga_status thc_rht_inverse(float* y, int64_t N, int64_t d, uint64_t se
         hipLaunchKernelGGL((rht_cross_kernel<false, GA_F32>), g1, dim3(kTT), 0, hs, ty, to, N, dbits, wbits, k0, k1, c, none);
     else
         hipLaunchKernelGGL((rht_cross_kernel<false, GA_BF16>), g1, dim3(kTT), 0, hs, ty, to, N, dbits, wbits, k0, k1, c, none);
+    return check_launch(what);
+}
+
+extern "C" ga_status thc_rht_quantize(const void* const* bufs, int32_t P, int32_t worker0, int64_t N,
+                                      ga_dtype dt, int64_t d, uint64_t rht_seed, const float* d_mM,
+                                      int32_t b, int32_t g, const int32_t* h_table,
+                                      uint64_t q_seed, float* const* y_scratch,
+                                      uint8_t* const* packed, void* stream) {
+    const char* what = "thc_rht_quantize";
+    if (!valid_dtype(dt)) return fail(GA_EINVAL, "%s: unknown dtype %d", what, (int)dt);
+    const int dbits = log2_block(d);
+    if (dbits < 0) return fail(GA_EINVAL, "%s: d = %lld is not a power of two in [2, 2^22]", what, (long long)d);
+    if (!valid_bits(b)) return fail(GA_EINVAL, "%s: b = %d is not 1, 2, 4 or 8", what, b);
+    if (N < 0 || worker0 < 0) return fail(GA_EINVAL, "%s: negative argument", what);
+    if (P < 1 || P > GA_MAX_WORKERS) return fail(GA_EINVAL, "%s: P = %d outside [1, %d]", what, P, GA_MAX_WORKERS);
+    TableArg tab{};
+    ga_status rc;
+    if (h_table && (rc = load_table(b, g, h_table, &tab, what))) return rc;
+    if (N == 0) return GA_OK;
+    if ((rc = check_workers(bufs, P, elem_size(dt), what))) return rc;
+    if ((rc = check_workers(reinterpret_cast<const void* const*>(packed), P, 16, what))) return rc;
+    if (!d_mM || !aligned(d_mM, 8)) return fail(GA_EINVAL, "%s: bad range pointer", what);
+    const bool two_pass = dbits > kTileBits;
+    if (two_pass) {
+        if (!y_scratch) return fail(GA_EINVAL, "%s: d > %d needs the scratch vectors", what, kTile);
+        if ((rc = check_workers(reinterpret_cast<const void* const*>(y_scratch), P, 4, what))) return rc;
+    }
+    const int64_t Np = ceil_div(N, d) * d;
+    const int64_t tiles = ceil_div(Np, kTile);
+    if (tiles > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: too many tiles", what);
+    PtrTable tx{}, ty{}, tp{};
+    for (int i = 0; i < P; i++) {
+        tx.p[i] = const_cast<void*>(bufs[i]);
+        tp.p[i] = packed[i];
+        if (two_pass) ty.p[i] = y_scratch[i];
+    }
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const uint32_t k0 = (uint32_t)rht_seed, k1 = (uint32_t)(rht_seed >> 32);
+    const uint32_t q0 = (uint32_t)q_seed, q1 = (uint32_t)(q_seed >> 32);
+    const float c = inv_sqrt_d(d);
+    const dim3 g1((unsigned)tiles, (unsigned)P);
+    const bool tb = h_table != nullptr;
+    if (!two_pass) {
+#define GA_TQ(DT, B)                                                                                   \
+        do {                                                                                           \
+            if (tb) hipLaunchKernelGGL((rht_tile_quant_kernel<DT, B, true>), g1, dim3(kTT), 0, hs, tx, tp, \
+                                       worker0, N, Np, dbits, k0, k1, c, d_mM, q0, q1, tab);          \
+            else hipLaunchKernelGGL((rht_tile_quant_kernel<DT, B, false>), g1, dim3(kTT), 0, hs, tx, tp, \
+                                    worker0, N, Np, dbits, k0, k1, c, d_mM, q0, q1, tab);             \
+        } while (0)
+#define GA_TQB(DT)                               \
+        switch (b) {                             \
+            case 1: GA_TQ(DT, 1); break;         \
+            case 2: GA_TQ(DT, 2); break;         \
+            case 4: GA_TQ(DT, 4); break;         \
+            default: GA_TQ(DT, 8); break;        \
+        }
+        if (dt == GA_F32) { GA_TQB(GA_F32) } else { GA_TQB(GA_BF16) }
+#undef GA_TQB
+#undef GA_TQ
+        return check_launch(what);
+    }
+    const float* none = nullptr;
+    if (dt == GA_F32)
+        hipLaunchKernelGGL((rht_tile_kernel<true, false, GA_F32>), g1, dim3(kTT), 0, hs, tx, ty, N, Np, (int)kTileBits, k0, k1, c, none);
+    else
+        hipLaunchKernelGGL((rht_tile_kernel<true, false, GA_BF16>), g1, dim3(kTT), 0, hs, tx, ty, N, Np, (int)kTileBits, k0, k1, c, none);
+    if ((rc = check_launch(what))) return rc;
+    const int wbits = 2 * kTileBits - dbits;
+#define GA_CQ(B)                                                                                        \
+    do {                                                                                                \
+        if (tb) hipLaunchKernelGGL((rht_cross_quant_kernel<B, true>), g1, dim3(kTT), 0, hs, ty, tp, worker0, \
+                                   dbits, wbits, c, d_mM, q0, q1, tab);                                \
+        else hipLaunchKernelGGL((rht_cross_quant_kernel<B, false>), g1, dim3(kTT), 0, hs, ty, tp, worker0, \
+                                dbits, wbits, c, d_mM, q0, q1, tab);                                   \
+    } while (0)
+    switch (b) {
+        case 1: GA_CQ(1); break;
+        case 2: GA_CQ(2); break;
+        case 4: GA_CQ(4); break;
+        default: GA_CQ(8); break;
+    }
+#undef GA_CQ
     return check_launch(what);
 }

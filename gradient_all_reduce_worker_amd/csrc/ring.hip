@@ -349,7 +349,7 @@ __global__ __launch_bounds__(kThreads) void fusion_ring_kernel(const ga_fusion_t
                     int64_t v[1] = {j0 + threadIdx.x};
                     bool ok[1] = {v[0] < j1};
                     const Rot rt = rot_of<DUAL>(first.chunk, P);
-                    if (P <= 8) fold_uniform<DT, 1, 16>(row, P, v, ok, rt, div);
+                    if (P <= 16) fold_uniform<DT, 1, 16>(row, P, v, ok, rt, div);
                     else fold_uniform<DT, 1, 8>(row, P, v, ok, rt, div);
                     continue;
                 }

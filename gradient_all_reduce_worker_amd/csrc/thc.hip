@@ -14,6 +14,7 @@
 
 #include "common.hpp"
 #include "philox.hpp"
+#include "quant.hpp"
 
 namespace ga {
 namespace {
@@ -209,31 +210,6 @@ constexpr int kQGroups = 4;
 constexpr size_t kLdsPerCu = 160 * 1024;      // LDS per CU (residency caps)
 constexpr int64_t kQSpan = (int64_t)kThreads * kQGroups * 8;   // elements per workgroup
 
-struct Grid {                // one partition's grid
-    float m;
-    float s;                 // L / (M - m), or 0 when M == m
-};
-
-__device__ __forceinline__ Grid grid_of(const float* mM, int64_t p, int L) {
-    const float m = mM[2 * p], M = mM[2 * p + 1];
-    const float range = M - m;
-    return {m, range == 0.0f ? 0.0f : (float)L / range};
-}
-
-// Stochastic rounding of one value to its grid index (binary32 throughout;
-// with s = 0 the index is 0).
-__device__ __forceinline__ uint32_t usq_index(float a, Grid g, int L, uint32_t r16) {
-    const float u = (a - g.m) * g.s;
-    const float z0 = fminf(floorf(u), (float)(L - 1));
-    const float f = u - z0;
-    const bool up = (float)(2u * r16 + 1u) < f * 131072.0f;
-    return (uint32_t)z0 + (up ? 1u : 0u);
-}
-
-__device__ __forceinline__ uint32_t uniform16(const Philox4& r, int i) {
-    return (r.v[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-}
-
 template <ga_dtype DT>
 __device__ __forceinline__ void load_group(const void* x, int64_t g, float* a) {
     if (DT == GA_BF16) {
@@ -249,64 +225,6 @@ __device__ __forceinline__ void load_group(const void* x, int64_t g, float* a) {
         a[6] = __uint_as_float(r1.z); a[7] = __uint_as_float(r1.w);
     }
 }
-
-// The 8 b-bit indices of a group, least significant bits first (8 b bits).
-template <int B>
-__device__ __forceinline__ uint64_t pack_group(const uint32_t* z) {
-    uint64_t acc = 0;
-#pragma unroll
-    for (int i = 0; i < 8; i++) acc |= (uint64_t)z[i] << (i * B);
-    return acc;
-}
-
-template <int B>
-__device__ __forceinline__ void store_group(uint8_t* out, int64_t g, uint64_t bits) {
-    if (B == 8) *reinterpret_cast<uint2*>(out + 8 * g) = make_uint2((uint32_t)bits, (uint32_t)(bits >> 32));
-    else if (B == 4) reinterpret_cast<uint32_t*>(out)[g] = (uint32_t)bits;
-    else if (B == 2) reinterpret_cast<uint16_t*>(out)[g] = (uint16_t)bits;
-    else out[g] = (uint8_t)bits;
-}
-
-// Rounding rules. Uniform THC: index k stands for m + k (M - m) / L. Non-
-// uniform THC ("THC" page, section 4, Algorithm 2): index z stands for the
-// table value T[z] on the finer grid m + t (M - m) / g, and a coordinate is
-// rounded stochastically to one of its two neighbouring table values. A
-// per-workgroup LDS map cell[k] = (z0, T[z0], T[z0 + 1]) for every integer
-// cell k in [0, g) gives the neighbours of a position u in [k, k + 1).
-constexpr int kMaxGranularity = 4095;
-
-struct TableArg {
-    uint16_t t[256];   // T[0 .. n-1], 0 = T[0] < ... < T[n-1] = g
-    int g;
-    int n;             // 2^b
-};
-
-template <bool TABLE>
-struct Rounder {
-    int levels;              // L for the uniform grid, g for a table
-    const uint32_t* cell;    // LDS cells (table only)
-    // The index of a; *v receives the grid level it stands for (the index
-    // itself, or its table value).
-    __device__ __forceinline__ uint32_t index_v(float a, Grid gr, uint32_t r16, float* v) const {
-        if (!TABLE) {
-            const uint32_t z = usq_index(a, gr, levels, r16);
-            *v = (float)z;
-            return z;
-        }
-        const float u = (a - gr.m) * gr.s;                      // position on <g+1>
-        const float k = fminf(floorf(u), (float)(levels - 1));
-        const uint32_t c = cell[(int)k];
-        const float lo = (float)((c >> 8) & 0xFFFu), hi = (float)(c >> 20);
-        const float f = (u - lo) / (hi - lo);
-        const bool up = (float)(2u * r16 + 1u) < f * 131072.0f;
-        *v = up ? hi : lo;
-        return (c & 0xFFu) + (up ? 1u : 0u);
-    }
-    __device__ __forceinline__ uint32_t index(float a, Grid gr, uint32_t r16) const {
-        float v;
-        return index_v(a, gr, r16, &v);
-    }
-};
 
 // Error feedback (THC page, section 5): the value a worker's own level v
 // stands for, m + v (M - m) / levels (m when M == m), the same binary32
@@ -340,22 +258,6 @@ __device__ __forceinline__ void store_err_group(float* err, int64_t g, const flo
     float4* q = reinterpret_cast<float4*>(err) + 2 * g;
     q[0] = make_float4(f[0], f[1], f[2], f[3]);
     q[1] = make_float4(f[4], f[5], f[6], f[7]);
-}
-
-// Called by every thread of the workgroup before any early exit.
-template <bool TABLE>
-__device__ __forceinline__ Rounder<TABLE> make_rounder(const TableArg& tab, int L, uint32_t* cells) {
-    if (!TABLE) return {L, nullptr};
-    for (int k = threadIdx.x; k < tab.g; k += kThreads) {
-        int lo = 0, hi = tab.n - 1;             // the largest z with T[z] <= k
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (tab.t[mid] <= k) lo = mid; else hi = mid - 1;
-        }
-        cells[k] = (uint32_t)lo | ((uint32_t)tab.t[lo] << 8) | ((uint32_t)tab.t[lo + 1] << 20);
-    }
-    __syncthreads();
-    return {tab.g, cells};
 }
 
 // Fast kernel: every group of the workgroup is whole, the buffers are
@@ -909,7 +811,6 @@ unsigned blocks_for(int64_t items, int per_thread) {
     return (unsigned)ceil_div(items, (int64_t)kThreads * per_thread);
 }
 
-bool valid_bits(int b) { return b == 1 || b == 2 || b == 4 || b == 8; }
 
 }  // namespace
 }  // namespace ga
@@ -981,28 +882,6 @@ extern "C" ga_status thc_ef_minmax(const void* const* bufs, const float* const* 
 
 namespace ga {
 namespace {
-
-// Host check of a non-uniform table: 0 = T[0] < ... < T[2^b - 1] = g,
-// 2^b - 1 <= g <= kMaxGranularity.
-ga_status load_table(int32_t b, int32_t g, const int32_t* h_table, TableArg* tab, const char* what) {
-    if (!valid_bits(b)) return fail(GA_EINVAL, "%s: b = %d is not 1, 2, 4 or 8", what, b);
-    if (!h_table) return fail(GA_EINVAL, "%s: null table", what);
-    const int n = 1 << b;
-    if (g < n - 1) return fail(GA_EINVAL, "%s: granularity %d < 2^b - 1", what, g);
-    if (g > kMaxGranularity)
-        return fail(GA_ENOTSUP, "%s: granularity %d above the supported %d", what, g, kMaxGranularity);
-    if (h_table[0] != 0 || h_table[n - 1] != g)
-        return fail(GA_EINVAL, "%s: table must start at 0 and end at g", what);
-    *tab = TableArg{};
-    for (int z = 0; z < n; z++) {
-        if (z > 0 && h_table[z] <= h_table[z - 1])
-            return fail(GA_EINVAL, "%s: table not strictly increasing at %d", what, z);
-        tab->t[z] = (uint16_t)h_table[z];
-    }
-    tab->g = g;
-    tab->n = n;
-    return GA_OK;
-}
 
 ga_status quantize_impl(const void* const* bufs, int32_t P, int32_t worker0, int64_t N, ga_dtype dt,
                         int64_t part_elems, const float* d_mM, int32_t b, uint64_t seed,

@@ -157,7 +157,8 @@ class Pipeline:
             self.rht_y, self.rht_sumsq, self.rht_mM, self.rht_avg = {}, {}, {}, {}
             for key, (b, g, d, _) in self.rht.items():
                 Np = ga.rht_padded(self.N, d)
-                self.rht_y[key] = worker_buffers(self.P, Np, torch.float32, dev)
+                # scratch of the transform's first pass (blocks above 8192)
+                self.rht_y[key] = worker_buffers(self.P, Np, torch.float32, dev) if d > 8192 else None
                 self.rht_sumsq[key] = torch.empty((self.P, Np // d), dtype=torch.float64, device=dev)
                 self.rht_mM[key] = torch.empty((Np // d, 2), dtype=torch.float32, device=dev)
                 self.packed[key] = [torch.empty(ga.packed_bytes(Np, b), dtype=torch.uint8,
@@ -221,10 +222,8 @@ class Pipeline:
             _call(timer, f"thc_rht_sumsq_{key}", ga.thc_rht_sumsq, self.flat, d, self.rht_sumsq[key])
             _call(timer, f"thc_rht_range_{key}", ga.thc_rht_range, self.rht_sumsq[key], d, tp,
                   self.rht_mM[key])
-            _call(timer, f"thc_rht_forward_{key}", ga.thc_rht_forward, self.flat, d, w.rht_seed,
-                  self.rht_mM[key], self.rht_y[key])
-            _call(timer, f"thc_nuhc_quantize_{key}", ga.thc_nuhc_quantize, self.rht_y[key],
-                  self.rht_mM[key], b, g, T, w.quant_seed, d, 0, self.packed[key])
+            _call(timer, f"thc_rht_quantize_{key}", ga.thc_rht_quantize, self.flat, d, w.rht_seed,
+                  self.rht_mM[key], b, w.quant_seed, 0, g, T, self.rht_y[key], self.packed[key])
         for b in w.ef_bits:
             k = f"ef{b}"
             _call(timer, f"thc_ef_minmax_{k}", ga.thc_ef_minmax, self.flat, self.err[k], part,
@@ -318,8 +317,7 @@ class Pipeline:
             nblk = Np // d
             out[f"thc_rht_sumsq_{k}"] = P * N * s + 8.0 * P * nblk
             out[f"thc_rht_range_{k}"] = 8.0 * P * nblk + 8.0 * nblk
-            out[f"thc_rht_forward_{k}"] = P * N * s + 4.0 * P * Np
-            out[f"thc_nuhc_quantize_{k}"] = P * Np * (4 + b / 8.0)
+            out[f"thc_rht_quantize_{k}"] = P * N * s + P * Np * b / 8.0
             out[f"thc_nuhc_aggregate_{k}"] = P * Np * b / 8.0 + 4.0 * Np
             out[f"thc_nuhc_dequant_{k}"] = 8.0 * Np
             out[f"thc_rht_inverse_{k}"] = 4.0 * Np + N * s

@@ -12,7 +12,8 @@
  *   thc_nuhc_quantize / thc_nuhc_aggregate / thc_nuhc_dequant
  *                                                  THC with lookup tables
  *   thc_ef_minmax / thc_ef_quantize                error feedback
- *   thc_rht_sumsq / thc_rht_range / thc_rht_forward / thc_rht_inverse
+ *   thc_rht_sumsq / thc_rht_range / thc_rht_forward / thc_rht_inverse /
+ *   thc_rht_quantize
  *                                                  randomized Hadamard
  *                                                  transform, norm-based
  *                                                  range, truncation
@@ -438,8 +439,30 @@ ga_status thc_rht_forward(const void* const* bufs, int32_t P, int64_t N, ga_dtyp
                           uint64_t seed, const float* d_mM, float* const* y, void* stream);
 
 /*
+ * thc_rht_quantize -- the forward transform with truncation followed by
+ * THC's quantizer on the transformed coordinates, in one call ([THC]
+ * section 5 feeding sections 3 and 4: each block of d coordinates is a
+ * partition with its range [m_p, M_p] from d_mM). The packed output is
+ * bit-identical to thc_rht_forward(bufs, ..., rht_seed, d_mM, y) followed
+ * by thc_usq_quantize (h_table NULL; g ignored) or thc_nuhc_quantize
+ * (h_table, g) on y with N' = Np, part_elems = d, worker0 and q_seed; the
+ * transformed vector itself is not kept.
+ *   bufs       P device vectors of N coordinates (fp32 or bf16)
+ *   d_mM       device, Np / d pairs (m_p, M_p) as from thc_rht_range
+ *   y_scratch  needed when d > 8192 (else may be NULL): P device buffers
+ *              of Np binary32, overwritten; must not overlap bufs
+ *   packed     P device buffers of ceil(Np b / 8) bytes, 16-byte aligned
+ * Errors as thc_rht_forward and thc_nuhc_quantize; GA_EINVAL when
+ * d > 8192 and y_scratch is NULL.
+ */
+ga_status thc_rht_quantize(const void* const* bufs, int32_t P, int32_t worker0, int64_t N,
+                           ga_dtype dt, int64_t d, uint64_t rht_seed, const float* d_mM,
+                           int32_t b, int32_t g, const int32_t* h_table, uint64_t q_seed,
+                           float* const* y_scratch, uint8_t* const* packed, void* stream);
+
+/*
  * thc_rht_inverse -- out = RHT^-1(y) for one vector: y holds Np binary32
- * (device; used as scratch and overwritten when d > 4096), out receives the
+ * (device; used as scratch and overwritten when d > 8192), out receives the
  * first N coordinates as fp32 or bf16 (round to nearest even).
  */
 ga_status thc_rht_inverse(float* y, int64_t N, int64_t d, uint64_t seed, void* out,

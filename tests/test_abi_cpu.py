@@ -27,7 +27,7 @@ def _declared():
 def test_header_declarations_are_exported():
     L = nat.load()
     names = _declared()
-    assert len(names) == 23
+    assert len(names) == 24
     assert set(names) == set(nat.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -187,6 +187,34 @@ def test_rht_argument_errors_before_enqueue():
     assert L.thc_rht_inverse(0x60002, 16, 8, 1, 0x70000, 0, None) == EINVAL
     assert b"thc_rht_inverse" in L.ga_last_error()
 
+
+
+def test_rht_quantize_argument_errors_before_enqueue():
+    L = nat.load()
+    good = _ptrs([0x10000 * (i + 1) for i in range(4)])
+    ys = _ptrs([0x100000 * (i + 1) for i in range(4)])
+    T = (C.c_int32 * 4)(0, 1, 3, 4)
+    bad = (C.c_int32 * 4)(0, 3, 3, 4)
+    q = L.thc_rht_quantize
+    ok = dict(P=4, w0=0, N=16, dt=0, d=8, rs=1, mM=0x50000, b=2, g=0, tab=None, qs=2, y=None, pk=good)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return q(good, a["P"], a["w0"], a["N"], a["dt"], a["d"], a["rs"], a["mM"], a["b"], a["g"],
+                 a["tab"], a["qs"], a["y"], a["pk"], None)
+    for d in (0, 1, 3, 6, 1 << 23):
+        assert call(d=d) == EINVAL
+    for b in (0, 3, 5, 16):
+        assert call(b=b) == EINVAL
+    assert call(P=0) == EINVAL and call(P=65) == EINVAL
+    assert call(N=-1) == EINVAL and call(w0=-1) == EINVAL and call(dt=2) == EINVAL
+    assert call(mM=0) == EINVAL and call(mM=0x50004) == EINVAL                 # null, misaligned
+    assert call(pk=_ptrs([0x10000, 0x20008, 0x30000, 0x40000])) == EINVAL      # packed not 16B
+    assert call(d=1 << 14) == EINVAL                                           # two passes, no scratch
+    assert call(d=1 << 14, y=_ptrs([0x100000, 0, 0x300000, 0x400000])) == EINVAL
+    assert call(g=4, tab=bad) == EINVAL and call(g=2, tab=T) == EINVAL
+    assert b"thc_rht_quantize" in L.ga_last_error()
+    assert call(N=0) == 0 and call(N=0, d=1 << 14) == 0                        # empty: nothing to do
 
 def _ftable(sizes):
     h = np.zeros(len(sizes), dtype=nat.FTENSOR_DTYPE)

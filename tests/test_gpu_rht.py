@@ -161,3 +161,69 @@ def test_full_rht_chain_matches_oracle(P, d, N, b):
     mean = np.mean(np.stack(xs), axis=0, dtype=np.float64)
     nm = oracle.nmse(mean.astype(np.float32), outw)[2]
     assert nm < {2: 0.6, 4: 0.05, 8: 0.02}[b]
+
+
+# transform-and-quantize in one call: partial groups of 8 (d < 8, Np not a
+# multiple of 8), one tile, a full tile, two passes, several blocks per tile
+QSHAPES = [(2, 2, 7), (3, 2, 9), (2, 4, 13), (3, 8, 1001), (2, 128, 300), (4, 4096, 3 * 4096 + 5),
+           (2, 8192, 2 * 8192 - 3), (2, 1 << 14, (1 << 14) + 77), (2, 1 << 16, 70000),
+           (2, 1 << 20, (1 << 20) + 999)]
+QMODES = [(1, 0, None), (2, 0, None), (4, 0, None), (8, 0, None),
+          (2, 8, (0, 3, 5, 8)), (4, 36, "center"), (8, 1000, "center")]
+
+
+@pytest.mark.parametrize("dt", [ga.F32, ga.BF16])
+@pytest.mark.parametrize("b,g,table", QMODES)
+@pytest.mark.parametrize("P,d,N", QSHAPES)
+def test_rht_quantize_matches_two_calls_and_oracle(P, d, N, b, g, table, dt):
+    """thc_rht_quantize against thc_rht_forward (with truncation) followed by
+    the quantizer on the transformed vector, and against the oracle's
+    forward -> clamp -> quantize, byte for byte."""
+    bufs = _inputs(P, N, dt, seed=3 * N + d + b)
+    xs = [_host(t) for t in bufs]
+    if table == "center":
+        table = ga.center_table(b, g)
+    t_p = statistics.NormalDist().inv_cdf(1 - 1 / 32)
+    mMw = oracle.rht_range(np.stack([oracle.rht_sumsq(x, d) for x in xs]), d, t_p)
+    mM = torch.from_numpy(mMw).to(DEV)
+    qseed, w0 = 0x5EED_0000_0000_0077 + b, 5
+    Np = ga.rht_padded(N, d)
+    nbytes = ga.packed_bytes(Np, b)
+    fused = ga.thc_rht_quantize(bufs, d, SEED, mM, b, qseed, worker0=w0, g=g, table=table)
+    y = ga.thc_rht_forward(bufs, d, SEED, mM=mM)
+    if table is None:
+        two = ga.thc_usq_quantize(y, mM, b, qseed, part_elems=d, worker0=w0)
+    else:
+        two = ga.thc_nuhc_quantize(y, mM, b, g, table, qseed, part_elems=d, worker0=w0)
+    for i in range(P):
+        got = fused[i].cpu().numpy()[:nbytes]
+        assert np.array_equal(got, two[i].cpu().numpy()[:nbytes]), i
+        yc = oracle.clamp(oracle.rht_forward(xs[i], d, SEED), d, mMw)
+        if table is None:
+            want = oracle.usq_quantize(yc, w0 + i, d, mMw, b, qseed)
+        else:
+            want = oracle.nuhc_quantize(yc, w0 + i, d, mMw, b, g, table, qseed)
+        assert np.array_equal(got, want), i
+
+
+def test_rht_quantize_caller_buffers_and_empty():
+    """Caller-provided scratch and packed buffers (reused across calls), and
+    N = 0 leaves the output untouched."""
+    P, d, N, b = 2, 1 << 15, 3 * (1 << 15) - 100, 4
+    bufs = _inputs(P, N, ga.F32, seed=99)
+    Np = ga.rht_padded(N, d)
+    mMw = oracle.rht_range(np.stack([oracle.rht_sumsq(_host(x), d) for x in bufs]), d, 2.0)
+    mM = torch.from_numpy(mMw).to(DEV)
+    ys = [torch.full((Np,), 7.0, device=DEV) for _ in range(P)]
+    pk = [torch.zeros(ga.packed_bytes(Np, b), dtype=torch.uint8, device=DEV) for _ in range(P)]
+    first = [t.clone() for t in ga.thc_rht_quantize(bufs, d, SEED, mM, b, 11, y_scratch=ys, packed=pk)]
+    again = ga.thc_rht_quantize(bufs, d, SEED, mM, b, 11, y_scratch=ys, packed=pk)
+    for i in range(P):
+        assert torch.equal(first[i], again[i])
+        want = oracle.usq_quantize(oracle.clamp(oracle.rht_forward(_host(bufs[i]), d, SEED), d, mMw),
+                                   i, d, mMw, b, 11)
+        assert np.array_equal(again[i].cpu().numpy(), want)
+    keep = pk[0].clone()
+    ga.thc_rht_quantize([torch.empty(0, device=DEV)], d, SEED, mM, b, 11, packed=[pk[0]])
+    torch.cuda.synchronize()
+    assert torch.equal(pk[0], keep)
