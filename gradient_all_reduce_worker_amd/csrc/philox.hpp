@@ -32,8 +32,9 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
         }
         const uint64_t pa = (uint64_t)kMulA * c0;
         const uint64_t pb = (uint64_t)kMulB * c2;
-        const uint32_t n0 = (uint32_t)(pb >> 32) ^ c1 ^ k0;
-        const uint32_t n2 = (uint32_t)(pa >> 32) ^ c3 ^ k1;
+        // three-input exclusive or in one instruction (truth table 0x96)
+        const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(pb >> 32), c1, k0, 0x96);
+        const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(pa >> 32), c3, k1, 0x96);
         c1 = (uint32_t)pb;
         c3 = (uint32_t)pa;
         c0 = n0;

@@ -22,14 +22,22 @@ __device__ __forceinline__ Grid grid_of(const float* mM, int64_t p, int L) {
     return {m, range == 0.0f ? 0.0f : (float)L / range};
 }
 
-// Stochastic rounding of one value to its grid index (binary32 throughout;
-// with s = 0 the index is 0).
+// Stochastic rounding of one value to its grid index, binary32 throughout
+// (a >= m, so the position u on the grid is >= 0; with s = 0 the index is
+// 0). The rule is: z0 = min(floor(u), L - 1), f = u - z0, go up when
+// 2 r + 1 < f 2^17 for the 16-bit uniform r. Computed here in fewer
+// instructions with the same result for every finite input:
+//  - u is first clamped to L; u >= L gives index L either way (f >= 1 and
+//    every r goes up, or f = 0 at z0 = L and none does), and below L the
+//    clamp changes nothing, so z0 = trunc(u) and f = fract(u) (exact);
+//  - 2 r + 1 < f 2^17  <=>  r < f 2^16 - 1/2, where f 2^16 is exact and so
+//    is the subtraction whenever the right side is >= 0 (otherwise both
+//    sides are false), so one fused multiply-add gives it exactly.
 __device__ __forceinline__ uint32_t usq_index(float a, Grid g, int L, uint32_t r16) {
-    const float u = (a - g.m) * g.s;
-    const float z0 = fminf(floorf(u), (float)(L - 1));
-    const float f = u - z0;
-    const bool up = (float)(2u * r16 + 1u) < f * 131072.0f;
-    return (uint32_t)z0 + (up ? 1u : 0u);
+    const float u = fminf((a - g.m) * g.s, (float)L);
+    const float f = __builtin_amdgcn_fractf(u);
+    const bool up = (float)r16 < __builtin_fmaf(f, 65536.0f, -0.5f);
+    return (uint32_t)u + (up ? 1u : 0u);
 }
 
 __device__ __forceinline__ uint32_t uniform16(const Philox4& r, int i) {
@@ -84,7 +92,7 @@ struct Rounder {
         const uint32_t c = cell[(int)k];
         const float lo = (float)((c >> 8) & 0xFFFu), hi = (float)(c >> 20);
         const float f = (u - lo) / (hi - lo);
-        const bool up = (float)(2u * r16 + 1u) < f * 131072.0f;
+        const bool up = (float)r16 < __builtin_fmaf(f, 65536.0f, -0.5f);   // as in usq_index
         *v = up ? hi : lo;
         return (c & 0xFFu) + (up ? 1u : 0u);
     }

@@ -270,12 +270,41 @@ __global__ __launch_bounds__(kTT) void rht_cross_kernel(PtrTable y, PtrTable out
 // by thc_usq_quantize / thc_nuhc_quantize, so the indices are identical;
 // the transformed vector is never written.
 
-// 8 consecutive coordinates from LDS, scaled, clamped and rounded; grid and
-// range per coordinate (a group can span blocks only when d < 8).
+// Range and grid of one block, read once for the coordinates that share it.
+struct BlockGrid {
+    float m, M;
+    Grid g;
+};
+
+__device__ __forceinline__ BlockGrid block_grid(const float* mM, int64_t p, int levels) {
+    return {mM[2 * p], mM[2 * p + 1], grid_of(mM, p, levels)};
+}
+
+// 8 consecutive coordinates from LDS (index i0 on, coordinate e on),
+// scaled, clamped and rounded on the grid of their block bg.
 template <int B, bool TABLE>
-__device__ __forceinline__ uint64_t round_group(const float* s, int i0, int n_in, int64_t e, int dbits,
-                                                float c, const float* mM, const Rounder<TABLE>& rd,
+__device__ __forceinline__ uint64_t round_group(const float* s, int i0, int64_t e, float c,
+                                                const BlockGrid& bg, const Rounder<TABLE>& rd,
                                                 uint32_t wid, uint32_t q0, uint32_t q1) {
+    const uint64_t g = (uint64_t)e >> 3;
+    const Philox4 r = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), wid, 0u, q0, q1);
+    uint32_t z[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        float v = s[pad(i0 + i)] * c;
+        v = v < bg.m ? bg.m : (v > bg.M ? bg.M : v);
+        z[i] = rd.index(v, bg.g, uniform16(r, i));
+    }
+    return pack_group<B>(z);
+}
+
+// As round_group when the n_in <= 8 coordinates may lie in different
+// blocks (d < 8): range and grid per coordinate; indices past n_in are 0.
+template <int B, bool TABLE>
+__device__ __forceinline__ uint64_t round_group_mixed(const float* s, int i0, int n_in, int64_t e,
+                                                      int dbits, float c, const float* mM,
+                                                      const Rounder<TABLE>& rd, uint32_t wid,
+                                                      uint32_t q0, uint32_t q1) {
     const uint64_t g = (uint64_t)e >> 3;
     const Philox4 r = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), wid, 0u, q0, q1);
     uint32_t z[8];
@@ -338,7 +367,9 @@ __global__ __launch_bounds__(kTT) void rht_tile_quant_kernel(PtrTable x, PtrTabl
         if (i0 >= n) continue;
         const int n_in = min(8, n - i0);
         const int64_t e = e0 + i0;
-        const uint64_t bits = round_group<B, TABLE>(s, i0, n_in, e, kbits, c, mM, rd, wid, q0, q1);
+        const uint64_t bits =
+            kbits >= 3 ? round_group<B, TABLE>(s, i0, e, c, block_grid(mM, e >> kbits, rd.levels), rd, wid, q0, q1)
+                       : round_group_mixed<B, TABLE>(s, i0, n_in, e, kbits, c, mM, rd, wid, q0, q1);
         if (n_in == 8) {
             store_group<B>(out, e >> 3, bits);
         } else {
@@ -376,11 +407,12 @@ __global__ __launch_bounds__(kTT) void rht_cross_quant_kernel(PtrTable y, PtrTab
     stages(s, wbits, kTileBits);
     uint8_t* out = static_cast<uint8_t*>(packed.p[w]);
     const uint32_t wid = (uint32_t)(worker0 + w);
+    const BlockGrid bg = block_grid(mM, b, rd.levels);   // one block per workgroup
 #pragma unroll
     for (int k = 0; k < kPer / 8; k++) {
         const int i0 = 8 * (threadIdx.x + k * kTT);
         const int64_t e = base + (int64_t)(i0 >> wbits) * kTile + (i0 & (W - 1));
-        store_group<B>(out, e >> 3, round_group<B, TABLE>(s, i0, 8, e, dbits, c, mM, rd, wid, q0, q1));
+        store_group<B>(out, e >> 3, round_group<B, TABLE>(s, i0, e, c, bg, rd, wid, q0, q1));
     }
 }
 
