@@ -47,9 +47,15 @@ __device__ __forceinline__ uint32_t uniform16(const Philox4& r, int i) {
 // The 8 b-bit indices of a group, least significant bits first (8 b bits).
 template <int B>
 __device__ __forceinline__ uint64_t pack_group(const uint32_t* z) {
-    uint64_t acc = 0;
+    if (B == 8) {
+        const uint32_t lo = z[0] | (z[1] << 8) | (z[2] << 16) | (z[3] << 24);
+        const uint32_t hi = z[4] | (z[5] << 8) | (z[6] << 16) | (z[7] << 24);
+        return (uint64_t)lo | ((uint64_t)hi << 32);
+    }
+    // one 32-bit shift-and-or per index (Horner order, most significant first)
+    uint32_t acc = z[7];
 #pragma unroll
-    for (int i = 0; i < 8; i++) acc |= (uint64_t)z[i] << (i * B);
+    for (int i = 6; i >= 0; i--) acc = (acc << B) | z[i];
     return acc;
 }
 
@@ -91,8 +97,18 @@ struct Rounder {
         const float k = fminf(floorf(u), (float)(levels - 1));
         const uint32_t c = cell[(int)k];
         const float lo = (float)((c >> 8) & 0xFFFu), hi = (float)(c >> 20);
-        const float f = (u - lo) / (hi - lo);
-        const bool up = (float)r16 < __builtin_fmaf(f, 65536.0f, -0.5f);   // as in usq_index
+        // up <=> r < fl((u - lo) / (hi - lo)) 2^16 - 1/2 (as in usq_index),
+        // with a correctly rounded quotient. u - lo and hi - lo are exact
+        // (integers <= 4095 and u < 2^12). The hardware reciprocal gives the
+        // quotient within 2^-21 relative, i.e. the threshold within 0.04 of
+        // the exact one (|quotient| <= 1 + 2^-10); r is an integer, so when it
+        // lies more than 1/8 from the estimate the decision is already fixed.
+        // Only the rest (about one coordinate in 2.6 10^5) takes the divide.
+        const float num = u - lo, den = hi - lo;
+        const float rf = (float)r16;
+        const float yq = __builtin_fmaf(num * __builtin_amdgcn_rcpf(den), 65536.0f, -0.5f);
+        bool up = rf < yq;
+        if (!(fabsf(rf - yq) > 0.125f)) up = rf < __builtin_fmaf(num / den, 65536.0f, -0.5f);
         *v = up ? hi : lo;
         return (c & 0xFFu) + (up ? 1u : 0u);
     }

@@ -209,6 +209,11 @@ __global__ __launch_bounds__(kThreads) void minmax_kernel(PtrTable bufs, PtrTabl
 constexpr int kQGroups = 4;
 constexpr size_t kLdsPerCu = 160 * 1024;      // LDS per CU (residency caps)
 constexpr int64_t kQSpan = (int64_t)kThreads * kQGroups * 8;   // elements per workgroup
+// The per-group fast kernel (bf16 input) is bound by the rounding
+// arithmetic; eight groups per thread spread its fixed costs (grid, base
+// addresses, counters) over twice as many elements.
+constexpr int kFGroups = 8;
+constexpr int64_t kFSpan = (int64_t)kThreads * kFGroups * 8;
 
 template <ga_dtype DT>
 __device__ __forceinline__ void load_group(const void* x, int64_t g, float* a) {
@@ -280,25 +285,25 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_fast_kernel(PtrTable bu
     float* err = EF ? static_cast<float*>(errs.p[slot]) : nullptr;
     uint8_t* out = static_cast<uint8_t*>(packed.p[slot]);
     const uint32_t wid = (uint32_t)(worker0 + slot);
-    const int64_t e_blk = (int64_t)blockIdx.x * kQSpan;
+    const int64_t e_blk = (int64_t)blockIdx.x * kFSpan;
     const Grid gb = grid_of(mM, e_blk / plen, rd.levels);
-    float a[kQGroups][8];
+    float a[kFGroups][8];
 #pragma unroll
-    for (int j = 0; j < kQGroups; j++)
+    for (int j = 0; j < kFGroups; j++)
         load_group<DT>(x, e_blk / 8 + (int64_t)j * kThreads + threadIdx.x, a[j]);
     if (EF) {
-        float ev[kQGroups][8];
+        float ev[kFGroups][8];
 #pragma unroll
-        for (int j = 0; j < kQGroups; j++)
+        for (int j = 0; j < kFGroups; j++)
             load_err_group(err, e_blk / 8 + (int64_t)j * kThreads + threadIdx.x, ev[j]);
 #pragma unroll
-        for (int j = 0; j < kQGroups; j++)
+        for (int j = 0; j < kFGroups; j++)
 #pragma unroll
             for (int i = 0; i < 8; i++) a[j][i] = a[j][i] + ev[j][i];
     }
     const EfGrid q = EF ? ef_grid_of(mM, e_blk / plen, rd.levels) : EfGrid{};
 #pragma unroll
-    for (int j = 0; j < kQGroups; j++) {
+    for (int j = 0; j < kFGroups; j++) {
         const int64_t g = e_blk / 8 + (int64_t)j * kThreads + threadIdx.x;
         const Philox4 r = philox4x32_10((uint32_t)g, (uint32_t)((uint64_t)g >> 32), wid, 0u, k0, k1);
         uint32_t z[8];
@@ -912,7 +917,7 @@ ga_status quantize_impl(const void* const* bufs, int32_t P, int32_t worker0, int
     if (ceil_div(N, kLSpan) > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: N too large", what);
     // workgroups wholly inside N and inside one partition take a fast kernel:
     // binary32 the lane kernel (2048 elements), bf16 the per-group one
-    const int64_t span = dt == GA_F32 ? kLSpan : kQSpan;
+    const int64_t span = dt == GA_F32 ? kLSpan : kFSpan;
     const int64_t fast = (vec_ok && plen % span == 0) ? N / span : 0;
     const int64_t e_begin = fast * span;
     const int64_t blocks = ceil_div(N - e_begin, kQSpan);       // generic workgroups

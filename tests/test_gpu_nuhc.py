@@ -40,8 +40,10 @@ def _host(t):
 
 @pytest.mark.parametrize("b,g,T", TABLES)
 @pytest.mark.parametrize("dt", [ga.F32, ga.BF16])
+# the last shape holds enough coordinates (4 M) that the rare exact-division
+# branch of the table rounding (about 1 in 2.6e5) is taken many times
 @pytest.mark.parametrize("P,N,part", [(3, 70001, 1000), (4, 8192 * 5 + 100, 8192), (2, 17, 0),
-                                      (8, 1 << 18, 1 << 16)])
+                                      (8, 1 << 18, 1 << 16), (2, 1 << 21, 1 << 20)])
 def test_nuhc_quantize_aggregate_dequant(P, N, part, dt, b, g, T):
     bufs = _inputs(P, N, dt, seed=N + b + g)
     seed = 0x1234_5678_9ABC_DEF0 + g
