@@ -43,6 +43,8 @@ constexpr int kTT = 512;                    // threads per transform workgroup
 constexpr int kPer = kTile / kTT;           // coordinates per thread (16)
 constexpr int kLds = kTile + kTile / 16;    // padded tile, in words
 constexpr int kMaxBits = 22;                // d <= 2^22: G <= 512, W >= 16
+// blocks per chunk of the pipelined two-pass transform-and-quantize
+constexpr int64_t kPipeUnits = 64;
 constexpr int kSignWords = 4 * 512;         // Philox blocks a workgroup may need, x 4
 static_assert(kPer == 16, "one set of 16 coordinates per thread and group");
 constexpr uint32_t kSignDomain = 0x52485400u;
@@ -55,12 +57,13 @@ __device__ __forceinline__ float load_coord(const void* x, int64_t e, int64_t N,
     return static_cast<const float*>(x)[e];
 }
 
-// Stages on index bits lo .. hi-1 of the tile in LDS (WB <= lo < hi <= WB + 4,
+// Stages on index bits LO .. HI-1 of the tile in LDS (WB <= LO < HI <= WB + 4,
 // WB <= kTileBits - 4): thread o takes the 16 coordinates whose index bits
 // WB .. WB+3 vary and whose other bits spell o. With WB fixed at compile
-// time the 16 LDS addresses are one register plus immediate offsets.
-template <int WB>
-__device__ __forceinline__ void group16(float* s, int lo, int hi) {
+// time the 16 LDS addresses are one register plus immediate offsets; with
+// LO and HI fixed too, every butterfly is straight-line code.
+template <int WB, int LO, int HI>
+__device__ __forceinline__ void group16(float* s) {
     const int o = threadIdx.x;
     const int base = ((o >> WB) << (WB + 4)) | (o & ((1 << WB) - 1));
     float* p = s + pad(base);
@@ -71,7 +74,7 @@ __device__ __forceinline__ void group16(float* s, int lo, int hi) {
     for (int r = 0; r < 16; r++) v[r] = p[r * step];
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-        if (WB + q >= lo && WB + q < hi) {
+        if (WB + q >= LO && WB + q < HI) {
             const int h = 1 << q;
 #pragma unroll
             for (int r = 0; r < 16; r++) {
@@ -87,24 +90,49 @@ __device__ __forceinline__ void group16(float* s, int lo, int hi) {
     for (int r = 0; r < 16; r++) p[r * step] = v[r];
 }
 
-// Stages on index bits lo .. hi-1, four at a time, a barrier after each group.
-__device__ __forceinline__ void stages(float* s, int lo, int hi) {
-    for (int b0 = lo; b0 < hi; b0 += 4) {
-        const int wb = b0 < kTileBits - 4 ? b0 : kTileBits - 4;
-        const int h = b0 + 4 < hi ? b0 + 4 : hi;
-        switch (wb) {
-            case 0: group16<0>(s, b0, h); break;
-            case 1: group16<1>(s, b0, h); break;
-            case 2: group16<2>(s, b0, h); break;
-            case 3: group16<3>(s, b0, h); break;
-            case 4: group16<4>(s, b0, h); break;
-            case 5: group16<5>(s, b0, h); break;
-            case 6: group16<6>(s, b0, h); break;
-            case 7: group16<7>(s, b0, h); break;
-            case 8: group16<8>(s, b0, h); break;
-            default: group16<kTileBits - 4>(s, b0, h); break;
-        }
+// Stages on index bits LO .. HI-1, four at a time, a barrier after each group.
+template <int LO, int HI>
+__device__ __forceinline__ void stages_ct(float* s) {
+    if constexpr (LO < HI) {
+        constexpr int WB = LO < kTileBits - 4 ? LO : kTileBits - 4;
+        constexpr int H = LO + 4 < HI ? LO + 4 : HI;
+        group16<WB, LO, H>(s);
         __syncthreads();
+        stages_ct<LO + 4, HI>(s);
+    }
+}
+
+// The two shapes in use: bits 0 .. hi-1 (a tile pass, 1 <= hi <= kTileBits)
+// and bits lo .. kTileBits-1 (a cross pass, 4 <= lo < kTileBits).
+__device__ __forceinline__ void stages(float* s, int lo, int hi) {
+    if (lo == 0) {
+        switch (hi) {
+            case 1: stages_ct<0, 1>(s); break;
+            case 2: stages_ct<0, 2>(s); break;
+            case 3: stages_ct<0, 3>(s); break;
+            case 4: stages_ct<0, 4>(s); break;
+            case 5: stages_ct<0, 5>(s); break;
+            case 6: stages_ct<0, 6>(s); break;
+            case 7: stages_ct<0, 7>(s); break;
+            case 8: stages_ct<0, 8>(s); break;
+            case 9: stages_ct<0, 9>(s); break;
+            case 10: stages_ct<0, 10>(s); break;
+            case 11: stages_ct<0, 11>(s); break;
+            case 12: stages_ct<0, 12>(s); break;
+            default: stages_ct<0, kTileBits>(s); break;
+        }
+        return;
+    }
+    switch (lo) {
+        case 4: stages_ct<4, kTileBits>(s); break;
+        case 5: stages_ct<5, kTileBits>(s); break;
+        case 6: stages_ct<6, kTileBits>(s); break;
+        case 7: stages_ct<7, kTileBits>(s); break;
+        case 8: stages_ct<8, kTileBits>(s); break;
+        case 9: stages_ct<9, kTileBits>(s); break;
+        case 10: stages_ct<10, kTileBits>(s); break;
+        case 11: stages_ct<11, kTileBits>(s); break;
+        default: stages_ct<12, kTileBits>(s); break;
     }
 }
 
@@ -380,24 +408,65 @@ __global__ __launch_bounds__(kTT) void rht_tile_quant_kernel(PtrTable x, PtrTabl
     }
 }
 
-// Second pass (d > kTile): as rht_cross_kernel, then the G x W sub-matrix
-// rounded in groups of 8 consecutive columns of a row (W >= 16).
-template <int B, bool TABLE>
-__global__ __launch_bounds__(kTT) void rht_cross_quant_kernel(PtrTable y, PtrTable packed, int worker0,
-                                                              int dbits, int wbits, float c,
-                                                              const float* __restrict__ mM,
-                                                              uint32_t q0, uint32_t q1, TableArg tab) {
-    constexpr int L = (1 << B) - 1;
+// First pass of the forward transform for one tile (d > kTile): signs on
+// load, stages 0 .. kTileBits-1, the unscaled partial transform stored to
+// y (as rht_tile_kernel<true, false>).
+template <ga_dtype DT>
+__device__ __forceinline__ void forward_tile_body(float* s, uint32_t* words, const void* x, float* y,
+                                                  int64_t tile, int64_t N, uint32_t k0, uint32_t k1) {
+    const int64_t e0 = tile * kTile;
+    const int nx = (int)max((int64_t)0, min((int64_t)kTile, N - e0));
+    sign_blocks(words, e0 >> 7, kTile >> 7, k0, k1);
+    float v[kPer];
+    if (nx == kTile) {
+#pragma unroll
+        for (int k = 0; k < kPer; k++) v[k] = load_tile<true, DT>(x, e0, threadIdx.x + k * kTT);
+    } else {
+#pragma unroll
+        for (int k = 0; k < kPer; k++) {
+            const int i = threadIdx.x + k * kTT;
+            v[k] = i < nx ? load_tile<true, DT>(x, e0, i) : 0.0f;
+        }
+    }
+    __syncthreads();                                  // the sign words
+#pragma unroll
+    for (int k = 0; k < kPer; k++) {
+        const int i = threadIdx.x + k * kTT;
+        s[pad(i)] = negated(words, i >> 7, i) ? -v[k] : v[k];
+    }
+    __syncthreads();
+    stages_ct<0, kTileBits - 1>(s);
+    // the last stage (index bit kTileBits-1) on the way out: coordinates i
+    // and i + kTile/2 of one butterfly are both this thread's
+#pragma unroll
+    for (int k = 0; k < kPer / 2; k++) {
+        const int i = threadIdx.x + k * kTT;
+        const float a = s[pad(i)], b = s[pad(i + kTile / 2)];
+        (y + e0)[i] = a + b;
+        (y + e0)[i + kTile / 2] = a - b;
+    }
+}
+
+template <ga_dtype DT>
+__global__ __launch_bounds__(kTT) void rht_forward_tile_kernel(PtrTable x, PtrTable y, int64_t N,
+                                                               uint32_t k0, uint32_t k1) {
     __shared__ float s[kLds];
-    __shared__ uint32_t cells[TABLE ? kMaxGranularity : 1];
-    const Rounder<TABLE> rd = make_rounder<TABLE, kTT>(tab, L, cells);
+    __shared__ uint32_t words[4 * (kTile / 128)];
     const int w = blockIdx.y;
+    forward_tile_body<DT>(s, words, x.p[w], static_cast<float*>(y.p[w]), blockIdx.x, N, k0, k1);
+}
+
+// Second pass (d > kTile): as rht_cross_kernel on rows j = 0 .. G-1 of
+// block b, columns cg W .. cg W + W - 1, then the G x W sub-matrix rounded
+// in groups of 8 consecutive columns of a row (W >= 16).
+template <int B, bool TABLE>
+__device__ __forceinline__ void cross_quant_body(float* s, const Rounder<TABLE>& rd, const float* y,
+                                                 uint8_t* out, uint32_t wid, int64_t b, int cg,
+                                                 int dbits, int wbits, float c, const float* mM,
+                                                 uint32_t q0, uint32_t q1) {
     const int W = 1 << wbits;
-    const int gbits = dbits - kTileBits;
-    const int G = 1 << gbits;
-    const int64_t b = blockIdx.x >> gbits;
-    const int64_t base = (b << dbits) + (int64_t)(blockIdx.x & (G - 1)) * W;
-    const float* yb = static_cast<const float*>(y.p[w]) + base;
+    const int64_t base = (b << dbits) + (int64_t)cg * W;
+    const float* yb = y + base;
 #pragma unroll
     for (int k = 0; k < kPer; k++) {
         const int i = threadIdx.x + k * kTT;
@@ -405,14 +474,58 @@ __global__ __launch_bounds__(kTT) void rht_cross_quant_kernel(PtrTable y, PtrTab
     }
     __syncthreads();
     stages(s, wbits, kTileBits);
-    uint8_t* out = static_cast<uint8_t*>(packed.p[w]);
-    const uint32_t wid = (uint32_t)(worker0 + w);
     const BlockGrid bg = block_grid(mM, b, rd.levels);   // one block per workgroup
 #pragma unroll
     for (int k = 0; k < kPer / 8; k++) {
         const int i0 = 8 * (threadIdx.x + k * kTT);
         const int64_t e = base + (int64_t)(i0 >> wbits) * kTile + (i0 & (W - 1));
         store_group<B>(out, e >> 3, round_group<B, TABLE>(s, i0, e, c, bg, rd, wid, q0, q1));
+    }
+}
+
+// Both passes of blocks above kTile, software-pipelined over launches: the
+// blocks (units u = worker * nblk + block) are cut into consecutive chunks,
+// and one launch runs the first pass of chunk k (units a0 .. a0+na-1) next
+// to the second pass of chunk k - 1 (units b0 .. b0+nb-1), whose first pass
+// the previous launch finished. The two roles touch disjoint parts of y.
+// The first pass is bound by HBM and the second by the rounding arithmetic,
+// so sharing the CUs overlaps them. Each unit has G = d / kTile
+// workgroups per role; workgroups alternate roles while both have work.
+template <ga_dtype DT, int B, bool TABLE>
+__global__ __launch_bounds__(kTT) void rht_quant_pipe_kernel(PtrTable x, PtrTable y, PtrTable packed,
+                                                             int worker0, int64_t N, int dbits,
+                                                             int64_t nblk, int64_t a0, int64_t na,
+                                                             int64_t b0, int64_t nb, uint32_t k0,
+                                                             uint32_t k1, float c,
+                                                             const float* __restrict__ mM,
+                                                             uint32_t q0, uint32_t q1, TableArg tab) {
+    constexpr int L = (1 << B) - 1;
+    constexpr int kAux = TABLE ? kMaxGranularity : 4 * (kTile / 128);
+    __shared__ float s[kLds];
+    __shared__ uint32_t aux[kAux];                   // sign words (first pass) or table cells
+    const int gbits = dbits - kTileBits;
+    const int64_t nA = na << gbits, nB = nb << gbits;
+    const int64_t i = blockIdx.x, both = 2 * min(nA, nB);
+    bool first;
+    int64_t j;
+    if (i < both) {
+        first = (i & 1) == 0;
+        j = i >> 1;
+    } else {
+        first = nA > nB;
+        j = i - both + min(nA, nB);
+    }
+    const int64_t unit = (first ? a0 : b0) + (j >> gbits);
+    const int w = (int)(unit / nblk);
+    const int64_t b = unit - (int64_t)w * nblk;
+    const int r = (int)(j & ((1 << gbits) - 1));
+    if (first) {
+        forward_tile_body<DT>(s, aux, x.p[w], static_cast<float*>(y.p[w]), (b << gbits) + r, N, k0, k1);
+    } else {
+        const Rounder<TABLE> rd = make_rounder<TABLE, kTT>(tab, L, aux);
+        cross_quant_body<B, TABLE>(s, rd, static_cast<const float*>(y.p[w]),
+                                   static_cast<uint8_t*>(packed.p[w]), (uint32_t)(worker0 + w), b, r,
+                                   dbits, 2 * kTileBits - dbits, c, mM, q0, q1);
     }
 }
 
@@ -556,9 +669,9 @@ extern "C" ga_status thc_rht_forward(const void* const* bufs, int32_t P, int64_t
         return check_launch(what);
     }
     if (dt == GA_F32)
-        hipLaunchKernelGGL((rht_tile_kernel<true, false, GA_F32>), g1, dim3(kTT), 0, hs, tx, ty, N, Np, kbits, k0, k1, c, d_mM);
+        hipLaunchKernelGGL((rht_forward_tile_kernel<GA_F32>), g1, dim3(kTT), 0, hs, tx, ty, N, k0, k1);
     else
-        hipLaunchKernelGGL((rht_tile_kernel<true, false, GA_BF16>), g1, dim3(kTT), 0, hs, tx, ty, N, Np, kbits, k0, k1, c, d_mM);
+        hipLaunchKernelGGL((rht_forward_tile_kernel<GA_BF16>), g1, dim3(kTT), 0, hs, tx, ty, N, k0, k1);
     if ((rc = check_launch(what))) return rc;
     const int wbits = 2 * kTileBits - dbits;         // W = kTile / G
     hipLaunchKernelGGL((rht_cross_kernel<true, GA_F32>), g1, dim3(kTT), 0, hs, ty, ty, Np, dbits, wbits, k0, k1, c, d_mM);
@@ -663,26 +776,36 @@ extern "C" ga_status thc_rht_quantize(const void* const* bufs, int32_t P, int32_
 #undef GA_TQ
         return check_launch(what);
     }
-    const float* none = nullptr;
-    if (dt == GA_F32)
-        hipLaunchKernelGGL((rht_tile_kernel<true, false, GA_F32>), g1, dim3(kTT), 0, hs, tx, ty, N, Np, (int)kTileBits, k0, k1, c, none);
-    else
-        hipLaunchKernelGGL((rht_tile_kernel<true, false, GA_BF16>), g1, dim3(kTT), 0, hs, tx, ty, N, Np, (int)kTileBits, k0, k1, c, none);
-    if ((rc = check_launch(what))) return rc;
-    const int wbits = 2 * kTileBits - dbits;
-#define GA_CQ(B)                                                                                        \
-    do {                                                                                                \
-        if (tb) hipLaunchKernelGGL((rht_cross_quant_kernel<B, true>), g1, dim3(kTT), 0, hs, ty, tp, worker0, \
-                                   dbits, wbits, c, d_mM, q0, q1, tab);                                \
-        else hipLaunchKernelGGL((rht_cross_quant_kernel<B, false>), g1, dim3(kTT), 0, hs, ty, tp, worker0, \
-                                dbits, wbits, c, d_mM, q0, q1, tab);                                   \
-    } while (0)
-    switch (b) {
-        case 1: GA_CQ(1); break;
-        case 2: GA_CQ(2); break;
-        case 4: GA_CQ(4); break;
-        default: GA_CQ(8); break;
+    // chunks of kPipeUnits blocks: launch k runs the first pass of chunk k
+    // and the second of chunk k - 1
+    const int64_t nblk = Np / d, units = (int64_t)P * nblk;
+    const int64_t U = min(units, kPipeUnits);
+    const int64_t nchunk = ceil_div(units, U);
+    if ((units << (dbits - kTileBits)) > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: too many tiles", what);
+    for (int64_t k = 0; k <= nchunk; k++) {
+        const int64_t a0 = k * U, na = k < nchunk ? min(U, units - a0) : 0;
+        const int64_t b0 = (k - 1) * U, nb = k > 0 ? min(U, units - b0) : 0;
+        const dim3 grid((unsigned)((na + nb) << (dbits - kTileBits)));
+#define GA_PQ(DT, B)                                                                                    \
+        do {                                                                                            \
+            if (tb) hipLaunchKernelGGL((rht_quant_pipe_kernel<DT, B, true>), grid, dim3(kTT), 0, hs, tx, \
+                                       ty, tp, worker0, N, dbits, nblk, a0, na, b0, nb, k0, k1, c, d_mM, \
+                                       q0, q1, tab);                                                    \
+            else hipLaunchKernelGGL((rht_quant_pipe_kernel<DT, B, false>), grid, dim3(kTT), 0, hs, tx,  \
+                                    ty, tp, worker0, N, dbits, nblk, a0, na, b0, nb, k0, k1, c, d_mM,   \
+                                    q0, q1, tab);                                                       \
+        } while (0)
+#define GA_PQB(DT)                               \
+        switch (b) {                             \
+            case 1: GA_PQ(DT, 1); break;         \
+            case 2: GA_PQ(DT, 2); break;         \
+            case 4: GA_PQ(DT, 4); break;         \
+            default: GA_PQ(DT, 8); break;        \
+        }
+        if (dt == GA_F32) { GA_PQB(GA_F32) } else { GA_PQB(GA_BF16) }
+#undef GA_PQB
+#undef GA_PQ
+        if ((rc = check_launch(what))) return rc;
     }
-#undef GA_CQ
-    return check_launch(what);
+    return GA_OK;
 }

@@ -164,10 +164,12 @@ def test_full_rht_chain_matches_oracle(P, d, N, b):
 
 
 # transform-and-quantize in one call: partial groups of 8 (d < 8, Np not a
-# multiple of 8), one tile, a full tile, two passes, several blocks per tile
+# multiple of 8), one tile, a full tile, two passes, several blocks per tile,
+# and more blocks (P x Np / d = 90) than one chunk of the pipelined two-pass
+# schedule holds (64), so its launches mix both passes
 QSHAPES = [(2, 2, 7), (3, 2, 9), (2, 4, 13), (3, 8, 1001), (2, 128, 300), (4, 4096, 3 * 4096 + 5),
            (2, 8192, 2 * 8192 - 3), (2, 1 << 14, (1 << 14) + 77), (2, 1 << 16, 70000),
-           (2, 1 << 20, (1 << 20) + 999)]
+           (2, 1 << 20, (1 << 20) + 999), (3, 1 << 14, 30 * (1 << 14) - 5)]
 QMODES = [(1, 0, None), (2, 0, None), (4, 0, None), (8, 0, None),
           (2, 8, (0, 3, 5, 8)), (4, 36, "center"), (8, 1000, "center")]
 
