@@ -116,14 +116,15 @@ def cmd_pmc(a):
 
 
 def cmd_pmc_table(a):
-    """Markdown table: per kernel, scaled fetch/write bytes per launch against
-    the algorithmic bytes given as NAME=REGEX=BYTES triples."""
+    """Markdown table: per kernel, scaled fetch/write bytes per call against
+    the algorithmic bytes given as NAME=REGEX=BYTES[=LAUNCHES] (LAUNCHES: a
+    call that runs as several launches of the kernel; default 1)."""
     fetch = _per_kernel(a.fetch, "FETCH_SIZE")
     write = _per_kernel(a.write, "WRITE_SIZE")
     pre = re.compile(a.probe)
     pf = max(x for k, v in fetch.items() if pre.search(k) for x in v)
     pw = max(x for k, v in write.items() if pre.search(k) for x in v)
-    print(f"# HBM traffic per launch from rocprofv3 PMC counters: {a.title}\n")
+    print(f"# HBM traffic per call from rocprofv3 PMC counters: {a.title}\n")
     print("FETCH_SIZE and WRITE_SIZE were collected in two separate runs and scaled by what")
     print(f"each reads for a plain copy of {a.probe_bytes:.0f} bytes each way (`{a.probe}`:")
     print(f"FETCH_SIZE {pf:.2f}, WRITE_SIZE {pw:.2f}).\n")
@@ -131,12 +132,14 @@ def cmd_pmc_table(a):
     print("| kernel | launches | read GB | written GB | algorithmic GB | traffic / algorithmic |")
     print("|---|---:|---:|---:|---:|---:|")
     for spec in a.kernels:
-        name, rx, alg = spec.split("=")
+        parts = spec.split("=")
+        name, rx, alg = parts[:3]
+        per_call = int(parts[3]) if len(parts) > 3 else 1
         r = re.compile(rx)
         kf = [x for k, v in fetch.items() if r.search(k) for x in v]
         kw = [x for k, v in write.items() if r.search(k) for x in v]
-        fb = statistics.mean(kf) * a.probe_bytes / pf
-        wb = statistics.mean(kw) * a.probe_bytes / pw
+        fb = statistics.mean(kf) * a.probe_bytes / pf * per_call
+        wb = statistics.mean(kw) * a.probe_bytes / pw * per_call
         print(f"| `{name}` | {len(kf)} | {fb / 1e9:.3f} | {wb / 1e9:.3f} | {float(alg) / 1e9:.3f} | "
               f"{(fb + wb) / float(alg):.4f} |")
 
