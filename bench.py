@@ -36,7 +36,8 @@ DESCRIPTIONS = {
     "small": "4 workers x 1,048,576 fp32 N(0,0.01^2); ring avg + THC USQ b=4",
     "fusion": "8 workers x 200 fp32 tensors (log-uniform 1K..256K); 64 MiB fusion, ring avg",
     "resnet101": "16 workers x ResNet-101 gradients (314 tensors, 44,549,160 fp32); fusion + ring avg",
-    "vgg16": ("32 workers x VGG-16 gradients (138,357,544 fp32); THC USQ b=4,8, table THC "
+    "vgg16": ("32 workers x VGG-16 gradients (138,357,544 fp32); THC USQ b=4,8 (2^20-element "
+              "partition grids), USQ b=4 on one grid for the whole vector, table THC "
               "b=4 g=36, RHT (d=2^20, p=1/32) + table THC b=4 g=36 + inverse, USQ b=4 with error "
               "feedback, b=4 partial aggregation without 3 stragglers; ring avg; NMSE"),
     "shard": ("8 workers x 2,147,483,648 bf16 Laplace(0,1e-3); ring avg with fp32 accumulation "
@@ -86,6 +87,11 @@ def cpu_baseline(pipe, samples, budget_s: float):
         mM = oracle.minmax(xs, n)
         packed = {b: [oracle.usq_quantize(xs[i], i, n, mM, b, w.quant_seed, e_offset=lo)
                       for i in range(P)] for b in w.thc_bits}
+        if w.global_bits:                               # the sample's extremes stand in for the
+            mg = oracle.minmax(xs, 0)                   # whole vector's (same work per element)
+        for b in w.global_bits:
+            packed[f"g{b}"] = [oracle.usq_quantize(xs[i], i, 0, mg, b, w.quant_seed, e_offset=lo)
+                               for i in range(P)]
         for k, (b, g, T) in pipe.nu_tables.items():
             packed[k] = [oracle.nuhc_quantize(xs[i], i, n, mM, b, g, T, w.quant_seed, e_offset=lo)
                          for i in range(P)]
@@ -108,6 +114,9 @@ def cpu_baseline(pipe, samples, budget_s: float):
             S = oracle.int_aggregate(packed[b], n, b)
             xh = oracle.dequant(S, P, b, n, mM, w.dtype)
             oracle.nmse(xs[0], xh)
+        for b in w.global_bits:
+            S = oracle.int_aggregate(packed[f"g{b}"], n, b)
+            oracle.nmse(xs[0], oracle.dequant(S, P, b, 0, mg, w.dtype))
         for k, (b, g, T) in pipe.nu_tables.items():
             Y = oracle.nuhc_aggregate(packed[k], n, b, g, T)
             oracle.nmse(xs[0], oracle.nuhc_dequant(Y, P, g, n, mM, w.dtype))

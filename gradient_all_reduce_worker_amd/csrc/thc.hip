@@ -686,7 +686,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const int32_t* __rest
                                                            int L, int pow2, float pf, float recip,
                                                            void* out, int vec_ok) {
     const int64_t e_blk = (int64_t)blockIdx.x * kDSpan;
-    const bool uniform = plen % kDSpan == 0;
+    const bool uniform = plen % kDSpan == 0 || plen >= N;    // one grid per workgroup
     float m0 = 0.0f, range0 = 0.0f, delta0 = 0.0f;
     if (uniform) {
         const int64_t p = e_blk / plen;
@@ -918,7 +918,7 @@ ga_status quantize_impl(const void* const* bufs, int32_t P, int32_t worker0, int
     // workgroups wholly inside N and inside one partition take a fast kernel:
     // binary32 the lane kernel (2048 elements), bf16 the per-group one
     const int64_t span = dt == GA_F32 ? kLSpan : kFSpan;
-    const int64_t fast = (vec_ok && plen % span == 0) ? N / span : 0;
+    const int64_t fast = (vec_ok && (plen % span == 0 || plen >= N)) ? N / span : 0;
     const int64_t e_begin = fast * span;
     const int64_t blocks = ceil_div(N - e_begin, kQSpan);       // generic workgroups
     // the lane kernel streams best with at most six workgroups per CU; with

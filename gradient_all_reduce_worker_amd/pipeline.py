@@ -142,6 +142,15 @@ class Pipeline:
             self.S = {b: torch.empty(self.N, dtype=torch.int32, device=dev) for b in w.thc_bits}
             self.xhat = {b: torch.empty(self.N, dtype=self.tdt, device=dev) for b in w.thc_bits}
             self.nmse = {b: torch.empty(3, dtype=torch.float64, device=dev) for b in w.thc_bits}
+            # uniform passes with one grid over the whole vector, keyed "g{b}"
+            self.mM_g = torch.empty((1, 2), dtype=torch.float32, device=dev)
+            for b in w.global_bits:
+                k = f"g{b}"
+                self.packed[k] = [torch.empty(ga.packed_bytes(self.N, b), dtype=torch.uint8,
+                                              device=dev) for _ in range(self.P)]
+                self.S[k] = torch.empty(self.N, dtype=torch.int32, device=dev)
+                self.xhat[k] = torch.empty(self.N, dtype=self.tdt, device=dev)
+                self.nmse[k] = torch.empty(3, dtype=torch.float64, device=dev)
             # non-uniform THC passes, keyed "nu{b}g{g}", with a centre-dense table
             self.nu_tables = {f"nu{b}g{g}": (b, g, ga.center_table(b, g)) for b, g in w.nuhc}
             for k, (b, g, _) in self.nu_tables.items():
@@ -214,6 +223,11 @@ class Pipeline:
         for b in w.thc_bits:
             _call(timer, f"thc_usq_quantize_b{b}", ga.thc_usq_quantize, self.flat, self.mM, b,
                   w.quant_seed, part, 0, self.packed[b])
+        if w.global_bits:
+            _call(timer, "thc_minmax_global", ga.thc_minmax, self.flat, 0, self.mM_g)
+        for b in w.global_bits:
+            _call(timer, f"thc_usq_quantize_g{b}", ga.thc_usq_quantize, self.flat, self.mM_g, b,
+                  w.quant_seed, 0, 0, self.packed[f"g{b}"])
         for k, (b, g, T) in self.nu_tables.items():
             _call(timer, f"thc_nuhc_quantize_{k}", ga.thc_nuhc_quantize, self.flat, self.mM, b, g, T,
                   w.quant_seed, part, 0, self.packed[k])
@@ -273,6 +287,14 @@ class Pipeline:
                   part, self.tdt, self.xhat[b])
             _call(timer, f"thc_nmse_b{b}", ga.thc_nmse, self.flat[0], self.xhat[b], self.nmse[b],
                   self.ws)
+        for b in w.global_bits:
+            k = f"g{b}"
+            _call(timer, f"thc_int_aggregate_{k}", ga.thc_int_aggregate, self.packed[k], self.N, b,
+                  self.S[k])
+            _call(timer, f"thc_dequant_{k}", ga.thc_dequant, self.S[k], self.N, self.P, b, self.mM_g,
+                  0, self.tdt, self.xhat[k])
+            _call(timer, f"thc_nmse_{k}", ga.thc_nmse, self.flat[0], self.xhat[k], self.nmse[k],
+                  self.ws)
 
     # ------------------------------------------------------------ accounting
     def stage_bytes(self) -> Dict[str, float]:
@@ -294,6 +316,14 @@ class Pipeline:
             out[f"thc_int_aggregate_b{b}"] = P * N * b / 8.0 + 4.0 * N
             out[f"thc_dequant_b{b}"] = 4.0 * N + N * s
             out[f"thc_nmse_b{b}"] = 2.0 * N * s
+        if w.global_bits:
+            out["thc_minmax_global"] = P * N * s
+        for b in w.global_bits:
+            k = f"g{b}"
+            out[f"thc_usq_quantize_{k}"] = P * N * (s + b / 8.0)
+            out[f"thc_int_aggregate_{k}"] = P * N * b / 8.0 + 4.0 * N
+            out[f"thc_dequant_{k}"] = 4.0 * N + N * s
+            out[f"thc_nmse_{k}"] = 2.0 * N * s
         for k, (b, g, _) in self.nu_tables.items():
             out[f"thc_nuhc_quantize_{k}"] = P * N * (s + b / 8.0)
             out[f"thc_nuhc_aggregate_{k}"] = P * N * b / 8.0 + 4.0 * N
@@ -350,6 +380,14 @@ class Pipeline:
                                   for i in range(self.P)]
                 d["xhat"][b] = synth.to_numpy_bits(self.xhat[b][lo:hi])
                 d["S"][b] = self.S[b][lo:hi].cpu().numpy().copy()
+            d["mM_g"] = self.mM_g[0].cpu().numpy().copy()
+            for b in self.w.global_bits:
+                k = f"g{b}"
+                bl, bh = lo * b // 8, (hi * b + 7) // 8
+                d["packed"][k] = [self.packed[k][i][bl:bh].cpu().numpy().copy()
+                                  for i in range(self.P)]
+                d["xhat"][k] = synth.to_numpy_bits(self.xhat[k][lo:hi])
+                d["S"][k] = self.S[k][lo:hi].cpu().numpy().copy()
             for k, (b, g, _) in self.nu_tables.items():
                 bl, bh = lo * b // 8, (hi * b + 7) // 8
                 d["packed"][k] = [self.packed[k][i][bl:bh].cpu().numpy().copy()

@@ -115,6 +115,7 @@ class Workload:
     part_elems: int = 0             # 0: one partition per fused buffer / vector
     ring_part_elems: int = 0
     thc_bits: Tuple[int, ...] = ()
+    global_bits: Tuple[int, ...] = ()   # uniform THC passes with one grid for the whole vector
     nuhc: Tuple[Tuple[int, int], ...] = ()   # (b, g) of non-uniform THC passes
     # (b, g, log2 d) of THC passes behind the randomized Hadamard transform;
     # a fraction rht_p of the transformed coordinates is expected to be cut
@@ -170,7 +171,8 @@ def workload(name: str) -> Workload:
         names, sizes = _rev(vgg16_shapes())
         return Workload("vgg16", 3, P=32, dtype=F32, sizes=sizes, names=names,
                         dist="normal_logsigma", part_elems=1 << 20, ring_part_elems=1 << 20,
-                        thc_bits=(4, 8), nuhc=((4, 36),), rht=((4, 36, 20),), ef_bits=(4,),
+                        thc_bits=(4, 8), global_bits=(4,), nuhc=((4, 36),), rht=((4, 36, 20),),
+                        ef_bits=(4,),
                         stragglers=3, fused=False)
     if name == "shard":
         return Workload("shard", 4, P=8, dtype=BF16, sizes=[1 << 31], names=["shard"],

@@ -59,6 +59,13 @@ def _check_partition(w, P, lo, xs, got, nu_tables=None, arrived=None):
                      for i in range(P)]
         for i in range(P):
             assert np.array_equal(got["packed"][b][i], packed[b][i]), (b, i)
+    mMg = got["mM_g"][None, :]      # the whole vector's grid, checked by the caller
+    for b in w.global_bits:
+        k = f"g{b}"
+        packed[k] = [oracle.usq_quantize(xs[i], i, 0, mMg, b, w.quant_seed, e_offset=lo)
+                     for i in range(P)]
+        for i in range(P):
+            assert np.array_equal(got["packed"][k][i], packed[k][i]), (k, i)
     for k, (b, g, T) in (nu_tables or {}).items():
         packed[k] = [oracle.nuhc_quantize(xs[i], i, n, mM, b, g, T, w.quant_seed, e_offset=lo)
                      for i in range(P)]
@@ -72,6 +79,11 @@ def _check_partition(w, P, lo, xs, got, nu_tables=None, arrived=None):
         assert np.array_equal(got["S"][b], S)
         xh = oracle.dequant(S, P, b, n, mM, w.dtype)
         assert np.array_equal(_u(got["xhat"][b]), _u(xh))
+    for b in w.global_bits:
+        k = f"g{b}"
+        S = oracle.int_aggregate(packed[k], n, b)
+        assert np.array_equal(got["S"][k], S), k
+        assert np.array_equal(_u(got["xhat"][k]), _u(oracle.dequant(S, P, b, 0, mMg, w.dtype))), k
     if arrived is not None and len(arrived) < P and w.thc_bits:
         b = w.thc_bits[0]
         k = f"part{b}"
@@ -132,6 +144,12 @@ def test_flat_workload_sampled(name):
     torch.cuda.synchronize()
     after = pipe.sample_outputs(which)
     plen = pipe.w.part_elems
+    if pipe.w.global_bits:
+        # the whole vector's grid is the extreme of the partitions' grids
+        # (each sampled one is checked against the oracle below)
+        mM = pipe.mM.cpu().numpy()
+        g = pipe.mM_g.cpu().numpy()[0]
+        assert g[0] == mM[:, 0].min() and g[1] == mM[:, 1].max()
     for p in which:
         _check_partition(pipe.w, pipe.P, p * plen, before[p], after[p], pipe.nu_tables,
                          pipe.arrived)
