@@ -62,16 +62,11 @@ __device__ __forceinline__ float load_coord(const void* x, int64_t e, int64_t N,
 // WB .. WB+3 vary and whose other bits spell o. With WB fixed at compile
 // time the 16 LDS addresses are one register plus immediate offsets; with
 // LO and HI fixed too, every butterfly is straight-line code.
+// The stages on bits LO .. HI-1 applied to 16 coordinates held in
+// registers, v[r] being coordinate base + (r << WB): stage WB + q pairs
+// v[r] with v[r | 2^q].
 template <int WB, int LO, int HI>
-__device__ __forceinline__ void group16(float* s) {
-    const int o = threadIdx.x;
-    const int base = ((o >> WB) << (WB + 4)) | (o & ((1 << WB) - 1));
-    float* p = s + pad(base);
-    // pad(base + (r << WB)) - pad(base): bits WB.. of base are clear
-    constexpr int step = WB >= 4 ? (1 << WB) + (1 << (WB - 4)) : 1;
-    float v[16];
-#pragma unroll
-    for (int r = 0; r < 16; r++) v[r] = p[r * step];
+__device__ __forceinline__ void butterflies(float* v) {
 #pragma unroll
     for (int q = 0; q < 4; q++) {
         if (WB + q >= LO && WB + q < HI) {
@@ -86,6 +81,26 @@ __device__ __forceinline__ void group16(float* s) {
             }
         }
     }
+}
+
+// LDS index of thread o's first coordinate in a group16<WB> pass, and the
+// distance between its 16 coordinates in the padded tile:
+// pad(base + (r << WB)) - pad(base), since bits WB.. of base are clear.
+template <int WB>
+__device__ __forceinline__ int group_base(int o) {
+    return ((o >> WB) << (WB + 4)) | (o & ((1 << WB) - 1));
+}
+template <int WB>
+constexpr int group_step() { return WB >= 4 ? (1 << WB) + (1 << (WB - 4)) : 1; }
+
+template <int WB, int LO, int HI>
+__device__ __forceinline__ void group16(float* s) {
+    float* p = s + pad(group_base<WB>(threadIdx.x));
+    constexpr int step = group_step<WB>();
+    float v[16];
+#pragma unroll
+    for (int r = 0; r < 16; r++) v[r] = p[r * step];
+    butterflies<WB, LO, HI>(v);
 #pragma unroll
     for (int r = 0; r < 16; r++) p[r * step] = v[r];
 }
@@ -408,36 +423,61 @@ __global__ __launch_bounds__(kTT) void rht_tile_quant_kernel(PtrTable x, PtrTabl
     }
 }
 
-// First pass of the forward transform for one tile (d > kTile): signs on
-// load, stages 0 .. kTileBits-1, the unscaled partial transform stored to
-// y (as rht_tile_kernel<true, false>).
+// First pass of the forward transform for one tile (d > kTile): the
+// unscaled partial transform over index bits 0 .. kTileBits-1, stored to y
+// (as rht_tile_kernel<true, false>). Thread o loads the 16 consecutive
+// coordinates 16o .. 16o+15 (16-byte loads when vec), whose signs are 16
+// bits of one Philox word, and runs stages 0-3 in registers before the
+// first LDS store; stages 4-11 go through LDS and stage 12 is applied on
+// the way out (a thread holds both coordinates of its last butterflies).
 template <ga_dtype DT>
 __device__ __forceinline__ void forward_tile_body(float* s, uint32_t* words, const void* x, float* y,
-                                                  int64_t tile, int64_t N, uint32_t k0, uint32_t k1) {
+                                                  int64_t tile, int64_t N, bool vec, uint32_t k0,
+                                                  uint32_t k1) {
     const int64_t e0 = tile * kTile;
     const int nx = (int)max((int64_t)0, min((int64_t)kTile, N - e0));
+    const int i0 = 16 * threadIdx.x;
     sign_blocks(words, e0 >> 7, kTile >> 7, k0, k1);
-    float v[kPer];
-    if (nx == kTile) {
+    float v[16];
+    if (vec && nx == kTile) {
+        if (DT == GA_BF16) {
+            const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + e0 + i0);
 #pragma unroll
-        for (int k = 0; k < kPer; k++) v[k] = load_tile<true, DT>(x, e0, threadIdx.x + k * kTT);
+            for (int h = 0; h < 2; h++) {
+                const uint4 q = src[h];
+                const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    v[8 * h + 2 * k] = __uint_as_float(w4[k] << 16);
+                    v[8 * h + 2 * k + 1] = __uint_as_float(w4[k] & 0xFFFF0000u);
+                }
+            }
+        } else {
+            const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(x) + e0 + i0);
+#pragma unroll
+            for (int h = 0; h < 4; h++) {
+                const float4 q = src[h];
+                v[4 * h] = q.x;
+                v[4 * h + 1] = q.y;
+                v[4 * h + 2] = q.z;
+                v[4 * h + 3] = q.w;
+            }
+        }
     } else {
 #pragma unroll
-        for (int k = 0; k < kPer; k++) {
-            const int i = threadIdx.x + k * kTT;
-            v[k] = i < nx ? load_tile<true, DT>(x, e0, i) : 0.0f;
-        }
+        for (int r = 0; r < 16; r++) v[r] = i0 + r < nx ? load_tile<true, DT>(x, e0, i0 + r) : 0.0f;
     }
     __syncthreads();                                  // the sign words
+    const uint32_t sw = words[4 * (i0 >> 7) + ((i0 >> 5) & 3)] >> (i0 & 31);
 #pragma unroll
-    for (int k = 0; k < kPer; k++) {
-        const int i = threadIdx.x + k * kTT;
-        s[pad(i)] = negated(words, i >> 7, i) ? -v[k] : v[k];
-    }
+    for (int r = 0; r < 16; r++)
+        if ((sw >> r) & 1u) v[r] = -v[r];
+    butterflies<0, 0, 4>(v);
+    float* p = s + pad(i0);
+#pragma unroll
+    for (int r = 0; r < 16; r++) p[r] = v[r];
     __syncthreads();
-    stages_ct<0, kTileBits - 1>(s);
-    // the last stage (index bit kTileBits-1) on the way out: coordinates i
-    // and i + kTile/2 of one butterfly are both this thread's
+    stages_ct<4, kTileBits - 1>(s);
 #pragma unroll
     for (int k = 0; k < kPer / 2; k++) {
         const int i = threadIdx.x + k * kTT;
@@ -449,37 +489,67 @@ __device__ __forceinline__ void forward_tile_body(float* s, uint32_t* words, con
 
 template <ga_dtype DT>
 __global__ __launch_bounds__(kTT) void rht_forward_tile_kernel(PtrTable x, PtrTable y, int64_t N,
-                                                               uint32_t k0, uint32_t k1) {
+                                                               int vec, uint32_t k0, uint32_t k1) {
     __shared__ float s[kLds];
     __shared__ uint32_t words[4 * (kTile / 128)];
     const int w = blockIdx.y;
-    forward_tile_body<DT>(s, words, x.p[w], static_cast<float*>(y.p[w]), blockIdx.x, N, k0, k1);
+    forward_tile_body<DT>(s, words, x.p[w], static_cast<float*>(y.p[w]), blockIdx.x, N, vec != 0,
+                          k0, k1);
 }
 
 // Second pass (d > kTile): as rht_cross_kernel on rows j = 0 .. G-1 of
-// block b, columns cg W .. cg W + W - 1, then the G x W sub-matrix rounded
-// in groups of 8 consecutive columns of a row (W >= 16).
-template <int B, bool TABLE>
+// block b, columns cg W .. cg W + W - 1 (W = 2^WBITS >= 16), then the G x W
+// sub-matrix rounded in groups of 8 consecutive columns of a row. The first
+// four stages (row bits) run in registers on coordinates loaded straight
+// from y: thread o takes 16 rows of one column, so each load instruction
+// reads consecutive columns across the wave.
+template <int B, bool TABLE, int WBITS>
 __device__ __forceinline__ void cross_quant_body(float* s, const Rounder<TABLE>& rd, const float* y,
                                                  uint8_t* out, uint32_t wid, int64_t b, int cg,
-                                                 int dbits, int wbits, float c, const float* mM,
-                                                 uint32_t q0, uint32_t q1) {
-    const int W = 1 << wbits;
+                                                 int dbits, float c, const float* mM, uint32_t q0,
+                                                 uint32_t q1) {
+    constexpr int W = 1 << WBITS;
+    constexpr int WB = WBITS < kTileBits - 4 ? WBITS : kTileBits - 4;
+    constexpr int H1 = WB + 4;                        // first pass: bits WBITS .. H1-1
     const int64_t base = (b << dbits) + (int64_t)cg * W;
     const float* yb = y + base;
+    const int lb = group_base<WB>(threadIdx.x);
+    float v[16];
 #pragma unroll
-    for (int k = 0; k < kPer; k++) {
-        const int i = threadIdx.x + k * kTT;
-        s[pad(i)] = yb[(i >> wbits) * kTile + (i & (W - 1))];
+    for (int r = 0; r < 16; r++) {
+        const int i = lb + (r << WB);
+        v[r] = yb[(i >> WBITS) * kTile + (i & (W - 1))];
     }
+    butterflies<WB, WBITS, H1>(v);
+    float* p = s + pad(lb);
+#pragma unroll
+    for (int r = 0; r < 16; r++) p[r * group_step<WB>()] = v[r];
     __syncthreads();
-    stages(s, wbits, kTileBits);
+    stages_ct<H1, kTileBits>(s);
     const BlockGrid bg = block_grid(mM, b, rd.levels);   // one block per workgroup
 #pragma unroll
     for (int k = 0; k < kPer / 8; k++) {
         const int i0 = 8 * (threadIdx.x + k * kTT);
-        const int64_t e = base + (int64_t)(i0 >> wbits) * kTile + (i0 & (W - 1));
+        const int64_t e = base + (int64_t)(i0 >> WBITS) * kTile + (i0 & (W - 1));
         store_group<B>(out, e >> 3, round_group<B, TABLE>(s, i0, e, c, bg, rd, wid, q0, q1));
+    }
+}
+
+template <int B, bool TABLE>
+__device__ __forceinline__ void cross_quant_dispatch(float* s, const Rounder<TABLE>& rd, const float* y,
+                                                     uint8_t* out, uint32_t wid, int64_t b, int cg,
+                                                     int dbits, float c, const float* mM, uint32_t q0,
+                                                     uint32_t q1) {
+    switch (2 * kTileBits - dbits) {                  // W = kTile / G
+        case 4: cross_quant_body<B, TABLE, 4>(s, rd, y, out, wid, b, cg, dbits, c, mM, q0, q1); break;
+        case 5: cross_quant_body<B, TABLE, 5>(s, rd, y, out, wid, b, cg, dbits, c, mM, q0, q1); break;
+        case 6: cross_quant_body<B, TABLE, 6>(s, rd, y, out, wid, b, cg, dbits, c, mM, q0, q1); break;
+        case 7: cross_quant_body<B, TABLE, 7>(s, rd, y, out, wid, b, cg, dbits, c, mM, q0, q1); break;
+        case 8: cross_quant_body<B, TABLE, 8>(s, rd, y, out, wid, b, cg, dbits, c, mM, q0, q1); break;
+        case 9: cross_quant_body<B, TABLE, 9>(s, rd, y, out, wid, b, cg, dbits, c, mM, q0, q1); break;
+        case 10: cross_quant_body<B, TABLE, 10>(s, rd, y, out, wid, b, cg, dbits, c, mM, q0, q1); break;
+        case 11: cross_quant_body<B, TABLE, 11>(s, rd, y, out, wid, b, cg, dbits, c, mM, q0, q1); break;
+        default: cross_quant_body<B, TABLE, 12>(s, rd, y, out, wid, b, cg, dbits, c, mM, q0, q1); break;
     }
 }
 
@@ -493,7 +563,7 @@ __device__ __forceinline__ void cross_quant_body(float* s, const Rounder<TABLE>&
 // workgroups per role; workgroups alternate roles while both have work.
 template <ga_dtype DT, int B, bool TABLE>
 __global__ __launch_bounds__(kTT) void rht_quant_pipe_kernel(PtrTable x, PtrTable y, PtrTable packed,
-                                                             int worker0, int64_t N, int dbits,
+                                                             int worker0, int64_t N, int vec, int dbits,
                                                              int64_t nblk, int64_t a0, int64_t na,
                                                              int64_t b0, int64_t nb, uint32_t k0,
                                                              uint32_t k1, float c,
@@ -520,12 +590,13 @@ __global__ __launch_bounds__(kTT) void rht_quant_pipe_kernel(PtrTable x, PtrTabl
     const int64_t b = unit - (int64_t)w * nblk;
     const int r = (int)(j & ((1 << gbits) - 1));
     if (first) {
-        forward_tile_body<DT>(s, aux, x.p[w], static_cast<float*>(y.p[w]), (b << gbits) + r, N, k0, k1);
+        forward_tile_body<DT>(s, aux, x.p[w], static_cast<float*>(y.p[w]), (b << gbits) + r, N,
+                              vec != 0, k0, k1);
     } else {
         const Rounder<TABLE> rd = make_rounder<TABLE, kTT>(tab, L, aux);
-        cross_quant_body<B, TABLE>(s, rd, static_cast<const float*>(y.p[w]),
-                                   static_cast<uint8_t*>(packed.p[w]), (uint32_t)(worker0 + w), b, r,
-                                   dbits, 2 * kTileBits - dbits, c, mM, q0, q1);
+        cross_quant_dispatch<B, TABLE>(s, rd, static_cast<const float*>(y.p[w]),
+                                       static_cast<uint8_t*>(packed.p[w]), (uint32_t)(worker0 + w), b, r,
+                                       dbits, c, mM, q0, q1);
     }
 }
 
@@ -651,9 +722,11 @@ extern "C" ga_status thc_rht_forward(const void* const* bufs, int32_t P, int64_t
     const int64_t tiles = ceil_div(Np, kTile);
     if (tiles > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: too many tiles", what);
     PtrTable tx{}, ty{};
+    int vec = 1;                                      // 16-byte loads of x in the first pass
     for (int i = 0; i < P; i++) {
         tx.p[i] = const_cast<void*>(bufs[i]);
         ty.p[i] = y[i];
+        vec &= aligned(bufs[i], 16);
     }
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
@@ -669,9 +742,9 @@ extern "C" ga_status thc_rht_forward(const void* const* bufs, int32_t P, int64_t
         return check_launch(what);
     }
     if (dt == GA_F32)
-        hipLaunchKernelGGL((rht_forward_tile_kernel<GA_F32>), g1, dim3(kTT), 0, hs, tx, ty, N, k0, k1);
+        hipLaunchKernelGGL((rht_forward_tile_kernel<GA_F32>), g1, dim3(kTT), 0, hs, tx, ty, N, vec, k0, k1);
     else
-        hipLaunchKernelGGL((rht_forward_tile_kernel<GA_BF16>), g1, dim3(kTT), 0, hs, tx, ty, N, k0, k1);
+        hipLaunchKernelGGL((rht_forward_tile_kernel<GA_BF16>), g1, dim3(kTT), 0, hs, tx, ty, N, vec, k0, k1);
     if ((rc = check_launch(what))) return rc;
     const int wbits = 2 * kTileBits - dbits;         // W = kTile / G
     hipLaunchKernelGGL((rht_cross_kernel<true, GA_F32>), g1, dim3(kTT), 0, hs, ty, ty, Np, dbits, wbits, k0, k1, c, d_mM);
@@ -745,10 +818,12 @@ extern "C" ga_status thc_rht_quantize(const void* const* bufs, int32_t P, int32_
     const int64_t tiles = ceil_div(Np, kTile);
     if (tiles > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: too many tiles", what);
     PtrTable tx{}, ty{}, tp{};
+    int vec = 1;                                      // 16-byte loads of x in the first pass
     for (int i = 0; i < P; i++) {
         tx.p[i] = const_cast<void*>(bufs[i]);
         tp.p[i] = packed[i];
         if (two_pass) ty.p[i] = y_scratch[i];
+        vec &= aligned(bufs[i], 16);
     }
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const uint32_t k0 = (uint32_t)rht_seed, k1 = (uint32_t)(rht_seed >> 32);
@@ -789,10 +864,10 @@ extern "C" ga_status thc_rht_quantize(const void* const* bufs, int32_t P, int32_
 #define GA_PQ(DT, B)                                                                                    \
         do {                                                                                            \
             if (tb) hipLaunchKernelGGL((rht_quant_pipe_kernel<DT, B, true>), grid, dim3(kTT), 0, hs, tx, \
-                                       ty, tp, worker0, N, dbits, nblk, a0, na, b0, nb, k0, k1, c, d_mM, \
+                                       ty, tp, worker0, N, vec, dbits, nblk, a0, na, b0, nb, k0, k1, c, d_mM, \
                                        q0, q1, tab);                                                    \
             else hipLaunchKernelGGL((rht_quant_pipe_kernel<DT, B, false>), grid, dim3(kTT), 0, hs, tx,  \
-                                    ty, tp, worker0, N, dbits, nblk, a0, na, b0, nb, k0, k1, c, d_mM,   \
+                                    ty, tp, worker0, N, vec, dbits, nblk, a0, na, b0, nb, k0, k1, c, d_mM,   \
                                     q0, q1, tab);                                                       \
         } while (0)
 #define GA_PQB(DT)                               \

@@ -229,3 +229,21 @@ def test_rht_quantize_caller_buffers_and_empty():
     ga.thc_rht_quantize([torch.empty(0, device=DEV)], d, SEED, mM, b, 11, packed=[pk[0]])
     torch.cuda.synchronize()
     assert torch.equal(pk[0], keep)
+
+
+@pytest.mark.parametrize("dt", [ga.F32, ga.BF16])
+def test_misaligned_inputs_two_pass(dt):
+    """Worker vectors that start one element past a 16-byte boundary take
+    the element-wise loads of the first pass: same bits."""
+    P, d, N = 2, 1 << 14, 3 * (1 << 14) - 7
+    big = _inputs(P, N + 1, dt, seed=77)
+    bufs = [t[1:] for t in big]
+    xs = [_host(t) for t in bufs]
+    mMw = oracle.rht_range(np.stack([oracle.rht_sumsq(x, d) for x in xs]), d, 2.0)
+    mM = torch.from_numpy(mMw).to(DEV)
+    y = ga.thc_rht_forward(bufs, d, SEED, mM=mM)
+    pk = ga.thc_rht_quantize(bufs, d, SEED, mM, 4, 5)
+    for i in range(P):
+        yc = oracle.clamp(oracle.rht_forward(xs[i], d, SEED), d, mMw)
+        assert np.array_equal(_bits(y[i].cpu().numpy()), _bits(yc)), i
+        assert np.array_equal(pk[i].cpu().numpy(), oracle.usq_quantize(yc, i, d, mMw, 4, 5)), i
