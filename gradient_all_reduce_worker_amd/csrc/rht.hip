@@ -10,8 +10,8 @@
 // bits do not commute in floating point, so they run strictly in that order.
 //
 // Layout of the work (512-thread workgroups, an 8192-coordinate tile of
-// 32 KiB in LDS, padded by one word per 16 against bank conflicts; three
-// workgroups fit a CU, so one loads while another computes):
+// 32 KiB in LDS, padded by one word per 16 against bank conflicts; three or
+// four workgroups fit a CU, so one loads while another computes):
 //  * tile pass: a workgroup loads 8192 consecutive coordinates (several
 //    whole blocks when d < 8192) and runs stages 0 .. log2(T) - 1 with
 //    T = min(d, 8192);
@@ -21,8 +21,11 @@
 // Inside a pass, stages go four at a time through registers: every thread
 // takes the 16 coordinates that differ only in four consecutive index bits,
 // runs the stages on those bits, and writes them back (one LDS round trip
-// per four stages). Each butterfly adds and subtracts the same two values
-// as the plain loop, so the output is bit-for-bit that loop's.
+// per four stages; the passes of the blocks above 8192 coordinates run
+// their first four stages on values loaded straight from memory and their
+// tile pass's last stage on the way out). Each butterfly adds and
+// subtracts the same two values as the plain loop, so the output is
+// bit-for-bit that loop's.
 //
 // The Rademacher signs come from Philox4x32-10: key (seed), counter
 // (q mod 2^32, q >> 32, 0x52485400, 0) with q = e / 128; coordinate e takes
