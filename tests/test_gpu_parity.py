@@ -201,7 +201,7 @@ def test_minmax_misaligned_and_signed_zero():
 
 QUANT_SHAPES = [(1, 1, 0), (2, 15, 0), (2, 16, 0), (3, 17, 0), (4, 1000, 0), (4, 70001, 1024),
                 (3, 5000, 1000), (2, 300, 5), (8, 1 << 18, 1 << 16), (32, 4099, 0),
-                (3, 8192 * 5 + 100, 8192), (2, 8192 * 3, 8192 * 3)]
+                (3, 8192 * 5 + 100, 8192), (2, 8192 * 3, 8192 * 3), (64, 20001, 4096)]
 
 
 @pytest.mark.parametrize("b", [1, 2, 4, 8])

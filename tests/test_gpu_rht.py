@@ -247,3 +247,21 @@ def test_misaligned_inputs_two_pass(dt):
         yc = oracle.clamp(oracle.rht_forward(xs[i], d, SEED), d, mMw)
         assert np.array_equal(_bits(y[i].cpu().numpy()), _bits(yc)), i
         assert np.array_equal(pk[i].cpu().numpy(), oracle.usq_quantize(yc, i, d, mMw, 4, 5)), i
+
+
+@pytest.mark.parametrize("table", [None, "center"])
+def test_rht_quantize_max_workers(table):
+    """64 workers (the largest P), two passes, two chunks of the pipelined
+    schedule; every worker's indices against the oracle."""
+    P, d, N, b = 64, 1 << 14, 2 * (1 << 14) - 3, 4
+    g = 36 if table else 0
+    T = ga.center_table(b, g) if table else None
+    bufs = _inputs(P, N, ga.F32, seed=640)
+    xs = [_host(t) for t in bufs]
+    mMw = oracle.rht_range(np.stack([oracle.rht_sumsq(x, d) for x in xs]), d, 2.0)
+    pk = ga.thc_rht_quantize(bufs, d, SEED, torch.from_numpy(mMw).to(DEV), b, 31, g=g, table=T)
+    for i in range(P):
+        yc = oracle.clamp(oracle.rht_forward(xs[i], d, SEED), d, mMw)
+        want = (oracle.nuhc_quantize(yc, i, d, mMw, b, g, T, 31) if table
+                else oracle.usq_quantize(yc, i, d, mMw, b, 31))
+        assert np.array_equal(pk[i].cpu().numpy(), want), i
