@@ -341,11 +341,60 @@ __device__ __forceinline__ void widen_f32(const uint4& r, float* f) {
     f[2] = __uint_as_float(r.z); f[3] = __uint_as_float(r.w);
 }
 
+// One span's 8 elements of this lane (a[h][i]: vector v0 + 256 h), rounded
+// on grid gb and stored; EF: the residual x - value(index) replaces e.
+template <int B, bool TABLE, bool EF>
+__device__ __forceinline__ void lane_span(float (&a)[2][4], const Rounder<TABLE>& rd, Grid gb,
+                                          EfGrid q, int64_t e_blk, int64_t v0, uint32_t wid,
+                                          uint32_t k0, uint32_t k1, uint8_t* out, uint4* err) {
+    const int t = threadIdx.x;
+    const bool odd = t & 1;
+    const int64_t g = e_blk / 8 + (odd ? 128 + (t >> 1) : (t >> 1));
+    const Philox4 r = philox4x32_10((uint32_t)g, (uint32_t)((uint64_t)g >> 32), wid, 0u, k0, k1);
+    const uint32_t ra = swap_pair(odd ? r.v[0] : r.v[2]);
+    const uint32_t rb = swap_pair(odd ? r.v[1] : r.v[3]);
+    // words of the uniforms of this lane's two half-groups
+    const uint32_t u[2][2] = {{odd ? ra : r.v[0], odd ? rb : r.v[1]},
+                              {odd ? r.v[2] : ra, odd ? r.v[3] : rb}};
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        uint32_t bits = 0;
+        float res[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const uint32_t r16 = (u[h][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+            float v;
+            bits |= rd.index_v(a[h][i], gb, r16, &v) << (i * B);
+            if (EF) res[i] = a[h][i] - ef_value(q, v);
+        }
+        const int64_t vv = v0 + h * 256;
+        if (B == 8) {
+            reinterpret_cast<uint32_t*>(out)[vv] = bits;
+        } else if (B == 4) {
+            reinterpret_cast<uint16_t*>(out)[vv] = (uint16_t)bits;
+        } else if (B == 2) {
+            out[vv] = (uint8_t)bits;
+        } else {                                    // two vectors per byte
+            const uint32_t other = swap_pair(bits);
+            if (!odd) out[vv >> 1] = (uint8_t)(bits | (other << 4));
+        }
+        if (EF)
+            store_stream(err + vv, make_uint4(__float_as_uint(res[0]), __float_as_uint(res[1]),
+                                              __float_as_uint(res[2]), __float_as_uint(res[3])));
+    }
+}
+
+// A workgroup takes `spans` consecutive spans, two at a time: the loads of
+// both are issued before either is rounded, and the grid (partition index
+// and L / (M - m), both computed in vector registers) is worked out once
+// per partition rather than per span. pshift >= 0: the partition of span
+// s is s >> pshift (partitions of 2^pshift spans, or one partition);
+// otherwise it is s kLSpan / plen.
 template <int B, bool TABLE, bool EF>
 __global__ __launch_bounds__(kThreads) void usq_quantize_lane_kernel(PtrTable bufs, PtrTable errs,
                                                                      PtrTable packed, int worker0,
-                                                                     int64_t plen, int64_t n_spans,
-                                                                     int spans,
+                                                                     int64_t plen, int pshift,
+                                                                     int64_t n_spans, int spans,
                                                                      const float* __restrict__ mM,
                                                                      uint32_t k0, uint32_t k1,
                                                                      TableArg tab) {
@@ -358,58 +407,49 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_lane_kernel(PtrTable bu
     uint8_t* out = static_cast<uint8_t*>(packed.p[slot]);
     const uint32_t wid = (uint32_t)(worker0 + slot);
     const int t = threadIdx.x;
-    const bool odd = t & 1;
-    for (int sp = 0; sp < spans; sp++) {                 // spans of this workgroup
+    int64_t p_have = -1;
+    Grid gb{};
+    EfGrid q{};
+    for (int sp = 0; sp < spans; sp += 2) {               // spans of this workgroup
         const int64_t blk = (int64_t)blockIdx.x * spans + sp;
         if (blk >= n_spans) break;
-        const int64_t e_blk = blk * kLSpan;
-        const Grid gb = grid_of(mM, e_blk / plen, rd.levels);
-        const int64_t v0 = e_blk / 4 + t;                // vectors v0 and v0 + 256
-        float a[2][4];
-        widen_f32(load_stream(x + v0), a[0]);
-        widen_f32(load_stream(x + v0 + 256), a[1]);
-        if (EF) {
-            float ev[2][4];
-            widen_f32(load_stream(err + v0), ev[0]);
-            widen_f32(load_stream(err + v0 + 256), ev[1]);
+        const bool two = sp + 1 < spans && blk + 1 < n_spans;
+        float a[2][2][4];
 #pragma unroll
-            for (int h = 0; h < 2; h++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) a[h][i] = a[h][i] + ev[h][i];
+        for (int k = 0; k < 2; k++) {
+            const int64_t v0 = (blk + k) * (kLSpan / 4) + t;
+            if (k == 0 || two) {
+                widen_f32(load_stream(x + v0), a[k][0]);
+                widen_f32(load_stream(x + v0 + 256), a[k][1]);
+            }
         }
-        const EfGrid q = EF ? ef_grid_of(mM, e_blk / plen, rd.levels) : EfGrid{};
-        const int64_t g = e_blk / 8 + (odd ? 128 + (t >> 1) : (t >> 1));
-        const Philox4 r = philox4x32_10((uint32_t)g, (uint32_t)((uint64_t)g >> 32), wid, 0u, k0, k1);
-        const uint32_t ra = swap_pair(odd ? r.v[0] : r.v[2]);
-        const uint32_t rb = swap_pair(odd ? r.v[1] : r.v[3]);
-        // words of the uniforms of this lane's two half-groups
-        const uint32_t u[2][2] = {{odd ? ra : r.v[0], odd ? rb : r.v[1]},
-                                  {odd ? r.v[2] : ra, odd ? r.v[3] : rb}};
+        if (EF) {
 #pragma unroll
-        for (int h = 0; h < 2; h++) {
-            uint32_t bits = 0;
-            float res[4];
+            for (int k = 0; k < 2; k++) {
+                const int64_t v0 = (blk + k) * (kLSpan / 4) + t;
+                if (k == 0 || two) {
+                    float ev[2][4];
+                    widen_f32(load_stream(err + v0), ev[0]);
+                    widen_f32(load_stream(err + v0 + 256), ev[1]);
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const uint32_t r16 = (u[h][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-                float v;
-                bits |= rd.index_v(a[h][i], gb, r16, &v) << (i * B);
-                if (EF) res[i] = a[h][i] - ef_value(q, v);
+                    for (int h = 0; h < 2; h++)
+#pragma unroll
+                        for (int i = 0; i < 4; i++) a[k][h][i] = a[k][h][i] + ev[h][i];
+                }
             }
-            const int64_t vv = v0 + h * 256;
-            if (B == 8) {
-                reinterpret_cast<uint32_t*>(out)[vv] = bits;
-            } else if (B == 4) {
-                reinterpret_cast<uint16_t*>(out)[vv] = (uint16_t)bits;
-            } else if (B == 2) {
-                out[vv] = (uint8_t)bits;
-            } else {                                    // two vectors per byte
-                const uint32_t other = swap_pair(bits);
-                if (!odd) out[vv >> 1] = (uint8_t)(bits | (other << 4));
+        }
+#pragma unroll
+        for (int k = 0; k < 2; k++) {
+            if (k == 1 && !two) break;
+            const int64_t s = blk + k;
+            const int64_t p = pshift >= 0 ? s >> pshift : s * kLSpan / plen;
+            if (p != p_have) {                           // workgroup-uniform
+                gb = grid_of(mM, p, rd.levels);
+                if (EF) q = ef_grid_of(mM, p, rd.levels);
+                p_have = p;
             }
-            if (EF)
-                store_stream(err + vv, make_uint4(__float_as_uint(res[0]), __float_as_uint(res[1]),
-                                                  __float_as_uint(res[2]), __float_as_uint(res[3])));
+            lane_span<B, TABLE, EF>(a[k], rd, gb, q, s * kLSpan, s * (kLSpan / 4) + t, wid, k0, k1,
+                                    out, err);
         }
     }
 }
@@ -926,6 +966,14 @@ ga_status quantize_impl(const void* const* bufs, int32_t P, int32_t worker0, int
     // spans to spread that over
     const size_t lane_lds = kLdsPerCu / 6 - 1024 - (table ? kMaxGranularity * 4 : 4);
     const int lane_spans = table ? 4 : 1;
+    // partitions of a power-of-two number of spans (or one partition): a shift
+    int pshift = -1;
+    if (plen >= N) {
+        pshift = 62;
+    } else if (plen % kLSpan == 0) {
+        const int64_t sp = plen / kLSpan;
+        if ((sp & (sp - 1)) == 0) pshift = __builtin_ctzll((unsigned long long)sp);
+    }
     const int64_t lane_blocks = ceil_div(fast, lane_spans);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
@@ -935,7 +983,8 @@ ga_status quantize_impl(const void* const* bufs, int32_t P, int32_t worker0, int
         if (fast > 0 && DT == GA_F32)                                                                 \
             hipLaunchKernelGGL((usq_quantize_lane_kernel<B, TB, EF>),                                 \
                                dim3((unsigned)lane_blocks, (unsigned)P), dim3(kThreads), lane_lds,    \
-                               hs, tx, te, tp, worker0, plen, fast, lane_spans, d_mM, k0, k1, tab);   \
+                               hs, tx, te, tp, worker0, plen, pshift, fast, lane_spans, d_mM, k0, k1,  \
+                               tab);                                                                  \
         else if (fast > 0)                                                                            \
             hipLaunchKernelGGL((usq_quantize_fast_kernel<DT, B, TB, EF>),                             \
                                dim3((unsigned)fast, (unsigned)P), dim3(kThreads), 0, hs, tx, te, tp,  \
