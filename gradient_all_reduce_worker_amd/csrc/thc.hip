@@ -273,7 +273,7 @@ __device__ __forceinline__ void store_err_group(float* err, int64_t g, const flo
 template <ga_dtype DT, int B, bool TABLE, bool EF>
 __global__ __launch_bounds__(kThreads) void usq_quantize_fast_kernel(PtrTable bufs, PtrTable errs,
                                                                      PtrTable packed, int worker0,
-                                                                     int64_t plen,
+                                                                     int64_t plen, int pshift,
                                                                      const float* __restrict__ mM,
                                                                      uint32_t k0, uint32_t k1,
                                                                      TableArg tab) {
@@ -286,7 +286,8 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_fast_kernel(PtrTable bu
     uint8_t* out = static_cast<uint8_t*>(packed.p[slot]);
     const uint32_t wid = (uint32_t)(worker0 + slot);
     const int64_t e_blk = (int64_t)blockIdx.x * kFSpan;
-    const Grid gb = grid_of(mM, e_blk / plen, rd.levels);
+    const int64_t part = pshift >= 0 ? (int64_t)blockIdx.x >> pshift : e_blk / plen;
+    const Grid gb = grid_of(mM, part, rd.levels);
     float a[kFGroups][8];
 #pragma unroll
     for (int j = 0; j < kFGroups; j++)
@@ -301,7 +302,7 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_fast_kernel(PtrTable bu
 #pragma unroll
             for (int i = 0; i < 8; i++) a[j][i] = a[j][i] + ev[j][i];
     }
-    const EfGrid q = EF ? ef_grid_of(mM, e_blk / plen, rd.levels) : EfGrid{};
+    const EfGrid q = EF ? ef_grid_of(mM, part, rd.levels) : EfGrid{};
 #pragma unroll
     for (int j = 0; j < kFGroups; j++) {
         const int64_t g = e_blk / 8 + (int64_t)j * kThreads + threadIdx.x;
@@ -966,12 +967,13 @@ ga_status quantize_impl(const void* const* bufs, int32_t P, int32_t worker0, int
     // spans to spread that over
     const size_t lane_lds = kLdsPerCu / 6 - 1024 - (table ? kMaxGranularity * 4 : 4);
     const int lane_spans = table ? 4 : 1;
-    // partitions of a power-of-two number of spans (or one partition): a shift
+    // partitions of a power-of-two number of fast spans (or one partition):
+    // the kernels find a span's partition by a shift
     int pshift = -1;
     if (plen >= N) {
         pshift = 62;
-    } else if (plen % kLSpan == 0) {
-        const int64_t sp = plen / kLSpan;
+    } else if (plen % span == 0) {
+        const int64_t sp = plen / span;
         if ((sp & (sp - 1)) == 0) pshift = __builtin_ctzll((unsigned long long)sp);
     }
     const int64_t lane_blocks = ceil_div(fast, lane_spans);
@@ -988,7 +990,7 @@ ga_status quantize_impl(const void* const* bufs, int32_t P, int32_t worker0, int
         else if (fast > 0)                                                                            \
             hipLaunchKernelGGL((usq_quantize_fast_kernel<DT, B, TB, EF>),                             \
                                dim3((unsigned)fast, (unsigned)P), dim3(kThreads), 0, hs, tx, te, tp,  \
-                               worker0, plen, d_mM, k0, k1, tab);                                     \
+                               worker0, plen, pshift, d_mM, k0, k1, tab);                             \
         if (blocks > 0)                                                                               \
             hipLaunchKernelGGL((usq_quantize_kernel<DT, B, TB, EF>),                                  \
                                dim3((unsigned)blocks, (unsigned)P), dim3(kThreads), 0, hs,            \
