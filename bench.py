@@ -153,6 +153,8 @@ def main():
                     help="fused workloads: pack -> ring -> unpack instead of the zero-copy ring")
     ap.add_argument("--ring-mode", default="fused", choices=["fused", "dual"],
                     help="single ring or the bidirectional dual ring fold order")
+    ap.add_argument("--separate-tail", action="store_true",
+                    help="THC passes: integer sum, dequant and NMSE as three calls, not one")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one 1 GiB torch copy first (PMC calibration)")
     args = ap.parse_args()
@@ -172,7 +174,7 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
 
-    pipe = Pipeline(args.workload, zero_copy=not args.copy_fusion,
+    pipe = Pipeline(args.workload, zero_copy=not args.copy_fusion, fused_tail=not args.separate_tail,
                     ring_mode=ga.RING_DUAL if args.ring_mode == "dual" else ga.RING_FUSED)
     t0 = time.perf_counter()
     pipe.setup()
@@ -245,6 +247,7 @@ def main():
                    "elem": "bf16" if pipe.w.dtype == ga.BF16 else "fp32",
                    "partition_elems": pipe.w.part_elems, "thc_bits": list(pipe.w.thc_bits),
                    "ring": args.ring_mode,
+                   "thc_tail": "separate" if args.separate_tail else "fused",
                    "fusion": (None if not pipe.w.fused else
                               "pack-ring-unpack" if args.copy_fusion else "zero-copy"),
                    "parallelism": "1 GPU, P simulated workers"},

@@ -28,7 +28,7 @@ EXPORTS = (
     "thc_nuhc_quantize", "thc_nuhc_aggregate", "thc_nuhc_dequant",
     "thc_rht_sumsq", "thc_rht_range", "thc_rht_forward", "thc_rht_inverse",
     "ga_fusion_ring_plan", "ga_fusion_ring_allreduce", "thc_ef_minmax", "thc_ef_quantize",
-    "thc_rht_quantize",
+    "thc_rht_quantize", "thc_aggregate_dequant", "thc_aggregate_dequant_ws_bytes",
 )
 
 
@@ -96,10 +96,14 @@ def load() -> C.CDLL:
     L.thc_ef_minmax.argtypes = [C.POINTER(vp), C.POINTER(vp), i32, i64, i32, i64, vp, vp]
     L.thc_ef_quantize.argtypes = [C.POINTER(vp), C.POINTER(vp), i32, i32, i64, i32, i64, vp, i32,
                                   i32, C.POINTER(i32), u64, C.POINTER(vp), vp]
+    L.thc_aggregate_dequant.argtypes = [C.POINTER(vp), i32, i64, i32, i32, C.POINTER(i32), i64, vp, vp,
+                                        vp, i32, vp, vp, vp, C.c_size_t, vp]
+    L.thc_aggregate_dequant_ws_bytes.argtypes = [i64]
+    L.thc_aggregate_dequant_ws_bytes.restype = C.c_size_t
     L.ga_last_error.argtypes = []
     L.ga_last_error.restype = C.c_char_p
     for name in EXPORTS:
-        if name not in ("thc_nmse_ws_bytes", "ga_last_error"):
+        if name not in ("thc_nmse_ws_bytes", "ga_last_error", "thc_aggregate_dequant_ws_bytes"):
             getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -446,6 +450,41 @@ def thc_ef_quantize(bufs: Sequence[torch.Tensor], errs: Sequence[torch.Tensor], 
                                   _table_arg(table) if table is not None else None, seed,
                                   _ptr_array(packed, "packed"), _stream(stream)))
     return packed
+
+
+def thc_aggregate_dequant_ws_bytes(N: int) -> int:
+    return load().thc_aggregate_dequant_ws_bytes(N)
+
+
+def thc_aggregate_dequant(packed: Sequence[torch.Tensor], N: int, b: int, mM: torch.Tensor,
+                          part_elems: int = 0, out_dtype=torch.float32, g: int = 0, table=None,
+                          x_ref: Optional[torch.Tensor] = None, keep_sum: bool = True,
+                          out: Optional[torch.Tensor] = None, S: Optional[torch.Tensor] = None,
+                          nmse_out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                          stream=None):
+    """Integer sum, dequantized average and (with x_ref) NMSE in one pass;
+    returns (S or None, x_hat, nmse or None)."""
+    dev = packed[0].device
+    if out is None:
+        out = torch.empty(max(N, 1), dtype=out_dtype, device=dev)
+    if keep_sum and S is None:
+        S = torch.empty(max(N, 1), dtype=torch.int32, device=dev)
+    if x_ref is not None:
+        if nmse_out is None:
+            nmse_out = torch.empty(3, dtype=torch.float64, device=dev)
+        if ws is None:
+            ws = torch.empty(load().thc_aggregate_dequant_ws_bytes(N), dtype=torch.uint8, device=dev)
+        if x_ref.dtype != out.dtype or x_ref.numel() < N:
+            raise ValueError("x_ref must have the output dtype and N elements")
+    _check(load().thc_aggregate_dequant(
+        _ptr_array(packed, "packed"), len(packed), N, b, g,
+        _table_arg(table) if table is not None else None, part_elems, _dev(mM, "mM"),
+        _dev(S, "sum") if keep_sum else None, _dev(out, "out"), _dt(out),
+        _dev(x_ref, "x_ref") if x_ref is not None else None,
+        _dev(nmse_out, "nmse") if x_ref is not None else None,
+        _dev(ws, "ws") if x_ref is not None else None,
+        ws.numel() if x_ref is not None else 0, _stream(stream)))
+    return (S if keep_sum else None), out, (nmse_out if x_ref is not None else None)
 
 
 # ------------------------------------------------------------------ randomized Hadamard transform

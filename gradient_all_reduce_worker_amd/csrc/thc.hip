@@ -558,36 +558,19 @@ __device__ __forceinline__ uint32_t unit_bits_bounded(const uint8_t* src, int64_
     return (uint32_t)((v >> (bit0 & 7)) & ((1ull << (4 * B)) - 1));
 }
 
-// TABLE: the server of non-uniform THC adds table values T[z] (from LDS)
-// instead of the indices themselves (at most P g, plain int32 lanes).
+// The sums of kAUnits units u[j] (4 elements each) over the P workers:
+// o[j][i] = sum of the indices (uniform) or of the table values tv[z]
+// (TABLE) of element 4 u[j] + i. Units at or past n_units give 0.
 template <int B, bool TABLE>
-__global__ __launch_bounds__(kThreads) void int_aggregate_kernel(PtrTable packed, int P, int64_t N,
-                                                                 int64_t nbytes,
-                                                                 int32_t* __restrict__ sum,
-                                                                 int vec_ok, int64_t u_begin,
-                                                                 TableArg tab) {
+__device__ __forceinline__ void unit_sums(const PtrTable& packed, int P, const int64_t* u,
+                                          const bool* full, int64_t n_units, int64_t nbytes,
+                                          const uint32_t* tv, int32_t (&o)[kAUnits][4]) {
     constexpr uint32_t LM = (1u << B) - 1u;
-    __shared__ uint32_t tv[TABLE ? 256 : 1];
-    if (TABLE) {
-        for (int z = threadIdx.x; z < tab.n; z += kThreads) tv[z] = tab.t[z];
-        __syncthreads();
-    }
-    const int64_t n_units = (N + 3) / 4;
-    const int64_t u_blk = u_begin + (int64_t)blockIdx.x * kThreads * kAUnits;
     uint32_t acc[kAUnits][4];
 #pragma unroll
     for (int j = 0; j < kAUnits; j++)
 #pragma unroll
         for (int i = 0; i < 4; i++) acc[j][i] = 0;
-
-    int64_t u[kAUnits];
-    bool full[kAUnits];
-#pragma unroll
-    for (int j = 0; j < kAUnits; j++) {
-        u[j] = u_blk + (int64_t)j * kThreads + threadIdx.x;
-        // every byte the unit's bits touch lies below nbytes
-        full[j] = vec_ok && (4 * (u[j] + 1) * B + 7) / 8 <= nbytes;
-    }
     constexpr int kBatch = 8;
     for (int i0 = 0; i0 < P; i0 += kBatch) {
         uint32_t w[kBatch][kAUnits];
@@ -623,22 +606,52 @@ __global__ __launch_bounds__(kThreads) void int_aggregate_kernel(PtrTable packed
     }
 #pragma unroll
     for (int j = 0; j < kAUnits; j++) {
-        if (u[j] >= n_units) continue;
-        int32_t o[4];
         if (B == 8 && !TABLE) {
-            o[0] = (int32_t)(acc[j][0] & 0xFFFFu); o[2] = (int32_t)(acc[j][0] >> 16);
-            o[1] = (int32_t)(acc[j][1] & 0xFFFFu); o[3] = (int32_t)(acc[j][1] >> 16);
+            o[j][0] = (int32_t)(acc[j][0] & 0xFFFFu); o[j][2] = (int32_t)(acc[j][0] >> 16);
+            o[j][1] = (int32_t)(acc[j][1] & 0xFFFFu); o[j][3] = (int32_t)(acc[j][1] >> 16);
         } else {
 #pragma unroll
-            for (int i = 0; i < 4; i++) o[i] = (int32_t)acc[j][i];
+            for (int i = 0; i < 4; i++) o[j][i] = (int32_t)acc[j][i];
         }
+    }
+}
+
+// TABLE: the server of non-uniform THC adds table values T[z] (from LDS)
+// instead of the indices themselves (at most P g, plain int32 lanes).
+template <int B, bool TABLE>
+__global__ __launch_bounds__(kThreads) void int_aggregate_kernel(PtrTable packed, int P, int64_t N,
+                                                                 int64_t nbytes,
+                                                                 int32_t* __restrict__ sum,
+                                                                 int vec_ok, int64_t u_begin,
+                                                                 TableArg tab) {
+    __shared__ uint32_t tv[TABLE ? 256 : 1];
+    if (TABLE) {
+        for (int z = threadIdx.x; z < tab.n; z += kThreads) tv[z] = tab.t[z];
+        __syncthreads();
+    }
+    const int64_t n_units = (N + 3) / 4;
+    const int64_t u_blk = u_begin + (int64_t)blockIdx.x * kThreads * kAUnits;
+    int64_t u[kAUnits];
+    bool full[kAUnits];
+#pragma unroll
+    for (int j = 0; j < kAUnits; j++) {
+        u[j] = u_blk + (int64_t)j * kThreads + threadIdx.x;
+        // every byte the unit's bits touch lies below nbytes
+        full[j] = vec_ok && (4 * (u[j] + 1) * B + 7) / 8 <= nbytes;
+    }
+    int32_t o[kAUnits][4];
+    unit_sums<B, TABLE>(packed, P, u, full, n_units, nbytes, tv, o);
+#pragma unroll
+    for (int j = 0; j < kAUnits; j++) {
+        if (u[j] >= n_units) continue;
         const int64_t e = 4 * u[j];
         if (vec_ok && e + 4 <= N) {
-            store_stream(sum + e, make_uint4((uint32_t)o[0], (uint32_t)o[1], (uint32_t)o[2], (uint32_t)o[3]));
+            store_stream(sum + e, make_uint4((uint32_t)o[j][0], (uint32_t)o[j][1], (uint32_t)o[j][2],
+                                             (uint32_t)o[j][3]));
         } else {
 #pragma unroll
             for (int i = 0; i < 4; i++)
-                if (e + i < N) sum[e + i] = o[i];
+                if (e + i < N) sum[e + i] = o[j][i];
         }
     }
 }
@@ -850,6 +863,139 @@ __global__ __launch_bounds__(kThreads) void nmse_final_kernel(const double* ws, 
         out[0] = num;
         out[1] = den;
         out[2] = den != 0.0 ? num / den : (num == 0.0 ? 0.0 : INFINITY);
+    }
+}
+
+// ------------------------------------------------------------------ fused server and worker side
+// One pass for THC's last three steps: the server's sum S of the P workers'
+// indices (or table values), the workers' dequantized average x̂ and, given
+// the exact average x, the NMSE partial sums. S and x̂ are computed with
+// the same code and arithmetic as int_aggregate_kernel and dequant_kernel,
+// so they are bit-identical; S need not be written (x̂ is computed from
+// registers), and x̂ is not read back for the NMSE. A grid of at most
+// kADBlocks workgroups strides over spans of kThreads * kAUnits units.
+constexpr int kADBlocks = 65536;
+
+template <int B, bool TABLE, ga_dtype OUT>
+__global__ __launch_bounds__(kThreads) void agg_dequant_kernel(PtrTable packed, int P, int64_t N,
+                                                               int64_t nbytes, int32_t* __restrict__ sum,
+                                                               int64_t plen, const float* __restrict__ mM,
+                                                               int L, int pow2, float pf, float recip,
+                                                               void* out, const void* xref, double* ws,
+                                                               int vec_ok, TableArg tab) {
+    __shared__ uint32_t tv[TABLE ? 256 : 1];
+    __shared__ double sh[kThreads / 64];
+    if (TABLE) {
+        for (int z = threadIdx.x; z < tab.n; z += kThreads) tv[z] = tab.t[z];
+        __syncthreads();
+    }
+    constexpr int64_t kSpanUnits = (int64_t)kThreads * kAUnits;
+    const int64_t n_units = (N + 3) / 4;
+    const bool uniform = plen % (4 * kSpanUnits) == 0 || plen >= N;   // one grid per span
+    double num = 0.0, den = 0.0;
+    for (int64_t u_blk = (int64_t)blockIdx.x * kSpanUnits; u_blk < n_units;
+         u_blk += (int64_t)gridDim.x * kSpanUnits) {
+        int64_t u[kAUnits];
+        bool full[kAUnits];
+#pragma unroll
+        for (int j = 0; j < kAUnits; j++) {
+            u[j] = u_blk + (int64_t)j * kThreads + threadIdx.x;
+            full[j] = vec_ok && (4 * (u[j] + 1) * B + 7) / 8 <= nbytes;
+        }
+        int32_t o[kAUnits][4];
+        unit_sums<B, TABLE>(packed, P, u, full, n_units, nbytes, tv, o);
+        float m0 = 0.0f, range0 = 0.0f, delta0 = 0.0f;
+        if (uniform) {
+            const int64_t p = 4 * u_blk / plen;
+            m0 = mM[2 * p];
+            range0 = mM[2 * p + 1] - m0;
+            delta0 = range0 / (float)L;
+        }
+#pragma unroll
+        for (int j = 0; j < kAUnits; j++) {
+            if (u[j] >= n_units) continue;
+            const int64_t e = 4 * u[j];
+            const bool whole = vec_ok && e + 4 <= N;
+            if (sum) {
+                if (whole) {
+                    store_stream(sum + e, make_uint4((uint32_t)o[j][0], (uint32_t)o[j][1],
+                                                     (uint32_t)o[j][2], (uint32_t)o[j][3]));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        if (e + i < N) sum[e + i] = o[j][i];
+                }
+            }
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                float m = m0, range = range0, delta = delta0;
+                if (!uniform) {
+                    const int64_t p = min(e + i, N - 1) / plen;
+                    m = mM[2 * p];
+                    range = mM[2 * p + 1] - m;
+                    delta = range / (float)L;
+                }
+                const float avg_index = pow2 ? (float)o[j][i] * recip : (float)o[j][i] / pf;
+                v[i] = range != 0.0f ? m + avg_index * delta : m;
+            }
+            float h[4];                                   // x̂ as stored
+            if (OUT == GA_F32) {
+                float* oo = static_cast<float*>(out);
+                if (whole) {
+                    store_stream(oo + e, make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                                    __float_as_uint(v[2]), __float_as_uint(v[3])));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        if (e + i < N) oo[e + i] = v[i];
+                }
+#pragma unroll
+                for (int i = 0; i < 4; i++) h[i] = v[i];
+            } else {
+                uint16_t* oo = static_cast<uint16_t*>(out);
+                uint32_t hb[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    hb[i] = f32_to_bf16_rne(v[i]);
+                    h[i] = __uint_as_float(hb[i] << 16);
+                }
+                if (whole) {
+                    *reinterpret_cast<uint2*>(oo + e) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        if (e + i < N) oo[e + i] = (uint16_t)hb[i];
+                }
+            }
+            if (xref) {
+                float a[4];
+                if (whole && OUT == GA_F32) {
+                    widen_f32(load_stream(static_cast<const uint4*>(xref) + e / 4), a);
+                } else if (whole) {
+                    const uint2 q = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(xref) + e);
+                    a[0] = __uint_as_float(q.x << 16); a[1] = __uint_as_float(q.x & 0xFFFF0000u);
+                    a[2] = __uint_as_float(q.y << 16); a[3] = __uint_as_float(q.y & 0xFFFF0000u);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; i++) a[i] = e + i < N ? load_as_f32(xref, e + i, OUT) : 0.0f;
+                }
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    if (e + i < N) {
+                        const double d = (double)a[i] - (double)h[i];
+                        num += d * d;
+                        den += (double)a[i] * (double)a[i];
+                    }
+                }
+            }
+        }
+    }
+    num = block_sum(num, sh);
+    den = block_sum(den, sh);
+    if (xref && threadIdx.x == 0) {
+        ws[2 * blockIdx.x] = num;
+        ws[2 * blockIdx.x + 1] = den;
     }
 }
 
@@ -1163,6 +1309,82 @@ extern "C" ga_status thc_nuhc_dequant(const int32_t* d_sum, int64_t N, int32_t P
     if (g < 1 || g > kMaxGranularity)
         return fail(GA_EINVAL, "thc_nuhc_dequant: granularity %d outside [1, %d]", g, kMaxGranularity);
     return dequant_impl(d_sum, N, P, g, part_elems, d_mM, out, out_dt, stream, "thc_nuhc_dequant");
+}
+
+extern "C" size_t thc_aggregate_dequant_ws_bytes(int64_t N) {
+    (void)N;
+    return (size_t)kADBlocks * 2 * sizeof(double);
+}
+
+extern "C" ga_status thc_aggregate_dequant(const uint8_t* const* packed, int32_t P, int64_t N, int32_t b,
+                                           int32_t g, const int32_t* h_table, int64_t part_elems,
+                                           const float* d_mM, int32_t* d_sum, void* out, ga_dtype out_dt,
+                                           const void* x_ref, double* d_nmse, void* d_ws, size_t ws_bytes,
+                                           void* stream) {
+    const char* what = "thc_aggregate_dequant";
+    if (!valid_dtype(out_dt)) return fail(GA_EINVAL, "%s: unknown dtype %d", what, (int)out_dt);
+    if (!valid_bits(b)) return fail(GA_EINVAL, "%s: b = %d is not 1, 2, 4 or 8", what, b);
+    if (P < 1 || P > GA_MAX_WORKERS) return fail(GA_EINVAL, "%s: P = %d outside [1, %d]", what, P, GA_MAX_WORKERS);
+    if (N < 0 || part_elems < 0) return fail(GA_EINVAL, "%s: negative size", what);
+    TableArg tab{};
+    ga_status rc;
+    if (h_table && (rc = load_table(b, g, h_table, &tab, what))) return rc;
+    if (x_ref) {
+        if (!d_nmse || !aligned(d_nmse, 8) || !d_ws || !aligned(d_ws, 8))
+            return fail(GA_EINVAL, "%s: null or misaligned NMSE output/workspace", what);
+        if (ws_bytes < thc_aggregate_dequant_ws_bytes(N))
+            return fail(GA_EINVAL, "%s: workspace of %zu bytes, need %zu", what, ws_bytes,
+                        thc_aggregate_dequant_ws_bytes(N));
+        if (!aligned(x_ref, elem_size(out_dt))) return fail(GA_EINVAL, "%s: misaligned x_ref", what);
+    }
+    if (N > 0) {
+        if ((rc = check_workers(reinterpret_cast<const void* const*>(packed), P, 1, what))) return rc;
+        if (!d_mM || !out || !aligned(d_mM, 4) || !aligned(out, elem_size(out_dt)) || (d_sum && !aligned(d_sum, 4)))
+            return fail(GA_EINVAL, "%s: null or misaligned pointer", what);
+    } else if (!x_ref) {
+        return GA_OK;
+    }
+    const int64_t plen = part_elems > 0 ? part_elems : std::max<int64_t>(N, 1);
+    const int64_t nbytes = (N * b + 7) / 8;
+    int vec_ok = aligned(out, 16) && (!d_sum || aligned(d_sum, 16)) && (!x_ref || aligned(x_ref, 16));
+    PtrTable t{};
+    for (int i = 0; i < P && N > 0; i++) {
+        t.p[i] = const_cast<uint8_t*>(packed[i]);
+        vec_ok &= aligned(packed[i], 4);
+    }
+    const int64_t spans = ceil_div(ceil_div(N, 4), (int64_t)kThreads * kAUnits);
+    const int64_t nblk = std::max<int64_t>(1, std::min<int64_t>(kADBlocks, spans));
+    const int levels = h_table ? g : (1 << b) - 1;
+    const int pow2 = (P & (P - 1)) == 0;
+    double* ws = static_cast<double*>(d_ws);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+#define GA_AD(B, TB)                                                                                  \
+    do {                                                                                              \
+        if (out_dt == GA_F32)                                                                         \
+            hipLaunchKernelGGL((agg_dequant_kernel<B, TB, GA_F32>), dim3((unsigned)nblk), dim3(kThreads), 0, hs, \
+                               t, P, N, nbytes, d_sum, plen, d_mM, levels, pow2, (float)P, 1.0f / (float)P, \
+                               out, x_ref, ws, vec_ok, tab);                                          \
+        else                                                                                          \
+            hipLaunchKernelGGL((agg_dequant_kernel<B, TB, GA_BF16>), dim3((unsigned)nblk), dim3(kThreads), 0, hs, \
+                               t, P, N, nbytes, d_sum, plen, d_mM, levels, pow2, (float)P, 1.0f / (float)P, \
+                               out, x_ref, ws, vec_ok, tab);                                          \
+    } while (0)
+#define GA_ADB(TB)                           \
+    switch (b) {                             \
+        case 1: GA_AD(1, TB); break;         \
+        case 2: GA_AD(2, TB); break;         \
+        case 4: GA_AD(4, TB); break;         \
+        default: GA_AD(8, TB); break;        \
+    }
+    if (h_table) { GA_ADB(true) } else { GA_ADB(false) }
+#undef GA_ADB
+#undef GA_AD
+    if ((rc = check_launch(what))) return rc;
+    if (x_ref) {
+        hipLaunchKernelGGL(nmse_final_kernel, dim3(1), dim3(kThreads), 0, hs, ws, (int)nblk, d_nmse);
+        return check_launch(what);
+    }
+    return GA_OK;
 }
 
 extern "C" size_t thc_nmse_ws_bytes(int64_t N) {

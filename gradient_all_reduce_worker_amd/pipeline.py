@@ -96,9 +96,12 @@ class Pipeline:
     rht: Dict[str, tuple] = {}
 
     def __init__(self, name: str, device="cuda", cap_bytes: int = 64 << 20, zero_copy: bool = True,
-                 ring_mode: int = ga.RING_FUSED):
+                 ring_mode: int = ga.RING_FUSED, fused_tail: bool = True):
         self.w = synth.workload(name)
         self.zero_copy = zero_copy
+        # THC's integer sum, dequant and NMSE in one pass (thc_aggregate_dequant)
+        # or as the three separate calls
+        self.fused_tail = fused_tail
         self.ring_mode = ring_mode
         self.device = torch.device(device)
         self.cap = cap_bytes
@@ -198,6 +201,8 @@ class Pipeline:
                 self.xhat[k] = torch.empty(self.N, dtype=self.tdt, device=dev)
                 self.nmse[k] = torch.empty(3, dtype=torch.float64, device=dev)
             self.ws = torch.empty(ga.thc_nmse_ws_bytes(self.N), dtype=torch.uint8, device=dev)
+            self.ws_ad = torch.empty(ga.thc_aggregate_dequant_ws_bytes(self.N), dtype=torch.uint8,
+                                     device=dev)
         torch.cuda.synchronize()
 
     # ------------------------------------------------------------ step
@@ -248,53 +253,50 @@ class Pipeline:
               w.ring_part_elems, self.ring_mode)
         for b in w.ef_bits:
             k = f"ef{b}"
-            _call(timer, f"thc_int_aggregate_{k}", ga.thc_int_aggregate, self.packed[k], self.N, b,
-                  self.S[k])
-            _call(timer, f"thc_dequant_{k}", ga.thc_dequant, self.S[k], self.N, self.P, b,
-                  self.mM_ef[k], part, self.tdt, self.xhat[k])
-            _call(timer, f"thc_nmse_{k}", ga.thc_nmse, self.flat[0], self.xhat[k], self.nmse[k],
-                  self.ws)
+            self._tail(timer, k, self.packed[k], b, self.mM_ef[k], part)
         if self.dropped and w.thc_bits:
             b = w.thc_bits[0]
-            k = f"part{b}"
-            _call(timer, f"thc_int_aggregate_{k}", ga.thc_int_aggregate,
-                  [self.packed[b][i] for i in self.arrived], self.N, b, self.S[k])
-            _call(timer, f"thc_dequant_{k}", ga.thc_dequant, self.S[k], self.N, len(self.arrived),
-                  b, self.mM, part, self.tdt, self.xhat[k])
-            _call(timer, f"thc_nmse_{k}", ga.thc_nmse, self.flat[0], self.xhat[k], self.nmse[k],
-                  self.ws)
+            self._tail(timer, f"part{b}", [self.packed[b][i] for i in self.arrived], b, self.mM, part)
         for key, (b, g, d, T) in self.rht.items():
             Np = self.rht_avg[key].numel()
-            _call(timer, f"thc_nuhc_aggregate_{key}", ga.thc_nuhc_aggregate, self.packed[key], Np, b,
-                  g, T, self.S[key])
-            _call(timer, f"thc_nuhc_dequant_{key}", ga.thc_nuhc_dequant, self.S[key], Np, self.P, g,
-                  self.rht_mM[key], d, torch.float32, self.rht_avg[key])
+            self._tail(timer, key, self.packed[key], b, self.rht_mM[key], d, g=g, table=T, n=Np,
+                       out=self.rht_avg[key], nmse=False)
             _call(timer, f"thc_rht_inverse_{key}", ga.thc_rht_inverse, self.rht_avg[key], self.N, d,
                   w.rht_seed, self.tdt, self.xhat[key])
             _call(timer, f"thc_nmse_{key}", ga.thc_nmse, self.flat[0], self.xhat[key], self.nmse[key],
                   self.ws)
         for k, (b, g, T) in self.nu_tables.items():
-            _call(timer, f"thc_nuhc_aggregate_{k}", ga.thc_nuhc_aggregate, self.packed[k], self.N, b,
-                  g, T, self.S[k])
-            _call(timer, f"thc_nuhc_dequant_{k}", ga.thc_nuhc_dequant, self.S[k], self.N, self.P, g,
-                  self.mM, part, self.tdt, self.xhat[k])
-            _call(timer, f"thc_nmse_{k}", ga.thc_nmse, self.flat[0], self.xhat[k], self.nmse[k],
-                  self.ws)
+            self._tail(timer, k, self.packed[k], b, self.mM, part, g=g, table=T)
         for b in w.thc_bits:
-            _call(timer, f"thc_int_aggregate_b{b}", ga.thc_int_aggregate, self.packed[b], self.N, b,
-                  self.S[b])
-            _call(timer, f"thc_dequant_b{b}", ga.thc_dequant, self.S[b], self.N, self.P, b, self.mM,
-                  part, self.tdt, self.xhat[b])
-            _call(timer, f"thc_nmse_b{b}", ga.thc_nmse, self.flat[0], self.xhat[b], self.nmse[b],
-                  self.ws)
+            self._tail(timer, f"b{b}", self.packed[b], b, self.mM, part, sum_key=b)
         for b in w.global_bits:
             k = f"g{b}"
-            _call(timer, f"thc_int_aggregate_{k}", ga.thc_int_aggregate, self.packed[k], self.N, b,
-                  self.S[k])
-            _call(timer, f"thc_dequant_{k}", ga.thc_dequant, self.S[k], self.N, self.P, b, self.mM_g,
-                  0, self.tdt, self.xhat[k])
-            _call(timer, f"thc_nmse_{k}", ga.thc_nmse, self.flat[0], self.xhat[k], self.nmse[k],
-                  self.ws)
+            self._tail(timer, k, self.packed[k], b, self.mM_g, 0)
+
+    def _tail(self, timer, key, packed, b, mM, part, g=0, table=None, n=None, out=None, nmse=True,
+              sum_key=None):
+        """Server sum, dequantized average and NMSE of one THC pass: one fused
+        call, or thc_(nuhc_)aggregate, thc_(nuhc_)dequant and thc_nmse."""
+        n = self.N if n is None else n
+        sk = key if sum_key is None else sum_key
+        out = self.xhat[sk] if out is None else out
+        odt = out.dtype
+        nP = len(packed)
+        if self.fused_tail:
+            _call(timer, f"thc_aggregate_dequant_{key}", ga.thc_aggregate_dequant, packed, n, b, mM,
+                  part, odt, g, table, self.flat[0] if nmse else None, True, out, self.S[sk],
+                  self.nmse[sk] if nmse else None, self.ws_ad if nmse else None)
+            return
+        if table is None:
+            _call(timer, f"thc_int_aggregate_{key}", ga.thc_int_aggregate, packed, n, b, self.S[sk])
+            _call(timer, f"thc_dequant_{key}", ga.thc_dequant, self.S[sk], n, nP, b, mM, part, odt, out)
+        else:
+            _call(timer, f"thc_nuhc_aggregate_{key}", ga.thc_nuhc_aggregate, packed, n, b, g, table,
+                  self.S[sk])
+            _call(timer, f"thc_nuhc_dequant_{key}", ga.thc_nuhc_dequant, self.S[sk], n, nP, g, mM, part,
+                  odt, out)
+        if nmse:
+            _call(timer, f"thc_nmse_{key}", ga.thc_nmse, self.flat[0], out, self.nmse[sk], self.ws)
 
     # ------------------------------------------------------------ accounting
     def stage_bytes(self) -> Dict[str, float]:
@@ -352,6 +354,23 @@ class Pipeline:
             out[f"thc_nuhc_dequant_{k}"] = 8.0 * Np
             out[f"thc_rht_inverse_{k}"] = 4.0 * Np + N * s
             out[f"thc_nmse_{k}"] = 2.0 * N * s
+        # the fused tail: packed indices in, sums and estimate out, the
+        # exact average read for the NMSE
+        def fused(nP, n, b, s_out, nmse):
+            return nP * n * b / 8.0 + 4.0 * n + n * s_out + (n * s if nmse else 0.0)
+        for b in w.thc_bits:
+            out[f"thc_aggregate_dequant_b{b}"] = fused(P, N, b, s, True)
+        for b in w.global_bits:
+            out[f"thc_aggregate_dequant_g{b}"] = fused(P, N, b, s, True)
+        for k, (b, g, _) in self.nu_tables.items():
+            out[f"thc_aggregate_dequant_{k}"] = fused(P, N, b, s, True)
+        for b in w.ef_bits:
+            out[f"thc_aggregate_dequant_ef{b}"] = fused(P, N, b, s, True)
+        if self.dropped and w.thc_bits:
+            b = w.thc_bits[0]
+            out[f"thc_aggregate_dequant_part{b}"] = fused(len(self.arrived), N, b, s, True)
+        for k, (b, g, d, _) in self.rht.items():
+            out[f"thc_aggregate_dequant_{k}"] = fused(P, ga.rht_padded(N, d), b, 4.0, False)
         return out
 
     # ------------------------------------------------------------ sampling

@@ -8,6 +8,7 @@
  *                                                  single or bidirectional)
  *   ga_fusion_ring_plan / ga_fusion_ring_allreduce zero-copy fusion ring
  *   thc_minmax / thc_usq_quantize / thc_int_aggregate / thc_dequant / thc_nmse
+ *   thc_aggregate_dequant (aggregate + dequant + NMSE in one pass)
  *                                                  THC uniform quantization
  *   thc_nuhc_quantize / thc_nuhc_aggregate / thc_nuhc_dequant
  *                                                  THC with lookup tables
@@ -317,6 +318,31 @@ size_t thc_nmse_ws_bytes(int64_t N);
  * Tables are host arrays (n int32), validated on every call; g above 4095
  * returns GA_ENOTSUP.
  */
+
+/*
+ * thc_aggregate_dequant -- THC's last three steps in one pass ([THC]
+ * Algorithm 1 server sum and worker decoding; Algorithm 2 with a table;
+ * the NMSE of section 2): S = sum_i z_i (h_table NULL) or sum_i T[z_i]
+ * (h_table, g), x_hat = the dequantized average (as thc_dequant /
+ * thc_nuhc_dequant with the same part_elems and d_mM), and, with x_ref,
+ * the NMSE of x_hat against x_ref (as thc_nmse).
+ *   packed   P device buffers as written by the quantizer (N indices each)
+ *   d_sum    device int32[N], or NULL: S is then not stored
+ *   out      device, N elements of out_dt (x_hat)
+ *   x_ref    device, N elements of out_dt (the exact average), or NULL: no
+ *            NMSE, and d_nmse / d_ws are ignored
+ *   d_nmse   device double[3]: sum (x - x_hat)^2, sum x^2, their ratio
+ *   d_ws     device workspace of thc_aggregate_dequant_ws_bytes(N) bytes
+ * S and x_hat are bit-identical to the separate calls; the NMSE sums may
+ * differ from thc_nmse's in their last bits (another summation order).
+ * Errors as thc_int_aggregate, thc_dequant and thc_nmse.
+ */
+ga_status thc_aggregate_dequant(const uint8_t* const* packed, int32_t P, int64_t N, int32_t b,
+                                int32_t g, const int32_t* h_table, int64_t part_elems,
+                                const float* d_mM, int32_t* d_sum, void* out, ga_dtype out_dt,
+                                const void* x_ref, double* d_nmse, void* d_ws, size_t ws_bytes,
+                                void* stream);
+size_t thc_aggregate_dequant_ws_bytes(int64_t N);
 
 /*
  * thc_nuhc_quantize -- as thc_usq_quantize, but each coordinate is rounded

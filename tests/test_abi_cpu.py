@@ -27,7 +27,7 @@ def _declared():
 def test_header_declarations_are_exported():
     L = nat.load()
     names = _declared()
-    assert len(names) == 24
+    assert len(names) == 26
     assert set(names) == set(nat.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -215,6 +215,31 @@ def test_rht_quantize_argument_errors_before_enqueue():
     assert call(g=4, tab=bad) == EINVAL and call(g=2, tab=T) == EINVAL
     assert b"thc_rht_quantize" in L.ga_last_error()
     assert call(N=0) == 0 and call(N=0, d=1 << 14) == 0                        # empty: nothing to do
+
+
+def test_aggregate_dequant_argument_errors_before_enqueue():
+    L = nat.load()
+    good = _ptrs([0x10000 * (i + 1) for i in range(4)])
+    T = (C.c_int32 * 4)(0, 1, 3, 4)
+    bad = (C.c_int32 * 4)(0, 3, 3, 4)
+    f = L.thc_aggregate_dequant
+    ws = L.thc_aggregate_dequant_ws_bytes(1000)
+    assert ws >= 16
+
+    def call(P=4, N=16, b=2, g=0, tab=None, part=0, mM=0x50000, S=0x60000, out=0x70000, dt=0,
+             x=None, nm=None, w=None, wsb=0):
+        return f(good, P, N, b, g, tab, part, mM, S, out, dt, x, nm, w, wsb, None)
+    for b in (0, 3, 16):
+        assert call(b=b) == EINVAL
+    assert call(P=0) == EINVAL and call(P=65) == EINVAL and call(N=-1) == EINVAL
+    assert call(part=-1) == EINVAL and call(dt=2) == EINVAL
+    assert call(g=4, tab=bad) == EINVAL and call(g=2, tab=T) == EINVAL
+    assert call(mM=0) == EINVAL and call(out=0) == EINVAL and call(S=0x60002) == EINVAL
+    assert call(x=0x80000) == EINVAL                                           # NMSE without outputs
+    assert call(x=0x80000, nm=0x90000, w=0xA0000, wsb=ws - 8) == EINVAL        # workspace too small
+    assert call(x=0x80002, nm=0x90000, w=0xA0000, wsb=ws) == EINVAL            # misaligned x_ref
+    assert b"thc_aggregate_dequant" in L.ga_last_error()
+    assert call(N=0) == 0                                                      # nothing to do
 
 def _ftable(sizes):
     h = np.zeros(len(sizes), dtype=nat.FTENSOR_DTYPE)
