@@ -851,11 +851,23 @@ __global__ __launch_bounds__(kThreads) void nmse_partial_kernel(const void* x, c
 
 __global__ __launch_bounds__(kThreads) void nmse_final_kernel(const double* ws, int nblk,
                                                               double* out) {
-    double num = 0.0, den = 0.0;
-    for (int i = threadIdx.x; i < nblk; i += kThreads) {
-        num += ws[2 * i];
-        den += ws[2 * i + 1];
+    // four independent partial sums per thread keep four loads in flight
+    // (tens of thousands of partials from the fused pass); fixed order
+    double n4[4] = {0.0, 0.0, 0.0, 0.0}, d4[4] = {0.0, 0.0, 0.0, 0.0};
+    int i = threadIdx.x;
+    for (; i + 3 * kThreads < nblk; i += 4 * kThreads) {
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            n4[k] += ws[2 * (i + k * kThreads)];
+            d4[k] += ws[2 * (i + k * kThreads) + 1];
+        }
     }
+    for (int k = 0; i < nblk; i += kThreads, k = (k + 1) & 3) {
+        n4[k] += ws[2 * i];
+        d4[k] += ws[2 * i + 1];
+    }
+    double num = (n4[0] + n4[1]) + (n4[2] + n4[3]);
+    double den = (d4[0] + d4[1]) + (d4[2] + d4[3]);
     __shared__ double sh[kThreads / 64];
     num = block_sum(num, sh);
     den = block_sum(den, sh);
