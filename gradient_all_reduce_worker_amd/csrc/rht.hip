@@ -98,14 +98,23 @@ constexpr int group_step() { return WB >= 4 ? (1 << WB) + (1 << (WB - 4)) : 1; }
 
 template <int WB, int LO, int HI>
 __device__ __forceinline__ void group16(float* s) {
-    float* p = s + pad(group_base<WB>(threadIdx.x));
-    constexpr int step = group_step<WB>();
+    const int base = group_base<WB>(threadIdx.x);
     float v[16];
+    if (WB == 0 || WB >= 4) {                     // a constant distance in the padded tile
+        float* p = s + pad(base);
+        constexpr int step = group_step<WB>();
 #pragma unroll
-    for (int r = 0; r < 16; r++) v[r] = p[r * step];
-    butterflies<WB, LO, HI>(v);
+        for (int r = 0; r < 16; r++) v[r] = p[r * step];
+        butterflies<WB, LO, HI>(v);
 #pragma unroll
-    for (int r = 0; r < 16; r++) p[r * step] = v[r];
+        for (int r = 0; r < 16; r++) p[r * step] = v[r];
+    } else {                                      // the 16 coordinates cross padding words
+#pragma unroll
+        for (int r = 0; r < 16; r++) v[r] = s[pad(base + (r << WB))];
+        butterflies<WB, LO, HI>(v);
+#pragma unroll
+        for (int r = 0; r < 16; r++) s[pad(base + (r << WB))] = v[r];
+    }
 }
 
 // Stages on index bits LO .. HI-1, four at a time, a barrier after each group.
