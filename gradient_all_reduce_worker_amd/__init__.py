@@ -17,5 +17,5 @@ from ._native import (  # noqa: F401
     thc_usq_quantize, upload_table, thc_nuhc_quantize, thc_nuhc_aggregate, thc_nuhc_dequant,
     center_table, RING_DUAL, FTENSOR_DTYPE, FusionRing, ga_fusion_ring_plan, rht_padded,
     thc_rht_sumsq, thc_rht_range, thc_rht_forward, thc_rht_inverse, thc_rht_quantize,
-    thc_aggregate_dequant, thc_aggregate_dequant_ws_bytes,
+    thc_aggregate_dequant, thc_aggregate_dequant_ws_bytes, thc_rht_norm_quantize,
 )

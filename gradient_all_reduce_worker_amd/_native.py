@@ -29,6 +29,7 @@ EXPORTS = (
     "thc_rht_sumsq", "thc_rht_range", "thc_rht_forward", "thc_rht_inverse",
     "ga_fusion_ring_plan", "ga_fusion_ring_allreduce", "thc_ef_minmax", "thc_ef_quantize",
     "thc_rht_quantize", "thc_aggregate_dequant", "thc_aggregate_dequant_ws_bytes",
+    "thc_rht_norm_quantize", "thc_rht_norm_quantize_ws_bytes",
 )
 
 
@@ -99,11 +100,17 @@ def load() -> C.CDLL:
     L.thc_aggregate_dequant.argtypes = [C.POINTER(vp), i32, i64, i32, i32, C.POINTER(i32), i64, vp, vp,
                                         vp, i32, vp, vp, vp, C.c_size_t, vp]
     L.thc_aggregate_dequant_ws_bytes.argtypes = [i64]
+    L.thc_rht_norm_quantize.argtypes = [C.POINTER(vp), i32, i32, i64, i32, i64, u64, C.c_double, i32,
+                                        i32, C.POINTER(i32), u64, vp, vp, C.POINTER(vp), vp, C.c_size_t,
+                                        C.POINTER(vp), vp]
+    L.thc_rht_norm_quantize_ws_bytes.argtypes = [i32, i64, i64]
+    L.thc_rht_norm_quantize_ws_bytes.restype = C.c_size_t
     L.thc_aggregate_dequant_ws_bytes.restype = C.c_size_t
     L.ga_last_error.argtypes = []
     L.ga_last_error.restype = C.c_char_p
     for name in EXPORTS:
-        if name not in ("thc_nmse_ws_bytes", "ga_last_error", "thc_aggregate_dequant_ws_bytes"):
+        if name not in ("thc_nmse_ws_bytes", "ga_last_error", "thc_aggregate_dequant_ws_bytes",
+                        "thc_rht_norm_quantize_ws_bytes"):
             getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -555,6 +562,36 @@ def thc_rht_quantize(bufs: Sequence[torch.Tensor], d: int, rht_seed: int, mM: to
                                    _ptr_array(y_scratch, "y_scratch") if y_scratch is not None else None,
                                    _ptr_array(packed, "packed"), _stream(stream)))
     return packed
+
+
+def thc_rht_norm_quantize(bufs: Sequence[torch.Tensor], d: int, rht_seed: int, t_p: float, b: int,
+                          q_seed: int, worker0: int = 0, g: int = 0, table=None,
+                          sumsq: Optional[torch.Tensor] = None, mM: Optional[torch.Tensor] = None,
+                          y_scratch: Optional[Sequence[torch.Tensor]] = None,
+                          ws: Optional[torch.Tensor] = None,
+                          packed: Optional[Sequence[torch.Tensor]] = None, stream=None):
+    """Block norms, range and the quantized truncated transform in one call;
+    returns (packed, mM, sumsq or None)."""
+    N = bufs[0].numel()
+    dev = bufs[0].device
+    Np = rht_padded(N, d)
+    nblk = max(Np // d, 1)
+    if mM is None:
+        mM = torch.empty((nblk, 2), dtype=torch.float32, device=dev)
+    if packed is None:
+        packed = [torch.empty(max(packed_bytes(Np, b), 1), dtype=torch.uint8, device=dev) for _ in bufs]
+    if y_scratch is None and d > 8192 and N > 0:
+        y_scratch = [torch.empty(Np, dtype=torch.float32, device=dev) for _ in bufs]
+    if ws is None:
+        ws = torch.empty(max(load().thc_rht_norm_quantize_ws_bytes(len(bufs), N, d), 8),
+                         dtype=torch.uint8, device=dev)
+    _check(load().thc_rht_norm_quantize(
+        _ptr_array(bufs, "buffer"), len(bufs), worker0, N, _dt(bufs[0]), d, rht_seed, float(t_p), b, g,
+        _table_arg(table) if table is not None else None, q_seed,
+        _dev(sumsq, "sumsq") if sumsq is not None else None, _dev(mM, "mM"),
+        _ptr_array(y_scratch, "y_scratch") if y_scratch is not None else None,
+        _dev(ws, "ws"), ws.numel(), _ptr_array(packed, "packed"), _stream(stream)))
+    return packed, mM, sumsq
 
 
 def thc_rht_inverse(y: torch.Tensor, N: int, d: int, seed: int, out_dtype=torch.float32,

@@ -445,7 +445,7 @@ __global__ __launch_bounds__(kTT) void rht_tile_quant_kernel(PtrTable x, PtrTabl
 template <ga_dtype DT>
 __device__ __forceinline__ void forward_tile_body(float* s, uint32_t* words, const void* x, float* y,
                                                   int64_t tile, int64_t N, bool vec, uint32_t k0,
-                                                  uint32_t k1) {
+                                                  uint32_t k1, double* norm = nullptr) {
     const int64_t e0 = tile * kTile;
     const int nx = (int)max((int64_t)0, min((int64_t)kTile, N - e0));
     const int i0 = 16 * threadIdx.x;
@@ -478,6 +478,23 @@ __device__ __forceinline__ void forward_tile_body(float* s, uint32_t* words, con
     } else {
 #pragma unroll
         for (int r = 0; r < 16; r++) v[r] = i0 + r < nx ? load_tile<true, DT>(x, e0, i0 + r) : 0.0f;
+    }
+    if (norm) {
+        // the tile's sum of squares of x (binary64, exact squares; a fixed
+        // tree over the workgroup), for the block norms
+        double acc = 0.0;
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc += (double)v[r] * (double)v[r];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+        __shared__ double sh[kTT / 64];
+        if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = acc;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            double t = 0.0;
+            for (int q = 0; q < kTT / 64; q++) t += sh[q];
+            *norm = t;
+        }
     }
     __syncthreads();                                  // the sign words
     const uint32_t sw = words[4 * (i0 >> 7) + ((i0 >> 5) & 3)] >> (i0 & 31);
@@ -580,7 +597,8 @@ __global__ __launch_bounds__(kTT) void rht_quant_pipe_kernel(PtrTable x, PtrTabl
                                                              int64_t b0, int64_t nb, uint32_t k0,
                                                              uint32_t k1, float c,
                                                              const float* __restrict__ mM,
-                                                             uint32_t q0, uint32_t q1, TableArg tab) {
+                                                             uint32_t q0, uint32_t q1, TableArg tab,
+                                                             int P, double* norms) {
     constexpr int L = (1 << B) - 1;
     constexpr int kAux = TABLE ? kMaxGranularity : 4 * (kTile / 128);
     __shared__ float s[kLds];
@@ -598,12 +616,22 @@ __global__ __launch_bounds__(kTT) void rht_quant_pipe_kernel(PtrTable x, PtrTabl
         j = i - both + min(nA, nB);
     }
     const int64_t unit = (first ? a0 : b0) + (j >> gbits);
-    const int w = (int)(unit / nblk);
-    const int64_t b = unit - (int64_t)w * nblk;
+    // units worker-major (w nblk + b), or block-major (b P + w) when the
+    // first pass also sums the squares of the tiles (norms: per unit, G
+    // partial sums; a chunk then holds every worker of its blocks)
+    int w;
+    int64_t b;
+    if (norms) {
+        b = unit / P;
+        w = (int)(unit - b * P);
+    } else {
+        w = (int)(unit / nblk);
+        b = unit - (int64_t)w * nblk;
+    }
     const int r = (int)(j & ((1 << gbits) - 1));
     if (first) {
         forward_tile_body<DT>(s, aux, x.p[w], static_cast<float*>(y.p[w]), (b << gbits) + r, N,
-                              vec != 0, k0, k1);
+                              vec != 0, k0, k1, norms ? norms + (unit << gbits) + r : nullptr);
     } else {
         const Rounder<TABLE> rd = make_rounder<TABLE, kTT>(tab, L, aux);
         cross_quant_dispatch<B, TABLE>(s, rd, static_cast<const float*>(y.p[w]),
@@ -661,6 +689,31 @@ __global__ __launch_bounds__(kThreads) void rht_range_kernel(const double* sumsq
     const float M = (float)(t_p * sqrt(mx) / sqrt(d));
     mM[2 * p] = -M;
     mM[2 * p + 1] = M;
+}
+
+// Blocks b0 .. b0+nb-1 of the block-major pipeline: every worker's sum of
+// squares from its G tile partials (in tile order), then the block's range
+// as rht_range_kernel. One workgroup per block, one thread per worker.
+__global__ __launch_bounds__(64) void rht_norms_range_kernel(const double* norms, int P, int G,
+                                                             int64_t b0, int64_t nblk, double d,
+                                                             double t_p, double* sumsq, float* mM) {
+    const int64_t b = b0 + blockIdx.x;
+    __shared__ double nw[GA_MAX_WORKERS];
+    for (int w = threadIdx.x; w < P; w += 64) {
+        const double* pw = norms + ((b * P + w) * G);
+        double t = 0.0;
+        for (int q = 0; q < G; q++) t += pw[q];
+        nw[w] = t;
+        if (sumsq) sumsq[(int64_t)w * nblk + b] = t;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double mx = 0.0;
+        for (int i = 0; i < P; i++) mx = fmax(mx, nw[i]);
+        const float M = (float)(t_p * sqrt(mx) / sqrt(d));
+        mM[2 * b] = -M;
+        mM[2 * b + 1] = M;
+    }
 }
 
 int log2_block(int64_t d) {
@@ -865,6 +918,7 @@ extern "C" ga_status thc_rht_quantize(const void* const* bufs, int32_t P, int32_
     }
     // chunks of kPipeUnits blocks: launch k runs the first pass of chunk k
     // and the second of chunk k - 1
+    double* const none_d = nullptr;
     const int64_t nblk = Np / d, units = (int64_t)P * nblk;
     const int64_t U = min(units, kPipeUnits);
     const int64_t nchunk = ceil_div(units, U);
@@ -877,10 +931,10 @@ extern "C" ga_status thc_rht_quantize(const void* const* bufs, int32_t P, int32_
         do {                                                                                            \
             if (tb) hipLaunchKernelGGL((rht_quant_pipe_kernel<DT, B, true>), grid, dim3(kTT), 0, hs, tx, \
                                        ty, tp, worker0, N, vec, dbits, nblk, a0, na, b0, nb, k0, k1, c, d_mM, \
-                                       q0, q1, tab);                                                    \
+                                       q0, q1, tab, P, none_d);                                         \
             else hipLaunchKernelGGL((rht_quant_pipe_kernel<DT, B, false>), grid, dim3(kTT), 0, hs, tx,  \
                                     ty, tp, worker0, N, vec, dbits, nblk, a0, na, b0, nb, k0, k1, c, d_mM,   \
-                                    q0, q1, tab);                                                       \
+                                    q0, q1, tab, P, none_d);                                            \
         } while (0)
 #define GA_PQB(DT)                               \
         switch (b) {                             \
@@ -893,6 +947,110 @@ extern "C" ga_status thc_rht_quantize(const void* const* bufs, int32_t P, int32_
 #undef GA_PQB
 #undef GA_PQ
         if ((rc = check_launch(what))) return rc;
+    }
+    return GA_OK;
+}
+
+extern "C" size_t thc_rht_norm_quantize_ws_bytes(int32_t P, int64_t N, int64_t d) {
+    const int dbits = log2_block(d);
+    if (dbits < 0 || P < 1 || N <= 0) return 0;
+    const int64_t nblk = ceil_div(N, d);
+    const int64_t per_block = dbits > kTileBits ? ((int64_t)1 << (dbits - kTileBits)) : 1;
+    return (size_t)P * (size_t)nblk * (size_t)per_block * sizeof(double);
+}
+
+extern "C" ga_status thc_rht_norm_quantize(const void* const* bufs, int32_t P, int32_t worker0, int64_t N,
+                                           ga_dtype dt, int64_t d, uint64_t rht_seed, double t_p,
+                                           int32_t b, int32_t g, const int32_t* h_table, uint64_t q_seed,
+                                           double* d_sumsq, float* d_mM, float* const* y_scratch,
+                                           void* d_ws, size_t ws_bytes, uint8_t* const* packed,
+                                           void* stream) {
+    const char* what = "thc_rht_norm_quantize";
+    if (!valid_dtype(dt)) return fail(GA_EINVAL, "%s: unknown dtype %d", what, (int)dt);
+    const int dbits = log2_block(d);
+    if (dbits < 0) return fail(GA_EINVAL, "%s: d = %lld is not a power of two in [2, 2^22]", what, (long long)d);
+    if (!valid_bits(b)) return fail(GA_EINVAL, "%s: b = %d is not 1, 2, 4 or 8", what, b);
+    if (N < 0 || worker0 < 0) return fail(GA_EINVAL, "%s: negative argument", what);
+    if (P < 1 || P > GA_MAX_WORKERS) return fail(GA_EINVAL, "%s: P = %d outside [1, %d]", what, P, GA_MAX_WORKERS);
+    if (!(t_p > 0.0) || !std::isfinite(t_p)) return fail(GA_EINVAL, "%s: bad t_p", what);
+    TableArg tab{};
+    ga_status rc;
+    if (h_table && (rc = load_table(b, g, h_table, &tab, what))) return rc;
+    if (N == 0) return GA_OK;
+    if ((rc = check_workers(bufs, P, elem_size(dt), what))) return rc;
+    if ((rc = check_workers(reinterpret_cast<const void* const*>(packed), P, 16, what))) return rc;
+    if (!d_mM || !aligned(d_mM, 8)) return fail(GA_EINVAL, "%s: bad range pointer", what);
+    if (d_sumsq && !aligned(d_sumsq, 8)) return fail(GA_EINVAL, "%s: misaligned sums", what);
+    if (!d_ws || !aligned(d_ws, 8) || ws_bytes < thc_rht_norm_quantize_ws_bytes(P, N, d))
+        return fail(GA_EINVAL, "%s: workspace missing or below %zu bytes", what,
+                    thc_rht_norm_quantize_ws_bytes(P, N, d));
+    const int64_t nblk = ceil_div(N, d);
+    if (nblk > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: too many blocks", what);
+    double* ws = static_cast<double*>(d_ws);
+    if (dbits <= kTileBits) {
+        // one pass quantizes as it transforms, so the norms come first
+        double* sums = d_sumsq ? d_sumsq : ws;
+        if ((rc = thc_rht_sumsq(bufs, P, N, dt, d, sums, stream))) return rc;
+        if ((rc = thc_rht_range(sums, P, nblk, d, t_p, d_mM, stream))) return rc;
+        return thc_rht_quantize(bufs, P, worker0, N, dt, d, rht_seed, d_mM, b, g, h_table, q_seed, nullptr,
+                                packed, stream);
+    }
+    if (!y_scratch) return fail(GA_EINVAL, "%s: d > %d needs the scratch vectors", what, kTile);
+    if ((rc = check_workers(reinterpret_cast<const void* const*>(y_scratch), P, 4, what))) return rc;
+    const int64_t Np = nblk * d;
+    PtrTable tx{}, ty{}, tp{};
+    int vec = 1;
+    for (int i = 0; i < P; i++) {
+        tx.p[i] = const_cast<void*>(bufs[i]);
+        tp.p[i] = packed[i];
+        ty.p[i] = y_scratch[i];
+        vec &= aligned(bufs[i], 16);
+    }
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const uint32_t k0 = (uint32_t)rht_seed, k1 = (uint32_t)(rht_seed >> 32);
+    const uint32_t q0 = (uint32_t)q_seed, q1 = (uint32_t)(q_seed >> 32);
+    const float c = inv_sqrt_d(d);
+    const bool tb = h_table != nullptr;
+    const int gbits = dbits - kTileBits;
+    // block-major units (every worker of a block in one chunk): launch k
+    // runs the first pass of chunk k (with the tiles' sums of squares) and
+    // the second pass of chunk k - 1, whose ranges the kernel launched
+    // after launch k - 1 derived from those sums
+    const int64_t units = (int64_t)P * nblk;
+    const int64_t bpc = std::max<int64_t>(1, kPipeUnits / P);          // blocks per chunk
+    const int64_t U = std::min(units, bpc * P);
+    const int64_t nchunk = ceil_div(units, U);
+    if ((units << gbits) > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: too many tiles", what);
+    (void)Np;
+    for (int64_t k = 0; k <= nchunk; k++) {
+        const int64_t a0 = k * U, na = k < nchunk ? std::min(U, units - a0) : 0;
+        const int64_t b0 = (k - 1) * U, nb = k > 0 ? std::min(U, units - b0) : 0;
+        const dim3 grid((unsigned)((na + nb) << gbits));
+#define GA_NQ(DT, B)                                                                                    \
+        do {                                                                                            \
+            if (tb) hipLaunchKernelGGL((rht_quant_pipe_kernel<DT, B, true>), grid, dim3(kTT), 0, hs, tx, \
+                                       ty, tp, worker0, N, vec, dbits, nblk, a0, na, b0, nb, k0, k1, c, d_mM, \
+                                       q0, q1, tab, P, ws);                                             \
+            else hipLaunchKernelGGL((rht_quant_pipe_kernel<DT, B, false>), grid, dim3(kTT), 0, hs, tx,  \
+                                    ty, tp, worker0, N, vec, dbits, nblk, a0, na, b0, nb, k0, k1, c, d_mM, \
+                                    q0, q1, tab, P, ws);                                                \
+        } while (0)
+#define GA_NQB(DT)                               \
+        switch (b) {                             \
+            case 1: GA_NQ(DT, 1); break;         \
+            case 2: GA_NQ(DT, 2); break;         \
+            case 4: GA_NQ(DT, 4); break;         \
+            default: GA_NQ(DT, 8); break;        \
+        }
+        if (dt == GA_F32) { GA_NQB(GA_F32) } else { GA_NQB(GA_BF16) }
+#undef GA_NQB
+#undef GA_NQ
+        if ((rc = check_launch(what))) return rc;
+        if (na > 0) {                                   // the chunk's blocks: a0 / P .. (a0 + na) / P - 1
+            hipLaunchKernelGGL(rht_norms_range_kernel, dim3((unsigned)(na / P)), dim3(64), 0, hs, ws, P,
+                               1 << gbits, a0 / P, nblk, (double)d, t_p, d_sumsq, d_mM);
+            if ((rc = check_launch(what))) return rc;
+        }
     }
     return GA_OK;
 }

@@ -166,12 +166,15 @@ class Pipeline:
             # are the transform's blocks
             self.rht = {f"rht{b}g{g}d{k}": (b, g, 1 << k, ga.center_table(b, g))
                         for b, g, k in w.rht}
-            self.rht_y, self.rht_sumsq, self.rht_mM, self.rht_avg = {}, {}, {}, {}
+            self.rht_y, self.rht_sumsq, self.rht_mM, self.rht_avg, self.rht_ws = {}, {}, {}, {}, {}
             for key, (b, g, d, _) in self.rht.items():
                 Np = ga.rht_padded(self.N, d)
                 # scratch of the transform's first pass (blocks above 8192)
                 self.rht_y[key] = worker_buffers(self.P, Np, torch.float32, dev) if d > 8192 else None
                 self.rht_sumsq[key] = torch.empty((self.P, Np // d), dtype=torch.float64, device=dev)
+                self.rht_ws[key] = torch.empty(
+                    max(ga.load().thc_rht_norm_quantize_ws_bytes(self.P, self.N, d), 8),
+                    dtype=torch.uint8, device=dev)
                 self.rht_mM[key] = torch.empty((Np // d, 2), dtype=torch.float32, device=dev)
                 self.packed[key] = [torch.empty(ga.packed_bytes(Np, b), dtype=torch.uint8,
                                                 device=dev) for _ in range(self.P)]
@@ -238,11 +241,9 @@ class Pipeline:
                   w.quant_seed, part, 0, self.packed[k])
         tp = t_p(w.rht_p)
         for key, (b, g, d, T) in self.rht.items():
-            _call(timer, f"thc_rht_sumsq_{key}", ga.thc_rht_sumsq, self.flat, d, self.rht_sumsq[key])
-            _call(timer, f"thc_rht_range_{key}", ga.thc_rht_range, self.rht_sumsq[key], d, tp,
-                  self.rht_mM[key])
-            _call(timer, f"thc_rht_quantize_{key}", ga.thc_rht_quantize, self.flat, d, w.rht_seed,
-                  self.rht_mM[key], b, w.quant_seed, 0, g, T, self.rht_y[key], self.packed[key])
+            _call(timer, f"thc_rht_norm_quantize_{key}", ga.thc_rht_norm_quantize, self.flat, d,
+                  w.rht_seed, tp, b, w.quant_seed, 0, g, T, self.rht_sumsq[key], self.rht_mM[key],
+                  self.rht_y[key], self.rht_ws[key], self.packed[key])
         for b in w.ef_bits:
             k = f"ef{b}"
             _call(timer, f"thc_ef_minmax_{k}", ga.thc_ef_minmax, self.flat, self.err[k], part,
@@ -347,6 +348,7 @@ class Pipeline:
         for k, (b, g, d, _) in self.rht.items():
             Np = ga.rht_padded(N, d)
             nblk = Np // d
+            out[f"thc_rht_norm_quantize_{k}"] = P * N * s + P * Np * b / 8.0 + 16.0 * P * nblk
             out[f"thc_rht_sumsq_{k}"] = P * N * s + 8.0 * P * nblk
             out[f"thc_rht_range_{k}"] = 8.0 * P * nblk + 8.0 * nblk
             out[f"thc_rht_quantize_{k}"] = P * N * s + P * Np * b / 8.0

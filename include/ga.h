@@ -14,7 +14,7 @@
  *                                                  THC with lookup tables
  *   thc_ef_minmax / thc_ef_quantize                error feedback
  *   thc_rht_sumsq / thc_rht_range / thc_rht_forward / thc_rht_inverse /
- *   thc_rht_quantize
+ *   thc_rht_quantize / thc_rht_norm_quantize
  *                                                  randomized Hadamard
  *                                                  transform, norm-based
  *                                                  range, truncation
@@ -485,6 +485,28 @@ ga_status thc_rht_quantize(const void* const* bufs, int32_t P, int32_t worker0, 
                            ga_dtype dt, int64_t d, uint64_t rht_seed, const float* d_mM,
                            int32_t b, int32_t g, const int32_t* h_table, uint64_t q_seed,
                            float* const* y_scratch, uint8_t* const* packed, void* stream);
+
+/*
+ * thc_rht_norm_quantize -- the block norms, the norm-based range and the
+ * truncated transform quantized, in one call ([THC] section 5 on top of
+ * sections 3 and 4): as thc_rht_sumsq, thc_rht_range (t_p) and
+ * thc_rht_quantize in sequence, with the same bits for d_mM and the packed
+ * indices (the norms are binary64 sums of exact squares, summed in another
+ * order: within 1e-12 relative of thc_rht_sumsq's). For d > 8192 the
+ * norms come from the first pass of the transform, which reads x anyway.
+ *   d_sumsq  device double[P][Np/d] (worker-major) or NULL
+ *   d_mM     device, receives Np/d pairs (-M_p, M_p)
+ *   y_scratch as thc_rht_quantize (needed when d > 8192)
+ *   d_ws     device workspace of thc_rht_norm_quantize_ws_bytes(P, N, d)
+ *            bytes (8-byte aligned)
+ * Errors as thc_rht_sumsq, thc_rht_range and thc_rht_quantize.
+ */
+ga_status thc_rht_norm_quantize(const void* const* bufs, int32_t P, int32_t worker0, int64_t N,
+                                ga_dtype dt, int64_t d, uint64_t rht_seed, double t_p, int32_t b,
+                                int32_t g, const int32_t* h_table, uint64_t q_seed, double* d_sumsq,
+                                float* d_mM, float* const* y_scratch, void* d_ws, size_t ws_bytes,
+                                uint8_t* const* packed, void* stream);
+size_t thc_rht_norm_quantize_ws_bytes(int32_t P, int64_t N, int64_t d);
 
 /*
  * thc_rht_inverse -- out = RHT^-1(y) for one vector: y holds Np binary32

@@ -27,7 +27,7 @@ def _declared():
 def test_header_declarations_are_exported():
     L = nat.load()
     names = _declared()
-    assert len(names) == 26
+    assert len(names) == 28
     assert set(names) == set(nat.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -240,6 +240,26 @@ def test_aggregate_dequant_argument_errors_before_enqueue():
     assert call(x=0x80002, nm=0x90000, w=0xA0000, wsb=ws) == EINVAL            # misaligned x_ref
     assert b"thc_aggregate_dequant" in L.ga_last_error()
     assert call(N=0) == 0                                                      # nothing to do
+
+
+def test_rht_norm_quantize_argument_errors_before_enqueue():
+    L = nat.load()
+    good = _ptrs([0x10000 * (i + 1) for i in range(4)])
+    f = L.thc_rht_norm_quantize
+    ws = L.thc_rht_norm_quantize_ws_bytes(4, 1 << 15, 1 << 14)
+    assert ws == 4 * 2 * 2 * 8                         # P x blocks x tiles per block doubles
+    assert L.thc_rht_norm_quantize_ws_bytes(4, 100, 8) == 4 * 13 * 8
+
+    def call(P=4, N=16, dt=0, d=8, tp=2.0, b=2, g=0, tab=None, mM=0x50000, y=None, w=0x60000,
+             wsb=4096, pk=good):
+        return f(good, P, 0, N, dt, d, 1, tp, b, g, tab, 2, None, mM, y, w, wsb, pk, None)
+    for tp in (0.0, -1.0, float("nan"), float("inf")):
+        assert call(tp=tp) == EINVAL
+    assert call(d=3) == EINVAL and call(b=3) == EINVAL and call(P=0) == EINVAL and call(dt=2) == EINVAL
+    assert call(mM=0) == EINVAL and call(w=0) == EINVAL and call(wsb=8) == EINVAL
+    assert call(d=1 << 14, N=1 << 15, wsb=ws) == EINVAL                         # no scratch
+    assert b"thc_rht_norm_quantize" in L.ga_last_error()
+    assert call(N=0) == 0
 
 def _ftable(sizes):
     h = np.zeros(len(sizes), dtype=nat.FTENSOR_DTYPE)

@@ -265,3 +265,42 @@ def test_rht_quantize_max_workers(table):
         want = (oracle.nuhc_quantize(yc, i, d, mMw, b, g, T, 31) if table
                 else oracle.usq_quantize(yc, i, d, mMw, b, 31))
         assert np.array_equal(pk[i].cpu().numpy(), want), i
+
+
+NSHAPES = [(2, 8, 1001), (3, 4096, 3 * 4096 + 5), (2, 1 << 14, (1 << 14) + 77),
+           (3, 1 << 14, 30 * (1 << 14) - 5), (2, 1 << 20, (1 << 20) + 999), (64, 1 << 14, 3 * (1 << 14) - 9)]
+
+
+@pytest.mark.parametrize("dt", [ga.F32, ga.BF16])
+@pytest.mark.parametrize("b,g,table", [(4, 0, None), (4, 36, "center"), (2, 0, None)])
+@pytest.mark.parametrize("P,d,N", NSHAPES)
+def test_rht_norm_quantize_matches_three_calls(P, d, N, b, g, table, dt):
+    """Norms, range and transform-and-quantize in one call against
+    thc_rht_sumsq + thc_rht_range + thc_rht_quantize (range and indices bit
+    for bit, sums within 1e-12) and against the oracle."""
+    bufs = _inputs(P, N, dt, seed=5 * N + d + b)
+    xs = [_host(t) for t in bufs]
+    if table == "center":
+        table = ga.center_table(b, g)
+    t_p = statistics.NormalDist().inv_cdf(1 - 1 / 32)
+    Np = ga.rht_padded(N, d)
+    S1 = ga.thc_rht_sumsq(bufs, d)
+    mM1 = ga.thc_rht_range(S1, d, t_p)
+    pk1 = ga.thc_rht_quantize(bufs, d, SEED, mM1, b, 17, worker0=3, g=g, table=table)
+    S2 = torch.empty_like(S1)
+    pk2, mM2, _ = ga.thc_rht_norm_quantize(bufs, d, SEED, t_p, b, 17, worker0=3, g=g, table=table,
+                                           sumsq=S2)
+    np.testing.assert_allclose(S2.cpu().numpy(), S1.cpu().numpy(), rtol=1e-12, atol=0)
+    assert np.array_equal(_bits(mM2.cpu().numpy()), _bits(mM1.cpu().numpy()))
+    nbytes = ga.packed_bytes(Np, b)
+    Sw = np.stack([oracle.rht_sumsq(x, d) for x in xs])
+    mMw = oracle.rht_range(Sw, d, t_p)
+    assert np.array_equal(_bits(mM2.cpu().numpy()), _bits(mMw))
+    for i in range(P):
+        got = pk2[i].cpu().numpy()[:nbytes]
+        assert np.array_equal(got, pk1[i].cpu().numpy()[:nbytes]), i
+        if i < 4:
+            yc = oracle.clamp(oracle.rht_forward(xs[i], d, SEED), d, mMw)
+            want = (oracle.nuhc_quantize(yc, 3 + i, d, mMw, b, g, table, 17) if table is not None
+                    else oracle.usq_quantize(yc, 3 + i, d, mMw, b, 17))
+            assert np.array_equal(got, want), i
