@@ -22,19 +22,47 @@ __device__ __forceinline__ Grid grid_of(const float* mM, int64_t p, int L) {
     return {m, range == 0.0f ? 0.0f : (float)L / range};
 }
 
+// floor(x) as an int32 in one instruction (the compiler splits it in two
+// when subnormals are kept; the arguments below are never subnormal).
+__device__ __forceinline__ int floor_i32(float x) {
+    int r;
+    asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+    return r;
+}
+
 // Stochastic rounding of one value to its grid index, binary32 throughout
 // (a >= m, so the position u on the grid is >= 0; with s = 0 the index is
 // 0). The rule is: z0 = min(floor(u), L - 1), f = u - z0, go up when
 // 2 r + 1 < f 2^17 for the 16-bit uniform r. Computed here in fewer
-// instructions with the same result for every finite input:
-//  - u is first clamped to L; u >= L gives index L either way (f >= 1 and
-//    every r goes up, or f = 0 at z0 = L and none does), and below L the
-//    clamp changes nothing, so z0 = trunc(u) and f = fract(u) (exact);
-//  - 2 r + 1 < f 2^17  <=>  r < f 2^16 - 1/2, where f 2^16 is exact and so
-//    is the subtraction whenever the right side is >= 0 (otherwise both
-//    sides are false), so one fused multiply-add gives it exactly.
+// instructions with the same result for every finite input in [m, M]:
+//  - u is first clamped to [0, L]; u >= L gives index L either way (f >= 1
+//    and every r goes up, or f = 0 at z0 = L and none does), and inside the
+//    range the clamp changes nothing;
+//  - with t = (2 r + 1) 2^-17 (exact), going up is t < f, so
+//    z = ceil(u - t) = -floor(t - u): if f > t, u - t lies in
+//    (floor u, floor u + 1); if f <= t, in (floor u - 1, floor u].
+//    t - u is exact when L < 128: for u >= 1 both are multiples of
+//    ulp(u) <= 2^-17 and |t - u| < u; for u < 1 and u >= t likewise; for
+//    u < t the rounded difference stays in (0, 1), whose floor is 0 as it
+//    should be. It is never subnormal (0, or at least 2^-41 in magnitude).
+//  - for L >= 128 (b = 8) t - u can round across an integer, so the
+//    decision is made as r < f 2^16 - 1/2 (f 2^16 is exact and so is the
+//    subtraction whenever the right side is >= 0), z = trunc(u) + up.
+// usq_neg_index returns -z mod 2^32 (L < 128), for packers that add the
+// negated indices and negate once per group.
+__device__ __forceinline__ float usq_position(float a, Grid g, int L) {
+    return __builtin_amdgcn_fmed3f((a - g.m) * g.s, 0.0f, (float)L);
+}
+
+__device__ __forceinline__ uint32_t usq_neg_index(float a, Grid g, int L, uint32_t r16) {
+    const float u = usq_position(a, g, L);
+    const float t = __builtin_fmaf((float)r16, 0x1p-16f, 0x1p-17f);
+    return (uint32_t)floor_i32(t - u);
+}
+
 __device__ __forceinline__ uint32_t usq_index(float a, Grid g, int L, uint32_t r16) {
-    const float u = fminf((a - g.m) * g.s, (float)L);
+    if (L < 128) return 0u - usq_neg_index(a, g, L, r16);
+    const float u = usq_position(a, g, L);
     const float f = __builtin_amdgcn_fractf(u);
     const bool up = (float)r16 < __builtin_fmaf(f, 65536.0f, -0.5f);
     return (uint32_t)u + (up ? 1u : 0u);
@@ -57,6 +85,18 @@ __device__ __forceinline__ uint64_t pack_group(const uint32_t* z) {
 #pragma unroll
     for (int i = 6; i >= 0; i--) acc = (acc << B) | z[i];
     return acc;
+}
+
+// The same from the negated indices w[i] = -z[i] mod 2^32 (B <= 4): the
+// Horner sum of the w is -(the packed word) mod 2^32.
+template <int B>
+__device__ __forceinline__ uint32_t pack_neg_group(const uint32_t* w) {
+    static_assert(B <= 4, "8 b-bit indices fit one word");
+    uint32_t acc = w[7];
+#pragma unroll
+    for (int i = 6; i >= 0; i--) acc = (acc << B) + w[i];
+    asm("" : "+v"(acc));        // keeps the one negation from being spread over the terms
+    return 0u - acc;
 }
 
 template <int B>

@@ -278,6 +278,7 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_fast_kernel(PtrTable bu
                                                                      uint32_t k0, uint32_t k1,
                                                                      TableArg tab) {
     constexpr int L = (1 << B) - 1;
+    constexpr bool NEG = !TABLE && L < 128;            // negated-index rounding
     __shared__ uint32_t cells[TABLE ? kMaxGranularity : 1];
     const Rounder<TABLE> rd = make_rounder<TABLE>(tab, L, cells);
     const int slot = blockIdx.y;
@@ -307,15 +308,21 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_fast_kernel(PtrTable bu
     for (int j = 0; j < kFGroups; j++) {
         const int64_t g = e_blk / 8 + (int64_t)j * kThreads + threadIdx.x;
         const Philox4 r = philox4x32_10((uint32_t)g, (uint32_t)((uint64_t)g >> 32), wid, 0u, k0, k1);
-        uint32_t z[8];
+        uint32_t z[8];                                  // NEG: -index mod 2^32
         float res[8];
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             float v;
-            z[i] = rd.index_v(a[j][i], gb, uniform16(r, i), &v);
+            if (NEG) {
+                z[i] = usq_neg_index(a[j][i], gb, L, uniform16(r, i));
+                v = -(float)(int)z[i];
+            } else {
+                z[i] = rd.index_v(a[j][i], gb, uniform16(r, i), &v);
+            }
             if (EF) res[i] = a[j][i] - ef_value(q, v);
         }
-        store_group<B>(out, g, pack_group<B>(z));
+        if constexpr (NEG) store_group<B>(out, g, pack_neg_group<B>(z));
+        else store_group<B>(out, g, pack_group<B>(z));
         if (EF) store_err_group(err, g, res);
     }
 }
@@ -357,6 +364,8 @@ __device__ __forceinline__ void lane_span(float (&a)[2][4], const Rounder<TABLE>
     // words of the uniforms of this lane's two half-groups
     const uint32_t u[2][2] = {{odd ? ra : r.v[0], odd ? rb : r.v[1]},
                               {odd ? r.v[2] : ra, odd ? r.v[3] : rb}};
+    constexpr int L = (1 << B) - 1;
+    constexpr bool NEG = !TABLE && L < 128;            // negated-index rounding
 #pragma unroll
     for (int h = 0; h < 2; h++) {
         uint32_t bits = 0;
@@ -365,8 +374,18 @@ __device__ __forceinline__ void lane_span(float (&a)[2][4], const Rounder<TABLE>
         for (int i = 0; i < 4; i++) {
             const uint32_t r16 = (u[h][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
             float v;
-            bits |= rd.index_v(a[h][i], gb, r16, &v) << (i * B);
+            if (NEG) {
+                const uint32_t w = usq_neg_index(a[h][i], gb, L, r16);
+                v = -(float)(int)w;
+                bits += w << (i * B);
+            } else {
+                bits |= rd.index_v(a[h][i], gb, r16, &v) << (i * B);
+            }
             if (EF) res[i] = a[h][i] - ef_value(q, v);
+        }
+        if (NEG) {
+            asm("" : "+v"(bits));   // one negation, not one per term
+            bits = 0u - bits;
         }
         const int64_t vv = v0 + h * 256;
         if (B == 8) {
