@@ -234,6 +234,64 @@ def test_usq_quantize_misaligned_and_flat_partition():
         assert np.array_equal(packed[i].cpu().numpy(), want)
 
 
+def _threshold_values(seed, worker, N, part, L, rng):
+    """fp32 values on the grid m = 0, M = L (so s = 1 and u = a exactly) that
+    sit on, just above and just below each element's own rounding threshold
+    k + (2 r + 1) 2^-17, plus integers and random points; every partition
+    starts with 0 and L so that its grid is exactly [0, L]."""
+    kmax = min(L, 127)                        # k + t exact in binary32
+    a = np.empty(N, dtype=np.float32)
+    for e in range(N):
+        r = oracle.uniform16(seed, worker, e)
+        k = e % kmax
+        kind = e % 5
+        tie = np.float32(k + (2 * r + 1) / 2.0 ** 17)
+        if kind == 0:
+            a[e] = tie
+        elif kind == 1:
+            a[e] = np.nextafter(tie, np.float32(np.inf))
+        elif kind == 2:
+            a[e] = np.nextafter(tie, np.float32(-np.inf))
+        elif kind == 3:
+            a[e] = k
+        else:
+            a[e] = rng.uniform(0, L)
+    plen = part if part > 0 else N
+    for p0 in range(0, N, plen):
+        a[p0] = 0.0
+        if p0 + 1 < N:
+            a[p0 + 1] = L
+    return a
+
+
+@pytest.mark.parametrize("b", [1, 2, 4, 8])
+@pytest.mark.parametrize("P,N,part", [(3, 70001, 0), (2, 8192 * 4 + 77, 8192)])
+def test_usq_quantize_on_thresholds(P, N, part, b):
+    """Coordinates exactly on the up/down threshold stay down (the rule is a
+    strict 2 r + 1 < f 2^17); one ulp above goes up, one below stays."""
+    L = (1 << b) - 1
+    seed, worker0 = 0x1234ABCD5678EF01 + b, 3
+    rng = np.random.default_rng(b)
+    xs = [_threshold_values(seed, worker0 + i, N, part, L, rng) for i in range(P)]
+    bufs = [torch.from_numpy(x).to(DEV) for x in xs]
+    mM = ga.thc_minmax(bufs, part)
+    mM_h = mM.cpu().numpy()
+    assert np.all(mM_h[:, 0] == 0.0) and np.all(mM_h[:, 1] == L)
+    packed = ga.thc_usq_quantize(bufs, mM, b, seed, part_elems=part, worker0=worker0)
+    for i in range(P):
+        want = oracle.usq_quantize(xs[i], worker0 + i, part, mM_h, b, seed)
+        z = oracle.unpack_indices(want, N, b)
+        e = np.arange(N)
+        k = e % min(L, 127)
+        inner = e >= 2                         # past the grid ends of the first partition
+        if part:
+            inner &= (e % part) >= 2
+        for kind, up in ((0, 0), (1, 1), (2, 0), (3, 0)):   # tie, above, below, integer
+            sel = inner & (e % 5 == kind)
+            assert np.all(z[sel] == k[sel] + up), kind
+        assert np.array_equal(packed[i].cpu().numpy(), want), i
+
+
 @pytest.mark.parametrize("b", [1, 2, 4, 8])
 @pytest.mark.parametrize("P,N", [(1, 1), (1, 1000), (3, 33), (8, 70001), (33, 4099), (64, 100003)])
 def test_int_aggregate(P, N, b):
