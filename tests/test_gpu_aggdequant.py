@@ -29,7 +29,8 @@ def _host(t):
 
 
 SHAPES = [(1, 1, 0), (2, 17, 0), (3, 1001, 100), (4, 4096 * 3 + 5, 4096), (8, 70001, 0),
-          (5, 20000, 1000), (16, 1 << 18, 1 << 16), (64, 9999, 0), (8, 4096 * 40, 4096 * 8)]
+          (5, 20000, 1000), (16, 1 << 18, 1 << 16), (64, 9999, 0), (8, 4096 * 40, 4096 * 8),
+          (33, 2048 * 5 + 3, 0), (20, 8192 * 3, 8192)]
 MODES = [(1, 0, None), (2, 0, None), (4, 0, None), (8, 0, None), (2, 8, (0, 3, 5, 8)),
          (4, 36, "center"), (8, 1000, "center")]
 
