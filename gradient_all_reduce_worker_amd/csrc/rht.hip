@@ -387,8 +387,8 @@ __global__ __launch_bounds__(kTT) void rht_tile_quant_kernel(PtrTable x, PtrTabl
     constexpr int L = (1 << B) - 1;
     __shared__ float s[kLds];
     __shared__ uint32_t words[4 * (kTile / 128)];
-    __shared__ uint32_t cells[TABLE ? kMaxGranularity : 1];
-    const Rounder<TABLE> rd = make_rounder<TABLE, kTT>(tab, L, cells);
+    extern __shared__ uint2 dyn_cells[];              // table cells (table_lds_bytes)
+    const Rounder<TABLE> rd = make_rounder<TABLE, kTT>(tab, L, dyn_cells);
     const int w = blockIdx.y;
     const int64_t e0 = (int64_t)blockIdx.x * kTile;
     const int n = (int)min((int64_t)kTile, Np - e0);
@@ -600,9 +600,10 @@ __global__ __launch_bounds__(kTT) void rht_quant_pipe_kernel(PtrTable x, PtrTabl
                                                              uint32_t q0, uint32_t q1, TableArg tab,
                                                              int P, double* norms) {
     constexpr int L = (1 << B) - 1;
-    constexpr int kAux = TABLE ? kMaxGranularity : 4 * (kTile / 128);
+    constexpr int kAux = 4 * (kTile / 128);
     __shared__ float s[kLds];
-    __shared__ uint32_t aux[kAux];                   // sign words (first pass) or table cells
+    __shared__ uint32_t aux[kAux];                   // sign words (first pass)
+    extern __shared__ uint2 dyn_cells[];              // table cells (second pass)
     const int gbits = dbits - kTileBits;
     const int64_t nA = na << gbits, nB = nb << gbits;
     const int64_t i = blockIdx.x, both = 2 * min(nA, nB);
@@ -633,7 +634,7 @@ __global__ __launch_bounds__(kTT) void rht_quant_pipe_kernel(PtrTable x, PtrTabl
         forward_tile_body<DT>(s, aux, x.p[w], static_cast<float*>(y.p[w]), (b << gbits) + r, N,
                               vec != 0, k0, k1, norms ? norms + (unit << gbits) + r : nullptr);
     } else {
-        const Rounder<TABLE> rd = make_rounder<TABLE, kTT>(tab, L, aux);
+        const Rounder<TABLE> rd = make_rounder<TABLE, kTT>(tab, L, dyn_cells);
         cross_quant_dispatch<B, TABLE>(s, rd, static_cast<const float*>(y.p[w]),
                                        static_cast<uint8_t*>(packed.p[w]), (uint32_t)(worker0 + w), b, r,
                                        dbits, c, mM, q0, q1);
@@ -899,7 +900,7 @@ extern "C" ga_status thc_rht_quantize(const void* const* bufs, int32_t P, int32_
     if (!two_pass) {
 #define GA_TQ(DT, B)                                                                                   \
         do {                                                                                           \
-            if (tb) hipLaunchKernelGGL((rht_tile_quant_kernel<DT, B, true>), g1, dim3(kTT), 0, hs, tx, tp, \
+            if (tb) hipLaunchKernelGGL((rht_tile_quant_kernel<DT, B, true>), g1, dim3(kTT), table_lds_bytes(tab), hs, tx, tp, \
                                        worker0, N, Np, dbits, k0, k1, c, d_mM, q0, q1, tab);          \
             else hipLaunchKernelGGL((rht_tile_quant_kernel<DT, B, false>), g1, dim3(kTT), 0, hs, tx, tp, \
                                     worker0, N, Np, dbits, k0, k1, c, d_mM, q0, q1, tab);             \
@@ -929,7 +930,7 @@ extern "C" ga_status thc_rht_quantize(const void* const* bufs, int32_t P, int32_
         const dim3 grid((unsigned)((na + nb) << (dbits - kTileBits)));
 #define GA_PQ(DT, B)                                                                                    \
         do {                                                                                            \
-            if (tb) hipLaunchKernelGGL((rht_quant_pipe_kernel<DT, B, true>), grid, dim3(kTT), 0, hs, tx, \
+            if (tb) hipLaunchKernelGGL((rht_quant_pipe_kernel<DT, B, true>), grid, dim3(kTT), table_lds_bytes(tab), hs, tx, \
                                        ty, tp, worker0, N, vec, dbits, nblk, a0, na, b0, nb, k0, k1, c, d_mM, \
                                        q0, q1, tab, P, none_d);                                         \
             else hipLaunchKernelGGL((rht_quant_pipe_kernel<DT, B, false>), grid, dim3(kTT), 0, hs, tx,  \
@@ -1028,7 +1029,7 @@ extern "C" ga_status thc_rht_norm_quantize(const void* const* bufs, int32_t P, i
         const dim3 grid((unsigned)((na + nb) << gbits));
 #define GA_NQ(DT, B)                                                                                    \
         do {                                                                                            \
-            if (tb) hipLaunchKernelGGL((rht_quant_pipe_kernel<DT, B, true>), grid, dim3(kTT), 0, hs, tx, \
+            if (tb) hipLaunchKernelGGL((rht_quant_pipe_kernel<DT, B, true>), grid, dim3(kTT), table_lds_bytes(tab), hs, tx, \
                                        ty, tp, worker0, N, vec, dbits, nblk, a0, na, b0, nb, k0, k1, c, d_mM, \
                                        q0, q1, tab, P, ws);                                             \
             else hipLaunchKernelGGL((rht_quant_pipe_kernel<DT, B, false>), grid, dim3(kTT), 0, hs, tx,  \

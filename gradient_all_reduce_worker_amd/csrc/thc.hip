@@ -279,8 +279,8 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_fast_kernel(PtrTable bu
                                                                      TableArg tab) {
     constexpr int L = (1 << B) - 1;
     constexpr bool NEG = !TABLE && L < 128;            // negated-index rounding
-    __shared__ uint32_t cells[TABLE ? kMaxGranularity : 1];
-    const Rounder<TABLE> rd = make_rounder<TABLE>(tab, L, cells);
+    extern __shared__ uint2 dyn_cells[];              // table cells (table_lds_bytes)
+    const Rounder<TABLE> rd = make_rounder<TABLE>(tab, L, dyn_cells);
     const int slot = blockIdx.y;
     const void* x = bufs.p[slot];
     float* err = EF ? static_cast<float*>(errs.p[slot]) : nullptr;
@@ -419,8 +419,8 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_lane_kernel(PtrTable bu
                                                                      uint32_t k0, uint32_t k1,
                                                                      TableArg tab) {
     constexpr int L = (1 << B) - 1;
-    __shared__ uint32_t cells[TABLE ? kMaxGranularity : 1];
-    const Rounder<TABLE> rd = make_rounder<TABLE>(tab, L, cells);
+    extern __shared__ uint2 dyn_cells[];              // table cells (table_lds_bytes)
+    const Rounder<TABLE> rd = make_rounder<TABLE>(tab, L, dyn_cells);
     const int slot = blockIdx.y;
     const uint4* x = static_cast<const uint4*>(bufs.p[slot]);
     uint4* err = EF ? static_cast<uint4*>(errs.p[slot]) : nullptr;
@@ -486,8 +486,8 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_kernel(PtrTable bufs, P
                                                                 int vec_ok, int64_t e_begin,
                                                                 TableArg tab) {
     constexpr int L = (1 << B) - 1;
-    __shared__ uint32_t cells[TABLE ? kMaxGranularity : 1];
-    const Rounder<TABLE> rd = make_rounder<TABLE>(tab, L, cells);
+    extern __shared__ uint2 dyn_cells[];              // table cells (table_lds_bytes)
+    const Rounder<TABLE> rd = make_rounder<TABLE>(tab, L, dyn_cells);
     const int slot = blockIdx.y;
     const void* x = bufs.p[slot];
     float* err = EF ? static_cast<float*>(errs.p[slot]) : nullptr;
@@ -1142,7 +1142,10 @@ ga_status quantize_impl(const void* const* bufs, int32_t P, int32_t worker0, int
     // the lane kernel streams best with at most six workgroups per CU; with
     // a table each workgroup builds its LDS cell map first, so it takes four
     // spans to spread that over
-    const size_t lane_lds = kLdsPerCu / 6 - 1024 - (table ? kMaxGranularity * 4 : 4);
+    // at most six resident lane workgroups per CU (the dynamic LDS also
+    // holds the table's cells)
+    const size_t cells_lds = table ? table_lds_bytes(*table) : 0;
+    const size_t lane_lds = std::max<size_t>(kLdsPerCu / 6 - 1024, cells_lds);
     const int lane_spans = table ? 4 : 1;
     // partitions of a power-of-two number of fast spans (or one partition):
     // the kernels find a span's partition by a shift
@@ -1166,11 +1169,11 @@ ga_status quantize_impl(const void* const* bufs, int32_t P, int32_t worker0, int
                                tab);                                                                  \
         else if (fast > 0)                                                                            \
             hipLaunchKernelGGL((usq_quantize_fast_kernel<DT, B, TB, EF>),                             \
-                               dim3((unsigned)fast, (unsigned)P), dim3(kThreads), 0, hs, tx, te, tp,  \
-                               worker0, plen, pshift, d_mM, k0, k1, tab);                             \
+                               dim3((unsigned)fast, (unsigned)P), dim3(kThreads), cells_lds, hs, tx,  \
+                               te, tp, worker0, plen, pshift, d_mM, k0, k1, tab);                     \
         if (blocks > 0)                                                                               \
             hipLaunchKernelGGL((usq_quantize_kernel<DT, B, TB, EF>),                                  \
-                               dim3((unsigned)blocks, (unsigned)P), dim3(kThreads), 0, hs,            \
+                               dim3((unsigned)blocks, (unsigned)P), dim3(kThreads), cells_lds, hs,    \
                                tx, te, tp, worker0, N, plen, d_mM, k0, k1, vec_ok, e_begin, tab);     \
     } while (0)
 #define GA_Q(DT, B, TB)                                \
