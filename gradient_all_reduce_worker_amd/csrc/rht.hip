@@ -46,8 +46,10 @@ constexpr int kTT = 512;                    // threads per transform workgroup
 constexpr int kPer = kTile / kTT;           // coordinates per thread (16)
 constexpr int kLds = kTile + kTile / 16;    // padded tile, in words
 constexpr int kMaxBits = 22;                // d <= 2^22: G <= 512, W >= 16
-// blocks per chunk of the pipelined two-pass transform-and-quantize
-constexpr int64_t kPipeUnits = 64;
+// blocks per chunk of the pipelined two-pass transform-and-quantize (32
+// workers x 138M fp32, d = 2^20: 64 -> 12.5 ms, 128 -> 12.1, 256 -> 12.0,
+// 512 -> 12.5; fewer launches against longer unpaired first and last ones)
+constexpr int64_t kPipeUnits = 256;
 constexpr int kSignWords = 4 * 512;         // Philox blocks a workgroup may need, x 4
 static_assert(kPer == 16, "one set of 16 coordinates per thread and group");
 constexpr uint32_t kSignDomain = 0x52485400u;

@@ -169,7 +169,8 @@ def test_full_rht_chain_matches_oracle(P, d, N, b):
 # schedule holds (64), so its launches mix both passes
 QSHAPES = [(2, 2, 7), (3, 2, 9), (2, 4, 13), (3, 8, 1001), (2, 128, 300), (4, 4096, 3 * 4096 + 5),
            (2, 8192, 2 * 8192 - 3), (2, 1 << 14, (1 << 14) + 77), (2, 1 << 16, 70000),
-           (2, 1 << 20, (1 << 20) + 999), (3, 1 << 14, 30 * (1 << 14) - 5)]
+           (2, 1 << 20, (1 << 20) + 999), (3, 1 << 14, 30 * (1 << 14) - 5),
+           (4, 1 << 14, 70 * (1 << 14) - 3)]          # 280 blocks: two pipeline chunks
 QMODES = [(1, 0, None), (2, 0, None), (4, 0, None), (8, 0, None),
           (2, 8, (0, 3, 5, 8)), (4, 36, "center"), (8, 1000, "center")]
 
@@ -268,7 +269,8 @@ def test_rht_quantize_max_workers(table):
 
 
 NSHAPES = [(2, 8, 1001), (3, 4096, 3 * 4096 + 5), (2, 1 << 14, (1 << 14) + 77),
-           (3, 1 << 14, 30 * (1 << 14) - 5), (2, 1 << 20, (1 << 20) + 999), (64, 1 << 14, 3 * (1 << 14) - 9)]
+           (3, 1 << 14, 30 * (1 << 14) - 5), (2, 1 << 20, (1 << 20) + 999), (64, 1 << 14, 3 * (1 << 14) - 9),
+           (8, 1 << 14, 40 * (1 << 14) - 9), (33, 1 << 14, 20 * (1 << 14) + 5)]   # 2 and 3 pipeline chunks
 
 
 @pytest.mark.parametrize("dt", [ga.F32, ga.BF16])
