@@ -1139,11 +1139,9 @@ ga_status quantize_impl(const void* const* bufs, int32_t P, int32_t worker0, int
     const int64_t fast = (vec_ok && (plen % span == 0 || plen >= N)) ? N / span : 0;
     const int64_t e_begin = fast * span;
     const int64_t blocks = ceil_div(N - e_begin, kQSpan);       // generic workgroups
-    // the lane kernel streams best with at most six workgroups per CU; with
-    // a table each workgroup builds its LDS cell map first, so it takes four
-    // spans to spread that over
-    // at most six resident lane workgroups per CU (the dynamic LDS also
-    // holds the table's cells)
+    // the lane kernel streams best with at most six workgroups per CU (the
+    // dynamic LDS also holds the table's cells); with a table each workgroup
+    // builds its LDS cell map first, so it takes four spans to spread that over
     const size_t cells_lds = table ? table_lds_bytes(*table) : 0;
     const size_t lane_lds = std::max<size_t>(kLdsPerCu / 6 - 1024, cells_lds);
     const int lane_spans = table ? 4 : 1;
