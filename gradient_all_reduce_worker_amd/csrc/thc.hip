@@ -559,9 +559,10 @@ constexpr int kAUnits = 4;
 
 template <int B>
 __device__ __forceinline__ uint32_t unit_bits(const uint8_t* src, int64_t u) {
-    if (B == 8) return reinterpret_cast<const uint32_t*>(src)[u];
-    if (B == 4) return reinterpret_cast<const uint16_t*>(src)[u];
-    if (B == 2) return src[u];
+    // read once: nontemporal (vgg16 b=4 fused pass 0.70 -> 0.67-0.68 ms)
+    if (B == 8) return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(src) + u);
+    if (B == 4) return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(src) + u);
+    if (B == 2) return __builtin_nontemporal_load(src + u);
     return (uint32_t)(src[u >> 1] >> (4 * (u & 1))) & 0xFu;
 }
 
