@@ -99,12 +99,27 @@ __device__ __forceinline__ uint32_t pack_neg_group(const uint32_t* w) {
     return 0u - acc;
 }
 
-template <int B>
+// Packed indices are written once. Where a store instruction covers whole
+// lines across the wave they go out nontemporal (32 x 138M fp32: b = 8
+// quantize 3.85 -> 3.46 ms, b = 4 3.38 -> 3.16 ms); where it covers pieces
+// of lines that other instructions or workgroups complete (NT = false),
+// through L2, which merges them (nontemporal there: RHT second pass +2%).
+template <int B, bool NT = true>
 __device__ __forceinline__ void store_group(uint8_t* out, int64_t g, uint64_t bits) {
-    if (B == 8) *reinterpret_cast<uint2*>(out + 8 * g) = make_uint2((uint32_t)bits, (uint32_t)(bits >> 32));
-    else if (B == 4) reinterpret_cast<uint32_t*>(out)[g] = (uint32_t)bits;
-    else if (B == 2) reinterpret_cast<uint16_t*>(out)[g] = (uint16_t)bits;
-    else out[g] = (uint8_t)bits;
+    if (!NT) {
+        if (B == 8) *reinterpret_cast<uint2*>(out + 8 * g) = make_uint2((uint32_t)bits, (uint32_t)(bits >> 32));
+        else if (B == 4) reinterpret_cast<uint32_t*>(out)[g] = (uint32_t)bits;
+        else if (B == 2) reinterpret_cast<uint16_t*>(out)[g] = (uint16_t)bits;
+        else out[g] = (uint8_t)bits;
+    } else if (B == 8) {
+        __builtin_nontemporal_store((unsigned long long)bits, reinterpret_cast<unsigned long long*>(out) + g);
+    } else if (B == 4) {
+        __builtin_nontemporal_store((uint32_t)bits, reinterpret_cast<uint32_t*>(out) + g);
+    } else if (B == 2) {
+        __builtin_nontemporal_store((uint16_t)bits, reinterpret_cast<uint16_t*>(out) + g);
+    } else {
+        __builtin_nontemporal_store((uint8_t)bits, out + g);
+    }
 }
 
 // Rounding rules. Uniform THC: index k stands for m + k (M - m) / L. Non-

@@ -562,7 +562,7 @@ __device__ __forceinline__ void cross_quant_body(float* s, const Rounder<TABLE>&
     for (int k = 0; k < kPer / 8; k++) {
         const int i0 = 8 * (threadIdx.x + k * kTT);
         const int64_t e = base + (int64_t)(i0 >> WBITS) * kTile + (i0 & (W - 1));
-        store_group<B>(out, e >> 3, round_group<B, TABLE>(s, i0, e, c, bg, rd, wid, q0, q1));
+        store_group<B, false>(out, e >> 3, round_group<B, TABLE>(s, i0, e, c, bg, rd, wid, q0, q1));
     }
 }
 

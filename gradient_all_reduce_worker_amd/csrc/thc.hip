@@ -388,12 +388,12 @@ __device__ __forceinline__ void lane_span(float (&a)[2][4], const Rounder<TABLE>
             bits = 0u - bits;
         }
         const int64_t vv = v0 + h * 256;
-        if (B == 8) {
-            reinterpret_cast<uint32_t*>(out)[vv] = bits;
+        if (B == 8) {                               // written once: nontemporal
+            __builtin_nontemporal_store(bits, reinterpret_cast<uint32_t*>(out) + vv);
         } else if (B == 4) {
-            reinterpret_cast<uint16_t*>(out)[vv] = (uint16_t)bits;
+            __builtin_nontemporal_store((uint16_t)bits, reinterpret_cast<uint16_t*>(out) + vv);
         } else if (B == 2) {
-            out[vv] = (uint8_t)bits;
+            __builtin_nontemporal_store((uint8_t)bits, out + vv);
         } else {                                    // two vectors per byte
             const uint32_t other = swap_pair(bits);
             if (!odd) out[vv >> 1] = (uint8_t)(bits | (other << 4));
