@@ -271,6 +271,9 @@ ga_status thc_minmax(const void* const* bufs, int32_t P, int64_t N, ga_dtype dt,
  *   b           1, 2, 4 or 8
  *   packed[P]   host array of device pointers, ceil(N b / 8) bytes each;
  *               bits past element N - 1 in the last byte are written 0
+ * Values are expected inside their partition's [m, M] (d_mM from
+ * thc_minmax over the same data). Any other value, NaN included, still
+ * gives an index in [0, 2^b - 1]: below m it is 0, above M it is 2^b - 1.
  */
 ga_status thc_usq_quantize(const void* const* bufs, int32_t P, int32_t worker0, int64_t N,
                            ga_dtype dt, int64_t part_elems, const float* d_mM, int32_t b,
@@ -350,7 +353,8 @@ size_t thc_aggregate_dequant_ws_bytes(int64_t N);
  * binary32 u = (a - m) (g / (M - m)); k = min(floor(u), g - 1); z0 = the
  * largest z with T[z] <= k; lo = T[z0], hi = T[z0 + 1];
  * f = (u - lo) / (hi - lo); z = z0 + [(2 r + 1) < f 2^17], with the same
- * 16-bit uniforms, keying and packing as thc_usq_quantize.
+ * 16-bit uniforms, keying and packing as thc_usq_quantize. A value outside
+ * [m, M] takes the first (or last) cell and still an index in [0, 2^b - 1].
  */
 ga_status thc_nuhc_quantize(const void* const* bufs, int32_t P, int32_t worker0, int64_t N,
                             ga_dtype dt, int64_t part_elems, const float* d_mM, int32_t b,

@@ -292,6 +292,37 @@ def test_usq_quantize_on_thresholds(P, N, part, b):
         assert np.array_equal(packed[i].cpu().numpy(), want), i
 
 
+@pytest.mark.parametrize("table", [False, True])
+@pytest.mark.parametrize("b", [1, 2, 4, 8])
+def test_quantize_outside_the_grid(b, table):
+    """A grid narrower than the data (not from thc_minmax): indices stay in
+    [0, 2^b - 1]; a value below m is sent as 0 and one above M as 2^b - 1,
+    i.e. as the oracle sends the value clipped to [m, M]; a NaN still gets a
+    valid index."""
+    N, m, M = 70001, -0.5, 0.5
+    x = np.random.default_rng(b).standard_normal(N).astype(np.float32)
+    x[5] = np.nan
+    mM = torch.tensor([[m, M]], dtype=torch.float32, device=DEV)
+    bufs = [torch.from_numpy(x).to(DEV)]
+    clipped = np.clip(np.nan_to_num(x, nan=m), np.float32(m), np.float32(M)).astype(np.float32)
+    mMh = mM.cpu().numpy()
+    if table:
+        g = max((1 << b) - 1, 36)
+        T = ga.center_table(b, g)
+        packed = ga.thc_nuhc_quantize(bufs, mM, b, g, T, 11)
+        want = oracle.nuhc_quantize(clipped, 0, 0, mMh, b, g, T, 11)
+    else:
+        packed = ga.thc_usq_quantize(bufs, mM, b, 11)
+        want = oracle.usq_quantize(clipped, 0, 0, mMh, b, 11)
+    z = oracle.unpack_indices(packed[0].cpu().numpy(), N, b)
+    zw = oracle.unpack_indices(want, N, b)
+    assert z.min() >= 0 and z.max() <= (1 << b) - 1
+    assert np.all(z[x < m] == 0) and np.all(z[x > M] == (1 << b) - 1)
+    ok = np.ones(N, dtype=bool)
+    ok[5] = False
+    assert np.array_equal(z[ok], zw[ok])
+
+
 @pytest.mark.parametrize("b", [1, 2, 4, 8])
 @pytest.mark.parametrize("P,N", [(1, 1), (1, 1000), (3, 33), (8, 70001), (33, 4099), (64, 100003)])
 def test_int_aggregate(P, N, b):
