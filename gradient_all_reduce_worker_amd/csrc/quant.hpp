@@ -156,8 +156,9 @@ struct Rounder {
             return z;
         }
         const float u = (a - gr.m) * gr.s;                      // position on <g+1>
-        // cell min(floor(u), g - 1) (u >= 0; a subnormal u floors to 0 either way)
-        const int k = min(max(floor_i32(u), 0), levels - 1);
+        // cell min(floor(u), g - 1), u clamped to [0, g - 1] first (same cell
+        // for every u >= 0; a value below m takes cell 0)
+        const int k = floor_i32(__builtin_amdgcn_fmed3f(u, 0.0f, (float)(levels - 1)));
         const uint2 c = cell[k];
         const float lo = __uint_as_float(c.x), den = __uint_as_float(c.y & ~0xFFu);
         // up <=> r < fl((u - lo) / den) 2^16 - 1/2 (as in usq_index's b = 8

@@ -184,9 +184,10 @@ __device__ __forceinline__ bool negated(const uint32_t* words, int blk, int e) {
     return (words[4 * blk + ((e >> 5) & 3)] >> (e & 31)) & 1u;
 }
 
+// v clamped to [m, M] (one median-of-three; the same value for every
+// finite v, as m <= M)
 __device__ __forceinline__ float clamp_to(float v, const float* mM, int64_t p) {
-    const float m = mM[2 * p], M = mM[2 * p + 1];
-    return v < m ? m : (v > M ? M : v);
+    return __builtin_amdgcn_fmed3f(v, mM[2 * p], mM[2 * p + 1]);
 }
 
 
@@ -348,8 +349,7 @@ __device__ __forceinline__ uint64_t round_group(const float* s, int i0, int64_t 
     uint32_t z[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-        float v = s[pad(i0 + i)] * c;
-        v = v < bg.m ? bg.m : (v > bg.M ? bg.M : v);
+        const float v = __builtin_amdgcn_fmed3f(s[pad(i0 + i)] * c, bg.m, bg.M);   // clamp
         z[i] = rd.index(v, bg.g, uniform16(r, i));
     }
     return pack_group<B>(z);
