@@ -129,10 +129,10 @@ __device__ __forceinline__ void store_group(uint8_t* out, int64_t g, uint64_t bi
 // per-workgroup LDS map cell[k] for every integer cell k in [0, g) gives the
 // neighbours of a position u in [k, k + 1): z0 = the largest z with
 // T[z] <= k, lo = T[z0] and den = T[z0 + 1] - T[z0], stored as the binary32
-// values lo and den with z0 in the low 8 bits of den (an integer <= 4095
-// leaves at least 11 low mantissa bits zero), so that one 8-byte LDS read
-// and two masks decode it. The cells live in dynamic LDS of
-// table_lds_bytes(g) bytes.
+// values lo, den (with z0 in its low 8 bits: an integer <= 4095 leaves at
+// least 11 low mantissa bits zero) and 1 / den correctly rounded, so that
+// one 16-byte LDS read and two masks decode it and no reciprocal is issued
+// per coordinate. The cells live in dynamic LDS of table_lds_bytes(g) bytes.
 constexpr int kMaxGranularity = 4095;
 
 struct TableArg {
@@ -141,12 +141,12 @@ struct TableArg {
     int n;             // 2^b
 };
 
-inline size_t table_lds_bytes(const TableArg& tab) { return (size_t)tab.g * sizeof(uint2); }
+inline size_t table_lds_bytes(const TableArg& tab) { return (size_t)tab.g * sizeof(uint4); }
 
 template <bool TABLE>
 struct Rounder {
     int levels;              // L for the uniform grid, g for a table
-    const uint2* cell;       // LDS cells (table only)
+    const uint4* cell;       // LDS cells (table only)
     // The index of a; *v receives the grid level it stands for (the index
     // itself, or its table value).
     __device__ __forceinline__ uint32_t index_v(float a, Grid gr, uint32_t r16, float* v) const {
@@ -159,18 +159,18 @@ struct Rounder {
         // cell min(floor(u), g - 1), u clamped to [0, g - 1] first (same cell
         // for every u >= 0; a value below m takes cell 0)
         const int k = floor_i32(__builtin_amdgcn_fmed3f(u, 0.0f, (float)(levels - 1)));
-        const uint2 c = cell[k];
+        const uint4 c = cell[k];
         const float lo = __uint_as_float(c.x), den = __uint_as_float(c.y & ~0xFFu);
         // up <=> r < fl((u - lo) / den) 2^16 - 1/2 (as in usq_index's b = 8
         // form), with a correctly rounded quotient. u - lo and den are exact
-        // (integers <= 4095 and u < 2^12). The hardware reciprocal gives the
-        // quotient within 2^-21 relative, i.e. the threshold within 0.04 of
-        // the exact one (|quotient| <= 1 + 2^-10); r is an integer, so when it
-        // lies more than 1/8 from the estimate the decision is already fixed.
-        // Only the rest (about one coordinate in 2.6 10^5) takes the divide.
+        // (integers <= 4095 and u < 2^12). num times the stored reciprocal
+        // gives the quotient within 2^-23 relative, i.e. the threshold within
+        // 0.01 of the exact one (|quotient| <= 1 + 2^-10); r is an integer, so
+        // when it lies more than 1/8 from the estimate the decision is already
+        // fixed. Only the rest (about one coordinate in 2.6 10^5) divides.
         const float num = u - lo;
         const float rf = (float)r16;
-        const float yq = __builtin_fmaf(num * __builtin_amdgcn_rcpf(den), 65536.0f, -0.5f);
+        const float yq = __builtin_fmaf(num * __uint_as_float(c.z), 65536.0f, -0.5f);
         bool up = rf < yq;
         if (!(fabsf(rf - yq) > 0.125f)) up = rf < __builtin_fmaf(num / den, 65536.0f, -0.5f);
         *v = up ? lo + den : lo;
@@ -185,7 +185,7 @@ struct Rounder {
 // Called by every thread of the workgroup (NT threads) before any early exit;
 // cells: the kernel's dynamic LDS (table_lds_bytes(g) bytes).
 template <bool TABLE, int NT = kThreads>
-__device__ __forceinline__ Rounder<TABLE> make_rounder(const TableArg& tab, int L, uint2* cells) {
+__device__ __forceinline__ Rounder<TABLE> make_rounder(const TableArg& tab, int L, uint4* cells) {
     if (!TABLE) return {L, nullptr};
     for (int k = threadIdx.x; k < tab.g; k += NT) {
         int lo = 0, hi = tab.n - 1;             // the largest z with T[z] <= k
@@ -194,7 +194,8 @@ __device__ __forceinline__ Rounder<TABLE> make_rounder(const TableArg& tab, int 
             if (tab.t[mid] <= k) lo = mid; else hi = mid - 1;
         }
         const float tl = (float)tab.t[lo], den = (float)(tab.t[lo + 1] - tab.t[lo]);
-        cells[k] = make_uint2(__float_as_uint(tl), __float_as_uint(den) | (uint32_t)lo);
+        cells[k] = make_uint4(__float_as_uint(tl), __float_as_uint(den) | (uint32_t)lo,
+                              __float_as_uint(1.0f / den), 0u);
     }
     __syncthreads();
     return {tab.g, cells};

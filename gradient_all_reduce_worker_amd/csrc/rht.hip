@@ -389,7 +389,7 @@ __global__ __launch_bounds__(kTT) void rht_tile_quant_kernel(PtrTable x, PtrTabl
     constexpr int L = (1 << B) - 1;
     __shared__ float s[kLds];
     __shared__ uint32_t words[4 * (kTile / 128)];
-    extern __shared__ uint2 dyn_cells[];              // table cells (table_lds_bytes)
+    extern __shared__ uint4 dyn_cells[];              // table cells (table_lds_bytes)
     const Rounder<TABLE> rd = make_rounder<TABLE, kTT>(tab, L, dyn_cells);
     const int w = blockIdx.y;
     const int64_t e0 = (int64_t)blockIdx.x * kTile;
@@ -605,7 +605,7 @@ __global__ __launch_bounds__(kTT) void rht_quant_pipe_kernel(PtrTable x, PtrTabl
     constexpr int kAux = 4 * (kTile / 128);
     __shared__ float s[kLds];
     __shared__ uint32_t aux[kAux];                   // sign words (first pass)
-    extern __shared__ uint2 dyn_cells[];              // table cells (second pass)
+    extern __shared__ uint4 dyn_cells[];              // table cells (second pass)
     const int gbits = dbits - kTileBits;
     const int64_t nA = na << gbits, nB = nb << gbits;
     const int64_t i = blockIdx.x, both = 2 * min(nA, nB);

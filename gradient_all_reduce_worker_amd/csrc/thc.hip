@@ -279,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_fast_kernel(PtrTable bu
                                                                      TableArg tab) {
     constexpr int L = (1 << B) - 1;
     constexpr bool NEG = !TABLE && L < 128;            // negated-index rounding
-    extern __shared__ uint2 dyn_cells[];              // table cells (table_lds_bytes)
+    extern __shared__ uint4 dyn_cells[];              // table cells (table_lds_bytes)
     const Rounder<TABLE> rd = make_rounder<TABLE>(tab, L, dyn_cells);
     const int slot = blockIdx.y;
     const void* x = bufs.p[slot];
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_lane_kernel(PtrTable bu
                                                                      uint32_t k0, uint32_t k1,
                                                                      TableArg tab) {
     constexpr int L = (1 << B) - 1;
-    extern __shared__ uint2 dyn_cells[];              // table cells (table_lds_bytes)
+    extern __shared__ uint4 dyn_cells[];              // table cells (table_lds_bytes)
     const Rounder<TABLE> rd = make_rounder<TABLE>(tab, L, dyn_cells);
     const int slot = blockIdx.y;
     const uint4* x = static_cast<const uint4*>(bufs.p[slot]);
@@ -486,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_kernel(PtrTable bufs, P
                                                                 int vec_ok, int64_t e_begin,
                                                                 TableArg tab) {
     constexpr int L = (1 << B) - 1;
-    extern __shared__ uint2 dyn_cells[];              // table cells (table_lds_bytes)
+    extern __shared__ uint4 dyn_cells[];              // table cells (table_lds_bytes)
     const Rounder<TABLE> rd = make_rounder<TABLE>(tab, L, dyn_cells);
     const int slot = blockIdx.y;
     const void* x = bufs.p[slot];
