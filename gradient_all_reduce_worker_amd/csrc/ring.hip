@@ -590,13 +590,13 @@ extern "C" ga_status ga_ring_allreduce_sim(void* const* bufs, int32_t P, int64_t
     {
         // every step sends one chunk per ring; the dual ring sends one
         // sub-chunk of ceil(n / 2P) in each direction
-        int64_t bytes = 0;
-        for (int64_t p0 = 0; p0 < N; p0 += plen) {
-            int64_t n = N - p0 < plen ? N - p0 : plen;
-            bytes += mode == GA_RING_DUAL
-                         ? 2 * 2 * (int64_t)(P - 1) * ceil_div(n, 2 * (int64_t)P) * (int64_t)es
-                         : 2 * (int64_t)(P - 1) * ceil_div(n, P) * (int64_t)es;
-        }
+        // whole partitions, then the short last one (closed form, no loop)
+        auto part_bytes = [&](int64_t n) {
+            return mode == GA_RING_DUAL
+                       ? 2 * 2 * (int64_t)(P - 1) * ceil_div(n, 2 * (int64_t)P) * (int64_t)es
+                       : 2 * (int64_t)(P - 1) * ceil_div(n, P) * (int64_t)es;
+        };
+        const int64_t bytes = (N / plen) * part_bytes(plen) + (N % plen ? part_bytes(N % plen) : 0);
         s.steps = N > 0 ? 2 * (int64_t)(P - 1) : 0;
         s.bytes_sent_per_worker = bytes;
         if (mode != GA_RING_STEPWISE)
@@ -714,11 +714,8 @@ extern "C" ga_status ga_fusion_ring_allreduce(const ga_fusion_tensor* d_tensors,
     if (fill > 0) {
         const int64_t plen = part_elems > 0 ? part_elems : fill;
         const int nch = mode == GA_RING_DUAL ? 2 * P : P;
-        int64_t bytes = 0;
-        for (int64_t p0 = 0; p0 < fill; p0 += plen) {
-            const int64_t n = fill - p0 < plen ? fill - p0 : plen;
-            bytes += 2 * (int64_t)(P - 1) * (nch / P) * ceil_div(n, nch) * es;
-        }
+        auto part_bytes = [&](int64_t n) { return 2 * (int64_t)(P - 1) * (nch / P) * ceil_div(n, nch) * es; };
+        const int64_t bytes = (fill / plen) * part_bytes(plen) + (fill % plen ? part_bytes(fill % plen) : 0);
         s.steps = 2 * (int64_t)(P - 1);
         s.bytes_sent_per_worker = bytes;
         s.hbm_bytes = P > 1 ? 2 * (int64_t)P * fill * es : 0;
