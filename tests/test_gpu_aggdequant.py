@@ -103,3 +103,24 @@ def test_empty_writes_zero_nmse():
     ga.thc_aggregate_dequant(packed, 0, 2, mM, x_ref=ref, nmse_out=nm)
     torch.cuda.synchronize()
     assert nm.cpu().numpy().tolist() == [0.0, 0.0, 0.0]
+
+
+@pytest.mark.parametrize("tdt", [torch.float32, torch.bfloat16])
+def test_many_spans_two_level_nmse(tdt):
+    """More spans than one partial group (the NMSE partials are summed in
+    two levels): S and x̂ bit-exact, NMSE within 1e-12 of thc_nmse."""
+    P, N, b, part = 2, 4096 * 4100 + 5, 4, 1 << 20
+    bufs = _inputs(P, N, tdt, seed=11)
+    mM = ga.thc_minmax(bufs, part)
+    packed = ga.thc_usq_quantize(bufs, mM, b, 5, part_elems=part)
+    S1 = ga.thc_int_aggregate(packed, N, b)
+    x1 = ga.thc_dequant(S1, N, P, b, mM, part_elems=part, out_dtype=tdt)
+    ref = [t.clone() for t in bufs]
+    ga.ga_ring_allreduce_sim(ref, ga.AVG, part)
+    ws = torch.empty(ga.thc_nmse_ws_bytes(N), dtype=torch.uint8, device=DEV)
+    n1 = ga.thc_nmse(ref[0], x1, torch.empty(3, dtype=torch.float64, device=DEV), ws)
+    S2, x2, n2 = ga.thc_aggregate_dequant(packed, N, b, mM, part_elems=part, out_dtype=tdt,
+                                          x_ref=ref[0])
+    assert torch.equal(S1[:N], S2[:N])
+    assert np.array_equal(_host(x1)[:N], _host(x2)[:N])
+    np.testing.assert_allclose(n2.cpu().numpy(), n1.cpu().numpy(), rtol=1e-12, atol=0)
