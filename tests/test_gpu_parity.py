@@ -373,10 +373,22 @@ def test_dequant(P, b, N, part, out_dt):
 
 
 @pytest.mark.parametrize("dt", [ga.F32, ga.BF16])
-@pytest.mark.parametrize("N", [1, 1000, 70001, 1 << 20])
+@pytest.mark.parametrize("N", [1, 1000, 70001, 1 << 20, (1 << 24) + 4099])   # last: two-level sum
 def test_nmse(N, dt):
     x = _inputs(1, N, dt, seed=N)[0]
     xh = _inputs(1, N, dt, seed=N + 1)[0]
+    out = ga.thc_nmse(x, xh).cpu().numpy()
+    num, den, nm = oracle.nmse(_host(x), _host(xh))
+    assert abs(out[0] - num) <= 1e-6 * num and abs(out[1] - den) <= 1e-6 * den
+    assert abs(out[2] - nm) <= 1e-6 * nm
+
+
+@pytest.mark.parametrize("dt", [ga.F32, ga.BF16])
+def test_nmse_misaligned(dt):
+    """Inputs one element past a 16-byte boundary go element by element."""
+    N = 300001
+    x = _inputs(1, N + 1, dt, seed=3)[0][1:]
+    xh = _inputs(1, N + 1, dt, seed=4)[0][1:]
     out = ga.thc_nmse(x, xh).cpu().numpy()
     num, den, nm = oracle.nmse(_host(x), _host(xh))
     assert abs(out[0] - num) <= 1e-6 * num and abs(out[1] - den) <= 1e-6 * den
