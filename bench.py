@@ -12,8 +12,9 @@ aggregate, dequantize, NMSE. `value` is aggregated gradient bytes
 
 Prints ONE JSON line. `roofline` describes the dominant kernel (the fused
 ring) from HIP events around its launches inside the timed steps;
-`cpu_baseline` times the oracle (plain C, one thread) on a bounded sample of
-the same workload's partitions on this host; `traffic` comes from the
+`cpu_baseline` times the oracle (plain C) on this host's cores, beside its
+one-thread figure: sampled whole partitions of a flat workload, or the
+whole pack-ring-unpack step of a fused one; `traffic` comes from the
 committed rocprofv3 PMC summary when it was taken on the current ring
 source, else null.
 """
@@ -67,78 +68,169 @@ def traffic_from_profile(workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(pipe, samples, budget_s: float):
-    """The oracle on whole partitions of the same workload: every stage of
-    the step, on the host, single-threaded. Returns aggregated GB/s."""
+def host_threads() -> int:
+    """Host threads for the oracle: the cores this process may run on
+    (bounded by OMP_NUM_THREADS when set, and by 16, one GPU's share of the
+    host)."""
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, min(n, 16))
+
+
+def oracle_partition(pipe, p, inputs) -> int:
+    """The oracle over one partition of a flat workload, every stage of the
+    step in the step's order; returns the partition's element count."""
     import numpy as np
 
     import oracle
     from gradient_all_reduce_worker_amd.pipeline import t_p
 
-    w = pipe.w
-    P = pipe.P
+    w, P = pipe.w, pipe.P
+    xs = [a.copy() for a in inputs]
+    n = xs[0].size
+    lo = p * (w.part_elems or pipe.N)
+    mM = oracle.minmax(xs, n)
+    packed = {b: [oracle.usq_quantize(xs[i], i, n, mM, b, w.quant_seed, e_offset=lo)
+                  for i in range(P)] for b in w.thc_bits}
+    if w.global_bits:                               # the partition's extremes stand in for the
+        mg = oracle.minmax(xs, 0)                   # whole vector's (same work per element)
+    for b in w.global_bits:
+        packed[f"g{b}"] = [oracle.usq_quantize(xs[i], i, 0, mg, b, w.quant_seed, e_offset=lo)
+                           for i in range(P)]
+    for k, (b, g, T) in pipe.nu_tables.items():
+        packed[k] = [oracle.nuhc_quantize(xs[i], i, n, mM, b, g, T, w.quant_seed, e_offset=lo)
+                     for i in range(P)]
+    ef = {}
+    for b in w.ef_bits:                             # first step: residuals are zero
+        xe = [oracle.ef_add(x, np.zeros(n, dtype=np.float32)) for x in xs]
+        me = oracle.minmax(xe, n)
+        pk = [oracle.usq_quantize(xe[i], i, n, me, b, w.quant_seed, e_offset=lo) for i in range(P)]
+        [oracle.ef_update(xe[i], pk[i], b, n, me) for i in range(P)]
+        ef[b] = (me, pk)
+    rht = {}
     tp = t_p(w.rht_p)
-    done_elems, t_total, used = 0, 0.0, 0
-    for p in sorted(samples):
-        xs = [a.copy() for a in samples[p]]
-        n = xs[0].size
-        lo = p * (w.part_elems or pipe.N)
+    for k, (b, g, d, T) in pipe.rht.items():       # blocks of d are the partitions
+        rm = oracle.rht_range(np.stack([oracle.rht_sumsq(x, d) for x in xs]), d, tp)
+        ys = [oracle.clamp(oracle.rht_forward(x, d, w.rht_seed, e0=lo), d, rm) for x in xs]
+        rht[k] = (rm, [oracle.nuhc_quantize(ys[i], i, d, rm, b, g, T, w.quant_seed, e_offset=lo)
+                       for i in range(P)])
+    oracle.ring_fold(xs, op=oracle.AVG, part=w.ring_part_elems and n)
+    for b in w.thc_bits:
+        S = oracle.int_aggregate(packed[b], n, b)
+        oracle.nmse(xs[0], oracle.dequant(S, P, b, n, mM, w.dtype))
+    for b in w.global_bits:
+        S = oracle.int_aggregate(packed[f"g{b}"], n, b)
+        oracle.nmse(xs[0], oracle.dequant(S, P, b, 0, mg, w.dtype))
+    for k, (b, g, T) in pipe.nu_tables.items():
+        Y = oracle.nuhc_aggregate(packed[k], n, b, g, T)
+        oracle.nmse(xs[0], oracle.nuhc_dequant(Y, P, g, n, mM, w.dtype))
+    for b, (me, pk) in ef.items():
+        oracle.nmse(xs[0], oracle.dequant(oracle.int_aggregate(pk, n, b), P, b, n, me, w.dtype))
+    if len(pipe.arrived) < P and w.thc_bits:
+        b = w.thc_bits[0]
+        S = oracle.int_aggregate([packed[b][i] for i in pipe.arrived], n, b)
+        oracle.nmse(xs[0], oracle.dequant(S, len(pipe.arrived), b, n, mM, w.dtype))
+    for k, (b, g, d, T) in pipe.rht.items():
+        rm, pk = rht[k]
+        avg = oracle.nuhc_dequant(oracle.nuhc_aggregate(pk, d, b, g, T), P, g, d, rm)
+        oracle.nmse(xs[0], oracle.rht_inverse(avg, d, w.rht_seed, w.dtype, e0=lo)[:n])
+    return n
+
+
+def cpu_baseline_flat(pipe, samples, budget_s: float, threads: int):
+    """The oracle on whole sampled partitions of a flat workload: first on
+    one host thread for a quarter of the budget, then partitions in waves of
+    one per thread on `threads` host threads for the rest (oracle calls
+    release the interpreter lock). Aggregated GB/s of each."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    w, P = pipe.w, pipe.P
+    order = sorted(samples)
+    with ThreadPoolExecutor(threads) as ex:         # untimed: first touch of the host buffers
+        list(ex.map(lambda p: oracle_partition(pipe, p, samples[p]), order[:threads]))
+    oracle_partition(pipe, order[0], samples[order[0]])    # untimed, on this thread
+    t1 = e1 = 0.0
+    used1 = 0
+    while t1 < budget_s / 4:
+        p = order[used1 % len(order)]
         t0 = time.perf_counter()
-        mM = oracle.minmax(xs, n)
-        packed = {b: [oracle.usq_quantize(xs[i], i, n, mM, b, w.quant_seed, e_offset=lo)
-                      for i in range(P)] for b in w.thc_bits}
-        if w.global_bits:                               # the sample's extremes stand in for the
-            mg = oracle.minmax(xs, 0)                   # whole vector's (same work per element)
-        for b in w.global_bits:
-            packed[f"g{b}"] = [oracle.usq_quantize(xs[i], i, 0, mg, b, w.quant_seed, e_offset=lo)
-                               for i in range(P)]
-        for k, (b, g, T) in pipe.nu_tables.items():
-            packed[k] = [oracle.nuhc_quantize(xs[i], i, n, mM, b, g, T, w.quant_seed, e_offset=lo)
-                         for i in range(P)]
-        ef = {}
-        for b in w.ef_bits:                             # first step: residuals are zero
-            xe = [oracle.ef_add(x, np.zeros(n, dtype=np.float32)) for x in xs]
-            me = oracle.minmax(xe, n)
-            pk = [oracle.usq_quantize(xe[i], i, n, me, b, w.quant_seed, e_offset=lo)
-                  for i in range(P)]
-            [oracle.ef_update(xe[i], pk[i], b, n, me) for i in range(P)]
-            ef[b] = (me, pk)
-        rht = {}
-        for k, (b, g, d, T) in pipe.rht.items():       # blocks of d are the partitions
-            rm = oracle.rht_range(np.stack([oracle.rht_sumsq(x, d) for x in xs]), d, tp)
-            ys = [oracle.clamp(oracle.rht_forward(x, d, w.rht_seed, e0=lo), d, rm) for x in xs]
-            rht[k] = (rm, [oracle.nuhc_quantize(ys[i], i, d, rm, b, g, T, w.quant_seed,
-                                                e_offset=lo) for i in range(P)])
-        oracle.ring_fold(xs, op=oracle.AVG, part=w.ring_part_elems and n)
-        for b in w.thc_bits:
-            S = oracle.int_aggregate(packed[b], n, b)
-            xh = oracle.dequant(S, P, b, n, mM, w.dtype)
-            oracle.nmse(xs[0], xh)
-        for b in w.global_bits:
-            S = oracle.int_aggregate(packed[f"g{b}"], n, b)
-            oracle.nmse(xs[0], oracle.dequant(S, P, b, 0, mg, w.dtype))
-        for k, (b, g, T) in pipe.nu_tables.items():
-            Y = oracle.nuhc_aggregate(packed[k], n, b, g, T)
-            oracle.nmse(xs[0], oracle.nuhc_dequant(Y, P, g, n, mM, w.dtype))
-        for b, (me, pk) in ef.items():
-            oracle.nmse(xs[0], oracle.dequant(oracle.int_aggregate(pk, n, b), P, b, n, me, w.dtype))
-        if len(pipe.arrived) < P and w.thc_bits:
-            b = w.thc_bits[0]
-            S = oracle.int_aggregate([packed[b][i] for i in pipe.arrived], n, b)
-            oracle.nmse(xs[0], oracle.dequant(S, len(pipe.arrived), b, n, mM, w.dtype))
-        for k, (b, g, d, T) in pipe.rht.items():
-            rm, pk = rht[k]
-            avg = oracle.nuhc_dequant(oracle.nuhc_aggregate(pk, d, b, g, T), P, g, d, rm)
-            oracle.nmse(xs[0], oracle.rht_inverse(avg, d, w.rht_seed, w.dtype, e0=lo)[:n])
-        t_total += time.perf_counter() - t0
-        done_elems += n
-        used += 1
-        if t_total >= budget_s:
-            break
-    gbs = P * done_elems * w.elem_bytes / t_total / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{used} of {pipe.n_partitions()} partitions ({done_elems} elements x {P} "
-                      f"workers), all stages, {t_total:.1f} s on one host thread"}
+        e1 += oracle_partition(pipe, p, samples[p])
+        t1 += time.perf_counter() - t0
+        used1 += 1
+    eN = 0
+    waves = 0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        k = 0
+        while True:
+            ps = [order[(k + j) % len(order)] for j in range(threads)]
+            k += threads
+            eN += sum(ex.map(lambda p: oracle_partition(pipe, p, samples[p]), ps))
+            waves += 1
+            if time.perf_counter() - t0 >= budget_s * 3 / 4:
+                break
+    tN = time.perf_counter() - t0
+    one = P * e1 * w.elem_bytes / t1 / 1e9
+    many = P * eN * w.elem_bytes / tN / 1e9
+    return {"value": round(many, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "single_thread_value": round(one, 4),
+            "sample": f"{len(order)} of {pipe.n_partitions()} partitions sampled evenly; every stage "
+                      f"of the step per partition, after one untimed wave; {threads} host threads, one partition each, "
+                      f"{waves} waves ({waves * threads} partitions x {P} workers) in {tN:.1f} s; "
+                      f"one thread: {used1} partitions in {t1:.1f} s"}
+
+
+def cpu_baseline_fused(pipe, host, threads: int):
+    """The oracle on the whole step of a fused workload (Tensor Fusion):
+    every worker's tensors packed into its fusion buffers, each buffer
+    ring-averaged, the buffers unpacked; on one host thread, then on
+    `threads` threads (one worker per thread for pack and unpack, one buffer
+    per thread for the ring). Aggregated GB/s of each."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+
+    w, P = pipe.w, pipe.P
+    buf_of, off_of, fill = pipe.buf_of, pipe.off_of, pipe.fill
+    ndt = np.float32 if w.dtype == 0 else np.uint16
+
+    def pack(i):
+        return oracle.fuse_pack(host[i], buf_of, off_of, fill, ndt)
+
+    def ring(fused, k):
+        oracle.ring_fold([fused[i][k] for i in range(P)], op=oracle.AVG, part=w.ring_part_elems)
+
+    def unpack(fused, i):
+        return oracle.fuse_unpack(fused[i], buf_of, off_of, w.sizes)
+
+    def threaded():
+        with ThreadPoolExecutor(threads) as ex:
+            fused = list(ex.map(pack, range(P)))
+            list(ex.map(lambda k: ring(fused, k), range(len(fill))))
+            list(ex.map(lambda i: unpack(fused, i), range(P)))
+
+    threaded()                      # untimed: first touch of the host buffers
+    t0 = time.perf_counter()
+    fused = [pack(i) for i in range(P)]
+    for k in range(len(fill)):
+        ring(fused, k)
+    [unpack(fused, i) for i in range(P)]
+    t1 = time.perf_counter() - t0
+    del fused
+    t0 = time.perf_counter()
+    threaded()
+    tN = time.perf_counter() - t0
+    nbytes = P * pipe.N * w.elem_bytes
+    return {"value": round(nbytes / tN / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "single_thread_value": round(nbytes / t1 / 1e9, 4),
+            "sample": f"the whole step ({P} workers x {len(w.sizes)} tensors, {len(fill)} fusion "
+                      f"buffers): pack, ring average, unpack, after one untimed pass; {threads} host threads (pack and unpack "
+                      f"one worker per thread, the ring one buffer per thread) in {tN:.2f} s; one "
+                      f"thread {t1:.2f} s"}
 
 
 def main():
@@ -147,7 +239,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="shard", choices=sorted(DESCRIPTIONS))
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=16.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-fusion", action="store_true",
                     help="fused workloads: pack -> ring -> unpack instead of the zero-copy ring")
@@ -180,12 +272,18 @@ def main():
     pipe.setup()
     log(f"setup {args.workload}: {time.perf_counter() - t0:.1f} s")
 
-    samples = None
+    # host copies for the oracle baseline, taken before the first step
+    # overwrites the gradients with their average
+    samples = host = None
+    threads = host_threads()
     if not args.no_cpu and not pipe.w.fused:
         n_part = pipe.n_partitions()
-        want = min(n_part, 160)
+        want = min(n_part, 4 * threads)
         which = sorted({int(i * n_part / want) for i in range(want)})
         samples = pipe.sample_inputs(which)
+    elif not args.no_cpu:
+        from gradient_all_reduce_worker_amd import synth
+        host = [[synth.to_numpy_bits(t) for t in pipe.tensors[i]] for i in range(pipe.P)]
 
     if args.copy_probe:
         # a plain device copy of known size (1 GiB read, 1 GiB written), for
@@ -257,7 +355,9 @@ def main():
         "stages": stages,
     }
     if samples is not None:
-        out["cpu_baseline"] = cpu_baseline(pipe, samples, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline_flat(pipe, samples, args.cpu_seconds, threads)
+    elif host is not None:
+        out["cpu_baseline"] = cpu_baseline_fused(pipe, host, threads)
     print(json.dumps(out), flush=True)
 
 

@@ -350,3 +350,17 @@ def test_ef_argument_errors_before_enqueue():
     bad = (C.c_int32 * 4)(0, 3, 3, 4)
     assert q(good, errs, 4, 0, 16, 0, 0, 0x50000, 2, 4, bad, 1, good, None) == EINVAL   # table
     assert q(good, errs, 4, 0, 0, 0, 0, 0x50000, 4, 0, None, 1, good, None) == 0        # empty
+
+
+def test_truncation_threshold_t_p():
+    """The RHT truncation threshold the pipeline hands to the kernels,
+    t_p = Phi^-1(1 - p/2) (THC page, section 5): textbook quantiles, and for
+    every p the two-sided normal tail beyond t_p, erfc(t_p / sqrt 2), is p."""
+    import math
+
+    from gradient_all_reduce_worker_amd.pipeline import t_p
+    assert abs(t_p(0.05) - 1.959963985) < 1e-9
+    assert abs(t_p(0.01) - 2.575829304) < 1e-9
+    for p in (0.05, 0.01, 1.0 / 32, 1e-3, 0.5):
+        assert abs(math.erfc(t_p(p) / math.sqrt(2.0)) - p) <= 1e-12 * p, p
+    assert abs(t_p(1.0 / 32) - 2.153874694061456) < 1e-9      # the vgg16 RHT pass

@@ -20,6 +20,10 @@ def _host(t):
     return t.numpy().copy()
 
 
+def _to_dev(h: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(h)).to(DEV)
+
+
 def _grads(P, N, dt, seed, misalign=0):
     rng = np.random.default_rng(seed)
     g = torch.from_numpy((rng.standard_normal((P, N + misalign)) * 0.01).astype(np.float32))
@@ -52,7 +56,9 @@ def test_ef_minmax_and_quantize(P, N, part, b, mis, dt, table):
     xs = [oracle.ef_add(gh[i], eh[i]) for i in range(P)]
     mMw = oracle.minmax(xs, part)
     assert np.array_equal(mM.cpu().numpy().view(np.uint32), mMw.view(np.uint32))
-    packed = ga.thc_ef_quantize(gs, es, mM, b, seed, part_elems=part, worker0=1, g=g, table=T)
+    # the quantizer runs on the oracle's grid
+    packed = ga.thc_ef_quantize(gs, es, _to_dev(mMw), b, seed, part_elems=part, worker0=1, g=g,
+                                table=T)
     for i in range(P):
         if T is None:
             pw = oracle.usq_quantize(xs[i], 1 + i, part, mMw, b, seed)
@@ -72,12 +78,15 @@ def test_ef_rounds_track_the_oracle():
         gh = [(rng.standard_normal(N) * 0.01).astype(np.float32) for _ in range(P)]
         gs = [torch.from_numpy(x).to(DEV) for x in gh]
         mM = ga.thc_ef_minmax(gs, es, part)
-        packed = ga.thc_ef_quantize(gs, es, mM, b, 77 + t, part_elems=part)
         xs = [oracle.ef_add(gh[i], eh[i]) for i in range(P)]
         mMw = oracle.minmax(xs, part)
+        assert np.array_equal(mM.cpu().numpy().view(np.uint32), mMw.view(np.uint32)), t
+        packed = ga.thc_ef_quantize(gs, es, _to_dev(mMw), b, 77 + t, part_elems=part)
         pw = [oracle.usq_quantize(xs[i], i, part, mMw, b, 77 + t) for i in range(P)]
         eh = [oracle.ef_update(xs[i], pw[i], b, part, mMw) for i in range(P)]
-        S = ga.thc_int_aggregate(packed, N, b)
+        for i in range(P):
+            assert np.array_equal(packed[i].cpu().numpy(), pw[i]), (t, i)
+        S = ga.thc_int_aggregate([_to_dev(p) for p in pw], N, b)
         assert np.array_equal(S.cpu().numpy()[:N], oracle.int_aggregate(pw, N, b))
     for i in range(P):
         assert np.array_equal(es[i].cpu().numpy().view(np.uint32), eh[i].view(np.uint32))
@@ -89,14 +98,14 @@ def test_partial_aggregation(b):
     count."""
     P, N, part = 10, 100003, 4096
     gs, _ = _grads(P, N, ga.F32, seed=b)
-    mM = ga.thc_minmax(gs, part)
-    packed = ga.thc_usq_quantize(gs, mM, b, 99, part_elems=part)
+    hosts = [_host(x) for x in gs]
+    mMw = oracle.minmax(hosts, part)
+    pw = [oracle.usq_quantize(hosts[i], i, part, mMw, b, 99) for i in range(P)]
     arrived = [0, 1, 3, 4, 6, 8, 9]
-    S = ga.thc_int_aggregate([packed[i] for i in arrived], N, b)
-    est = ga.thc_dequant(S, N, len(arrived), b, mM, part_elems=part)
-    mMw = mM.cpu().numpy()
-    pw = [oracle.usq_quantize(_host(gs[i]), i, part, mMw, b, 99) for i in arrived]
-    Sw = oracle.int_aggregate(pw, N, b)
+    # the server side gets the oracle's indices of the arrived workers
+    S = ga.thc_int_aggregate([_to_dev(pw[i]) for i in arrived], N, b)
+    Sw = oracle.int_aggregate([pw[i] for i in arrived], N, b)
     assert np.array_equal(S.cpu().numpy()[:N], Sw)
+    est = ga.thc_dequant(_to_dev(Sw), N, len(arrived), b, _to_dev(mMw), part_elems=part)
     want = oracle.dequant(Sw, len(arrived), b, part, mMw)
     assert np.array_equal(est.cpu().numpy()[:N].view(np.uint32), want.view(np.uint32))

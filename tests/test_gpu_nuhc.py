@@ -31,6 +31,10 @@ def _inputs(P, N, dt, seed):
     return [t[i].clone().to(DEV) for i in range(P)]
 
 
+def _to_dev(h: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(h)).to(DEV)
+
+
 def _host(t):
     t = t.detach().cpu()
     if t.dtype == torch.bfloat16:
@@ -47,19 +51,21 @@ def _host(t):
 def test_nuhc_quantize_aggregate_dequant(P, N, part, dt, b, g, T):
     bufs = _inputs(P, N, dt, seed=N + b + g)
     seed = 0x1234_5678_9ABC_DEF0 + g
-    mM = ga.thc_minmax(bufs, part)
+    # every stage starts from the oracle's values: its grid, its indices, its sums
+    hosts = [_host(t) for t in bufs]
+    mM_h = oracle.minmax(hosts, part)
+    mM = _to_dev(mM_h)
     packed = ga.thc_nuhc_quantize(bufs, mM, b, g, T, seed, part_elems=part, worker0=2)
-    mM_h = mM.cpu().numpy()
     want = []
     for i in range(P):
-        w = oracle.nuhc_quantize(_host(bufs[i]), 2 + i, part, mM_h, b, g, T, seed)
+        w = oracle.nuhc_quantize(hosts[i], 2 + i, part, mM_h, b, g, T, seed)
         assert np.array_equal(packed[i].cpu().numpy(), w), i
         want.append(w)
-    Y = ga.thc_nuhc_aggregate(packed, N, b, g, T)
+    Y = ga.thc_nuhc_aggregate([_to_dev(w) for w in want], N, b, g, T)
     Yw = oracle.nuhc_aggregate(want, N, b, g, T)
     assert np.array_equal(Y.cpu().numpy()[:N], Yw)
     out_dtype = torch.float32 if dt == ga.F32 else torch.bfloat16
-    xh = ga.thc_nuhc_dequant(Y, N, P, g, mM, part_elems=part, out_dtype=out_dtype)
+    xh = ga.thc_nuhc_dequant(_to_dev(Yw), N, P, g, mM, part_elems=part, out_dtype=out_dtype)
     assert np.array_equal(_host(xh)[:N], oracle.nuhc_dequant(Yw, P, g, part, mM_h, dt))
 
 
@@ -82,11 +88,11 @@ def test_flat_partition_and_misaligned():
     views = [v[1:] for v in big]
     for v in views:
         v[:1000] = 0.25
-    mM = ga.thc_minmax(views, 1000)
+    mM_h = oracle.minmax([_host(v) for v in views], 1000)
+    assert mM_h[0, 0] == mM_h[0, 1]
     T = [0, 1, 3, 4]
     packed = [torch.zeros(N * 2 // 8 + 1, dtype=torch.uint8, device=DEV)[1:] for _ in views]
-    ga.thc_nuhc_quantize(views, mM, 2, 4, T, 5, part_elems=1000, packed=packed)
-    mM_h = mM.cpu().numpy()
+    ga.thc_nuhc_quantize(views, _to_dev(mM_h), 2, 4, T, 5, part_elems=1000, packed=packed)
     for i in range(P):
         assert np.array_equal(packed[i].cpu().numpy(),
                               oracle.nuhc_quantize(_host(views[i]), i, 1000, mM_h, 2, 4, T, 5))

@@ -36,6 +36,11 @@ def _host(t: torch.Tensor) -> np.ndarray:
     return t.numpy().copy()
 
 
+def _dev_grid(mM_h: np.ndarray) -> torch.Tensor:
+    """A host grid table (partitions x 2 binary32) on the device."""
+    return torch.from_numpy(np.ascontiguousarray(mM_h, dtype=np.float32)).to(DEV)
+
+
 def _inputs(P, N, dt, seed, wide=True):
     """P seeded gradient vectors; magnitudes spread over many binades so the
     fold order shows in the last bits."""
@@ -211,11 +216,11 @@ def test_usq_quantize(P, N, part, dt, b):
     bufs = _inputs(P, N, dt, seed=3 * N + P, wide=False)
     seed = 0xDEADBEEF12345678 + b
     worker0 = 5
-    mM = ga.thc_minmax(bufs, part)
-    packed = ga.thc_usq_quantize(bufs, mM, b, seed, part_elems=part, worker0=worker0)
-    mM_h = mM.cpu().numpy()
+    hosts = [_host(t) for t in bufs]
+    mM_h = oracle.minmax(hosts, part)          # the oracle's grid, given to both sides
+    packed = ga.thc_usq_quantize(bufs, _dev_grid(mM_h), b, seed, part_elems=part, worker0=worker0)
     for i in range(P):
-        want = oracle.usq_quantize(_host(bufs[i]), worker0 + i, part, mM_h, b, seed)
+        want = oracle.usq_quantize(hosts[i], worker0 + i, part, mM_h, b, seed)
         assert np.array_equal(packed[i].cpu().numpy(), want), i
 
 
@@ -224,10 +229,9 @@ def test_usq_quantize_misaligned_and_flat_partition():
     views = [v[1:] for v in big]
     views[1][:1000] = 0.125           # a partition with M == m
     views[0][:1000] = 0.125
-    mM = ga.thc_minmax(views, 1000)
+    mM_h = oracle.minmax([_host(v) for v in views], 1000)
     packed = [torch.zeros(3000 * 4 // 8 + 1, dtype=torch.uint8, device=DEV)[1:] for _ in views]
-    ga.thc_usq_quantize(views, mM, 4, 9, part_elems=1000, packed=packed)
-    mM_h = mM.cpu().numpy()
+    ga.thc_usq_quantize(views, _dev_grid(mM_h), 4, 9, part_elems=1000, packed=packed)
     assert mM_h[0, 0] == mM_h[0, 1]
     for i in range(2):
         want = oracle.usq_quantize(_host(views[i]), i, 1000, mM_h, 4, 9)
@@ -274,10 +278,11 @@ def test_usq_quantize_on_thresholds(P, N, part, b):
     rng = np.random.default_rng(b)
     xs = [_threshold_values(seed, worker0 + i, N, part, L, rng) for i in range(P)]
     bufs = [torch.from_numpy(x).to(DEV) for x in xs]
-    mM = ga.thc_minmax(bufs, part)
-    mM_h = mM.cpu().numpy()
-    assert np.all(mM_h[:, 0] == 0.0) and np.all(mM_h[:, 1] == L)
-    packed = ga.thc_usq_quantize(bufs, mM, b, seed, part_elems=part, worker0=worker0)
+    # every partition holds 0 and L and nothing outside [0, L]: its grid is
+    # [0, L] by construction
+    mM_h = np.tile(np.array([[0.0, L]], dtype=np.float32), (ga.n_partitions(N, part), 1))
+    assert np.array_equal(oracle.minmax(xs, part), mM_h)
+    packed = ga.thc_usq_quantize(bufs, _dev_grid(mM_h), b, seed, part_elems=part, worker0=worker0)
     for i in range(P):
         want = oracle.usq_quantize(xs[i], worker0 + i, part, mM_h, b, seed)
         z = oracle.unpack_indices(want, N, b)

@@ -301,8 +301,7 @@ def test_rht_norm_quantize_matches_three_calls(P, d, N, b, g, table, dt):
     for i in range(P):
         got = pk2[i].cpu().numpy()[:nbytes]
         assert np.array_equal(got, pk1[i].cpu().numpy()[:nbytes]), i
-        if i < 4:
-            yc = oracle.clamp(oracle.rht_forward(xs[i], d, SEED), d, mMw)
-            want = (oracle.nuhc_quantize(yc, 3 + i, d, mMw, b, g, table, 17) if table is not None
-                    else oracle.usq_quantize(yc, 3 + i, d, mMw, b, 17))
-            assert np.array_equal(got, want), i
+        yc = oracle.clamp(oracle.rht_forward(xs[i], d, SEED), d, mMw)
+        want = (oracle.nuhc_quantize(yc, 3 + i, d, mMw, b, g, table, 17) if table is not None
+                else oracle.usq_quantize(yc, 3 + i, d, mMw, b, 17))
+        assert np.array_equal(got, want), i

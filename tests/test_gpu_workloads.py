@@ -2,13 +2,22 @@
 same launch configuration) that bench.py times.
 
 small, fusion, resnet101: every output element of every worker against the
-oracle. vgg16 (32 x 138M fp32) and shard (8 x 2^31 bf16): the oracle checks
-whole sampled partitions (first, middle, last) for every stage - grid
-extremes, packed indices, ring average, integer sums, dequantized values -
-and the whole-vector NMSE is checked against an fp64 torch evaluation of its
-definition on the same outputs.
+oracle. vgg16 (32 x 138M fp32) and shard (8 x 2^31 bf16):
+  * every partition's grid extremes (and, for vgg16, the error-feedback
+    grids and the RHT ranges of every block) against the oracle, streamed
+    partition by partition over a thread pool; the whole-vector grid is the
+    extreme of the oracle's partition extremes (the THC page's preliminary
+    round takes local extremes, then global ones);
+  * 16 evenly spaced partitions, first and last included, element by
+    element for every stage -- packed indices, ring average, integer sums,
+    dequantized values -- with every oracle stage fed the oracle's own
+    previous output;
+  * the whole-vector NMSE against an fp64 torch evaluation of its definition
+    on the same outputs, and all workers' averages bitwise equal.
 """
 import gc
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -20,6 +29,11 @@ from gradient_all_reduce_worker_amd import synth
 from gradient_all_reduce_worker_amd.pipeline import Pipeline, t_p
 
 pytestmark = pytest.mark.gpu
+
+# oracle calls release the interpreter lock (ctypes), so threads run them in
+# parallel; the GPU machine grants 16 cores to one GPU
+POOL = max(1, min(16, len(os.sched_getaffinity(0))))
+N_SAMPLED = 16
 
 
 def _u(a):
@@ -33,9 +47,10 @@ def _free_memory():
     torch.cuda.empty_cache()
 
 
-def _check_partition(w, P, lo, xs, got, nu_tables=None, arrived=None):
+def _check_partition(w, P, lo, xs, got, mMg, nu_tables=None, arrived=None):
     """Oracle on one partition [lo, lo + n) of a flat workload (first step:
-    error-feedback residuals start at zero)."""
+    error-feedback residuals start at zero); mMg is the oracle's grid of the
+    whole vector."""
     n = xs[0].size
     xs = [x.copy() for x in xs]
     for b in w.ef_bits:
@@ -59,7 +74,6 @@ def _check_partition(w, P, lo, xs, got, nu_tables=None, arrived=None):
                      for i in range(P)]
         for i in range(P):
             assert np.array_equal(got["packed"][b][i], packed[b][i]), (b, i)
-    mMg = got["mM_g"][None, :]      # the whole vector's grid, checked by the caller
     for b in w.global_bits:
         k = f"g{b}"
         packed[k] = [oracle.usq_quantize(xs[i], i, 0, mMg, b, w.quant_seed, e_offset=lo)
@@ -132,34 +146,97 @@ def _nmse_property(pipe, slab=1 << 26):
         assert abs(got[2] - num / den) <= 1e-6 * (num / den)
 
 
+def _sampled(n_part: int):
+    """N_SAMPLED evenly spaced partitions, the first and the last included."""
+    k = min(N_SAMPLED, n_part)
+    return sorted({round(j * (n_part - 1) / max(k - 1, 1)) for j in range(k)})
+
+
+def _oracle_grids(pipe, keep):
+    """The oracle over every partition of the pristine gradients: its grid
+    per partition, the error-feedback grid (residuals zero) and, per RHT pass,
+    the range of every block. Partitions are copied to the host a slab at a
+    time and handed to a thread pool; the inputs of the partitions in `keep`
+    are returned for the element-by-element checks."""
+    w, P, N = pipe.w, pipe.P, pipe.N
+    plen = w.part_elems
+    n_part = pipe.n_partitions()
+    es = w.elem_bytes
+    grid = np.empty((n_part, 2), dtype=np.float32)
+    ef = {f"ef{b}": np.empty((n_part, 2), dtype=np.float32) for b in w.ef_bits}
+    rht = {k: np.empty((n_part, 2), dtype=np.float32) for k in pipe.rht}
+    tp = t_p(w.rht_p)
+    kept = {}
+
+    def job(p, xs):
+        n = xs[0].size
+        grid[p] = oracle.minmax(xs, n)[0]
+        if ef:
+            zero = np.zeros(n, dtype=np.float32)
+            g = oracle.minmax([oracle.ef_add(x, zero) for x in xs], n)[0]
+            for k in ef:
+                ef[k][p] = g
+        for k, (_, _, d, _) in pipe.rht.items():
+            assert d == plen                 # RHT blocks are the partitions
+            S2 = np.stack([oracle.rht_sumsq(x, d) for x in xs])
+            rht[k][p] = oracle.rht_range(S2, d, tp)[0]
+
+    per_slab = max(1, (1 << 30) // (P * plen * es))     # about 1 GiB of inputs per slab
+    with ThreadPoolExecutor(POOL) as ex:
+        for p0 in range(0, n_part, per_slab):
+            p1 = min(p0 + per_slab, n_part)
+            lo, hi = p0 * plen, min(p1 * plen, N)
+            slab = [synth.to_numpy_bits(pipe.flat[i][lo:hi]) for i in range(P)]
+            futs = []
+            for p in range(p0, p1):
+                a, c = p * plen - lo, min((p + 1) * plen, N) - lo
+                xs = [np.ascontiguousarray(x[a:c]) for x in slab]
+                if p in keep:
+                    kept[p] = [x.copy() for x in xs]
+                futs.append(ex.submit(job, p, xs))
+            for f in futs:
+                f.result()
+    return grid, ef, rht, kept
+
+
 @pytest.mark.parametrize("name", ["vgg16", "shard"])
 def test_flat_workload_sampled(name):
     pipe = Pipeline(name)
     print(f"workload {name}: P={pipe.P} N={pipe.N}", flush=True)
     pipe.setup()
     n_part = pipe.n_partitions()
-    which = [0, n_part // 2, n_part - 1]
-    before = pipe.sample_inputs(which)
+    which = _sampled(n_part)
+    grid, ef, rht, before = _oracle_grids(pipe, set(which))
+    print(f"oracle grids of {n_part} partitions done", flush=True)
     pipe.step()
     torch.cuda.synchronize()
-    after = pipe.sample_outputs(which)
-    plen = pipe.w.part_elems
+    # every partition's grid, bit for bit
+    assert np.array_equal(pipe.mM.cpu().numpy().view(np.uint32), grid.view(np.uint32))
+    for k, g in ef.items():
+        assert np.array_equal(pipe.mM_ef[k].cpu().numpy().view(np.uint32), g.view(np.uint32)), k
+    for k, g in rht.items():
+        assert np.array_equal(pipe.rht_mM[k].cpu().numpy().view(np.uint32), g.view(np.uint32)), k
+    # the whole vector's grid: global extremes of the oracle's local ones
+    mMg = np.array([[grid[:, 0].min(), grid[:, 1].max()]], dtype=np.float32)
     if pipe.w.global_bits:
-        # the whole vector's grid is the extreme of the partitions' grids
-        # (each sampled one is checked against the oracle below)
-        mM = pipe.mM.cpu().numpy()
-        g = pipe.mM_g.cpu().numpy()[0]
-        assert g[0] == mM[:, 0].min() and g[1] == mM[:, 1].max()
-    for p in which:
-        _check_partition(pipe.w, pipe.P, p * plen, before[p], after[p], pipe.nu_tables,
+        assert np.array_equal(pipe.mM_g.cpu().numpy().view(np.uint32), mMg.view(np.uint32))
+    after = pipe.sample_outputs(which)
+    rht_after = {key: pipe.sample_rht_outputs(key, which) for key in pipe.rht}
+    plen = pipe.w.part_elems
+
+    def check(p):
+        _check_partition(pipe.w, pipe.P, p * plen, before[p], after[p], mMg, pipe.nu_tables,
                          pipe.arrived)
-    for key, (_, _, d, _) in pipe.rht.items():
-        assert d == plen                    # RHT blocks are the sampled partitions
-        got = pipe.sample_rht_outputs(key, which)
-        for p in which:
-            _check_rht_block(pipe, key, p, before[p], got[p])
-    # all workers end with identical averages (sampled: every worker's first
-    # and last partition were compared above; here, whole buffers on device)
+        for key in pipe.rht:
+            _check_rht_block(pipe, key, p, before[p], rht_after[key][p])
+        return p
+
+    with ThreadPoolExecutor(POOL) as ex:
+        done = list(ex.map(check, which))
+    assert done == which
+    print(f"{len(which)} partitions checked element by element", flush=True)
+    # all workers end with identical averages (every worker of the sampled
+    # partitions was compared above; here, whole buffers on device)
     for i in range(1, pipe.P):
         assert torch.equal(pipe.flat[i].view(torch.int16 if pipe.w.dtype else torch.int32),
                            pipe.flat[0].view(torch.int16 if pipe.w.dtype else torch.int32))
@@ -175,7 +252,7 @@ def test_small_workload_full():
     pipe.step()
     torch.cuda.synchronize()
     got = pipe.sample_outputs([0])[0]
-    _check_partition(pipe.w, pipe.P, 0, xs, got)
+    _check_partition(pipe.w, pipe.P, 0, xs, got, oracle.minmax(xs, 0))
     ref = [x.copy() for x in xs]
     oracle.ring_fold(ref, op=oracle.AVG, part=0)
     nm = oracle.nmse(ref[0], oracle.dequant(got["S"][4], 4, 4, 0, got["mM"][None, :]))

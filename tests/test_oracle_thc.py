@@ -253,20 +253,30 @@ def test_nmse_definition_and_expectation():
 
 
 def test_partitions_use_their_own_grid():
-    """Each partition is quantized on its own [m, M]; the generator is keyed
-    by the element's index in the whole vector, not within its partition."""
+    """Each partition is quantized on its own [m, M] (one grid per 4 MB
+    partition, THC page section 2): in every partition the smallest element
+    is sent as index 0 and the largest as 2^b - 1 (the deterministic ends of
+    stochastic rounding: f = 0 never rounds up, f = 1 always does), which one
+    grid over the whole vector does not do for the partitions of small scale;
+    and a partition's indices do not move when another partition's grid
+    does."""
     rng = np.random.default_rng(8)
     N, part, b = 300, 128, 4
+    L = (1 << b) - 1
     x = (rng.standard_normal(N) * np.repeat([1e-3, 1.0, 10.0], 100)).astype(np.float32)
     mM = oracle.minmax([x], part)
-    whole = oracle.usq_quantize(x, 2, part, mM, b, 77)
+    z = oracle.unpack_indices(oracle.usq_quantize(x, 2, part, mM, b, 77), N, b)
+    zg = oracle.unpack_indices(oracle.usq_quantize(x, 2, 0, oracle.minmax([x], 0), b, 77), N, b)
     for p in range(mM.shape[0]):
         lo, hi = p * part, min((p + 1) * part, N)
-        sub = oracle.unpack_indices(oracle.usq_quantize(x, 2, part, mM, b, 77), N, b)[lo:hi]
-        assert np.array_equal(sub, oracle.unpack_indices(whole, N, b)[lo:hi])
-        xhat = oracle.dequant(oracle.unpack_indices(whole, N, b), 1, b, part, mM)[lo:hi]
-        tol = 1e-6 * max(abs(float(mM[p, 0])), abs(float(mM[p, 1])))
-        assert np.all(xhat >= mM[p, 0] - tol) and np.all(xhat <= mM[p, 1] + tol)
+        seg = x[lo:hi]
+        assert z[lo + int(np.argmin(seg))] == 0 and z[lo + int(np.argmax(seg))] == L, p
+    assert zg[int(np.argmax(x[:part]))] != L      # partition 0 spans a sliver of the whole range
+    moved = mM.copy()
+    moved[1] = [-100.0, 100.0]
+    z2 = oracle.unpack_indices(oracle.usq_quantize(x, 2, part, moved, b, 77), N, b)
+    assert np.array_equal(z2[:part], z[:part]) and np.array_equal(z2[2 * part:], z[2 * part:])
+    assert not np.array_equal(z2[part:2 * part], z[part:2 * part])
 
 
 def test_offset_quantize_equals_slice_of_whole():
