@@ -50,8 +50,8 @@ class RingStats(C.Structure):
 
 DESC_DTYPE = np.dtype([("src", np.uint64), ("dst", np.uint64), ("n", np.int64), ("start", np.int64)])
 # ga_fusion_tensor
-FTENSOR_DTYPE = np.dtype([("start", np.int64), ("n", np.int64), ("vstart", np.int64),
-                          ("vec", np.int32), ("reserved", np.int32)])
+FTENSOR_DTYPE = np.dtype([("start", np.int64), ("n", np.int64), ("buf", np.int32),
+                          ("reserved", np.int32)])
 
 _lib = None
 
@@ -91,8 +91,9 @@ def load() -> C.CDLL:
     L.thc_rht_inverse.argtypes = [vp, i64, i64, u64, vp, i32, vp]
     L.thc_rht_quantize.argtypes = [C.POINTER(vp), i32, i32, i64, i32, i64, u64, vp, i32, i32,
                                    C.POINTER(i32), u64, C.POINTER(vp), C.POINTER(vp), vp]
-    L.ga_fusion_ring_plan.argtypes = [vp, vp, i64, i32, i32, i64, C.POINTER(i64)]
-    L.ga_fusion_ring_allreduce.argtypes = [vp, vp, i64, i64, i32, i64, i32, i32, i32, i64,
+    L.ga_fusion_ring_plan.argtypes = [vp, vp, i64, i32, i32, P64, i32, i64, i32, vp, i64,
+                                      C.POINTER(i64)]
+    L.ga_fusion_ring_allreduce.argtypes = [vp, i64, i32, i32, i32, P64, i32, i64, i32,
                                            C.POINTER(RingStats), vp]
     L.thc_ef_minmax.argtypes = [C.POINTER(vp), C.POINTER(vp), i32, i64, i32, i64, vp, vp]
     L.thc_ef_quantize.argtypes = [C.POINTER(vp), C.POINTER(vp), i32, i32, i64, i32, i64, vp, i32,
@@ -254,67 +255,107 @@ def ga_ring_allreduce_sim(bufs: Sequence[torch.Tensor], op: int = AVG, part_elem
 
 
 # ------------------------------------------------------------------ zero-copy fusion ring
-def ga_fusion_ring_plan(h_tensors: np.ndarray, h_ptrs: np.ndarray, P: int, dt: int, fill: int) -> int:
-    """Host-only: checks the table of one fusion buffer (FTENSOR_DTYPE rows
-    in buffer order; h_ptrs uint64 [n_tensors, P]), fills vstart and vec in
-    place, returns the number of work vectors."""
+FUSION_BLOCK = 256          # GA_FUSION_BLOCK
+
+
+def fusion_block_bytes(P: int) -> int:
+    """GA_FUSION_BLOCK_BYTES(P): a 16-byte header and P pointers."""
+    return 16 + 8 * P
+
+
+def _fills(fill: Sequence[int]):
+    return (C.c_int64 * max(len(fill), 1))(*[int(f) for f in fill])
+
+
+def ga_fusion_ring_plan(h_tensors: np.ndarray, h_ptrs: np.ndarray, P: int, dt: int,
+                        fill: Sequence[int], part_elems: int = 0, mode: int = RING_FUSED) -> np.ndarray:
+    """Host-only: the planned work blocks (a uint8 array of n_blocks x
+    fusion_block_bytes(P)) of a table (FTENSOR_DTYPE rows, buffer by buffer
+    in buffer order; h_ptrs uint64 [n_tensors, P]) for the given ring
+    geometry."""
     if h_tensors.dtype != FTENSOR_DTYPE or not h_tensors.flags.c_contiguous:
         raise TypeError("h_tensors must be a contiguous FTENSOR_DTYPE array")
     h_ptrs = np.ascontiguousarray(h_ptrs, dtype=np.uint64)
     if h_ptrs.size != h_tensors.size * P:
         raise ValueError("h_ptrs must hold n_tensors x P pointers")
+    L = load()
+    args = (h_tensors.ctypes.data if h_tensors.size else None,
+            h_ptrs.ctypes.data if h_ptrs.size else None, h_tensors.size, P, dt, _fills(fill),
+            len(fill), part_elems, mode)
     n = C.c_int64(0)
-    _check(load().ga_fusion_ring_plan(h_tensors.ctypes.data if h_tensors.size else None,
-                                      h_ptrs.ctypes.data if h_ptrs.size else None,
-                                      h_tensors.size, P, dt, fill, C.byref(n)))
-    return int(n.value)
+    _check(L.ga_fusion_ring_plan(*args, None, 0, C.byref(n)))
+    work = np.zeros(max(n.value, 1) * fusion_block_bytes(P), dtype=np.uint8)
+    _check(L.ga_fusion_ring_plan(*args, work.ctypes.data, n.value, C.byref(n)))
+    return work[:n.value * fusion_block_bytes(P)]
 
 
 class FusionRing:
-    """Tensor Fusion without the fusion buffers: for every buffer of a plan,
-    the table of its tensors and the P workers' pointers to them, checked
-    and uploaded once; allreduce() then folds each buffer in place in the
-    workers' tensors (one launch per buffer)."""
+    """Tensor Fusion without the fusion buffers: the table of a plan's
+    tensors (buffer id, offset, size) and the P workers' pointers to them.
+    allreduce() folds every buffer of the plan in place in the workers'
+    tensors in one launch; allreduce_buffer(k) folds buffer k alone, as a
+    caller does when buffers are reduced as they fill. The work blocks of
+    each (buffers, mode, part_elems) are planned on the host and uploaded on
+    first use."""
 
     def __init__(self, worker_tensors: List[List[torch.Tensor]], buf_of: Sequence[int],
                  off_of: Sequence[int], fill: Sequence[int]):
         self.P = len(worker_tensors)
         self.dt = _dt(worker_tensors[0][0])
         self.fill = [int(f) for f in fill]
-        device = worker_tensors[0][0].device
-        self.bufs = []
-        for k, f in enumerate(self.fill):
-            ts = sorted((int(off_of[t]), t) for t in range(len(buf_of)) if buf_of[t] == k)
-            h = np.zeros(len(ts), dtype=FTENSOR_DTYPE)
-            ptrs = np.zeros((len(ts), self.P), dtype=np.uint64)
-            for r, (off, t) in enumerate(ts):
-                h[r]["start"] = off
-                h[r]["n"] = worker_tensors[0][t].numel()
-                for i in range(self.P):
-                    x = worker_tensors[i][t]
-                    if _dt(x) != self.dt or x.numel() != h[r]["n"]:
-                        raise TypeError("workers' tensors must agree in size and data type")
-                    ptrs[r, i] = _dev(x, "tensor")
-            n_work = ga_fusion_ring_plan(h, ptrs, self.P, self.dt, f)
-            d_t = torch.from_numpy(h.view(np.uint8).copy()).to(device)
-            d_p = torch.from_numpy(ptrs.view(np.uint8).reshape(-1).copy()).to(device)
-            self.bufs.append((d_t, d_p, len(ts), n_work, f))
+        self.device = worker_tensors[0][0].device
+        rows = sorted((int(buf_of[t]), int(off_of[t]), t) for t in range(len(buf_of)))
+        self._rows = rows
+        self._ptrs = np.zeros((len(rows), self.P), dtype=np.uint64)
+        self._sizes = []
+        for r, (_, _, t) in enumerate(rows):
+            n = worker_tensors[0][t].numel()
+            for i in range(self.P):
+                x = worker_tensors[i][t]
+                if _dt(x) != self.dt or x.numel() != n:
+                    raise TypeError("workers' tensors must agree in size and data type")
+                self._ptrs[r, i] = _dev(x, "tensor")
+            self._sizes.append(n)
+        self._work = {}
+        self._plan(None, RING_FUSED, 0)        # checks the table now
 
-    def allreduce_buffer(self, k: int, op: int = AVG, mode: int = RING_FUSED, part_elems: int = 0,
-                         stream=None) -> dict:
-        d_t, d_p, nt, n_work, f = self.bufs[k]
+    def _plan(self, only: Optional[int], mode: int, part_elems: int):
+        """The uploaded work of every buffer (only = None) or of buffer
+        `only`, renumbered as buffer 0 of a one-buffer table."""
+        key = (only, mode, part_elems)
+        if key not in self._work:
+            rows = [q for q, (b, _, _) in enumerate(self._rows) if only is None or b == only]
+            h = np.zeros(len(rows), dtype=FTENSOR_DTYPE)
+            for r, q in enumerate(rows):
+                k, off, _ = self._rows[q]
+                h[r]["buf"] = 0 if only is not None else k
+                h[r]["start"] = off
+                h[r]["n"] = self._sizes[q]
+            fill = [self.fill[only]] if only is not None else self.fill
+            work = ga_fusion_ring_plan(h, self._ptrs[rows], self.P, self.dt, fill, part_elems, mode)
+            n_blocks = work.size // fusion_block_bytes(self.P)
+            d_w = torch.from_numpy(work.copy() if work.size else np.zeros(8, np.uint8)).to(self.device)
+            self._work[key] = (d_w, n_blocks, fill)
+        return self._work[key]
+
+    def _run(self, only, op, mode, part_elems, stream) -> dict:
+        d_w, n_blocks, fill = self._plan(only, mode, part_elems)
         st = RingStats()
-        _check(load().ga_fusion_ring_allreduce(d_t.data_ptr() if nt else None,
-                                               d_p.data_ptr() if nt else None, nt, n_work, self.P,
-                                               f, self.dt, op, mode, part_elems, C.byref(st),
-                                               _stream(stream)))
+        _check(load().ga_fusion_ring_allreduce(d_w.data_ptr(), n_blocks, self.P, self.dt, op,
+                                               _fills(fill), len(fill), part_elems, mode,
+                                               C.byref(st), _stream(stream)))
         return {"steps": st.steps, "bytes_sent_per_worker": st.bytes_sent_per_worker,
                 "hbm_bytes": st.hbm_bytes, "launches": st.launches}
 
     def allreduce(self, op: int = AVG, mode: int = RING_FUSED, part_elems: int = 0,
-                  stream=None) -> None:
-        for k in range(len(self.bufs)):
-            self.allreduce_buffer(k, op, mode, part_elems, stream)
+                  stream=None) -> dict:
+        """Every buffer of the plan, one launch."""
+        return self._run(None, op, mode, part_elems, stream)
+
+    def allreduce_buffer(self, k: int, op: int = AVG, mode: int = RING_FUSED, part_elems: int = 0,
+                         stream=None) -> dict:
+        """Buffer k alone, one launch."""
+        return self._run(k, op, mode, part_elems, stream)
 
 
 # ------------------------------------------------------------------ THC

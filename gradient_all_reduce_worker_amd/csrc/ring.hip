@@ -31,6 +31,7 @@
 // loads; the few workgroups straddling a chunk or partition boundary, the
 // ragged tail and unaligned buffers take a per-element path.
 #include <algorithm>
+#include <cstring>
 #include <utility>
 #include <vector>
 
@@ -300,79 +301,39 @@ __global__ __launch_bounds__(kThreads) void ring_fused_elem_kernel(PtrTable bufs
 
 // ---------------------------------------------------------------- zero-copy fusion ring
 
-// Largest t with T[t].vstart <= u: the tensor holding work vector u.
-__device__ __forceinline__ int64_t tensor_of(const ga_fusion_tensor* T, int64_t nt, int64_t u) {
-    int64_t lo = 0, hi = nt - 1;
-    while (lo < hi) {
-        const int64_t mid = (lo + hi + 1) >> 1;
-        if (T[mid].vstart <= u) lo = mid;
-        else hi = mid - 1;
-    }
-    return lo;
-}
+static_assert(GA_FUSION_BLOCK == kThreads, "one fusion-ring block per workgroup");
 
-// Tensor Fusion without the copies: the fold of a fusion buffer is taken at
-// each tensor's own memory. Work vector u is 16 bytes of one tensor (its
-// last one possibly short); its elements sit at buffer offsets start + j,
-// which decide the partition, chunk and so the fold order, exactly as in the
-// packed buffer. A workgroup walks `blocks` consecutive blocks of kThreads
-// vectors; the tensor of its first vector is found by binary search once,
-// later ones by stepping forward. A block whose vectors are
-// whole, lie in one tensor with 16-byte aligned copies, and share one chunk
-// folds with one rotation and the tensor's pointers read once; any other
-// goes vector by vector.
-template <ga_dtype DT, bool DUAL>
-__global__ __launch_bounds__(kThreads) void fusion_ring_kernel(const ga_fusion_tensor* __restrict__ T,
-                                                               void* const* __restrict__ ptrs,
-                                                               int64_t nt, int64_t n_work, int P,
-                                                               int64_t fill, int64_t plen, int blocks,
-                                                               Div div) {
-    using E = Elem<DT>;
-    constexpr int V = E::kVec;
-    const int nch = DUAL ? 2 * P : P;
-    const int64_t w0 = (int64_t)blockIdx.x * kThreads * blocks;
-    const int64_t w1 = min(w0 + (int64_t)kThreads * blocks, n_work);
-    int64_t t0 = tensor_of(T, nt, w0);
-    for (int64_t u0 = w0; u0 < w1; u0 += kThreads) {
-        const int64_t u1 = min(u0 + (int64_t)kThreads, w1);
-        while (t0 + 1 < nt && T[t0 + 1].vstart <= u0) t0++;        // tensor of u0
-        int64_t tl = t0;                                            // tensor of u1 - 1
-        while (tl + 1 < nt && T[tl + 1].vstart <= u1 - 1) tl++;
-        if (tl == t0 && T[t0].vec) {
-            const ga_fusion_tensor d = T[t0];
-            const int64_t j0 = u0 - d.vstart, j1 = u1 - d.vstart;   // vectors of the tensor
-            if (j1 * V <= d.n) {
-                const Where first = locate(d.start + j0 * V, fill, plen, nch);
-                const Where last = locate(d.start + j1 * V - 1, fill, plen, nch);
-                if (first.part == last.part && first.chunk == last.chunk) {
-                    const RowPtrs row{ptrs + t0 * P};
-                    int64_t v[1] = {j0 + threadIdx.x};
-                    bool ok[1] = {v[0] < j1};
-                    const Rot rt = rot_of<DUAL>(first.chunk, P);
-                    if (P <= 16) fold_uniform<DT, 1, 16>(row, P, v, ok, rt, div);
-                    else fold_uniform<DT, 1, 8>(row, P, v, ok, rt, div);
-                    continue;
-                }
-            }
-        }
-        const int64_t u = u0 + threadIdx.x;
-        if (u >= u1) continue;
-        int64_t t = t0;                                             // t0 <= tensor of u <= tl
-        while (t < tl && T[t + 1].vstart <= u) t++;
-        const ga_fusion_tensor d = T[t];
-        const RowPtrs row{ptrs + t * P};
-        const int64_t j = u - d.vstart;
-        const int64_t e0 = j * V, e1 = min(e0 + V, d.n);            // tensor elements
-        if (d.vec && e1 - e0 == V) {
-            const Where a = locate(d.start + e0, fill, plen, nch);
-            const Where b = locate(d.start + e1 - 1, fill, plen, nch);
-            if (a.part == b.part && a.chunk == b.chunk) {
-                fold_vec<DT>(row, P, j, rot_of<DUAL>(a.chunk, P), div);
-                continue;
-            }
-        }
-        for (int64_t e = e0; e < e1; e++)
-            fold_elem<DT>(row, P, e, rot_of<DUAL>(locate(d.start + e, fill, plen, nch).chunk, P), div);
+// Header of a planned block of the zero-copy fusion ring; the P workers'
+// pointers (to the block's first vector or element) follow it.
+struct FusionBlock {
+    int32_t count;   // vectors (kind 0) or elements (kind 1), 1..GA_FUSION_BLOCK
+    int32_t start;   // first worker of the fold
+    int32_t dir;     // +1 or -1
+    int32_t kind;    // 0: 16-byte vectors, 1: single elements
+};
+static_assert(sizeof(FusionBlock) == 16, "block header is 16 bytes");
+
+// Tensor Fusion without the copies: every fusion buffer of a plan folded at
+// its tensors' own memory, all buffers in one launch. The host cut every
+// tensor at its buffer's partition and chunk boundaries, so each block lies
+// in one chunk of one tensor: one fold start and direction for the whole
+// workgroup, the P copies' addresses read once (scalar loads of the block),
+// thread i folding vector (or element) i of the block.
+template <ga_dtype DT>
+__global__ __launch_bounds__(kThreads) void fusion_ring_kernel(const uint8_t* __restrict__ work,
+                                                               int64_t stride, int P, Div div) {
+    const uint8_t* blk = work + (int64_t)blockIdx.x * stride;
+    const FusionBlock h = *reinterpret_cast<const FusionBlock*>(blk);
+    const RowPtrs row{reinterpret_cast<void* const*>(blk + sizeof(FusionBlock))};
+    const Rot rt{h.start, h.dir};
+    const int i = threadIdx.x;
+    if (h.kind == 0) {
+        int64_t v[1] = {i};
+        bool ok[1] = {i < h.count};
+        if (P <= 16) fold_uniform<DT, 1, 16>(row, P, v, ok, rt, div);
+        else fold_uniform<DT, 1, 8>(row, P, v, ok, rt, div);
+    } else if (i < h.count) {
+        fold_elem<DT>(row, P, i, rt, div);
     }
 }
 
@@ -499,11 +460,12 @@ FoldShape fold_shape(int P, int64_t total_bytes) {
     return {4, 4, big ? cap_workgroups_per_cu(4) : 0};
 }
 
-// The zero-copy fusion ring: two resident workgroups per CU on large
-// buffers (ResNet-101 buffers, 16 workers: 0.60 -> 0.64 of 8 TB/s).
-size_t fusion_cap(int64_t total_bytes) {
-    return total_bytes >= (int64_t)1 << 30 ? cap_workgroups_per_cu(2) : 0;
-}
+// The zero-copy fusion ring: a workgroup starts with scalar loads of its
+// planned block, as cheaply as the flat fold, so the flat fold's residency
+// caps apply (ResNet-101 plan, 16 workers: 0.65 of 8 TB/s at two resident
+// workgroups per CU, 0.685 at one; the flat ring over the fusion buffers
+// 0.684).
+size_t fusion_cap(int P, int64_t total_bytes) { return fold_shape(P, total_bytes).lds; }
 
 // The fused fold over the whole buffer: the vector kernel over 16-byte
 // vectors when every buffer is 16-byte aligned, the element kernel for the
@@ -647,55 +609,150 @@ extern "C" ga_status ga_ring_allreduce_sim(void* const* bufs, int32_t P, int64_t
 
 // ---------------------------------------------------------------- zero-copy fusion ring (host)
 
-extern "C" ga_status ga_fusion_ring_plan(ga_fusion_tensor* h_tensors, void* const* h_ptrs,
-                                         int64_t n_tensors, int32_t P, ga_dtype dt, int64_t fill,
-                                         int64_t* n_work) {
+namespace {
+
+// Appends the blocks of one piece [a, b) of tensor t (tensor elements, one
+// chunk: fold start r, direction dir) to the work array (or only counts).
+struct WorkWriter {
+    uint8_t* out;
+    int64_t cap;
+    int64_t n = 0;
+    int P;
+    int64_t es;
+    void* const* ptrs;     // the tensor's P pointers
+    void add(int kind, int64_t first, int64_t count, Rot rt) {
+        if (out && n < cap) {
+            uint8_t* blk = out + n * (int64_t)GA_FUSION_BLOCK_BYTES(P);
+            FusionBlock h{(int32_t)count, rt.r, rt.dir, kind};
+            memcpy(blk, &h, sizeof h);
+            const int64_t unit = kind == 0 ? 16 : es;
+            for (int i = 0; i < P; i++) {
+                void* q = static_cast<uint8_t*>(ptrs[i]) + first * unit;
+                memcpy(blk + sizeof h + 8 * i, &q, 8);
+            }
+        }
+        n++;
+    }
+    void span(int kind, int64_t lo, int64_t hi, Rot rt) {      // units [lo, hi)
+        for (int64_t k = lo; k < hi; k += GA_FUSION_BLOCK)
+            add(kind, k, std::min<int64_t>(GA_FUSION_BLOCK, hi - k), rt);
+    }
+    void piece(int64_t a, int64_t b, bool vec, Rot rt) {
+        const int64_t V = 16 / es;
+        const int64_t va = ceil_div(a, V), vb = b / V;         // whole vectors inside [a, b)
+        if (!vec || va >= vb) {
+            span(1, a, b, rt);
+            return;
+        }
+        span(1, a, va * V, rt);
+        span(0, va, vb, rt);
+        span(1, vb * V, b, rt);
+    }
+};
+
+}  // namespace
+
+extern "C" ga_status ga_fusion_ring_plan(const ga_fusion_tensor* h_tensors, void* const* h_ptrs,
+                                         int64_t n_tensors, int32_t P, ga_dtype dt,
+                                         const int64_t* fill, int32_t n_buf, int64_t part_elems,
+                                         ga_ring_mode mode, void* h_work, int64_t cap_blocks,
+                                         int64_t* n_blocks) {
     const char* what = "ga_fusion_ring_plan";
     if (!valid_dtype(dt)) return fail(GA_EINVAL, "%s: unknown dtype %d", what, (int)dt);
     if (P < 1 || P > GA_MAX_WORKERS)
         return fail(GA_EINVAL, "%s: P = %d outside [1, %d]", what, P, GA_MAX_WORKERS);
-    if (n_tensors < 0 || fill < 0 || !n_work) return fail(GA_EINVAL, "%s: bad sizes", what);
+    if (mode == GA_RING_STEPWISE)
+        return fail(GA_ENOTSUP, "%s: the zero-copy ring runs the fused fold only", what);
+    if (mode != GA_RING_FUSED && mode != GA_RING_DUAL)
+        return fail(GA_EINVAL, "%s: unknown mode %d", what, (int)mode);
+    if (n_tensors < 0 || n_buf < 0 || part_elems < 0 || cap_blocks < 0 || !n_blocks)
+        return fail(GA_EINVAL, "%s: bad sizes", what);
     if (n_tensors > 0 && (!h_tensors || !h_ptrs)) return fail(GA_EINVAL, "%s: null table", what);
+    if (n_buf > 0 && !fill) return fail(GA_EINVAL, "%s: null fills", what);
+    for (int32_t k = 0; k < n_buf; k++)
+        if (fill[k] < 0) return fail(GA_EINVAL, "%s: buffer %d has fill %lld", what, k, (long long)fill[k]);
     const int64_t es = (int64_t)elem_size(dt);
-    const int64_t V = 16 / es;
-    int64_t off = 0, nv = 0;
+    const int nch = mode == GA_RING_DUAL ? 2 * P : P;
+    int64_t off = 0;
+    int32_t cur = 0;             // buffer being walked; buffers below it are complete
     std::vector<std::pair<uintptr_t, uintptr_t>> spans;
     spans.reserve((size_t)(n_tensors * P));
+    // the buffer being walked must be complete; buffers before k that no
+    // row lists must be empty
+    auto skip_to = [&](int32_t k) -> ga_status {
+        if (off != fill[cur])
+            return fail(GA_EINVAL, "%s: buffer %d's tensors cover %lld elements, its fill is %lld",
+                        what, cur, (long long)off, (long long)fill[cur]);
+        for (int32_t q = cur + 1; q < k; q++)
+            if (fill[q] != 0)
+                return fail(GA_EINVAL, "%s: buffer %d has fill %lld but no tensors", what, q,
+                            (long long)fill[q]);
+        cur = k;
+        off = 0;
+        return GA_OK;
+    };
+    // first pass: check the table
     for (int64_t t = 0; t < n_tensors; t++) {
-        ga_fusion_tensor& d = h_tensors[t];
+        const ga_fusion_tensor& d = h_tensors[t];
+        if (d.buf < 0 || d.buf >= n_buf || d.buf < cur)
+            return fail(GA_EINVAL, "%s: tensor %lld has buffer %d (buffers [0, %d), never "
+                        "decreasing; the table is at buffer %d)", what, (long long)t, d.buf, n_buf, cur);
+        if (d.buf > cur) {
+            ga_status rc = skip_to(d.buf);
+            if (rc) return rc;
+        }
         if (d.n < 0 || d.start != off)
             return fail(GA_EINVAL, "%s: tensor %lld is not dense in buffer order (start %lld, "
                         "expected %lld)", what, (long long)t, (long long)d.start, (long long)off);
-        int vec = 1;
         for (int i = 0; i < P; i++) {
             const void* q = h_ptrs[t * P + i];
             if (d.n > 0 && (!q || !aligned(q, (uintptr_t)es)))
                 return fail(GA_EINVAL, "%s: tensor %lld, worker %d: null or misaligned pointer",
                             what, (long long)t, i);
-            vec = vec && aligned(q, 16);
             if (d.n > 0) spans.push_back({(uintptr_t)q, (uintptr_t)q + (uintptr_t)(d.n * es)});
         }
-        d.vstart = nv;
-        d.vec = vec;
-        d.reserved = 0;
         off += d.n;
-        nv += ceil_div(d.n, V);
     }
-    if (off != fill)
-        return fail(GA_EINVAL, "%s: tensors cover %lld elements, fill is %lld", what,
-                    (long long)off, (long long)fill);
+    if (n_buf > 0) {
+        ga_status rc = skip_to(n_buf);
+        if (rc) return rc;
+    }
     std::sort(spans.begin(), spans.end());
     for (size_t k = 1; k < spans.size(); k++)
         if (spans[k].first < spans[k - 1].second)
             return fail(GA_EINVAL, "%s: two tensor copies overlap", what);
-    *n_work = nv;
+    // second pass: cut every tensor at its buffer's partition and chunk
+    // boundaries (the chunk rule of the ring: C = ceil(n_p / nch))
+    WorkWriter ww{static_cast<uint8_t*>(h_work), cap_blocks, 0, P, es, nullptr};
+    for (int64_t t = 0; t < n_tensors; t++) {
+        const ga_fusion_tensor& d = h_tensors[t];
+        const int64_t F = fill[d.buf];
+        const int64_t plen = part_elems > 0 ? part_elems : F;
+        bool vec = true;
+        for (int i = 0; i < P; i++) vec = vec && aligned(h_ptrs[t * P + i], 16);
+        ww.ptrs = h_ptrs + t * P;
+        for (int64_t e = d.start; e < d.start + d.n;) {
+            const int64_t p0 = e / plen * plen;
+            const int64_t np = std::min(plen, F - p0);
+            const int64_t C = ceil_div(np, nch);
+            const int c = (int)((e - p0) / C);
+            const int64_t end = std::min(p0 + std::min((int64_t)(c + 1) * C, np), d.start + d.n);
+            const Rot rt = (mode == GA_RING_DUAL && c >= P) ? Rot{c - P, -1} : Rot{c, 1};
+            ww.piece(e - d.start, end - d.start, vec, rt);
+            e = end;
+        }
+    }
+    if (h_work && ww.n > cap_blocks)
+        return fail(GA_EINVAL, "%s: %lld blocks do not fit in %lld", what, (long long)ww.n,
+                    (long long)cap_blocks);
+    *n_blocks = ww.n;
     return GA_OK;
 }
 
-extern "C" ga_status ga_fusion_ring_allreduce(const ga_fusion_tensor* d_tensors, void* const* d_ptrs,
-                                              int64_t n_tensors, int64_t n_work, int32_t P,
-                                              int64_t fill, ga_dtype dt, ga_op op, ga_ring_mode mode,
-                                              int64_t part_elems, ga_ring_stats* st, void* stream) {
+extern "C" ga_status ga_fusion_ring_allreduce(const void* d_work, int64_t n_blocks, int32_t P,
+                                              ga_dtype dt, ga_op op, const int64_t* fill,
+                                              int32_t n_buf, int64_t part_elems, ga_ring_mode mode,
+                                              ga_ring_stats* st, void* stream) {
     const char* what = "ga_fusion_ring_allreduce";
     if (!valid_dtype(dt)) return fail(GA_EINVAL, "%s: unknown dtype %d", what, (int)dt);
     if (op != GA_SUM && op != GA_AVG) return fail(GA_EINVAL, "%s: unknown op %d", what, (int)op);
@@ -705,42 +762,45 @@ extern "C" ga_status ga_fusion_ring_allreduce(const ga_fusion_tensor* d_tensors,
         return fail(GA_EINVAL, "%s: unknown mode %d", what, (int)mode);
     if (P < 1 || P > GA_MAX_WORKERS)
         return fail(GA_EINVAL, "%s: P = %d outside [1, %d]", what, P, GA_MAX_WORKERS);
-    if (n_tensors < 0 || n_work < 0 || fill < 0 || part_elems < 0)
+    if (n_blocks < 0 || n_buf < 0 || part_elems < 0)
         return fail(GA_EINVAL, "%s: negative size", what);
-    if (n_work > 0 && (n_tensors == 0 || fill == 0))
-        return fail(GA_EINVAL, "%s: work without tensors", what);
-    const int64_t es = (int64_t)elem_size(dt);
-    ga_ring_stats s{};
-    if (fill > 0) {
-        const int64_t plen = part_elems > 0 ? part_elems : fill;
-        const int nch = mode == GA_RING_DUAL ? 2 * P : P;
-        auto part_bytes = [&](int64_t n) { return 2 * (int64_t)(P - 1) * (nch / P) * ceil_div(n, nch) * es; };
-        const int64_t bytes = (fill / plen) * part_bytes(plen) + (fill % plen ? part_bytes(fill % plen) : 0);
-        s.steps = 2 * (int64_t)(P - 1);
-        s.bytes_sent_per_worker = bytes;
-        s.hbm_bytes = P > 1 ? 2 * (int64_t)P * fill * es : 0;
+    if (n_buf > 0 && !fill) return fail(GA_EINVAL, "%s: null fills", what);
+    int64_t total = 0;
+    for (int32_t k = 0; k < n_buf; k++) {
+        if (fill[k] < 0) return fail(GA_EINVAL, "%s: negative fill", what);
+        total += fill[k];
     }
-    if (n_work == 0 || P == 1) {
+    if (n_blocks > 0 && total == 0) return fail(GA_EINVAL, "%s: work without tensors", what);
+    const int64_t es = (int64_t)elem_size(dt);
+    const int nch = mode == GA_RING_DUAL ? 2 * P : P;
+    ga_ring_stats s{};
+    {
+        auto part_bytes = [&](int64_t n) { return 2 * (int64_t)(P - 1) * (nch / P) * ceil_div(n, nch) * es; };
+        int64_t bytes = 0;
+        for (int32_t k = 0; k < n_buf; k++) {
+            if (fill[k] == 0) continue;
+            const int64_t plen = part_elems > 0 ? part_elems : fill[k];
+            bytes += (fill[k] / plen) * part_bytes(plen) + (fill[k] % plen ? part_bytes(fill[k] % plen) : 0);
+        }
+        s.steps = total > 0 ? 2 * (int64_t)(P - 1) : 0;
+        s.bytes_sent_per_worker = bytes;
+        s.hbm_bytes = P > 1 ? 2 * (int64_t)P * total * es : 0;
+    }
+    if (n_blocks == 0 || P == 1) {
         if (st) *st = s;
         return GA_OK;
     }
-    if (!d_tensors || !d_ptrs || !aligned(d_tensors, 8) || !aligned(d_ptrs, 8))
-        return fail(GA_EINVAL, "%s: null or misaligned table", what);
-    if (ceil_div(n_work, (int64_t)kThreads) > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: too much work", what);
-    const int64_t plen = part_elems > 0 ? part_elems : fill;
+    if (!d_work || !aligned(d_work, 8)) return fail(GA_EINVAL, "%s: null or misaligned blocks", what);
+    if (n_blocks > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: too many blocks", what);
     Div div{op == GA_AVG, (P & (P - 1)) == 0, (float)P, 1.0f / (float)P};
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    const size_t lds = fusion_cap(2 * (int64_t)P * fill * es);
-    const int blocks = 1;   // measured fastest at every residency (ResNet-101 buffers)
-    const dim3 grid((unsigned)ceil_div(n_work, (int64_t)kThreads * blocks));
-    if (dt == GA_F32 && mode == GA_RING_DUAL)
-        hipLaunchKernelGGL((fusion_ring_kernel<GA_F32, true>), grid, dim3(kThreads), lds, hs, d_tensors, d_ptrs, n_tensors, n_work, P, fill, plen, blocks, div);
-    else if (dt == GA_F32)
-        hipLaunchKernelGGL((fusion_ring_kernel<GA_F32, false>), grid, dim3(kThreads), lds, hs, d_tensors, d_ptrs, n_tensors, n_work, P, fill, plen, blocks, div);
-    else if (mode == GA_RING_DUAL)
-        hipLaunchKernelGGL((fusion_ring_kernel<GA_BF16, true>), grid, dim3(kThreads), lds, hs, d_tensors, d_ptrs, n_tensors, n_work, P, fill, plen, blocks, div);
+    const size_t lds = fusion_cap(P, 2 * (int64_t)P * total * es);
+    const int64_t stride = (int64_t)GA_FUSION_BLOCK_BYTES(P);
+    const uint8_t* w = static_cast<const uint8_t*>(d_work);
+    if (dt == GA_F32)
+        hipLaunchKernelGGL((fusion_ring_kernel<GA_F32>), dim3((unsigned)n_blocks), dim3(kThreads), lds, hs, w, stride, P, div);
     else
-        hipLaunchKernelGGL((fusion_ring_kernel<GA_BF16, false>), grid, dim3(kThreads), lds, hs, d_tensors, d_ptrs, n_tensors, n_work, P, fill, plen, blocks, div);
+        hipLaunchKernelGGL((fusion_ring_kernel<GA_BF16>), dim3((unsigned)n_blocks), dim3(kThreads), lds, hs, w, stride, P, div);
     ga_status rc = check_launch(what);
     if (rc) return rc;
     s.launches = 1;

@@ -2,8 +2,8 @@
 
 A step runs, in this order, on the current stream:
   fused workloads (Tensor Fusion, Horovod page section 3.4):
-      zero_copy (default): ring-average each fusion buffer in place in the
-      workers' tensors, one launch per buffer, no copies;
+      zero_copy (default): ring-average every fusion buffer in place in the
+      workers' tensors, all buffers in one launch, no copies;
       else: pack every worker's tensors into its fusion buffers (one
       launch), ring-average each fusion buffer across the P workers, unpack
       the averages back into the tensors (one launch); a tensor larger than
@@ -212,9 +212,8 @@ class Pipeline:
     def step(self, timer: Optional[StageTimer] = None) -> None:
         w = self.w
         if w.fused and self.zero_copy:
-            for k in range(len(self.fill)):
-                _call(timer, "fusion_ring", self.fring.allreduce_buffer, k, ga.AVG, self.ring_mode,
-                      w.ring_part_elems)
+            _call(timer, "fusion_ring", self.fring.allreduce, ga.AVG, self.ring_mode,
+                  w.ring_part_elems)
             return
         if w.fused:
             if self.tables is not None:
@@ -305,7 +304,7 @@ class Pipeline:
         w, P, N, s = self.w, self.P, self.N, self.w.elem_bytes
         out = {}
         if w.fused and self.zero_copy:
-            out["fusion_ring"] = 2.0 * P * N * s / len(self.fill)    # mean over the buffers
+            out["fusion_ring"] = 2.0 * P * N * s                     # every buffer, one launch
             return out
         if w.fused:
             moved = sum(int(n) for t, n in enumerate(w.sizes) if self.buf_of[t] not in self.alone)

@@ -194,50 +194,76 @@ ga_status ga_ring_allreduce_sim(void* const* bufs, int32_t P, int64_t N, ga_dtyp
 /* ------------------------------------------------------------------ */
 
 /*
- * One tensor of a fusion buffer: elements [start, start + n) of the buffer
- * the fusion plan assigned it to (ga_fuse_plan's offsets). vstart and vec
- * are filled in by ga_fusion_ring_plan.
+ * One tensor of a fusion plan: elements [start, start + n) of fusion buffer
+ * `buf` (ga_fuse_plan's buffer ids and offsets). A table lists the tensors
+ * of one or more buffers, buffer by buffer in increasing id, each buffer's
+ * tensors in offset order.
  */
 typedef struct {
-    int64_t start;    /* offset in the fusion buffer, elements */
+    int64_t start;    /* offset in its fusion buffer, elements */
     int64_t n;        /* elements */
-    int64_t vstart;   /* first work vector (16 bytes of the tensor) */
-    int32_t vec;      /* 1: all P copies are 16-byte aligned */
+    int32_t buf;      /* fusion buffer id */
     int32_t reserved; /* 0 */
 } ga_fusion_tensor;
 
-/*
- * ga_fusion_ring_plan -- host-only check and completion of the table of one
- * fusion buffer before ga_fusion_ring_allreduce: the n_tensors entries must
- * be in buffer order and dense (start[0] = 0, start[t + 1] = start[t] +
- * n[t], the last ending at fill); h_ptrs is a host array of n_tensors x P
- * worker pointers (tensor-major: h_ptrs[t P + i] is worker i's copy of
- * tensor t), each non-null and aligned to the element size, and no two of
- * the P n_tensors regions may overlap. Fills vstart and vec; *n_work
- * receives the number of work vectors. Enqueues nothing.
- */
-ga_status ga_fusion_ring_plan(ga_fusion_tensor* h_tensors, void* const* h_ptrs, int64_t n_tensors,
-                              int32_t P, ga_dtype dt, int64_t fill, int64_t* n_work);
+/* Work vectors (or elements) per block of the zero-copy fusion ring; one
+ * workgroup folds one block. */
+#define GA_FUSION_BLOCK 256
+/* Bytes of one planned block for P workers: a 16-byte header and P device
+ * pointers (the layout is internal to the library). */
+#define GA_FUSION_BLOCK_BYTES(P) (16 + 8 * (size_t)(P))
 
 /*
- * ga_fusion_ring_allreduce -- in place in every worker's tensors: exactly
- * what ga_fuse_pack, ga_ring_allreduce_sim over the fusion buffer (mode
- * GA_RING_FUSED or GA_RING_DUAL, same op and part_elems) and ga_fuse_unpack
- * leave in them, bit for bit, without the fusion buffers: each element is
- * folded at its tensor's address in the order its buffer offset gives.
- * HBM traffic 2 P fill elem_bytes instead of 6 P fill elem_bytes.
- *   d_tensors, d_ptrs  device copies of the planned table and pointers
- *   n_work             from ga_fusion_ring_plan
- *   mode               GA_RING_FUSED or GA_RING_DUAL; GA_RING_STEPWISE ->
- *                      GA_ENOTSUP
- *   st                 optional accounting, as for ga_ring_allreduce_sim
- * The device tables are trusted (ga_fusion_ring_plan checked their host
- * originals); a table that does not match n_work or fill is undefined.
+ * ga_fusion_ring_plan -- host only: the work of the zero-copy fusion ring
+ * over the buffers a table lists, for ring geometry (part_elems, mode).
+ *   h_tensors   n_tensors rows; each row's buf in [0, n_buf), never
+ *               decreasing down the table; the rows of a buffer dense in
+ *               buffer order (the first starts at 0, start[t + 1] = start[t]
+ *               + n[t]) and ending at fill[buf]; a buffer listed in no row
+ *               must have fill 0
+ *   h_ptrs      n_tensors x P device pointers, tensor-major (h_ptrs[t P + i]
+ *               is worker i's copy of tensor t), each non-null and aligned
+ *               to the element size; no two of the P n_tensors regions may
+ *               overlap
+ *   fill        host array of n_buf buffer lengths, elements
+ *   part_elems  partition length inside every buffer (0: one partition per
+ *               buffer); mode GA_RING_FUSED or GA_RING_DUAL (the chunks and
+ *               fold directions of ga_ring_allreduce_sim)
+ *   h_work      host array of cap_blocks blocks of GA_FUSION_BLOCK_BYTES(P)
+ *               bytes, or null to count only; *n_blocks receives the count
+ * Every tensor is cut at its buffer's partition and chunk boundaries; each
+ * piece becomes blocks of up to GA_FUSION_BLOCK whole 16-byte vectors (when
+ * all P copies are 16-byte aligned) plus blocks of up to GA_FUSION_BLOCK
+ * elements for its unaligned ends, each block carrying its fold's first
+ * worker and direction and the P copies' addresses of its first vector or
+ * element. Enqueues nothing; GA_EINVAL if cap_blocks is too small.
  */
-ga_status ga_fusion_ring_allreduce(const ga_fusion_tensor* d_tensors, void* const* d_ptrs,
-                                   int64_t n_tensors, int64_t n_work, int32_t P, int64_t fill,
-                                   ga_dtype dt, ga_op op, ga_ring_mode mode, int64_t part_elems,
-                                   ga_ring_stats* st, void* stream);
+ga_status ga_fusion_ring_plan(const ga_fusion_tensor* h_tensors, void* const* h_ptrs,
+                              int64_t n_tensors, int32_t P, ga_dtype dt, const int64_t* fill,
+                              int32_t n_buf, int64_t part_elems, ga_ring_mode mode, void* h_work,
+                              int64_t cap_blocks, int64_t* n_blocks);
+
+/*
+ * ga_fusion_ring_allreduce -- in place in every worker's tensors, for every
+ * buffer of the plan, in ONE launch: exactly what ga_fuse_pack,
+ * ga_ring_allreduce_sim over each fusion buffer (the plan's part_elems and
+ * mode, this op) and ga_fuse_unpack leave in them, bit for bit, without
+ * the fusion buffers: each element is folded at its tensor's address in
+ * the order its offset in its buffer gives. HBM traffic 2 P (sum of fills)
+ * elem_bytes instead of 6 P (sum of fills) elem_bytes.
+ *   d_work, n_blocks   device copy of ga_fusion_ring_plan's blocks
+ *   P, dt              as planned
+ *   fill, n_buf, part_elems, mode
+ *                      as planned (the accounting and the launch shape);
+ *                      GA_RING_STEPWISE -> GA_ENOTSUP
+ *   st                 optional accounting summed over the buffers (steps:
+ *                      2 (P - 1) per ring; launches: 1)
+ * The device blocks are trusted (ga_fusion_ring_plan made them from checked
+ * tables); blocks that do not come from it for these P and dt are undefined.
+ */
+ga_status ga_fusion_ring_allreduce(const void* d_work, int64_t n_blocks, int32_t P, ga_dtype dt,
+                                   ga_op op, const int64_t* fill, int32_t n_buf, int64_t part_elems,
+                                   ga_ring_mode mode, ga_ring_stats* st, void* stream);
 
 /* ------------------------------------------------------------------ */
 /* THC uniform stochastic quantization  ([THC] 2-4, Algorithm 1)        */

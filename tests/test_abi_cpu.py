@@ -261,33 +261,107 @@ def test_rht_norm_quantize_argument_errors_before_enqueue():
     assert b"thc_rht_norm_quantize" in L.ga_last_error()
     assert call(N=0) == 0
 
-def _ftable(sizes):
+def _ftable(sizes, bufs=None):
+    """Rows of a plan table for tensors of the given sizes, all in buffer 0
+    or in the given buffers (non-decreasing); returns the table and the
+    buffers' fills."""
+    bufs = [0] * len(sizes) if bufs is None else bufs
     h = np.zeros(len(sizes), dtype=nat.FTENSOR_DTYPE)
-    off = 0
-    for r, n in enumerate(sizes):
-        h[r]["start"], h[r]["n"] = off, n
-        off += n
-    return h, off
+    fill = [0] * (max(bufs) + 1 if bufs else 1)
+    for r, (n, k) in enumerate(zip(sizes, bufs)):
+        h[r]["buf"], h[r]["start"], h[r]["n"] = k, fill[k], n
+        fill[k] += n
+    return h, fill
 
 
-def test_fusion_ring_plan_fills_vectors_and_alignment():
-    sizes = [5, 8, 0, 13, 4]
-    h, fill = _ftable(sizes)
-    P = 3
+def _fake_ptrs(sizes, P, es, misaligned=()):
+    """Disjoint, 256-byte spaced host addresses for every (tensor, worker);
+    (t, i) in `misaligned` is moved one element off its 16-byte boundary."""
     ptrs = np.zeros((len(sizes), P), dtype=np.uint64)
     base = 0x100000
     for t, n in enumerate(sizes):
         for i in range(P):
-            ptrs[t, i] = base
-            base += (n * 4 + 255) // 256 * 256 + 256
-    ptrs[3, 1] += 4                    # one misaligned (by 16) copy of tensor 3
-    n_work = nat.ga_fusion_ring_plan(h, ptrs, P, nat.F32, fill)
-    want_v = np.cumsum([0] + [-(-n // 4) for n in sizes])
-    assert n_work == want_v[-1]
-    assert h["vstart"].tolist() == want_v[:-1].tolist()
-    assert h["vec"].tolist() == [1, 1, 1, 0, 1]
-    h2, _ = _ftable(sizes)
-    assert nat.ga_fusion_ring_plan(h2, ptrs, P, nat.BF16, fill) == sum(-(-n // 8) for n in sizes)
+            ptrs[t, i] = base + (es if (t, i) in misaligned else 0)
+            base += (n * es + 255) // 256 * 256 + 512
+    return ptrs
+
+
+def _decode(work, P):
+    bb = nat.fusion_block_bytes(P)
+    n = work.size // bb
+    rows = work.reshape(n, bb)
+    hdr = rows[:, :16].copy().view(np.int32).reshape(n, 4)          # count, start, dir, kind
+    ptr = rows[:, 16:].copy().view(np.uint64).reshape(n, P)
+    return hdr, ptr
+
+
+def _chunk_rule(e, F, part, P, dual):
+    """Fold start and direction of buffer element e (the ring's chunks:
+    C = ceil(n_p / nch) per partition; the dual ring's upper sub-chunks
+    fold the other way)."""
+    plen = part if part > 0 else F
+    p0 = e // plen * plen
+    n_p = min(plen, F - p0)
+    nch = 2 * P if dual else P
+    C = -(-n_p // nch)
+    c = (e - p0) // C
+    return (c - P, -1) if dual and c >= P else (c, 1)
+
+
+@pytest.mark.parametrize("dt", [nat.F32, nat.BF16])
+@pytest.mark.parametrize("mode", [nat.RING_FUSED, nat.RING_DUAL])
+@pytest.mark.parametrize("part", [0, 7, 1000])
+def test_fusion_ring_plan_covers_every_element_once_in_its_chunk(part, mode, dt):
+    """Decoding the planned blocks: every element of every tensor is folded
+    by exactly one block thread, with its chunk's fold start and direction;
+    vector blocks only where all P copies are 16-byte aligned; every block
+    holds 1..256 vectors or elements; worker i's address is worker 0's moved
+    by the same offset inside its own copy."""
+    rng = np.random.default_rng(part + 10 * mode + 100 * dt)
+    P, es = 3, (4 if dt == nat.F32 else 2)
+    V = 16 // es
+    sizes = [int(v) for v in rng.integers(0, 900, size=30)] + [0, 1, 3000]
+    bufs = sorted(int(v) for v in rng.integers(0, 3, size=len(sizes)))
+    h, fill = _ftable(sizes, bufs)
+    ptrs = _fake_ptrs(sizes, P, es, misaligned={(4, 1), (9, 0)})
+    work = nat.ga_fusion_ring_plan(h, ptrs, P, dt, fill, part, mode)
+    hdr, ptr = _decode(work, P)
+    assert np.all((hdr[:, 0] >= 1) & (hdr[:, 0] <= nat.FUSION_BLOCK))
+    seen = {}
+    for b in range(hdr.shape[0]):
+        count, start, d, kind = (int(v) for v in hdr[b])
+        if kind == 0:
+            assert all(int(ptr[b, i]) % 16 == 0 for i in range(P))
+            addrs = [int(ptr[b, 0]) + v * 16 + j * es for v in range(count) for j in range(V)]
+        else:
+            assert kind == 1
+            addrs = [int(ptr[b, 0]) + e * es for e in range(count)]
+        for a in addrs:
+            assert a not in seen, hex(a)
+            seen[a] = (start, d, b)
+    want = {}
+    for t, n in enumerate(sizes):
+        F = fill[bufs[t]]
+        for j in range(n):
+            want[int(ptrs[t, 0]) + j * es] = _chunk_rule(int(h[t]["start"]) + j, F, part, P,
+                                                         mode == nat.RING_DUAL)
+    assert set(seen) == set(want)
+    for a, (start, d, b) in seen.items():
+        assert (start, d) == want[a], hex(a)
+    # worker i's pointer: same offset inside worker i's copy of the tensor
+    t_of = {}
+    for t, n in enumerate(sizes):
+        for j in range(n):
+            t_of[int(ptrs[t, 0]) + j * es] = t
+    for b in range(hdr.shape[0]):
+        t = t_of[int(ptr[b, 0])]
+        off = int(ptr[b, 0]) - int(ptrs[t, 0])
+        for i in range(P):
+            assert int(ptr[b, i]) - int(ptrs[t, i]) == off
+    # the misaligned tensors are folded element by element only
+    for t in (4, 9):
+        blocks = {seen[int(ptrs[t, 0]) + j * es][2] for j in range(sizes[t])}
+        assert all(hdr[b, 3] == 1 for b in blocks)
 
 
 def test_fusion_ring_plan_errors():
@@ -296,7 +370,17 @@ def test_fusion_ring_plan_errors():
     ptrs = np.array([[0x10000, 0x20000], [0x30000, 0x40000]], dtype=np.uint64)
     h, fill = _ftable(sizes)
     with pytest.raises(nat.GAError):                              # fill mismatch
-        nat.ga_fusion_ring_plan(h, ptrs, P, nat.F32, fill + 1)
+        nat.ga_fusion_ring_plan(h, ptrs, P, nat.F32, [fill[0] + 1])
+    h, fill = _ftable(sizes, [0, 1])
+    with pytest.raises(nat.GAError):                              # a buffer id out of range
+        nat.ga_fusion_ring_plan(h, ptrs, P, nat.F32, fill[:1])
+    with pytest.raises(nat.GAError):                              # a listed-nowhere buffer not empty
+        nat.ga_fusion_ring_plan(h, ptrs, P, nat.F32, fill + [5])
+    assert nat.ga_fusion_ring_plan(h, ptrs, P, nat.F32, fill + [0]).size > 0
+    h, fill = _ftable(sizes, [0, 1])
+    h[0]["buf"], h[1]["buf"] = 1, 0                               # buffers out of order
+    with pytest.raises(nat.GAError):
+        nat.ga_fusion_ring_plan(h, ptrs, P, nat.F32, [20, 10])
     h, fill = _ftable(sizes)
     h[1]["start"] += 1                                            # not dense
     with pytest.raises(nat.GAError):
@@ -310,29 +394,46 @@ def test_fusion_ring_plan_errors():
     bad[0, 0] = 0x10002                                           # misaligned for fp32
     with pytest.raises(nat.GAError):
         nat.ga_fusion_ring_plan(h, bad, P, nat.F32, fill)
-    assert nat.ga_fusion_ring_plan(h, bad, P, nat.BF16, fill) > 0
+    assert nat.ga_fusion_ring_plan(h, bad, P, nat.BF16, fill).size > 0
     bad = ptrs.copy()
     bad[1, 0] = 0
     with pytest.raises(nat.GAError):
         nat.ga_fusion_ring_plan(h, bad, P, nat.F32, fill)
+    with pytest.raises(nat.GAError) as e:                         # stepwise has no zero-copy form
+        nat.ga_fusion_ring_plan(h, ptrs, P, nat.F32, fill, 0, nat.RING_STEPWISE)
+    assert e.value.status == ENOTSUP
+    L = nat.load()
+    n = C.c_int64(0)
+    F = (C.c_int64 * 1)(30)
+    assert L.ga_fusion_ring_plan(h.ctypes.data, ptrs.ctypes.data, 2, P, nat.F32, F, 1, 0, 0,
+                                 0x1000, 0, C.byref(n)) == EINVAL      # no room for the blocks
     h0 = np.zeros(0, dtype=nat.FTENSOR_DTYPE)
-    assert nat.ga_fusion_ring_plan(h0, np.zeros((0, P), dtype=np.uint64), P, nat.F32, 0) == 0
+    assert nat.ga_fusion_ring_plan(h0, np.zeros((0, P), dtype=np.uint64), P, nat.F32, [0]).size == 0
+    assert nat.ga_fusion_ring_plan(h0, np.zeros((0, P), dtype=np.uint64), P, nat.F32, []).size == 0
+    with pytest.raises(nat.GAError):
+        nat.ga_fusion_ring_plan(h0, np.zeros((0, P), dtype=np.uint64), P, nat.F32, [3])
 
 
 def test_fusion_ring_allreduce_errors_before_enqueue():
     L = nat.load()
     st = nat.RingStats()
     f = L.ga_fusion_ring_allreduce
-    assert f(0x1000, 0x2000, 2, 8, 2, 30, 0, 1, 1, 0, C.byref(st), None) == ENOTSUP   # stepwise
-    assert f(0x1000, 0x2000, 2, 8, 2, 30, 0, 1, 5, 0, None, None) == EINVAL            # mode
-    assert f(0x1000, 0x2000, 2, 8, 0, 30, 0, 1, 0, 0, None, None) == EINVAL            # P = 0
-    assert f(0x1000, 0x2000, 2, 8, 2, 30, 3, 1, 0, 0, None, None) == EINVAL            # dtype
-    assert f(0x1000, 0x2000, 2, 8, 2, 30, 0, 4, 0, 0, None, None) == EINVAL            # op
-    assert f(None, 0x2000, 2, 8, 2, 30, 0, 1, 0, 0, None, None) == EINVAL              # table
-    assert f(0x1000, 0x2000, 0, 8, 2, 0, 0, 1, 0, 0, None, None) == EINVAL             # work, no tensors
-    # nothing to do: still the accounting of the ring over fill elements
-    assert f(None, None, 0, 0, 4, 0, 0, 1, 0, 0, C.byref(st), None) == 0
-    assert f(0x1000, 0x2000, 2, 8, 1, 30, 0, 1, 2, 0, C.byref(st), None) == 0          # P = 1
+    F = (C.c_int64 * 2)(30, 12)
+    Z = (C.c_int64 * 1)(0)
+    assert f(0x1000, 8, 2, 0, 1, F, 1, 0, 1, C.byref(st), None) == ENOTSUP   # stepwise
+    assert f(0x1000, 8, 2, 0, 1, F, 1, 0, 5, None, None) == EINVAL            # mode
+    assert f(0x1000, 8, 0, 0, 1, F, 1, 0, 0, None, None) == EINVAL            # P = 0
+    assert f(0x1000, 8, 2, 3, 1, F, 1, 0, 0, None, None) == EINVAL            # dtype
+    assert f(0x1000, 8, 2, 0, 4, F, 1, 0, 0, None, None) == EINVAL            # op
+    assert f(None, 8, 2, 0, 1, F, 1, 0, 0, None, None) == EINVAL              # blocks
+    assert f(0x1004, 8, 2, 0, 1, F, 1, 0, 0, None, None) == EINVAL            # misaligned blocks
+    assert f(0x1000, 8, 2, 0, 1, None, 1, 0, 0, None, None) == EINVAL         # fills
+    assert f(0x1000, 8, 2, 0, 1, Z, 1, 0, 0, None, None) == EINVAL            # work, no tensors
+    # nothing to do: still the accounting of the rings over the buffers
+    assert f(None, 0, 4, 0, 1, F, 2, 0, 0, C.byref(st), None) == 0
+    assert st.steps == 6 and st.launches == 0
+    assert st.bytes_sent_per_worker == 2 * 3 * (8 + 3) * 4 and st.hbm_bytes == 2 * 4 * 42 * 4
+    assert f(0x1000, 8, 1, 0, 1, F, 2, 0, 2, C.byref(st), None) == 0          # P = 1
     assert st.steps == 0 and st.launches == 0
 
 

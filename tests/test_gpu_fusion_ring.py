@@ -199,3 +199,36 @@ def test_zero_copy_leaves_neighbours_alone():
         for st, n in zip(starts, sizes):
             mask[st:st + n] = False
         assert torch.all(slabs[i][mask] == 9.5)
+
+
+@pytest.mark.parametrize("dt", [ga.F32, ga.BF16])
+@pytest.mark.parametrize("mode", [ga.RING_FUSED, ga.RING_DUAL])
+@pytest.mark.parametrize("part", [0, 1000])
+def test_one_launch_equals_per_buffer_and_oracle(part, mode, dt):
+    """Every buffer of a plan in one launch (one table over all buffers)
+    leaves the same bits as one launch per buffer (one-buffer tables, taken
+    in reverse order: buffers are independent) and as the oracle's pack ->
+    fold per buffer -> unpack; the accounting sums over the buffers."""
+    P, cap = 6, 1 << 20
+    es = 4 if dt == ga.F32 else 2
+    sizes = _sizes(90, seed=21, extra=(0, 1, (2 * cap) // es))     # the last one oversize
+    a = _tensors(P, sizes, dt, seed=5)
+    b = [[x.clone() for x in row] for row in a]
+    host = [[_host(x) for x in row] for row in a]
+    want = _oracle_fused(host, sizes, dt, cap, ga.AVG, part, mode == ga.RING_DUAL)
+    buf_of, off_of, fill, _ = ga.ga_fuse_plan(sizes, [dt] * len(sizes), cap)
+    assert len(fill) >= 4
+    st = ga.FusionRing(a, buf_of, off_of, fill).allreduce(op=ga.AVG, mode=mode, part_elems=part)
+    assert st["launches"] == 1 and st["hbm_bytes"] == 2 * P * sum(fill) * es
+    fr = ga.FusionRing(b, buf_of, off_of, fill)
+    sent = 0
+    for k in reversed(range(len(fill))):
+        s = fr.allreduce_buffer(k, op=ga.AVG, mode=mode, part_elems=part)
+        assert s["launches"] == 1
+        sent += s["bytes_sent_per_worker"]
+    assert sent == st["bytes_sent_per_worker"]
+    torch.cuda.synchronize()
+    for i in range(P):
+        for t in range(len(sizes)):
+            assert np.array_equal(_host(a[i][t]).view(np.uint8), want[i][t].view(np.uint8)), (i, t)
+            assert torch.equal(a[i][t], b[i][t]), (i, t)
