@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libga.so")
 EXPORTS = (
     "ga_fuse_plan", "ga_fuse_desc_check", "ga_fuse_pack", "ga_fuse_unpack",
     "ga_ring_allreduce_sim", "thc_minmax", "thc_usq_quantize", "thc_int_aggregate",
-    "thc_dequant", "thc_nmse", "thc_nmse_ws_bytes", "ga_last_error",
+    "thc_dequant", "thc_nmse", "thc_nmse_ws_bytes", "thc_nmse_noalloc", "ga_last_error",
     "thc_nuhc_quantize", "thc_nuhc_aggregate", "thc_nuhc_dequant",
     "thc_rht_sumsq", "thc_rht_range", "thc_rht_forward", "thc_rht_inverse",
     "ga_fusion_ring_plan", "ga_fusion_ring_allreduce", "thc_ef_minmax", "thc_ef_quantize",
@@ -79,6 +79,7 @@ def load() -> C.CDLL:
     L.thc_int_aggregate.argtypes = [C.POINTER(vp), i32, i64, i32, vp, vp]
     L.thc_dequant.argtypes = [vp, i64, i32, i32, i64, vp, vp, i32, vp]
     L.thc_nmse.argtypes = [vp, vp, i64, i32, vp, vp, C.c_size_t, vp]
+    L.thc_nmse_noalloc.argtypes = [vp, vp, i64, i32, vp, vp]
     L.thc_nmse_ws_bytes.argtypes = [i64]
     L.thc_nmse_ws_bytes.restype = C.c_size_t
     L.thc_nuhc_quantize.argtypes = [C.POINTER(vp), i32, i32, i64, i32, i64, vp, i32, i32,
@@ -426,6 +427,18 @@ def thc_nmse(x: torch.Tensor, xhat: torch.Tensor, out: Optional[torch.Tensor] = 
         ws = torch.empty(thc_nmse_ws_bytes(N), dtype=torch.uint8, device=x.device)
     _check(load().thc_nmse(_dev(x, "x"), _dev(xhat, "xhat"), N, _dt(x), _dev(out, "out"),
                            _dev(ws, "ws"), ws.numel(), _stream(stream)))
+    return out
+
+
+def thc_nmse_noalloc(x: torch.Tensor, xhat: torch.Tensor, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """thc_nmse without a workspace: the library's static per-GPU scratch
+    holds the partials; `out` (3 float64 on the device) is the caller's."""
+    if x.numel() != xhat.numel() or _dt(x) != _dt(xhat):
+        raise ValueError("x and xhat need the same size and dtype")
+    if out.dtype != torch.float64 or out.numel() < 3:
+        raise ValueError("out must hold 3 float64")
+    _check(load().thc_nmse_noalloc(_dev(x, "x"), _dev(xhat, "xhat"), x.numel(), _dt(x),
+                                   _dev(out, "out"), _stream(stream)))
     return out
 
 

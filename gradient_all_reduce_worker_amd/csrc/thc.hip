@@ -12,6 +12,8 @@
 #include <algorithm>
 #include <cmath>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "philox.hpp"
 #include "quant.hpp"
@@ -1493,23 +1495,26 @@ extern "C" size_t thc_nmse_ws_bytes(int64_t N) {
     return (size_t)(nblk + ng) * 2 * sizeof(double);
 }
 
-extern "C" ga_status thc_nmse(const void* x, const void* xhat, int64_t N, ga_dtype dt, double* d_out,
-                              void* d_ws, size_t ws_bytes, void* stream) {
-    const char* what = "thc_nmse";
+namespace {
+
+ga_status nmse_check(const void* x, const void* xhat, int64_t N, ga_dtype dt, double* d_out,
+                     const char* what) {
     if (!valid_dtype(dt)) return fail(GA_EINVAL, "%s: unknown dtype %d", what, (int)dt);
     if (N < 0) return fail(GA_EINVAL, "%s: negative size", what);
-    if (!d_out || !aligned(d_out, 8) || !d_ws || !aligned(d_ws, 8))
-        return fail(GA_EINVAL, "%s: null or misaligned output/workspace", what);
-    if (ws_bytes < thc_nmse_ws_bytes(N))
-        return fail(GA_EINVAL, "%s: workspace of %zu bytes, need %zu", what, ws_bytes, thc_nmse_ws_bytes(N));
+    if (!d_out || !aligned(d_out, 8)) return fail(GA_EINVAL, "%s: null or misaligned output", what);
     if (N > 0 && (!x || !xhat || !aligned(x, elem_size(dt)) || !aligned(xhat, elem_size(dt))))
         return fail(GA_EINVAL, "%s: null or misaligned input", what);
+    if (nmse_blocks(N, dt == GA_F32 ? 4 : 8) > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: N too large", what);
+    return GA_OK;
+}
+
+// The NMSE launches over the partials array ws (thc_nmse_ws_bytes(N)
+// bytes): one partial per piece, summed in one or two levels.
+ga_status nmse_launch(const void* x, const void* xhat, int64_t N, ga_dtype dt, double* d_out,
+                      double* ws, hipStream_t hs, const char* what) {
     const int E = dt == GA_F32 ? 4 : 8;
     const int vec_ok = N > 0 && aligned(x, 16) && aligned(xhat, 16);
     const int64_t nblk = nmse_blocks(N, E);
-    if (nblk > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: N too large", what);
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    double* ws = static_cast<double*>(d_ws);
     ga_status rc;
     if (dt == GA_F32)
         hipLaunchKernelGGL(nmse_partial_kernel<GA_F32>, dim3((unsigned)nblk), dim3(kThreads), 0, hs, x, xhat, N, ws, vec_ok);
@@ -1526,4 +1531,73 @@ extern "C" ga_status thc_nmse(const void* x, const void* xhat, int64_t N, ga_dty
         hipLaunchKernelGGL(nmse_final_kernel, dim3(1), dim3(kThreads), 0, hs, ws, (int)nblk, d_out);
     }
     return check_launch(what);
+}
+
+// Partials of thc_nmse_noalloc: a file-scope device array, one copy per GPU
+// for the life of the process. Its name in host code is not a device
+// address: each GPU's copy is found with hipGetSymbolAddress, once per
+// device, and only that address is handed to kernels. Every slot a call
+// reads is written earlier in the same call, so nothing needs clearing.
+constexpr size_t kNmseScratchBytes = 160 << 10;
+static __device__ __align__(256) double scratch[kNmseScratchBytes / sizeof(double)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the GPU that owns stream hs.
+ga_status scratch_of(hipStream_t hs, double** out, const char* what) {
+    int dev = 0;
+    if (hs) {
+        hipDevice_t d;
+        if (hipStreamGetDevice(hs, &d) != hipSuccess) return fail(GA_EHIP, "%s: unknown stream", what);
+        dev = (int)d;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return fail(GA_EHIP, "%s: no current device", what);
+    }
+    if (dev < 0 || dev >= kMaxDevices) return fail(GA_EINVAL, "%s: device %d out of range", what, dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess) return fail(GA_EHIP, "%s: no current device", what);
+        if (cur != dev && hipSetDevice(dev) != hipSuccess)
+            return fail(GA_EHIP, "%s: cannot select device %d", what, dev);
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !p)
+            return fail(GA_EHIP, "%s: hipGetSymbolAddress of the scratch array: %s", what,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = static_cast<double*>(g_scratch_ptr[dev]);
+    return GA_OK;
+}
+
+}  // namespace
+
+extern "C" ga_status thc_nmse(const void* x, const void* xhat, int64_t N, ga_dtype dt, double* d_out,
+                              void* d_ws, size_t ws_bytes, void* stream) {
+    const char* what = "thc_nmse";
+    ga_status rc = nmse_check(x, xhat, N, dt, d_out, what);
+    if (rc) return rc;
+    if (!d_ws || !aligned(d_ws, 8)) return fail(GA_EINVAL, "%s: null or misaligned workspace", what);
+    if (ws_bytes < thc_nmse_ws_bytes(N))
+        return fail(GA_EINVAL, "%s: workspace of %zu bytes, need %zu", what, ws_bytes, thc_nmse_ws_bytes(N));
+    return nmse_launch(x, xhat, N, dt, d_out, static_cast<double*>(d_ws), static_cast<hipStream_t>(stream),
+                       what);
+}
+
+extern "C" ga_status thc_nmse_noalloc(const void* x, const void* xhat, int64_t N, ga_dtype dt,
+                                      double* d_out, void* stream) {
+    const char* what = "thc_nmse_noalloc";
+    ga_status rc = nmse_check(x, xhat, N, dt, d_out, what);
+    if (rc) return rc;
+    if (thc_nmse_ws_bytes(N) > kNmseScratchBytes)
+        return fail(GA_EINVAL, "%s: N = %lld needs %zu bytes of partials, more than the %zu bytes of "
+                    "the static scratch", what, (long long)N, thc_nmse_ws_bytes(N), kNmseScratchBytes);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    double* ws = nullptr;
+    if ((rc = scratch_of(hs, &ws, what))) return rc;
+    return nmse_launch(x, xhat, N, dt, d_out, ws, hs, what);
 }

@@ -8,6 +8,8 @@
  *                                                  single or bidirectional)
  *   ga_fusion_ring_plan / ga_fusion_ring_allreduce zero-copy fusion ring
  *   thc_minmax / thc_usq_quantize / thc_int_aggregate / thc_dequant / thc_nmse
+ *   thc_nmse_noalloc (thc_nmse without a workspace, for callers that
+ *   cannot allocate)
  *   thc_aggregate_dequant (aggregate + dequant + NMSE in one pass)
  *                                                  THC uniform quantization
  *   thc_nuhc_quantize / thc_nuhc_aggregate / thc_nuhc_dequant
@@ -334,6 +336,21 @@ ga_status thc_dequant(const int32_t* d_sum, int64_t N, int32_t P, int32_t b, int
 ga_status thc_nmse(const void* x, const void* xhat, int64_t N, ga_dtype dt, double* d_out,
                    void* d_ws, size_t ws_bytes, void* stream);
 size_t thc_nmse_ws_bytes(int64_t N);
+
+/*
+ * thc_nmse_noalloc -- thc_nmse for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): same kernels, same result, bit for bit, but the
+ * partials live in a 160 KiB array inside the library, one copy per GPU
+ * (held until the process ends), instead of a caller workspace. The call
+ * allocates nothing. Every N that thc_nmse_ws_bytes(N) maps to at most
+ * 160 KiB is accepted (the piece count is capped near 8,192, so that is
+ * every N in practice); a larger need returns GA_EINVAL. The first call on
+ * a GPU looks up that GPU's copy (the stream's device). Calls that overlap
+ * on one GPU share the array and race: order them on one stream.
+ */
+ga_status thc_nmse_noalloc(const void* x, const void* xhat, int64_t N, ga_dtype dt, double* d_out,
+                           void* stream);
 
 /* ------------------------------------------------------------------ */
 /* Non-uniform THC: lookup tables  ([THC] section 4, Algorithm 2)       */

@@ -27,7 +27,7 @@ def _declared():
 def test_header_declarations_are_exported():
     L = nat.load()
     names = _declared()
-    assert len(names) == 28
+    assert len(names) == 29
     assert set(names) == set(nat.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -465,3 +465,15 @@ def test_truncation_threshold_t_p():
     for p in (0.05, 0.01, 1.0 / 32, 1e-3, 0.5):
         assert abs(math.erfc(t_p(p) / math.sqrt(2.0)) - p) <= 1e-12 * p, p
     assert abs(t_p(1.0 / 32) - 2.153874694061456) < 1e-9      # the vgg16 RHT pass
+
+
+def test_nmse_noalloc_argument_errors_before_enqueue():
+    L = nat.load()
+    out = 0x3000
+    assert L.thc_nmse_noalloc(0x1000, 0x2000, 100, 0, None, None) == EINVAL     # no output
+    assert L.thc_nmse_noalloc(0x1000, 0x2000, 100, 0, 0x3004, None) == EINVAL   # misaligned output
+    assert L.thc_nmse_noalloc(0x1000, 0x2000, 100, 3, out, None) == EINVAL      # dtype
+    assert L.thc_nmse_noalloc(0x1000, 0x2000, -1, 0, out, None) == EINVAL       # negative size
+    assert L.thc_nmse_noalloc(None, 0x2000, 100, 0, out, None) == EINVAL        # no input
+    assert L.thc_nmse_noalloc(0x1002, 0x2000, 100, 0, out, None) == EINVAL      # misaligned input
+    assert b"thc_nmse_noalloc" in L.ga_last_error()
