@@ -145,14 +145,40 @@ int orc_ring_fold(void *const *bufs, int P, int64_t N, int dt, int op, int64_t p
 }
 
 /*
- * orc_ring_stepwise: the literal 2(P-1)-step schedule of [RING] section 7,
- * run on binary32 working copies of every worker's partition, with explicit
- * per-step send copies standing in for the simultaneous transfers.
- *   scatter-reduce step s: worker i sends chunk (i-s) mod P; worker i adds the
- *     chunk received from worker i-1 into its chunk (i-s-1) mod P.
- *   all-gather step s: worker i sends chunk (i-s+1) mod P; worker i
- *     overwrites its chunk (i-s) mod P with what it received.
- * With op = avg every worker divides its buffer by P at the end ([HVD] 3.4).
+ * One communication step of one ring direction on binary32 working copies,
+ * stated from the chunk-owner rule of [RING] sections 4 and 7: at step
+ * `shift` worker i holds the running partial (scatter-reduce) or the
+ * finished value (all-gather) of ring chunk (i - dir * shift) mod P, and
+ * hands it to worker i + dir. Chunk k of the direction is index base + k of
+ * the partition's chunks of length C (the last ones short or empty). All P
+ * transfers of a step happen at once, so every worker first copies out what
+ * it sends; then each receiver adds it in (reduce) or overwrites its copy.
+ */
+static void ring_step(float **work, float **send, int P, int dir, int base, int64_t C, int64_t n,
+                      int shift, int reduce)
+{
+    for (int i = 0; i < P; i++) {
+        int64_t k = base + mod_p(i - (int64_t)dir * shift, P);
+        int64_t lo = k * C < n ? k * C : n, hi = (k + 1) * C < n ? (k + 1) * C : n;
+        memcpy(send[i], work[i] + lo, (size_t)(hi - lo) * sizeof(float));
+    }
+    for (int i = 0; i < P; i++) {
+        int j = mod_p(i + dir, P);                       /* the receiver */
+        int64_t k = base + mod_p(i - (int64_t)dir * shift, P);
+        int64_t lo = k * C < n ? k * C : n, hi = (k + 1) * C < n ? (k + 1) * C : n;
+        for (int64_t t = lo; t < hi; t++)
+            work[j][t] = reduce ? work[j][t] + send[i][t - lo] : send[i][t - lo];
+    }
+}
+
+/*
+ * orc_ring_stepwise: the ring's 2(P-1) communication steps of [RING]
+ * section 7 executed one by one on binary32 working copies of every
+ * worker's partition: P - 1 scatter-reduce steps (ring_step with shift s,
+ * the partial of chunk c growing by one worker per step from worker c on),
+ * then P - 1 all-gather steps (shift s - 1: the worker that finished chunk
+ * c passes it on, and each receiver overwrites its copy). With op = avg
+ * every worker divides its buffer by P at the end ([HVD] 3.4).
  * rs_only != 0 stops after scatter-reduce and stores the binary32 partial
  * state back (fp32 buffers only), so the state after the first phase can be
  * inspected.
@@ -173,7 +199,7 @@ int orc_ring_stepwise(void *const *bufs, int P, int64_t N, int dt, int op, int64
         int64_t C = (n + P - 1) / P;
         for (int i = 0; i < P; i++) {
             work[i] = (float *)malloc((size_t)n * sizeof(float));
-            send[i] = (float *)malloc((size_t)C * sizeof(float));
+            send[i] = (float *)malloc((size_t)(C > 0 ? C : 1) * sizeof(float));
             if (!work[i] || !send[i])
                 rc = -2;
         }
@@ -181,39 +207,16 @@ int orc_ring_stepwise(void *const *bufs, int P, int64_t N, int dt, int op, int64
             for (int i = 0; i < P; i++)
                 for (int64_t t = 0; t < n; t++)
                     work[i][t] = load_elem(bufs[i], dt, p0 + t);
-            /* chunk c covers [c*C, c*C + len(c)) inside the partition */
-#define CHUNK_LEN(c) ((n - (int64_t)(c) * C) < 0 ? 0 : ((n - (int64_t)(c) * C) < C ? (n - (int64_t)(c) * C) : C))
-            for (int s = 0; s < P - 1; s++) {
-                for (int i = 0; i < P; i++) {
-                    int sc = mod_p(i - s, P);
-                    memcpy(send[i], work[i] + sc * C, (size_t)CHUNK_LEN(sc) * sizeof(float));
-                }
-                for (int i = 0; i < P; i++) {
-                    int rcv = mod_p(i - s - 1, P);
-                    const float *got = send[mod_p(i - 1, P)];
-                    float *dst = work[i] + rcv * C;
-                    for (int64_t t = 0; t < CHUNK_LEN(rcv); t++)
-                        dst[t] += got[t];
-                }
-            }
+            for (int s = 0; s < P - 1; s++)
+                ring_step(work, send, P, +1, 0, C, n, s, 1);
             if (!rs_only) {
-                for (int s = 0; s < P - 1; s++) {
-                    for (int i = 0; i < P; i++) {
-                        int sc = mod_p(i - s + 1, P);
-                        memcpy(send[i], work[i] + sc * C, (size_t)CHUNK_LEN(sc) * sizeof(float));
-                    }
-                    for (int i = 0; i < P; i++) {
-                        int rcv = mod_p(i - s, P);
-                        memcpy(work[i] + rcv * C, send[mod_p(i - 1, P)],
-                               (size_t)CHUNK_LEN(rcv) * sizeof(float));
-                    }
-                }
+                for (int s = 0; s < P - 1; s++)
+                    ring_step(work, send, P, +1, 0, C, n, s - 1, 0);
                 if (op == ORC_AVG)
                     for (int i = 0; i < P; i++)
                         for (int64_t t = 0; t < n; t++)
                             work[i][t] = work[i][t] / (float)P;
             }
-#undef CHUNK_LEN
             for (int i = 0; i < P; i++)
                 for (int64_t t = 0; t < n; t++)
                     store_elem(bufs[i], dt, p0 + t, work[i][t]);
@@ -268,31 +271,11 @@ int orc_dual_ring_fold(void *const *bufs, int P, int64_t N, int dt, int op, int6
     return 0;
 }
 
-/* One communication step of one ring direction on the working copies:
- * every worker i first copies out ring sub-chunk (i - dir * shift) mod P
- * (index base + that, length len(...)), then worker i + dir adds (reduce)
- * or writes (gather) what it received into the same sub-chunk. */
-static void dual_step(float **work, float **send, int P, int dir, int base, int64_t C2, int64_t n,
-                      int shift, int reduce)
-{
-    for (int i = 0; i < P; i++) {
-        int64_t k = base + mod_p(i - (int64_t)dir * shift, P);
-        int64_t lo = k * C2 < n ? k * C2 : n, hi = (k + 1) * C2 < n ? (k + 1) * C2 : n;
-        memcpy(send[i], work[i] + lo, (size_t)(hi - lo) * sizeof(float));
-    }
-    for (int i = 0; i < P; i++) {
-        int j = mod_p(i + dir, P);                       /* the receiver */
-        int64_t k = base + mod_p(i - (int64_t)dir * shift, P);
-        int64_t lo = k * C2 < n ? k * C2 : n, hi = (k + 1) * C2 < n ? (k + 1) * C2 : n;
-        for (int64_t t = lo; t < hi; t++)
-            work[j][t] = reduce ? work[j][t] + send[i][t - lo] : send[i][t - lo];
-    }
-}
-
 /*
- * orc_dual_ring_stepwise: the literal schedule of the bidirectional ring,
+ * orc_dual_ring_stepwise: the steps of the bidirectional ring one by one,
  * P - 1 scatter-reduce steps then P - 1 all-gather steps, both directions
- * in every step, on binary32 working copies with explicit send copies.
+ * in every step (ring_step over sub-chunks of C2; the counter-clockwise
+ * ring's chunks are sub-chunks P .. 2P - 1).
  * Scatter-reduce step s moves sub-chunk (i - dir s) of worker i; all-gather
  * step s moves (i - dir (s - 1)), the finished one. avg divides at the end.
  */
@@ -320,12 +303,12 @@ int orc_dual_ring_stepwise(void *const *bufs, int P, int64_t N, int dt, int op, 
                 for (int64_t t = 0; t < n; t++)
                     work[i][t] = load_elem(bufs[i], dt, p0 + t);
             for (int s = 0; s < P - 1; s++) {
-                dual_step(work, send, P, +1, 0, C2, n, s, 1);
-                dual_step(work, send, P, -1, P, C2, n, s, 1);
+                ring_step(work, send, P, +1, 0, C2, n, s, 1);
+                ring_step(work, send, P, -1, P, C2, n, s, 1);
             }
             for (int s = 0; s < P - 1; s++) {
-                dual_step(work, send, P, +1, 0, C2, n, s - 1, 0);
-                dual_step(work, send, P, -1, P, C2, n, s - 1, 0);
+                ring_step(work, send, P, +1, 0, C2, n, s - 1, 0);
+                ring_step(work, send, P, -1, P, C2, n, s - 1, 0);
             }
             if (op == ORC_AVG)
                 for (int i = 0; i < P; i++)
