@@ -439,10 +439,12 @@ bool disjoint(void* const* bufs, int P, int64_t bytes) {
 // Launch shape of the fused fold, measured on MI355X. Folding P streams and
 // writing P back keeps 2P DRAM streams open per workgroup; on large buffers
 // fewer resident workgroups per CU keep fewer rows open and stream faster
-// (8 x 4 GiB bf16: 0.72 -> 0.79 of 8 TB/s at two workgroups per CU; 16
-// workers of 66 MB: 0.68 -> 0.74 at one; 32 workers of 553 MB with four
-// vectors per thread: 0.73 -> 0.77 at four). Residency is capped with
-// unused dynamic LDS (160 KiB per CU). Small buffers keep full occupancy.
+// (8 x 4 GiB bf16: 0.72 -> 0.79 of 8 TB/s at two workgroups per CU, and
+// from 256 MiB moved on: the 200-tensor fusion plan, 8 workers, 553 MB,
+// 0.64 -> 0.66 flat and 0.69 -> 0.72 zero-copy; 16 workers of 66 MB:
+// 0.68 -> 0.74 at one; 32 workers of 553 MB with four vectors per thread:
+// 0.73 -> 0.77 at four). Residency is capped with unused dynamic LDS
+// (160 KiB per CU). Small buffers keep full occupancy.
 struct FoldShape {
     int vpt;        // 16-byte vectors per thread
     int batch;      // worker loads in flight per vector
@@ -455,7 +457,7 @@ size_t cap_workgroups_per_cu(int k) { return kLdsPerCu / (size_t)k - 1024; }
 
 FoldShape fold_shape(int P, int64_t total_bytes) {
     const bool big = total_bytes >= (int64_t)1 << 30;
-    if (P <= 8) return {1, 16, big ? cap_workgroups_per_cu(2) : 0};
+    if (P <= 8) return {1, 16, total_bytes >= ((int64_t)1 << 28) ? cap_workgroups_per_cu(2) : 0};
     if (P <= 16) return {1, 16, big ? cap_workgroups_per_cu(1) : 0};
     return {4, 4, big ? cap_workgroups_per_cu(4) : 0};
 }
