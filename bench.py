@@ -30,7 +30,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "aggregated gradient GB/s (P·N·bytes/s) vs HBM peak; THC quantize Gelem/s + NMSE"
 HBM_PEAK_GBS = 8000.0
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "ring_fused_shard_pmc.json")
+# rocprofv3 PMC summaries of the dominant kernel, per workload: profiles/
+# ring_fused_<workload>_pmc.json (flat ring) or fusion_ring_<workload>_pmc.json
+# (zero-copy fusion ring), each stamped with the ring source's hash
+PMC_FILE = {"ring_fused_vec_kernel": "ring_fused_{}_pmc.json",
+            "fusion_ring_kernel": "fusion_ring_{}_pmc.json"}
 RING_SRC = os.path.join(ROOT, "gradient_all_reduce_worker_amd", "csrc", "ring.hip")
 
 DESCRIPTIONS = {
@@ -55,13 +59,14 @@ def ring_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profile(workload: str):
-    """HBM bytes per ring launch from the committed PMC summary, if it was
-    measured on this workload and on the current ring source."""
+def traffic_from_profile(workload: str, kernel: str):
+    """HBM bytes per launch of the ring kernel from the committed PMC
+    summary, if one was measured on this workload and on the current ring
+    source; else None."""
     try:
-        with open(PMC_SUMMARY) as f:
+        with open(os.path.join(ROOT, "profiles", PMC_FILE[kernel].format(workload))) as f:
             d = json.load(f)
-    except (OSError, ValueError):
+    except (OSError, ValueError, KeyError):
         return None
     if d.get("workload") != workload or d.get("ring_src_sha256_16") != ring_source_hash():
         return None
@@ -328,18 +333,24 @@ def main():
              if k.startswith(("thc_usq_quantize", "thc_nuhc_quantize"))}
 
     ring_key = "ring_allreduce" if "ring_allreduce" in stage_ms else "fusion_ring"
+    kernel = "ring_fused_vec_kernel" if ring_key == "ring_allreduce" else "fusion_ring_kernel"
     ring_ms = stage_ms[ring_key]
     achieved = nbytes[ring_key] / (ring_ms * 1e-3) / 1e9
+    # the copy path runs one ring launch per fusion buffer: its summary would
+    # be per buffer, so only single-launch rings carry traffic
+    one_launch = calls[ring_key] // args.steps == 1
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic_from_profile(args.workload) if ring_key == "ring_allreduce" else None,
-                "kernel": "ring_fused_vec_kernel" if ring_key == "ring_allreduce" else "fusion_ring_kernel",
-                "alg_bytes_per_launch": nbytes[ring_key]}
+                "traffic": traffic_from_profile(args.workload, kernel) if one_launch else None,
+                "kernel": kernel, "alg_bytes_per_launch": nbytes[ring_key]}
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        # the arithmetic of the path: binary32 folds, grid positions and
+        # dequantization on every workload (bf16 gradients are widened
+        # exactly; config.elem names the storage type)
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{args.workload}: {DESCRIPTIONS[args.workload]}", "P": P, "N": N,
                    "elem": "bf16" if pipe.w.dtype == ga.BF16 else "fp32",
