@@ -5,13 +5,16 @@
 One step is one pass of every stage over one batch of synthetic gradients
 already resident in HBM (see gradient_all_reduce_worker_amd.pipeline):
 for the default workload, 8 simulated workers x 2^31 bf16 gradients each
-(Laplace(0, 1e-3)): THC min/max, USQ quantize (b = 2), ring all-reduce
-average with fp32 accumulation over 2^20-element partitions, integer
-aggregate, dequantize, NMSE. `value` is aggregated gradient bytes
-(P N elem_bytes) per second of step time.
+(Laplace(0, 1e-3)): THC min/max, then one pass that quantizes (USQ b = 2),
+ring-averages with fp32 accumulation over 2^20-element partitions, sums the
+indices as integers, dequantizes and measures the NMSE (thc_ring_step;
+--separate-step runs the quantizer, the ring and the tail as their own
+calls). `value` is aggregated gradient bytes (P N elem_bytes) per second of
+step time.
 
-Prints ONE JSON line. `roofline` describes the dominant kernel (the fused
-ring) from HIP events around its launches inside the timed steps;
+Prints ONE JSON line. `roofline` describes the dominant kernel (the
+one-read step pass, or the ring where there is none) from HIP events around
+its launches inside the timed steps;
 `cpu_baseline` times the oracle (plain C) on this host's cores, beside its
 one-thread figure: sampled whole partitions of a flat workload, or the
 whole pack-ring-unpack step of a fused one; `traffic` comes from the
@@ -34,8 +37,11 @@ HBM_PEAK_GBS = 8000.0
 # ring_fused_<workload>_pmc.json (flat ring) or fusion_ring_<workload>_pmc.json
 # (zero-copy fusion ring), each stamped with the ring source's hash
 PMC_FILE = {"ring_fused_vec_kernel": "ring_fused_{}_pmc.json",
-            "fusion_ring_kernel": "fusion_ring_{}_pmc.json"}
-RING_SRC = os.path.join(ROOT, "gradient_all_reduce_worker_amd", "csrc", "ring.hip")
+            "fusion_ring_kernel": "fusion_ring_{}_pmc.json",
+            "thc_ring_kernel": "thc_ring_{}_pmc.json"}
+CSRC = os.path.join(ROOT, "gradient_all_reduce_worker_amd", "csrc")
+KERNEL_SRC = {"ring_fused_vec_kernel": "ring.hip", "fusion_ring_kernel": "ring.hip",
+              "thc_ring_kernel": "step.hip"}
 
 DESCRIPTIONS = {
     "small": "4 workers x 1,048,576 fp32 N(0,0.01^2); ring avg + THC USQ b=4",
@@ -54,21 +60,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def ring_source_hash() -> str:
-    with open(RING_SRC, "rb") as f:
+def source_hash(kernel: str) -> str:
+    with open(os.path.join(CSRC, KERNEL_SRC[kernel]), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def traffic_from_profile(workload: str, kernel: str):
-    """HBM bytes per launch of the ring kernel from the committed PMC
-    summary, if one was measured on this workload and on the current ring
-    source; else None."""
+    """HBM bytes per launch of the dominant kernel from the committed PMC
+    summary, if one was measured on this workload and on the kernel's
+    current source; else None."""
     try:
         with open(os.path.join(ROOT, "profiles", PMC_FILE[kernel].format(workload))) as f:
             d = json.load(f)
     except (OSError, ValueError, KeyError):
         return None
-    if d.get("workload") != workload or d.get("ring_src_sha256_16") != ring_source_hash():
+    if d.get("workload") != workload or d.get("ring_src_sha256_16") != source_hash(kernel):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -252,6 +258,9 @@ def main():
                     help="single ring or the bidirectional dual ring fold order")
     ap.add_argument("--separate-tail", action="store_true",
                     help="THC passes: integer sum, dequant and NMSE as three calls, not one")
+    ap.add_argument("--separate-step", action="store_true",
+                    help="flat workloads: quantizer, ring and tail as separate calls instead of the "
+                         "one-read thc_ring_step")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one 1 GiB torch copy first (PMC calibration)")
     args = ap.parse_args()
@@ -272,7 +281,8 @@ def main():
         sys.exit(1)
 
     pipe = Pipeline(args.workload, zero_copy=not args.copy_fusion, fused_tail=not args.separate_tail,
-                    ring_mode=ga.RING_DUAL if args.ring_mode == "dual" else ga.RING_FUSED)
+                    ring_mode=ga.RING_DUAL if args.ring_mode == "dual" else ga.RING_FUSED,
+                    fused_step=not args.separate_step)
     t0 = time.perf_counter()
     pipe.setup()
     log(f"setup {args.workload}: {time.perf_counter() - t0:.1f} s")
@@ -332,8 +342,13 @@ def main():
     quant = {k: round(P * N / (v * 1e-3) / 1e9, 2) for k, v in stage_ms.items()
              if k.startswith(("thc_usq_quantize", "thc_nuhc_quantize"))}
 
-    ring_key = "ring_allreduce" if "ring_allreduce" in stage_ms else "fusion_ring"
-    kernel = "ring_fused_vec_kernel" if ring_key == "ring_allreduce" else "fusion_ring_kernel"
+    step_keys = [k for k in stage_ms if k.startswith("thc_ring_step")]
+    if step_keys:
+        ring_key, kernel = step_keys[0], "thc_ring_kernel"
+    elif "ring_allreduce" in stage_ms:
+        ring_key, kernel = "ring_allreduce", "ring_fused_vec_kernel"
+    else:
+        ring_key, kernel = "fusion_ring", "fusion_ring_kernel"
     ring_ms = stage_ms[ring_key]
     achieved = nbytes[ring_key] / (ring_ms * 1e-3) / 1e9
     # the copy path runs one ring launch per fusion buffer: its summary would
@@ -357,6 +372,7 @@ def main():
                    "partition_elems": pipe.w.part_elems, "thc_bits": list(pipe.w.thc_bits),
                    "ring": args.ring_mode,
                    "thc_tail": "separate" if args.separate_tail else "fused",
+                   "thc_ring_step": "fused" if pipe.fused_step else "separate",
                    "fusion": (None if not pipe.w.fused else
                               "pack-ring-unpack" if args.copy_fusion else "zero-copy"),
                    "parallelism": "1 GPU, P simulated workers"},

@@ -29,7 +29,8 @@ EXPORTS = (
     "thc_rht_sumsq", "thc_rht_range", "thc_rht_forward", "thc_rht_inverse",
     "ga_fusion_ring_plan", "ga_fusion_ring_allreduce", "thc_ef_minmax", "thc_ef_quantize",
     "thc_rht_quantize", "thc_aggregate_dequant", "thc_aggregate_dequant_ws_bytes",
-    "thc_rht_norm_quantize", "thc_rht_norm_quantize_ws_bytes",
+    "thc_rht_norm_quantize", "thc_rht_norm_quantize_ws_bytes", "thc_ring_step",
+    "thc_ring_step_ws_bytes",
 )
 
 
@@ -105,6 +106,10 @@ def load() -> C.CDLL:
     L.thc_rht_norm_quantize.argtypes = [C.POINTER(vp), i32, i32, i64, i32, i64, u64, C.c_double, i32,
                                         i32, C.POINTER(i32), u64, vp, vp, C.POINTER(vp), vp, C.c_size_t,
                                         C.POINTER(vp), vp]
+    L.thc_ring_step.argtypes = [C.POINTER(vp), i32, i64, i32, i64, vp, i64, i32, u64, i32,
+                                C.POINTER(vp), vp, vp, vp, vp, C.c_size_t, vp]
+    L.thc_ring_step_ws_bytes.argtypes = [i64]
+    L.thc_ring_step_ws_bytes.restype = C.c_size_t
     L.thc_rht_norm_quantize_ws_bytes.argtypes = [i32, i64, i64]
     L.thc_rht_norm_quantize_ws_bytes.restype = C.c_size_t
     L.thc_aggregate_dequant_ws_bytes.restype = C.c_size_t
@@ -112,7 +117,7 @@ def load() -> C.CDLL:
     L.ga_last_error.restype = C.c_char_p
     for name in EXPORTS:
         if name not in ("thc_nmse_ws_bytes", "ga_last_error", "thc_aggregate_dequant_ws_bytes",
-                        "thc_rht_norm_quantize_ws_bytes"):
+                        "thc_rht_norm_quantize_ws_bytes", "thc_ring_step_ws_bytes"):
             getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -441,6 +446,49 @@ def thc_nmse_noalloc(x: torch.Tensor, xhat: torch.Tensor, out: torch.Tensor, str
                                    _dev(out, "out"), _stream(stream)))
     return out
 
+
+def thc_ring_step_ws_bytes(N: int) -> int:
+    return int(load().thc_ring_step_ws_bytes(N))
+
+
+def thc_ring_step(bufs: Sequence[torch.Tensor], mM: torch.Tensor, b: int, seed: int,
+                  ring_part: int = 0, q_part: int = 0, worker0: int = 0,
+                  packed: Optional[Sequence[torch.Tensor]] = None, keep_packed: bool = True,
+                  sum_out: Optional[torch.Tensor] = None, keep_sum: bool = True,
+                  xhat: Optional[torch.Tensor] = None, nmse_out: Optional[torch.Tensor] = None,
+                  ws: Optional[torch.Tensor] = None, with_nmse: bool = True, stream=None):
+    """Quantize, ring-average, integer sum, dequant and NMSE in one pass;
+    returns (packed or None, sum or None, xhat, nmse or None). The ring
+    average is left in every buffer."""
+    P = len(bufs)
+    N = bufs[0].numel()
+    dev = bufs[0].device
+    if keep_packed and packed is None:
+        packed = [torch.empty(max(packed_bytes(N, b), 8), dtype=torch.uint8, device=dev) for _ in range(P)]
+    if not keep_packed:
+        packed = None
+    if keep_sum and sum_out is None:
+        sum_out = torch.empty(max(N, 1), dtype=torch.int32, device=dev)
+    if not keep_sum:
+        sum_out = None
+    if xhat is None:
+        xhat = torch.empty(max(N, 1), dtype=bufs[0].dtype, device=dev)
+    if with_nmse:
+        if nmse_out is None:
+            nmse_out = torch.empty(3, dtype=torch.float64, device=dev)
+        if ws is None:
+            ws = torch.empty(thc_ring_step_ws_bytes(N), dtype=torch.uint8, device=dev)
+    else:
+        nmse_out = ws = None
+    pk = _ptr_array(packed, "packed") if packed is not None else None
+    _check(load().thc_ring_step(_ptr_array(bufs, "buffer"), P, N, _dt(bufs[0]), ring_part,
+                                _dev(mM, "mM"), q_part, b, seed, worker0, pk,
+                                _dev(sum_out, "sum") if sum_out is not None else None,
+                                _dev(xhat, "xhat"),
+                                _dev(nmse_out, "nmse") if nmse_out is not None else None,
+                                _dev(ws, "ws") if ws is not None else None,
+                                ws.numel() if ws is not None else 0, _stream(stream)))
+    return packed, sum_out, xhat, nmse_out
 
 # ------------------------------------------------------------------ non-uniform THC
 def _table_arg(T):

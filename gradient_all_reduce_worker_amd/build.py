@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libga.so")
-SOURCES = ["common.hip", "fusion.hip", "ring.hip", "thc.hip", "rht.hip"]
+SOURCES = ["common.hip", "fusion.hip", "ring.hip", "thc.hip", "rht.hip", "step.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

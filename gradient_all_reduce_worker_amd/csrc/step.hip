@@ -1,0 +1,380 @@
+// step.hip -- the ring average and one uniform THC pass in a single read of
+// the workers' gradients.
+//
+// A step of the simulated data-parallel job computes, over P workers'
+// buffers, THC's uniform quantization of every worker's gradient, the
+// server's integer sum of the indices with the dequantized average and its
+// NMSE ("THC: Accelerating Distributed Deep Learning Using Tensor
+// Homomorphic Compression", sections 2-3, Algorithm 1), and the exact
+// average by the ring all-reduce ("Horovod: Fast and Easy Distributed Deep
+// Learning in TensorFlow", section 3.4; systemcraft lesson "Collective
+// Communication: Ring All-Reduce", sections 4 and 7), which THC's estimate is
+// measured against. Run one after another those stages read every gradient
+// twice (quantizer, ring) and the indices and the average once more (sum,
+// dequant, NMSE). Here one pass reads each gradient once and produces all of
+// it: per group of 8 elements a thread loads each worker's 8 values,
+// quantizes them with the worker's Philox stream and the partition's grid,
+// adds the indices into the server's sum, and folds the values in the
+// ring's order; then it writes the average to every worker, the
+// dequantized average x̂, optionally the packed indices and the sums, and
+// adds the NMSE terms. Every output is bit for bit what thc_usq_quantize,
+// thc_aggregate_dequant and ga_ring_allreduce_sim (fused, op = avg) leave;
+// the NMSE is summed in another order (within rounding of it).
+//
+// A workgroup takes 256 consecutive groups. When they lie in one chunk of
+// one ring partition (every workgroup when chunks are multiples of 2048
+// elements), the workers are loaded in the chunk's fold order, so the fold
+// is the load order and each value is quantized as it arrives; otherwise the
+// indices are made in worker order and each element is folded in its own
+// chunk's order from memory.
+#include <algorithm>
+
+#include "common.hpp"
+#include "philox.hpp"
+#include "quant.hpp"
+#include "reduce.hpp"
+
+namespace ga {
+namespace {
+
+constexpr int kBatch = 16;        // worker loads in flight per thread (P given at run time)
+
+// x / P, or x * (1/P) when that is exact (P a power of two): the ring's
+// average and the dequantizer's S / P.
+struct Avg {
+    int pow2;
+    float pf;
+    float recip;
+    __device__ __forceinline__ float apply(float x) const { return pow2 ? x * recip : x / pf; }
+};
+
+// 8 consecutive elements (one group) of a worker as binary32.
+template <ga_dtype DT> struct Group8;
+
+template <> struct Group8<GA_BF16> {
+    static constexpr int kVecs = 1;       // 16-byte vectors per group
+    __device__ static __forceinline__ void widen(const uint4* r, float* f) {
+        f[0] = bf16_lo(r[0].x); f[1] = bf16_hi(r[0].x); f[2] = bf16_lo(r[0].y); f[3] = bf16_hi(r[0].y);
+        f[4] = bf16_lo(r[0].z); f[5] = bf16_hi(r[0].z); f[6] = bf16_lo(r[0].w); f[7] = bf16_hi(r[0].w);
+    }
+    // stored value of f (round to nearest even) as bits, and as binary32
+    __device__ static __forceinline__ void narrow(const float* f, uint4* r, float* back) {
+        uint32_t h[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            h[i] = f32_to_bf16_rne(f[i]);
+            back[i] = __uint_as_float(h[i] << 16);
+        }
+        r[0] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+    }
+    __device__ static __forceinline__ float load1(const void* p, int64_t e) {
+        return __uint_as_float((uint32_t) static_cast<const uint16_t*>(p)[e] << 16);
+    }
+};
+
+template <> struct Group8<GA_F32> {
+    static constexpr int kVecs = 2;
+    __device__ static __forceinline__ void widen(const uint4* r, float* f) {
+        f[0] = __uint_as_float(r[0].x); f[1] = __uint_as_float(r[0].y);
+        f[2] = __uint_as_float(r[0].z); f[3] = __uint_as_float(r[0].w);
+        f[4] = __uint_as_float(r[1].x); f[5] = __uint_as_float(r[1].y);
+        f[6] = __uint_as_float(r[1].z); f[7] = __uint_as_float(r[1].w);
+    }
+    __device__ static __forceinline__ void narrow(const float* f, uint4* r, float* back) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) back[i] = f[i];
+        r[0] = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+        r[1] = make_uint4(__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]), __float_as_uint(f[7]));
+    }
+    __device__ static __forceinline__ float load1(const void* p, int64_t e) {
+        return static_cast<const float*>(p)[e];
+    }
+};
+
+template <ga_dtype DT>
+__device__ __forceinline__ void load8(const void* p, int64_t g, uint4* r) {
+    constexpr int K = Group8<DT>::kVecs;
+#pragma unroll
+    for (int v = 0; v < K; v++) r[v] = load_stream(static_cast<const uint4*>(p) + K * g + v);
+}
+
+template <ga_dtype DT>
+__device__ __forceinline__ void store8(void* p, int64_t g, const uint4* r) {
+    constexpr int K = Group8<DT>::kVecs;
+#pragma unroll
+    for (int v = 0; v < K; v++) store_stream(static_cast<uint4*>(p) + K * g + v, r[v]);
+}
+
+// The ring chunk of element e: partition p of length plen (the last one
+// short), chunk c = (e - p0) / ceil(n_p / P); the chunk's fold starts at
+// worker c.
+struct Chunk {
+    int64_t part;
+    int c;
+};
+
+__device__ __forceinline__ Chunk chunk_of(int64_t e, int64_t N, int64_t plen, int P) {
+    const int64_t p = e / plen, p0 = p * plen;
+    const int64_t n = min(N - p0, plen);
+    const int64_t C = (n + P - 1) / P;
+    return {p, (int)((e - p0) / C)};
+}
+
+// One worker's 8 values a of group g: quantized with the worker's Philox
+// block of the group, indices added into zs (negated modulo 2^32 when the
+// grid has fewer than 128 levels, as the quantizer's packer keeps them) and
+// packed to the worker's index buffer.
+template <int B>
+__device__ __forceinline__ void quantize8(const float* a, Grid gq, int64_t g, uint32_t wid, uint32_t k0,
+                                          uint32_t k1, uint32_t* zs, uint8_t* out) {
+    constexpr int L = (1 << B) - 1;
+    const Philox4 r = philox4x32_10((uint32_t)g, (uint32_t)((uint64_t)g >> 32), wid, 0u, k0, k1);
+    uint32_t z[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        z[i] = L < 128 ? usq_neg_index(a[i], gq, L, uniform16(r, i)) : usq_index(a[i], gq, L, uniform16(r, i));
+        zs[i] += z[i];
+    }
+    if (out) {
+        if constexpr (L < 128) store_group<B>(out, g, pack_neg_group<B>(z));
+        else store_group<B>(out, g, pack_group<B>(z));
+    }
+}
+
+// PT > 0: P fixed at compile time (every worker loop unrolled, so the
+// workers' Philox rounds and roundings interleave); WPE: waves per SIMD the
+// register allocation aims for. Measured on 8 x 2^31 bf16, b = 2: P at run
+// time (110 registers, 4 waves) 16.9-17.2 ms; P = 8 at compile time 14.5-15.5
+// ms (96 registers); and held to 5 waves (92 registers, no spills) 14.2 ms;
+// 6 waves spills and is slower.
+template <ga_dtype DT, int B, int PT, int WPE>
+__global__ __attribute__((amdgpu_waves_per_eu(WPE))) __launch_bounds__(kThreads) void thc_ring_kernel(
+        PtrTable bufs, PtrTable packed, int has_packed, int P_, int worker0, int64_t N, int64_t rplen,
+        int64_t qplen, const float* __restrict__ mM, uint32_t k0, uint32_t k1, Avg avg,
+        int32_t* __restrict__ sum, void* xhat, double* ws) {
+    using G = Group8<DT>;
+    constexpr int K = G::kVecs;
+    constexpr int L = (1 << B) - 1;
+    constexpr int kB = PT > 0 ? PT : kBatch;          // worker loads in flight
+    const int P = PT > 0 ? PT : P_;
+    __shared__ double sh[kThreads / 64];
+    const int64_t n_groups = N / 8;
+    const int64_t g0 = (int64_t)blockIdx.x * kThreads;
+    const int64_t g = g0 + threadIdx.x;
+    const bool live = g < n_groups;
+    const int64_t gl = min(g0 + (int64_t)kThreads, n_groups) - 1;       // last group here
+    const Chunk first = chunk_of(8 * g0, N, rplen, P), last = chunk_of(8 * gl + 7, N, rplen, P);
+    const bool uniform = first.part == last.part && first.c == last.c;
+    // the group's quantizer partition (qplen is a multiple of 8)
+    const int64_t q = live ? 8 * g / qplen : 0;
+    const Grid gq = grid_of(mM, q, L);
+    float acc[8];
+    uint32_t zs[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) zs[i] = 0u;
+    if (uniform) {
+        // workers in the chunk's fold order first.c, first.c + 1, ...
+        for (int kb = 0; kb < P; kb += kB) {
+            uint4 raw[kB][K];
+#pragma unroll
+            for (int kk = 0; kk < kB; kk++) {
+                if (kb + kk < P && live) {
+                    int w = first.c + kb + kk;
+                    if (w >= P) w -= P;
+                    load8<DT>(bufs.p[w], g, raw[kk]);
+                }
+            }
+#pragma unroll
+            for (int kk = 0; kk < kB; kk++) {
+                if (kb + kk < P && live) {
+                    int w = first.c + kb + kk;
+                    if (w >= P) w -= P;
+                    float a[8];
+                    G::widen(raw[kk], a);
+                    if (kb + kk == 0) {
+#pragma unroll
+                        for (int i = 0; i < 8; i++) acc[i] = a[i];
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 8; i++) acc[i] = acc[i] + a[i];
+                    }
+                    quantize8<B>(a, gq, g, (uint32_t)(worker0 + w), k0, k1, zs,
+                                 has_packed ? static_cast<uint8_t*>(packed.p[w]) : nullptr);
+                }
+            }
+        }
+    } else if (live) {
+        // indices in worker order, then each element folded in its own
+        // chunk's order, read again (a few workgroups per chunk boundary)
+        for (int w = 0; w < P; w++) {
+            uint4 raw[K];
+            load8<DT>(bufs.p[w], g, raw);
+            float a[8];
+            G::widen(raw, a);
+            quantize8<B>(a, gq, g, (uint32_t)(worker0 + w), k0, k1, zs,
+                         has_packed ? static_cast<uint8_t*>(packed.p[w]) : nullptr);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int64_t e = 8 * g + i;
+            int w = chunk_of(e, N, rplen, P).c;
+            float s = G::load1(bufs.p[w], e);
+            for (int k = 1; k < P; k++) {
+                w = w + 1 == P ? 0 : w + 1;
+                s = s + G::load1(bufs.p[w], e);
+            }
+            acc[i] = s;
+        }
+    }
+    double num = 0.0, den = 0.0;
+    if (live) {
+        // the ring's average, to every worker
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) acc[i] = avg.apply(acc[i]);
+        uint4 o[K];
+        G::narrow(acc, o, x);
+        for (int w = 0; w < P; w++) store8<DT>(bufs.p[w], g, o);
+        // the server's sum and the dequantized average m + (S / P) delta
+        const float m = mM[2 * q], range = mM[2 * q + 1] - m, delta = range / (float)L;
+        int32_t S[8];
+        float v[8], h[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            S[i] = L < 128 ? (int32_t)(0u - zs[i]) : (int32_t)zs[i];
+            v[i] = range != 0.0f ? m + avg.apply((float)S[i]) * delta : m;
+        }
+        if (sum) {
+            store_stream(sum + 8 * g, make_uint4((uint32_t)S[0], (uint32_t)S[1], (uint32_t)S[2], (uint32_t)S[3]));
+            store_stream(sum + 8 * g + 4, make_uint4((uint32_t)S[4], (uint32_t)S[5], (uint32_t)S[6], (uint32_t)S[7]));
+        }
+        uint4 ho[K];
+        G::narrow(v, ho, h);
+        store8<DT>(xhat, g, ho);
+        // NMSE terms of the values as stored
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const double d = (double)x[i] - (double)h[i];
+            num += d * d;
+            den += (double)x[i] * (double)x[i];
+        }
+    }
+    if (ws) {
+        num = block_sum(num, sh);
+        den = block_sum(den, sh);
+        if (threadIdx.x == 0) {
+            ws[2 * blockIdx.x] = num;
+            ws[2 * blockIdx.x + 1] = den;
+        }
+    }
+}
+
+int64_t step_blocks(int64_t N) { return std::max<int64_t>(1, ceil_div(std::max<int64_t>(N, 0) / 8, kThreads)); }
+
+// Workgroups resident per CU on large inputs. The ring alone streams best
+// with few (its 2P open DRAM streams), but here the rounding arithmetic needs
+// the waves to hide behind: 8 x 2^31 bf16, b = 2, 23.6 ms at two per CU,
+// 16.9 at four, 16.9-17.3 uncapped. At 32 workers (fp32, 138M) two per CU
+// measured best (14.0 ms; four 15.0, uncapped 15.1-15.7). Capped with unused
+// dynamic LDS, as the ring does.
+size_t step_lds(int P, int64_t bytes) {
+    constexpr size_t kLdsPerCu = 160 * 1024;
+    if (bytes < ((int64_t)1 << 28) || P <= 16) return 0;
+    return kLdsPerCu / 2 - 1024;
+}
+
+}  // namespace
+}  // namespace ga
+
+using namespace ga;
+
+extern "C" size_t thc_ring_step_ws_bytes(int64_t N) {
+    const int64_t nblk = step_blocks(N);
+    const int64_t ng = nblk > kNmseGroup ? ceil_div(nblk, kNmseGroup) : 0;
+    return (size_t)(nblk + ng) * 2 * sizeof(double);
+}
+
+extern "C" ga_status thc_ring_step(void* const* bufs, int32_t P, int64_t N, ga_dtype dt, int64_t ring_part,
+                                   const float* d_mM, int64_t q_part, int32_t b, uint64_t seed,
+                                   int32_t worker0, uint8_t* const* packed, int32_t* d_sum, void* xhat,
+                                   double* d_nmse, void* d_ws, size_t ws_bytes, void* stream) {
+    const char* what = "thc_ring_step";
+    if (!valid_dtype(dt)) return fail(GA_EINVAL, "%s: unknown dtype %d", what, (int)dt);
+    if (b != 1 && b != 2 && b != 4 && b != 8) return fail(GA_EINVAL, "%s: b = %d not in {1, 2, 4, 8}", what, b);
+    if (N < 0 || ring_part < 0 || q_part < 0 || worker0 < 0)
+        return fail(GA_EINVAL, "%s: negative size or worker", what);
+    if (P < 1 || P > GA_MAX_WORKERS)
+        return fail(GA_EINVAL, "%s: P = %d outside [1, %d]", what, P, GA_MAX_WORKERS);
+    if ((int64_t)P * ((1 << b) - 1) > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: sums overflow int32", what);
+    if (N == 0) return GA_OK;
+    ga_status rc = check_workers(bufs, P, 16, what);
+    if (rc) return rc;
+    const int64_t rplen = ring_part > 0 ? ring_part : N, qplen = q_part > 0 ? q_part : N;
+    if (N % 8 || qplen % 8)
+        return fail(GA_ENOTSUP, "%s: N and the quantizer partition must be multiples of 8 (groups of "
+                    "8 elements); use the separate calls", what);
+    const int64_t es = (int64_t)elem_size(dt);
+    for (int i = 0; i < P; i++)
+        for (int j = i + 1; j < P; j++) {
+            const uintptr_t a = (uintptr_t)bufs[i], c = (uintptr_t)bufs[j];
+            if (a < c + (uintptr_t)(N * es) && c < a + (uintptr_t)(N * es))
+                return fail(GA_EINVAL, "%s: worker buffers overlap", what);
+        }
+    if (!d_mM || !aligned(d_mM, 8)) return fail(GA_EINVAL, "%s: null or misaligned grid", what);
+    if (!xhat || !aligned(xhat, 16)) return fail(GA_EINVAL, "%s: null or misaligned estimate", what);
+    if (d_sum && !aligned(d_sum, 16)) return fail(GA_EINVAL, "%s: misaligned sums", what);
+    if (packed)
+        for (int i = 0; i < P; i++)
+            if (!packed[i] || !aligned(packed[i], 8))
+                return fail(GA_EINVAL, "%s: worker %d: null or misaligned index buffer", what, i);
+    if (d_nmse) {
+        if (!aligned(d_nmse, 8) || !d_ws || !aligned(d_ws, 8))
+            return fail(GA_EINVAL, "%s: null or misaligned NMSE output or workspace", what);
+        if (ws_bytes < thc_ring_step_ws_bytes(N))
+            return fail(GA_EINVAL, "%s: workspace of %zu bytes, need %zu", what, ws_bytes,
+                        thc_ring_step_ws_bytes(N));
+    }
+    const int64_t nblk = step_blocks(N);
+    if (nblk > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: N too large", what);
+    PtrTable tb{}, tp{};
+    for (int i = 0; i < P; i++) {
+        tb.p[i] = bufs[i];
+        tp.p[i] = packed ? packed[i] : nullptr;
+    }
+    const Avg avg{(P & (P - 1)) == 0, (float)P, 1.0f / (float)P};
+    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    double* ws = d_nmse ? static_cast<double*>(d_ws) : nullptr;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const size_t lds = step_lds(P, 2 * (int64_t)P * N * es);
+    const dim3 grid((unsigned)nblk);
+    const int hp = packed != nullptr;
+#define GA_STEP(DT, B, PT, W)                                                                   \
+    hipLaunchKernelGGL((thc_ring_kernel<DT, B, PT, W>), grid, dim3(kThreads), lds, hs, tb, tp, hp, P, \
+                       worker0, N, rplen, qplen, d_mM, k0, k1, avg, d_sum, xhat, ws)
+#define GA_STEP_P(DT, B)                                                                        \
+    do {                                                                                        \
+        if (P == 8) GA_STEP(DT, B, 8, DT == GA_BF16 ? 5 : 3);                                   \
+        else if (P == 16) GA_STEP(DT, B, 16, DT == GA_BF16 ? 3 : 2);                            \
+        else GA_STEP(DT, B, 0, 1);                                                              \
+    } while (0)
+    if (dt == GA_F32) {
+        if (b == 1) GA_STEP_P(GA_F32, 1); else if (b == 2) GA_STEP_P(GA_F32, 2);
+        else if (b == 4) GA_STEP_P(GA_F32, 4); else GA_STEP_P(GA_F32, 8);
+    } else {
+        if (b == 1) GA_STEP_P(GA_BF16, 1); else if (b == 2) GA_STEP_P(GA_BF16, 2);
+        else if (b == 4) GA_STEP_P(GA_BF16, 4); else GA_STEP_P(GA_BF16, 8);
+    }
+#undef GA_STEP_P
+#undef GA_STEP
+    if ((rc = check_launch(what))) return rc;
+    if (!d_nmse) return GA_OK;
+    if (nblk > kNmseGroup) {                             // two levels
+        const int64_t ng = ceil_div(nblk, kNmseGroup);
+        hipLaunchKernelGGL(nmse_group_kernel, dim3((unsigned)ng), dim3(kThreads), 0, hs, ws, nblk, ws + 2 * nblk);
+        if ((rc = check_launch(what))) return rc;
+        hipLaunchKernelGGL(nmse_final_kernel, dim3(1), dim3(kThreads), 0, hs, ws + 2 * nblk, (int)ng, d_nmse);
+    } else {
+        hipLaunchKernelGGL(nmse_final_kernel, dim3(1), dim3(kThreads), 0, hs, ws, (int)nblk, d_nmse);
+    }
+    return check_launch(what);
+}

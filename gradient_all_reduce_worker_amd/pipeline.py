@@ -9,16 +9,20 @@ A step runs, in this order, on the current stream:
       the averages back into the tensors (one launch); a tensor larger than
       the fusion buffer is reduced alone, in place;
   flat workloads (one gradient vector per worker):
-      THC min/max per partition, USQ quantize for every bit width (both read
-      the workers' gradients before the ring overwrites them),
+      THC min/max per partition, USQ quantize for every bit width but the
+      first (these read the workers' gradients before the ring overwrites
+      them),
       for every THC pass behind the randomized Hadamard transform (THC page
       section 5): per-block norms, the norm-based range, the transform with
       truncation, the table quantizer on the transformed coordinates,
       for every error-feedback pass (THC page section 5): min/max and the
       quantizer on gradient + residual, the residual written back,
-      ring-average the gradients in place (the exact average),
-      then per bit width: integer aggregate, dequantize, NMSE of the THC
-      estimate against the exact average (for RHT passes: table-sum
+      one pass (thc_ring_step) that quantizes the first bit width, leaves
+      the ring's exact average in place and sums, dequantizes and measures
+      that width's estimate against the average (fused_step; else the
+      quantizer, the ring and the tail as three calls),
+      then per remaining pass: integer aggregate, dequantize, NMSE of the
+      THC estimate against the exact average (for RHT passes: table-sum
       aggregate, dequantize, inverse transform, NMSE); the partial pass
       (THC page section 8) sums only the workers that arrived and divides
       by their count.
@@ -96,9 +100,21 @@ class Pipeline:
     rht: Dict[str, tuple] = {}
 
     def __init__(self, name: str, device="cuda", cap_bytes: int = 64 << 20, zero_copy: bool = True,
-                 ring_mode: int = ga.RING_FUSED, fused_tail: bool = True):
+                 ring_mode: int = ga.RING_FUSED, fused_tail: bool = True, fused_step: bool = True):
         self.w = synth.workload(name)
         self.zero_copy = zero_copy
+        # the first uniform THC pass, the ring average and that pass's sum,
+        # dequant and NMSE in one read (thc_ring_step), where the sizes allow
+        # and it measured faster: up to 16 workers (8 x 2^31 bf16, b = 2:
+        # 13.9 ms against 22.0 ms for the three calls; 16 x 2^28 bf16 3.5
+        # against 5.8; 8 x 2^28 fp32 3.9 against 4.9). At 32 workers
+        # (32 x 138M fp32) it is slower (12.8 against 9.5 ms): the fold keeps
+        # 32 workers' loads for the rounding, and a group of 8 fp32 per thread
+        # leaves every 16-byte access instruction covering every other half
+        # of the wave's lines.
+        w = self.w
+        self.fused_step = (fused_step and not w.fused and bool(w.thc_bits) and w.N % 8 == 0
+                           and w.part_elems % 8 == 0 and ring_mode == ga.RING_FUSED and w.P <= 16)
         # THC's integer sum, dequant and NMSE in one pass (thc_aggregate_dequant)
         # or as the three separate calls
         self.fused_tail = fused_tail
@@ -204,6 +220,7 @@ class Pipeline:
                 self.xhat[k] = torch.empty(self.N, dtype=self.tdt, device=dev)
                 self.nmse[k] = torch.empty(3, dtype=torch.float64, device=dev)
             self.ws = torch.empty(ga.thc_nmse_ws_bytes(self.N), dtype=torch.uint8, device=dev)
+            self.ws_step = torch.empty(ga.thc_ring_step_ws_bytes(self.N), dtype=torch.uint8, device=dev)
             self.ws_ad = torch.empty(ga.thc_aggregate_dequant_ws_bytes(self.N), dtype=torch.uint8,
                                      device=dev)
         torch.cuda.synchronize()
@@ -226,8 +243,11 @@ class Pipeline:
                 _call(timer, "fuse_unpack", self.tables.unpack)
             return
         part = w.part_elems
+        b0 = w.thc_bits[0] if self.fused_step else None
         _call(timer, "thc_minmax", ga.thc_minmax, self.flat, part, self.mM)
         for b in w.thc_bits:
+            if b == b0:
+                continue
             _call(timer, f"thc_usq_quantize_b{b}", ga.thc_usq_quantize, self.flat, self.mM, b,
                   w.quant_seed, part, 0, self.packed[b])
         if w.global_bits:
@@ -249,8 +269,13 @@ class Pipeline:
                   self.mM_ef[k])
             _call(timer, f"thc_ef_quantize_{k}", ga.thc_ef_quantize, self.flat, self.err[k],
                   self.mM_ef[k], b, w.quant_seed, part, 0, 0, None, self.packed[k])
-        _call(timer, "ring_allreduce", ga.ga_ring_allreduce_sim, self.flat, ga.AVG,
-              w.ring_part_elems, self.ring_mode)
+        if self.fused_step:
+            _call(timer, f"thc_ring_step_b{b0}", ga.thc_ring_step, self.flat, self.mM, b0, w.quant_seed,
+                  w.ring_part_elems, part, 0, self.packed[b0], True, self.S[b0], True, self.xhat[b0],
+                  self.nmse[b0], self.ws_step)
+        else:
+            _call(timer, "ring_allreduce", ga.ga_ring_allreduce_sim, self.flat, ga.AVG,
+                  w.ring_part_elems, self.ring_mode)
         for b in w.ef_bits:
             k = f"ef{b}"
             self._tail(timer, k, self.packed[k], b, self.mM_ef[k], part)
@@ -268,7 +293,8 @@ class Pipeline:
         for k, (b, g, T) in self.nu_tables.items():
             self._tail(timer, k, self.packed[k], b, self.mM, part, g=g, table=T)
         for b in w.thc_bits:
-            self._tail(timer, f"b{b}", self.packed[b], b, self.mM, part, sum_key=b)
+            if b != b0:
+                self._tail(timer, f"b{b}", self.packed[b], b, self.mM, part, sum_key=b)
         for b in w.global_bits:
             k = f"g{b}"
             self._tail(timer, k, self.packed[k], b, self.mM_g, 0)
@@ -313,6 +339,10 @@ class Pipeline:
             return out
         out["thc_minmax"] = 1.0 * P * N * s
         out["ring_allreduce"] = 2.0 * P * N * s
+        for b in w.thc_bits:
+            # gradients read once and the average written back, the indices,
+            # the sums and the estimate written
+            out[f"thc_ring_step_b{b}"] = 2.0 * P * N * s + P * N * b / 8.0 + 4.0 * N + N * s
         for b in w.thc_bits:
             out[f"thc_usq_quantize_b{b}"] = P * N * (s + b / 8.0)
             out[f"thc_int_aggregate_b{b}"] = P * N * b / 8.0 + 4.0 * N

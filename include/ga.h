@@ -11,6 +11,7 @@
  *   thc_nmse_noalloc (thc_nmse without a workspace, for callers that
  *   cannot allocate)
  *   thc_aggregate_dequant (aggregate + dequant + NMSE in one pass)
+ *   thc_ring_step (quantize, ring average, sum, dequant, NMSE: one read)
  *                                                  THC uniform quantization
  *   thc_nuhc_quantize / thc_nuhc_aggregate / thc_nuhc_dequant
  *                                                  THC with lookup tables
@@ -351,6 +352,32 @@ size_t thc_nmse_ws_bytes(int64_t N);
  */
 ga_status thc_nmse_noalloc(const void* x, const void* xhat, int64_t N, ga_dtype dt, double* d_out,
                            void* stream);
+
+/*
+ * thc_ring_step -- one pass over the P workers' buffers that leaves exactly
+ * what these calls leave in turn, reading every gradient once:
+ *   thc_usq_quantize(bufs, P, worker0, N, dt, q_part, d_mM, b, seed, packed)
+ *   ga_ring_allreduce_sim(bufs, P, N, dt, GA_AVG, ring_part, GA_RING_FUSED)
+ *   thc_aggregate_dequant(packed, P, N, b, d_mM, q_part, out = xhat in dt,
+ *                         sum = d_sum, NMSE against the ring's average)
+ * ([THC] sections 2-3, Algorithm 1: quantize, integer sum, decode the
+ * average; [HVD] 3.4 and [RING] sections 4, 7: the ring average the
+ * estimate is measured against). The indices are made from the gradients
+ * before the average overwrites them. packed (host array of P device
+ * pointers, each 8-byte aligned, ceil(N b / 8) bytes) and d_sum (N int32,
+ * 16-byte aligned) may be null to skip writing them; xhat (N elements of
+ * dt, 16-byte aligned) is required; d_nmse (num, den, ratio) may be null,
+ * else d_ws holds thc_ring_step_ws_bytes(N) bytes. bufs: 16-byte aligned,
+ * disjoint. Packed bytes, sums, x̂ and the averages are bit for bit those
+ * of the separate calls; the NMSE sums are in another order (within 1e-12
+ * relative). GA_ENOTSUP when N or the quantizer partition is not a multiple
+ * of 8 (the separate calls take any size).
+ */
+ga_status thc_ring_step(void* const* bufs, int32_t P, int64_t N, ga_dtype dt, int64_t ring_part,
+                        const float* d_mM, int64_t q_part, int32_t b, uint64_t seed, int32_t worker0,
+                        uint8_t* const* packed, int32_t* d_sum, void* xhat, double* d_nmse, void* d_ws,
+                        size_t ws_bytes, void* stream);
+size_t thc_ring_step_ws_bytes(int64_t N);
 
 /* ------------------------------------------------------------------ */
 /* Non-uniform THC: lookup tables  ([THC] section 4, Algorithm 2)       */

@@ -27,7 +27,7 @@ def _declared():
 def test_header_declarations_are_exported():
     L = nat.load()
     names = _declared()
-    assert len(names) == 29
+    assert len(names) == 31
     assert set(names) == set(nat.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
