@@ -76,10 +76,32 @@ __device__ __forceinline__ void store_stream(void* p, uint4 v) {
     __builtin_nontemporal_store(r, (g_u32x4_t*)p);
 }
 
-// 64-bit element index of the first element handled by this thread when
-// every thread of the grid handles `per_thread` consecutive elements.
-__device__ __forceinline__ int64_t thread_base(int per_thread) {
-    return ((int64_t)blockIdx.x * kThreads + threadIdx.x) * per_thread;
+// ------------------------------------------------------------------ launch geometry
+// A dispatch packet carries each grid dimension as a 32-bit count of
+// work-items: a launch of more than 2^32 - 1 work-items along x does not
+// fail, the count wraps and fewer workgroups run. kMaxBlocksX is the most
+// kThreads-thread workgroups one launch takes along x. Kernels whose
+// workgroup count grows with N take a folded grid: flat_grid(n, y) spreads n
+// workgroups over x and z (y stays free for the worker slot), and the kernel
+// reads its linear index with flat_block() and returns when it is >= n
+// (fewer than z such workgroups).
+constexpr int64_t kMaxBlocksX = 0xFFFFFFFFll / kThreads;
+constexpr int64_t kMaxFoldZ = 1024;
+
+// A plain (unfolded) launch of `blocks` workgroups of `threads` threads fits.
+inline bool grid_fits(int64_t blocks, int threads = kThreads) {
+    return blocks >= 0 && blocks <= 0xFFFFFFFFll / threads;
+}
+// flat_grid can cover `blocks` workgroups.
+inline bool flat_fits(int64_t blocks) { return blocks >= 0 && blocks <= kMaxBlocksX * kMaxFoldZ; }
+
+inline dim3 flat_grid(int64_t blocks, unsigned y = 1) {
+    const int64_t z = blocks > kMaxBlocksX ? ceil_div(blocks, kMaxBlocksX) : 1;
+    return dim3((unsigned)ceil_div(blocks, z), y, (unsigned)z);
+}
+
+__device__ __forceinline__ int64_t flat_block() {
+    return (int64_t)blockIdx.z * gridDim.x + blockIdx.x;
 }
 
 }  // namespace ga

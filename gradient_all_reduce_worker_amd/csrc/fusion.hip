@@ -105,7 +105,8 @@ __device__ void copy_segment(const char* __restrict__ s, char* __restrict__ d, i
 __global__ __launch_bounds__(kThreads) void fuse_copy_kernel(const ga_copy_desc* __restrict__ desc,
                                                              int64_t n_desc, int64_t total,
                                                              int64_t tile, int es) {
-    const int64_t g0 = (int64_t)blockIdx.x * tile;
+    const int64_t g0 = flat_block() * tile;
+    if (g0 >= total) return;                           // past the folded grid's end
     const int64_t g1 = min(g0 + tile, total);
     // last descriptor whose start is <= g0
     int64_t lo = 0, hi = n_desc - 1;
@@ -133,8 +134,8 @@ ga_status launch_copy(const ga_copy_desc* d_desc, int64_t n_desc, int64_t total,
     const int es = (int)elem_size(dt);
     const int64_t tile = (total * es >= ((int64_t)1 << 30) ? kTileBytesLarge : kTileBytesSmall) / es;
     const int64_t blocks = ceil_div(total, tile);
-    if (blocks > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: too many elements", what);
-    hipLaunchKernelGGL(fuse_copy_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
+    if (!flat_fits(blocks)) return fail(GA_EINVAL, "%s: too many elements", what);
+    hipLaunchKernelGGL(fuse_copy_kernel, flat_grid(blocks), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), d_desc, n_desc, total, tile, es);
     return check_launch(what);
 }

@@ -651,7 +651,8 @@ template <ga_dtype DT>
 __global__ __launch_bounds__(kThreads) void rht_sumsq_kernel(PtrTable x, int64_t N, int dbits,
                                                              int64_t nblk, double* sumsq) {
     const int w = blockIdx.y;
-    const int64_t b = blockIdx.x;
+    const int64_t b = flat_block();
+    if (b >= nblk) return;                              // past the folded grid's end
     const int64_t lo = b << dbits, hi = min(lo + ((int64_t)1 << dbits), N);
     const void* xw = x.p[w];
     double acc = 0.0;
@@ -685,7 +686,7 @@ __global__ __launch_bounds__(kThreads) void rht_sumsq_kernel(PtrTable x, int64_t
 
 __global__ __launch_bounds__(kThreads) void rht_range_kernel(const double* sumsq, int P, int64_t nblk,
                                                              double d, double t_p, float* mM) {
-    const int64_t p = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t p = flat_block() * kThreads + threadIdx.x;
     if (p >= nblk) return;
     double mx = 0.0;
     for (int i = 0; i < P; i++) mx = fmax(mx, sumsq[(int64_t)i * nblk + p]);
@@ -747,14 +748,14 @@ extern "C" ga_status thc_rht_sumsq(const void* const* bufs, int32_t P, int64_t N
     if (rc) return rc;
     if (!d_sumsq || !aligned(d_sumsq, 8)) return fail(GA_EINVAL, "%s: bad output pointer", what);
     const int64_t nblk = ceil_div(N, d);
-    if (nblk > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: too many blocks", what);
+    if (!flat_fits(nblk)) return fail(GA_EINVAL, "%s: too many blocks", what);
     PtrTable t{};
     for (int i = 0; i < P; i++) t.p[i] = const_cast<void*>(bufs[i]);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (dt == GA_F32)
-        hipLaunchKernelGGL(rht_sumsq_kernel<GA_F32>, dim3((unsigned)nblk, (unsigned)P), dim3(kThreads), 0, hs, t, N, dbits, nblk, d_sumsq);
+        hipLaunchKernelGGL(rht_sumsq_kernel<GA_F32>, flat_grid(nblk, (unsigned)P), dim3(kThreads), 0, hs, t, N, dbits, nblk, d_sumsq);
     else
-        hipLaunchKernelGGL(rht_sumsq_kernel<GA_BF16>, dim3((unsigned)nblk, (unsigned)P), dim3(kThreads), 0, hs, t, N, dbits, nblk, d_sumsq);
+        hipLaunchKernelGGL(rht_sumsq_kernel<GA_BF16>, flat_grid(nblk, (unsigned)P), dim3(kThreads), 0, hs, t, N, dbits, nblk, d_sumsq);
     return check_launch(what);
 }
 
@@ -767,7 +768,8 @@ extern "C" ga_status thc_rht_range(const double* d_sumsq, int32_t P, int64_t nbl
     if (nblk == 0) return GA_OK;
     if (!d_sumsq || !d_mM || !aligned(d_sumsq, 8) || !aligned(d_mM, 8))
         return fail(GA_EINVAL, "%s: bad pointer", what);
-    hipLaunchKernelGGL(rht_range_kernel, dim3((unsigned)ceil_div(nblk, kThreads)), dim3(kThreads), 0,
+    if (!flat_fits(ceil_div(nblk, kThreads))) return fail(GA_EINVAL, "%s: too many blocks", what);
+    hipLaunchKernelGGL(rht_range_kernel, flat_grid(ceil_div(nblk, kThreads)), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), d_sumsq, P, nblk, (double)d, t_p, d_mM);
     return check_launch(what);
 }
@@ -788,7 +790,7 @@ extern "C" ga_status thc_rht_forward(const void* const* bufs, int32_t P, int64_t
     if (d_mM && !aligned(d_mM, 8)) return fail(GA_EINVAL, "%s: misaligned range", what);
     const int64_t Np = ceil_div(N, d) * d;
     const int64_t tiles = ceil_div(Np, kTile);
-    if (tiles > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: too many tiles", what);
+    if (!grid_fits(tiles, kTT)) return fail(GA_EINVAL, "%s: too many tiles", what);
     PtrTable tx{}, ty{};
     int vec = 1;                                      // 16-byte loads of x in the first pass
     for (int i = 0; i < P; i++) {
@@ -831,7 +833,7 @@ extern "C" ga_status thc_rht_inverse(float* y, int64_t N, int64_t d, uint64_t se
         return fail(GA_EINVAL, "%s: null or misaligned pointer", what);
     const int64_t Np = ceil_div(N, d) * d;
     const int64_t tiles = ceil_div(Np, kTile);
-    if (tiles > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: too many tiles", what);
+    if (!grid_fits(tiles, kTT)) return fail(GA_EINVAL, "%s: too many tiles", what);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
     const float c = inv_sqrt_d(d);
@@ -884,7 +886,7 @@ extern "C" ga_status thc_rht_quantize(const void* const* bufs, int32_t P, int32_
     }
     const int64_t Np = ceil_div(N, d) * d;
     const int64_t tiles = ceil_div(Np, kTile);
-    if (tiles > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: too many tiles", what);
+    if (!grid_fits(tiles, kTT)) return fail(GA_EINVAL, "%s: too many tiles", what);
     PtrTable tx{}, ty{}, tp{};
     int vec = 1;                                      // 16-byte loads of x in the first pass
     for (int i = 0; i < P; i++) {

@@ -256,7 +256,8 @@ __global__ __launch_bounds__(kThreads) void ring_fused_vec_kernel(PtrTable bufs,
     using E = Elem<DT>;
     constexpr int V = E::kVec;
     const int nch = DUAL ? 2 * P : P;
-    const int64_t vb0 = (int64_t)blockIdx.x * (kThreads * VPT);
+    const int64_t vb0 = flat_block() * (kThreads * VPT);
+    if (vb0 >= n_vec) return;                              // past the folded grid's end
     const int64_t vb1 = min(vb0 + (int64_t)(kThreads * VPT), n_vec);
     const Where first = locate(vb0 * V, N, plen, nch);
     const Where last = locate(vb1 * V - 1, N, plen, nch);
@@ -321,8 +322,11 @@ static_assert(sizeof(FusionBlock) == 16, "block header is 16 bytes");
 // thread i folding vector (or element) i of the block.
 template <ga_dtype DT>
 __global__ __launch_bounds__(kThreads) void fusion_ring_kernel(const uint8_t* __restrict__ work,
-                                                               int64_t stride, int P, Div div) {
-    const uint8_t* blk = work + (int64_t)blockIdx.x * stride;
+                                                               int64_t stride, int64_t n_blocks, int P,
+                                                               Div div) {
+    const int64_t b = flat_block();
+    if (b >= n_blocks) return;                             // past the folded grid's end
+    const uint8_t* blk = work + b * stride;
     const FusionBlock h = *reinterpret_cast<const FusionBlock*>(blk);
     const RowPtrs row{reinterpret_cast<void* const*>(blk + sizeof(FusionBlock))};
     const Rot rt{h.start, h.dir};
@@ -376,7 +380,8 @@ __global__ __launch_bounds__(kThreads) void ring_step_vec_kernel(PtrTable bufs, 
                                                                  int64_t plen, int64_t n_vec,
                                                                  Step st, Div div) {
     constexpr int V = 4;
-    const int64_t vb0 = (int64_t)blockIdx.x * (kThreads * kVecPerThread);
+    const int64_t vb0 = flat_block() * (kThreads * kVecPerThread);
+    if (vb0 >= n_vec) return;                              // past the folded grid's end
     const int64_t vb1 = min(vb0 + (int64_t)(kThreads * kVecPerThread), n_vec);
     const Where first = locate(vb0 * V, N, plen, P);
     const Where last = locate(vb1 * V - 1, N, plen, P);
@@ -485,7 +490,9 @@ int64_t launch_fused(void* const* bufs, int P, int64_t N, ga_dtype dt, int64_t p
     ga_status rc;
     if (vec_ok && n_vec > 0) {
         const FoldShape sh = fold_shape(P, 2 * (int64_t)P * N * (int64_t)elem_size(dt));
-        const unsigned blocks = (unsigned)ceil_div(n_vec, (int64_t)kThreads * sh.vpt);
+        const int64_t nb = ceil_div(n_vec, (int64_t)kThreads * sh.vpt);
+        if (!flat_fits(nb)) return fail(GA_EINVAL, "%s: N too large", what);
+        const dim3 blocks = flat_grid(nb);
         if (dt == GA_F32 && sh.vpt == 4)
             hipLaunchKernelGGL((ring_fused_vec_kernel<GA_F32, 4, 4, DUAL>), dim3(blocks),
                                dim3(kThreads), sh.lds, hs, t, P, N, plen, n_vec, div);
@@ -575,6 +582,7 @@ extern "C" ga_status ga_ring_allreduce_sim(void* const* bufs, int32_t P, int64_t
 
     if (N > 0 && P > 1) {
         const int64_t vblocks = ceil_div(n_vec, kThreads * kVecPerThread);
+        if (!flat_fits(vblocks)) return fail(GA_EINVAL, "%s: N too large", what);
         if (mode == GA_RING_FUSED || mode == GA_RING_DUAL) {
             const int64_t n = mode == GA_RING_DUAL
                                   ? launch_fused<true>(bufs, P, N, dt, plen, div, hs, what)
@@ -589,7 +597,7 @@ extern "C" ga_status ga_ring_allreduce_sim(void* const* bufs, int32_t P, int64_t
                 for (int step = 0; step < P - 1; step++) {
                     Step sp{step, phase == 0, phase == 0 && step == P - 2 && op == GA_AVG};
                     if (vec_ok && n_vec > 0) {
-                        hipLaunchKernelGGL(ring_step_vec_kernel, dim3((unsigned)vblocks),
+                        hipLaunchKernelGGL(ring_step_vec_kernel, flat_grid(vblocks),
                                            dim3(kThreads), 0, hs, t, P, N, plen, n_vec, sp, div);
                         launches++;
                         if ((rc = check_launch(what))) return rc;
@@ -793,16 +801,18 @@ extern "C" ga_status ga_fusion_ring_allreduce(const void* d_work, int64_t n_bloc
         return GA_OK;
     }
     if (!d_work || !aligned(d_work, 8)) return fail(GA_EINVAL, "%s: null or misaligned blocks", what);
-    if (n_blocks > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: too many blocks", what);
+    if (!flat_fits(n_blocks)) return fail(GA_EINVAL, "%s: too many blocks", what);
     Div div{op == GA_AVG, (P & (P - 1)) == 0, (float)P, 1.0f / (float)P};
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const size_t lds = fusion_cap(P, 2 * (int64_t)P * total * es);
     const int64_t stride = (int64_t)GA_FUSION_BLOCK_BYTES(P);
     const uint8_t* w = static_cast<const uint8_t*>(d_work);
     if (dt == GA_F32)
-        hipLaunchKernelGGL((fusion_ring_kernel<GA_F32>), dim3((unsigned)n_blocks), dim3(kThreads), lds, hs, w, stride, P, div);
+        hipLaunchKernelGGL((fusion_ring_kernel<GA_F32>), flat_grid(n_blocks), dim3(kThreads), lds, hs, w, stride,
+                           n_blocks, P, div);
     else
-        hipLaunchKernelGGL((fusion_ring_kernel<GA_BF16>), dim3((unsigned)n_blocks), dim3(kThreads), lds, hs, w, stride, P, div);
+        hipLaunchKernelGGL((fusion_ring_kernel<GA_BF16>), flat_grid(n_blocks), dim3(kThreads), lds, hs, w, stride,
+                           n_blocks, P, div);
     ga_status rc = check_launch(what);
     if (rc) return rc;
     s.launches = 1;

@@ -159,7 +159,9 @@ __global__ __attribute__((amdgpu_waves_per_eu(WPE))) __launch_bounds__(kThreads)
     const int P = PT > 0 ? PT : P_;
     __shared__ double sh[kThreads / 64];
     const int64_t n_groups = N / 8;
-    const int64_t g0 = (int64_t)blockIdx.x * kThreads;
+    const int64_t blk = flat_block();
+    const int64_t g0 = blk * kThreads;
+    if (g0 >= n_groups) return;                        // past the folded grid's end
     const int64_t g = g0 + threadIdx.x;
     const bool live = g < n_groups;
     const int64_t gl = min(g0 + (int64_t)kThreads, n_groups) - 1;       // last group here
@@ -263,8 +265,8 @@ __global__ __attribute__((amdgpu_waves_per_eu(WPE))) __launch_bounds__(kThreads)
         num = block_sum(num, sh);
         den = block_sum(den, sh);
         if (threadIdx.x == 0) {
-            ws[2 * blockIdx.x] = num;
-            ws[2 * blockIdx.x + 1] = den;
+            ws[2 * blk] = num;
+            ws[2 * blk + 1] = den;
         }
     }
 }
@@ -335,7 +337,7 @@ extern "C" ga_status thc_ring_step(void* const* bufs, int32_t P, int64_t N, ga_d
                         thc_ring_step_ws_bytes(N));
     }
     const int64_t nblk = step_blocks(N);
-    if (nblk > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: N too large", what);
+    if (!flat_fits(nblk)) return fail(GA_EINVAL, "%s: N too large", what);
     PtrTable tb{}, tp{};
     for (int i = 0; i < P; i++) {
         tb.p[i] = bufs[i];
@@ -346,7 +348,7 @@ extern "C" ga_status thc_ring_step(void* const* bufs, int32_t P, int64_t N, ga_d
     double* ws = d_nmse ? static_cast<double*>(d_ws) : nullptr;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const size_t lds = step_lds(P, 2 * (int64_t)P * N * es);
-    const dim3 grid((unsigned)nblk);
+    const dim3 grid = flat_grid(nblk);
     const int hp = packed != nullptr;
 #define GA_STEP(DT, B, PT, W)                                                                   \
     hipLaunchKernelGGL((thc_ring_kernel<DT, B, PT, W>), grid, dim3(kThreads), lds, hs, tb, tp, hp, P, \

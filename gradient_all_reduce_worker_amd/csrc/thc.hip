@@ -59,7 +59,7 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 }
 
 __global__ __launch_bounds__(kThreads) void minmax_init_kernel(uint32_t* keys, int64_t n_part) {
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t i = flat_block() * kThreads + threadIdx.x;
     if (i < n_part) {
         keys[2 * i] = 0xFFFFFFFFu;
         keys[2 * i + 1] = 0u;
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void minmax_init_kernel(uint32_t* keys, i
 }
 
 __global__ __launch_bounds__(kThreads) void minmax_final_kernel(uint32_t* keys, int64_t n_part) {
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t i = flat_block() * kThreads + threadIdx.x;
     if (i < n_part) {
         // "+ 0.0f" turns a negative zero into +0
         const float m = key_value(keys[2 * i]) + 0.0f;
@@ -106,8 +106,9 @@ __global__ __launch_bounds__(kThreads) void minmax_kernel(PtrTable bufs, PtrTabl
                                                           int64_t slice_len, uint32_t* keys) {
     using V = Vec16<DT>;
     constexpr int E = V::kElems;
-    const int64_t p = blockIdx.x / slices;
-    const int64_t j = blockIdx.x % slices;
+    const int64_t blk = flat_block();                     // a folded grid's extra workgroups
+    const int64_t p = blk / slices;                        // find lo >= hi below
+    const int64_t j = blk % slices;
     const int64_t p0 = p * plen;
     const int64_t pend = min(p0 + plen, N);
     const int64_t lo = p0 + j * slice_len;
@@ -434,8 +435,8 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_lane_kernel(PtrTable bu
     Grid gb{};
     EfGrid q{};
     for (int sp = 0; sp < spans; sp += 2) {               // spans of this workgroup
-        const int64_t blk = (int64_t)blockIdx.x * spans + sp;
-        if (blk >= n_spans) break;
+        const int64_t blk = flat_block() * spans + sp;
+        if (blk >= n_spans) break;                       // also a folded grid's extras
         const bool two = sp + 1 < spans && blk + 1 < n_spans;
         float a[2][2][4];
 #pragma unroll
@@ -653,7 +654,8 @@ __global__ __launch_bounds__(kThreads) void int_aggregate_kernel(PtrTable packed
         __syncthreads();
     }
     const int64_t n_units = (N + 3) / 4;
-    const int64_t u_blk = u_begin + (int64_t)blockIdx.x * kThreads * kAUnits;
+    const int64_t u_blk = u_begin + flat_block() * kThreads * kAUnits;
+    if (u_blk >= n_units) return;                      // past the folded grid's end
     int64_t u[kAUnits];
     bool full[kAUnits];
 #pragma unroll
@@ -691,7 +693,9 @@ __global__ __launch_bounds__(kThreads) void int_aggregate_kernel(PtrTable packed
 template <int B, bool TABLE>
 __global__ __launch_bounds__(kThreads) void int_aggregate_wide_kernel(PtrTable packed, int P,
                                                                       int32_t* __restrict__ sum,
-                                                                      TableArg tab) {
+                                                                      int64_t n_blocks, TableArg tab) {
+    const int64_t blk = flat_block();
+    if (blk >= n_blocks) return;                       // past the folded grid's end
     constexpr int E = 128 / B;                 // indices per 16 bytes
     constexpr int H = 16 / B;                  // index pairs (s, s + H) per 32-bit word
     constexpr uint32_t LM = (1u << B) - 1u;
@@ -702,7 +706,7 @@ __global__ __launch_bounds__(kThreads) void int_aggregate_wide_kernel(PtrTable p
         for (int z = threadIdx.x; z < tab.n; z += kThreads) tv[z] = tab.t[z];
         __syncthreads();
     }
-    const int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t v = blk * kThreads + threadIdx.x;
     uint32_t acc[TABLE ? E : 4 * H];
 #pragma unroll
     for (int i = 0; i < (TABLE ? E : 4 * H); i++) acc[i] = 0;
@@ -741,7 +745,7 @@ __global__ __launch_bounds__(kThreads) void int_aggregate_wide_kernel(PtrTable p
         }
     }
     __syncthreads();
-    int32_t* out = sum + (int64_t)blockIdx.x * kThreads * E;
+    int32_t* out = sum + blk * kThreads * E;
 #pragma unroll
     for (int r = 0; r < E / 4; r++) {
         const int idx = (r * kThreads + threadIdx.x) * 4;
@@ -903,18 +907,21 @@ __global__ __launch_bounds__(kThreads) void agg_dequant_kernel(PtrTable packed, 
                                                                int L, int pow2, float pf, float recip,
                                                                void* out, const void* xref, double* ws,
                                                                int vec_ok, TableArg tab) {
+    constexpr int64_t kSpanUnits = (int64_t)kThreads * kAUnits;
+    const int64_t n_units = (N + 3) / 4;
+    const int64_t blk = flat_block();
+    if (blk > 0 && blk * kSpanUnits >= n_units) return; // past the folded grid's end (N = 0: one
+                                                        // workgroup writes the zero NMSE partials)
     __shared__ uint32_t tv[TABLE ? 256 : 1];
     __shared__ double sh[kThreads / 64];
     if (TABLE) {
         for (int z = threadIdx.x; z < tab.n; z += kThreads) tv[z] = tab.t[z];
         __syncthreads();
     }
-    constexpr int64_t kSpanUnits = (int64_t)kThreads * kAUnits;
-    const int64_t n_units = (N + 3) / 4;
     const bool uniform = plen % (4 * kSpanUnits) == 0 || plen >= N;   // one grid per span
     double num = 0.0, den = 0.0;
-    for (int64_t u_blk = (int64_t)blockIdx.x * kSpanUnits; u_blk < n_units;
-         u_blk += (int64_t)gridDim.x * kSpanUnits) {
+    for (int64_t u_blk = blk * kSpanUnits; u_blk < n_units;
+         u_blk += (int64_t)gridDim.x * gridDim.z * kSpanUnits) {
         int64_t u[kAUnits];
         bool full[kAUnits];
 #pragma unroll
@@ -1014,15 +1021,10 @@ __global__ __launch_bounds__(kThreads) void agg_dequant_kernel(PtrTable packed, 
     num = block_sum(num, sh);
     den = block_sum(den, sh);
     if (xref && threadIdx.x == 0) {
-        ws[2 * blockIdx.x] = num;
-        ws[2 * blockIdx.x + 1] = den;
+        ws[2 * blk] = num;
+        ws[2 * blk + 1] = den;
     }
 }
-
-unsigned blocks_for(int64_t items, int per_thread) {
-    return (unsigned)ceil_div(items, (int64_t)kThreads * per_thread);
-}
-
 
 }  // namespace
 }  // namespace ga
@@ -1049,7 +1051,7 @@ ga_status minmax_impl(const void* const* bufs, const float* const* errs, int32_t
     int64_t slices = std::max<int64_t>(1, std::min<int64_t>(ceil_div(plen, 4096), ceil_div(4096, n_part)));
     int64_t slice_len = ceil_div(ceil_div(plen, slices), 64) * 64;
     slices = ceil_div(plen, slice_len);
-    if (n_part * slices > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: too many partitions", what);
+    if (!flat_fits(n_part * slices)) return fail(GA_EINVAL, "%s: too many partitions", what);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     uint32_t* keys = reinterpret_cast<uint32_t*>(d_mM);
     PtrTable t{}, te{};
@@ -1061,9 +1063,10 @@ ga_status minmax_impl(const void* const* bufs, const float* const* errs, int32_t
             vec_ok &= aligned(bufs[i], 16) && aligned(errs[i], 16);
         }
     }
-    hipLaunchKernelGGL(minmax_init_kernel, dim3(blocks_for(n_part, 1)), dim3(kThreads), 0, hs, keys, n_part);
+    hipLaunchKernelGGL(minmax_init_kernel, flat_grid(ceil_div(n_part, kThreads)), dim3(kThreads), 0, hs, keys,
+                       n_part);
     if ((rc = check_launch(what))) return rc;
-    const dim3 grid((unsigned)(n_part * slices));
+    const dim3 grid = flat_grid(n_part * slices);
     if (dt == GA_F32 && errs)
         hipLaunchKernelGGL((minmax_kernel<GA_F32, true>), grid, dim3(kThreads), 0, hs, t, te, vec_ok, P, N, plen, (int)slices, slice_len, keys);
     else if (dt == GA_F32)
@@ -1073,7 +1076,8 @@ ga_status minmax_impl(const void* const* bufs, const float* const* errs, int32_t
     else
         hipLaunchKernelGGL((minmax_kernel<GA_BF16, false>), grid, dim3(kThreads), 0, hs, t, te, vec_ok, P, N, plen, (int)slices, slice_len, keys);
     if ((rc = check_launch(what))) return rc;
-    hipLaunchKernelGGL(minmax_final_kernel, dim3(blocks_for(n_part, 1)), dim3(kThreads), 0, hs, keys, n_part);
+    hipLaunchKernelGGL(minmax_final_kernel, flat_grid(ceil_div(n_part, kThreads)), dim3(kThreads), 0, hs, keys,
+                       n_part);
     return check_launch(what);
 }
 
@@ -1121,7 +1125,6 @@ ga_status quantize_impl(const void* const* bufs, int32_t P, int32_t worker0, int
             vec_ok &= aligned(errs[i], 16);
         }
     }
-    if (ceil_div(N, kLSpan) > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: N too large", what);
     // workgroups wholly inside N and inside one partition take a fast kernel:
     // binary32 the lane kernel (2048 elements), bf16 the per-group one
     const int64_t span = dt == GA_F32 ? kLSpan : kFSpan;
@@ -1144,6 +1147,8 @@ ga_status quantize_impl(const void* const* bufs, int32_t P, int32_t worker0, int
         if ((sp & (sp - 1)) == 0) pshift = __builtin_ctzll((unsigned long long)sp);
     }
     const int64_t lane_blocks = ceil_div(fast, lane_spans);
+    if (!(dt == GA_F32 ? flat_fits(lane_blocks) : grid_fits(fast)) || !grid_fits(blocks))
+        return fail(GA_EINVAL, "%s: N too large", what);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
     const TableArg tab = table ? *table : TableArg{};
@@ -1151,7 +1156,7 @@ ga_status quantize_impl(const void* const* bufs, int32_t P, int32_t worker0, int
     do {                                                                                              \
         if (fast > 0 && DT == GA_F32)                                                                 \
             hipLaunchKernelGGL((usq_quantize_lane_kernel<B, TB, EF>),                                 \
-                               dim3((unsigned)lane_blocks, (unsigned)P), dim3(kThreads), lane_lds,    \
+                               flat_grid(lane_blocks, (unsigned)P), dim3(kThreads), lane_lds,         \
                                hs, tx, te, tp, worker0, plen, pshift, fast, lane_spans, d_mM, k0, k1,  \
                                tab);                                                                  \
         else if (fast > 0)                                                                            \
@@ -1210,19 +1215,19 @@ ga_status aggregate_impl(const uint8_t* const* packed, int32_t P, int64_t N, int
     const int64_t wide_blocks = wide_ok ? (N / E) / kThreads : 0;
     const int64_t u_begin = wide_blocks * kThreads * E / 4;
     const int64_t blocks = ceil_div(ceil_div(N, 4) - u_begin, (int64_t)kThreads * kAUnits);
-    if (blocks > 0x7FFFFFFF || wide_blocks > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: N too large", what);
+    if (!flat_fits(blocks) || !flat_fits(wide_blocks)) return fail(GA_EINVAL, "%s: N too large", what);
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    const dim3 grid((unsigned)blocks);
+    const dim3 grid = flat_grid(blocks), wide_grid = flat_grid(wide_blocks);
     const TableArg tab = table ? *table : TableArg{};
 #define GA_A(B)                                                                                       \
     do {                                                                                              \
         if (wide_blocks > 0 && (B == 4 || B == 8)) {                                                  \
             if (table)                                                                                \
-                hipLaunchKernelGGL((int_aggregate_wide_kernel<(B == 4 ? 4 : 8), true>),               \
-                                   dim3((unsigned)wide_blocks), dim3(kThreads), 0, hs, t, P, d_sum, tab); \
+                hipLaunchKernelGGL((int_aggregate_wide_kernel<(B == 4 ? 4 : 8), true>), wide_grid,    \
+                                   dim3(kThreads), 0, hs, t, P, d_sum, wide_blocks, tab);             \
             else                                                                                      \
-                hipLaunchKernelGGL((int_aggregate_wide_kernel<(B == 4 ? 4 : 8), false>),              \
-                                   dim3((unsigned)wide_blocks), dim3(kThreads), 0, hs, t, P, d_sum, tab); \
+                hipLaunchKernelGGL((int_aggregate_wide_kernel<(B == 4 ? 4 : 8), false>), wide_grid,   \
+                                   dim3(kThreads), 0, hs, t, P, d_sum, wide_blocks, tab);             \
         }                                                                                             \
         if (blocks > 0) {                                                                             \
             if (table)                                                                                \
@@ -1255,7 +1260,7 @@ ga_status dequant_impl(const int32_t* d_sum, int64_t N, int32_t P, int32_t level
     const int64_t plen = part_elems > 0 ? part_elems : N;
     const int vec_ok = aligned(d_sum, 16) && aligned(out, 16);
     const int64_t blocks = ceil_div(N, kDSpan);
-    if (blocks > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: N too large", what);
+    if (!grid_fits(blocks)) return fail(GA_EINVAL, "%s: N too large", what);
     const int pow2 = (P & (P - 1)) == 0;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (out_dt == GA_F32)
@@ -1380,7 +1385,7 @@ extern "C" ga_status thc_aggregate_dequant(const uint8_t* const* packed, int32_t
         vec_ok &= aligned(packed[i], 4);
     }
     const int64_t nblk = ad_blocks(N);                  // one workgroup per span
-    if (nblk > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: N too large", what);
+    if (!flat_fits(nblk)) return fail(GA_EINVAL, "%s: N too large", what);
     const int levels = h_table ? g : (1 << b) - 1;
     const int pow2 = (P & (P - 1)) == 0;
     double* ws = static_cast<double*>(d_ws);
@@ -1388,11 +1393,11 @@ extern "C" ga_status thc_aggregate_dequant(const uint8_t* const* packed, int32_t
 #define GA_AD(B, TB)                                                                                  \
     do {                                                                                              \
         if (out_dt == GA_F32)                                                                         \
-            hipLaunchKernelGGL((agg_dequant_kernel<B, TB, GA_F32>), dim3((unsigned)nblk), dim3(kThreads), 0, hs, \
+            hipLaunchKernelGGL((agg_dequant_kernel<B, TB, GA_F32>), flat_grid(nblk), dim3(kThreads), 0, hs, \
                                t, P, N, nbytes, d_sum, plen, d_mM, levels, pow2, (float)P, 1.0f / (float)P, \
                                out, x_ref, ws, vec_ok, tab);                                          \
         else                                                                                          \
-            hipLaunchKernelGGL((agg_dequant_kernel<B, TB, GA_BF16>), dim3((unsigned)nblk), dim3(kThreads), 0, hs, \
+            hipLaunchKernelGGL((agg_dequant_kernel<B, TB, GA_BF16>), flat_grid(nblk), dim3(kThreads), 0, hs, \
                                t, P, N, nbytes, d_sum, plen, d_mM, levels, pow2, (float)P, 1.0f / (float)P, \
                                out, x_ref, ws, vec_ok, tab);                                          \
     } while (0)
@@ -1444,7 +1449,7 @@ ga_status nmse_check(const void* x, const void* xhat, int64_t N, ga_dtype dt, do
     if (!d_out || !aligned(d_out, 8)) return fail(GA_EINVAL, "%s: null or misaligned output", what);
     if (N > 0 && (!x || !xhat || !aligned(x, elem_size(dt)) || !aligned(xhat, elem_size(dt))))
         return fail(GA_EINVAL, "%s: null or misaligned input", what);
-    if (nmse_blocks(N, dt == GA_F32 ? 4 : 8) > 0x7FFFFFFF) return fail(GA_EINVAL, "%s: N too large", what);
+    if (!grid_fits(nmse_blocks(N, dt == GA_F32 ? 4 : 8))) return fail(GA_EINVAL, "%s: N too large", what);
     return GA_OK;
 }
 
