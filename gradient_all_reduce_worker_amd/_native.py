@@ -30,7 +30,7 @@ EXPORTS = (
     "ga_fusion_ring_plan", "ga_fusion_ring_allreduce", "thc_ef_minmax", "thc_ef_quantize",
     "thc_rht_quantize", "thc_aggregate_dequant", "thc_aggregate_dequant_ws_bytes",
     "thc_rht_norm_quantize", "thc_rht_norm_quantize_ws_bytes", "thc_ring_step",
-    "thc_ring_step_ws_bytes",
+    "thc_ring_step_ws_bytes", "ga_ring_stage_bytes", "ga_ring_stepwise_staged",
 )
 
 
@@ -74,6 +74,10 @@ def load() -> C.CDLL:
     L.ga_fuse_unpack.argtypes = [vp, i64, i64, i32, vp]
     L.ga_ring_allreduce_sim.argtypes = [C.POINTER(vp), i32, i64, i32, i32, i64, i32,
                                         C.POINTER(RingStats), vp]
+    L.ga_ring_stage_bytes.argtypes = [i32, i64]
+    L.ga_ring_stage_bytes.restype = C.c_size_t
+    L.ga_ring_stepwise_staged.argtypes = [C.POINTER(vp), i32, i64, i32, i32, i64, vp, C.c_size_t,
+                                          C.POINTER(RingStats), vp]
     L.thc_minmax.argtypes = [C.POINTER(vp), i32, i64, i32, i64, vp, vp]
     L.thc_usq_quantize.argtypes = [C.POINTER(vp), i32, i32, i64, i32, i64, vp, i32, u64,
                                    C.POINTER(vp), vp]
@@ -115,9 +119,8 @@ def load() -> C.CDLL:
     L.thc_aggregate_dequant_ws_bytes.restype = C.c_size_t
     L.ga_last_error.argtypes = []
     L.ga_last_error.restype = C.c_char_p
-    for name in EXPORTS:
-        if name not in ("thc_nmse_ws_bytes", "ga_last_error", "thc_aggregate_dequant_ws_bytes",
-                        "thc_rht_norm_quantize_ws_bytes", "thc_ring_step_ws_bytes"):
+    for name in EXPORTS:                 # every other call returns a ga_status
+        if not name.endswith("_bytes") and name != "ga_last_error":
             getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -256,6 +259,35 @@ def ga_ring_allreduce_sim(bufs: Sequence[torch.Tensor], op: int = AVG, part_elem
     st = RingStats()
     _check(L.ga_ring_allreduce_sim(_ptr_array(bufs, "buffer"), P, N, dt, op, part_elems, mode,
                                    C.byref(st), _stream(stream)))
+    return {"steps": st.steps, "bytes_sent_per_worker": st.bytes_sent_per_worker,
+            "hbm_bytes": st.hbm_bytes, "launches": st.launches}
+
+
+def ga_ring_stage_bytes(P: int, N: int) -> int:
+    return int(load().ga_ring_stage_bytes(P, N))
+
+
+def ga_ring_stepwise_staged(bufs: Sequence[torch.Tensor], op: int = AVG, part_elems: int = 0,
+                            stage: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """The ring schedule one step per launch, partials in a binary32 stage
+    (allocated here when not given)."""
+    L = load()
+    P = len(bufs)
+    if P == 0:
+        raise ValueError("no buffers")
+    N = bufs[0].numel()
+    dt = _dt(bufs[0])
+    for b in bufs:
+        if b.numel() != N or _dt(b) != dt:
+            raise ValueError("all worker buffers need the same size and dtype")
+    need = ga_ring_stage_bytes(P, N)
+    if stage is None and need > 0:
+        stage = torch.empty(need // 4, dtype=torch.float32, device=bufs[0].device)
+    st = RingStats()
+    _check(L.ga_ring_stepwise_staged(_ptr_array(bufs, "buffer"), P, N, dt, op, part_elems,
+                                     _dev(stage, "stage") if stage is not None else None,
+                                     stage.numel() * stage.element_size() if stage is not None else 0,
+                                     C.byref(st), _stream(stream)))
     return {"steps": st.steps, "bytes_sent_per_worker": st.bytes_sent_per_worker,
             "hbm_bytes": st.hbm_bytes, "launches": st.launches}
 

@@ -427,6 +427,107 @@ __global__ __launch_bounds__(kThreads) void ring_step_elem_kernel(PtrTable bufs,
         step_one(bufs, P, N, plen, e, st, div);
 }
 
+// ---------------------------------------------------------------- staged stepwise
+
+// The stepwise schedule with the partials on a binary32 wire: at scatter-
+// reduce step s every element e (chunk c) has exactly one partial in flight,
+// from worker c + s to worker c + s + 1, so one binary32 array stage[N]
+// holds all of them. The receiver adds its own value to the partial (at the
+// first step the sender's own value, read from its buffer) and writes the
+// stage; at the last step it divides (op = avg) and stores the finished
+// value, rounded once, into its own buffer. All-gather steps copy the
+// finished chunk between worker buffers in the buffers' own type. The fold
+// order and the roundings are those of the fused fold.
+struct Staged {
+    int s;
+    int rs;          // 1: scatter-reduce step, 0: all-gather step
+    int first;      // scatter-reduce step 0: the partial comes from the sender's buffer
+    int last;       // scatter-reduce step P - 2: the finished value goes to the receiver's buffer
+};
+
+template <ga_dtype DT>
+__device__ __forceinline__ void staged_one(const PtrTable& bufs, float* stage, int P, int64_t N,
+                                           int64_t plen, int64_t e, Staged st, Div div) {
+    using E = Elem<DT>;
+    int d, s;
+    step_workers(locate(e, N, plen, P).chunk, P, Step{st.s, st.rs, 0}, &d, &s);
+    if (!st.rs) {                                    // all-gather: the bits as they are
+        if (DT == GA_F32) static_cast<uint32_t*>(bufs.p[d])[e] = static_cast<const uint32_t*>(bufs.p[s])[e];
+        else static_cast<uint16_t*>(bufs.p[d])[e] = static_cast<const uint16_t*>(bufs.p[s])[e];
+        return;
+    }
+    const float a = st.first ? E::load1(bufs.p[s], e) : stage[e];
+    float x = a + E::load1(bufs.p[d], e);
+    if (st.last) {
+        if (div.avg) x = div.apply(x);
+        E::store1(bufs.p[d], e, x);
+    } else {
+        stage[e] = x;
+    }
+}
+
+// One 16-byte vector of the buffers' type per thread (4 binary32 or 8 bf16
+// elements; the stage holds them in one or two 16-byte vectors); a
+// workgroup whose vectors lie in more than one chunk goes element by element.
+template <ga_dtype DT>
+__global__ __launch_bounds__(kThreads) void ring_staged_vec_kernel(PtrTable bufs, float* __restrict__ stage,
+                                                                   int P, int64_t N, int64_t plen,
+                                                                   int64_t n_vec, Staged st, Div div) {
+    using E = Elem<DT>;
+    constexpr int V = E::kVec;
+    const int64_t vb0 = flat_block() * kThreads;
+    if (vb0 >= n_vec) return;                              // past the folded grid's end
+    const int64_t vb1 = min(vb0 + (int64_t)kThreads, n_vec);
+    const Where first = locate(vb0 * V, N, plen, P);
+    const Where last = locate(vb1 * V - 1, N, plen, P);
+    if (first.part != last.part || first.chunk != last.chunk) {
+        for (int64_t e = vb0 * V + threadIdx.x; e < vb1 * V; e += kThreads)
+            staged_one<DT>(bufs, stage, P, N, plen, e, st, div);
+        return;
+    }
+    const int64_t v = vb0 + threadIdx.x;
+    if (v >= vb1) return;
+    int d, s;
+    step_workers(first.chunk, P, Step{st.s, st.rs, 0}, &d, &s);
+    uint4* dst = static_cast<uint4*>(bufs.p[d]);
+    if (!st.rs) {
+        dst[v] = static_cast<const uint4*>(bufs.p[s])[v];
+        return;
+    }
+    constexpr int K = V / 4;                               // stage vectors per buffer vector
+    uint4* sv = reinterpret_cast<uint4*>(stage) + K * v;
+    float a[V], x[V];
+    if (st.first) {
+        E::widen(static_cast<const uint4*>(bufs.p[s])[v], a);
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; k++) Elem<GA_F32>::widen(sv[k], a + 4 * k);
+    }
+    E::widen(dst[v], x);
+#pragma unroll
+    for (int i = 0; i < V; i++) x[i] = a[i] + x[i];
+    if (st.last) {
+        if (div.avg) {
+#pragma unroll
+            for (int i = 0; i < V; i++) x[i] = div.apply(x[i]);
+        }
+        dst[v] = E::narrow(x);
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; k++) sv[k] = Elem<GA_F32>::narrow(x + 4 * k);
+    }
+}
+
+template <ga_dtype DT>
+__global__ __launch_bounds__(kThreads) void ring_staged_elem_kernel(PtrTable bufs, float* __restrict__ stage,
+                                                                    int P, int64_t N, int64_t plen,
+                                                                    int64_t e_begin, int64_t e_end,
+                                                                    Staged st, Div div) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t e = e_begin + (int64_t)blockIdx.x * kThreads + threadIdx.x; e < e_end; e += stride)
+        staged_one<DT>(bufs, stage, P, N, plen, e, st, div);
+}
+
 int elem_grid(int64_t count) {
     int64_t b = ceil_div(count, kThreads);
     return (int)(b < 65536 ? (b < 1 ? 1 : b) : 65536);
@@ -609,6 +710,99 @@ extern "C" ga_status ga_ring_allreduce_sim(void* const* bufs, int32_t P, int64_t
                         if ((rc = check_launch(what))) return rc;
                     }
                 }
+            }
+        }
+    }
+    s.launches = launches;
+    if (st) *st = s;
+    return GA_OK;
+}
+
+extern "C" size_t ga_ring_stage_bytes(int32_t P, int64_t N) {
+    return (P > 2 && N > 0) ? (size_t)N * sizeof(float) : 0;
+}
+
+extern "C" ga_status ga_ring_stepwise_staged(void* const* bufs, int32_t P, int64_t N, ga_dtype dt, ga_op op,
+                                             int64_t part_elems, float* d_stage, size_t stage_bytes,
+                                             ga_ring_stats* st, void* stream) {
+    const char* what = "ga_ring_stepwise_staged";
+    if (!valid_dtype(dt)) return fail(GA_EINVAL, "%s: unknown dtype %d", what, (int)dt);
+    if (op != GA_SUM && op != GA_AVG) return fail(GA_EINVAL, "%s: unknown op %d", what, (int)op);
+    if (N < 0 || part_elems < 0) return fail(GA_EINVAL, "%s: negative size", what);
+    if (P < 1 || P > GA_MAX_WORKERS)
+        return fail(GA_EINVAL, "%s: P = %d outside [1, %d]", what, P, GA_MAX_WORKERS);
+    if (N == 0) {
+        if (st) *st = ga_ring_stats{0, 0, 0, 0};
+        return GA_OK;
+    }
+    const int64_t es = (int64_t)elem_size(dt);
+    ga_status rc = check_workers(bufs, P, (size_t)es, what);
+    if (rc) return rc;
+    if (!disjoint(bufs, P, N * es)) return fail(GA_EINVAL, "%s: worker buffers overlap", what);
+    const size_t need = ga_ring_stage_bytes(P, N);
+    if (need > 0) {
+        if (!d_stage || !aligned(d_stage, 16))
+            return fail(GA_EINVAL, "%s: null or misaligned stage (16 bytes)", what);
+        if (stage_bytes < need)
+            return fail(GA_EINVAL, "%s: stage of %zu bytes, need %zu", what, stage_bytes, need);
+        const uintptr_t a = (uintptr_t)d_stage;
+        for (int i = 0; i < P; i++) {
+            const uintptr_t b = (uintptr_t)bufs[i];
+            if (a < b + (uintptr_t)(N * es) && b < a + need)
+                return fail(GA_EINVAL, "%s: stage overlaps worker %d", what, i);
+        }
+    }
+    const int64_t plen = part_elems > 0 ? part_elems : N;
+    ga_ring_stats s{};
+    {
+        // scatter-reduce partials travel in binary32, the all-gather in the
+        // buffers' type
+        auto part_bytes = [&](int64_t n) { return (int64_t)(P - 1) * ceil_div(n, P) * (4 + es); };
+        s.steps = 2 * (int64_t)(P - 1);
+        s.bytes_sent_per_worker = (N / plen) * part_bytes(plen) + (N % plen ? part_bytes(N % plen) : 0);
+        // step 0 reads two buffers and writes the stage, the middle steps read
+        // the stage and a buffer and write the stage, the last reads the
+        // stage and a buffer and writes a buffer (P = 2: two buffers in, one
+        // out); every all-gather step copies N elements
+        const int64_t rs = P == 1 ? 0
+                         : P == 2 ? 3 * es * N
+                                  : (2 * es + 4) * N + (int64_t)(P - 3) * (8 + es) * N + (4 + 2 * es) * N;
+        s.hbm_bytes = rs + (int64_t)(P - 1) * 2 * es * N;
+    }
+    const int V = dt == GA_F32 ? 4 : 8;
+    bool vec_ok = true;
+    for (int i = 0; i < P; i++) vec_ok = vec_ok && aligned(bufs[i], 16);
+    const int64_t n_vec = vec_ok ? N / V : 0;
+    const int64_t vblocks = ceil_div(n_vec, kThreads);
+    if (!flat_fits(vblocks)) return fail(GA_EINVAL, "%s: N too large", what);
+    const int64_t e0 = n_vec * V;
+    PtrTable t{};
+    for (int i = 0; i < P; i++) t.p[i] = bufs[i];
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const Div div{op == GA_AVG, (P & (P - 1)) == 0, (float)P, 1.0f / (float)P};
+    int64_t launches = 0;
+    for (int phase = 0; phase < 2 && P > 1; phase++) {
+        for (int step = 0; step < P - 1; step++) {
+            const Staged sp{step, phase == 0, phase == 0 && step == 0, phase == 0 && step == P - 2};
+            if (n_vec > 0) {
+                if (dt == GA_F32)
+                    hipLaunchKernelGGL(ring_staged_vec_kernel<GA_F32>, flat_grid(vblocks), dim3(kThreads), 0, hs,
+                                       t, d_stage, P, N, plen, n_vec, sp, div);
+                else
+                    hipLaunchKernelGGL(ring_staged_vec_kernel<GA_BF16>, flat_grid(vblocks), dim3(kThreads), 0, hs,
+                                       t, d_stage, P, N, plen, n_vec, sp, div);
+                launches++;
+                if ((rc = check_launch(what))) return rc;
+            }
+            if (e0 < N) {
+                if (dt == GA_F32)
+                    hipLaunchKernelGGL(ring_staged_elem_kernel<GA_F32>, dim3(elem_grid(N - e0)), dim3(kThreads), 0,
+                                       hs, t, d_stage, P, N, plen, e0, N, sp, div);
+                else
+                    hipLaunchKernelGGL(ring_staged_elem_kernel<GA_BF16>, dim3(elem_grid(N - e0)), dim3(kThreads), 0,
+                                       hs, t, d_stage, P, N, plen, e0, N, sp, div);
+                launches++;
+                if ((rc = check_launch(what))) return rc;
             }
         }
     }

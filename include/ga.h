@@ -6,6 +6,8 @@
  *   ga_fuse_plan / ga_fuse_pack / ga_fuse_unpack   Tensor Fusion
  *   ga_ring_allreduce_sim                          ring all-reduce (sum | avg;
  *                                                  single or bidirectional)
+ *   ga_ring_stepwise_staged                        its schedule step by step,
+ *                                                  partials on a binary32 wire
  *   ga_fusion_ring_plan / ga_fusion_ring_allreduce zero-copy fusion ring
  *   thc_minmax / thc_usq_quantize / thc_int_aggregate / thc_dequant / thc_nmse
  *   thc_nmse_noalloc (thc_nmse without a workspace, for callers that
@@ -177,7 +179,8 @@ typedef struct {
  *               GA_RING_STEPWISE: one launch per communication step,
  *               2 (P - 1) launches moving the chunks as the schedule does
  *               (5 (P - 1) N elem_bytes); GA_F32 only (bf16 partials need
- *               binary32 storage on the wire) -> GA_ENOTSUP for GA_BF16.
+ *               binary32 storage on the wire) -> GA_ENOTSUP for GA_BF16;
+ *               ga_ring_stepwise_staged runs the schedule for either type.
  *               GA_RING_DUAL: the bidirectional ring of [RING] section 11
  *               (Exercise 1), executed like GA_RING_FUSED: each partition
  *               is cut into 2P sub-chunks of C2 = ceil(n / 2P); sub-chunk c
@@ -191,6 +194,34 @@ typedef struct {
 ga_status ga_ring_allreduce_sim(void* const* bufs, int32_t P, int64_t N, ga_dtype dt, ga_op op,
                                 int64_t part_elems, ga_ring_mode mode, ga_ring_stats* st,
                                 void* stream);
+
+/*
+ * ga_ring_stepwise_staged -- the same schedule one communication step per
+ * launch ([RING] sections 4 and 7; [HVD] 3.4), with the partial sums on a
+ * binary32 wire: at scatter-reduce step s every element of chunk c has
+ * exactly one partial in flight, from worker (c + s) mod P to (c + s + 1)
+ * mod P, so one binary32 array of N elements (the stage) holds them all.
+ * Step 0 adds the receiver's value to the sender's own, the middle steps
+ * add it to the staged partial, the last step (s = P - 2) divides by P
+ * (op = GA_AVG) and stores the finished value, rounded once to dt, into the
+ * owner's buffer; the P - 1 all-gather steps copy the finished chunk on in
+ * dt. Results are bit-identical to ga_ring_allreduce_sim (GA_RING_FUSED),
+ * for GA_F32 and GA_BF16: the same fold order and roundings.
+ *   bufs, P, N, dt, op, part_elems   as ga_ring_allreduce_sim
+ *   d_stage      device, at least ga_ring_stage_bytes(P, N) bytes (4 N when
+ *                P > 2, else none: may be null), 16-byte aligned, disjoint
+ *                from every buffer; caller-owned, contents on return
+ *                unspecified
+ *   st           optional accounting: bytes_sent_per_worker counts the
+ *                scatter-reduce partials as binary32 and the all-gather
+ *                chunks in dt; hbm_bytes the steps' reads and writes
+ * Errors (nothing enqueued): GA_EINVAL for a bad dtype, op, size, P,
+ * pointer, overlap or a stage that is too small.
+ */
+size_t ga_ring_stage_bytes(int32_t P, int64_t N);
+ga_status ga_ring_stepwise_staged(void* const* bufs, int32_t P, int64_t N, ga_dtype dt, ga_op op,
+                                  int64_t part_elems, float* d_stage, size_t stage_bytes,
+                                  ga_ring_stats* st, void* stream);
 
 /* ------------------------------------------------------------------ */
 /* Zero-copy Tensor Fusion ring  ([HVD] 3.4: Tensor Fusion + ring)      */

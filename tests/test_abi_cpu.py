@@ -27,7 +27,7 @@ def _declared():
 def test_header_declarations_are_exported():
     L = nat.load()
     names = _declared()
-    assert len(names) == 31
+    assert len(names) == 33
     assert set(names) == set(nat.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -144,6 +144,35 @@ def test_center_tables_are_valid():
             assert T[0] == 0 and T[-1] == g and len(T) == 1 << b
             assert all(T[i] < T[i + 1] for i in range(len(T) - 1))
     assert nat.center_table(2, 3) == [0, 1, 2, 3]
+
+
+def test_staged_stepwise_errors_before_enqueue():
+    """The staged schedule checks its stage (size, alignment, overlap with
+    a worker) before anything is enqueued; P <= 2 needs none."""
+    L = nat.load()
+    good = _ptrs([0x100000 * (i + 1) for i in range(4)])
+    st = nat.RingStats()
+    call = L.ga_ring_stepwise_staged
+    N = 1000
+    assert nat.ga_ring_stage_bytes(4, N) == 4 * N
+    assert nat.ga_ring_stage_bytes(2, N) == 0 and nat.ga_ring_stage_bytes(1, N) == 0
+    assert nat.ga_ring_stage_bytes(4, 0) == 0
+    assert nat.ga_ring_stage_bytes(8, 1 << 31) == 1 << 33                        # size_t, not int
+    stage = 0x900000
+    assert call(good, 4, N, 1, 1, 0, None, 0, None, None) == EINVAL                 # no stage
+    assert call(good, 4, N, 1, 1, 0, stage, 4 * N - 4, None, None) == EINVAL        # too small
+    assert b"need 4000" in L.ga_last_error()
+    assert call(good, 4, N, 1, 1, 0, stage + 4, 4 * N, None, None) == EINVAL        # misaligned
+    assert call(good, 4, N, 1, 1, 0, 0x200000 + 256, 4 * N, None, None) == EINVAL   # overlaps worker 1
+    assert b"overlaps worker 1" in L.ga_last_error()
+    assert call(good, 4, N, 3, 1, 0, stage, 4 * N, None, None) == EINVAL            # dtype
+    assert call(good, 4, N, 1, 5, 0, stage, 4 * N, None, None) == EINVAL            # op
+    assert call(good, 0, N, 1, 1, 0, stage, 4 * N, None, None) == EINVAL            # P
+    assert call(_ptrs([0x100000, 0x100010, 0x300000, 0x400000]), 4, N, 1, 1, 0, stage, 4 * N,
+                None, None) == EINVAL                                                 # buffers overlap
+    # empty input: a no-op that reports zero accounting
+    assert call(good, 4, 0, 1, 1, 0, None, 0, C.byref(st), None) == 0
+    assert st.steps == 0 and st.launches == 0
 
 
 def test_nuhc_table_errors_before_enqueue():

@@ -90,6 +90,54 @@ def test_ring_stepwise(P, N, part, op):
 
 
 @pytest.mark.parametrize("dt", [ga.F32, ga.BF16])
+@pytest.mark.parametrize("op", [ga.SUM, ga.AVG])
+@pytest.mark.parametrize("P,N,part", [s for s in RING_SHAPES if s[1] <= 1 << 17])
+def test_ring_stepwise_staged(P, N, part, dt, op):
+    """The schedule step by step with binary32 partials in the stage: the
+    oracle's stepwise schedule (binary32 working copies), bit for bit; the
+    stage starts out holding NaNs, which no result may see."""
+    bufs = _inputs(P, N, dt, seed=P * 37 + N + 2)
+    ref = [_host(b) for b in bufs]
+    need = ga.ga_ring_stage_bytes(P, N)
+    stage = torch.full((max(need // 4, 1),), float("nan"), device=DEV)
+    st = ga.ga_ring_stepwise_staged(bufs, op=op, part_elems=part, stage=stage if need else None)
+    oracle.ring_stepwise(ref, op=op, part=part)
+    for i in range(P):
+        assert np.array_equal(_bits(bufs[i]), ref[i].view(np.uint32 if dt == ga.F32 else np.uint16)), i
+    es = 4 if dt == ga.F32 else 2
+    plen = part or max(N, 1)
+    if N and P > 1:
+        assert st["steps"] == 2 * (P - 1)
+        assert st["bytes_sent_per_worker"] == sum((P - 1) * -(-min(plen, N - p0) // P) * (4 + es)
+                                                  for p0 in range(0, N, plen))
+        rs = 3 * es * N if P == 2 else (2 * es + 4) * N + (P - 3) * (8 + es) * N + (4 + 2 * es) * N
+        assert st["hbm_bytes"] == rs + (P - 1) * 2 * es * N
+
+
+@pytest.mark.parametrize("dt", [ga.F32, ga.BF16])
+def test_ring_stepwise_staged_views_and_guards(dt):
+    """Views one element past a 16-byte boundary take the element kernel;
+    the stage's bytes beyond 4 N and the memory around every worker keep
+    their values; the result equals the oracle's fold and the fused ring's."""
+    P, N, guard = 5, 3001, 64
+    big = _inputs(P, N + 1 + 2 * guard, dt, seed=98)
+    lo, hi = guard + 1, guard + 1 + N
+    views = [b[lo:hi] for b in big]
+    ref = [_host(v) for v in views]
+    outside = [torch.cat([b[:lo], b[hi:]]) for b in big]
+    fused = [v.clone() for v in views]
+    stage = torch.full((N + guard,), 7.25, device=DEV)
+    ga.ga_ring_stepwise_staged(views, op=ga.AVG, part_elems=1000, stage=stage)
+    ga.ga_ring_allreduce_sim(fused, op=ga.AVG, part_elems=1000)
+    oracle.ring_fold(ref, op=ga.AVG, part=1000)
+    assert torch.all(stage[N:] == 7.25)
+    for i in range(P):
+        assert np.array_equal(_bits(views[i]), ref[i].view(np.uint32 if dt == ga.F32 else np.uint16)), i
+        assert np.array_equal(_bits(views[i]), _bits(fused[i])), i
+        assert torch.equal(torch.cat([big[i][:lo], big[i][hi:]]), outside[i]), i
+
+
+@pytest.mark.parametrize("dt", [ga.F32, ga.BF16])
 def test_ring_misaligned_buffers(dt):
     """Views that start one element past a 16-byte boundary take the
     per-element path; results are the same bits."""

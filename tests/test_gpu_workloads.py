@@ -279,3 +279,29 @@ def test_fused_workload_full(name, zero_copy):
         for t in range(len(w.sizes)):
             got = synth.to_numpy_bits(pipe.tensors[i][t])
             assert np.array_equal(got.view(np.uint32), out[t].view(np.uint32)), (i, t)
+
+
+def test_shard_stepwise_staged():
+    """The shard's shape (8 x 2^31 bf16, partitions of 2^20) through the
+    stepwise schedule with binary32 partials staged between steps: all
+    workers bitwise equal, and 16 evenly spaced partitions against the
+    oracle's fold element by element."""
+    P, N, part = 8, 1 << 31, 1 << 20
+    print(f"staged stepwise P={P} N={N} bf16 part={part}", flush=True)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(21)
+    bufs = [torch.randn(N, generator=g, device="cuda", dtype=torch.bfloat16) * (2.0 ** (i - 4))
+            for i in range(P)]
+    which = _sampled(N // part)
+    before = {p: [x[p * part:(p + 1) * part].cpu().view(torch.int16).numpy().view(np.uint16).copy()
+                  for x in bufs] for p in which}
+    st = ga.ga_ring_stepwise_staged(bufs, op=ga.AVG, part_elems=part)
+    torch.cuda.synchronize()
+    assert st["launches"] == 2 * (P - 1)
+    for i in range(1, P):
+        assert torch.equal(bufs[i].view(torch.int16), bufs[0].view(torch.int16)), i
+    for p in which:
+        ref = before[p]
+        oracle.ring_fold(ref, op=oracle.AVG, part=part)
+        got = bufs[0][p * part:(p + 1) * part].cpu().view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got, ref[0]), p
