@@ -254,8 +254,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-fusion", action="store_true",
                     help="fused workloads: pack -> ring -> unpack instead of the zero-copy ring")
-    ap.add_argument("--ring-mode", default="fused", choices=["fused", "dual"],
-                    help="single ring or the bidirectional dual ring fold order")
+    ap.add_argument("--ring-mode", default="fused", choices=["fused", "dual", "staged"],
+                    help="single ring, the bidirectional dual ring fold order, or the single "
+                         "ring's schedule one launch per step with binary32 partials staged "
+                         "(flat workloads; implies --separate-step)")
     ap.add_argument("--separate-tail", action="store_true",
                     help="THC passes: integer sum, dequant and NMSE as three calls, not one")
     ap.add_argument("--separate-step", action="store_true",
@@ -273,7 +275,7 @@ def main():
     import torch
 
     import gradient_all_reduce_worker_amd as ga
-    from gradient_all_reduce_worker_amd.pipeline import Pipeline, StageTimer
+    from gradient_all_reduce_worker_amd.pipeline import RING_STAGED, Pipeline, StageTimer
 
     ga.load()                       # fails loudly without the HIP library
     if not torch.cuda.is_available():
@@ -281,7 +283,8 @@ def main():
         sys.exit(1)
 
     pipe = Pipeline(args.workload, zero_copy=not args.copy_fusion, fused_tail=not args.separate_tail,
-                    ring_mode=ga.RING_DUAL if args.ring_mode == "dual" else ga.RING_FUSED,
+                    ring_mode={"dual": ga.RING_DUAL, "staged": RING_STAGED}.get(args.ring_mode,
+                                                                              ga.RING_FUSED),
                     fused_step=not args.separate_step)
     t0 = time.perf_counter()
     pipe.setup()
@@ -347,17 +350,22 @@ def main():
         ring_key, kernel = step_keys[0], "thc_ring_kernel"
     elif "ring_allreduce" in stage_ms:
         ring_key, kernel = "ring_allreduce", "ring_fused_vec_kernel"
+    elif "ring_staged" in stage_ms:
+        ring_key, kernel = "ring_staged", "ring_staged_vec_kernel"
     else:
         ring_key, kernel = "fusion_ring", "fusion_ring_kernel"
     ring_ms = stage_ms[ring_key]
     achieved = nbytes[ring_key] / (ring_ms * 1e-3) / 1e9
+    # the staged schedule is 2 (P - 1) launches per call: the rate is their
+    # mean, bytes per launch their mean too
+    per_launch = nbytes[ring_key] / (2 * (P - 1) if ring_key == "ring_staged" else 1)
     # the copy path runs one ring launch per fusion buffer: its summary would
     # be per buffer, so only single-launch rings carry traffic
     one_launch = calls[ring_key] // args.steps == 1
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profile(args.workload, kernel) if one_launch else None,
-                "kernel": kernel, "alg_bytes_per_launch": nbytes[ring_key]}
+                "kernel": kernel, "alg_bytes_per_launch": per_launch}
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,

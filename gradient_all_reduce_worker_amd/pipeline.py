@@ -41,6 +41,11 @@ import torch
 from . import _native as ga
 from . import synth
 
+# ring_mode value (beside ga.RING_FUSED and ga.RING_DUAL) selecting
+# ga_ring_stepwise_staged: the schedule one launch per step, binary32
+# partials staged between steps (flat workloads)
+RING_STAGED = "staged"
+
 
 class StageTimer:
     """Events around every library call of a step, per stage name."""
@@ -113,6 +118,8 @@ class Pipeline:
         # leaves every 16-byte access instruction covering every other half
         # of the wave's lines.
         w = self.w
+        if ring_mode == RING_STAGED and w.fused:
+            raise ValueError("the staged stepwise schedule runs on flat workloads")
         self.fused_step = (fused_step and not w.fused and bool(w.thc_bits) and w.N % 8 == 0
                            and w.part_elems % 8 == 0 and ring_mode == ga.RING_FUSED and w.P <= 16)
         # THC's integer sum, dequant and NMSE in one pass (thc_aggregate_dequant)
@@ -223,6 +230,9 @@ class Pipeline:
             self.ws_step = torch.empty(ga.thc_ring_step_ws_bytes(self.N), dtype=torch.uint8, device=dev)
             self.ws_ad = torch.empty(ga.thc_aggregate_dequant_ws_bytes(self.N), dtype=torch.uint8,
                                      device=dev)
+            if self.ring_mode == RING_STAGED:
+                self.stage = torch.empty(max(ga.ga_ring_stage_bytes(self.P, self.N) // 4, 1),
+                                         dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
 
     # ------------------------------------------------------------ step
@@ -273,6 +283,9 @@ class Pipeline:
             _call(timer, f"thc_ring_step_b{b0}", ga.thc_ring_step, self.flat, self.mM, b0, w.quant_seed,
                   w.ring_part_elems, part, 0, self.packed[b0], True, self.S[b0], True, self.xhat[b0],
                   self.nmse[b0], self.ws_step)
+        elif self.ring_mode == RING_STAGED:
+            _call(timer, "ring_staged", ga.ga_ring_stepwise_staged, self.flat, ga.AVG,
+                  w.ring_part_elems, self.stage)
         else:
             _call(timer, "ring_allreduce", ga.ga_ring_allreduce_sim, self.flat, ga.AVG,
                   w.ring_part_elems, self.ring_mode)
@@ -339,6 +352,13 @@ class Pipeline:
             return out
         out["thc_minmax"] = 1.0 * P * N * s
         out["ring_allreduce"] = 2.0 * P * N * s
+        # the staged schedule, all 2 (P - 1) launches: step 0 reads two
+        # buffers and writes the binary32 stage, the middle steps read the
+        # stage and a buffer and write the stage, the last reads the stage
+        # and a buffer and writes a buffer; each all-gather step copies N
+        rs = (3 * s * N if P == 2 else
+              (2 * s + 4) * N + (P - 3) * (8 + s) * N + (4 + 2 * s) * N) if P > 1 else 0
+        out["ring_staged"] = float(rs + (P - 1) * 2 * s * N)
         for b in w.thc_bits:
             # gradients read once and the average written back, the indices,
             # the sums and the estimate written
