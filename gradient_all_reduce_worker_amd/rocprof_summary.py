@@ -16,6 +16,11 @@
       --fetch DIR1 --write DIR2 --probe REGEX --probe-bytes B --cmd "..." \
       NAME=REGEX=ALG_BYTES ...
       The same scaling for several kernels, as a markdown table.
+
+  python -m gradient_all_reduce_worker_amd.rocprof_summary counters \
+      --dir DIR [--dir DIR2 ...] --cmd "..." NAME=REGEX=UNITS[=LAUNCHES] ...
+      Every counter of the runs (e.g. SQ instruction counts), per call of
+      each kernel and per unit of work (UNITS per call).
 """
 import argparse
 import csv
@@ -144,6 +149,40 @@ def cmd_pmc_table(a):
               f"{(fb + wb) / float(alg):.4f} |")
 
 
+def cmd_counters(a):
+    """Markdown table: per kernel, every counter of the runs under DIRs,
+    summed over a call's launches and averaged over calls, and divided by
+    the call's units (NAME=REGEX=UNITS[=LAUNCHES]: e.g. UNITS = coordinates
+    a call processes, LAUNCHES = launches per call, default 1)."""
+    per = defaultdict(lambda: defaultdict(float))      # (kernel, dispatch) -> counter -> value
+    names = {}
+    for d in a.dir:
+        for r in _rows(d, "counter_collection.csv"):
+            key = (d, r["kernel_name"], r.get("dispatch_id", r.get("correlation_id", "")))
+            per[key][r["counter_name"].strip()] += float(r["counter_value"])
+            names[r["counter_name"].strip()] = True
+    counters = sorted(names)
+    print(f"# rocprofv3 counters per call: {a.title}\n")
+    print(f"Commands (run from the repository root on one MI355X):\n\n    {a.cmd}\n")
+    print("Each counter is summed over a call's launches and averaged over the calls; "
+          "the second figure divides it by the units the call processes.\n")
+    print("| kernel | units per call | " + " | ".join(counters) + " |")
+    print("|---|---:|" + "---:|" * len(counters))
+    for spec in a.kernels:
+        parts = spec.split("=")
+        name, rx, units = parts[0], re.compile(parts[1]), float(parts[2])
+        per_call = int(parts[3]) if len(parts) > 3 else 1
+        cells = []
+        for c in counters:
+            vals = [v[c] for (d, k, _), v in per.items() if rx.search(k) and c in v]
+            if not vals:
+                cells.append("—")
+                continue
+            call = sum(vals) / (len(vals) / per_call)
+            cells.append(f"{call:.4g} ({call / units:.3g})")
+        print(f"| `{name}` | {units:.4g} | " + " | ".join(cells) + " |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -169,8 +208,14 @@ def main():
     t.add_argument("--title", default="")
     t.add_argument("--cmd", required=True)
     t.add_argument("kernels", nargs="+", help="NAME=REGEX=ALG_BYTES")
+    c = sub.add_parser("counters")
+    c.add_argument("--dir", action="append", required=True)
+    c.add_argument("--title", default="")
+    c.add_argument("--cmd", required=True)
+    c.add_argument("kernels", nargs="+", help="NAME=REGEX=UNITS[=LAUNCHES]")
     a = ap.parse_args()
-    {"stats": cmd_stats, "pmc": cmd_pmc, "pmc-table": cmd_pmc_table}[a.mode](a)
+    {"stats": cmd_stats, "pmc": cmd_pmc, "pmc-table": cmd_pmc_table,
+     "counters": cmd_counters}[a.mode](a)
 
 
 if __name__ == "__main__":
