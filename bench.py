@@ -356,16 +356,19 @@ def main():
         ring_key, kernel = "fusion_ring", "fusion_ring_kernel"
     ring_ms = stage_ms[ring_key]
     achieved = nbytes[ring_key] / (ring_ms * 1e-3) / 1e9
-    # the staged schedule is 2 (P - 1) launches per call: the rate is their
-    # mean, bytes per launch their mean too
-    per_launch = nbytes[ring_key] / (2 * (P - 1) if ring_key == "ring_staged" else 1)
+    # a call of the one-read pass is several equal launches (pieces of 2^26
+    # elements), the staged schedule 2 (P - 1): the rate is over the whole
+    # call (gaps between launches included), bytes per launch its mean
+    launches = (ga.thc_ring_step_launches(N) if ring_key.startswith("thc_ring_step") else
+                2 * (P - 1) if ring_key == "ring_staged" else 1)
+    per_launch = nbytes[ring_key] / launches
     # the copy path runs one ring launch per fusion buffer: its summary would
     # be per buffer, so only single-launch rings carry traffic
     one_launch = calls[ring_key] // args.steps == 1
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profile(args.workload, kernel) if one_launch else None,
-                "kernel": kernel, "alg_bytes_per_launch": per_launch}
+                "kernel": kernel, "alg_bytes_per_launch": per_launch, "launches_per_call": launches}
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,

@@ -18,4 +18,7 @@ from ._native import (  # noqa: F401
     center_table, RING_DUAL, FTENSOR_DTYPE, FusionRing, ga_fusion_ring_plan, rht_padded,
     thc_rht_sumsq, thc_rht_range, thc_rht_forward, thc_rht_inverse, thc_rht_quantize,
     thc_aggregate_dequant, thc_aggregate_dequant_ws_bytes, thc_rht_norm_quantize,
+    thc_rht_norm_quantize_ws_bytes, ga_ring_stage_bytes, ga_ring_stepwise_staged,
+    fusion_block_bytes, thc_nmse_noalloc, thc_ring_step, thc_ring_step_ws_bytes,
+    thc_ring_step_launches, thc_ef_minmax, thc_ef_quantize,
 )

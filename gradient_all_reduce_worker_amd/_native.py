@@ -31,6 +31,7 @@ EXPORTS = (
     "thc_rht_quantize", "thc_aggregate_dequant", "thc_aggregate_dequant_ws_bytes",
     "thc_rht_norm_quantize", "thc_rht_norm_quantize_ws_bytes", "thc_ring_step",
     "thc_ring_step_ws_bytes", "ga_ring_stage_bytes", "ga_ring_stepwise_staged",
+    "thc_ring_step_launches",
 )
 
 
@@ -114,13 +115,15 @@ def load() -> C.CDLL:
                                 C.POINTER(vp), vp, vp, vp, vp, C.c_size_t, vp]
     L.thc_ring_step_ws_bytes.argtypes = [i64]
     L.thc_ring_step_ws_bytes.restype = C.c_size_t
+    L.thc_ring_step_launches.argtypes = [i64]
+    L.thc_ring_step_launches.restype = i64
     L.thc_rht_norm_quantize_ws_bytes.argtypes = [i32, i64, i64]
     L.thc_rht_norm_quantize_ws_bytes.restype = C.c_size_t
     L.thc_aggregate_dequant_ws_bytes.restype = C.c_size_t
     L.ga_last_error.argtypes = []
     L.ga_last_error.restype = C.c_char_p
     for name in EXPORTS:                 # every other call returns a ga_status
-        if not name.endswith("_bytes") and name != "ga_last_error":
+        if not name.endswith(("_bytes", "_launches")) and name != "ga_last_error":
             getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -483,6 +486,10 @@ def thc_ring_step_ws_bytes(N: int) -> int:
     return int(load().thc_ring_step_ws_bytes(N))
 
 
+def thc_ring_step_launches(N: int) -> int:
+    return int(load().thc_ring_step_launches(N))
+
+
 def thc_ring_step(bufs: Sequence[torch.Tensor], mM: torch.Tensor, b: int, seed: int,
                   ring_part: int = 0, q_part: int = 0, worker0: int = 0,
                   packed: Optional[Sequence[torch.Tensor]] = None, keep_packed: bool = True,
@@ -698,6 +705,10 @@ def thc_rht_quantize(bufs: Sequence[torch.Tensor], d: int, rht_seed: int, mM: to
     return packed
 
 
+def thc_rht_norm_quantize_ws_bytes(P: int, N: int, d: int) -> int:
+    return int(load().thc_rht_norm_quantize_ws_bytes(P, N, d))
+
+
 def thc_rht_norm_quantize(bufs: Sequence[torch.Tensor], d: int, rht_seed: int, t_p: float, b: int,
                           q_seed: int, worker0: int = 0, g: int = 0, table=None,
                           sumsq: Optional[torch.Tensor] = None, mM: Optional[torch.Tensor] = None,
@@ -717,7 +728,7 @@ def thc_rht_norm_quantize(bufs: Sequence[torch.Tensor], d: int, rht_seed: int, t
     if y_scratch is None and d > 8192 and N > 0:
         y_scratch = [torch.empty(Np, dtype=torch.float32, device=dev) for _ in bufs]
     if ws is None:
-        ws = torch.empty(max(load().thc_rht_norm_quantize_ws_bytes(len(bufs), N, d), 8),
+        ws = torch.empty(max(thc_rht_norm_quantize_ws_bytes(len(bufs), N, d), 8),
                          dtype=torch.uint8, device=dev)
     _check(load().thc_rht_norm_quantize(
         _ptr_array(bufs, "buffer"), len(bufs), worker0, N, _dt(bufs[0]), d, rht_seed, float(t_p), b, g,

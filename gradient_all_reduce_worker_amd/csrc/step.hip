@@ -151,7 +151,7 @@ template <ga_dtype DT, int B, int PT, int WPE>
 __global__ __attribute__((amdgpu_waves_per_eu(WPE))) __launch_bounds__(kThreads) void thc_ring_kernel(
         PtrTable bufs, PtrTable packed, int has_packed, int P_, int worker0, int64_t N, int64_t rplen,
         int64_t qplen, const float* __restrict__ mM, uint32_t k0, uint32_t k1, Avg avg,
-        int32_t* __restrict__ sum, void* xhat, double* ws) {
+        int32_t* __restrict__ sum, void* xhat, double* ws, int64_t blk_base) {
     using G = Group8<DT>;
     constexpr int K = G::kVecs;
     constexpr int L = (1 << B) - 1;
@@ -159,7 +159,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(WPE))) __launch_bounds__(kThreads)
     const int P = PT > 0 ? PT : P_;
     __shared__ double sh[kThreads / 64];
     const int64_t n_groups = N / 8;
-    const int64_t blk = flat_block();
+    const int64_t blk = blk_base + flat_block();       // this piece's first workgroup + ours
     const int64_t g0 = blk * kThreads;
     if (g0 >= n_groups) return;                        // past the folded grid's end
     const int64_t g = g0 + threadIdx.x;
@@ -271,6 +271,13 @@ __global__ __attribute__((amdgpu_waves_per_eu(WPE))) __launch_bounds__(kThreads)
     }
 }
 
+// The pass is launched in pieces of at most kStepPiece workgroups (2^26
+// elements); each piece's workgroups carry on the global numbering.
+// Measured on 8 x 2^31 bf16, b = 2, builds loaded side by side and their
+// calls interleaved (medians of 12): one launch 16.69 ms; pieces of 2^14 /
+// 2^15 / 2^16 / 2^17 workgroups 16.16 / 16.00 / 16.19 / 16.45 ms.
+constexpr int64_t kStepPiece = (int64_t)1 << 15;
+
 int64_t step_blocks(int64_t N) { return std::max<int64_t>(1, ceil_div(std::max<int64_t>(N, 0) / 8, kThreads)); }
 
 // Workgroups resident per CU on large inputs. The ring alone streams best
@@ -289,6 +296,10 @@ size_t step_lds(int P, int64_t bytes) {
 }  // namespace ga
 
 using namespace ga;
+
+extern "C" int64_t thc_ring_step_launches(int64_t N) {
+    return N > 0 ? ceil_div(step_blocks(N), kStepPiece) : 0;
+}
 
 extern "C" size_t thc_ring_step_ws_bytes(int64_t N) {
     const int64_t nblk = step_blocks(N);
@@ -348,27 +359,29 @@ extern "C" ga_status thc_ring_step(void* const* bufs, int32_t P, int64_t N, ga_d
     double* ws = d_nmse ? static_cast<double*>(d_ws) : nullptr;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const size_t lds = step_lds(P, 2 * (int64_t)P * N * es);
-    const dim3 grid = flat_grid(nblk);
     const int hp = packed != nullptr;
 #define GA_STEP(DT, B, PT, W)                                                                   \
-    hipLaunchKernelGGL((thc_ring_kernel<DT, B, PT, W>), grid, dim3(kThreads), lds, hs, tb, tp, hp, P, \
-                       worker0, N, rplen, qplen, d_mM, k0, k1, avg, d_sum, xhat, ws)
+    hipLaunchKernelGGL((thc_ring_kernel<DT, B, PT, W>), flat_grid(nb), dim3(kThreads), lds, hs, tb, tp, hp, \
+                       P, worker0, N, rplen, qplen, d_mM, k0, k1, avg, d_sum, xhat, ws, b0)
 #define GA_STEP_P(DT, B)                                                                        \
     do {                                                                                        \
         if (P == 8) GA_STEP(DT, B, 8, DT == GA_BF16 ? 5 : 3);                                   \
         else if (P == 16) GA_STEP(DT, B, 16, DT == GA_BF16 ? 3 : 2);                            \
         else GA_STEP(DT, B, 0, 1);                                                              \
     } while (0)
-    if (dt == GA_F32) {
-        if (b == 1) GA_STEP_P(GA_F32, 1); else if (b == 2) GA_STEP_P(GA_F32, 2);
-        else if (b == 4) GA_STEP_P(GA_F32, 4); else GA_STEP_P(GA_F32, 8);
-    } else {
-        if (b == 1) GA_STEP_P(GA_BF16, 1); else if (b == 2) GA_STEP_P(GA_BF16, 2);
-        else if (b == 4) GA_STEP_P(GA_BF16, 4); else GA_STEP_P(GA_BF16, 8);
+    for (int64_t b0 = 0; b0 < nblk; b0 += kStepPiece) {
+        const int64_t nb = std::min(kStepPiece, nblk - b0);
+        if (dt == GA_F32) {
+            if (b == 1) GA_STEP_P(GA_F32, 1); else if (b == 2) GA_STEP_P(GA_F32, 2);
+            else if (b == 4) GA_STEP_P(GA_F32, 4); else GA_STEP_P(GA_F32, 8);
+        } else {
+            if (b == 1) GA_STEP_P(GA_BF16, 1); else if (b == 2) GA_STEP_P(GA_BF16, 2);
+            else if (b == 4) GA_STEP_P(GA_BF16, 4); else GA_STEP_P(GA_BF16, 8);
+        }
+        if ((rc = check_launch(what))) return rc;
     }
 #undef GA_STEP_P
 #undef GA_STEP
-    if ((rc = check_launch(what))) return rc;
     if (!d_nmse) return GA_OK;
     if (nblk > kNmseGroup) {                             // two levels
         const int64_t ng = ceil_div(nblk, kNmseGroup);

@@ -409,6 +409,10 @@ ga_status thc_ring_step(void* const* bufs, int32_t P, int64_t N, ga_dtype dt, in
                         uint8_t* const* packed, int32_t* d_sum, void* xhat, double* d_nmse, void* d_ws,
                         size_t ws_bytes, void* stream);
 size_t thc_ring_step_ws_bytes(int64_t N);
+/* Kernel launches thc_ring_step enqueues for its pass over N elements (it
+ * runs in pieces of 2^26 elements, which measured faster than one launch;
+ * the NMSE adds one or two small launches): for timing per launch. */
+int64_t thc_ring_step_launches(int64_t N);
 
 /* ------------------------------------------------------------------ */
 /* Non-uniform THC: lookup tables  ([THC] section 4, Algorithm 2)       */

@@ -27,7 +27,7 @@ def _declared():
 def test_header_declarations_are_exported():
     L = nat.load()
     names = _declared()
-    assert len(names) == 33
+    assert len(names) == 34
     assert set(names) == set(nat.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -35,6 +35,16 @@ def test_header_declarations_are_exported():
                           text=True, check=True).stdout
     exported = {line.split()[-1] for line in syms.splitlines() if " T " in line}
     assert set(names) <= exported
+
+
+def test_package_binds_every_export_by_name():
+    """The Python binding offers every C entry point under its own name
+    (ga_last_error and the fusion ring's two calls sit behind GAError and
+    FusionRing)."""
+    import gradient_all_reduce_worker_amd as pkg
+    behind = {"ga_last_error", "ga_fusion_ring_allreduce"}
+    missing = [n for n in nat.EXPORTS if n not in behind and not callable(getattr(pkg, n, None))]
+    assert not missing, missing
 
 
 @pytest.mark.parametrize("name", ["fusion", "resnet101", "vgg16"])
@@ -158,6 +168,8 @@ def test_staged_stepwise_errors_before_enqueue():
     assert nat.ga_ring_stage_bytes(2, N) == 0 and nat.ga_ring_stage_bytes(1, N) == 0
     assert nat.ga_ring_stage_bytes(4, 0) == 0
     assert nat.ga_ring_stage_bytes(8, 1 << 31) == 1 << 33                        # size_t, not int
+    # the one-read pass: pieces of 2^26 elements
+    assert [nat.thc_ring_step_launches(n) for n in (0, 8, 1 << 26, (1 << 26) + 8, 1 << 31)] == [0, 1, 1, 2, 32]
     stage = 0x900000
     assert call(good, 4, N, 1, 1, 0, None, 0, None, None) == EINVAL                 # no stage
     assert call(good, 4, N, 1, 1, 0, stage, 4 * N - 4, None, None) == EINVAL        # too small
