@@ -263,6 +263,9 @@ def main():
     ap.add_argument("--separate-step", action="store_true",
                     help="flat workloads: quantizer, ring and tail as separate calls instead of the "
                          "one-read thc_ring_step")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the K steps again as replays of one step captured in a HIP graph and "
+                         "report those (the stage breakdown and roofline stay the eager steps')")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one 1 GiB torch copy first (PMC calibration)")
     args = ap.parse_args()
@@ -331,6 +334,17 @@ def main():
     stage_ms = timer.mean_ms()
     calls = timer.count()
     log(f"timed {args.steps} steps: {elapsed:.3f} s")
+    eager_ms = elapsed / args.steps * 1e3
+    if args.graph:
+        graph = pipe.capture(warmup=max(args.warmup, 1))
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        log(f"timed {args.steps} graph replays: {elapsed:.3f} s")
 
     P, N, s = pipe.P, pipe.N, pipe.w.elem_bytes
     ms_step = elapsed / args.steps * 1e3
@@ -386,12 +400,15 @@ def main():
                    "thc_ring_step": "fused" if pipe.fused_step else "separate",
                    "fusion": (None if not pipe.w.fused else
                               "pack-ring-unpack" if args.copy_fusion else "zero-copy"),
+                   "launch": "graph" if args.graph else "eager",
                    "parallelism": "1 GPU, P simulated workers"},
         "roofline": roofline,
         "thc_quantize_gelem_s": quant,
         "nmse": {(f"b{b}" if isinstance(b, int) else b): v[2] for b, v in nmse.items()},
         "stages": stages,
     }
+    if args.graph:
+        out["eager_ms_per_step"] = round(eager_ms, 4)
     if samples is not None:
         out["cpu_baseline"] = cpu_baseline_flat(pipe, samples, args.cpu_seconds, threads)
     elif host is not None:

@@ -104,9 +104,10 @@ class Pipeline:
     nu_tables: Dict[str, tuple] = {}
     rht: Dict[str, tuple] = {}
 
-    def __init__(self, name: str, device="cuda", cap_bytes: int = 64 << 20, zero_copy: bool = True,
+    def __init__(self, name, device="cuda", cap_bytes: int = 64 << 20, zero_copy: bool = True,
                  ring_mode: int = ga.RING_FUSED, fused_tail: bool = True, fused_step: bool = True):
-        self.w = synth.workload(name)
+        # a workload by name, or a synth.Workload built by the caller
+        self.w = synth.workload(name) if isinstance(name, str) else name
         self.zero_copy = zero_copy
         # the first uniform THC pass, the ring average and that pass's sum,
         # dequant and NMSE in one read (thc_ring_step), where the sizes allow
@@ -336,6 +337,31 @@ class Pipeline:
                   odt, out)
         if nmse:
             _call(timer, f"thc_nmse_{key}", ga.thc_nmse, self.flat[0], out, self.nmse[sk], self.ws)
+
+    # ------------------------------------------------------------ graphs
+    def state_buffers(self) -> List[torch.Tensor]:
+        """Every buffer a step reads and then overwrites: the gradients (the
+        ring leaves their average in them) and the error-feedback residuals."""
+        if self.w.fused:
+            return [t for ts in self.tensors for t in ts]
+        return list(self.flat) + [e for k in self.err for e in self.err[k]]
+
+    def capture(self, warmup: int = 2) -> torch.cuda.CUDAGraph:
+        """One step recorded into a HIP graph: every call of a step only
+        enqueues kernels (no allocation, copy or memset), so the graph holds
+        the step's kernels with their arguments; replay() runs it again on the
+        same buffers. The warm-up steps (on a side stream, as capture wants)
+        run first and change the state buffers like any step."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(warmup):
+                self.step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.step()
+        return graph
 
     # ------------------------------------------------------------ accounting
     def stage_bytes(self) -> Dict[str, float]:
