@@ -37,10 +37,12 @@ HBM_PEAK_GBS = 8000.0
 # ring_fused_<workload>_pmc.json (flat ring) or fusion_ring_<workload>_pmc.json
 # (zero-copy fusion ring), each stamped with the ring source's hash
 PMC_FILE = {"ring_fused_vec_kernel": "ring_fused_{}_pmc.json",
+            "thc_ring_lane_kernel": "thc_ring_lane_{}_pmc.json",
             "fusion_ring_kernel": "fusion_ring_{}_pmc.json",
             "thc_ring_kernel": "thc_ring_{}_pmc.json"}
 CSRC = os.path.join(ROOT, "gradient_all_reduce_worker_amd", "csrc")
 KERNEL_SRC = {"ring_fused_vec_kernel": "ring.hip", "fusion_ring_kernel": "ring.hip",
+              "thc_ring_lane_kernel": "step.hip",
               "thc_ring_kernel": "step.hip"}
 
 DESCRIPTIONS = {
@@ -361,7 +363,9 @@ def main():
 
     step_keys = [k for k in stage_ms if k.startswith("thc_ring_step")]
     if step_keys:
-        ring_key, kernel = step_keys[0], "thc_ring_kernel"
+        # bf16 buffers hold whole groups per thread, binary32 ones lane pairs
+        ring_key = step_keys[0]
+        kernel = "thc_ring_lane_kernel" if pipe.w.dtype == ga.F32 else "thc_ring_kernel"
     elif "ring_allreduce" in stage_ms:
         ring_key, kernel = "ring_allreduce", "ring_fused_vec_kernel"
     elif "ring_staged" in stage_ms:

@@ -68,6 +68,12 @@ __device__ __forceinline__ uint32_t usq_index(float a, Grid g, int L, uint32_t r
     return (uint32_t)u + (up ? 1u : 0u);
 }
 
+// Lanes 2k and 2k+1 exchange v (DPP quad permute [1, 0, 3, 2]); every lane
+// of the wave must take part.
+__device__ __forceinline__ uint32_t swap_pair(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+
 __device__ __forceinline__ uint32_t uniform16(const Philox4& r, int i) {
     return (r.v[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
 }

@@ -21,12 +21,15 @@
 // thc_aggregate_dequant and ga_ring_allreduce_sim (fused, op = avg) leave;
 // the NMSE is summed in another order (within rounding of it).
 //
-// A workgroup takes 256 consecutive groups. When they lie in one chunk of
-// one ring partition (every workgroup when chunks are multiples of 2048
-// elements), the workers are loaded in the chunk's fold order, so the fold
-// is the load order and each value is quantized as it arrives; otherwise the
-// indices are made in worker order and each element is folded in its own
-// chunk's order from memory.
+// A workgroup takes 256 consecutive groups (2048 elements). When they lie
+// in one chunk of one ring partition (every workgroup when chunks are
+// multiples of 2048 elements), the workers are loaded in the chunk's fold
+// order, so the fold is the load order and each value is quantized as it
+// arrives; otherwise the indices are made in worker order and each element
+// is folded in its own chunk's order from memory. bf16 buffers take
+// thc_ring_kernel (a thread holds whole groups: 16 bytes per worker);
+// binary32 buffers take thc_ring_lane_kernel (lane pairs share groups, so
+// every load instruction is contiguous across the wave).
 #include <algorithm>
 
 #include "common.hpp"
@@ -48,7 +51,8 @@ struct Avg {
     __device__ __forceinline__ float apply(float x) const { return pow2 ? x * recip : x / pf; }
 };
 
-// 8 consecutive elements (one group) of a worker as binary32.
+// 8 consecutive elements (one group) of a worker as binary32 (bf16 buffers;
+// binary32 ones take the lane-pair kernel below).
 template <ga_dtype DT> struct Group8;
 
 template <> struct Group8<GA_BF16> {
@@ -69,25 +73,6 @@ template <> struct Group8<GA_BF16> {
     }
     __device__ static __forceinline__ float load1(const void* p, int64_t e) {
         return __uint_as_float((uint32_t) static_cast<const uint16_t*>(p)[e] << 16);
-    }
-};
-
-template <> struct Group8<GA_F32> {
-    static constexpr int kVecs = 2;
-    __device__ static __forceinline__ void widen(const uint4* r, float* f) {
-        f[0] = __uint_as_float(r[0].x); f[1] = __uint_as_float(r[0].y);
-        f[2] = __uint_as_float(r[0].z); f[3] = __uint_as_float(r[0].w);
-        f[4] = __uint_as_float(r[1].x); f[5] = __uint_as_float(r[1].y);
-        f[6] = __uint_as_float(r[1].z); f[7] = __uint_as_float(r[1].w);
-    }
-    __device__ static __forceinline__ void narrow(const float* f, uint4* r, float* back) {
-#pragma unroll
-        for (int i = 0; i < 8; i++) back[i] = f[i];
-        r[0] = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
-        r[1] = make_uint4(__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]), __float_as_uint(f[7]));
-    }
-    __device__ static __forceinline__ float load1(const void* p, int64_t e) {
-        return static_cast<const float*>(p)[e];
     }
 };
 
@@ -271,12 +256,216 @@ __global__ __attribute__((amdgpu_waves_per_eu(WPE))) __launch_bounds__(kThreads)
     }
 }
 
+// ---------------------------------------------------------------- binary32 in lane pairs
+
+// A group of 8 binary32 is 32 bytes, so a thread holding whole groups makes
+// each 16-byte load instruction cover every other half of the wave's lines.
+// For binary32 the pass takes a workgroup's 2048 elements as the lane
+// quantizer does: thread t holds 16-byte vectors t and t + 256 of the span
+// (one half of group t/2 and one half of group 128 + t/2); per worker the
+// even lane of a pair draws the Philox block of the first group and the odd
+// lane that of the second, and they swap two words, so every element gets
+// the uniform of the same counter and word as in the per-group pass.
+
+// One worker's 8 values a[h][i] (vector v[h], element i) of this lane:
+// indices on the grids gq[h] added into zs, packed into out.
+template <int B>
+__device__ __forceinline__ void lane_quantize(const float (&a)[2][4], const Grid (&gq)[2], int64_t g_lane,
+                                              bool odd, uint32_t wid, uint32_t k0, uint32_t k1,
+                                              uint32_t (&zs)[2][4], uint8_t* out, const int64_t (&v)[2],
+                                              const bool (&live)[2]) {
+    constexpr int L = (1 << B) - 1;
+    constexpr bool NEG = L < 128;                  // negated indices, one negation per vector
+    const Philox4 r = philox4x32_10((uint32_t)g_lane, (uint32_t)((uint64_t)g_lane >> 32), wid, 0u, k0, k1);
+    const uint32_t ra = swap_pair(odd ? r.v[0] : r.v[2]);
+    const uint32_t rb = swap_pair(odd ? r.v[1] : r.v[3]);
+    const uint32_t u[2][2] = {{odd ? ra : r.v[0], odd ? rb : r.v[1]},
+                              {odd ? r.v[2] : ra, odd ? r.v[3] : rb}};
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        uint32_t bits = 0;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const uint32_t r16 = (u[h][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+            if (NEG) {
+                const uint32_t w = usq_neg_index(a[h][i], gq[h], L, r16);
+                zs[h][i] += w;
+                bits += w << (i * B);
+            } else {
+                const uint32_t z = usq_index(a[h][i], gq[h], L, r16);
+                zs[h][i] += z;
+                bits |= z << (i * B);
+            }
+        }
+        if (NEG) {
+            asm("" : "+v"(bits));
+            bits = 0u - bits;
+        }
+        if (B == 1) {                              // two vectors per byte: every lane swaps
+            const uint32_t other = swap_pair(bits);
+            if (out && live[h] && !odd) out[v[h] >> 1] = (uint8_t)(bits | (other << 4));
+        } else if (out && live[h]) {
+            if (B == 8) __builtin_nontemporal_store(bits, reinterpret_cast<uint32_t*>(out) + v[h]);
+            else if (B == 4) __builtin_nontemporal_store((uint16_t)bits, reinterpret_cast<uint16_t*>(out) + v[h]);
+            else __builtin_nontemporal_store((uint8_t)bits, out + v[h]);
+        }
+    }
+}
+
+// As thc_ring_kernel for binary32 buffers, in lane pairs; KB worker loads in
+// flight per vector.
+template <int B, int PT, int KB, int WPE>
+__global__ __attribute__((amdgpu_waves_per_eu(WPE))) __launch_bounds__(kThreads) void thc_ring_lane_kernel(
+        PtrTable bufs, PtrTable packed, int has_packed, int P_, int worker0, int64_t N, int64_t rplen,
+        int64_t qplen, const float* __restrict__ mM, uint32_t k0, uint32_t k1, Avg avg,
+        int32_t* __restrict__ sum, void* xhat, double* ws, int64_t blk_base) {
+    constexpr int L = (1 << B) - 1;
+    const int P = PT > 0 ? PT : P_;
+    __shared__ double sh[kThreads / 64];
+    const int64_t n_vec = N / 4;
+    const int64_t blk = blk_base + flat_block();
+    const int64_t vb = blk * (2 * kThreads);         // the span's first vector
+    if (vb >= n_vec) return;                         // past the folded grid's end
+    const int t = threadIdx.x;
+    const bool odd = t & 1;
+    const int64_t v[2] = {vb + t, vb + t + kThreads};
+    const bool live[2] = {v[0] < n_vec, v[1] < n_vec};
+    const int64_t g_lane = (vb >> 1) + (odd ? kThreads / 2 + (t >> 1) : (t >> 1));
+    const int64_t e_last = min(vb + 2 * kThreads, n_vec) * 4 - 1;
+    const Chunk first = chunk_of(vb * 4, N, rplen, P), last = chunk_of(e_last, N, rplen, P);
+    const bool uniform = first.part == last.part && first.c == last.c;
+    int64_t q[2];
+    Grid gq[2];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        q[h] = live[h] ? 4 * v[h] / qplen : 0;     // qplen is a multiple of 8
+        gq[h] = grid_of(mM, q[h], L);
+    }
+    float acc[2][4];
+    uint32_t zs[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) zs[h][i] = 0u;
+    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+    if (uniform) {
+        // workers in the chunk's fold order first.c, first.c + 1, ...
+        for (int kb = 0; kb < P; kb += KB) {
+            uint4 raw[KB][2];
+#pragma unroll
+            for (int kk = 0; kk < KB; kk++) {
+                if (kb + kk < P) {
+                    int w = first.c + kb + kk;
+                    if (w >= P) w -= P;
+                    const uint4* src = static_cast<const uint4*>(bufs.p[w]);
+#pragma unroll
+                    for (int h = 0; h < 2; h++) raw[kk][h] = live[h] ? load_stream(src + v[h]) : zero;
+                }
+            }
+#pragma unroll
+            for (int kk = 0; kk < KB; kk++) {
+                if (kb + kk < P) {
+                    int w = first.c + kb + kk;
+                    if (w >= P) w -= P;
+                    float a[2][4];
+#pragma unroll
+                    for (int h = 0; h < 2; h++) {
+                        a[h][0] = __uint_as_float(raw[kk][h].x); a[h][1] = __uint_as_float(raw[kk][h].y);
+                        a[h][2] = __uint_as_float(raw[kk][h].z); a[h][3] = __uint_as_float(raw[kk][h].w);
+#pragma unroll
+                        for (int i = 0; i < 4; i++) acc[h][i] = kb + kk == 0 ? a[h][i] : acc[h][i] + a[h][i];
+                    }
+                    lane_quantize<B>(a, gq, g_lane, odd, (uint32_t)(worker0 + w), k0, k1, zs,
+                                     has_packed ? static_cast<uint8_t*>(packed.p[w]) : nullptr, v, live);
+                }
+            }
+        }
+    } else {
+        // indices in worker order, then each element folded in its own
+        // chunk's order, read again (a few workgroups per chunk boundary)
+        for (int w = 0; w < P; w++) {
+            const uint4* src = static_cast<const uint4*>(bufs.p[w]);
+            float a[2][4];
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const uint4 r4 = live[h] ? load_stream(src + v[h]) : zero;
+                a[h][0] = __uint_as_float(r4.x); a[h][1] = __uint_as_float(r4.y);
+                a[h][2] = __uint_as_float(r4.z); a[h][3] = __uint_as_float(r4.w);
+            }
+            lane_quantize<B>(a, gq, g_lane, odd, (uint32_t)(worker0 + w), k0, k1, zs,
+                             has_packed ? static_cast<uint8_t*>(packed.p[w]) : nullptr, v, live);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                if (!live[h]) continue;
+                const int64_t e = 4 * v[h] + i;
+                int w = chunk_of(e, N, rplen, P).c;
+                float x = static_cast<const float*>(bufs.p[w])[e];
+                for (int k = 1; k < P; k++) {
+                    w = w + 1 == P ? 0 : w + 1;
+                    x = x + static_cast<const float*>(bufs.p[w])[e];
+                }
+                acc[h][i] = x;
+            }
+        }
+    }
+    double num = 0.0, den = 0.0;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        if (!live[h]) continue;
+        // the ring's average, to every worker
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) x[i] = avg.apply(acc[h][i]);
+        const uint4 o = make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                                   __float_as_uint(x[3]));
+        for (int w = 0; w < P; w++) store_stream(static_cast<uint4*>(bufs.p[w]) + v[h], o);
+        // the server's sum and the dequantized average m + (S / P) delta
+        const float m = mM[2 * q[h]], range = mM[2 * q[h] + 1] - m, delta = range / (float)L;
+        int32_t S[4];
+        float hv[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            S[i] = L < 128 ? (int32_t)(0u - zs[h][i]) : (int32_t)zs[h][i];
+            hv[i] = range != 0.0f ? m + avg.apply((float)S[i]) * delta : m;
+        }
+        if (sum) store_stream(sum + 4 * v[h], make_uint4((uint32_t)S[0], (uint32_t)S[1], (uint32_t)S[2], (uint32_t)S[3]));
+        store_stream(static_cast<uint4*>(xhat) + v[h], make_uint4(__float_as_uint(hv[0]), __float_as_uint(hv[1]),
+                                                                   __float_as_uint(hv[2]), __float_as_uint(hv[3])));
+        // NMSE terms of the values as stored
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const double d = (double)x[i] - (double)hv[i];
+            num += d * d;
+            den += (double)x[i] * (double)x[i];
+        }
+    }
+    if (ws) {
+        num = block_sum(num, sh);
+        den = block_sum(den, sh);
+        if (threadIdx.x == 0) {
+            ws[2 * blk] = num;
+            ws[2 * blk + 1] = den;
+        }
+    }
+}
+
 // The pass is launched in pieces of at most kStepPiece workgroups (2^26
 // elements); each piece's workgroups carry on the global numbering.
 // Measured on 8 x 2^31 bf16, b = 2, builds loaded side by side and their
 // calls interleaved (medians of 12): one launch 16.69 ms; pieces of 2^14 /
 // 2^15 / 2^16 / 2^17 workgroups 16.16 / 16.00 / 16.19 / 16.45 ms.
 constexpr int64_t kStepPiece = (int64_t)1 << 15;
+// The lane-pair kernel with P at run time, 8 worker loads in flight per
+// vector and 4 waves per SIMD (110-114 registers, no spills). Measured
+// against the per-group layout with the same results, byte for byte:
+// 32 x 138M binary32, b = 4: 14.50 -> 7.97 ms; 16 x 2^27, b = 4: 3.74 ->
+// 3.63 ms; 8 x 2^28, b = 2: 3.88 -> 3.66 ms. P fixed at compile time spills
+// at 4 waves; 16 loads in flight (168 registers, spills) 8.55 ms at 32 x 138M.
+constexpr int kLaneWaves = 4;
+constexpr int kLaneBatch = 8;
 
 int64_t step_blocks(int64_t N) { return std::max<int64_t>(1, ceil_div(std::max<int64_t>(N, 0) / 8, kThreads)); }
 
@@ -365,21 +554,27 @@ extern "C" ga_status thc_ring_step(void* const* bufs, int32_t P, int64_t N, ga_d
                        P, worker0, N, rplen, qplen, d_mM, k0, k1, avg, d_sum, xhat, ws, b0)
 #define GA_STEP_P(DT, B)                                                                        \
     do {                                                                                        \
-        if (P == 8) GA_STEP(DT, B, 8, DT == GA_BF16 ? 5 : 3);                                   \
-        else if (P == 16) GA_STEP(DT, B, 16, DT == GA_BF16 ? 3 : 2);                            \
+        if (P == 8) GA_STEP(DT, B, 8, 5);                                                       \
+        else if (P == 16) GA_STEP(DT, B, 16, 3);                                                \
         else GA_STEP(DT, B, 0, 1);                                                              \
     } while (0)
+#define GA_LANE(B, PT, KB, W)                                                                   \
+    hipLaunchKernelGGL((thc_ring_lane_kernel<B, PT, KB, W>), flat_grid(nb), dim3(kThreads), lds, hs, tb, tp, \
+                       hp, P, worker0, N, rplen, qplen, d_mM, k0, k1, avg, d_sum, xhat, ws, b0)
+#define GA_LANE_P(B) GA_LANE(B, 0, kLaneBatch, kLaneWaves)
     for (int64_t b0 = 0; b0 < nblk; b0 += kStepPiece) {
         const int64_t nb = std::min(kStepPiece, nblk - b0);
         if (dt == GA_F32) {
-            if (b == 1) GA_STEP_P(GA_F32, 1); else if (b == 2) GA_STEP_P(GA_F32, 2);
-            else if (b == 4) GA_STEP_P(GA_F32, 4); else GA_STEP_P(GA_F32, 8);
+            if (b == 1) GA_LANE_P(1); else if (b == 2) GA_LANE_P(2);
+            else if (b == 4) GA_LANE_P(4); else GA_LANE_P(8);
         } else {
             if (b == 1) GA_STEP_P(GA_BF16, 1); else if (b == 2) GA_STEP_P(GA_BF16, 2);
             else if (b == 4) GA_STEP_P(GA_BF16, 4); else GA_STEP_P(GA_BF16, 8);
         }
         if ((rc = check_launch(what))) return rc;
     }
+#undef GA_LANE_P
+#undef GA_LANE
 #undef GA_STEP_P
 #undef GA_STEP
     if (!d_nmse) return GA_OK;

@@ -344,10 +344,6 @@ __global__ __launch_bounds__(kThreads) void usq_quantize_fast_kernel(PtrTable bu
 // 8 TB/s, b = 8 0.68 -> 0.75.)
 constexpr int64_t kLSpan = 2048;       // elements per workgroup of the lane kernel
 
-__device__ __forceinline__ uint32_t swap_pair(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // lanes 2k <-> 2k+1
-}
-
 __device__ __forceinline__ void widen_f32(const uint4& r, float* f) {
     f[0] = __uint_as_float(r.x); f[1] = __uint_as_float(r.y);
     f[2] = __uint_as_float(r.z); f[3] = __uint_as_float(r.w);

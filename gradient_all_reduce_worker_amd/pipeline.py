@@ -111,18 +111,17 @@ class Pipeline:
         self.zero_copy = zero_copy
         # the first uniform THC pass, the ring average and that pass's sum,
         # dequant and NMSE in one read (thc_ring_step), where the sizes allow
-        # and it measured faster: up to 16 workers (8 x 2^31 bf16, b = 2:
-        # 13.9 ms against 22.0 ms for the three calls; 16 x 2^28 bf16 3.5
-        # against 5.8; 8 x 2^28 fp32 3.9 against 4.9). At 32 workers
-        # (32 x 138M fp32) it is slower (12.8 against 9.5 ms): the fold keeps
-        # 32 workers' loads for the rounding, and a group of 8 fp32 per thread
-        # leaves every 16-byte access instruction covering every other half
-        # of the wave's lines.
+        # and it measured faster: binary32 at any P (lane pairs; 32 x 138M,
+        # b = 4: 7.97 ms against 10.6 ms for the three calls) and bf16 up to
+        # 16 workers (8 x 2^31 bf16, b = 2: 13.9 ms against 22.0 ms; 16 x
+        # 2^28: 3.5 against 5.8). bf16 holds whole groups per thread, whose
+        # loads at 32 workers stay live for the rounding.
         w = self.w
         if ring_mode == RING_STAGED and w.fused:
             raise ValueError("the staged stepwise schedule runs on flat workloads")
         self.fused_step = (fused_step and not w.fused and bool(w.thc_bits) and w.N % 8 == 0
-                           and w.part_elems % 8 == 0 and ring_mode == ga.RING_FUSED and w.P <= 16)
+                           and w.part_elems % 8 == 0 and ring_mode == ga.RING_FUSED
+                           and (w.dtype == ga.F32 or w.P <= 16))
         # THC's integer sum, dequant and NMSE in one pass (thc_aggregate_dequant)
         # or as the three separate calls
         self.fused_tail = fused_tail
