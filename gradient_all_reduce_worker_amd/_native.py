@@ -31,7 +31,7 @@ EXPORTS = (
     "thc_rht_quantize", "thc_aggregate_dequant", "thc_aggregate_dequant_ws_bytes",
     "thc_rht_norm_quantize", "thc_rht_norm_quantize_ws_bytes", "thc_ring_step",
     "thc_ring_step_ws_bytes", "ga_ring_stage_bytes", "ga_ring_stepwise_staged",
-    "thc_ring_step_launches",
+    "thc_ring_step_launches", "thc_minmax_combine",
 )
 
 
@@ -80,6 +80,7 @@ def load() -> C.CDLL:
     L.ga_ring_stepwise_staged.argtypes = [C.POINTER(vp), i32, i64, i32, i32, i64, vp, C.c_size_t,
                                           C.POINTER(RingStats), vp]
     L.thc_minmax.argtypes = [C.POINTER(vp), i32, i64, i32, i64, vp, vp]
+    L.thc_minmax_combine.argtypes = [vp, i64, vp, vp]
     L.thc_usq_quantize.argtypes = [C.POINTER(vp), i32, i32, i64, i32, i64, vp, i32, u64,
                                    C.POINTER(vp), vp]
     L.thc_int_aggregate.argtypes = [C.POINTER(vp), i32, i64, i32, vp, vp]
@@ -420,6 +421,16 @@ def thc_minmax(bufs: Sequence[torch.Tensor], part_elems: int = 0, out: Optional[
 
 def packed_bytes(N: int, b: int) -> int:
     return (N * b + 7) // 8
+
+
+def thc_minmax_combine(parts: torch.Tensor, out: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """The whole vector's grid (1 x 2) from thc_minmax's partition grids."""
+    if out is None:
+        out = torch.empty((1, 2), dtype=torch.float32, device=parts.device)
+    _check(load().thc_minmax_combine(_dev(parts, "parts"), parts.numel() // 2, _dev(out, "mM"),
+                                     _stream(stream)))
+    return out
 
 
 def thc_usq_quantize(bufs: Sequence[torch.Tensor], mM: torch.Tensor, b: int, seed: int,

@@ -1077,8 +1077,52 @@ ga_status minmax_impl(const void* const* bufs, const float* const* errs, int32_t
     return check_launch(what);
 }
 
+// Extremes of n partition grids: the smallest m and the largest M. min and
+// max are exact, so this equals the extremes over the partitions' elements.
+__global__ __launch_bounds__(kThreads) void minmax_combine_kernel(const float* __restrict__ parts,
+                                                                  int64_t n, float* out) {
+    float mn = INFINITY, mx = -INFINITY;
+    for (int64_t i = threadIdx.x; i < n; i += kThreads) {
+        mn = fminf(mn, parts[2 * i]);
+        mx = fmaxf(mx, parts[2 * i + 1]);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        mn = fminf(mn, __shfl_xor(mn, o));
+        mx = fmaxf(mx, __shfl_xor(mx, o));
+    }
+    __shared__ float sh[2][kThreads / 64];
+    if ((threadIdx.x & 63) == 0) {
+        sh[0][threadIdx.x >> 6] = mn;
+        sh[1][threadIdx.x >> 6] = mx;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < kThreads / 64; w++) {
+            mn = fminf(mn, sh[0][w]);
+            mx = fmaxf(mx, sh[1][w]);
+        }
+        out[0] = mn + 0.0f;                          // a negative zero as +0
+        out[1] = mx + 0.0f;
+    }
+}
+
 }  // namespace
 }  // namespace ga
+
+extern "C" ga_status thc_minmax_combine(const float* d_parts, int64_t n_part, float* d_mM, void* stream) {
+    const char* what = "thc_minmax_combine";
+    if (n_part < 0) return fail(GA_EINVAL, "%s: negative size", what);
+    if (n_part == 0) return GA_OK;
+    if (!d_parts || !d_mM || !aligned(d_parts, 8) || !aligned(d_mM, 8))
+        return fail(GA_EINVAL, "%s: null or misaligned pointer", what);
+    const uintptr_t a = (uintptr_t)d_parts, o = (uintptr_t)d_mM;
+    if (o < a + (uintptr_t)(8 * n_part) && a < o + 8)
+        return fail(GA_EINVAL, "%s: output overlaps the partition grids", what);
+    hipLaunchKernelGGL(minmax_combine_kernel, dim3(1), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                       d_parts, n_part, d_mM);
+    return check_launch(what);
+}
 
 extern "C" ga_status thc_minmax(const void* const* bufs, int32_t P, int64_t N, ga_dtype dt,
                                 int64_t part_elems, float* d_mM, void* stream) {

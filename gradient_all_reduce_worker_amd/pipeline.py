@@ -261,7 +261,8 @@ class Pipeline:
             _call(timer, f"thc_usq_quantize_b{b}", ga.thc_usq_quantize, self.flat, self.mM, b,
                   w.quant_seed, part, 0, self.packed[b])
         if w.global_bits:
-            _call(timer, "thc_minmax_global", ga.thc_minmax, self.flat, 0, self.mM_g)
+            # the whole vector's grid from the partition grids (no second read)
+            _call(timer, "thc_minmax_global", ga.thc_minmax_combine, self.mM, self.mM_g)
         for b in w.global_bits:
             _call(timer, f"thc_usq_quantize_g{b}", ga.thc_usq_quantize, self.flat, self.mM_g, b,
                   w.quant_seed, 0, 0, self.packed[f"g{b}"])
@@ -394,7 +395,7 @@ class Pipeline:
             out[f"thc_dequant_b{b}"] = 4.0 * N + N * s
             out[f"thc_nmse_b{b}"] = 2.0 * N * s
         if w.global_bits:
-            out["thc_minmax_global"] = P * N * s
+            out["thc_minmax_global"] = 8.0 * ga.n_partitions(N, w.part_elems)   # the partition grids
         for b in w.global_bits:
             k = f"g{b}"
             out[f"thc_usq_quantize_{k}"] = P * N * (s + b / 8.0)

@@ -9,7 +9,8 @@
  *   ga_ring_stepwise_staged                        its schedule step by step,
  *                                                  partials on a binary32 wire
  *   ga_fusion_ring_plan / ga_fusion_ring_allreduce zero-copy fusion ring
- *   thc_minmax / thc_usq_quantize / thc_int_aggregate / thc_dequant / thc_nmse
+ *   thc_minmax / thc_minmax_combine / thc_usq_quantize / thc_int_aggregate /
+ *   thc_dequant / thc_nmse
  *   thc_nmse_noalloc (thc_nmse without a workspace, for callers that
  *   cannot allocate)
  *   thc_aggregate_dequant (aggregate + dequant + NMSE in one pass)
@@ -312,6 +313,20 @@ ga_status ga_fusion_ring_allreduce(const void* d_work, int64_t n_blocks, int32_t
  */
 ga_status thc_minmax(const void* const* bufs, int32_t P, int64_t N, ga_dtype dt,
                      int64_t part_elems, float* d_mM, void* stream);
+
+/*
+ * thc_minmax_combine -- the extremes of n_part partition grids (thc_minmax's
+ * output): d_mM[0] = the smallest m, d_mM[1] = the largest M (+0 for a
+ * negative zero). Algorithm 1's preliminary round takes local extremes and
+ * then global ones ([THC] section 3); min and max are exact, so this equals
+ * thc_minmax over the same elements with one partition, bit for bit, without
+ * reading them again.
+ *   d_parts   device, 2 n_part floats (8-byte aligned)
+ *   d_mM      device, 2 floats (8-byte aligned), disjoint from d_parts
+ * n_part = 0: nothing is done. Errors (nothing enqueued): GA_EINVAL for a
+ * negative n_part, a null, misaligned or overlapping pointer.
+ */
+ga_status thc_minmax_combine(const float* d_parts, int64_t n_part, float* d_mM, void* stream);
 
 /*
  * thc_usq_quantize -- every worker quantizes its vector on the shared grid

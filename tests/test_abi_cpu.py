@@ -27,7 +27,7 @@ def _declared():
 def test_header_declarations_are_exported():
     L = nat.load()
     names = _declared()
-    assert len(names) == 34
+    assert len(names) == 35
     assert set(names) == set(nat.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -154,6 +154,17 @@ def test_center_tables_are_valid():
             assert T[0] == 0 and T[-1] == g and len(T) == 1 << b
             assert all(T[i] < T[i + 1] for i in range(len(T) - 1))
     assert nat.center_table(2, 3) == [0, 1, 2, 3]
+
+
+def test_minmax_combine_errors_before_enqueue():
+    L = nat.load()
+    f = L.thc_minmax_combine
+    assert f(0x1000, -1, 0x2000, None) == EINVAL                  # negative size
+    assert f(None, 4, 0x2000, None) == EINVAL                     # null parts
+    assert f(0x1004, 4, 0x2000, None) == EINVAL                   # misaligned
+    assert f(0x1000, 4, 0x1010, None) == EINVAL                   # output inside the grids
+    assert b"overlaps" in L.ga_last_error()
+    assert f(None, 0, None, None) == 0                            # nothing to combine
 
 
 def test_staged_stepwise_errors_before_enqueue():

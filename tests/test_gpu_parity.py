@@ -241,6 +241,27 @@ def test_minmax(P, N, part, dt):
     assert np.array_equal(mM.cpu().numpy().view(np.uint32), want.view(np.uint32))
 
 
+@pytest.mark.parametrize("dt", [ga.F32, ga.BF16])
+@pytest.mark.parametrize("P,N,part", [(1, 1, 0), (3, 5000, 1000), (4, 70001, 1024), (8, 1 << 20, 4096),
+                                      (2, 300, 5), (32, 4099, 64)])
+def test_minmax_combine_equals_one_partition(P, N, part, dt):
+    """The whole vector's grid from the partition grids, bit for bit the
+    one-partition min/max and the oracle's."""
+    bufs = _inputs(P, N, dt, seed=N + 3 * P)
+    parts = ga.thc_minmax(bufs, part)
+    got = ga.thc_minmax_combine(parts).cpu().numpy()
+    whole = ga.thc_minmax(bufs, 0).cpu().numpy()
+    want = oracle.minmax([_host(b) for b in bufs], 0)
+    assert np.array_equal(got.view(np.uint32), whole.view(np.uint32))
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_minmax_combine_signed_zero():
+    z = [torch.cat([torch.full((100,), -0.0, device=DEV), torch.zeros(100, device=DEV)]) for _ in range(2)]
+    got = ga.thc_minmax_combine(ga.thc_minmax(z, 50)).cpu().numpy()
+    assert np.array_equal(got, np.zeros((1, 2), np.float32)) and not np.signbit(got).any()
+
+
 def test_minmax_misaligned_and_signed_zero():
     big = _inputs(3, 5001, ga.F32, seed=1)
     views = [b[1:] for b in big]
