@@ -21,4 +21,5 @@ from ._native import (  # noqa: F401
     thc_rht_norm_quantize_ws_bytes, ga_ring_stage_bytes, ga_ring_stepwise_staged,
     fusion_block_bytes, thc_nmse_noalloc, thc_ring_step, thc_ring_step_ws_bytes,
     thc_ring_step_launches, thc_ef_minmax, thc_ef_quantize, thc_minmax_combine,
+    thc_ef_minmax_pair,
 )

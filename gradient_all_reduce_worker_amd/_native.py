@@ -31,7 +31,7 @@ EXPORTS = (
     "thc_rht_quantize", "thc_aggregate_dequant", "thc_aggregate_dequant_ws_bytes",
     "thc_rht_norm_quantize", "thc_rht_norm_quantize_ws_bytes", "thc_ring_step",
     "thc_ring_step_ws_bytes", "ga_ring_stage_bytes", "ga_ring_stepwise_staged",
-    "thc_ring_step_launches", "thc_minmax_combine",
+    "thc_ring_step_launches", "thc_minmax_combine", "thc_ef_minmax_pair",
 )
 
 
@@ -104,6 +104,7 @@ def load() -> C.CDLL:
     L.ga_fusion_ring_allreduce.argtypes = [vp, i64, i32, i32, i32, P64, i32, i64, i32,
                                            C.POINTER(RingStats), vp]
     L.thc_ef_minmax.argtypes = [C.POINTER(vp), C.POINTER(vp), i32, i64, i32, i64, vp, vp]
+    L.thc_ef_minmax_pair.argtypes = [C.POINTER(vp), C.POINTER(vp), i32, i64, i32, i64, vp, vp, vp]
     L.thc_ef_quantize.argtypes = [C.POINTER(vp), C.POINTER(vp), i32, i32, i64, i32, i64, vp, i32,
                                   i32, C.POINTER(i32), u64, C.POINTER(vp), vp]
     L.thc_aggregate_dequant.argtypes = [C.POINTER(vp), i32, i64, i32, i32, C.POINTER(i32), i64, vp, vp,
@@ -593,6 +594,22 @@ def thc_ef_minmax(bufs: Sequence[torch.Tensor], errs: Sequence[torch.Tensor], pa
     _check(load().thc_ef_minmax(_ptr_array(bufs, "buffer"), _errs(errs, N), len(bufs), N,
                                 _dt(bufs[0]), part_elems, _dev(out, "mM"), _stream(stream)))
     return out
+
+
+def thc_ef_minmax_pair(bufs: Sequence[torch.Tensor], errs: Sequence[torch.Tensor], part_elems: int = 0,
+                       out_x: Optional[torch.Tensor] = None, out_ef: Optional[torch.Tensor] = None,
+                       stream=None):
+    """The grids of x and of x + e in one read; returns (grids of x, grids of x + e)."""
+    N = bufs[0].numel()
+    shape = (max(n_partitions(N, part_elems), 1), 2)
+    if out_x is None:
+        out_x = torch.empty(shape, dtype=torch.float32, device=bufs[0].device)
+    if out_ef is None:
+        out_ef = torch.empty(shape, dtype=torch.float32, device=bufs[0].device)
+    _check(load().thc_ef_minmax_pair(_ptr_array(bufs, "buffer"), _errs(errs, N), len(bufs), N,
+                                     _dt(bufs[0]), part_elems, _dev(out_x, "mM"), _dev(out_ef, "mM"),
+                                     _stream(stream)))
+    return out_x, out_ef
 
 
 def thc_ef_quantize(bufs: Sequence[torch.Tensor], errs: Sequence[torch.Tensor], mM: torch.Tensor,

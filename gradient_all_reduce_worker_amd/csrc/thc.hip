@@ -100,10 +100,14 @@ __device__ __forceinline__ void load_err_vec(const float* err, int64_t v, float*
 // Workgroup (p, j) scans slice j of partition p in every worker's buffer.
 // EF: the values scanned are x + e (error feedback) in binary32; vec_ok
 // says every x and e buffer is 16-byte aligned, else elements go one by one.
-template <ga_dtype DT, bool EF>
+// BOTH (with EF): the extremes of x alone as well, into keys_x, from the
+// same loads (the plain grid and the error-feedback grid in one read).
+template <ga_dtype DT, bool EF, bool BOTH = false>
 __global__ __launch_bounds__(kThreads) void minmax_kernel(PtrTable bufs, PtrTable errs, int vec_ok,
                                                           int P, int64_t N, int64_t plen, int slices,
-                                                          int64_t slice_len, uint32_t* keys) {
+                                                          int64_t slice_len, uint32_t* keys,
+                                                          uint32_t* keys_x = nullptr) {
+    static_assert(EF || !BOTH, "both grids need the residuals");
     using V = Vec16<DT>;
     constexpr int E = V::kElems;
     const int64_t blk = flat_block();                     // a folded grid's extra workgroups
@@ -115,11 +119,17 @@ __global__ __launch_bounds__(kThreads) void minmax_kernel(PtrTable bufs, PtrTabl
     const int64_t hi = min(lo + slice_len, pend);
     if (lo >= hi) return;
     float mn = INFINITY, mx = -INFINITY;
+    float mn0 = INFINITY, mx0 = -INFINITY;                // BOTH: x alone
     constexpr int es = DT == GA_BF16 ? 2 : 4;
     if (EF && !vec_ok) {
         for (int w = 0; w < P; w++)
             for (int64_t e = lo + threadIdx.x; e < hi; e += kThreads) {
-                const float a = load_as_f32(bufs.p[w], e, DT) + static_cast<const float*>(errs.p[w])[e];
+                const float x0 = load_as_f32(bufs.p[w], e, DT);
+                if (BOTH) {
+                    mn0 = fminf(mn0, x0);
+                    mx0 = fmaxf(mx0, x0);
+                }
+                const float a = x0 + static_cast<const float*>(errs.p[w])[e];
                 mn = fminf(mn, a);
                 mx = fmaxf(mx, a);
             }
@@ -134,7 +144,12 @@ __global__ __launch_bounds__(kThreads) void minmax_kernel(PtrTable bufs, PtrTabl
         const int64_t vhi = vlo + nv * E;
         const float* ew = EF ? static_cast<const float*>(errs.p[w]) : nullptr;
         for (int64_t e = lo + threadIdx.x; e < vlo; e += kThreads) {
-            const float a = EF ? load_as_f32(x, e, DT) + ew[e] : load_as_f32(x, e, DT);
+            const float x0 = load_as_f32(x, e, DT);
+            if (BOTH) {
+                mn0 = fminf(mn0, x0);
+                mx0 = fmaxf(mx0, x0);
+            }
+            const float a = EF ? x0 + ew[e] : x0;
             mn = fminf(mn, a);
             mx = fmaxf(mx, a);
         }
@@ -154,7 +169,13 @@ __global__ __launch_bounds__(kThreads) void minmax_kernel(PtrTable bufs, PtrTabl
 #pragma unroll
                 for (int u = 0; u < 4; u++)
 #pragma unroll
-                    for (int i = 0; i < E; i++) f[u][i] = f[u][i] + g[u][i];
+                    for (int i = 0; i < E; i++) {
+                        if (BOTH) {
+                            mn0 = fminf(mn0, f[u][i]);
+                            mx0 = fmaxf(mx0, f[u][i]);
+                        }
+                        f[u][i] = f[u][i] + g[u][i];
+                    }
             }
 #pragma unroll
             for (int u = 0; u < 4; u++)
@@ -171,7 +192,13 @@ __global__ __launch_bounds__(kThreads) void minmax_kernel(PtrTable bufs, PtrTabl
                 float g[E];
                 load_err_vec<DT>(ea, v, g);
 #pragma unroll
-                for (int i = 0; i < E; i++) f[i] = f[i] + g[i];
+                for (int i = 0; i < E; i++) {
+                    if (BOTH) {
+                        mn0 = fminf(mn0, f[i]);
+                        mx0 = fmaxf(mx0, f[i]);
+                    }
+                    f[i] = f[i] + g[i];
+                }
             }
 #pragma unroll
             for (int i = 0; i < E; i++) {
@@ -181,26 +208,47 @@ __global__ __launch_bounds__(kThreads) void minmax_kernel(PtrTable bufs, PtrTabl
         }
         // tail
         for (int64_t e = vhi + threadIdx.x; e < hi; e += kThreads) {
-            const float a = EF ? load_as_f32(x, e, DT) + ew[e] : load_as_f32(x, e, DT);
+            const float x0 = load_as_f32(x, e, DT);
+            if (BOTH) {
+                mn0 = fminf(mn0, x0);
+                mx0 = fmaxf(mx0, x0);
+            }
+            const float a = EF ? x0 + ew[e] : x0;
             mn = fminf(mn, a);
             mx = fmaxf(mx, a);
         }
     }
-    __shared__ float smn[kThreads / 64], smx[kThreads / 64];
+    __shared__ float smn[2][kThreads / 64], smx[2][kThreads / 64];
     mn = wave_min(mn);
     mx = wave_max(mx);
+    if (BOTH) {
+        mn0 = wave_min(mn0);
+        mx0 = wave_max(mx0);
+    }
     if ((threadIdx.x & 63) == 0) {
-        smn[threadIdx.x >> 6] = mn;
-        smx[threadIdx.x >> 6] = mx;
+        smn[0][threadIdx.x >> 6] = mn;
+        smx[0][threadIdx.x >> 6] = mx;
+        if (BOTH) {
+            smn[1][threadIdx.x >> 6] = mn0;
+            smx[1][threadIdx.x >> 6] = mx0;
+        }
     }
     __syncthreads();
     if (threadIdx.x == 0) {
         for (int i = 1; i < kThreads / 64; i++) {
-            mn = fminf(mn, smn[i]);
-            mx = fmaxf(mx, smx[i]);
+            mn = fminf(mn, smn[0][i]);
+            mx = fmaxf(mx, smx[0][i]);
+            if (BOTH) {
+                mn0 = fminf(mn0, smn[1][i]);
+                mx0 = fmaxf(mx0, smx[1][i]);
+            }
         }
         atomicMin(&keys[2 * p], order_key(mn));
         atomicMax(&keys[2 * p + 1], order_key(mx));
+        if (BOTH) {
+            atomicMin(&keys_x[2 * p], order_key(mn0));
+            atomicMax(&keys_x[2 * p + 1], order_key(mx0));
+        }
     }
 }
 
@@ -1030,8 +1078,10 @@ using namespace ga;
 namespace ga {
 namespace {
 
+// d_mM_x (with errs): the grids of x alone as well, from the same read.
 ga_status minmax_impl(const void* const* bufs, const float* const* errs, int32_t P, int64_t N,
-                      ga_dtype dt, int64_t part_elems, float* d_mM, void* stream, const char* what) {
+                      ga_dtype dt, int64_t part_elems, float* d_mM, void* stream, const char* what,
+                      float* d_mM_x = nullptr) {
     if (!valid_dtype(dt)) return fail(GA_EINVAL, "%s: unknown dtype %d", what, (int)dt);
     if (N < 0 || part_elems < 0) return fail(GA_EINVAL, "%s: negative size", what);
     if (P < 1 || P > GA_MAX_WORKERS) return fail(GA_EINVAL, "%s: P = %d outside [1, %d]", what, P, GA_MAX_WORKERS);
@@ -1042,6 +1092,11 @@ ga_status minmax_impl(const void* const* bufs, const float* const* errs, int32_t
     if (!d_mM || !aligned(d_mM, 8)) return fail(GA_EINVAL, "%s: bad output pointer", what);
     const int64_t plen = part_elems > 0 ? part_elems : N;
     const int64_t n_part = n_partitions(N, part_elems);
+    if (d_mM_x) {
+        const uintptr_t a = (uintptr_t)d_mM, b = (uintptr_t)d_mM_x, n = (uintptr_t)(8 * n_part);
+        if (!errs || !aligned(d_mM_x, 8) || (a < b + n && b < a + n))
+            return fail(GA_EINVAL, "%s: bad or overlapping output pointer", what);
+    }
     // ~4096 workgroups in total, slices of at least 4096 elements, a
     // multiple of 64 elements so aligned partitions keep aligned slices
     int64_t slices = std::max<int64_t>(1, std::min<int64_t>(ceil_div(plen, 4096), ceil_div(4096, n_part)));
@@ -1050,6 +1105,7 @@ ga_status minmax_impl(const void* const* bufs, const float* const* errs, int32_t
     if (!flat_fits(n_part * slices)) return fail(GA_EINVAL, "%s: too many partitions", what);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     uint32_t* keys = reinterpret_cast<uint32_t*>(d_mM);
+    uint32_t* keys_x = reinterpret_cast<uint32_t*>(d_mM_x);
     PtrTable t{}, te{};
     int vec_ok = 1;
     for (int i = 0; i < P; i++) {
@@ -1062,8 +1118,17 @@ ga_status minmax_impl(const void* const* bufs, const float* const* errs, int32_t
     hipLaunchKernelGGL(minmax_init_kernel, flat_grid(ceil_div(n_part, kThreads)), dim3(kThreads), 0, hs, keys,
                        n_part);
     if ((rc = check_launch(what))) return rc;
+    if (keys_x) {
+        hipLaunchKernelGGL(minmax_init_kernel, flat_grid(ceil_div(n_part, kThreads)), dim3(kThreads), 0, hs,
+                           keys_x, n_part);
+        if ((rc = check_launch(what))) return rc;
+    }
     const dim3 grid = flat_grid(n_part * slices);
-    if (dt == GA_F32 && errs)
+    if (keys_x && dt == GA_F32)
+        hipLaunchKernelGGL((minmax_kernel<GA_F32, true, true>), grid, dim3(kThreads), 0, hs, t, te, vec_ok, P, N, plen, (int)slices, slice_len, keys, keys_x);
+    else if (keys_x)
+        hipLaunchKernelGGL((minmax_kernel<GA_BF16, true, true>), grid, dim3(kThreads), 0, hs, t, te, vec_ok, P, N, plen, (int)slices, slice_len, keys, keys_x);
+    else if (dt == GA_F32 && errs)
         hipLaunchKernelGGL((minmax_kernel<GA_F32, true>), grid, dim3(kThreads), 0, hs, t, te, vec_ok, P, N, plen, (int)slices, slice_len, keys);
     else if (dt == GA_F32)
         hipLaunchKernelGGL((minmax_kernel<GA_F32, false>), grid, dim3(kThreads), 0, hs, t, te, vec_ok, P, N, plen, (int)slices, slice_len, keys);
@@ -1074,6 +1139,11 @@ ga_status minmax_impl(const void* const* bufs, const float* const* errs, int32_t
     if ((rc = check_launch(what))) return rc;
     hipLaunchKernelGGL(minmax_final_kernel, flat_grid(ceil_div(n_part, kThreads)), dim3(kThreads), 0, hs, keys,
                        n_part);
+    if (keys_x) {
+        if ((rc = check_launch(what))) return rc;
+        hipLaunchKernelGGL(minmax_final_kernel, flat_grid(ceil_div(n_part, kThreads)), dim3(kThreads), 0, hs,
+                           keys_x, n_part);
+    }
     return check_launch(what);
 }
 
@@ -1134,6 +1204,14 @@ extern "C" ga_status thc_ef_minmax(const void* const* bufs, const float* const* 
                                    void* stream) {
     if (!errs) return fail(GA_EINVAL, "thc_ef_minmax: null error buffers");
     return minmax_impl(bufs, errs, P, N, dt, part_elems, d_mM, stream, "thc_ef_minmax");
+}
+
+extern "C" ga_status thc_ef_minmax_pair(const void* const* bufs, const float* const* errs, int32_t P,
+                                        int64_t N, ga_dtype dt, int64_t part_elems, float* d_mM_x,
+                                        float* d_mM_ef, void* stream) {
+    if (!errs) return fail(GA_EINVAL, "thc_ef_minmax_pair: null residuals");
+    if (!d_mM_x) return fail(GA_EINVAL, "thc_ef_minmax_pair: bad output pointer");
+    return minmax_impl(bufs, errs, P, N, dt, part_elems, d_mM_ef, stream, "thc_ef_minmax_pair", d_mM_x);
 }
 
 namespace ga {

@@ -254,7 +254,14 @@ class Pipeline:
             return
         part = w.part_elems
         b0 = w.thc_bits[0] if self.fused_step else None
-        _call(timer, "thc_minmax", ga.thc_minmax, self.flat, part, self.mM)
+        # with error feedback, the partition grids of x and of the first
+        # error-feedback pass's x + e in one read of x and e
+        ef0 = f"ef{w.ef_bits[0]}" if w.ef_bits else None
+        if ef0:
+            _call(timer, f"thc_ef_minmax_pair_{ef0}", ga.thc_ef_minmax_pair, self.flat, self.err[ef0], part,
+                  self.mM, self.mM_ef[ef0])
+        else:
+            _call(timer, "thc_minmax", ga.thc_minmax, self.flat, part, self.mM)
         for b in w.thc_bits:
             if b == b0:
                 continue
@@ -276,8 +283,9 @@ class Pipeline:
                   self.rht_y[key], self.rht_ws[key], self.packed[key])
         for b in w.ef_bits:
             k = f"ef{b}"
-            _call(timer, f"thc_ef_minmax_{k}", ga.thc_ef_minmax, self.flat, self.err[k], part,
-                  self.mM_ef[k])
+            if k != ef0:
+                _call(timer, f"thc_ef_minmax_{k}", ga.thc_ef_minmax, self.flat, self.err[k], part,
+                      self.mM_ef[k])
             _call(timer, f"thc_ef_quantize_{k}", ga.thc_ef_quantize, self.flat, self.err[k],
                   self.mM_ef[k], b, w.quant_seed, part, 0, 0, None, self.packed[k])
         if self.fused_step:
@@ -410,6 +418,7 @@ class Pipeline:
         for b in w.ef_bits:
             k = f"ef{b}"
             out[f"thc_ef_minmax_{k}"] = P * N * (s + 4.0)
+            out[f"thc_ef_minmax_pair_{k}"] = P * N * (s + 4.0)      # x and e read once, both grids
             out[f"thc_ef_quantize_{k}"] = P * N * (s + 8.0 + b / 8.0)
             out[f"thc_int_aggregate_{k}"] = P * N * b / 8.0 + 4.0 * N
             out[f"thc_dequant_{k}"] = 4.0 * N + N * s

@@ -18,7 +18,8 @@
  *                                                  THC uniform quantization
  *   thc_nuhc_quantize / thc_nuhc_aggregate / thc_nuhc_dequant
  *                                                  THC with lookup tables
- *   thc_ef_minmax / thc_ef_quantize                error feedback
+ *   thc_ef_minmax / thc_ef_minmax_pair / thc_ef_quantize
+ *                                                  error feedback
  *   thc_rht_sumsq / thc_rht_range / thc_rht_forward / thc_rht_inverse /
  *   thc_rht_quantize / thc_rht_norm_quantize
  *                                                  randomized Hadamard
@@ -515,6 +516,19 @@ ga_status thc_nuhc_dequant(const int32_t* d_sum, int64_t N, int32_t P, int32_t g
  */
 ga_status thc_ef_minmax(const void* const* bufs, const float* const* errs, int32_t P, int64_t N,
                         ga_dtype dt, int64_t part_elems, float* d_mM, void* stream);
+
+/*
+ * thc_ef_minmax_pair -- thc_minmax and thc_ef_minmax of the same buffers in
+ * one read of the gradients and residuals: d_mM_x receives the grids of x
+ * alone and d_mM_ef those of x + e, each bit for bit what the single call
+ * writes ([THC] section 3, preliminary round; section 5, error feedback).
+ *   d_mM_x, d_mM_ef   device, 2 ceil(N / part_elems) floats each (8-byte
+ *                     aligned), disjoint
+ * Other arguments and errors as thc_ef_minmax.
+ */
+ga_status thc_ef_minmax_pair(const void* const* bufs, const float* const* errs, int32_t P, int64_t N,
+                             ga_dtype dt, int64_t part_elems, float* d_mM_x, float* d_mM_ef,
+                             void* stream);
 
 /*
  * thc_ef_quantize -- as thc_usq_quantize (h_table NULL; g ignored) or

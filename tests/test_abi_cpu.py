@@ -27,7 +27,7 @@ def _declared():
 def test_header_declarations_are_exported():
     L = nat.load()
     names = _declared()
-    assert len(names) == 35
+    assert len(names) == 36
     assert set(names) == set(nat.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -154,6 +154,18 @@ def test_center_tables_are_valid():
             assert T[0] == 0 and T[-1] == g and len(T) == 1 << b
             assert all(T[i] < T[i + 1] for i in range(len(T) - 1))
     assert nat.center_table(2, 3) == [0, 1, 2, 3]
+
+
+def test_ef_minmax_pair_errors_before_enqueue():
+    L = nat.load()
+    good = _ptrs([0x100000 * (i + 1) for i in range(2)])
+    errs = _ptrs([0x900000 * (i + 1) for i in range(2)])
+    f = L.thc_ef_minmax_pair
+    assert f(good, None, 2, 1000, 0, 100, 0x5000, 0x6000, None) == EINVAL      # no residuals
+    assert f(good, errs, 2, 1000, 0, 100, None, 0x6000, None) == EINVAL        # no grid of x
+    assert f(good, errs, 2, 1000, 0, 100, 0x5004, 0x6000, None) == EINVAL      # misaligned
+    assert f(good, errs, 2, 1000, 0, 100, 0x5000, 0x5040, None) == EINVAL      # overlapping grids
+    assert f(good, errs, 2, 1000, 5, 100, 0x5000, 0x6000, None) == EINVAL      # dtype
 
 
 def test_minmax_combine_errors_before_enqueue():

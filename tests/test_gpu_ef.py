@@ -109,3 +109,22 @@ def test_partial_aggregation(b):
     est = ga.thc_dequant(_to_dev(Sw), N, len(arrived), b, _to_dev(mMw), part_elems=part)
     want = oracle.dequant(Sw, len(arrived), b, part, mMw)
     assert np.array_equal(est.cpu().numpy()[:N].view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("dt", [ga.F32, ga.BF16])
+@pytest.mark.parametrize("P,N,part,mis", [(3, 70001, 1000, 0), (4, 8192 * 6, 8192, 0), (2, 17, 0, 0),
+                                          (8, 1 << 18, 1 << 16, 0), (5, 9000, 0, 1), (32, 4099, 64, 0)])
+def test_ef_minmax_pair_equals_both_calls(P, N, part, mis, dt):
+    """The grids of x and of x + e in one read: bit for bit thc_minmax and
+    thc_ef_minmax, and the oracle's (views one element off alignment take
+    the per-element path)."""
+    gs, es = _grads(P, N, dt, seed=N + P + mis, misalign=mis)
+    mx, mef = ga.thc_ef_minmax_pair(gs, es, part)
+    want_x = ga.thc_minmax(gs, part)
+    want_ef = ga.thc_ef_minmax(gs, es, part)
+    assert np.array_equal(mx.cpu().numpy().view(np.uint32), want_x.cpu().numpy().view(np.uint32))
+    assert np.array_equal(mef.cpu().numpy().view(np.uint32), want_ef.cpu().numpy().view(np.uint32))
+    hg = [_host(g) for g in gs]
+    assert np.array_equal(mx.cpu().numpy().view(np.uint32), oracle.minmax(hg, part).view(np.uint32))
+    xe = [oracle.ef_add(h, _host(e)) for h, e in zip(hg, es)]
+    assert np.array_equal(mef.cpu().numpy().view(np.uint32), oracle.minmax(xe, part).view(np.uint32))
