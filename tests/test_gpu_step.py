@@ -131,6 +131,56 @@ def test_step_two_level_nmse_and_optional_outputs(tdt):
         assert abs(got[k] - nmw[k]) <= 1e-6 * abs(nmw[k]), k
 
 
+def _tie_inputs(P, N):
+    """bf16 workers whose average lies exactly halfway between two bf16
+    values: every worker holds v and one (element e's worker e mod P) holds v
+    plus P/2 units in the last place, so the binary32 fold is exact and the
+    average is v + half a unit. Element kinds by e mod 6: near 1 and near -1,
+    subnormal (k * 2^-133) positive and negative, -0 in every worker, near
+    2^100; v's last bit alternates, so both ties to even (down and up) occur."""
+    e = np.arange(N)
+    kind, a = e % 6, (e // 6) % (128 - P // 2)
+    v = np.select([kind == 0, kind == 1, kind == 2, kind == 3, kind == 4],
+                  [0x3F80 + a, 0xBF80 + a, 1 + a, 0x8001 + a, 0x8000], 0x7180 + a).astype(np.uint16)
+    bump = np.where(kind == 4, 0, P // 2).astype(np.uint16)
+    return [np.where(e % P == w, v + bump, v).astype(np.uint16) for w in range(P)]
+
+
+@pytest.mark.parametrize("P", [2, 8, 16])
+def test_step_bf16_average_rounds_ties_to_even(P):
+    """The pass narrows the binary32 average and estimate to bf16 in
+    hardware; on exact ties, subnormals and -0 it gives the oracle's
+    round-to-nearest-even bits and the separate ring's."""
+    N, b, seed = 6 * 2048 * 4, 2, 77
+    print(f"thc_ring_step ties P={P} N={N}", flush=True)
+    hosts = _tie_inputs(P, N)
+    exact = sum(oracle.bf16_to_f32(h).astype(np.float64) for h in hosts) / P
+    low = exact.astype(np.float32).view(np.uint32) & 0xFFFF
+    kind = np.arange(N) % 6
+    assert np.all(low[kind != 4] == 0x8000)                   # every non-zero element is a tie
+    mMh = oracle.minmax(hosts, 0)
+    pk = [oracle.usq_quantize(hosts[i], i, 0, mMh, b, seed) for i in range(P)]
+    Sw = oracle.int_aggregate(pk, N, b)
+    xw = oracle.dequant(Sw, P, b, 0, mMh, oracle.BF16)
+    avg = [h.copy() for h in hosts]
+    oracle.ring_fold(avg, op=oracle.AVG, part=0)
+    kept = (exact.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    up = avg[0] != kept
+    assert up[kind != 4].any() and (~up[kind != 4]).any()     # ties rounded both ways
+    assert np.array_equal(avg[0][kind == 4], np.full((kind == 4).sum(), 0x8000, np.uint16))
+    bufs = [_to_dev(h, torch.bfloat16) for h in hosts]
+    sep = [t.clone() for t in bufs]
+    mM = _to_dev(mMh)
+    ga.ga_ring_allreduce_sim(sep, ga.AVG)
+    _, S2, x2, _ = ga.thc_ring_step(bufs, mM, b, seed)
+    torch.cuda.synchronize()
+    for i in range(P):
+        assert np.array_equal(_host(bufs[i]), avg[i]), i
+        assert np.array_equal(_host(sep[i]), avg[i]), i
+    assert np.array_equal(S2.cpu().numpy()[:N], Sw)
+    assert np.array_equal(_host(x2)[:N], xw)
+
+
 def test_step_refuses_what_it_does_not_cover():
     bufs = _inputs(2, 1004, torch.float32, seed=1)           # N not a multiple of 8
     mM = torch.zeros((1, 2), device=DEV)
