@@ -10,8 +10,8 @@
 // bits do not commute in floating point, so they run strictly in that order.
 //
 // Layout of the work (512-thread workgroups, an 8192-coordinate tile of
-// 32 KiB in LDS, padded by one word per 16 against bank conflicts; three or
-// four workgroups fit a CU, so one loads while another computes):
+// 32 KiB in LDS, padded against bank conflicts (pad() below); three or four
+// workgroups fit a CU, so one loads while another computes):
 //  * tile pass: a workgroup loads 8192 consecutive coordinates (several
 //    whole blocks when d < 8192) and runs stages 0 .. log2(T) - 1 with
 //    T = min(d, 8192);
@@ -44,7 +44,7 @@ constexpr int kTileBits = 13;
 constexpr int kTile = 1 << kTileBits;       // coordinates per LDS tile
 constexpr int kTT = 512;                    // threads per transform workgroup
 constexpr int kPer = kTile / kTT;           // coordinates per thread (16)
-constexpr int kLds = kTile + kTile / 16;    // padded tile, in words
+constexpr int kLds = kTile + kTile / 32 + 8 * (kTile / 256);   // padded tile, in words
 constexpr int kMaxBits = 22;                // d <= 2^22: G <= 512, W >= 16
 // blocks per chunk of the pipelined two-pass transform-and-quantize (32
 // workers x 138M fp32, d = 2^20: 64 -> 12.5 ms, 128 -> 12.1, 256 -> 12.0,
@@ -54,7 +54,23 @@ constexpr int kSignWords = 4 * 512;         // Philox blocks a workgroup may nee
 static_assert(kPer == 16, "one set of 16 coordinates per thread and group");
 constexpr uint32_t kSignDomain = 0x52485400u;
 
-__device__ __forceinline__ int pad(int i) { return i + (i >> 4); }
+// LDS word of tile index i. The LDS serves a wave's 32-bit accesses one
+// half-wave at a time over 32 banks (measured on gfx950: lanes 0-31 over
+// words 0-15 and 32-47 take two passes, lanes 0-31 over words 0-31 and
+// lanes 32-63 over 64-95 one). One word per 32 keeps 32 consecutive indices
+// on 32 banks (the loads, stores and rounding reads); eight more per 256
+// separate the half-wave's two rows in the 16-stride passes (indices
+// 0-15 and 256-271). Of the transform's patterns only a thread's 16
+// consecutive stores (first pass) still meet two to a bank. A sum of
+// shifted copies of i splits over disjoint bits: pad(a + b) = pad(a) +
+// pad(b) when a and b share no set bit, so a thread's 16 words are one
+// register plus immediate offsets.
+__host__ __device__ constexpr int pad(int i) { return i + (i >> 5) + 8 * (i >> 8); }
+static_assert(pad(kTile - 1) < kLds, "the padded tile fits");
+
+// pad(o + k kTT) for thread o < kTT, given po = pad(o): o and k kTT share
+// no set bit (kTT a power of two), so the sum is split at compile time.
+__device__ __forceinline__ int pad_at(int po, int k) { return po + pad(k * kTT); }
 
 __device__ __forceinline__ float load_coord(const void* x, int64_t e, int64_t N, ga_dtype dt) {
     if (e >= N) return 0.0f;                 // zero padding to a whole block
@@ -88,35 +104,23 @@ __device__ __forceinline__ void butterflies(float* v) {
     }
 }
 
-// LDS index of thread o's first coordinate in a group16<WB> pass, and the
-// distance between its 16 coordinates in the padded tile:
-// pad(base + (r << WB)) - pad(base), since bits WB.. of base are clear.
+// LDS index of thread o's first coordinate in a group16<WB> pass; bits
+// WB .. WB+3 of it are clear, so coordinate r of the thread sits at
+// pad(base) + pad(r << WB).
 template <int WB>
 __device__ __forceinline__ int group_base(int o) {
     return ((o >> WB) << (WB + 4)) | (o & ((1 << WB) - 1));
 }
-template <int WB>
-constexpr int group_step() { return WB >= 4 ? (1 << WB) + (1 << (WB - 4)) : 1; }
 
 template <int WB, int LO, int HI>
 __device__ __forceinline__ void group16(float* s) {
-    const int base = group_base<WB>(threadIdx.x);
+    float* p = s + pad(group_base<WB>(threadIdx.x));
     float v[16];
-    if (WB == 0 || WB >= 4) {                     // a constant distance in the padded tile
-        float* p = s + pad(base);
-        constexpr int step = group_step<WB>();
 #pragma unroll
-        for (int r = 0; r < 16; r++) v[r] = p[r * step];
-        butterflies<WB, LO, HI>(v);
+    for (int r = 0; r < 16; r++) v[r] = p[pad(r << WB)];
+    butterflies<WB, LO, HI>(v);
 #pragma unroll
-        for (int r = 0; r < 16; r++) p[r * step] = v[r];
-    } else {                                      // the 16 coordinates cross padding words
-#pragma unroll
-        for (int r = 0; r < 16; r++) v[r] = s[pad(base + (r << WB))];
-        butterflies<WB, LO, HI>(v);
-#pragma unroll
-        for (int r = 0; r < 16; r++) s[pad(base + (r << WB))] = v[r];
-    }
+    for (int r = 0; r < 16; r++) p[pad(r << WB)] = v[r];
 }
 
 // Stages on index bits LO .. HI-1, four at a time, a barrier after each group.
@@ -233,17 +237,18 @@ __global__ __launch_bounds__(kTT) void rht_tile_kernel(PtrTable x, PtrTable y, i
         }
     }
     __syncthreads();                                  // the sign words
+    const int po = pad(threadIdx.x);
 #pragma unroll
     for (int k = 0; k < kPer; k++) {
         const int i = threadIdx.x + k * kTT;
-        s[pad(i)] = FWD && negated(words, i >> 7, i) ? -v[k] : v[k];
+        s[pad_at(po, k)] = FWD && negated(words, i >> 7, i) ? -v[k] : v[k];
     }
     __syncthreads();
     stages(s, 0, kbits);
 #pragma unroll
     for (int k = 0; k < kPer; k++) {
         const int i = threadIdx.x + k * kTT;
-        float r = s[pad(i)];
+        float r = s[pad_at(po, k)];
         if (!FINAL) {
             if (i < n) (static_cast<float*>(y.p[w]) + e0)[i] = r;
         } else if (FWD) {
@@ -279,10 +284,11 @@ __global__ __launch_bounds__(kTT) void rht_cross_kernel(PtrTable y, PtrTable out
     const int64_t b = blockIdx.x >> gbits;
     const int64_t base = (b << dbits) + (int64_t)(blockIdx.x & (G - 1)) * W;   // a multiple of 16
     float* yb = static_cast<float*>(y.p[w]) + base;
+    const int po = pad(threadIdx.x);
 #pragma unroll
     for (int k = 0; k < kPer; k++) {
         const int i = threadIdx.x + k * kTT;
-        s[pad(i)] = yb[(i >> wbits) * kTile + (i & (W - 1))];
+        s[pad_at(po, k)] = yb[(i >> wbits) * kTile + (i & (W - 1))];
     }
     // inverse: the Philox blocks of every (row, 128-column group); R per row
     const int R = W >= 128 ? W >> 7 : 1;
@@ -306,7 +312,7 @@ __global__ __launch_bounds__(kTT) void rht_cross_kernel(PtrTable y, PtrTable out
         const int i = threadIdx.x + k * kTT;
         const int j = i >> wbits, col = i & (W - 1);
         const int off = j * kTile + col;
-        float v = s[pad(i)] * c;
+        float v = s[pad_at(po, k)] * c;
         if (FWD) {
             yb[off] = mM ? clamp_to(v, mM, b) : v;
         } else if (off < nb) {
@@ -346,10 +352,11 @@ __device__ __forceinline__ uint64_t round_group(const float* s, int i0, int64_t 
                                                 uint32_t wid, uint32_t q0, uint32_t q1) {
     const uint64_t g = (uint64_t)e >> 3;
     const Philox4 r = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), wid, 0u, q0, q1);
+    const float* q = s + pad(i0);                    // i0 a multiple of 8: pad(i0 + i) = pad(i0) + i
     uint32_t z[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-        const float v = __builtin_amdgcn_fmed3f(s[pad(i0 + i)] * c, bg.m, bg.M);   // clamp
+        const float v = __builtin_amdgcn_fmed3f(q[i] * c, bg.m, bg.M);   // clamp
         z[i] = rd.index(v, bg.g, uniform16(r, i));
     }
     return pack_group<B>(z);
@@ -364,12 +371,13 @@ __device__ __forceinline__ uint64_t round_group_mixed(const float* s, int i0, in
                                                       uint32_t q0, uint32_t q1) {
     const uint64_t g = (uint64_t)e >> 3;
     const Philox4 r = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), wid, 0u, q0, q1);
+    const float* q = s + pad(i0);                    // i0 a multiple of 8
     uint32_t z[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) {
         if (i < n_in) {
             const int64_t blk = (e + i) >> dbits;
-            const float v = clamp_to(s[pad(i0 + i)] * c, mM, blk);
+            const float v = clamp_to(q[i] * c, mM, blk);
             z[i] = rd.index(v, grid_of(mM, blk, rd.levels), uniform16(r, i));
         } else {
             z[i] = 0u;                               // past the vector's end: index 0
@@ -408,10 +416,11 @@ __global__ __launch_bounds__(kTT) void rht_tile_quant_kernel(PtrTable x, PtrTabl
         }
     }
     __syncthreads();                                  // the sign words
+    const int po = pad(threadIdx.x);
 #pragma unroll
     for (int k = 0; k < kPer; k++) {
         const int i = threadIdx.x + k * kTT;
-        s[pad(i)] = negated(words, i >> 7, i) ? -v[k] : v[k];
+        s[pad_at(po, k)] = negated(words, i >> 7, i) ? -v[k] : v[k];
     }
     __syncthreads();
     stages(s, 0, kbits);
@@ -509,10 +518,11 @@ __device__ __forceinline__ void forward_tile_body(float* s, uint32_t* words, con
     for (int r = 0; r < 16; r++) p[r] = v[r];
     __syncthreads();
     stages_ct<4, kTileBits - 1>(s);
+    const int po = pad(threadIdx.x);
 #pragma unroll
     for (int k = 0; k < kPer / 2; k++) {
-        const int i = threadIdx.x + k * kTT;
-        const float a = s[pad(i)], b = s[pad(i + kTile / 2)];
+        const int i = threadIdx.x + k * kTT;            // < kTile / 2
+        const float a = s[pad_at(po, k)], b = s[pad_at(po, k) + pad(kTile / 2)];
         (y + e0)[i] = a + b;
         (y + e0)[i + kTile / 2] = a - b;
     }
@@ -554,7 +564,7 @@ __device__ __forceinline__ void cross_quant_body(float* s, const Rounder<TABLE>&
     butterflies<WB, WBITS, H1>(v);
     float* p = s + pad(lb);
 #pragma unroll
-    for (int r = 0; r < 16; r++) p[r * group_step<WB>()] = v[r];
+    for (int r = 0; r < 16; r++) p[pad(r << WB)] = v[r];
     __syncthreads();
     stages_ct<H1, kTileBits>(s);
     const BlockGrid bg = block_grid(mM, b, rd.levels);   // one block per workgroup
