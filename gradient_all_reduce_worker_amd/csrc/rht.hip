@@ -48,7 +48,11 @@ constexpr int kLds = kTile + kTile / 32 + 8 * (kTile / 256);   // padded tile, i
 constexpr int kMaxBits = 22;                // d <= 2^22: G <= 512, W >= 16
 // blocks per chunk of the pipelined two-pass transform-and-quantize (32
 // workers x 138M fp32, d = 2^20: 64 -> 12.5 ms, 128 -> 12.1, 256 -> 12.0,
-// 512 -> 12.5; fewer launches against longer unpaired first and last ones)
+// 512 -> 12.5; fewer launches against longer unpaired first and last ones).
+// Chunks whose transformed vectors would fit the 256 MB Infinity Cache
+// between the two passes (16 or 32 blocks: 64 or 128 MiB) take 13.8 ms:
+// the second pass does not get its input from the cache, and the launches
+// multiply.
 constexpr int64_t kPipeUnits = 256;
 constexpr int kSignWords = 4 * 512;         // Philox blocks a workgroup may need, x 4
 static_assert(kPer == 16, "one set of 16 coordinates per thread and group");
