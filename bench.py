@@ -68,6 +68,31 @@ def source_hash(kernel: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def runtime_copy_rate(nbytes: int = 4 << 30, reps: int = 5) -> dict:
+    """The HIP runtime's own device-to-device copy of nbytes (its copy
+    kernel: one read and one write stream), timed on this machine after the
+    bench's steps. Context for `frac`, not a ceiling: MI355X machines differ
+    by several percent for the same streaming kernel, and this shows what a
+    vendor streaming kernel reaches on the same machine in the same run."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ms = []
+    for _ in range(reps):
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    del src, dst
+    t = sorted(ms)[reps // 2]
+    gbs = 2 * nbytes / (t * 1e-3) / 1e9
+    return {"GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes": 2 * nbytes}
+
+
 def traffic_from_profile(workload: str, kernel: str):
     """HBM bytes per launch of the dominant kernel from the committed PMC
     summary, if one was measured on this workload and on the kernel's
@@ -394,7 +419,8 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profile(args.workload, kernel) if one_launch else None,
-                "kernel": kernel, "alg_bytes_per_launch": per_launch, "launches_per_call": launches}
+                "kernel": kernel, "alg_bytes_per_launch": per_launch, "launches_per_call": launches,
+                "runtime_copy": runtime_copy_rate()}
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
