@@ -420,7 +420,9 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profile(args.workload, kernel) if one_launch else None,
                 "kernel": kernel, "alg_bytes_per_launch": per_launch, "launches_per_call": launches,
-                "runtime_copy": runtime_copy_rate()}
+                # not in counter runs: their byte scale is the 1 GiB copy above,
+                # the largest runtime copy of the run
+                "runtime_copy": None if args.copy_probe else runtime_copy_rate()}
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,

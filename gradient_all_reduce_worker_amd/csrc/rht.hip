@@ -457,10 +457,20 @@ __global__ __launch_bounds__(kTT) void rht_tile_quant_kernel(PtrTable x, PtrTabl
 // bits of one Philox word, and runs stages 0-3 in registers before the
 // first LDS store; stages 4-11 go through LDS and stage 12 is applied on
 // the way out (a thread holds both coordinates of its last butterflies).
+// wbits = 0: y in the vector's order. wbits > 0 (scratch for the second
+// pass of blocks of G = 2^(kTileBits - wbits) tiles): column-blocked, so
+// that each second-pass workgroup reads one contiguous run. Within a block,
+// column i of tile (row) j sits at (i >> wbits) kTile + j W + (i mod W),
+// W = 2^wbits: the G x W sub-matrix of column group i >> wbits is one
+// kTile-long run. Written and read once, in whole lines, both nontemporal.
+// Measured on 32 x 138M fp32, d = 2^20, table b = 4 (uniform b = 4), builds
+// in alternating processes on one box: the vector's order 12.1 (12.7) ms;
+// column-blocked 11.8 (12.4); its stores nontemporal 11.0 (11.8); loads too
+// 11.0 (11.2).
 template <ga_dtype DT>
 __device__ __forceinline__ void forward_tile_body(float* s, uint32_t* words, const void* x, float* y,
                                                   int64_t tile, int64_t N, bool vec, uint32_t k0,
-                                                  uint32_t k1, double* norm = nullptr) {
+                                                  uint32_t k1, double* norm = nullptr, int wbits = 0) {
     const int64_t e0 = tile * kTile;
     const int nx = (int)max((int64_t)0, min((int64_t)kTile, N - e0));
     const int i0 = 16 * threadIdx.x;
@@ -523,12 +533,27 @@ __device__ __forceinline__ void forward_tile_body(float* s, uint32_t* words, con
     __syncthreads();
     stages_ct<4, kTileBits - 1>(s);
     const int po = pad(threadIdx.x);
+    if (wbits == 0) {
 #pragma unroll
-    for (int k = 0; k < kPer / 2; k++) {
-        const int i = threadIdx.x + k * kTT;            // < kTile / 2
-        const float a = s[pad_at(po, k)], b = s[pad_at(po, k) + pad(kTile / 2)];
-        (y + e0)[i] = a + b;
-        (y + e0)[i + kTile / 2] = a - b;
+        for (int k = 0; k < kPer / 2; k++) {
+            const int i = threadIdx.x + k * kTT;        // < kTile / 2
+            const float a = s[pad_at(po, k)], b = s[pad_at(po, k) + pad(kTile / 2)];
+            (y + e0)[i] = a + b;
+            (y + e0)[i + kTile / 2] = a - b;
+        }
+    } else {
+        const int W = 1 << wbits;
+        const int j = (int)(tile & ((1 << (kTileBits - wbits)) - 1));      // row in the block
+        float* yb = y + (e0 - (int64_t)j * kTile) + j * W;                 // the block, row j
+        const int half = (kTile / 2) >> wbits;                             // column groups to i + kTile / 2
+#pragma unroll
+        for (int k = 0; k < kPer / 2; k++) {
+            const int i = threadIdx.x + k * kTT;
+            const float a = s[pad_at(po, k)], b = s[pad_at(po, k) + pad(kTile / 2)];
+            const int off = (i >> wbits) * kTile + (i & (W - 1));
+            __builtin_nontemporal_store(a + b, yb + off);      // read once, by the second pass
+            __builtin_nontemporal_store(a - b, yb + off + half * kTile);
+        }
     }
 }
 
@@ -546,8 +571,10 @@ __global__ __launch_bounds__(kTT) void rht_forward_tile_kernel(PtrTable x, PtrTa
 // block b, columns cg W .. cg W + W - 1 (W = 2^WBITS >= 16), then the G x W
 // sub-matrix rounded in groups of 8 consecutive columns of a row. The first
 // four stages (row bits) run in registers on coordinates loaded straight
-// from y: thread o takes 16 rows of one column, so each load instruction
-// reads consecutive columns across the wave.
+// from y, which the first pass left column-blocked: the sub-matrix is one
+// contiguous run of kTile values, row after row; thread o takes 16 rows of
+// one column, so each load instruction reads consecutive values across the
+// wave.
 template <int B, bool TABLE, int WBITS>
 __device__ __forceinline__ void cross_quant_body(float* s, const Rounder<TABLE>& rd, const float* y,
                                                  uint8_t* out, uint32_t wid, int64_t b, int cg,
@@ -556,15 +583,12 @@ __device__ __forceinline__ void cross_quant_body(float* s, const Rounder<TABLE>&
     constexpr int W = 1 << WBITS;
     constexpr int WB = WBITS < kTileBits - 4 ? WBITS : kTileBits - 4;
     constexpr int H1 = WB + 4;                        // first pass: bits WBITS .. H1-1
-    const int64_t base = (b << dbits) + (int64_t)cg * W;
-    const float* yb = y + base;
+    const int64_t base = (b << dbits) + (int64_t)cg * W;             // row 0, column cg W
+    const float* yb = y + (b << dbits) + (int64_t)cg * kTile;         // the sub-matrix's run
     const int lb = group_base<WB>(threadIdx.x);
     float v[16];
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-        const int i = lb + (r << WB);
-        v[r] = yb[(i >> WBITS) * kTile + (i & (W - 1))];
-    }
+    for (int r = 0; r < 16; r++) v[r] = __builtin_nontemporal_load(yb + lb + (r << WB));
     butterflies<WB, WBITS, H1>(v);
     float* p = s + pad(lb);
 #pragma unroll
@@ -648,7 +672,8 @@ __global__ __launch_bounds__(kTT) void rht_quant_pipe_kernel(PtrTable x, PtrTabl
     const int r = (int)(j & ((1 << gbits) - 1));
     if (first) {
         forward_tile_body<DT>(s, aux, x.p[w], static_cast<float*>(y.p[w]), (b << gbits) + r, N,
-                              vec != 0, k0, k1, norms ? norms + (unit << gbits) + r : nullptr);
+                              vec != 0, k0, k1, norms ? norms + (unit << gbits) + r : nullptr,
+                              2 * kTileBits - dbits);
     } else {
         const Rounder<TABLE> rd = make_rounder<TABLE, kTT>(tab, L, dyn_cells);
         cross_quant_dispatch<B, TABLE>(s, rd, static_cast<const float*>(y.p[w]),
