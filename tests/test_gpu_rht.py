@@ -209,6 +209,39 @@ def test_rht_quantize_matches_two_calls_and_oracle(P, d, N, b, g, table, dt):
         assert np.array_equal(got, want), i
 
 
+@pytest.mark.parametrize("table", [None, "center"])
+@pytest.mark.parametrize("dbits", [15, 17, 18, 19, 21, 22])
+def test_rht_quantize_every_column_width(dbits, table):
+    """The two-pass call keeps the first pass's output column-blocked for the
+    second (column groups of W = 2^(26 - dbits) values, W = 16 .. 2048): every
+    block size that takes that path, with a ragged last block, byte for byte
+    against the row-major forward transform followed by the quantizer, and
+    against the oracle."""
+    d = 1 << dbits
+    P, N, b = 2, d + 4097, 4
+    g = 36 if table else 0
+    T = ga.center_table(b, g) if table else None
+    bufs = _inputs(P, N, ga.F32, seed=dbits + 7)
+    xs = [_host(t) for t in bufs]
+    t_p = statistics.NormalDist().inv_cdf(1 - 1 / 32)
+    mMw = oracle.rht_range(np.stack([oracle.rht_sumsq(x, d) for x in xs]), d, t_p)
+    mM = torch.from_numpy(mMw).to(DEV)
+    Np = ga.rht_padded(N, d)
+    nbytes = ga.packed_bytes(Np, b)
+    print(f"rht_quantize d=2^{dbits} N={N} table={table is not None}", flush=True)
+    fused = ga.thc_rht_quantize(bufs, d, SEED, mM, b, 21, g=g, table=T)
+    y = ga.thc_rht_forward(bufs, d, SEED, mM=mM)
+    two = (ga.thc_usq_quantize(y, mM, b, 21, part_elems=d) if T is None else
+           ga.thc_nuhc_quantize(y, mM, b, g, T, 21, part_elems=d))
+    for i in range(P):
+        got = fused[i].cpu().numpy()[:nbytes]
+        assert np.array_equal(got, two[i].cpu().numpy()[:nbytes]), i
+    yc = oracle.clamp(oracle.rht_forward(xs[0], d, SEED), d, mMw)
+    want = (oracle.usq_quantize(yc, 0, d, mMw, b, 21) if T is None else
+            oracle.nuhc_quantize(yc, 0, d, mMw, b, g, T, 21))
+    assert np.array_equal(fused[0].cpu().numpy()[:nbytes], want)
+
+
 def test_rht_quantize_caller_buffers_and_empty():
     """Caller-provided scratch and packed buffers (reused across calls), and
     N = 0 leaves the output untouched."""
