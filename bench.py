@@ -70,7 +70,7 @@ def source_hash(kernel: str) -> str:
 
 def runtime_copy_rate(nbytes: int = 4 << 30, reps: int = 5) -> dict:
     """The HIP runtime's own device-to-device copy of nbytes (its copy
-    kernel: one read and one write stream), timed on this box after the
+    kernel: one read and one write stream), timed on this machine after the
     bench's steps. Context for `frac`, not a ceiling: MI355X machines differ
     by several percent for the same streaming kernel, and this shows what a
     vendor streaming kernel reaches on the same machine in the same run."""

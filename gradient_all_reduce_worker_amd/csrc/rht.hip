@@ -464,7 +464,7 @@ __global__ __launch_bounds__(kTT) void rht_tile_quant_kernel(PtrTable x, PtrTabl
 // W = 2^wbits: the G x W sub-matrix of column group i >> wbits is one
 // kTile-long run. Written and read once, in whole lines, both nontemporal.
 // Measured on 32 x 138M fp32, d = 2^20, table b = 4 (uniform b = 4), builds
-// in alternating processes on one box: the vector's order 12.1 (12.7) ms;
+// in alternating processes on one machine: the vector's order 12.1 (12.7) ms;
 // column-blocked 11.8 (12.4); its stores nontemporal 11.0 (11.8); loads too
 // 11.0 (11.2).
 template <ga_dtype DT>

@@ -31,7 +31,7 @@ from gradient_all_reduce_worker_amd.pipeline import Pipeline, t_p
 pytestmark = pytest.mark.gpu
 
 # oracle calls release the interpreter lock (ctypes), so threads run them in
-# parallel; the GPU machine grants 16 cores to one GPU
+# parallel; at most 16 threads, one GPU's share of a host
 POOL = max(1, min(16, len(os.sched_getaffinity(0))))
 N_SAMPLED = 16
 
